@@ -1,0 +1,260 @@
+"""CPU oracle for the sub-byte KV cache -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, obviously correct implementation of what the GPU library
+computes: the 4-bit Hadamard-32 row codec, the fp8 e4m3 latent codec, and
+decode attention over both caches in fp64.  The arithmetic lives in
+kvq_oracle.c (see its header for the pages and readings it follows); this
+module only marshals numpy arrays through ctypes.
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The product library (fp8_quantized_kv_amd) never imports it,
+and the two share no code.
+
+Parity pins: every function here is pinned by tests/test_oracle_*.py to
+values fixed by the pages or by mathematics (exact-scale example, exhaustive
+e4m3 and binary16 checks, Hadamard orthogonality, brute-force fp64
+attention); none is "parity unpinned".
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_D = ctypes.c_double
+
+
+def lib():
+    """Load liboracle.so, building it first if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = ctypes.CDLL(_LIB_PATH)
+        sig = {
+            "kvqo_num_threads": ([], _I),
+            "kvqo_f32_to_f16": ([ctypes.c_float], ctypes.c_uint16),
+            "kvqo_f16_to_f32": ([ctypes.c_uint16], ctypes.c_float),
+            "kvqo_e4m3_encode": ([ctypes.c_float], ctypes.c_uint8),
+            "kvqo_e4m3_decode": ([ctypes.c_uint8], _D),
+            "kvqo_q4_row_bytes": ([_I], ctypes.c_size_t),
+            "kvqo_q4_encode_row": ([_P, _I, _P], _I),
+            "kvqo_q4_encode_rows": ([_P, _I64, _I, _P], _I),
+            "kvqo_q4_decode_rows": ([_P, _I64, _I, _P], None),
+            "kvqo_hadamard32_f32_rows": ([_P, _I64], None),
+            "kvqo_rotate_f64": ([_P, _P, _I], None),
+            "kvqo_q4_store": ([_P, _P, _I, _I, _I, _I, _P, _P, _P, _I], _I),
+            "kvqo_q4_attention": ([_P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _D, _P, _P], _I),
+            "kvqo_q4_attention_chunked": ([_P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _D, _I, _I,
+                                           _P, _P, _P, _P, _P], _I),
+            "kvqo_fp8_encode_part": ([_P, _I, _P, _P], None),
+            "kvqo_fp8_store": ([_P, _P, _I, _I, _I64, _P, _P, _I], _I),
+            "kvqo_mla_attention": ([_P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _D, _P, _P], _I),
+            "kvqo_mla_attention_chunked": ([_P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _D, _I, _I,
+                                            _P, _P, _P, _P, _P], _I),
+            "kvqo_f32_to_f16_array": ([_P, _P, _I64], None),
+            "kvqo_e4m3_encode_array": ([_P, _P, _I64], None),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with status {rc}")
+
+
+def num_threads():
+    return lib().kvqo_num_threads()
+
+
+# ---------------------------------------------------------------- scalars
+
+def f32_to_f16_bits(x):
+    """binary16 bits of float32 values, round to nearest even (array)."""
+    x = _c(x, np.float32)
+    y = np.empty(x.shape, np.uint16)
+    lib().kvqo_f32_to_f16_array(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def f16_bits_to_f32(h):
+    return np.array([lib().kvqo_f16_to_f32(int(v)) for v in np.ravel(h)], np.float32).reshape(np.shape(h))
+
+
+def e4m3_encode(x):
+    """e4m3 codes of float32 values (array), saturating, NaN -> 0."""
+    x = _c(x, np.float32)
+    y = np.empty(x.shape, np.uint8)
+    lib().kvqo_e4m3_encode_array(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def e4m3_decode(codes):
+    return np.array([lib().kvqo_e4m3_decode(int(c)) for c in np.ravel(codes)], np.float64).reshape(np.shape(codes))
+
+
+# ---------------------------------------------------------------- 4-bit codec
+
+def q4_row_bytes(D):
+    return int(lib().kvqo_q4_row_bytes(D))
+
+
+def hadamard32_f32(x):
+    """The fp32 storage rotation applied to every 32-group of x (returns a copy)."""
+    x = np.array(x, dtype=np.float32, order="C", copy=True)
+    assert x.size % 32 == 0
+    lib().kvqo_hadamard32_f32_rows(_ptr(x), x.size // 32)
+    return x
+
+
+def rotate_f64(x):
+    """H32 applied to every 32-group of the last axis, fp64 (returns a copy)."""
+    x = _c(x, np.float64)
+    D = x.shape[-1]
+    flat = x.reshape(-1, D)
+    y = np.empty_like(flat)
+    for r in range(flat.shape[0]):
+        lib().kvqo_rotate_f64(_ptr(flat[r]), _ptr(y[r]), D)
+    return y.reshape(x.shape)
+
+
+def q4_encode_rows(x):
+    """x [..., D] float32 -> packed rows [..., D/2 + 2*D/32] uint8."""
+    x = _c(x, np.float32)
+    D = x.shape[-1]
+    n = x.size // D
+    out = np.empty(x.shape[:-1] + (q4_row_bytes(D),), np.uint8)
+    _check(lib().kvqo_q4_encode_rows(_ptr(x), n, D, _ptr(out)), "q4_encode_rows")
+    return out
+
+
+def q4_decode_rows(rows, D):
+    """packed rows [..., row_bytes] -> dequantized rotated values [..., D] fp64."""
+    rows = _c(rows, np.uint8)
+    n = rows.size // q4_row_bytes(D)
+    out = np.empty(rows.shape[:-1] + (D,), np.float64)
+    lib().kvqo_q4_decode_rows(_ptr(rows), n, D, _ptr(out))
+    return out
+
+
+def q4_pool_shape(num_pages, n_kv_heads, page_size, D):
+    return (num_pages, n_kv_heads, page_size, q4_row_bytes(D))
+
+
+def q4_store(k_pool, v_pool, k, v, slots, page_size):
+    """Encode K and V [n_tok][H_kv][D] into the paged pools (in place)."""
+    num_pages, H, ps, rb = k_pool.shape
+    assert ps == page_size and v_pool.shape == k_pool.shape
+    assert k_pool.flags.c_contiguous and v_pool.flags.c_contiguous
+    k = _c(k, np.float32)
+    v = _c(v, np.float32)
+    slots = _c(slots, np.int64)
+    D = k.shape[-1]
+    _check(lib().kvqo_q4_store(_ptr(k_pool), _ptr(v_pool), H, D, page_size, num_pages, _ptr(k), _ptr(v),
+                               _ptr(slots), len(slots)), "q4_store")
+
+
+def q4_attention(k_pool, v_pool, q, page_table, seq_lens, sm_scale, chunk=None, n_chunks=None,
+                 return_partials=False):
+    """fp64 decode attention over the paged 4-bit cache.
+
+    q: [B][H_q][D] float32 (unrotated).  Returns (o [B][H_q][D], lse [B][H_q]),
+    plus (acc, m, z) chunk partials when chunk is given and return_partials.
+    """
+    num_pages, H_kv, ps, rb = k_pool.shape
+    q = _c(q, np.float32)
+    B, H_q, D = q.shape
+    pt = _c(page_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    out = np.empty((B, H_q, D), np.float64)
+    lse = np.empty((B, H_q), np.float64)
+    if chunk is None:
+        _check(lib().kvqo_q4_attention(_ptr(k_pool), _ptr(v_pool), H_kv, D, ps, num_pages, _ptr(q), H_q,
+                                       _ptr(pt), pt.shape[1], _ptr(sl), B, float(sm_scale), _ptr(out),
+                                       _ptr(lse)), "q4_attention")
+        return out, lse
+    if n_chunks is None:
+        n_chunks = max(1, -(-int(sl.max()) // chunk)) if B else 1
+    pa = np.empty((B, H_q, n_chunks, D), np.float64) if return_partials else None
+    pm = np.empty((B, H_q, n_chunks), np.float64) if return_partials else None
+    pz = np.empty((B, H_q, n_chunks), np.float64) if return_partials else None
+    _check(lib().kvqo_q4_attention_chunked(_ptr(k_pool), _ptr(v_pool), H_kv, D, ps, num_pages, _ptr(q), H_q,
+                                           _ptr(pt), pt.shape[1], _ptr(sl), B, float(sm_scale), chunk, n_chunks,
+                                           _ptr(pa), _ptr(pm), _ptr(pz), _ptr(out), _ptr(lse)),
+           "q4_attention_chunked")
+    if return_partials:
+        return out, lse, (pa, pm, pz)
+    return out, lse
+
+
+# ---------------------------------------------------------------- fp8 latent codec
+
+def fp8_encode_part(x):
+    """One row part -> (codes uint8 [n], scale float32)."""
+    x = _c(x, np.float32)
+    codes = np.empty(x.shape, np.uint8)
+    sc = np.zeros(1, np.float32)
+    lib().kvqo_fp8_encode_part(_ptr(x), x.size, _ptr(codes), _ptr(sc))
+    return codes, sc[0]
+
+
+def fp8_store(codes_pool, scale_pool, x, slots, rope_dim):
+    """Encode latent rows x [n_tok][D] into codes_pool [n_slots][D], scale_pool [n_slots][2]."""
+    n_slots, D = codes_pool.shape
+    assert scale_pool.shape == (n_slots, 2) and scale_pool.dtype == np.float32
+    x = _c(x, np.float32)
+    slots = _c(slots, np.int64)
+    _check(lib().kvqo_fp8_store(_ptr(codes_pool), _ptr(scale_pool), D, rope_dim, n_slots, _ptr(x), _ptr(slots),
+                                len(slots)), "fp8_store")
+
+
+def mla_attention(codes_pool, scale_pool, q, page_table, seq_lens, sm_scale, rope_dim, page_size, chunk=None,
+                  n_chunks=None, return_partials=False):
+    """fp64 absorbed attention over the fp8 latent cache.  q: [B][H][D]."""
+    n_slots, D = codes_pool.shape
+    num_pages = n_slots // page_size
+    q = _c(q, np.float32)
+    B, H, Dq = q.shape
+    assert Dq == D
+    L = D - rope_dim
+    pt = _c(page_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    out = np.empty((B, H, L), np.float64)
+    lse = np.empty((B, H), np.float64)
+    if chunk is None:
+        _check(lib().kvqo_mla_attention(_ptr(codes_pool), _ptr(scale_pool), D, rope_dim, page_size, num_pages,
+                                        _ptr(q), H, _ptr(pt), pt.shape[1], _ptr(sl), B, float(sm_scale), _ptr(out),
+                                        _ptr(lse)), "mla_attention")
+        return out, lse
+    if n_chunks is None:
+        n_chunks = max(1, -(-int(sl.max()) // chunk)) if B else 1
+    pa = np.empty((B, H, n_chunks, L), np.float64) if return_partials else None
+    pm = np.empty((B, H, n_chunks), np.float64) if return_partials else None
+    pz = np.empty((B, H, n_chunks), np.float64) if return_partials else None
+    _check(lib().kvqo_mla_attention_chunked(_ptr(codes_pool), _ptr(scale_pool), D, rope_dim, page_size, num_pages,
+                                            _ptr(q), H, _ptr(pt), pt.shape[1], _ptr(sl), B, float(sm_scale), chunk,
+                                            n_chunks, _ptr(pa), _ptr(pm), _ptr(pz), _ptr(out), _ptr(lse)),
+           "mla_attention_chunked")
+    if return_partials:
+        return out, lse, (pa, pm, pz)
+    return out, lse

@@ -1,0 +1,644 @@
+/*
+ * kvq_oracle.c -- plain, slow CPU oracle for the sub-byte KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file states what the GPU library has to
+ * compute, as literally as possible, so that tests can compare the GPU
+ * results with it.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg load it.  The GPU library neither links nor calls it, and
+ * the two share no source: no headers, helpers, tables or constants.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC.
+ * Every float operation below is a single IEEE operation in the stated
+ * precision (fp32 for the codecs, fp64 for attention); nothing is fused.
+ *
+ * Sources (web pages, cited by title and the section the fact is in):
+ *   [TF]  TensorFold issue "qwen27 CUDA: an opt-in 4-bit attention cache
+ *         (262K on a 24 GB card)": section "What it is" (144-byte rows of
+ *         Hadamard-rotated 32-value groups, 4-bit codes plus an fp16 scale;
+ *         rotate the query once, attend in rotated space over 512-key
+ *         chunks and each row's tail, merge in order, rotate the output back).
+ *   [FT]  FreeToken pull request "feat(kvcache): add reliable quantized KV
+ *         cache": PR description (32 values -> 16 bytes + one fp16 scale,
+ *         0.5625 B/element) and the test-fix commit (scale = amax/8, the
+ *         exact-scale example, int32 arithmetic-shift sign extension).
+ *   [CO]  colibri pull request "KV cache quantization: fp8 (KV8) + 4-bit
+ *         TurboQuant (KV_TQ) on CPU, CUDA, and Metal": KV8 commit (e4m3
+ *         rows with a per-row f32 amax/448 scale, round-to-nearest-even
+ *         encoder saturating at +-448 with signed zero kept and NaN stored as
+ *         0, a guard for an amax so small that 448/amax overflows, absorbed
+ *         attention where the latent is key and value), split-T commit
+ *         (partials (cl[K], m, z) and a log-sum-exp merge), the
+ *         correctness/performance commit (NaN codes read as 0).
+ *
+ * Readings of points the pages leave open (each one is listed in the design
+ * notes with its reason):
+ *   - Hadamard: Sylvester order, orthonormal (entries +-1/sqrt(32)), no random
+ *     signs; it is its own inverse.
+ *   - fp32 butterfly in stages h = 1,2,4,8,16, then one multiply by
+ *     fp32(1/sqrt(32)) = 0x3E3504F3.
+ *   - scale = fp16_rne(amax/8); codes divide by that stored scale widened to
+ *     fp32; round half to even; clamp to [-8, 7]; scale 0 gives all-zero codes.
+ *   - element 2k in the low nibble, 2k+1 in the high nibble, two's complement.
+ *   - a row is D/2 bytes of codes (group after group), then D/32 fp16 scales,
+ *     little-endian.
+ *   - fp8 latent rows keep two scales per position: one for the 512-wide
+ *     latent part, one for the 64-wide rope part.
+ *   - an fp8 row whose amax is 0, non-finite, or so small that 448/amax is not
+ *     finite is stored inert: scale 0 and every code 0x00.
+ *   - the chunk partition of a sequence depends only on its length; chunks
+ *     are merged in ascending order.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define KVQO_OK 0
+#define KVQO_EDOMAIN (-1)
+#define KVQO_ERANGE (-2)
+#define KVQO_EARG (-3)
+
+int kvqo_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------ */
+/* IEEE binary16, round to nearest even ([TF] "What it is": fp16 scale) */
+/* ------------------------------------------------------------------ */
+
+/* Nearest binary16 value of f, ties to even mantissa, overflow to infinity.
+ * Written as "pick the nearest multiple of the binade's spacing" rather than
+ * as bit manipulation. */
+uint16_t kvqo_f32_to_f16(float f) {
+    double v = (double)f;
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (isnan(v)) return (uint16_t)(sign | 0x7E00u);
+    if (isinf(v)) return (uint16_t)(sign | 0x7C00u);
+    if (a == 0.0) return sign;
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal binade: spacing 2^-24; n == 1024 is the smallest normal */
+        double n = nearbyint(ldexp(a, 24));
+        return (uint16_t)(sign | (uint16_t)n);
+    }
+    int e2;
+    frexp(a, &e2);          /* a in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;         /* a in [2^E, 2^(E+1)) */
+    double n = nearbyint(ldexp(a, 10 - E)); /* in [1024, 2048] */
+    if (n == 2048.0) { n = 1024.0; E += 1; }
+    if (E > 15) return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | (uint16_t)(((E + 15) << 10) | ((int)n - 1024)));
+}
+
+float kvqo_f16_to_f32(uint16_t h) {
+    int s = (h >> 15) & 1, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 0) v = ldexp((double)m, -24);
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else v = ldexp((double)(1024 + m), e - 25);
+    return (float)(s ? -v : v);
+}
+
+/* ------------------------------------------------------------------ */
+/* Hadamard-32                                                         */
+/* ------------------------------------------------------------------ */
+
+/* fp32(1/sqrt(32)): the correctly rounded single of 0.17677669529663688... */
+static float kvqo_inv_sqrt32_f32(void) {
+    uint32_t bits = 0x3E3504F3u;
+    float c;
+    memcpy(&c, &bits, 4);
+    return c;
+}
+
+/* The storage rotation of one 32-value group, in fp32 ([TF] "What it is":
+ * rows are Hadamard-rotated in groups of 32).  Stages h = 1,2,4,8,16; each
+ * stage replaces (t_i, t_{i+h}) by (t_i + t_{i+h}, t_i - t_{i+h}) for every i
+ * with bit h clear; then every element is multiplied by fp32(1/sqrt(32)). */
+void kvqo_hadamard32_f32(float t[32]) {
+    for (int h = 1; h < 32; h <<= 1) {
+        for (int i = 0; i < 32; ++i) {
+            if (i & h) continue;
+            float a = t[i], b = t[i + h];
+            t[i] = a + b;
+            t[i + h] = a - b;
+        }
+    }
+    float c = kvqo_inv_sqrt32_f32();
+    for (int i = 0; i < 32; ++i) t[i] = t[i] * c;
+}
+
+/* Entry (i, j) of the orthonormal Sylvester Hadamard matrix of order 32. */
+static double kvqo_h32(int i, int j) {
+    return (__builtin_popcount((unsigned)(i & j)) & 1) ? -1.0 / sqrt(32.0) : 1.0 / sqrt(32.0);
+}
+
+/* y = H32 x for every 32-group of a length-n vector, in fp64, as a plain
+ * matrix-vector product.  H32 is symmetric and orthonormal, so the same call
+ * rotates the query ([TF] "rotate the queries once") and rotates the output
+ * back ("rotate the output back once"). */
+void kvqo_rotate_f64(const double* x, double* y, int n) {
+    for (int g = 0; g < n / 32; ++g) {
+        for (int i = 0; i < 32; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < 32; ++j) acc += kvqo_h32(i, j) * x[32 * g + j];
+            y[32 * g + i] = acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* 4-bit Hadamard-32 row codec                                         */
+/* ------------------------------------------------------------------ */
+
+size_t kvqo_q4_row_bytes(int D) { return (size_t)(D / 2 + 2 * (D / 32)); }
+
+/* Encode one row of D values (D % 32 == 0) into D/2 + 2*D/32 bytes.
+ * [TF] "What it is": rotated groups of 32, 4-bit codes plus an fp16 scale;
+ * [FT] PR description: 32 values -> 16 bytes + one fp16 scale;
+ * [FT] test-fix commit: scale = amax/8.
+ * Returns KVQO_EDOMAIN for a non-finite value or a scale beyond fp16 range. */
+int kvqo_q4_encode_row(const float* x, int D, uint8_t* row) {
+    if (D <= 0 || D % 32) return KVQO_EARG;
+    const int G = D / 32;
+    uint8_t* codes = row;
+    uint8_t* scales = row + D / 2;
+    for (int g = 0; g < G; ++g) {
+        float t[32];
+        for (int i = 0; i < 32; ++i) {
+            t[i] = x[32 * g + i];
+            if (!isfinite(t[i])) return KVQO_EDOMAIN;
+        }
+        kvqo_hadamard32_f32(t);
+        float amax = 0.0f;
+        for (int i = 0; i < 32; ++i) {
+            float a = fabsf(t[i]);
+            if (a > amax) amax = a;
+        }
+        uint16_t s16 = kvqo_f32_to_f16(amax / 8.0f);
+        if ((s16 & 0x7C00u) == 0x7C00u) return KVQO_EDOMAIN;
+        float s = kvqo_f16_to_f32(s16);
+        int q[32];
+        for (int i = 0; i < 32; ++i) {
+            if (s == 0.0f) { q[i] = 0; continue; }
+            float r = t[i] / s;           /* one correctly rounded fp32 divide */
+            float n = nearbyintf(r);      /* half to even */
+            if (n > 7.0f) n = 7.0f;
+            if (n < -8.0f) n = -8.0f;
+            q[i] = (int)n;
+        }
+        for (int k = 0; k < 16; ++k)
+            codes[16 * g + k] = (uint8_t)((q[2 * k] & 0xF) | ((q[2 * k + 1] & 0xF) << 4));
+        scales[2 * g] = (uint8_t)(s16 & 0xFF);
+        scales[2 * g + 1] = (uint8_t)(s16 >> 8);
+    }
+    return KVQO_OK;
+}
+
+/* Signed value of a two's-complement nibble. */
+static int kvqo_nibble(unsigned v) { return (v & 8u) ? (int)v - 16 : (int)v; }
+
+/* Dequantized row in the rotated domain: v_i = scale_g * code_i, exact in fp64. */
+void kvqo_q4_decode_row(const uint8_t* row, int D, double* out) {
+    const uint8_t* codes = row;
+    const uint8_t* scales = row + D / 2;
+    for (int g = 0; g < D / 32; ++g) {
+        uint16_t s16 = (uint16_t)(scales[2 * g] | (scales[2 * g + 1] << 8));
+        double s = (double)kvqo_f16_to_f32(s16);
+        for (int k = 0; k < 16; ++k) {
+            uint8_t b = codes[16 * g + k];
+            out[32 * g + 2 * k] = s * kvqo_nibble(b & 0xFu);
+            out[32 * g + 2 * k + 1] = s * kvqo_nibble(b >> 4);
+        }
+    }
+}
+
+/* Byte offset of the row of (slot, kv head) in a pool laid out as
+ * [num_pages][n_kv_heads][page_size][row_bytes]. */
+static size_t kvqo_row_offset(int64_t slot, int head, int n_kv_heads, int page_size, size_t row_bytes) {
+    int64_t page = slot / page_size, off = slot % page_size;
+    return (size_t)(((page * n_kv_heads + head) * page_size + off) * (int64_t)row_bytes);
+}
+
+/* Write K and V rows of n_tokens tokens into paged 4-bit pools.
+ * k, v: [n_tokens][n_kv_heads][D] fp32.  slot < 0 skips the token. */
+int kvqo_q4_store(uint8_t* k_pool, uint8_t* v_pool, int n_kv_heads, int D, int page_size, int num_pages,
+                  const float* k, const float* v, const int64_t* slots, int n_tokens) {
+    const size_t rb = kvqo_q4_row_bytes(D);
+    const int64_t n_slots = (int64_t)num_pages * page_size;
+    int err = KVQO_OK;
+    for (int t = 0; t < n_tokens; ++t)
+        if (slots[t] >= n_slots) return KVQO_ERANGE;
+#pragma omp parallel for schedule(static) reduction(min : err)
+    for (int t = 0; t < n_tokens; ++t) {
+        if (slots[t] < 0) continue;
+        for (int h = 0; h < n_kv_heads; ++h) {
+            size_t src = ((size_t)t * n_kv_heads + h) * D;
+            size_t dst = kvqo_row_offset(slots[t], h, n_kv_heads, page_size, rb);
+            int e1 = kvqo_q4_encode_row(k + src, D, k_pool + dst);
+            int e2 = kvqo_q4_encode_row(v + src, D, v_pool + dst);
+            if (e1 < err) err = e1;
+            if (e2 < err) err = e2;
+        }
+    }
+    return err;
+}
+
+/* ------------------------------------------------------------------ */
+/* Q4 decode attention                                                 */
+/* ------------------------------------------------------------------ */
+
+/* Slot of logical position j of sequence b (16-token or other pages). */
+static int64_t kvqo_slot(const int32_t* page_table, int max_pages, int b, int64_t j, int page_size) {
+    return (int64_t)page_table[(int64_t)b * max_pages + j / page_size] * page_size + j % page_size;
+}
+
+/* Decode attention over the 4-bit cache, as the definition states it
+ * ([TF] "What it is", decode rounds): q_rot = H q; for query head h of
+ * sequence b, KV head g = h / (n_q_heads / n_kv_heads), T = seq_lens[b]:
+ *   s_j = sm_scale * <q_rot, k_j>  over dequantized rotated keys, j < T
+ *   p = softmax(s)                  (fp64, max subtracted)
+ *   o = H * sum_j p_j v_j           (the output rotated back)
+ *   lse = max_j s_j + log(sum_j exp(s_j - max))
+ * T = 0 gives o = 0 and lse = -inf.  q: [B][n_q_heads][D] fp32, unrotated.
+ * out: [B][n_q_heads][D], lse: [B][n_q_heads] (may be NULL). */
+int kvqo_q4_attention(const uint8_t* k_pool, const uint8_t* v_pool, int n_kv_heads, int D, int page_size,
+                      int num_pages, const float* q, int n_q_heads, const int32_t* page_table, int max_pages,
+                      const int32_t* seq_lens, int B, double sm_scale, double* out, double* lse) {
+    if (n_q_heads % n_kv_heads) return KVQO_EARG;
+    const int G = n_q_heads / n_kv_heads;
+    const size_t rb = kvqo_q4_row_bytes(D);
+    for (int b = 0; b < B; ++b)
+        if (seq_lens[b] < 0 || (int64_t)seq_lens[b] > (int64_t)max_pages * page_size) return KVQO_ERANGE;
+    int err = KVQO_OK;
+#pragma omp parallel for schedule(dynamic, 1) reduction(min : err)
+    for (int bh = 0; bh < B * n_q_heads; ++bh) {
+        const int b = bh / n_q_heads, h = bh % n_q_heads, g = h / G;
+        const int64_t T = seq_lens[b];
+        double* o = out + (size_t)bh * D;
+        double* qd = malloc(sizeof(double) * D);
+        double* qr = malloc(sizeof(double) * D);
+        double* row = malloc(sizeof(double) * D);
+        double* orot = calloc((size_t)D, sizeof(double));
+        double* s = malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+        int st = KVQO_OK;
+        for (int i = 0; i < D; ++i) qd[i] = q[(size_t)bh * D + i];
+        kvqo_rotate_f64(qd, qr, D);
+        double m = -INFINITY;
+        for (int64_t j = 0; j < T; ++j) {
+            int64_t slot = kvqo_slot(page_table, max_pages, b, j, page_size);
+            if (slot < 0 || slot >= (int64_t)num_pages * page_size) { st = KVQO_ERANGE; break; }
+            kvqo_q4_decode_row(k_pool + kvqo_row_offset(slot, g, n_kv_heads, page_size, rb), D, row);
+            double dot = 0.0;
+            for (int i = 0; i < D; ++i) dot += qr[i] * row[i];
+            s[j] = sm_scale * dot;
+            if (s[j] > m) m = s[j];
+        }
+        double z = 0.0;
+        if (st == KVQO_OK) {
+            for (int64_t j = 0; j < T; ++j) {
+                int64_t slot = kvqo_slot(page_table, max_pages, b, j, page_size);
+                double w = exp(s[j] - m);
+                z += w;
+                kvqo_q4_decode_row(v_pool + kvqo_row_offset(slot, g, n_kv_heads, page_size, rb), D, row);
+                for (int i = 0; i < D; ++i) orot[i] += w * row[i];
+            }
+        }
+        if (T > 0) {
+            for (int i = 0; i < D; ++i) orot[i] /= z;
+            kvqo_rotate_f64(orot, o, D);
+        } else {
+            for (int i = 0; i < D; ++i) o[i] = 0.0;
+        }
+        if (lse) lse[bh] = T > 0 ? m + log(z) : -INFINITY;
+        if (st < err) err = st;
+        free(qd); free(qr); free(row); free(orot); free(s);
+    }
+    return err;
+}
+
+/* The same attention in the method's own structure ([TF] "What it is":
+ * chunks at absolute multiples of `chunk` keys, the last partial chunk being
+ * the row's tail, merged in order; [CO] split-T commit: each chunk yields
+ * (acc, m, z), combined by a log-sum-exp merge).  Per chunk c:
+ *   m_c = max s_j, z_c = sum exp(s_j - m_c), acc_c = sum exp(s_j - m_c) v_j
+ * (rotated domain, natural-log units of the scaled score); chunks past the
+ * end of a sequence are empty: m = -inf, z = 0, acc = 0.  Merge, ascending c:
+ *   M = max m_c, Z = sum z_c exp(m_c - M), o = H (sum acc_c exp(m_c - M)) / Z.
+ * part_acc [B][n_q_heads][n_chunks][D], part_m/part_z [B][n_q_heads][n_chunks]
+ * may be NULL; n_chunks = ceil(max(seq_lens) / chunk) when given. */
+int kvqo_q4_attention_chunked(const uint8_t* k_pool, const uint8_t* v_pool, int n_kv_heads, int D, int page_size,
+                              int num_pages, const float* q, int n_q_heads, const int32_t* page_table,
+                              int max_pages, const int32_t* seq_lens, int B, double sm_scale, int chunk,
+                              int n_chunks, double* part_acc, double* part_m, double* part_z, double* out,
+                              double* lse) {
+    if (n_q_heads % n_kv_heads || chunk <= 0) return KVQO_EARG;
+    const int G = n_q_heads / n_kv_heads;
+    const size_t rb = kvqo_q4_row_bytes(D);
+    for (int b = 0; b < B; ++b) {
+        if (seq_lens[b] < 0 || (int64_t)seq_lens[b] > (int64_t)max_pages * page_size) return KVQO_ERANGE;
+        if (((int64_t)seq_lens[b] + chunk - 1) / chunk > n_chunks) return KVQO_EARG;
+    }
+    int err = KVQO_OK;
+#pragma omp parallel for schedule(dynamic, 1) reduction(min : err)
+    for (int bh = 0; bh < B * n_q_heads; ++bh) {
+        const int b = bh / n_q_heads, h = bh % n_q_heads, g = h / G;
+        const int64_t T = seq_lens[b];
+        double* qd = malloc(sizeof(double) * D);
+        double* qr = malloc(sizeof(double) * D);
+        double* row = malloc(sizeof(double) * D);
+        double* acc = malloc(sizeof(double) * (size_t)n_chunks * D);
+        double* cm = malloc(sizeof(double) * (size_t)n_chunks);
+        double* cz = malloc(sizeof(double) * (size_t)n_chunks);
+        double* s = malloc(sizeof(double) * (size_t)chunk);
+        int st = KVQO_OK;
+        for (int i = 0; i < D; ++i) qd[i] = q[(size_t)bh * D + i];
+        kvqo_rotate_f64(qd, qr, D);
+        for (int c = 0; c < n_chunks; ++c) {
+            double* a = acc + (size_t)c * D;
+            for (int i = 0; i < D; ++i) a[i] = 0.0;
+            int64_t j0 = (int64_t)c * chunk, j1 = j0 + chunk < T ? j0 + chunk : T;
+            double m = -INFINITY, z = 0.0;
+            for (int64_t j = j0; j < j1; ++j) {
+                int64_t slot = kvqo_slot(page_table, max_pages, b, j, page_size);
+                if (slot < 0 || slot >= (int64_t)num_pages * page_size) { st = KVQO_ERANGE; j1 = j; break; }
+                kvqo_q4_decode_row(k_pool + kvqo_row_offset(slot, g, n_kv_heads, page_size, rb), D, row);
+                double dot = 0.0;
+                for (int i = 0; i < D; ++i) dot += qr[i] * row[i];
+                s[j - j0] = sm_scale * dot;
+                if (s[j - j0] > m) m = s[j - j0];
+            }
+            for (int64_t j = j0; j < j1; ++j) {
+                int64_t slot = kvqo_slot(page_table, max_pages, b, j, page_size);
+                double w = exp(s[j - j0] - m);
+                z += w;
+                kvqo_q4_decode_row(v_pool + kvqo_row_offset(slot, g, n_kv_heads, page_size, rb), D, row);
+                for (int i = 0; i < D; ++i) a[i] += w * row[i];
+            }
+            cm[c] = m;
+            cz[c] = z;
+        }
+        double M = -INFINITY;
+        for (int c = 0; c < n_chunks; ++c) if (cm[c] > M) M = cm[c];
+        double Z = 0.0;
+        double* orot = calloc((size_t)D, sizeof(double));
+        if (M > -INFINITY) {
+            for (int c = 0; c < n_chunks; ++c) {
+                if (cz[c] == 0.0) continue;
+                double f = exp(cm[c] - M);
+                Z += cz[c] * f;
+                for (int i = 0; i < D; ++i) orot[i] += acc[(size_t)c * D + i] * f;
+            }
+            for (int i = 0; i < D; ++i) orot[i] /= Z;
+            kvqo_rotate_f64(orot, out + (size_t)bh * D, D);
+        } else {
+            for (int i = 0; i < D; ++i) out[(size_t)bh * D + i] = 0.0;
+        }
+        if (lse) lse[bh] = M > -INFINITY ? M + log(Z) : -INFINITY;
+        if (part_m) for (int c = 0; c < n_chunks; ++c) part_m[(size_t)bh * n_chunks + c] = cm[c];
+        if (part_z) for (int c = 0; c < n_chunks; ++c) part_z[(size_t)bh * n_chunks + c] = cz[c];
+        if (part_acc) memcpy(part_acc + (size_t)bh * n_chunks * D, acc, sizeof(double) * (size_t)n_chunks * D);
+        if (st < err) err = st;
+        free(qd); free(qr); free(row); free(acc); free(cm); free(cz); free(s); free(orot);
+    }
+    return err;
+}
+
+/* ------------------------------------------------------------------ */
+/* fp8 e4m3 (OCP "fn": bias 7, max 448, 0x7F/0xFF are NaN)              */
+/* ------------------------------------------------------------------ */
+
+/* Value of an e4m3 code; the two NaN codes read as 0 ([CO] correctness
+ * commit: the CPU table reads 0 for NaN codes). */
+double kvqo_e4m3_decode(uint8_t c) {
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return 0.0;
+    double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return s ? -v : v;
+}
+
+/* Nearest e4m3 code of v ([CO] KV8 commit: round to nearest even,
+ * saturating at +-448, signed zero kept, NaN stored as 0).  The nearest
+ * value is found as the nearest multiple of the binade's spacing. */
+uint8_t kvqo_e4m3_encode(float v) {
+    if (isnan(v)) return 0x00;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal binade: spacing 2^-9; n == 8 is the smallest normal 0x08 */
+        double n = nearbyint(ldexp(a, 9));
+        return (uint8_t)(sign | (uint8_t)n);
+    }
+    int e2;
+    frexp(a, &e2);
+    int E = e2 - 1;                         /* a in [2^E, 2^(E+1)), E in [-6, 8] */
+    double n = nearbyint(ldexp(a, 3 - E));  /* in [8, 16] */
+    if (n == 16.0) { n = 8.0; E += 1; }
+    /* E + 7 <= 15 here; E + 7 == 15 with n - 8 == 7 would be 480, which the
+     * a >= 448 test excludes (values in [448, 464] already returned). */
+    return (uint8_t)(sign | (uint8_t)(((E + 7) << 3) | ((int)n - 8)));
+}
+
+/* One fp8 row part of n values -> n codes and an f32 scale ([CO] KV8 commit:
+ * per-row f32 scale amax/448; codes = e4m3(x * (448/amax))). */
+void kvqo_fp8_encode_part(const float* x, int n, uint8_t* codes, float* scale) {
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float a = fabsf(x[i]);
+        if (a > amax) amax = a;          /* NaN compares false: ignored */
+    }
+    float inv = 448.0f / amax;
+    if (amax == 0.0f || !isfinite(amax) || !isfinite(inv)) {
+        for (int i = 0; i < n; ++i) codes[i] = 0x00;
+        *scale = 0.0f;
+        return;
+    }
+    for (int i = 0; i < n; ++i) codes[i] = kvqo_e4m3_encode(x[i] * inv);
+    *scale = amax / 448.0f;
+}
+
+/* Store latent rows: x [n_tokens][D] with D = kv_lora + rope_dim.  Codes go
+ * to codes_pool[slot][D], scales to scale_pool[slot][2] = {latent, rope}. */
+int kvqo_fp8_store(uint8_t* codes_pool, float* scale_pool, int D, int rope_dim, int64_t n_slots,
+                   const float* x, const int64_t* slots, int n_tokens) {
+    if (rope_dim < 0 || rope_dim >= D) return KVQO_EARG;
+    for (int t = 0; t < n_tokens; ++t)
+        if (slots[t] >= n_slots) return KVQO_ERANGE;
+    const int L = D - rope_dim;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < n_tokens; ++t) {
+        if (slots[t] < 0) continue;
+        const float* r = x + (size_t)t * D;
+        uint8_t* c = codes_pool + (size_t)slots[t] * D;
+        float* sc = scale_pool + (size_t)slots[t] * 2;
+        kvqo_fp8_encode_part(r, L, c, &sc[0]);
+        if (rope_dim > 0) kvqo_fp8_encode_part(r + L, rope_dim, c + L, &sc[1]);
+        else sc[1] = 0.0f;
+    }
+    return KVQO_OK;
+}
+
+/* Absorbed latent attention over the fp8 cache ([CO] KV8 commit: the latent
+ * is both key and value; split-T commit: the context cl[K]).  For head h of
+ * sequence b, T = seq_lens[b], latent width L = D - rope_dim:
+ *   s_j = sm_scale * (scL_j <qL_h, dec(Lc_j)> + scR_j <qR_h, dec(Rc_j)>)
+ *   p = softmax(s), cl_h = sum_j p_j scL_j dec(Lc_j)
+ * q: [B][n_heads][D] fp32; out: [B][n_heads][L]; lse: [B][n_heads]. */
+int kvqo_mla_attention(const uint8_t* codes_pool, const float* scale_pool, int D, int rope_dim, int page_size,
+                       int num_pages, const float* q, int n_heads, const int32_t* page_table, int max_pages,
+                       const int32_t* seq_lens, int B, double sm_scale, double* out, double* lse) {
+    const int L = D - rope_dim;
+    for (int b = 0; b < B; ++b)
+        if (seq_lens[b] < 0 || (int64_t)seq_lens[b] > (int64_t)max_pages * page_size) return KVQO_ERANGE;
+    int err = KVQO_OK;
+#pragma omp parallel for schedule(dynamic, 1) reduction(min : err)
+    for (int bh = 0; bh < B * n_heads; ++bh) {
+        const int b = bh / n_heads;
+        const int64_t T = seq_lens[b];
+        const float* qh = q + (size_t)bh * D;
+        double* o = out + (size_t)bh * L;
+        double* s = malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+        int st = KVQO_OK;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < T; ++j) {
+            int64_t slot = kvqo_slot(page_table, max_pages, b, j, page_size);
+            if (slot < 0 || slot >= (int64_t)num_pages * page_size) { st = KVQO_ERANGE; break; }
+            const uint8_t* c = codes_pool + (size_t)slot * D;
+            double dl = 0.0, dr = 0.0;
+            for (int i = 0; i < L; ++i) dl += (double)qh[i] * kvqo_e4m3_decode(c[i]);
+            for (int i = L; i < D; ++i) dr += (double)qh[i] * kvqo_e4m3_decode(c[i]);
+            s[j] = sm_scale * ((double)scale_pool[2 * slot] * dl + (double)scale_pool[2 * slot + 1] * dr);
+            if (s[j] > m) m = s[j];
+        }
+        for (int i = 0; i < L; ++i) o[i] = 0.0;
+        double z = 0.0;
+        if (st == KVQO_OK) {
+            for (int64_t j = 0; j < T; ++j) {
+                int64_t slot = kvqo_slot(page_table, max_pages, b, j, page_size);
+                const uint8_t* c = codes_pool + (size_t)slot * D;
+                double w = exp(s[j] - m);
+                z += w;
+                double ws = w * (double)scale_pool[2 * slot];
+                for (int i = 0; i < L; ++i) o[i] += ws * kvqo_e4m3_decode(c[i]);
+            }
+        }
+        if (T > 0) for (int i = 0; i < L; ++i) o[i] /= z;
+        if (lse) lse[bh] = T > 0 ? m + log(z) : -INFINITY;
+        if (st < err) err = st;
+        free(s);
+    }
+    return err;
+}
+
+/* The latent attention split into chunks of `chunk` positions with partials
+ * (acc, m, z) and the in-order log-sum-exp merge ([CO] split-T commit). */
+int kvqo_mla_attention_chunked(const uint8_t* codes_pool, const float* scale_pool, int D, int rope_dim,
+                               int page_size, int num_pages, const float* q, int n_heads,
+                               const int32_t* page_table, int max_pages, const int32_t* seq_lens, int B,
+                               double sm_scale, int chunk, int n_chunks, double* part_acc, double* part_m,
+                               double* part_z, double* out, double* lse) {
+    const int L = D - rope_dim;
+    if (chunk <= 0) return KVQO_EARG;
+    for (int b = 0; b < B; ++b) {
+        if (seq_lens[b] < 0 || (int64_t)seq_lens[b] > (int64_t)max_pages * page_size) return KVQO_ERANGE;
+        if (((int64_t)seq_lens[b] + chunk - 1) / chunk > n_chunks) return KVQO_EARG;
+    }
+    int err = KVQO_OK;
+#pragma omp parallel for schedule(dynamic, 1) reduction(min : err)
+    for (int bh = 0; bh < B * n_heads; ++bh) {
+        const int b = bh / n_heads;
+        const int64_t T = seq_lens[b];
+        const float* qh = q + (size_t)bh * D;
+        double* acc = calloc((size_t)n_chunks * L, sizeof(double));
+        double* cm = malloc(sizeof(double) * (size_t)n_chunks);
+        double* cz = malloc(sizeof(double) * (size_t)n_chunks);
+        double* s = malloc(sizeof(double) * (size_t)chunk);
+        int st = KVQO_OK;
+        for (int c = 0; c < n_chunks; ++c) {
+            int64_t j0 = (int64_t)c * chunk, j1 = j0 + chunk < T ? j0 + chunk : T;
+            double m = -INFINITY, z = 0.0;
+            for (int64_t j = j0; j < j1; ++j) {
+                int64_t slot = kvqo_slot(page_table, max_pages, b, j, page_size);
+                if (slot < 0 || slot >= (int64_t)num_pages * page_size) { st = KVQO_ERANGE; j1 = j; break; }
+                const uint8_t* cc = codes_pool + (size_t)slot * D;
+                double dl = 0.0, dr = 0.0;
+                for (int i = 0; i < L; ++i) dl += (double)qh[i] * kvqo_e4m3_decode(cc[i]);
+                for (int i = L; i < D; ++i) dr += (double)qh[i] * kvqo_e4m3_decode(cc[i]);
+                s[j - j0] = sm_scale * ((double)scale_pool[2 * slot] * dl + (double)scale_pool[2 * slot + 1] * dr);
+                if (s[j - j0] > m) m = s[j - j0];
+            }
+            double* a = acc + (size_t)c * L;
+            for (int64_t j = j0; j < j1; ++j) {
+                int64_t slot = kvqo_slot(page_table, max_pages, b, j, page_size);
+                const uint8_t* cc = codes_pool + (size_t)slot * D;
+                double w = exp(s[j - j0] - m);
+                z += w;
+                double ws = w * (double)scale_pool[2 * slot];
+                for (int i = 0; i < L; ++i) a[i] += ws * kvqo_e4m3_decode(cc[i]);
+            }
+            cm[c] = m;
+            cz[c] = z;
+        }
+        double M = -INFINITY, Z = 0.0;
+        for (int c = 0; c < n_chunks; ++c) if (cm[c] > M) M = cm[c];
+        double* o = out + (size_t)bh * L;
+        for (int i = 0; i < L; ++i) o[i] = 0.0;
+        if (M > -INFINITY) {
+            for (int c = 0; c < n_chunks; ++c) {
+                if (cz[c] == 0.0) continue;
+                double f = exp(cm[c] - M);
+                Z += cz[c] * f;
+                for (int i = 0; i < L; ++i) o[i] += acc[(size_t)c * L + i] * f;
+            }
+            for (int i = 0; i < L; ++i) o[i] /= Z;
+        }
+        if (lse) lse[bh] = M > -INFINITY ? M + log(Z) : -INFINITY;
+        if (part_m) for (int c = 0; c < n_chunks; ++c) part_m[(size_t)bh * n_chunks + c] = cm[c];
+        if (part_z) for (int c = 0; c < n_chunks; ++c) part_z[(size_t)bh * n_chunks + c] = cz[c];
+        if (part_acc) memcpy(part_acc + (size_t)bh * n_chunks * L, acc, sizeof(double) * (size_t)n_chunks * L);
+        if (st < err) err = st;
+        free(acc); free(cm); free(cz); free(s);
+    }
+    return err;
+}
+
+/* Batch helpers for the tests: element-wise codecs over arrays. */
+void kvqo_f32_to_f16_array(const float* x, uint16_t* y, int64_t n) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) y[i] = kvqo_f32_to_f16(x[i]);
+}
+
+void kvqo_e4m3_encode_array(const float* x, uint8_t* y, int64_t n) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) y[i] = kvqo_e4m3_encode(x[i]);
+}
+
+/* Encode/decode many rows at once: x [n_rows][D] -> rows [n_rows][row_bytes]. */
+int kvqo_q4_encode_rows(const float* x, int64_t n_rows, int D, uint8_t* rows) {
+    const size_t rb = kvqo_q4_row_bytes(D);
+    int err = KVQO_OK;
+#pragma omp parallel for schedule(static) reduction(min : err)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int e = kvqo_q4_encode_row(x + (size_t)r * D, D, rows + (size_t)r * rb);
+        if (e < err) err = e;
+    }
+    return err;
+}
+
+void kvqo_q4_decode_rows(const uint8_t* rows, int64_t n_rows, int D, double* out) {
+    const size_t rb = kvqo_q4_row_bytes(D);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n_rows; ++r) kvqo_q4_decode_row(rows + (size_t)r * rb, D, out + (size_t)r * D);
+}
+
+void kvqo_hadamard32_f32_rows(float* x, int64_t n_groups) {
+    for (int64_t g = 0; g < n_groups; ++g) kvqo_hadamard32_f32(x + 32 * g);
+}
