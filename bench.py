@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark for the 4-bit Hadamard-32 KV cache on one MI355X.
+
+One step = one pass of the hot path over every layer of the workload:
+kvq_store of the step's new token (K and V), kvq_rotate_q, kvq_decode_attn
+(split-K over the paged 4-bit cache), kvq_merge (log-sum-exp merge and the
+inverse rotation).  Inputs are synthetic and seeded (module `workloads`) and
+resident in HBM before timing starts; 16 layer caches are cycled so the
+working set (4.8 GB at 262K) is far above the 256 MB Infinity Cache.
+
+Prints one JSON line: whole-step KV-read throughput (algorithmic bytes:
+T x KV heads x (K, V) x 144 B per layer) and microseconds per layer; a
+roofline object for the decode kernel, whose launches are bracketed by HIP
+events on the stream they run on; and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+METRIC = "KV-read GB/s (% of HBM peak) and µs/layer, 4-bit split-K decode at 32K/262K"
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Q4Bench:
+    """Every layer's cache, query and buffers for one 4-bit workload, plus the
+    raw C-ABI argument tuples of one step (validated once by building them
+    through the binding's checks)."""
+
+    def __init__(self, w, device="cuda"):
+        import numpy as np
+        import torch
+
+        import fp8_quantized_kv_amd as kvq
+        import workloads as wl
+        self.w, self.kvq = w, kvq
+        T = w.seq_len
+        self.T = T
+        lay = wl.page_layout(w, [T])
+        self.page_table = lay.page_table.to(device)
+        self.seq_lens = torch.tensor([T], dtype=torch.int32, device=device)
+        self.caches, self.q, self.k_new, self.v_new = [], [], [], []
+        chunk = 32768
+        slots_all = wl.slots_for(lay.page_table[0], np.arange(T), w.page_size).to(device)
+        for layer in range(w.n_layers):
+            c = kvq.Q4Cache(lay.num_pages, w.n_kv_heads, w.head_dim, w.page_size, device)
+            q = wl.q4_query(w, layer, device)
+            for t0 in range(0, T, chunk):
+                n = min(chunk, T - t0)
+                k, v = wl.q4_kv_tokens(w, layer, t0, n, device)
+                wl.plant(w, k, q, t0)
+                kvq.kvq_store(c, k, v, slots_all[t0:t0 + n])
+                if t0 + n == T:
+                    self.k_new.append(k[-1:].clone())
+                    self.v_new.append(v[-1:].clone())
+            self.caches.append(c)
+            self.q.append(q)
+        self.slot_new = slots_all[T - 1:T].clone()
+        acc_shape, mz_shape = kvq.partial_shapes(self.caches[0], 1, w.n_q_heads, T, w.split_keys)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.q_rot = torch.empty((1, w.n_q_heads, w.head_dim), **f32)
+        self.pa, self.pm, self.pz = torch.empty(acc_shape, **f32), torch.empty(mz_shape, **f32), torch.empty(mz_shape, **f32)
+        self.out = torch.empty((w.n_layers, 1, w.n_q_heads, w.head_dim), **f32)
+        self.lse = torch.empty((w.n_layers, 1, w.n_q_heads), **f32)
+        torch.cuda.synchronize()
+        # One checked pass through the binding validates every argument once.
+        for layer in range(w.n_layers):
+            self._checked_layer(layer)
+        torch.cuda.synchronize()
+        self._build_raw_args()
+
+    def _checked_layer(self, layer):
+        kvq, w = self.kvq, self.w
+        c = self.caches[layer]
+        kvq.kvq_store(c, self.k_new[layer], self.v_new[layer], self.slot_new)
+        kvq.kvq_rotate_q(self.q[layer], out=self.q_rot)
+        kvq.kvq_decode_attn(c, self.q_rot, self.page_table, self.seq_lens, self.T, w.sm_scale, w.split_keys,
+                            self.pa, self.pm, self.pz)
+        kvq.kvq_merge(c, self.pa, self.pm, self.pz, self.seq_lens, self.T, w.split_keys, out=self.out[layer],
+                      lse=self.lse[layer])
+
+    def _build_raw_args(self):
+        import torch
+        P = ctypes.c_void_p
+        w = self.w
+        stream = P(torch.cuda.current_stream().cuda_stream)
+        self.stream = stream
+        self.raw = []
+        for layer, c in enumerate(self.caches):
+            d = ctypes.byref(c.desc)
+            self.raw.append((
+                (d, P(self.k_new[layer].data_ptr()), P(self.v_new[layer].data_ptr()),
+                 self.kvq._DTYPES[self.k_new[layer].dtype], P(self.slot_new.data_ptr()), 1, stream),
+                (P(self.q[layer].data_ptr()), 0, P(self.q_rot.data_ptr()), w.n_q_heads, w.head_dim, stream),
+                (d, P(self.q_rot.data_ptr()), w.n_q_heads, P(self.page_table.data_ptr()), self.page_table.shape[1],
+                 P(self.seq_lens.data_ptr()), 1, self.T, ctypes.c_float(w.sm_scale), w.split_keys,
+                 P(self.pa.data_ptr()), P(self.pm.data_ptr()), P(self.pz.data_ptr()), stream),
+                (d, P(self.pa.data_ptr()), P(self.pm.data_ptr()), P(self.pz.data_ptr()), P(self.seq_lens.data_ptr()),
+                 1, w.n_q_heads, self.T, w.split_keys, 1, P(self.out[layer].data_ptr()),
+                 P(self.lse[layer].data_ptr()), stream),
+            ))
+
+    def step(self, events=None):
+        """Enqueue one step; if events is a list of (start, end) pairs, bracket each decode launch."""
+        L = self.kvq.lib
+        for layer, (st, rq, dec, mg) in enumerate(self.raw):
+            rc = L.kvq_store(*st) | L.kvq_rotate_q(*rq)
+            if events is not None:
+                events[layer][0].record()
+            rc |= L.kvq_decode_attn(*dec)
+            if events is not None:
+                events[layer][1].record()
+            rc |= L.kvq_merge(*mg)
+            if rc:
+                raise RuntimeError(f"launch failed in layer {layer}")
+
+    @property
+    def kv_bytes_per_layer(self):
+        w = self.w
+        return self.T * w.n_kv_heads * 2 * w.row_bytes
+
+
+def time_steps(b, steps, warmup, per_kernel_events=True):
+    import torch
+    for _ in range(warmup):
+        b.step()
+    torch.cuda.synchronize()
+    ev = None
+    if per_kernel_events:
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(b.w.n_layers)] for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for s in range(steps):
+        b.step(ev[s] if ev else None)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    dec_ms = None
+    if ev:
+        d = [e0.elapsed_time(e1) for row in ev for (e0, e1) in row]
+        dec_ms = sum(d) / len(d)
+    return total_ms / steps, dec_ms, wall
+
+
+def cpu_baseline(w, sample_tokens, repeats=3):
+    """The oracle (fp64, OpenMP over heads) on one layer of the workload,
+    restricted to its first `sample_tokens` positions; median of `repeats`."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+    T = min(sample_tokens, w.seq_len)
+    lay = wl.page_layout(wl.shrink(w, seq_len=T), [T])
+    shape = oracle.q4_pool_shape(lay.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+    kp, vp = np.zeros(shape, np.uint8), np.zeros(shape, np.uint8)
+    q = wl.q4_query(w, 0)
+    for t0 in range(0, T, 32768):
+        n = min(32768, T - t0)
+        k, v = wl.q4_kv_tokens(w, 0, t0, n)
+        wl.plant(w, k, q, t0)
+        oracle.q4_store(kp, vp, k.float().numpy(), v.float().numpy(), np.arange(t0, t0 + n), w.page_size)
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oracle.q4_attention(kp, vp, q.numpy(), lay.page_table.numpy(), np.array([T], np.int32), w.sm_scale)
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
+    kv_bytes = T * w.n_kv_heads * 2 * w.row_bytes
+    threads = min(oracle.num_threads(), w.batch * w.n_q_heads)
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"layer 0 of {w.name}, first {T} positions, all {w.n_q_heads} query heads "
+                      f"(decode attention + merge in fp64; median {dt:.2f} s of {repeats})",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gqa_q4_262k")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=262144)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the decode path is "
+              "built and measured for a single GPU's share of the work", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as wl
+    w = wl.WORKLOADS[args.workload]
+    assert isinstance(w, wl.Q4Workload), "the headline benchmark is the 4-bit decode"
+    torch.cuda.set_device(0)
+    _log(f"bench: setting up {w.name} ({w.n_layers} layers, T={w.seq_len})")
+    b = Q4Bench(w)
+    _log(f"bench: timing {args.steps} steps after {args.warmup} warm-up steps")
+    ms_step, dec_ms, wall = time_steps(b, args.steps, args.warmup)
+    kvb = b.kv_bytes_per_layer
+    value = kvb * w.n_layers / (ms_step * 1e-3) / 1e9
+    us_layer = ms_step * 1e3 / w.n_layers
+    achieved = kvb / (dec_ms * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.n_layers, "batch": w.batch, "seq_len": w.seq_len,
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "split_keys": w.split_keys, "kv_bytes_per_layer": kvb},
+        "us_per_layer": round(us_layer, 3),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"kernel": "kvq_decode_attn (4-bit split-K)", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "avg_launch_us": round(dec_ms * 1e3, 3), "traffic": None},
+        "wall_s": round(wall, 3),
+    }
+    del b
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        _log(f"bench: oracle CPU baseline on {args.cpu_sample_tokens} positions")
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,252 @@
+"""fp8_quantized_kv_amd -- sub-byte KV cache and split-K decode attention on MI355X.
+
+A thin Python binding over libkvq.so (C ABI in include/kvq.h).  The
+functions carry the C names -- kvq_store, kvq_rotate_q, kvq_decode_attn,
+kvq_merge -- and only marshal arguments: they check device, dtype, shape
+and contiguity of torch tensors, then pass raw pointers and torch's current
+HIP stream.  Every step of the computation runs in the library's HIP
+kernels; there is no CPU path.  Importing this package without a built
+libkvq.so raises ImportError.
+
+Method: TensorFold issue "qwen27 CUDA: an opt-in 4-bit attention cache"
+("What it is"), FreeToken pull request "feat(kvcache): add reliable
+quantized KV cache", colibri pull request "KV cache quantization: fp8 (KV8)
++ 4-bit TurboQuant (KV_TQ)" (KV8 and split-T commits).
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+KVQ_OK = 0
+KVQ_ERR_INVALID_ARG = -1
+KVQ_ERR_UNSUPPORTED = -2
+KVQ_ERR_LAUNCH = -3
+
+FMT_Q4_H32 = 1
+FMT_FP8_E4M3_ROW = 2
+
+DT_F32, DT_BF16, DT_F16 = 0, 1, 2
+_DTYPES = {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float16: DT_F16}
+
+EXPORTED = ("kvq_status_string", "kvq_row_bytes", "kvq_pool_bytes", "kvq_num_splits", "kvq_store",
+            "kvq_rotate_q", "kvq_decode_attn", "kvq_merge")
+
+
+class KvqCacheDesc(ctypes.Structure):
+    """Mirror of struct kvq_cache."""
+    _fields_ = [("format", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("rope_dim", ctypes.c_int32), ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p), ("scale_pool", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                          "python fp8_quantized_kv_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    C = ctypes.POINTER(KvqCacheDesc)
+    sig = {
+        "kvq_status_string": ([I32], ctypes.c_char_p),
+        "kvq_row_bytes": ([I32, I32, I32], ctypes.c_size_t),
+        "kvq_pool_bytes": ([C], ctypes.c_size_t),
+        "kvq_num_splits": ([I32, I32], I32),
+        "kvq_store": ([C, P, P, I32, P, I32, P], I32),
+        "kvq_rotate_q": ([P, I32, P, I32, I32, P], I32),
+        "kvq_decode_attn": ([C, P, I32, P, I32, P, I32, I32, F, I32, P, P, P, P], I32),
+        "kvq_merge": ([C, P, P, P, P, I32, I32, I32, I32, I32, P, P, P], I32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    return L
+
+
+lib = _load()
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {lib.kvq_status_string(status).decode()} ({status})")
+
+
+def _check(status, what):
+    if status != KVQ_OK:
+        raise KvqError(status, what)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def kvq_row_bytes(fmt, head_dim, rope_dim=0):
+    return int(lib.kvq_row_bytes(fmt, head_dim, rope_dim))
+
+
+def kvq_num_splits(max_seq_len, split_keys):
+    return int(lib.kvq_num_splits(max_seq_len, split_keys))
+
+
+class Q4Cache:
+    """Paged 4-bit Hadamard-32 K and V pools: [num_pages][H_kv][page_size][row_bytes] uint8."""
+
+    fmt = FMT_Q4_H32
+
+    def __init__(self, num_pages, num_kv_heads, head_dim, page_size=16, device="cuda"):
+        rb = kvq_row_bytes(FMT_Q4_H32, head_dim)
+        if rb == 0:
+            raise ValueError(f"head_dim {head_dim} is not a multiple of 32")
+        shape = (num_pages, num_kv_heads, page_size, rb)
+        self.k_pool = torch.zeros(shape, dtype=torch.uint8, device=device)
+        self.v_pool = torch.zeros(shape, dtype=torch.uint8, device=device)
+        self.num_kv_heads, self.head_dim, self.page_size, self.num_pages = num_kv_heads, head_dim, page_size, num_pages
+        self.rope_dim = 0
+        self.dv = head_dim
+        self.desc = KvqCacheDesc(FMT_Q4_H32, num_kv_heads, head_dim, 0, page_size, num_pages,
+                                 self.k_pool.data_ptr(), self.v_pool.data_ptr(), None)
+
+    @property
+    def device(self):
+        return self.k_pool.device
+
+    def pool_bytes(self):
+        return int(lib.kvq_pool_bytes(ctypes.byref(self.desc)))
+
+
+class Fp8Cache:
+    """Paged fp8 e4m3 latent rows: codes [num_pages*page_size][head_dim] uint8, scales [..][2] f32."""
+
+    fmt = FMT_FP8_E4M3_ROW
+
+    def __init__(self, num_pages, head_dim=576, rope_dim=64, page_size=16, device="cuda"):
+        slots = num_pages * page_size
+        self.codes = torch.zeros((slots, head_dim), dtype=torch.uint8, device=device)
+        self.scales = torch.zeros((slots, 2), dtype=torch.float32, device=device)
+        self.num_kv_heads, self.head_dim, self.rope_dim = 1, head_dim, rope_dim
+        self.page_size, self.num_pages = page_size, num_pages
+        self.dv = head_dim - rope_dim
+        self.desc = KvqCacheDesc(FMT_FP8_E4M3_ROW, 1, head_dim, rope_dim, page_size, num_pages,
+                                 self.codes.data_ptr(), None, self.scales.data_ptr())
+
+    @property
+    def device(self):
+        return self.codes.device
+
+    def pool_bytes(self):
+        return int(lib.kvq_pool_bytes(ctypes.byref(self.desc)))
+
+
+def kvq_store(cache, k, v, slot_mapping):
+    """Quantize new rows into the cache.
+
+    Q4: k, v [n_tokens][H_kv][head_dim] (f32/bf16/f16).  FP8: k [n_tokens][head_dim], v None.
+    slot_mapping: int64 [n_tokens] (negative slots are skipped)."""
+    n = int(slot_mapping.shape[0])
+    dt = _DTYPES.get(k.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {k.dtype}")
+    if cache.fmt == FMT_Q4_H32:
+        shape = (n, cache.num_kv_heads, cache.head_dim)
+        kp = _dev(k, "k", shape=shape)
+        vp = _dev(v, "v", dtype=k.dtype, shape=shape)
+    else:
+        if v is not None:
+            raise ValueError("the fp8 latent cache takes no v")
+        kp = _dev(k, "k", shape=(n, cache.head_dim))
+        vp = None
+    sp = _dev(slot_mapping, "slot_mapping", dtype=torch.int64)
+    _check(lib.kvq_store(ctypes.byref(cache.desc), kp, vp, dt, sp, n, _stream(k)), "kvq_store")
+
+
+def kvq_rotate_q(q, out=None):
+    """q_rot = H32 q for every 32-group of the last axis; returns an f32 tensor of q's shape."""
+    dt = _DTYPES.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    D = int(q.shape[-1])
+    rows = q.numel() // D if D else 0
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    qp = _dev(q, "q")
+    op = _dev(out, "out", dtype=torch.float32, shape=q.shape)
+    _check(lib.kvq_rotate_q(qp, dt, op, rows, D, _stream(q)), "kvq_rotate_q")
+    return out
+
+
+def partial_shapes(cache, batch, n_q_heads, max_seq_len, split_keys):
+    S = kvq_num_splits(max_seq_len, split_keys)
+    return (batch, n_q_heads, S, cache.dv), (batch, n_q_heads, S)
+
+
+def kvq_decode_attn(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_keys, part_acc=None, part_m=None,
+                    part_z=None):
+    """Split-K decode attention; returns the partials (acc, m, z).
+
+    q: f32 [B][H_q][head_dim] (for Q4 already rotated with kvq_rotate_q);
+    page_table: int32 [B][max_pages]; seq_lens: int32 [B]."""
+    B, Hq, D = q.shape
+    acc_shape, mz_shape = partial_shapes(cache, B, Hq, max_seq_len, split_keys)
+    if part_acc is None:
+        part_acc = torch.empty(acc_shape, dtype=torch.float32, device=q.device)
+        part_m = torch.empty(mz_shape, dtype=torch.float32, device=q.device)
+        part_z = torch.empty(mz_shape, dtype=torch.float32, device=q.device)
+    qp = _dev(q, "q", dtype=torch.float32, shape=(B, Hq, cache.head_dim))
+    ptp = _dev(page_table, "page_table", dtype=torch.int32)
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [batch][max_pages]")
+    slp = _dev(seq_lens, "seq_lens", dtype=torch.int32, shape=(B,))
+    pa = _dev(part_acc, "part_acc", dtype=torch.float32, shape=acc_shape)
+    pm = _dev(part_m, "part_m", dtype=torch.float32, shape=mz_shape)
+    pz = _dev(part_z, "part_z", dtype=torch.float32, shape=mz_shape)
+    _check(lib.kvq_decode_attn(ctypes.byref(cache.desc), qp, Hq, ptp, int(page_table.shape[1]), slp, B,
+                               int(max_seq_len), float(sm_scale), int(split_keys), pa, pm, pz, _stream(q)),
+           "kvq_decode_attn")
+    return part_acc, part_m, part_z
+
+
+def kvq_merge(cache, part_acc, part_m, part_z, seq_lens, max_seq_len, split_keys, out=None, lse=None,
+              want_lse=True):
+    """Log-sum-exp merge of the partials, then (Q4) the inverse rotation.  Returns (out, lse)."""
+    B, Hq, S, Dv = part_acc.shape
+    if out is None:
+        out = torch.empty((B, Hq, Dv), dtype=torch.float32, device=part_acc.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=part_acc.device)
+    acc_shape, mz_shape = partial_shapes(cache, B, Hq, max_seq_len, split_keys)
+    pa = _dev(part_acc, "part_acc", dtype=torch.float32, shape=acc_shape)
+    pm = _dev(part_m, "part_m", dtype=torch.float32, shape=mz_shape)
+    pz = _dev(part_z, "part_z", dtype=torch.float32, shape=mz_shape)
+    slp = _dev(seq_lens, "seq_lens", dtype=torch.int32, shape=(B,))
+    op = _dev(out, "out", dtype=torch.float32, shape=(B, Hq, Dv))
+    lp = _dev(lse, "lse", dtype=torch.float32, shape=(B, Hq)) if lse is not None else None
+    _check(lib.kvq_merge(ctypes.byref(cache.desc), pa, pm, pz, slp, B, Hq, int(max_seq_len), int(split_keys),
+                         1 if cache.fmt == FMT_Q4_H32 else 0, op, lp, _stream(part_acc)), "kvq_merge")
+    return out, lse
+
+
+def decode_step(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_keys, bufs=None):
+    """rotate (Q4) -> decode -> merge on preallocated buffers; returns (out, lse)."""
+    if cache.fmt == FMT_Q4_H32:
+        q = kvq_rotate_q(q, out=None if bufs is None else bufs.get("q_rot"))
+    pa, pm, pz = kvq_decode_attn(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_keys,
+                                 *(() if bufs is None else (bufs["part_acc"], bufs["part_m"], bufs["part_z"])))
+    return kvq_merge(cache, pa, pm, pz, seq_lens, max_seq_len, split_keys,
+                     out=None if bufs is None else bufs.get("out"), lse=None if bufs is None else bufs.get("lse"))

@@ -1,0 +1,105 @@
+// internal.h -- declarations shared by the kernels and the C-ABI layer of
+// libkvq (not installed; the public interface is include/kvq.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace kvq {
+
+// Element types a store or rotation may read.
+enum class InType : int { F32 = 0, BF16 = 1, F16 = 2 };
+
+// Rows of the 4-bit format: D/2 code bytes then D/32 fp16 scales.
+__host__ __device__ constexpr int q4_row_bytes(int D) { return D / 2 + 2 * (D / 32); }
+
+// ln(2) and log2(e) in fp32.
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.442695040888963407f;
+
+// fp32(1/sqrt(32)) = 0x3E3504F3, the Hadamard-32 normalisation.
+__device__ __forceinline__ float inv_sqrt32() { return __uint_as_float(0x3E3504F3u); }
+
+template <InType T>
+__device__ __forceinline__ float load_elem(const void* p, int64_t i);
+
+template <>
+__device__ __forceinline__ float load_elem<InType::F32>(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+}
+template <>
+__device__ __forceinline__ float load_elem<InType::BF16>(const void* p, int64_t i) {
+    return __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
+}
+template <>
+__device__ __forceinline__ float load_elem<InType::F16>(const void* p, int64_t i) {
+    return __half2float(__ushort_as_half(static_cast<const uint16_t*>(p)[i]));
+}
+
+// ------------------------------------------------------------------ launchers
+// Each returns the hipError_t of its launch; shapes are validated by the caller.
+
+struct Q4Pool {
+    uint8_t* k;
+    uint8_t* v;
+    int n_kv_heads;
+    int head_dim;
+    int page_size;
+    int num_pages;
+};
+
+struct Fp8Pool {
+    uint8_t* codes;   // [slots][head_dim]
+    float* scales;    // [slots][2]
+    int head_dim;
+    int rope_dim;
+    int page_size;
+    int num_pages;
+};
+
+hipError_t launch_store_q4(const Q4Pool& pool, const void* k, const void* v, InType dt, const int64_t* slots,
+                           int n_tokens, hipStream_t s);
+hipError_t launch_store_fp8(const Fp8Pool& pool, const void* x, InType dt, const int64_t* slots, int n_tokens,
+                            hipStream_t s);
+hipError_t launch_rotate_q(const void* q, InType dt, float* q_rot, int n_rows, int head_dim, hipStream_t s);
+
+struct DecodeArgs {
+    const float* q;
+    int n_q_heads;
+    const int32_t* page_table;
+    int max_pages;
+    const int32_t* seq_lens;
+    int batch;
+    int max_seq_len;
+    int n_splits;
+    float sm_scale;
+    int split_keys;
+    float* part_acc;
+    float* part_m;
+    float* part_z;
+};
+
+// Plain fp32 vector-math kernels (any supported head_dim).
+hipError_t launch_decode_q4_simple(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_fp8_simple(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s);
+
+struct MergeArgs {
+    const float* part_acc;
+    const float* part_m;
+    const float* part_z;
+    const int32_t* seq_lens;
+    int batch;
+    int n_q_heads;
+    int max_seq_len;
+    int n_splits;
+    int split_keys;
+    int dv;
+    bool rotate;
+    float* out;
+    float* lse;
+};
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
+}  // namespace kvq

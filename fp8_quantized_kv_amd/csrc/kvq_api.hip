@@ -1,0 +1,170 @@
+// kvq_api.hip -- the C ABI (include/kvq.h): argument validation on the host,
+// then kernel launches on the caller's stream.  Nothing here allocates,
+// frees or synchronizes.
+#include "kvq.h"
+
+#include "internal.h"
+
+namespace {
+
+using kvq::InType;
+
+constexpr uintptr_t kAlign = 16;
+
+bool aligned(const void* p, uintptr_t a = kAlign) { return p && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool q4_dim_ok(int32_t D) { return D == 64 || D == 128 || D == 256 || D == 512; }
+
+// Validates a descriptor; returns KVQ_OK or the status to report.
+kvq_status check_cache(const kvq_cache* c) {
+    if (!c) return KVQ_ERR_INVALID_ARG;
+    if (c->page_size < 1 || c->num_pages < 1 || c->num_kv_heads < 1 || c->head_dim < 1) return KVQ_ERR_INVALID_ARG;
+    if (int64_t(c->num_pages) * c->page_size > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
+    if (c->format == KVQ_FMT_Q4_H32) {
+        if (c->head_dim % 32 || c->rope_dim != 0) return KVQ_ERR_INVALID_ARG;
+        if (!q4_dim_ok(c->head_dim)) return KVQ_ERR_UNSUPPORTED;
+        if (!aligned(c->k_pool) || !aligned(c->v_pool) || c->scale_pool) return KVQ_ERR_INVALID_ARG;
+        return KVQ_OK;
+    }
+    if (c->format == KVQ_FMT_FP8_E4M3_ROW) {
+        if (c->num_kv_heads != 1 || c->rope_dim <= 0 || c->rope_dim >= c->head_dim) return KVQ_ERR_INVALID_ARG;
+        if (c->head_dim % 16 || (c->head_dim - c->rope_dim) % 64) return KVQ_ERR_INVALID_ARG;
+        if (c->head_dim - c->rope_dim != 512 || c->rope_dim != 64) return KVQ_ERR_UNSUPPORTED;
+        if (!aligned(c->k_pool) || c->v_pool || !aligned(c->scale_pool)) return KVQ_ERR_INVALID_ARG;
+        return KVQ_OK;
+    }
+    return KVQ_ERR_INVALID_ARG;
+}
+
+bool dtype_ok(int32_t dt) { return dt == KVQ_DT_F32 || dt == KVQ_DT_BF16 || dt == KVQ_DT_F16; }
+
+kvq::Q4Pool q4_pool(const kvq_cache* c) {
+    return kvq::Q4Pool{static_cast<uint8_t*>(c->k_pool), static_cast<uint8_t*>(c->v_pool), c->num_kv_heads,
+                       c->head_dim, c->page_size, c->num_pages};
+}
+
+kvq::Fp8Pool fp8_pool(const kvq_cache* c) {
+    return kvq::Fp8Pool{static_cast<uint8_t*>(c->k_pool), static_cast<float*>(c->scale_pool), c->head_dim,
+                        c->rope_dim, c->page_size, c->num_pages};
+}
+
+kvq_status launched(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH; }
+
+// Shared checks of kvq_decode_attn / kvq_merge arguments.
+kvq_status check_seq_args(const kvq_cache* c, int32_t n_q_heads, const int32_t* seq_lens, int32_t batch,
+                          int32_t max_seq_len, int32_t split_keys) {
+    if (n_q_heads < 1 || batch < 0 || max_seq_len < 0 || split_keys < 512 || split_keys % 512) return KVQ_ERR_INVALID_ARG;
+    if (n_q_heads % c->num_kv_heads) return KVQ_ERR_INVALID_ARG;
+    if (batch > 0 && !aligned(seq_lens, 4)) return KVQ_ERR_INVALID_ARG;
+    if (batch > 65535) return KVQ_ERR_UNSUPPORTED;
+    if (c->format == KVQ_FMT_Q4_H32 && n_q_heads / c->num_kv_heads > 16) return KVQ_ERR_UNSUPPORTED;
+    if (kvq_num_splits(max_seq_len, split_keys) > 65535) return KVQ_ERR_UNSUPPORTED;
+    return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_string(kvq_status s) {
+    switch (s) {
+        case KVQ_OK: return "ok";
+        case KVQ_ERR_INVALID_ARG: return "invalid argument";
+        case KVQ_ERR_UNSUPPORTED: return "unsupported shape or format";
+        case KVQ_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+size_t kvq_row_bytes(int32_t format, int32_t head_dim, int32_t rope_dim) {
+    if (format == KVQ_FMT_Q4_H32) {
+        if (head_dim <= 0 || head_dim % 32 || rope_dim != 0) return 0;
+        return size_t(kvq::q4_row_bytes(head_dim));
+    }
+    if (format == KVQ_FMT_FP8_E4M3_ROW) {
+        if (head_dim <= 0 || rope_dim <= 0 || rope_dim >= head_dim) return 0;
+        return size_t(head_dim);
+    }
+    return 0;
+}
+
+size_t kvq_pool_bytes(const kvq_cache* c) {
+    if (!c || c->page_size < 1 || c->num_pages < 1 || c->num_kv_heads < 1) return 0;
+    const size_t rb = kvq_row_bytes(c->format, c->head_dim, c->rope_dim);
+    if (!rb) return 0;
+    const size_t slots = size_t(c->num_pages) * size_t(c->page_size);
+    if (c->format == KVQ_FMT_Q4_H32) return 2 * slots * size_t(c->num_kv_heads) * rb;
+    return slots * (rb + 2 * sizeof(float));
+}
+
+int32_t kvq_num_splits(int32_t max_seq_len, int32_t split_keys) {
+    if (max_seq_len < 0 || split_keys <= 0) return 0;
+    const int32_t n = int32_t((int64_t(max_seq_len) + split_keys - 1) / split_keys);
+    return n < 1 ? 1 : n;
+}
+
+kvq_status kvq_store(const kvq_cache* cache, const void* k, const void* v, int32_t dtype,
+                     const int64_t* slot_mapping, int32_t n_tokens, hipStream_t stream) {
+    kvq_status st = check_cache(cache);
+    if (st != KVQ_OK) return st;
+    if (!dtype_ok(dtype) || n_tokens < 0) return KVQ_ERR_INVALID_ARG;
+    if (n_tokens == 0) return KVQ_OK;
+    if (!aligned(slot_mapping, 8)) return KVQ_ERR_INVALID_ARG;
+    const InType dt = static_cast<InType>(dtype);
+    if (cache->format == KVQ_FMT_Q4_H32) {
+        if (!aligned(k) || !aligned(v)) return KVQ_ERR_INVALID_ARG;
+        return launched(kvq::launch_store_q4(q4_pool(cache), k, v, dt, slot_mapping, n_tokens, stream));
+    }
+    if (!aligned(k) || v) return KVQ_ERR_INVALID_ARG;
+    return launched(kvq::launch_store_fp8(fp8_pool(cache), k, dt, slot_mapping, n_tokens, stream));
+}
+
+kvq_status kvq_rotate_q(const void* q, int32_t dtype, float* q_rot, int32_t n_rows, int32_t head_dim,
+                        hipStream_t stream) {
+    if (!dtype_ok(dtype) || n_rows < 0 || head_dim <= 0 || head_dim % 32) return KVQ_ERR_INVALID_ARG;
+    if (n_rows == 0) return KVQ_OK;
+    if (!aligned(q) || !aligned(q_rot)) return KVQ_ERR_INVALID_ARG;
+    if (q == q_rot && dtype != KVQ_DT_F32) return KVQ_ERR_INVALID_ARG;
+    return launched(kvq::launch_rotate_q(q, static_cast<InType>(dtype), q_rot, n_rows, head_dim, stream));
+}
+
+kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
+                           int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                           float sm_scale, int32_t split_keys, float* part_acc, float* part_m, float* part_z,
+                           hipStream_t stream) {
+    kvq_status st = check_cache(cache);
+    if (st != KVQ_OK) return st;
+    st = check_seq_args(cache, n_q_heads, seq_lens, batch, max_seq_len, split_keys);
+    if (st != KVQ_OK) return st;
+    if (max_pages < 1 || int64_t(max_seq_len) > int64_t(max_pages) * cache->page_size) return KVQ_ERR_INVALID_ARG;
+    if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return KVQ_ERR_INVALID_ARG;
+    if (batch == 0) return KVQ_OK;
+    if (!aligned(q) || !aligned(page_table, 4) || !aligned(part_acc) || !aligned(part_m, 4) || !aligned(part_z, 4))
+        return KVQ_ERR_INVALID_ARG;
+    kvq::DecodeArgs a{q, n_q_heads, page_table, max_pages, seq_lens, batch, max_seq_len,
+                      kvq_num_splits(max_seq_len, split_keys), sm_scale, split_keys, part_acc, part_m, part_z};
+    if (cache->format == KVQ_FMT_Q4_H32) return launched(kvq::launch_decode_q4_simple(q4_pool(cache), a, stream));
+    return launched(kvq::launch_decode_fp8_simple(fp8_pool(cache), a, stream));
+}
+
+kvq_status kvq_merge(const kvq_cache* cache, const float* part_acc, const float* part_m, const float* part_z,
+                     const int32_t* seq_lens, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
+                     int32_t split_keys, int32_t inverse_rotate, float* out, float* lse, hipStream_t stream) {
+    kvq_status st = check_cache(cache);
+    if (st != KVQ_OK) return st;
+    st = check_seq_args(cache, n_q_heads, seq_lens, batch, max_seq_len, split_keys);
+    if (st != KVQ_OK) return st;
+    const bool q4 = cache->format == KVQ_FMT_Q4_H32;
+    if (inverse_rotate != (q4 ? 1 : 0)) return KVQ_ERR_INVALID_ARG;
+    if (batch == 0) return KVQ_OK;
+    if (!aligned(part_acc) || !aligned(part_m, 4) || !aligned(part_z, 4) || !aligned(out) ||
+        (lse && !aligned(lse, 4)))
+        return KVQ_ERR_INVALID_ARG;
+    if (int64_t(batch) * n_q_heads > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
+    kvq::MergeArgs a{part_acc, part_m, part_z, seq_lens, batch, n_q_heads, max_seq_len,
+                     kvq_num_splits(max_seq_len, split_keys), split_keys,
+                     q4 ? cache->head_dim : cache->head_dim - cache->rope_dim, q4, out, lse};
+    return launched(kvq::launch_merge(a, stream));
+}
+
+}  // extern "C"

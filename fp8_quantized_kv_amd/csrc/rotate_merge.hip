@@ -1,0 +1,147 @@
+// rotate_merge.hip -- the query rotation and the log-sum-exp merge.
+//
+// TensorFold issue "qwen27 CUDA: an opt-in 4-bit attention cache", section
+// "What it is": rotate the queries once, merge the chunk partials in order,
+// rotate the output back once.  colibri pull request "KV cache quantization:
+// fp8 (KV8) + 4-bit TurboQuant", split-T commit: partials (cl[K], m, z) and
+// a log-sum-exp merge kernel.
+#include "internal.h"
+
+namespace kvq {
+namespace {
+
+// One thread per 32-group of the query: fp32 butterfly (stages 1..16), then
+// x fp32(1/sqrt(32)) -- the same transform the store applies to K and V.
+template <InType DT>
+__global__ __launch_bounds__(256) void rotate_q_kernel(const void* __restrict__ q, float* __restrict__ q_rot,
+                                                       int64_t n_groups) {
+    const int64_t gi = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (gi >= n_groups) return;
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = load_elem<DT>(q, gi * 32 + i);
+#pragma unroll
+    for (int hs = 1; hs < 32; hs <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            if (i & hs) continue;
+            const float a = x[i], b = x[i + hs];
+            x[i] = a + b;
+            x[i + hs] = a - b;
+        }
+    }
+    const float c = inv_sqrt32();
+    float4* o = reinterpret_cast<float4*>(q_rot + gi * 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = make_float4(x[4 * i] * c, x[4 * i + 1] * c, x[4 * i + 2] * c, x[4 * i + 3] * c);
+}
+
+constexpr int kMergeThreads = 256;
+
+// One workgroup per (sequence, query head).  Weights w_s = exp(m_s - M) / Z
+// are formed once per split; each thread then owns output channels and sums
+// acc_s[c] * w_s in ascending s, so the result does not depend on anything
+// but the sequence's own partials.  For the 4-bit cache the rotated-domain
+// sum is rotated back with H32 (its own inverse): out[c] = sum_j H[c%32][j]
+// * O[32*(c/32) + j], H[i][j] = (-1)^popcount(i&j) / sqrt(32).
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part_acc,
+                                                              const float* __restrict__ part_m,
+                                                              const float* __restrict__ part_z,
+                                                              const int32_t* __restrict__ seq_lens, int n_q_heads,
+                                                              int max_seq_len, int S, int split_keys, int dv,
+                                                              int rotate, float* __restrict__ out,
+                                                              float* __restrict__ lse) {
+    extern __shared__ float smem[];  // [S] weights, then [dv] rotated-domain output
+    float* w = smem;
+    float* o_rot = smem + S;
+    __shared__ float red[kMergeThreads / 64];
+    __shared__ float s_M, s_Z;
+
+    const int bh = blockIdx.x;
+    const int b = bh / n_q_heads;
+    const int tid = threadIdx.x;
+    int T = seq_lens[b];
+    T = T < 0 ? 0 : (T > max_seq_len ? max_seq_len : T);
+    const int n = (T + split_keys - 1) / split_keys;
+    float* o = out + int64_t(bh) * dv;
+    if (n == 0) {
+        for (int c = tid; c < dv; c += kMergeThreads) o[c] = 0.0f;
+        if (lse && tid == 0) lse[bh] = -INFINITY;
+        return;
+    }
+    const float* pm = part_m + int64_t(bh) * S;
+    const float* pz = part_z + int64_t(bh) * S;
+
+    // M = max over the used splits (max is exact, so the reduction order is moot).
+    float mx = -INFINITY;
+    for (int s = tid; s < n; s += kMergeThreads) mx = fmaxf(mx, pm[s]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    if (tid == 0) {
+        float M = red[0];
+        for (int i = 1; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[i]);
+        s_M = M;
+    }
+    __syncthreads();
+    const float M = s_M;
+    for (int s = tid; s < n; s += kMergeThreads) {
+        const float z = pz[s];
+        w[s] = z > 0.0f ? expf(pm[s] - M) : 0.0f;
+    }
+    __syncthreads();
+    if (tid == 0) {  // Z in ascending split order
+        float Z = 0.0f;
+        for (int s = 0; s < n; ++s) Z += pz[s] * w[s];
+        s_Z = Z;
+    }
+    __syncthreads();
+    const float invZ = 1.0f / s_Z;
+    const float* pa = part_acc + int64_t(bh) * S * dv;
+    for (int c = tid; c < dv; c += kMergeThreads) {
+        float acc = 0.0f;
+        for (int s = 0; s < n; ++s) acc += pa[int64_t(s) * dv + c] * w[s];
+        o_rot[c] = acc * invZ;
+    }
+    __syncthreads();
+    if (rotate) {
+        const float k = inv_sqrt32();
+        for (int c = tid; c < dv; c += kMergeThreads) {
+            const float* blk = o_rot + (c & ~31);
+            const int i = c & 31;
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) acc += (__popc(unsigned(i & j)) & 1) ? -blk[j] : blk[j];
+            o[c] = acc * k;
+        }
+    } else {
+        for (int c = tid; c < dv; c += kMergeThreads) o[c] = o_rot[c];
+    }
+    if (lse && tid == 0) lse[bh] = M + logf(s_Z);
+}
+
+}  // namespace
+
+hipError_t launch_rotate_q(const void* q, InType dt, float* q_rot, int n_rows, int head_dim, hipStream_t s) {
+    const int64_t n_groups = int64_t(n_rows) * (head_dim / 32);
+    if (n_groups == 0) return hipSuccess;
+    const dim3 block(256), grid(unsigned((n_groups + 255) / 256));
+    switch (dt) {
+        case InType::F32: rotate_q_kernel<InType::F32><<<grid, block, 0, s>>>(q, q_rot, n_groups); break;
+        case InType::BF16: rotate_q_kernel<InType::BF16><<<grid, block, 0, s>>>(q, q_rot, n_groups); break;
+        case InType::F16: rotate_q_kernel<InType::F16><<<grid, block, 0, s>>>(q, q_rot, n_groups); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
+    if (a.batch == 0) return hipSuccess;
+    const size_t shm = sizeof(float) * (size_t(a.n_splits) + size_t(a.dv));
+    merge_kernel<<<dim3(unsigned(a.batch * a.n_q_heads)), dim3(kMergeThreads), shm, s>>>(
+        a.part_acc, a.part_m, a.part_z, a.seq_lens, a.n_q_heads, a.max_seq_len, a.n_splits, a.split_keys, a.dv,
+        a.rotate ? 1 : 0, a.out, a.lse);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,195 @@
+// store.hip -- quantize new K/V rows into the paged caches.
+//
+// 4-bit Hadamard-32 rows (TensorFold issue "qwen27 CUDA: an opt-in 4-bit
+// attention cache", section "What it is"; FreeToken pull request
+// "feat(kvcache): add reliable quantized KV cache", PR description and
+// test-fix commit: 16 code bytes + one fp16 scale per 32 values, scale =
+// amax/8) and fp8 e4m3 latent rows (colibri pull request "KV cache
+// quantization: fp8 (KV8) + 4-bit TurboQuant", KV8 commit: per-row f32
+// scale amax/448, RNE, saturating, NaN stored as 0, guard for an amax whose
+// 448/amax overflows).
+//
+// The codes are bit-exact by construction: every step is one IEEE fp32
+// operation in a fixed order (this file is compiled without contraction and
+// with the correctly rounded fp32 divide), and binary16 conversion is the
+// hardware's round-to-nearest-even convert.
+#include "internal.h"
+
+#pragma clang fp contract(off)
+
+namespace kvq {
+namespace {
+
+// One thread quantizes one 32-value group of one row: the whole group lives
+// in registers, the butterfly needs no exchange, and the 16 code bytes leave
+// as one 16-byte store when the row allows it.  The store is off the decode
+// critical path (one token per layer per step), so simplicity wins here.
+template <InType DT>
+__global__ __launch_bounds__(256) void store_q4_kernel(const void* __restrict__ k, const void* __restrict__ v,
+                                                       const int64_t* __restrict__ slots, int n_tokens,
+                                                       uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                                                       int H, int D, int page_size, int64_t n_slots) {
+    const int G = D / 32;
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = int64_t(n_tokens) * H * 2 * G;
+    if (idx >= total) return;
+    const int g = int(idx % G);
+    int64_t r = idx / G;
+    const int which = int(r & 1);
+    r >>= 1;
+    const int h = int(r % H);
+    const int64_t t = r / H;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= n_slots) return;
+
+    const void* src = which ? v : k;
+    const int64_t base = (t * H + h) * D + 32 * g;
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = load_elem<DT>(src, base + i);
+
+    // Hadamard butterfly, stages 1, 2, 4, 8, 16: (a, b) -> (a + b, a - b).
+#pragma unroll
+    for (int hs = 1; hs < 32; hs <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            if (i & hs) continue;
+            const float a = x[i], b = x[i + hs];
+            x[i] = a + b;
+            x[i + hs] = a - b;
+        }
+    }
+    const float c = inv_sqrt32();
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        x[i] = x[i] * c;
+        amax = fmaxf(amax, fabsf(x[i]));
+    }
+    // scale = fp16_rne(amax / 8); amax * 0.125 is the same exactly rounded value.
+    const __half s16 = __float2half_rn(amax * 0.125f);
+    const float s = __half2float(s16);
+
+    uint32_t words[4] = {0u, 0u, 0u, 0u};
+    if (s != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            float n = rintf(x[i] / s);  // correctly rounded divide, then half-to-even
+            n = fminf(fmaxf(n, -8.0f), 7.0f);
+            const uint32_t nib = uint32_t(int(n)) & 0xFu;
+            words[i >> 3] |= nib << (4 * (i & 7));
+        }
+    }
+    const int rb = q4_row_bytes(D);
+    const int64_t page = slot / page_size, off = slot % page_size;
+    uint8_t* row = (which ? v_pool : k_pool) + ((page * H + h) * page_size + off) * rb;
+    uint32_t* cw = reinterpret_cast<uint32_t*>(row + 16 * g);
+    if ((reinterpret_cast<uintptr_t>(cw) & 15u) == 0) {
+        *reinterpret_cast<uint4*>(cw) = make_uint4(words[0], words[1], words[2], words[3]);
+    } else {
+        cw[0] = words[0];
+        cw[1] = words[1];
+        cw[2] = words[2];
+        cw[3] = words[3];
+    }
+    reinterpret_cast<uint16_t*>(row + D / 2)[g] = __half_as_ushort(s16);
+}
+
+// e4m3 ("fn": bias 7, max 448) code of v, round to nearest even, saturating
+// to +-448, NaN -> 0x00, signed zero kept.  Bit manipulation on the fp32
+// encoding: the top 3 mantissa bits survive and the 20 below decide rounding.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return 0u;                 // NaN
+    if (a >= 0x43E00000u) return sign | 0x7Eu;      // |v| >= 448, incl. infinity
+    if (a < 0x3C800000u) {                          // |v| < 2^-6: spacing 2^-9
+        const float n = rintf(__uint_as_float(a) * 512.0f);  // exact scaling, then RNE
+        return sign | uint32_t(n);                  // n == 8 is the smallest normal
+    }
+    uint32_t code = ((((a >> 23) - 127u + 7u)) << 3) | ((a >> 20) & 7u);
+    const uint32_t rem = a & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) code += 1u;  // carry may bump the exponent
+    return sign | code;
+}
+
+// One wave per token: the latent part (L values) and the rope part (R values)
+// each get their own amax, reduced across the wave, then every lane encodes
+// the elements it strides over.
+template <InType DT>
+__global__ __launch_bounds__(64) void store_fp8_kernel(const void* __restrict__ x, const int64_t* __restrict__ slots,
+                                                       int n_tokens, uint8_t* __restrict__ codes,
+                                                       float* __restrict__ scales, int D, int R, int64_t n_slots) {
+    const int t = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= n_slots) return;
+    const int L = D - R;
+    const int64_t base = int64_t(t) * D;
+    uint8_t* out = codes + slot * D;
+#pragma unroll 1
+    for (int part = 0; part < 2; ++part) {
+        const int lo = part ? L : 0, n = part ? R : L;
+        float amax = 0.0f;
+        for (int i = lane; i < n; i += 64) amax = fmaxf(amax, fabsf(load_elem<DT>(x, base + lo + i)));  // NaN ignored
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+        const float inv = 448.0f / amax;
+        const bool inert = !(amax > 0.0f) || !isfinite(amax) || !isfinite(inv);
+        for (int i = lane; i < n; i += 64) {
+            const float e = load_elem<DT>(x, base + lo + i);
+            out[lo + i] = inert ? uint8_t(0) : uint8_t(e4m3_encode(e * inv));
+        }
+        if (lane == 0) scales[slot * 2 + part] = inert ? 0.0f : amax / 448.0f;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_store_q4(const Q4Pool& pool, const void* k, const void* v, InType dt, const int64_t* slots,
+                           int n_tokens, hipStream_t s) {
+    const int64_t total = int64_t(n_tokens) * pool.n_kv_heads * 2 * (pool.head_dim / 32);
+    if (total == 0) return hipSuccess;
+    const dim3 block(256), grid(unsigned((total + 255) / 256));
+    const int64_t n_slots = int64_t(pool.num_pages) * pool.page_size;
+    switch (dt) {
+        case InType::F32:
+            store_q4_kernel<InType::F32><<<grid, block, 0, s>>>(k, v, slots, n_tokens, pool.k, pool.v,
+                                                                pool.n_kv_heads, pool.head_dim, pool.page_size, n_slots);
+            break;
+        case InType::BF16:
+            store_q4_kernel<InType::BF16><<<grid, block, 0, s>>>(k, v, slots, n_tokens, pool.k, pool.v,
+                                                                 pool.n_kv_heads, pool.head_dim, pool.page_size, n_slots);
+            break;
+        case InType::F16:
+            store_q4_kernel<InType::F16><<<grid, block, 0, s>>>(k, v, slots, n_tokens, pool.k, pool.v,
+                                                                pool.n_kv_heads, pool.head_dim, pool.page_size, n_slots);
+            break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_store_fp8(const Fp8Pool& pool, const void* x, InType dt, const int64_t* slots, int n_tokens,
+                            hipStream_t s) {
+    if (n_tokens == 0) return hipSuccess;
+    const int64_t n_slots = int64_t(pool.num_pages) * pool.page_size;
+    const dim3 block(64), grid(static_cast<unsigned>(n_tokens));
+    switch (dt) {
+        case InType::F32:
+            store_fp8_kernel<InType::F32><<<grid, block, 0, s>>>(x, slots, n_tokens, pool.codes, pool.scales,
+                                                                 pool.head_dim, pool.rope_dim, n_slots);
+            break;
+        case InType::BF16:
+            store_fp8_kernel<InType::BF16><<<grid, block, 0, s>>>(x, slots, n_tokens, pool.codes, pool.scales,
+                                                                  pool.head_dim, pool.rope_dim, n_slots);
+            break;
+        case InType::F16:
+            store_fp8_kernel<InType::F16><<<grid, block, 0, s>>>(x, slots, n_tokens, pool.codes, pool.scales,
+                                                                 pool.head_dim, pool.rope_dim, n_slots);
+            break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvq

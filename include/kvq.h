@@ -1,0 +1,205 @@
+/*
+ * kvq.h -- C ABI of the MI355X (gfx950) sub-byte KV cache library.
+ *
+ * Quantize new K/V rows into a paged sub-byte cache and run decode attention
+ * directly over it, split-K (flash-decoding) style, then merge the partials.
+ *
+ * Method (web pages, cited by title and section):
+ *  - TensorFold issue "qwen27 CUDA: an opt-in 4-bit attention cache (262K on
+ *    a 24 GB card)", section "What it is": each (position, KV head) row is
+ *    Hadamard-rotated in groups of 32 and stored as 4-bit codes plus an fp16
+ *    scale (144 bytes at head_dim 256); a decode round packs the new keys and
+ *    values, rotates the queries once, attends over the 4-bit cache in
+ *    rotated space in shared 512-key chunks plus each row's tail with an
+ *    in-order merge, and rotates the output back once.
+ *  - FreeToken pull request "feat(kvcache): add reliable quantized KV cache":
+ *    PR description (32 values -> 16 bytes + one fp16 scale; one layout
+ *    constant shared by pool, store and attention) and its CLI-plumbing
+ *    commit (head_dim must be divisible by the 32-value block; unsupported
+ *    pools are refused at configuration time); test-fix commit (scale =
+ *    amax/8, codes sign-extended as int32).
+ *  - colibri pull request "KV cache quantization: fp8 (KV8) + 4-bit
+ *    TurboQuant (KV_TQ) on CPU, CUDA, and Metal": KV8 commit (latent rows
+ *    of kv_lora + rope values stored as e4m3 with a per-row f32 amax/448
+ *    scale, RNE, saturating at +-448, NaN stored as 0; absorbed attention
+ *    where the latent is both key and value) and split-T commit (partial
+ *    blocks per (head, split) holding (cl[K], m, z), then a log-sum-exp
+ *    merge kernel).
+ *
+ * Conventions for every entry point:
+ *  - Ownership: the caller allocates and owns every buffer (device memory
+ *    unless stated).  The library never allocates, frees or synchronizes,
+ *    and keeps no mutable global state, so calls are thread-safe.
+ *  - Asynchrony: work is enqueued on `stream` (0 = the null stream).  The
+ *    returned status covers argument validation, done on the host before any
+ *    launch, and the launch itself; a device fault surfaces at the caller's
+ *    next synchronization.
+ *  - Validation: an invalid argument returns KVQ_ERR_INVALID_ARG (or
+ *    KVQ_ERR_UNSUPPORTED for a valid but unimplemented shape) and launches
+ *    nothing.  There is no fallback path.
+ *  - Determinism: the split partition of a sequence depends only on its own
+ *    length and split_keys, partials are merged in ascending split order, and
+ *    no atomics are used, so outputs are bit-reproducible and independent of
+ *    the other sequences in the batch.
+ *  - Device pointers must be 16-byte aligned unless stated otherwise.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size or pairing */
+    KVQ_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement */
+    KVQ_ERR_LAUNCH = -3        /* the HIP runtime rejected a launch */
+} kvq_status;
+
+typedef enum {
+    KVQ_FMT_Q4_H32 = 1,        /* 4-bit Hadamard-32 groups + fp16 scale, K and V pools */
+    KVQ_FMT_FP8_E4M3_ROW = 2   /* e4m3 latent rows + f32 scales (latent, rope) */
+} kvq_format;
+
+typedef enum {
+    KVQ_DT_F32 = 0,
+    KVQ_DT_BF16 = 1,
+    KVQ_DT_F16 = 2
+} kvq_dtype;
+
+/* A paged cache.  A slot is page * page_size + offset.
+ *
+ * KVQ_FMT_Q4_H32 (the "What it is" row of the TensorFold issue):
+ *   head_dim D, a multiple of 32 (64, 128, 256 or 512); rope_dim = 0.
+ *   k_pool and v_pool: [num_pages][num_kv_heads][page_size][row_bytes] bytes,
+ *   row_bytes = D/2 + 2*(D/32).  A row is the D/2 code bytes, group after
+ *   group (byte k of a group holds element 2k in its low nibble and element
+ *   2k+1 in its high nibble, two's complement), then the D/32 fp16 scales,
+ *   little-endian.  scale_pool = NULL.
+ * KVQ_FMT_FP8_E4M3_ROW (the KV8 commit of the colibri pull request):
+ *   num_kv_heads = 1 (one latent shared by all heads), head_dim = kv_lora +
+ *   rope_dim (a multiple of 16; kv_lora a multiple of 64), rope_dim > 0.
+ *   k_pool: e4m3 codes [num_pages*page_size][head_dim]; v_pool = NULL;
+ *   scale_pool: f32 [num_pages*page_size][2] = {latent scale, rope scale}.
+ */
+typedef struct kvq_cache {
+    int32_t format;        /* kvq_format */
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t rope_dim;
+    int32_t page_size;     /* tokens per page, >= 1 */
+    int32_t num_pages;
+    void* k_pool;
+    void* v_pool;
+    void* scale_pool;
+} kvq_cache;
+
+/* ---------------------------------------------------------------- helpers */
+
+/* Human-readable name of a status (static storage). */
+const char* kvq_status_string(kvq_status s);
+
+/* Bytes of one stored row: Q4 -> D/2 + 2*D/32 (144 at D = 256, the TensorFold
+ * "What it is" figure); FP8 -> head_dim (codes only; scales are separate).
+ * Returns 0 for an invalid format or size.  Host only. */
+size_t kvq_row_bytes(int32_t format, int32_t head_dim, int32_t rope_dim);
+
+/* Bytes of the pool(s) a cache descriptor needs: k_pool + v_pool (Q4), or
+ * codes + scales (FP8).  0 if the descriptor is invalid.  Host only. */
+size_t kvq_pool_bytes(const kvq_cache* cache);
+
+/* Number of splits (partials per head) for sequences up to max_seq_len:
+ * ceil(max_seq_len / split_keys), at least 1.  0 on invalid input.  Host only. */
+int32_t kvq_num_splits(int32_t max_seq_len, int32_t split_keys);
+
+/* ---------------------------------------------------------------- store */
+
+/* Quantize n_tokens new rows into the cache (TensorFold "What it is": pack
+ * the window's new keys and values; colibri KV8 commit: the producer
+ * quantizes the fresh row).
+ *
+ * Q4:  k, v: [n_tokens][num_kv_heads][head_dim] of `dtype` (f32, bf16, f16).
+ *      Per row and group of 32: fp32 Hadamard butterfly (stages 1,2,4,8,16)
+ *      then x fp32(1/sqrt(32)); amax; scale = fp16_rne(amax/8); codes =
+ *      clamp(round_half_even(y / scale), -8, 7), all codes 0 when the scale
+ *      is 0.  Rows whose scale would overflow fp16 or that hold NaN/Inf are
+ *      outside the format's domain; their stored bytes are unspecified.
+ * FP8: k: [n_tokens][head_dim] of `dtype`, v = NULL.  Latent part and rope
+ *      part are quantized separately: amax (NaN ignored); if amax is 0 or
+ *      not finite or 448/amax is not finite, scale 0 and codes 0x00;
+ *      otherwise codes = e4m3_rne_saturating(x * (448/amax)) with NaN -> 0x00,
+ *      scale = amax/448.
+ * slot_mapping: device int64 [n_tokens]; a negative slot skips the token;
+ * every other slot must be < num_pages * page_size (not checked on device).
+ * n_tokens = 0 is a no-op.  k/v need 4-byte alignment only. */
+kvq_status kvq_store(const kvq_cache* cache, const void* k, const void* v, int32_t dtype,
+                     const int64_t* slot_mapping, int32_t n_tokens, hipStream_t stream);
+
+/* ---------------------------------------------------------------- rotate */
+
+/* q_rot = H32 q for every 32-group of every row (TensorFold "What it is":
+ * rotate the queries once), H32 the orthonormal Sylvester Hadamard matrix,
+ * computed as the fp32 butterfly then x fp32(1/sqrt(32)).
+ * q: [n_rows][head_dim] of `dtype`; q_rot: [n_rows][head_dim] f32.  In place
+ * (q == q_rot) is allowed for f32.  Q4 only; head_dim % 32 == 0. */
+kvq_status kvq_rotate_q(const void* q, int32_t dtype, float* q_rot, int32_t n_rows, int32_t head_dim,
+                        hipStream_t stream);
+
+/* ---------------------------------------------------------------- decode */
+
+/* Split-K decode attention over the cache, writing one partial per
+ * (sequence, query head, split) (colibri split-T commit: (cl[K], m, z)).
+ *
+ * Split s of sequence b covers positions [s*split_keys, min((s+1)*split_keys,
+ * T_b)), T_b = seq_lens[b]; splits at or past the end are written empty
+ * (m = -inf, z = 0, acc = 0).  Position j lives at slot
+ * page_table[b*max_pages + j/page_size]*page_size + j%page_size.
+ * Scores are natural-log units: s_j = sm_scale * <q, k_j>.
+ *   m = max_j s_j, z = sum_j exp(s_j - m), acc = sum_j exp(s_j - m) v_j.
+ *
+ * Q4:  q = q_rot [batch][n_q_heads][head_dim] f32 (already rotated); query
+ *      head h reads KV head h / (n_q_heads / num_kv_heads); k_j, v_j are the
+ *      dequantized rotated rows (scale * code), acc is in the rotated domain.
+ *      Dv = head_dim.
+ * FP8: q = [batch][n_q_heads][head_dim] f32 (latent part then rope part);
+ *      s_j = sm_scale*(scL_j <qL, dec(Lc_j)> + scR_j <qR, dec(Rc_j)>),
+ *      v_j = scL_j dec(Lc_j) (the latent is the value); Dv = head_dim -
+ *      rope_dim.  NaN codes (0x7F, 0xFF) read as 0.
+ * page_table: device int32 [batch][max_pages]; seq_lens: device int32
+ * [batch], each in [0, max_seq_len]; max_seq_len <= max_pages*page_size.
+ * split_keys: a positive multiple of 512 (the TensorFold chunk size).
+ * part_acc: [batch][n_q_heads][S][Dv] f32, part_m / part_z: [batch][n_q_heads][S]
+ * f32 with S = kvq_num_splits(max_seq_len, split_keys).
+ * Requires n_q_heads % num_kv_heads == 0 and a group of at most 16 query
+ * heads per KV head (Q4). */
+kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
+                           int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                           float sm_scale, int32_t split_keys, float* part_acc, float* part_m, float* part_z,
+                           hipStream_t stream);
+
+/* ---------------------------------------------------------------- merge */
+
+/* Log-sum-exp merge of the partials (colibri split-T commit), in ascending
+ * split order (TensorFold "What it is": an in-order merge), followed for Q4
+ * by the single inverse rotation (H32 is its own inverse):
+ *   M = max_s m_s, Z = sum_s z_s exp(m_s - M),
+ *   out = R( sum_s acc_s exp(m_s - M) / Z ),  R = H32 (Q4) or identity (FP8),
+ *   lse = M + log Z.
+ * A sequence with T = 0 gives out = 0 and lse = -inf.  Only the splits that
+ * cover [0, T_b) are read.  inverse_rotate must be 1 for Q4 and 0 for FP8.
+ * out: [batch][n_q_heads][Dv] f32; lse: [batch][n_q_heads] f32 or NULL. */
+kvq_status kvq_merge(const kvq_cache* cache, const float* part_acc, const float* part_m, const float* part_z,
+                     const int32_t* seq_lens, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
+                     int32_t split_keys, int32_t inverse_rotate, float* out, float* lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

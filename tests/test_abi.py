@@ -1,0 +1,167 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/kvq.h
+declares, its host helpers compute the documented sizes, and invalid
+arguments are rejected on the host before any launch (no GPU needed: every
+call here returns before touching the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    import fp8_quantized_kv_amd as m
+    return m
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(kvq):
+    names = _declared()
+    assert set(names) >= {"kvq_store", "kvq_rotate_q", "kvq_decode_attn", "kvq_merge"}
+    raw = ctypes.CDLL(kvq.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), f"libkvq.so does not export {n}"
+    assert set(names) == set(kvq.EXPORTED)
+
+
+def test_size_helpers(kvq):
+    L = kvq.lib
+    assert L.kvq_row_bytes(kvq.FMT_Q4_H32, 256, 0) == 144
+    assert L.kvq_row_bytes(kvq.FMT_Q4_H32, 128, 0) == 72
+    assert L.kvq_row_bytes(kvq.FMT_Q4_H32, 100, 0) == 0
+    assert L.kvq_row_bytes(kvq.FMT_FP8_E4M3_ROW, 576, 64) == 576
+    assert L.kvq_row_bytes(7, 256, 0) == 0
+    assert L.kvq_num_splits(262144, 2048) == 128
+    assert L.kvq_num_splits(262145, 2048) == 129
+    assert L.kvq_num_splits(0, 512) == 1
+    assert L.kvq_num_splits(100, 0) == 0
+    d = kvq.KvqCacheDesc(kvq.FMT_Q4_H32, 4, 256, 0, 16, 16384, 0x1000, 0x2000, None)
+    assert L.kvq_pool_bytes(ctypes.byref(d)) == 2 * 16384 * 16 * 4 * 144   # K and V pools
+    e = kvq.KvqCacheDesc(kvq.FMT_FP8_E4M3_ROW, 1, 576, 64, 16, 16384, 0x1000, None, 0x2000)
+    assert L.kvq_pool_bytes(ctypes.byref(e)) == 16384 * 16 * 584
+    assert L.kvq_status_string(-2) == b"unsupported shape or format"
+
+
+# Fake, aligned device addresses: every call below must be rejected on the
+# host before it could be dereferenced.
+A = 0x7F0000000000
+
+
+def _q4(kvq, **kw):
+    f = dict(format=kvq.FMT_Q4_H32, num_kv_heads=4, head_dim=256, rope_dim=0, page_size=16, num_pages=64,
+             k_pool=A, v_pool=A + 0x100000, scale_pool=None)
+    f.update(kw)
+    return kvq.KvqCacheDesc(**f)
+
+
+def _fp8(kvq, **kw):
+    f = dict(format=kvq.FMT_FP8_E4M3_ROW, num_kv_heads=1, head_dim=576, rope_dim=64, page_size=16, num_pages=64,
+             k_pool=A, v_pool=None, scale_pool=A + 0x100000)
+    f.update(kw)
+    return kvq.KvqCacheDesc(**f)
+
+
+INVALID, UNSUPPORTED = -1, -2
+
+
+@pytest.mark.parametrize("desc_kw,expect", [
+    (dict(format=9), INVALID),
+    (dict(head_dim=100), INVALID),
+    (dict(head_dim=96), UNSUPPORTED),
+    (dict(page_size=0), INVALID),
+    (dict(num_pages=0), INVALID),
+    (dict(k_pool=A + 4), INVALID),
+    (dict(v_pool=None), INVALID),
+    (dict(scale_pool=A), INVALID),
+    (dict(rope_dim=64), INVALID),
+])
+def test_store_rejects_bad_q4_cache(kvq, desc_kw, expect):
+    d = _q4(kvq, **desc_kw)
+    rc = kvq.lib.kvq_store(ctypes.byref(d), ctypes.c_void_p(A), ctypes.c_void_p(A), 0, ctypes.c_void_p(A), 4, None)
+    assert rc == expect
+
+
+@pytest.mark.parametrize("desc_kw,expect", [
+    (dict(num_kv_heads=2), INVALID),
+    (dict(rope_dim=0), INVALID),
+    (dict(head_dim=320, rope_dim=64), UNSUPPORTED),
+    (dict(v_pool=A), INVALID),
+    (dict(scale_pool=None), INVALID),
+])
+def test_store_rejects_bad_fp8_cache(kvq, desc_kw, expect):
+    d = _fp8(kvq, **desc_kw)
+    rc = kvq.lib.kvq_store(ctypes.byref(d), ctypes.c_void_p(A), None, 0, ctypes.c_void_p(A), 4, None)
+    assert rc == expect
+
+
+def test_store_argument_checks(kvq):
+    d = _q4(kvq)
+    P = ctypes.c_void_p
+    assert kvq.lib.kvq_store(None, P(A), P(A), 0, P(A), 4, None) == INVALID
+    assert kvq.lib.kvq_store(ctypes.byref(d), P(A), P(A), 7, P(A), 4, None) == INVALID      # dtype
+    assert kvq.lib.kvq_store(ctypes.byref(d), P(A), P(A), 0, P(A), -1, None) == INVALID     # n_tokens
+    assert kvq.lib.kvq_store(ctypes.byref(d), P(A + 2), P(A), 0, P(A), 4, None) == INVALID  # misaligned k
+    assert kvq.lib.kvq_store(ctypes.byref(d), P(A), P(A), 0, P(A + 4), 4, None) == INVALID  # misaligned slots
+    assert kvq.lib.kvq_store(ctypes.byref(d), P(A), P(A), 0, P(A), 0, None) == 0            # no-op
+    f = _fp8(kvq)
+    assert kvq.lib.kvq_store(ctypes.byref(f), P(A), P(A), 0, P(A), 4, None) == INVALID      # fp8 takes no v
+
+
+def test_rotate_argument_checks(kvq):
+    P = ctypes.c_void_p
+    r = kvq.lib.kvq_rotate_q
+    assert r(P(A), 0, P(A), 4, 100, None) == INVALID      # head_dim % 32
+    assert r(P(A), 1, P(A), 4, 256, None) == INVALID      # in place needs f32
+    assert r(P(A + 8), 0, P(A), 4, 256, None) == INVALID
+    assert r(P(A), 0, P(A), 0, 256, None) == 0
+
+
+def _decode(kvq, d, **kw):
+    P = ctypes.c_void_p
+    a = dict(q=P(A), n_q_heads=24, page_table=P(A), max_pages=64, seq_lens=P(A), batch=1, max_seq_len=1024,
+             sm_scale=0.0625, split_keys=512, part_acc=P(A), part_m=P(A), part_z=P(A))
+    a.update(kw)
+    return kvq.lib.kvq_decode_attn(ctypes.byref(d), a["q"], a["n_q_heads"], a["page_table"], a["max_pages"],
+                                   a["seq_lens"], a["batch"], a["max_seq_len"], a["sm_scale"], a["split_keys"],
+                                   a["part_acc"], a["part_m"], a["part_z"], None)
+
+
+def test_decode_argument_checks(kvq):
+    d = _q4(kvq)
+    assert _decode(kvq, d, split_keys=500) == INVALID
+    assert _decode(kvq, d, split_keys=0) == INVALID
+    assert _decode(kvq, d, n_q_heads=23) == INVALID          # not a multiple of the KV heads
+    assert _decode(kvq, d, n_q_heads=4 * 17) == UNSUPPORTED  # group of 17
+    assert _decode(kvq, d, max_seq_len=64 * 16 + 1) == INVALID  # beyond the page table
+    assert _decode(kvq, d, max_pages=0) == INVALID
+    assert _decode(kvq, d, sm_scale=float("nan")) == INVALID
+    assert _decode(kvq, d, q=ctypes.c_void_p(A + 4)) == INVALID
+    assert _decode(kvq, d, part_acc=None) == INVALID
+    assert _decode(kvq, d, batch=-1) == INVALID
+    assert _decode(kvq, d, batch=0) == 0
+
+
+def test_merge_argument_checks(kvq):
+    P = ctypes.c_void_p
+    m = kvq.lib.kvq_merge
+    d, f = _q4(kvq), _fp8(kvq)
+    assert m(ctypes.byref(d), P(A), P(A), P(A), P(A), 1, 24, 1024, 512, 0, P(A), None, None) == INVALID  # Q4 rotates
+    assert m(ctypes.byref(f), P(A), P(A), P(A), P(A), 1, 16, 1024, 512, 1, P(A), None, None) == INVALID  # fp8 does not
+    assert m(ctypes.byref(d), P(A), P(A), P(A), P(A), 1, 24, 1024, 1000, 1, P(A), None, None) == INVALID
+    assert m(ctypes.byref(d), P(A), P(A), P(A), P(A), 1, 24, 1024, 512, 1, P(A + 8), None, None) == INVALID
+    assert m(ctypes.byref(d), P(A), P(A), P(A), P(A), 0, 24, 1024, 512, 1, P(A), None, None) == 0
+
+
+def test_python_binding_checks_tensors(kvq):
+    import torch
+    with pytest.raises(ValueError):
+        kvq.kvq_rotate_q(torch.zeros(4, 256))    # a CPU tensor is refused: no CPU path exists

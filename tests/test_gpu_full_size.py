@@ -1,0 +1,87 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (each workload's split_keys).  Codes are compared in full;
+attention is compared for every head (4-bit) or a sample of heads (fp8
+latent, whose fp64 oracle is slow at 262K positions)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from helpers import TOL, MlaCase, Q4Case, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    assert torch.cuda.is_available(), "no GPU"
+    import fp8_quantized_kv_amd as m
+    return m
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("name", ["gqa_q4_32k", "gqa_q4_262k"])
+def test_dense_gqa_full(kvq, name):
+    w = wl.WORKLOADS[name]
+    _say(f"full {name}: T={w.seq_len} split={w.split_keys}")
+    case = Q4Case(w, [w.seq_len], layer=1)
+    torch.cuda.synchronize()
+    assert np.array_equal(case.cache.k_pool.cpu().numpy(), case.k_ref)
+    assert np.array_equal(case.cache.v_pool.cpu().numpy(), case.v_ref)
+    o, lse = case.gpu_attention(w.split_keys)
+    ro, rl = case.ref_attention()
+    err = rel_err(o, ro)
+    _say(f"  max_rel_err={err.max():.2e}")
+    assert err.max() < TOL
+    assert np.max(np.abs(lse - rl)) < 1e-3 * max(1.0, np.abs(rl).max())
+    if w.plant_at is not None:
+        # the planted key is recalled: its value dominates each group's first head
+        vrow = case.v_ref[w.plant_at // 16, :, w.plant_at % 16]
+        v_planted = oracle.rotate_f64(oracle.q4_decode_rows(vrow, w.head_dim))
+        for g in range(w.n_kv_heads):
+            h = g * w.group
+            assert np.linalg.norm(o[0, h] - v_planted[g]) < 0.25 * np.linalg.norm(v_planted[g])
+
+
+def test_ragged_full_with_prefill_chunk(kvq):
+    w = wl.RAGGED
+    lens = wl.seq_lens(w)
+    _say(f"full ragged: lens={lens}")
+    case = Q4Case(w, lens)
+    # the step's 2048-token prefill chunk of a 17th sequence is packed through
+    # kvq_store into its reserved pages (stored, not attended)
+    k, v = wl.q4_prefill_chunk(w, 0, "cuda")
+    pages = case.lay.prefill_pages.to(torch.int64)
+    j = torch.arange(w.prefill_chunk, dtype=torch.int64)
+    slots = pages[j // w.page_size] * w.page_size + j % w.page_size
+    kvq.kvq_store(case.cache, k, v, slots.cuda())
+    oracle.q4_store(case.k_ref, case.v_ref, k.float().cpu().numpy(), v.float().cpu().numpy(), slots.numpy(),
+                    w.page_size)
+    torch.cuda.synchronize()
+    assert np.array_equal(case.cache.k_pool.cpu().numpy(), case.k_ref)
+    assert np.array_equal(case.cache.v_pool.cpu().numpy(), case.v_ref)
+    o, lse = case.gpu_attention(w.split_keys)
+    ro, rl = case.ref_attention()
+    err = rel_err(o, ro)
+    _say(f"  max_rel_err={err.max():.2e}")
+    assert err.max() < TOL
+
+
+def test_mla_full_sampled_heads(kvq):
+    w = wl.MLA_262K
+    _say(f"full mla: T={w.seq_len} split={w.split_keys}")
+    case = MlaCase(w, [w.seq_len])
+    torch.cuda.synchronize()
+    assert np.array_equal(case.cache.codes.cpu().numpy(), case.codes_ref)
+    assert np.array_equal(case.cache.scales.cpu().numpy().view(np.uint32), case.scales_ref.view(np.uint32))
+    o, lse = case.gpu_attention(w.split_keys)
+    heads = [0, 17, 64, 127]
+    ro, rl = case.ref_attention(heads=heads)
+    err = rel_err(o[:, heads], ro)
+    _say(f"  max_rel_err={err.max():.2e}")
+    assert err.max() < TOL
+    assert np.max(np.abs(lse[:, heads] - rl)) < 1e-3 * max(1.0, np.abs(rl).max())

@@ -1,0 +1,262 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Bar: cache codes and scales bit-exact; attention output within 2e-3 of the
+oracle's fp64 result (max abs error / max abs reference value, per sequence
+and head); outputs bit-identical between a sequence run alone and inside a
+batch.  Sizes here run in seconds and still span several tiles, several
+splits and ragged tails; test_gpu_full_size.py covers the full workloads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from helpers import TOL, MlaCase, Q4Case, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    assert torch.cuda.is_available(), "no GPU"
+    import fp8_quantized_kv_amd as m
+    return m
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ----------------------------------------------------------------- store
+
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_store_q4_bit_exact(kvq, D, dtype):
+    _say(f"store_q4 D={D} dtype={dtype}")
+    g = torch.Generator().manual_seed(D)
+    n_tok, H, ps, pages = 300, 3, 16, 40
+    k = (torch.randn((n_tok, H, D), generator=g) * torch.exp(torch.randn((n_tok, H, 1), generator=g))).to(dtype)
+    v = torch.randn((n_tok, H, D), generator=g).to(dtype)
+    k[5, 1, 3] = 40.0
+    k[7] = 0.0                          # all-zero rows: scale 0, codes 0
+    slots = torch.randperm(pages * ps, generator=g)[:n_tok].to(torch.int64)
+    slots[::17] = -1                    # skipped tokens
+    cache = kvq.Q4Cache(pages, H, D, ps)
+    kvq.kvq_store(cache, k.cuda(), v.cuda(), slots.cuda())
+    kref = np.zeros(cache.k_pool.shape, np.uint8)
+    vref = np.zeros_like(kref)
+    oracle.q4_store(kref, vref, k.float().numpy(), v.float().numpy(), slots.numpy(), ps)
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.k_pool.cpu().numpy(), kref)
+    assert np.array_equal(cache.v_pool.cpu().numpy(), vref)
+
+
+def test_store_q4_token_by_token_equals_bulk(kvq):
+    """Storing a sequence one token per call gives the same bytes as one call."""
+    w = wl.TINY
+    a = Q4Case(w, [w.seq_len], build_oracle=False)
+    b = Q4Case(w, [w.seq_len], store_chunk=1, build_oracle=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a.cache.k_pool, b.cache.k_pool) and torch.equal(a.cache.v_pool, b.cache.v_pool)
+
+
+def test_store_q4_exact_scale_example(kvq):
+    """Rotated-domain integers with amax 8 store scale 1.0 and codes equal to
+    the integers (FreeToken test-fix commit, exact-scale example)."""
+    import scipy.linalg
+    H = scipy.linalg.hadamard(32) / np.sqrt(32.0)
+    rng = np.random.default_rng(0)
+    c = rng.integers(-8, 8, size=(64, 32))
+    c[:, 0] = -8
+    x = torch.from_numpy((c @ H.T).astype(np.float32)).reshape(64, 1, 32).repeat(1, 1, 2)
+    cache = kvq.Q4Cache(4, 1, 64, 16)
+    kvq.kvq_store(cache, x.cuda().contiguous(), x.cuda().contiguous(), torch.arange(64, dtype=torch.int64).cuda())
+    rows = cache.k_pool.cpu().numpy().reshape(64, 36)
+    assert np.all(rows[:, 32:36].copy().view(np.uint16) == 0x3C00)
+    lo = (rows[:, :16].astype(np.int16) & 0xF)
+    hi = (rows[:, :16].astype(np.int16) >> 4)
+    codes = np.empty((64, 32), np.int16)
+    codes[:, 0::2] = np.where(lo > 7, lo - 16, lo)
+    codes[:, 1::2] = np.where(hi > 7, hi - 16, hi)
+    assert np.array_equal(codes, c)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_store_fp8_bit_exact(kvq, dtype):
+    _say(f"store_fp8 dtype={dtype}")
+    g = torch.Generator().manual_seed(3)
+    n_tok, pages, ps = 200, 16, 16
+    x = (torch.randn((n_tok, 576), generator=g) * torch.exp(2 * torch.randn((n_tok, 1), generator=g)))
+    x[3] = 0.0                     # inert
+    x[4, 7] = float("nan")         # NaN element -> 0x00, ignored by amax
+    x[5, 544] = float("inf")       # non-finite amax -> inert rope part
+    x[6, :512] = 1e-39             # 448/amax overflows -> inert latent part
+    x[7, 100] = 1e6                # one huge element: the scale follows it
+    x = x.to(dtype)
+    slots = torch.randperm(pages * ps, generator=g)[:n_tok].to(torch.int64)
+    slots[::13] = -1
+    cache = kvq.Fp8Cache(pages, 576, 64, ps)
+    kvq.kvq_store(cache, x.cuda(), None, slots.cuda())
+    cref = np.zeros((pages * ps, 576), np.uint8)
+    sref = np.zeros((pages * ps, 2), np.float32)
+    oracle.fp8_store(cref, sref, x.float().numpy(), slots.numpy(), 64)
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.codes.cpu().numpy(), cref)
+    assert np.array_equal(cache.scales.cpu().numpy().view(np.uint32), sref.view(np.uint32))
+
+
+# ----------------------------------------------------------------- rotate
+
+def test_rotate_q_matches_oracle_butterfly(kvq):
+    """kvq_rotate_q is the fp32 butterfly: bit-identical to the oracle's, and
+    within fp32 rounding of the exact fp64 rotation."""
+    q = torch.randn((24, 256), generator=torch.Generator().manual_seed(1))
+    got = kvq.kvq_rotate_q(q.cuda()).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), oracle.hadamard32_f32(q.numpy()).view(np.uint32))
+    ref = oracle.rotate_f64(q.double().numpy())
+    assert np.max(np.abs(got - ref)) < 1e-5
+    qq = q.cuda().clone()
+    kvq.kvq_rotate_q(qq, out=qq)            # in place
+    assert np.array_equal(qq.cpu().numpy(), got)
+
+
+# ----------------------------------------------------------------- 4-bit decode
+
+def _check_q4(case, split_keys, chunked_partials=False):
+    o, lse = case.gpu_attention(split_keys)
+    ro, rl = case.ref_attention()
+    err = rel_err(o, ro)
+    _say(f"  {case.w.name} lens={case.lens[:6]} split={split_keys} max_rel_err={err.max():.2e}")
+    assert err.max() < TOL, err.max()
+    for b, T in enumerate(case.lens):
+        if T == 0:
+            assert np.all(o[b] == 0) and np.all(np.isneginf(lse[b]))
+        else:
+            assert np.max(np.abs(lse[b] - rl[b])) < 1e-3 * max(1.0, np.abs(rl[b]).max())
+
+
+def test_tiny_workload(kvq):
+    """The tiny 4-bit workload in full: D=128, 4 query heads on 1 KV head, T=1024."""
+    w = wl.TINY
+    case = Q4Case(w, [w.seq_len])
+    assert np.array_equal(case.cache.k_pool.cpu().numpy(), case.k_ref)
+    assert np.array_equal(case.cache.v_pool.cpu().numpy(), case.v_ref)
+    _check_q4(case, 512)
+    _check_q4(case, 1024)
+
+
+def test_tiny_partials_match_oracle_chunks(kvq):
+    """The GPU partials at 512-key splits match the oracle's 512-key chunk
+    partials (m, z and acc), so the merge has the same inputs on both sides."""
+    w = wl.TINY
+    case = Q4Case(w, [w.seq_len])
+    _, _, (pa, pm, pz) = case.gpu_attention(512, want_partials=True)
+    _, _, (ra, rm, rz) = case.ref_attention(chunk=512, return_partials=True)
+    assert np.max(np.abs(pm - rm)) < 1e-4 * max(1, np.abs(rm).max())
+    assert np.max(np.abs(pz - rz) / rz) < 1e-4
+    assert np.max(np.abs(pa - ra)) < 1e-4 * np.abs(ra).max()
+
+
+@pytest.mark.parametrize("split_keys", [512, 1024, 2048])
+def test_gqa_several_splits_and_tail(kvq, split_keys):
+    w = wl.shrink(wl.GQA_32K, n_layers=1, seq_len=5000)
+    case = Q4Case(w, [5000])
+    assert np.array_equal(case.cache.k_pool.cpu().numpy(), case.k_ref)
+    _check_q4(case, split_keys)
+
+
+def test_planted_key_recalled(kvq):
+    """The planted key (K = the group's first query) dominates its heads."""
+    w = wl.shrink(wl.GQA_262K, n_layers=1, seq_len=6000, plant_at=3000)
+    case = Q4Case(w, [6000])
+    o, _ = case.gpu_attention(2048)
+    ro, _ = case.ref_attention()
+    assert rel_err(o, ro).max() < TOL
+    # the output of each group's first head is close to the planted value
+    vrow = case.v_ref[3000 // 16, :, 3000 % 16]
+    v_planted = oracle.rotate_f64(oracle.q4_decode_rows(vrow, w.head_dim))
+    for g in range(w.n_kv_heads):
+        h = g * w.group
+        assert np.linalg.norm(o[0, h] - v_planted[g]) < 0.25 * np.linalg.norm(v_planted[g])
+
+
+def test_ragged_batch_paged(kvq):
+    """Ragged lengths (incl. 0, 1, page and split edges) over a shuffled page table."""
+    w = wl.shrink(wl.RAGGED, prefill_chunk=0)
+    lens = [0, 1, 16, 17, 511, 512, 513, 2047, 2048, 2049, 4100, 777]
+    case = Q4Case(w, lens)
+    assert np.array_equal(case.cache.k_pool.cpu().numpy(), case.k_ref)
+    _check_q4(case, 512)
+    _check_q4(case, 2048)
+
+
+def test_batch_invariance(kvq):
+    """A sequence's output does not depend on the batch around it: solo and
+    batched runs are bit-identical (TensorFold "What it is": concurrent
+    replies equal solo runs)."""
+    w = wl.shrink(wl.RAGGED, prefill_chunk=0)
+    lens = [3000, 700, 4500]
+    batch = Q4Case(w, lens, build_oracle=False)
+    ob, lb = batch.gpu_attention(1024)
+    import fp8_quantized_kv_amd as kvq_mod
+    for b, T in enumerate(lens):
+        pt = batch.page_table[b:b + 1].contiguous()
+        sl = batch.seq_lens[b:b + 1].contiguous()
+        q_rot = kvq_mod.kvq_rotate_q(batch.q[b:b + 1].contiguous())
+        # solo run with a larger max_seq_len than needed: still identical
+        for max_len in (T, max(lens)):
+            pa, pm, pz = kvq_mod.kvq_decode_attn(batch.cache, q_rot, pt, sl, max_len, w.sm_scale, 1024)
+            o, l = kvq_mod.kvq_merge(batch.cache, pa, pm, pz, sl, max_len, 1024)
+            assert np.array_equal(o.cpu().numpy()[0], ob[b]) and np.array_equal(l.cpu().numpy()[0], lb[b])
+
+
+def test_mha_and_large_group(kvq):
+    """Group sizes 1 (plain multi-head) and 16 (the largest the kernels take)."""
+    for hq, hkv in ((3, 3), (16, 1)):
+        w = wl.shrink(wl.GQA_32K, n_layers=1, seq_len=1500, n_q_heads=hq, n_kv_heads=hkv, heavy_channels=8)
+        _check_q4(Q4Case(w, [1500]), 512)
+
+
+def test_empty_splits_are_written_empty(kvq):
+    w = wl.shrink(wl.RAGGED, prefill_chunk=0)
+    case = Q4Case(w, [600, 3000], build_oracle=False)
+    import fp8_quantized_kv_amd as kvq_mod
+    q_rot = kvq_mod.kvq_rotate_q(case.q)
+    pa, pm, pz = kvq_mod.kvq_decode_attn(case.cache, q_rot, case.page_table, case.seq_lens, 3000, w.sm_scale, 512)
+    pa, pm, pz = pa.cpu(), pm.cpu(), pz.cpu()
+    assert torch.all(pz[0, :, 2:] == 0) and torch.all(torch.isneginf(pm[0, :, 2:])) and torch.all(pa[0, :, 2:] == 0)
+    assert torch.all(pz[0, :, :2] >= 1) and torch.all(pz[1] >= 1)
+
+
+# ----------------------------------------------------------------- fp8 latent decode
+
+def test_mla_small(kvq):
+    w = wl.shrink(wl.MLA_262K, n_heads=20, seq_len=0)
+    lens = [3000, 1, 0, 1025]
+    case = MlaCase(w, lens)
+    assert np.array_equal(case.cache.codes.cpu().numpy(), case.codes_ref)
+    for split in (1024, 2048):
+        o, lse = case.gpu_attention(split)
+        ro, rl = case.ref_attention()
+        err = rel_err(o, ro)
+        _say(f"  mla lens={lens} split={split} max_rel_err={err.max():.2e}")
+        assert err.max() < TOL
+        fin = np.isfinite(rl)
+        assert np.array_equal(fin, np.isfinite(lse)) and np.max(np.abs(lse[fin] - rl[fin])) < 1e-3
+        assert np.all(o[2] == 0)
+
+
+def test_mla_nan_codes_read_zero(kvq):
+    """Codes 0x7F/0xFF (e4m3 NaN) in a cache read as 0 (colibri correctness
+    commit: the CPU table reads 0 for NaN codes)."""
+    w = wl.shrink(wl.MLA_262K, n_heads=16, seq_len=0)
+    case = MlaCase(w, [700])
+    case.cache.codes[5, 10] = 0x7F
+    case.cache.codes[9, 537] = 0xFF
+    case.codes_ref[5, 10] = 0x7F
+    case.codes_ref[9, 537] = 0xFF
+    o, _ = case.gpu_attention(1024)
+    ro, _ = case.ref_attention()
+    assert rel_err(o, ro).max() < TOL
+    assert np.all(np.isfinite(o))
