@@ -39,12 +39,24 @@ def test_dense_gqa_full(kvq, name):
     assert err.max() < TOL
     assert np.max(np.abs(lse - rl)) < 1e-3 * max(1.0, np.abs(rl).max())
     if w.plant_at is not None:
-        # the planted key is recalled: its value dominates each group's first head
-        vrow = case.v_ref[w.plant_at // 16, :, w.plant_at % 16]
-        v_planted = oracle.rotate_f64(oracle.q4_decode_rows(vrow, w.head_dim))
+        # The planted key (K = the group's first query) keeps its score through
+        # the 4-bit rotated encoding: within 3% of the exact |q|^2 * sm_scale.
+        # Whether it wins the softmax depends on the data, not on the kernels:
+        # the Student-t(3) channels give a few random keys scores above it
+        # (one KV head has a key at 21.4 against the needle's 14.3), so
+        # neither its rank nor its weight is asserted; both are printed.
+        q = case.q.cpu().double().numpy()
+        T, j = w.seq_len, np.arange(w.seq_len)
         for g in range(w.n_kv_heads):
             h = g * w.group
-            assert np.linalg.norm(o[0, h] - v_planted[g]) < 0.25 * np.linalg.norm(v_planted[g])
+            K = oracle.q4_decode_rows(case.k_ref[j // 16, g, j % 16], w.head_dim)
+            s = w.sm_scale * (K @ oracle.rotate_f64(q[0, h]))
+            exact = w.sm_scale * float(q[0, h] @ q[0, h])
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            _say(f"  kv head {g}: planted score {s[w.plant_at]:.3f} (exact {exact:.3f}), weight {p[w.plant_at]:.3f}, "
+                 f"best other {np.max(np.delete(s, w.plant_at)):.3f}")
+            assert abs(s[w.plant_at] - exact) < 0.03 * exact
 
 
 def test_ragged_full_with_prefill_chunk(kvq):
