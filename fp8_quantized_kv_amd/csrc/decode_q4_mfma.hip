@@ -1,0 +1,397 @@
+// decode_q4_mfma.hip -- split-K decode over the 4-bit Hadamard-32 cache with
+// matrix cores (gfx950 v_mfma_f32_16x16x32_f16).
+//
+// Method: TensorFold issue "qwen27 CUDA: an opt-in 4-bit attention cache",
+// section "What it is" (attend in rotated space over the 4-bit cache in
+// chunks, merge in order); colibri pull request "KV cache quantization: fp8
+// (KV8) + 4-bit TurboQuant", split-T commit (partial blocks per (head,
+// split) writing (cl[K], m, z)).  The query arrives rotated (kvq_rotate_q).
+//
+// Why matrix cores: per (key, KV head) the G = 6 query heads of a group need
+// 2 x 6 x 256 multiply-adds against only 288 bytes of cache, which the fp32
+// vector units cannot keep up with at HBM speed.  With the heads as the
+// 16-wide M dimension the score and context products become 16x16x32 MFMAs,
+// and the vector units are left with unpacking, scaling and the softmax.
+//
+// Workgroup = 4 waves = (split s, KV head g, sequence b); each wave streams
+// its own quarter of the split in 32-key sub-tiles and keeps its own online
+// softmax; the four are merged in LDS at the end into one partial.
+//
+// Per sub-tile:
+//  * DMA: the sub-tile's K and V rows (two 16-row page runs per pool) are
+//    copied global -> LDS with global_load_lds_dwordx4, double-buffered per
+//    wave, issued two sub-tiles ahead and waited for with s_waitcnt vmcnt.
+//  * Scores: for each 16-key block and 32-channel group, A = the keys' codes
+//    (lane (key n, quarter q) holds code dword 4*group + q of key n), B = the
+//    pre-scaled query split into f16 hi + lo parts (two MFMAs).  Codes enter
+//    as f16 subnormals: (nibble ^ 8) masked into place is (code + 8) * 2^-24
+//    (or x16 for the high nibble of a byte, compensated in B), so unpacking a
+//    dword of 8 codes takes 6 integer ops.  The +8 offset is removed by the
+//    MFMA's C input (-8 * 2^-24 * sum of the group's query), and the group's
+//    fp16 scale is applied per key with one mixed-precision FMA.
+//  * Softmax: lane (head h, quarter q) holds 8 scores of head h; the running
+//    maximum only moves when a tile exceeds it by more than 2^6, so the
+//    accumulators are rescaled a handful of times per split, not per tile.
+//  * Context: ds_read_b64_tr_b4 transposes a 16x16 tile of nibbles so that
+//    lane (channel n, quarter q) receives channel n of the 8 keys it needs
+//    as MFMA k-slots; the same 6-op unpack makes the B operand.  A = P times
+//    the keys' V scale for the group (f16), and a second MFMA against a
+//    constant B removes the +8 offset.
+#include "internal.h"
+
+#pragma clang diagnostic ignored "-Winline-asm"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kSub = 32;          // keys per sub-tile
+constexpr int kMaxRuns = 128;     // 16-key runs per wave (split_keys <= 8192)
+constexpr float kTwo24 = 16777216.0f;
+constexpr float kRescale = 6.0f;  // log2 headroom before the running max moves
+
+template <int D>
+struct Shape {
+    static constexpr int NG = D / 32;               // 32-channel groups per row
+    static constexpr int RB = D / 2 + D / 16;       // row bytes
+    static constexpr int NB = D / 16;               // 16-channel output blocks
+    static constexpr int RUN = 16 * RB;             // bytes of 16 rows (one run)
+    static constexpr int RUN_INSTR = (RUN / 16 + 63) / 64;  // 16-byte DMA instructions per run
+    static constexpr int TILE = kSub * RB;          // bytes of a sub-tile, one pool
+    static constexpr int STAGE = 2 * TILE;          // K then V
+    static constexpr int DMA_PER_SUB = 4 * RUN_INSTR;
+    static constexpr int LDS = kWaves * 2 * STAGE;
+};
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return uint32_t(uintptr_t((__attribute__((address_space(3))) const void*)(p)));
+}
+
+// 16 bytes per lane from global (SGPR base + VGPR offset) to LDS at
+// m0 + 16 * lane.  Issued from asm so the compiler does not serialise it.
+// base and lds must be wave-uniform; they are moved to SGPRs here.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
+    const uint64_t b = uint64_t(uintptr_t(base));
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(b));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(b >> 32));
+    const uint64_t sb = (uint64_t(hi) << 32) | lo;
+    const uint32_t sl = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(sl)
+                 : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Copies one 16-row run (RUN bytes) from global to LDS.
+template <int D>
+__device__ __forceinline__ void dma_run(const uint8_t* src, uint32_t lds, int lane) {
+    using S = Shape<D>;
+#pragma unroll
+    for (int i = 0; i < S::RUN_INSTR; ++i) {
+        const int chunk = i * 64 + lane;
+        if (i + 1 < S::RUN_INSTR || chunk < S::RUN / 16)
+            dma16(src, uint32_t(chunk * 16), lds + uint32_t(i * 1024));
+    }
+}
+
+// 8 codes of a dword as MFMA k-slots: (c0,c4) (c1,c5)x16 (c2,c6) (c3,c7)x16,
+// each the f16 subnormal (code + 8) * 2^-24 (x16 where marked).
+__device__ __forceinline__ half8_t unpack8(uint32_t w) {
+    w ^= 0x88888888u;
+    const uint32_t w2 = w >> 8;
+    const u32x4 r = {w & 0x000F000Fu, w & 0x00F000F0u, w2 & 0x000F000Fu, w2 & 0x00F000F0u};
+    return __builtin_bit_cast(half8_t, r);
+}
+
+__device__ __forceinline__ f32x4 mfma(half8_t a, half8_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float lo_half(uint32_t w) { return float(__builtin_bit_cast(half2_t, w)[0]); }
+__device__ __forceinline__ float hi_half(uint32_t w) { return float(__builtin_bit_cast(half2_t, w)[1]); }
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* __restrict__ k_pool,
+                                                                  const uint8_t* __restrict__ v_pool, int H,
+                                                                  int page_size, int num_pages, DecodeArgs a) {
+    using S = Shape<D>;
+    constexpr int NG = S::NG, RB = S::RB, NB = S::NB;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS];
+    __shared__ int64_t run_off[kWaves][kMaxRuns];
+
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n16 = lane & 15, q4 = lane >> 4;  // MFMA column / row-quarter of this lane
+    const int G = a.n_q_heads / H;
+    const int Sn = a.n_splits;
+    int T = a.seq_lens[b];
+    T = T < 0 ? 0 : (T > a.max_seq_len ? a.max_seq_len : T);
+    const int j0 = s * a.split_keys;
+    const int j1 = min(j0 + a.split_keys, T);
+    const int64_t hb = int64_t(b) * a.n_q_heads + int64_t(g) * G;
+
+    if (j0 >= j1) {  // split past the end: an empty partial
+        for (int i = tid; i < G * D; i += kWaves * 64) a.part_acc[((hb + i / D) * Sn + s) * D + i % D] = 0.0f;
+        if (tid < G) {
+            a.part_m[(hb + tid) * Sn + s] = -INFINITY;
+            a.part_z[(hb + tid) * Sn + s] = 0.0f;
+        }
+        return;
+    }
+
+    // This wave's keys: a contiguous quarter of the split.
+    const int kq = a.split_keys / kWaves;
+    const int w0 = j0 + wave * kq;
+    const int w1 = min(w0 + kq, j1);
+    const int n_keys = w1 > w0 ? w1 - w0 : 0;
+    const int n_sub = (n_keys + kSub - 1) / kSub;
+
+    // Byte offset (within a pool) of every 16-row run of this wave; runs past
+    // the last key repeat the last valid run so every copy stays in bounds.
+    const int32_t* pt = a.page_table + int64_t(b) * a.max_pages;
+    const int last_run = n_keys > 0 ? (n_keys - 1) / 16 : 0;
+    for (int r = lane; r < 2 * n_sub; r += 64) {
+        const int pos = w0 + 16 * min(r, last_run);
+        int page = pt[pos / page_size];
+        page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+        run_off[wave][r] = ((int64_t(page) * H + g) * page_size + pos % page_size) * RB;
+    }
+
+    // B operands of the score MFMAs: pre-scaled query (log2 units) of head
+    // n16 for the 8 channels that k-slots (q4, 0..7) of each group hold,
+    // split into f16 hi + lo.  Slot order (c0,c4,c1,c5,c2,c6,c3,c7) of the
+    // dword 8*q4..8*q4+7 of the group; slots 2,3,6,7 carry x16 in A, so /16 here.
+    half8_t bq_hi[NG], bq_lo[NG];
+    f32x4 cbias[NG];
+    {
+        const float qscale = a.sm_scale * kLog2e;
+        const bool live = n16 < G;
+        const float* qh = a.q + (hb + (live ? n16 : 0)) * D;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            float v[8];
+            const float4 lo4 = *reinterpret_cast<const float4*>(qh + 32 * gi + 8 * q4);
+            const float4 hi4 = *reinterpret_cast<const float4*>(qh + 32 * gi + 8 * q4 + 4);
+            const float c8[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+            constexpr int order[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+            float sum = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float f = (k & 2) ? 0.0625f : 1.0f;
+                v[k] = live ? c8[order[k]] * qscale * f : 0.0f;
+                const _Float16 h = _Float16(v[k]);
+                const _Float16 l = _Float16(v[k] - float(h));
+                bq_hi[gi][k] = h;
+                bq_lo[gi][k] = l;
+                sum += (float(h) + float(l)) * ((k & 2) ? 16.0f : 1.0f);
+            }
+            sum += __shfl_xor(sum, 16, 64);
+            sum += __shfl_xor(sum, 32, 64);
+            const float bias = -8.0f * sum / kTwo24;
+            cbias[gi] = f32x4{bias, bias, bias, bias};
+        }
+    }
+    // Constant B of the context offset MFMA: -8 * 2^-24 (x16 on slots 2,3,6,7).
+    half8_t bconst;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) bconst[k] = _Float16((k & 2) ? -128.0f / kTwo24 : -8.0f / kTwo24);
+
+    f32x4 o[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY;  // running max (log2 units) of head n16
+    float z_run = 0.0f;       // this lane's share of the running sum
+
+    uint8_t* stage0 = smem + wave * 2 * S::STAGE;
+    const uint32_t lds0 = lds_addr(stage0);
+    __syncthreads();  // run_off visible
+
+    auto issue = [&](int t) {
+        const int st = t & 1;
+        const uint32_t dst = lds0 + uint32_t(st * S::STAGE);
+        const int64_t r0 = run_off[wave][2 * t], r1 = run_off[wave][2 * t + 1];
+        wait_lgkm0();
+        dma_run<D>(k_pool + r0, dst, lane);
+        dma_run<D>(k_pool + r1, dst + S::RUN, lane);
+        dma_run<D>(v_pool + r0, dst + S::TILE, lane);
+        dma_run<D>(v_pool + r1, dst + S::TILE + S::RUN, lane);
+    };
+
+    if (n_sub > 0) issue(0);
+    if (n_sub > 1) issue(1);
+
+    // tr_b4 row address of this lane: key K(q4, e) for e = n16 & 7, where
+    // K(q, e) = 4q + e (e < 4) or 16 + 4q + e - 4, at channel half n16 >> 3.
+    const int e7 = n16 & 7;
+    const int tr_key = e7 < 4 ? 4 * q4 + e7 : 16 + 4 * q4 + e7 - 4;
+    const int tr_off = S::TILE + tr_key * RB + 8 * (n16 >> 3);
+
+    for (int t = 0; t < n_sub; ++t) {
+        if (t + 1 < n_sub) wait_vmcnt<S::DMA_PER_SUB>();
+        else wait_vmcnt<0>();
+        const uint8_t* kt = stage0 + (t & 1) * S::STAGE;
+        const int valid = min(kSub, n_keys - t * kSub);
+
+        // ---- scores: two 16-key blocks; lane holds keys 16*kb + 4*q4 + i of head n16
+        float sc[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const uint8_t* arow = kt + (16 * kb + n16) * RB;
+            u32x4 ks[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ks[i] = *reinterpret_cast<const u32x4*>(kt + (16 * kb + 4 * q4 + i) * RB + D / 2);
+            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const uint32_t w = *reinterpret_cast<const uint32_t*>(arow + 16 * gi + 4 * q4);
+                const half8_t av = unpack8(w);
+                f32x4 d = mfma(av, bq_hi[gi], cbias[gi]);
+                d = mfma(av, bq_lo[gi], d);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t sw = ks[i][gi >> 1];
+                    acc[i] = fmaf(d[i], (gi & 1) ? hi_half(sw) : lo_half(sw), acc[i]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = 16 * kb + 4 * q4 + i;
+                sc[kb][i] = key < valid ? acc[i] * kTwo24 : -INFINITY;
+            }
+        }
+
+        // ---- online softmax over the tile (per head = per column n16)
+        float tmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                           fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const bool move = tmax > m_run + kRescale || m_run == -INFINITY;
+        if (__builtin_amdgcn_ballot_w64(move) != 0ull) {
+            const float m_new = move ? fmaxf(m_run, tmax) : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+            z_run *= alpha;
+            m_run = m_new;
+            float al[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * q4 + i, 64);  // rows 4*q4+i are heads
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[blk][i] *= al[i];
+        }
+        // p for keys of slots 2,3,6,7 (i = 1, 3) is taken /16 to undo the x16
+        // those V codes carry.
+        float p[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[kb][i] = __builtin_amdgcn_exp2f(sc[kb][i] - m_run - ((i & 1) ? 4.0f : 0.0f));
+                z_run += (i & 1) ? 16.0f * p[kb][i] : p[kb][i];
+            }
+        half2_t pp[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pp[r] = half2_t{_Float16(p[0][r]), _Float16(p[1][r])};
+
+        // ---- context: per group, two 16-channel blocks
+        const uint8_t* vt = kt + S::TILE;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            const i32x2 cv = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+                (__attribute__((address_space(3))) i32x2*)(kt + tr_off + 16 * gi));
+            // scale pair (key 4q+r, key 16+4q+r) of group gi, r = 0..3
+            half8_t av;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t sa = *reinterpret_cast<const uint32_t*>(vt + (4 * q4 + r) * RB + D / 2 + 4 * (gi >> 1));
+                const uint32_t sb = *reinterpret_cast<const uint32_t*>(vt + (16 + 4 * q4 + r) * RB + D / 2 + 4 * (gi >> 1));
+                const uint32_t pair = (gi & 1) ? __builtin_amdgcn_perm(sb, sa, 0x07060302u)
+                                               : __builtin_amdgcn_perm(sb, sa, 0x05040100u);
+                const half2_t w = pp[r] * __builtin_bit_cast(half2_t, pair);
+                av[2 * r] = w[0];
+                av[2 * r + 1] = w[1];
+            }
+            const half8_t b0 = unpack8(uint32_t(cv[0]));
+            const half8_t b1 = unpack8(uint32_t(cv[1]));
+            o[2 * gi] = mfma(av, b0, o[2 * gi]);
+            o[2 * gi] = mfma(av, bconst, o[2 * gi]);
+            o[2 * gi + 1] = mfma(av, b1, o[2 * gi + 1]);
+            o[2 * gi + 1] = mfma(av, bconst, o[2 * gi + 1]);
+        }
+        if (t + 2 < n_sub) issue(t + 2);
+    }
+
+    // ---- per-wave results: m (log2), z per head; o rows = heads 4*q4 + i
+    z_run += __shfl_xor(z_run, 16, 64);
+    z_run += __shfl_xor(z_run, 32, 64);
+    __syncthreads();  // every wave is done with its tile buffers
+    float* wo = reinterpret_cast<float*>(smem);         // [kWaves][16][D]
+    float* wm = wo + kWaves * 16 * D;                     // [kWaves][16]
+    float* wz = wm + kWaves * 16;                         // [kWaves][16]
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wo[(wave * 16 + 4 * q4 + i) * D + 16 * blk + n16] = o[blk][i] * kTwo24;
+    if (lane < 16) {
+        wm[wave * 16 + lane] = n_keys > 0 ? m_run : -INFINITY;
+        wz[wave * 16 + lane] = n_keys > 0 ? z_run : 0.0f;
+    }
+    __syncthreads();
+    for (int i = tid; i < G * D; i += kWaves * 64) {
+        const int h = i / D, c = i % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w * 16 + h]);
+        float acc = 0.0f, Z = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float zw = wz[w * 16 + h];
+            if (zw > 0.0f) {
+                const float f = __builtin_amdgcn_exp2f(wm[w * 16 + h] - M);
+                acc += wo[(w * 16 + h) * D + c] * f;
+                Z += zw * f;
+            }
+        }
+        a.part_acc[((hb + h) * Sn + s) * D + c] = acc;
+        if (c == 0) {
+            a.part_m[(hb + h) * Sn + s] = M * kLn2;
+            a.part_z[(hb + h) * Sn + s] = Z;
+        }
+    }
+}
+
+}  // namespace
+
+bool decode_q4_mfma_supported(const Q4Pool& pool, const DecodeArgs& a) {
+    const int G = a.n_q_heads / pool.n_kv_heads;
+    return (pool.head_dim == 128 || pool.head_dim == 256) && G >= 1 && G <= 16 && pool.page_size % 16 == 0 &&
+           a.split_keys % 128 == 0 && a.split_keys / kWaves <= 16 * kMaxRuns;
+}
+
+hipError_t launch_decode_q4_mfma(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s) {
+    const dim3 grid(unsigned(a.n_splits), unsigned(pool.n_kv_heads), unsigned(a.batch)), block(kWaves * 64);
+    switch (pool.head_dim) {
+        case 128:
+            decode_q4_mfma<128><<<grid, block, 0, s>>>(pool.k, pool.v, pool.n_kv_heads, pool.page_size, pool.num_pages, a);
+            break;
+        case 256:
+            decode_q4_mfma<256><<<grid, block, 0, s>>>(pool.k, pool.v, pool.n_kv_heads, pool.page_size, pool.num_pages, a);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvq

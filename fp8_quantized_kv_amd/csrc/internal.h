@@ -80,6 +80,11 @@ struct DecodeArgs {
     float* part_z;
 };
 
+// Matrix-core kernel for the 4-bit cache (head_dim 128/256, pages of a
+// multiple of 16 tokens, groups of up to 16 query heads, split_keys <= 8192).
+bool decode_q4_mfma_supported(const Q4Pool& pool, const DecodeArgs& a);
+hipError_t launch_decode_q4_mfma(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s);
+
 // Plain fp32 vector-math kernels (any supported head_dim).
 hipError_t launch_decode_q4_simple(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_fp8_simple(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s);

@@ -143,7 +143,11 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_h
         return KVQ_ERR_INVALID_ARG;
     kvq::DecodeArgs a{q, n_q_heads, page_table, max_pages, seq_lens, batch, max_seq_len,
                       kvq_num_splits(max_seq_len, split_keys), sm_scale, split_keys, part_acc, part_m, part_z};
-    if (cache->format == KVQ_FMT_Q4_H32) return launched(kvq::launch_decode_q4_simple(q4_pool(cache), a, stream));
+    if (cache->format == KVQ_FMT_Q4_H32) {
+        const kvq::Q4Pool pool = q4_pool(cache);
+        if (kvq::decode_q4_mfma_supported(pool, a)) return launched(kvq::launch_decode_q4_mfma(pool, a, stream));
+        return launched(kvq::launch_decode_q4_simple(pool, a, stream));
+    }
     return launched(kvq::launch_decode_fp8_simple(fp8_pool(cache), a, stream));
 }
 

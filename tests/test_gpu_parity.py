@@ -218,6 +218,16 @@ def test_mha_and_large_group(kvq):
         _check_q4(Q4Case(w, [1500]), 512)
 
 
+@pytest.mark.parametrize("D,page_size,hq,hkv", [(512, 16, 8, 2), (256, 8, 12, 2), (64, 16, 4, 4), (128, 32, 10, 1)])
+def test_other_shapes(kvq, D, page_size, hq, hkv):
+    """Head sizes and page sizes on both kernel paths (the matrix-core kernel
+    takes head_dim 128/256 with pages of a multiple of 16 tokens; the others
+    run on the plain kernel)."""
+    w = wl.shrink(wl.RAGGED, prefill_chunk=0, head_dim=D, page_size=page_size, n_q_heads=hq, n_kv_heads=hkv,
+                  heavy_channels=D // 16)
+    _check_q4(Q4Case(w, [1300, 2600, 40]), 1024)
+
+
 def test_empty_splits_are_written_empty(kvq):
     w = wl.shrink(wl.RAGGED, prefill_chunk=0)
     case = Q4Case(w, [600, 3000], build_oracle=False)
