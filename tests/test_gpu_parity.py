@@ -148,14 +148,16 @@ def test_tiny_workload(kvq):
 
 def test_tiny_partials_match_oracle_chunks(kvq):
     """The GPU partials at 512-key splits match the oracle's 512-key chunk
-    partials (m, z and acc), so the merge has the same inputs on both sides."""
+    partials.  A partial (m, z, acc) may use any reference m (the kernels
+    move m lazily), so compare what does not depend on it: the chunk's
+    log-sum-exp m + log z and its normalized context acc / z."""
     w = wl.TINY
     case = Q4Case(w, [w.seq_len])
     _, _, (pa, pm, pz) = case.gpu_attention(512, want_partials=True)
     _, _, (ra, rm, rz) = case.ref_attention(chunk=512, return_partials=True)
-    assert np.max(np.abs(pm - rm)) < 1e-4 * max(1, np.abs(rm).max())
-    assert np.max(np.abs(pz - rz) / rz) < 1e-4
-    assert np.max(np.abs(pa - ra)) < 1e-4 * np.abs(ra).max()
+    assert np.max(np.abs((pm + np.log(pz)) - (rm + np.log(rz)))) < 1e-3
+    na, nr = pa / pz[..., None], ra / rz[..., None]
+    assert rel_err(na, nr).max() < TOL
 
 
 @pytest.mark.parametrize("split_keys", [512, 1024, 2048])
