@@ -108,10 +108,25 @@ __device__ __forceinline__ void dma_run(const uint8_t* src, uint32_t lds, int la
 // 8 codes of a dword as MFMA k-slots: (c0,c4) (c1,c5)x16 (c2,c6) (c3,c7)x16,
 // each the f16 subnormal (code + 8) * 2^-24 (x16 where marked).
 __device__ __forceinline__ half8_t unpack8(uint32_t w) {
-    w ^= 0x88888888u;
+    constexpr uint32_t X = 0x88888888u;  // two's complement -> offset binary, per nibble
     const uint32_t w2 = w >> 8;
-    const u32x4 r = {w & 0x000F000Fu, w & 0x00F000F0u, w2 & 0x000F000Fu, w2 & 0x00F000F0u};
+    const u32x4 r = {(w ^ X) & 0x000F000Fu, (w ^ X) & 0x00F000F0u, (w2 ^ X) & 0x000F000Fu, (w2 ^ X) & 0x00F000F0u};
     return __builtin_bit_cast(half8_t, r);
+}
+
+// Max / sum of a value over the four lanes l, l^16, l^32, l^48 with
+// cross-lane moves on the vector ALU (no LDS round trip).
+__device__ __forceinline__ float quad_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ f32x4 mfma(half8_t a, half8_t b, f32x4 c) {
@@ -157,8 +172,20 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
     const int n_keys = w1 > w0 ? w1 - w0 : 0;
     const int n_sub = (n_keys + kSub - 1) / kSub;
 
+    // The query of head n16 (log2-scaled later), loaded first so its latency
+    // overlaps the page-table reads and the first copies.
+    const bool live = n16 < G;
+    const float* qh = a.q + (hb + (live ? n16 : 0)) * D;
+    float4 qv[NG][2];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        qv[gi][0] = *reinterpret_cast<const float4*>(qh + 32 * gi + 8 * q4);
+        qv[gi][1] = *reinterpret_cast<const float4*>(qh + 32 * gi + 8 * q4 + 4);
+    }
+
     // Byte offset (within a pool) of every 16-row run of this wave; runs past
     // the last key repeat the last valid run so every copy stays in bounds.
+    // Each wave reads back only entries its own lanes wrote.
     const int32_t* pt = a.page_table + int64_t(b) * a.max_pages;
     const int last_run = n_keys > 0 ? (n_keys - 1) / 16 : 0;
     for (int r = lane; r < 2 * n_sub; r += 64) {
@@ -168,6 +195,21 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
         run_off[wave][r] = ((int64_t(page) * H + g) * page_size + pos % page_size) * RB;
     }
 
+    uint8_t* stage0 = smem + wave * 2 * S::STAGE;
+    const uint32_t lds0 = lds_addr(stage0);
+    auto issue = [&](int t) {
+        const int st = t & 1;
+        const uint32_t dst = lds0 + uint32_t(st * S::STAGE);
+        const int64_t r0 = run_off[wave][2 * t], r1 = run_off[wave][2 * t + 1];
+        wait_lgkm0();
+        dma_run<D>(k_pool + r0, dst, lane);
+        dma_run<D>(k_pool + r1, dst + S::RUN, lane);
+        dma_run<D>(v_pool + r0, dst + S::TILE, lane);
+        dma_run<D>(v_pool + r1, dst + S::TILE + S::RUN, lane);
+    };
+    if (n_sub > 0) issue(0);
+    if (n_sub > 1) issue(1);
+
     // B operands of the score MFMAs: pre-scaled query (log2 units) of head
     // n16 for the 8 channels that k-slots (q4, 0..7) of each group hold,
     // split into f16 hi + lo.  Slot order (c0,c4,c1,c5,c2,c6,c3,c7) of the
@@ -176,28 +218,23 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
     f32x4 cbias[NG];
     {
         const float qscale = a.sm_scale * kLog2e;
-        const bool live = n16 < G;
-        const float* qh = a.q + (hb + (live ? n16 : 0)) * D;
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
-            float v[8];
-            const float4 lo4 = *reinterpret_cast<const float4*>(qh + 32 * gi + 8 * q4);
-            const float4 hi4 = *reinterpret_cast<const float4*>(qh + 32 * gi + 8 * q4 + 4);
+            const float4 lo4 = qv[gi][0], hi4 = qv[gi][1];
             const float c8[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
             constexpr int order[8] = {0, 4, 1, 5, 2, 6, 3, 7};
             float sum = 0.0f;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const float f = (k & 2) ? 0.0625f : 1.0f;
-                v[k] = live ? c8[order[k]] * qscale * f : 0.0f;
-                const _Float16 h = _Float16(v[k]);
-                const _Float16 l = _Float16(v[k] - float(h));
+                const float v = live ? c8[order[k]] * qscale * f : 0.0f;
+                const _Float16 h = _Float16(v);
+                const _Float16 l = _Float16(v - float(h));
                 bq_hi[gi][k] = h;
                 bq_lo[gi][k] = l;
                 sum += (float(h) + float(l)) * ((k & 2) ? 16.0f : 1.0f);
             }
-            sum += __shfl_xor(sum, 16, 64);
-            sum += __shfl_xor(sum, 32, 64);
+            sum = quad_sum(sum);
             const float bias = -8.0f * sum / kTwo24;
             cbias[gi] = f32x4{bias, bias, bias, bias};
         }
@@ -212,24 +249,6 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
     for (int i = 0; i < NB; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY;  // running max (log2 units) of head n16
     float z_run = 0.0f;       // this lane's share of the running sum
-
-    uint8_t* stage0 = smem + wave * 2 * S::STAGE;
-    const uint32_t lds0 = lds_addr(stage0);
-    __syncthreads();  // run_off visible
-
-    auto issue = [&](int t) {
-        const int st = t & 1;
-        const uint32_t dst = lds0 + uint32_t(st * S::STAGE);
-        const int64_t r0 = run_off[wave][2 * t], r1 = run_off[wave][2 * t + 1];
-        wait_lgkm0();
-        dma_run<D>(k_pool + r0, dst, lane);
-        dma_run<D>(k_pool + r1, dst + S::RUN, lane);
-        dma_run<D>(v_pool + r0, dst + S::TILE, lane);
-        dma_run<D>(v_pool + r1, dst + S::TILE + S::RUN, lane);
-    };
-
-    if (n_sub > 0) issue(0);
-    if (n_sub > 1) issue(1);
 
     // tr_b4 row address of this lane: key K(q4, e) for e = n16 & 7, where
     // K(q, e) = 4q + e (e < 4) or 16 + 4q + e - 4, at channel half n16 >> 3.
@@ -266,17 +285,20 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = 16 * kb + 4 * q4 + i;
-                sc[kb][i] = key < valid ? acc[i] * kTwo24 : -INFINITY;
-            }
+            for (int i = 0; i < 4; ++i) sc[kb][i] = acc[i];  // log2 units / 2^24
+        }
+        if (valid < kSub) {  // only the last tile of a wave can be partial
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * kb + 4 * q4 + i >= valid) sc[kb][i] = -INFINITY;
         }
 
         // ---- online softmax over the tile (per head = per column n16)
         float tmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                            fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        tmax = quad_max(tmax) * kTwo24;
         const bool move = tmax > m_run + kRescale || m_run == -INFINITY;
         if (__builtin_amdgcn_ballot_w64(move) != 0ull) {
             const float m_new = move ? fmaxf(m_run, tmax) : m_run;
@@ -294,12 +316,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
         // p for keys of slots 2,3,6,7 (i = 1, 3) is taken /16 to undo the x16
         // those V codes carry.
         float p[2][4];
+        const float nm0 = -m_run, nm4 = -m_run - 4.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[kb][i] = __builtin_amdgcn_exp2f(sc[kb][i] - m_run - ((i & 1) ? 4.0f : 0.0f));
-                z_run += (i & 1) ? 16.0f * p[kb][i] : p[kb][i];
+                p[kb][i] = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], kTwo24, (i & 1) ? nm4 : nm0));
+                z_run = (i & 1) ? fmaf(16.0f, p[kb][i], z_run) : z_run + p[kb][i];
             }
         half2_t pp[4];
 #pragma unroll
@@ -334,8 +357,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
     }
 
     // ---- per-wave results: m (log2), z per head; o rows = heads 4*q4 + i
-    z_run += __shfl_xor(z_run, 16, 64);
-    z_run += __shfl_xor(z_run, 32, 64);
+    z_run = quad_sum(z_run);
     __syncthreads();  // every wave is done with its tile buffers
     float* wo = reinterpret_cast<float*>(smem);         // [kWaves][16][D]
     float* wm = wo + kWaves * 16 * D;                     // [kWaves][16]

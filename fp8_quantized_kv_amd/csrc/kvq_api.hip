@@ -58,7 +58,7 @@ kvq_status check_seq_args(const kvq_cache* c, int32_t n_q_heads, const int32_t* 
     if (batch > 0 && !aligned(seq_lens, 4)) return KVQ_ERR_INVALID_ARG;
     if (batch > 65535) return KVQ_ERR_UNSUPPORTED;
     if (c->format == KVQ_FMT_Q4_H32 && n_q_heads / c->num_kv_heads > 16) return KVQ_ERR_UNSUPPORTED;
-    if (kvq_num_splits(max_seq_len, split_keys) > 65535) return KVQ_ERR_UNSUPPORTED;
+    if (kvq_num_splits(max_seq_len, split_keys) > 16384) return KVQ_ERR_UNSUPPORTED;  // merge keeps one weight per split in LDS
     return KVQ_OK;
 }
 

@@ -36,89 +36,95 @@ __global__ __launch_bounds__(256) void rotate_q_kernel(const void* __restrict__ 
     for (int i = 0; i < 8; ++i) o[i] = make_float4(x[4 * i] * c, x[4 * i + 1] * c, x[4 * i + 2] * c, x[4 * i + 3] * c);
 }
 
-constexpr int kMergeThreads = 256;
+constexpr int kMergeWaves = 4;
+constexpr int kMergeCh = 64;   // output channels per workgroup (two Hadamard groups)
 
-// One workgroup per (sequence, query head).  Weights w_s = exp(m_s - M) / Z
-// are formed once per split; each thread then owns output channels and sums
-// acc_s[c] * w_s in ascending s, so the result does not depend on anything
-// but the sequence's own partials.  For the 4-bit cache the rotated-domain
-// sum is rotated back with H32 (its own inverse): out[c] = sum_j H[c%32][j]
-// * O[32*(c/32) + j], H[i][j] = (-1)^popcount(i&j) / sqrt(32).
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part_acc,
-                                                              const float* __restrict__ part_m,
-                                                              const float* __restrict__ part_z,
-                                                              const int32_t* __restrict__ seq_lens, int n_q_heads,
-                                                              int max_seq_len, int S, int split_keys, int dv,
-                                                              int rotate, float* __restrict__ out,
-                                                              float* __restrict__ lse) {
-    extern __shared__ float smem[];  // [S] weights, then [dv] rotated-domain output
-    float* w = smem;
-    float* o_rot = smem + S;
-    __shared__ float red[kMergeThreads / 64];
+// Workgroup (sequence x query head, 64-channel block).  Weights w_s =
+// exp(m_s - M) are formed per used split; wave w sums acc_s[c] * w_s over a
+// contiguous quarter of the splits in ascending order, and the quarters are
+// added in order, so the result depends only on the sequence's own partials.
+// For the 4-bit cache the normalized rotated-domain vector is rotated back
+// with H32 (its own inverse): out[c] = sum_j H[c%32][j] * O[32*(c/32) + j],
+// H[i][j] = (-1)^popcount(i&j) / sqrt(32).
+__global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __restrict__ part_acc,
+                                                                 const float* __restrict__ part_m,
+                                                                 const float* __restrict__ part_z,
+                                                                 const int32_t* __restrict__ seq_lens,
+                                                                 int n_q_heads, int max_seq_len, int S,
+                                                                 int split_keys, int dv, int rotate,
+                                                                 float* __restrict__ out, float* __restrict__ lse) {
+    extern __shared__ float w[];  // [S] split weights
+    __shared__ float part[kMergeWaves][kMergeCh];
+    __shared__ float o_rot[kMergeCh];
+    __shared__ float red[kMergeWaves];
     __shared__ float s_M, s_Z;
 
-    const int bh = blockIdx.x;
+    const int bh = blockIdx.x, c0 = blockIdx.y * kMergeCh;
     const int b = bh / n_q_heads;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     int T = seq_lens[b];
     T = T < 0 ? 0 : (T > max_seq_len ? max_seq_len : T);
     const int n = (T + split_keys - 1) / split_keys;
     float* o = out + int64_t(bh) * dv;
     if (n == 0) {
-        for (int c = tid; c < dv; c += kMergeThreads) o[c] = 0.0f;
-        if (lse && tid == 0) lse[bh] = -INFINITY;
+        if (tid < kMergeCh) o[c0 + tid] = 0.0f;
+        if (lse && blockIdx.y == 0 && tid == 0) lse[bh] = -INFINITY;
         return;
     }
     const float* pm = part_m + int64_t(bh) * S;
     const float* pz = part_z + int64_t(bh) * S;
 
-    // M = max over the used splits (max is exact, so the reduction order is moot).
+    // M = max over the used splits (exact, so the reduction order is moot).
     float mx = -INFINITY;
-    for (int s = tid; s < n; s += kMergeThreads) mx = fmaxf(mx, pm[s]);
+    for (int s = tid; s < n; s += kMergeWaves * 64) mx = fmaxf(mx, pm[s]);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
-    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    if (lane == 0) red[wave] = mx;
     __syncthreads();
-    if (tid == 0) {
-        float M = red[0];
-        for (int i = 1; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[i]);
-        s_M = M;
-    }
+    if (tid == 0) s_M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();
     const float M = s_M;
-    for (int s = tid; s < n; s += kMergeThreads) {
-        const float z = pz[s];
-        w[s] = z > 0.0f ? expf(pm[s] - M) : 0.0f;
-    }
+    for (int s = tid; s < n; s += kMergeWaves * 64) w[s] = pz[s] > 0.0f ? expf(pm[s] - M) : 0.0f;
     __syncthreads();
-    if (tid == 0) {  // Z in ascending split order
-        float Z = 0.0f;
-        for (int s = 0; s < n; ++s) Z += pz[s] * w[s];
-        s_Z = Z;
-    }
-    __syncthreads();
-    const float invZ = 1.0f / s_Z;
-    const float* pa = part_acc + int64_t(bh) * S * dv;
-    for (int c = tid; c < dv; c += kMergeThreads) {
-        float acc = 0.0f;
-        for (int s = 0; s < n; ++s) acc += pa[int64_t(s) * dv + c] * w[s];
-        o_rot[c] = acc * invZ;
-    }
-    __syncthreads();
-    if (rotate) {
-        const float k = inv_sqrt32();
-        for (int c = tid; c < dv; c += kMergeThreads) {
-            const float* blk = o_rot + (c & ~31);
-            const int i = c & 31;
-            float acc = 0.0f;
+    if (wave == 0) {  // Z: lane-strided partial sums in ascending order, then a fixed butterfly
+        float z = 0.0f;
+        for (int s = lane; s < n; s += 64) z += pz[s] * w[s];
 #pragma unroll
-            for (int j = 0; j < 32; ++j) acc += (__popc(unsigned(i & j)) & 1) ? -blk[j] : blk[j];
-            o[c] = acc * k;
-        }
-    } else {
-        for (int c = tid; c < dv; c += kMergeThreads) o[c] = o_rot[c];
+        for (int m = 1; m < 64; m <<= 1) z += __shfl_xor(z, m, 64);
+        if (lane == 0) s_Z = z;
     }
-    if (lse && tid == 0) lse[bh] = M + logf(s_Z);
+    // this wave's contiguous quarter of the splits
+    const int per = (n + kMergeWaves - 1) / kMergeWaves;
+    const int s0 = wave * per, s1 = min(s0 + per, n);
+    const float* pa = part_acc + int64_t(bh) * S * dv + c0 + lane;
+    float acc = 0.0f;
+    int s = s0;
+    for (; s + 8 <= s1; s += 8) {  // eight loads in flight, then the sums in order
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = pa[int64_t(s + k) * dv];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc += v[k] * w[s + k];
+    }
+    for (; s < s1; ++s) acc += pa[int64_t(s) * dv] * w[s];
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (tid < kMergeCh)
+        o_rot[tid] = (((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid]) / s_Z;
+    __syncthreads();
+    if (tid < kMergeCh) {
+        if (rotate) {
+            const float* blk = o_rot + (tid & ~31);
+            const int i = tid & 31;
+            float r = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) r += (__popc(unsigned(i & j)) & 1) ? -blk[j] : blk[j];
+            o[c0 + tid] = r * inv_sqrt32();
+        } else {
+            o[c0 + tid] = o_rot[tid];
+        }
+    }
+    if (lse && blockIdx.y == 0 && tid == 0) lse[bh] = M + logf(s_Z);
 }
 
 }  // namespace
@@ -137,8 +143,9 @@ hipError_t launch_rotate_q(const void* q, InType dt, float* q_rot, int n_rows, i
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
     if (a.batch == 0) return hipSuccess;
-    const size_t shm = sizeof(float) * (size_t(a.n_splits) + size_t(a.dv));
-    merge_kernel<<<dim3(unsigned(a.batch * a.n_q_heads)), dim3(kMergeThreads), shm, s>>>(
+    const size_t shm = sizeof(float) * size_t(a.n_splits);
+    const dim3 grid(unsigned(a.batch * a.n_q_heads), unsigned(a.dv / kMergeCh));
+    merge_kernel<<<grid, dim3(kMergeWaves * 64), shm, s>>>(
         a.part_acc, a.part_m, a.part_z, a.seq_lens, a.n_q_heads, a.max_seq_len, a.n_splits, a.split_keys, a.dv,
         a.rotate ? 1 : 0, a.out, a.lse);
     return hipGetLastError();

@@ -38,9 +38,10 @@
  *    KVQ_ERR_UNSUPPORTED for a valid but unimplemented shape) and launches
  *    nothing.  There is no fallback path.
  *  - Determinism: the split partition of a sequence depends only on its own
- *    length and split_keys, partials are merged in ascending split order, and
- *    no atomics are used, so outputs are bit-reproducible and independent of
- *    the other sequences in the batch.
+ *    length and split_keys, the merge adds the partials in a fixed order that
+ *    depends only on the number of splits, and no atomics are used, so outputs
+ *    are bit-reproducible and independent of the other sequences in the
+ *    batch.
  *  - Device pointers must be 16-byte aligned unless stated otherwise.
  */
 #ifndef KVQ_H
@@ -135,9 +136,9 @@ int32_t kvq_num_splits(int32_t max_seq_len, int32_t split_keys);
  *      not finite or 448/amax is not finite, scale 0 and codes 0x00;
  *      otherwise codes = e4m3_rne_saturating(x * (448/amax)) with NaN -> 0x00,
  *      scale = amax/448.
- * slot_mapping: device int64 [n_tokens]; a negative slot skips the token;
- * every other slot must be < num_pages * page_size (not checked on device).
- * n_tokens = 0 is a no-op.  k/v need 4-byte alignment only. */
+ * slot_mapping: device int64 [n_tokens] (8-byte aligned); a token whose slot
+ * is negative or >= num_pages * page_size is skipped (nothing is written for
+ * it and no error is reported).  n_tokens = 0 is a no-op. */
 kvq_status kvq_store(const kvq_cache* cache, const void* k, const void* v, int32_t dtype,
                      const int64_t* slot_mapping, int32_t n_tokens, hipStream_t stream);
 
@@ -173,7 +174,8 @@ kvq_status kvq_rotate_q(const void* q, int32_t dtype, float* q_rot, int32_t n_ro
  *      rope_dim.  NaN codes (0x7F, 0xFF) read as 0.
  * page_table: device int32 [batch][max_pages]; seq_lens: device int32
  * [batch], each in [0, max_seq_len]; max_seq_len <= max_pages*page_size.
- * split_keys: a positive multiple of 512 (the TensorFold chunk size).
+ * split_keys: a positive multiple of 512 (the TensorFold chunk size); at most
+ * 16384 splits per sequence.
  * part_acc: [batch][n_q_heads][S][Dv] f32, part_m / part_z: [batch][n_q_heads][S]
  * f32 with S = kvq_num_splits(max_seq_len, split_keys).
  * Requires n_q_heads % num_kv_heads == 0 and a group of at most 16 query
@@ -185,9 +187,10 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_h
 
 /* ---------------------------------------------------------------- merge */
 
-/* Log-sum-exp merge of the partials (colibri split-T commit), in ascending
- * split order (TensorFold "What it is": an in-order merge), followed for Q4
- * by the single inverse rotation (H32 is its own inverse):
+/* Log-sum-exp merge of the partials (colibri split-T commit), in split order
+ * (TensorFold "What it is": an in-order merge: the splits are summed in
+ * ascending order within four contiguous blocks, and the blocks in order),
+ * followed for Q4 by the single inverse rotation (H32 is its own inverse):
  *   M = max_s m_s, Z = sum_s z_s exp(m_s - M),
  *   out = R( sum_s acc_s exp(m_s - M) / Z ),  R = H32 (Q4) or identity (FP8),
  *   lse = M + log Z.
