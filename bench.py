@@ -9,10 +9,13 @@ resident in HBM before timing starts; 16 layer caches are cycled so the
 working set (4.8 GB at 262K) is far above the 256 MB Infinity Cache.
 
 Prints one JSON line: whole-step KV-read throughput (algorithmic bytes:
-T x KV heads x (K, V) x 144 B per layer) and microseconds per layer; a
-roofline object for the decode kernel, whose launches are bracketed by HIP
-events on the stream they run on; and the CPU oracle timed on a bounded
-sample of the same workload.
+T x KV heads x (K, V) x 144 B per layer) and microseconds per layer, from
+uninstrumented steps; a roofline object for the decode kernel, from as many
+further steps whose decode launches are bracketed by HIP events on the
+stream they run on (event records stall the queue briefly, so those steps
+are kept out of the step time); side measurements of the 32K 4-bit and the
+262K fp8-latent workloads; and the CPU oracle timed on a bounded sample of
+the headline workload.
 """
 import argparse
 import ctypes
@@ -33,10 +36,34 @@ def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-class Q4Bench:
+class _Bench:
+    """Per-layer raw C-ABI calls of one step: a list of (entry point, args)
+    per layer, with the index of the decode call."""
+
+    DECODE = None
+
+    def step(self, events=None):
+        """Enqueue one step; if events is a list of (start, end) pairs, bracket
+        each decode launch with them (on the stream the kernels run on)."""
+        L = self.kvq.lib
+        for layer, calls in enumerate(self.raw):
+            rc = 0
+            for i, (fn, args) in enumerate(calls):
+                if events is not None and i == self.DECODE:
+                    events[layer][0].record()
+                rc |= getattr(L, fn)(*args)
+                if events is not None and i == self.DECODE:
+                    events[layer][1].record()
+            if rc:
+                raise RuntimeError(f"launch failed in layer {layer}")
+
+
+class Q4Bench(_Bench):
     """Every layer's cache, query and buffers for one 4-bit workload, plus the
     raw C-ABI argument tuples of one step (validated once by building them
-    through the binding's checks)."""
+    through the binding's checks).  Step per layer: store, rotate, decode, merge."""
+
+    DECODE = 2
 
     def __init__(self, w, device="cuda"):
         import numpy as np
@@ -76,86 +103,159 @@ class Q4Bench:
         torch.cuda.synchronize()
         # One checked pass through the binding validates every argument once.
         for layer in range(w.n_layers):
-            self._checked_layer(layer)
+            c = self.caches[layer]
+            kvq.kvq_store(c, self.k_new[layer], self.v_new[layer], self.slot_new)
+            kvq.kvq_rotate_q(self.q[layer], out=self.q_rot)
+            kvq.kvq_decode_attn(c, self.q_rot, self.page_table, self.seq_lens, T, w.sm_scale, w.split_keys,
+                                self.pa, self.pm, self.pz)
+            kvq.kvq_merge(c, self.pa, self.pm, self.pz, self.seq_lens, T, w.split_keys, out=self.out[layer],
+                          lse=self.lse[layer])
         torch.cuda.synchronize()
-        self._build_raw_args()
-
-    def _checked_layer(self, layer):
-        kvq, w = self.kvq, self.w
-        c = self.caches[layer]
-        kvq.kvq_store(c, self.k_new[layer], self.v_new[layer], self.slot_new)
-        kvq.kvq_rotate_q(self.q[layer], out=self.q_rot)
-        kvq.kvq_decode_attn(c, self.q_rot, self.page_table, self.seq_lens, self.T, w.sm_scale, w.split_keys,
-                            self.pa, self.pm, self.pz)
-        kvq.kvq_merge(c, self.pa, self.pm, self.pz, self.seq_lens, self.T, w.split_keys, out=self.out[layer],
-                      lse=self.lse[layer])
-
-    def _build_raw_args(self):
-        import torch
         P = ctypes.c_void_p
-        w = self.w
         stream = P(torch.cuda.current_stream().cuda_stream)
-        self.stream = stream
         self.raw = []
         for layer, c in enumerate(self.caches):
             d = ctypes.byref(c.desc)
-            self.raw.append((
-                (d, P(self.k_new[layer].data_ptr()), P(self.v_new[layer].data_ptr()),
-                 self.kvq._DTYPES[self.k_new[layer].dtype], P(self.slot_new.data_ptr()), 1, stream),
-                (P(self.q[layer].data_ptr()), 0, P(self.q_rot.data_ptr()), w.n_q_heads, w.head_dim, stream),
-                (d, P(self.q_rot.data_ptr()), w.n_q_heads, P(self.page_table.data_ptr()), self.page_table.shape[1],
-                 P(self.seq_lens.data_ptr()), 1, self.T, ctypes.c_float(w.sm_scale), w.split_keys,
-                 P(self.pa.data_ptr()), P(self.pm.data_ptr()), P(self.pz.data_ptr()), stream),
-                (d, P(self.pa.data_ptr()), P(self.pm.data_ptr()), P(self.pz.data_ptr()), P(self.seq_lens.data_ptr()),
-                 1, w.n_q_heads, self.T, w.split_keys, 1, P(self.out[layer].data_ptr()),
-                 P(self.lse[layer].data_ptr()), stream),
-            ))
-
-    def step(self, events=None):
-        """Enqueue one step; if events is a list of (start, end) pairs, bracket each decode launch."""
-        L = self.kvq.lib
-        for layer, (st, rq, dec, mg) in enumerate(self.raw):
-            rc = L.kvq_store(*st) | L.kvq_rotate_q(*rq)
-            if events is not None:
-                events[layer][0].record()
-            rc |= L.kvq_decode_attn(*dec)
-            if events is not None:
-                events[layer][1].record()
-            rc |= L.kvq_merge(*mg)
-            if rc:
-                raise RuntimeError(f"launch failed in layer {layer}")
+            self.raw.append([
+                ("kvq_store", (d, P(self.k_new[layer].data_ptr()), P(self.v_new[layer].data_ptr()),
+                               kvq._DTYPES[self.k_new[layer].dtype], P(self.slot_new.data_ptr()), 1, stream)),
+                ("kvq_rotate_q", (P(self.q[layer].data_ptr()), 0, P(self.q_rot.data_ptr()), w.n_q_heads, w.head_dim,
+                                  stream)),
+                ("kvq_decode_attn", (d, P(self.q_rot.data_ptr()), w.n_q_heads, P(self.page_table.data_ptr()),
+                                     self.page_table.shape[1], P(self.seq_lens.data_ptr()), 1, T,
+                                     ctypes.c_float(w.sm_scale), w.split_keys, P(self.pa.data_ptr()),
+                                     P(self.pm.data_ptr()), P(self.pz.data_ptr()), stream)),
+                ("kvq_merge", (d, P(self.pa.data_ptr()), P(self.pm.data_ptr()), P(self.pz.data_ptr()),
+                               P(self.seq_lens.data_ptr()), 1, w.n_q_heads, T, w.split_keys, 1,
+                               P(self.out[layer].data_ptr()), P(self.lse[layer].data_ptr()), stream)),
+            ])
 
     @property
     def kv_bytes_per_layer(self):
         w = self.w
         return self.T * w.n_kv_heads * 2 * w.row_bytes
 
+    flops_per_layer = None
 
-def time_steps(b, steps, warmup, per_kernel_events=True):
+
+class MlaBench(_Bench):
+    """The fp8 latent workload: every layer's cache and query; step per layer:
+    store the step's token, decode (absorbed attention, split-T), merge."""
+
+    DECODE = 1
+
+    def __init__(self, w, device="cuda"):
+        import numpy as np
+        import torch
+
+        import fp8_quantized_kv_amd as kvq
+        import workloads as wl
+        self.w, self.kvq = w, kvq
+        T = w.seq_len
+        self.T = T
+        lay = wl.page_layout(w, [T])
+        self.page_table = lay.page_table.to(device)
+        self.seq_lens = torch.tensor([T], dtype=torch.int32, device=device)
+        slots_all = wl.slots_for(lay.page_table[0], np.arange(T), w.page_size).to(device)
+        self.caches, self.q, self.x_new = [], [], []
+        chunk = 32768
+        for layer in range(w.n_layers):
+            c = kvq.Fp8Cache(lay.num_pages, w.head_dim, w.rope_dim, w.page_size, device)
+            for t0 in range(0, T, chunk):
+                n = min(chunk, T - t0)
+                x = wl.mla_rows(w, layer, t0, n, device)
+                kvq.kvq_store(c, x, None, slots_all[t0:t0 + n])
+                if t0 + n == T:
+                    self.x_new.append(x[-1:].clone())
+            self.caches.append(c)
+            self.q.append(wl.mla_query(w, layer, device))
+        self.slot_new = slots_all[T - 1:T].clone()
+        acc_shape, mz_shape = kvq.partial_shapes(self.caches[0], 1, w.n_heads, T, w.split_keys)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.pa, self.pm, self.pz = torch.empty(acc_shape, **f32), torch.empty(mz_shape, **f32), torch.empty(mz_shape, **f32)
+        self.out = torch.empty((w.n_layers, 1, w.n_heads, w.kv_lora), **f32)
+        self.lse = torch.empty((w.n_layers, 1, w.n_heads), **f32)
+        torch.cuda.synchronize()
+        for layer in range(w.n_layers):
+            c = self.caches[layer]
+            kvq.kvq_store(c, self.x_new[layer], None, self.slot_new)
+            kvq.kvq_decode_attn(c, self.q[layer], self.page_table, self.seq_lens, T, w.sm_scale, w.split_keys,
+                                self.pa, self.pm, self.pz)
+            kvq.kvq_merge(c, self.pa, self.pm, self.pz, self.seq_lens, T, w.split_keys, out=self.out[layer],
+                          lse=self.lse[layer])
+        torch.cuda.synchronize()
+        P = ctypes.c_void_p
+        stream = P(torch.cuda.current_stream().cuda_stream)
+        self.raw = []
+        for layer, c in enumerate(self.caches):
+            d = ctypes.byref(c.desc)
+            self.raw.append([
+                ("kvq_store", (d, P(self.x_new[layer].data_ptr()), None, kvq._DTYPES[self.x_new[layer].dtype],
+                               P(self.slot_new.data_ptr()), 1, stream)),
+                ("kvq_decode_attn", (d, P(self.q[layer].data_ptr()), w.n_heads, P(self.page_table.data_ptr()),
+                                     self.page_table.shape[1], P(self.seq_lens.data_ptr()), 1, T,
+                                     ctypes.c_float(w.sm_scale), w.split_keys, P(self.pa.data_ptr()),
+                                     P(self.pm.data_ptr()), P(self.pz.data_ptr()), stream)),
+                ("kvq_merge", (d, P(self.pa.data_ptr()), P(self.pm.data_ptr()), P(self.pz.data_ptr()),
+                               P(self.seq_lens.data_ptr()), 1, w.n_heads, T, w.split_keys, 0,
+                               P(self.out[layer].data_ptr()), P(self.lse[layer].data_ptr()), stream)),
+            ])
+
+    @property
+    def kv_bytes_per_layer(self):
+        # 576 code bytes + two f32 scales per position
+        return self.T * (self.w.head_dim + 8)
+
+    @property
+    def flops_per_layer(self):
+        # per position and head: <q, k> over 576 values and the 512-wide value accumulation, 2 flop per MAC
+        w = self.w
+        return self.T * w.n_heads * 2 * (w.head_dim + w.kv_lora)
+
+
+def time_steps(b, steps, warmup):
+    """ms per step of `steps` uninstrumented steps after `warmup` warm-up steps."""
     import torch
     for _ in range(warmup):
         b.step()
     torch.cuda.synchronize()
-    ev = None
-    if per_kernel_events:
-        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(b.w.n_layers)] for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
-    for s in range(steps):
-        b.step(ev[s] if ev else None)
+    for _ in range(steps):
+        b.step()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    dec_ms = None
-    if ev:
-        d = [e0.elapsed_time(e1) for row in ev for (e0, e1) in row]
-        dec_ms = sum(d) / len(d)
-    return total_ms / steps, dec_ms, wall
+    return t_start.elapsed_time(t_end) / steps, wall
+
+
+def time_decode(b, steps):
+    """Average decode launch in ms: `steps` more steps with every decode
+    launch bracketed by HIP events.  (Event records stall the queue for a few
+    microseconds, so these steps are not the ones whose time is reported.)"""
+    import torch
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(b.w.n_layers)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        b.step(ev[s])
+    torch.cuda.synchronize()
+    d = [e0.elapsed_time(e1) for row in ev for (e0, e1) in row]
+    return sum(d) / len(d)
+
+
+def measure(b, steps, warmup):
+    ms_step, wall = time_steps(b, steps, warmup)
+    dec_ms = time_decode(b, steps)
+    kvb = b.kv_bytes_per_layer
+    L = b.w.n_layers
+    r = {"ms_per_step": ms_step, "us_per_layer": ms_step * 1e3 / L, "decode_us": dec_ms * 1e3,
+         "step_gbs": kvb * L / (ms_step * 1e-3) / 1e9, "decode_gbs": kvb / (dec_ms * 1e-3) / 1e9, "wall_s": wall}
+    if b.flops_per_layer:
+        r["decode_tflops"] = b.flops_per_layer / (dec_ms * 1e-3) / 1e12
+    return r
 
 
 def cpu_baseline(w, sample_tokens, repeats=3):
@@ -197,6 +297,7 @@ def main():
     ap.add_argument("--workload", default="gqa_q4_262k")
     ap.add_argument("--cpu-sample-tokens", type=int, default=262144)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the 32K and fp8-latent side measurements")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the decode path is "
@@ -211,28 +312,45 @@ def main():
     torch.cuda.set_device(0)
     _log(f"bench: setting up {w.name} ({w.n_layers} layers, T={w.seq_len})")
     b = Q4Bench(w)
-    _log(f"bench: timing {args.steps} steps after {args.warmup} warm-up steps")
-    ms_step, dec_ms, wall = time_steps(b, args.steps, args.warmup)
+    _log(f"bench: timing {args.steps} steps after {args.warmup} warm-up steps, then {args.steps} event-bracketed steps")
+    m = measure(b, args.steps, args.warmup)
     kvb = b.kv_bytes_per_layer
-    value = kvb * w.n_layers / (ms_step * 1e-3) / 1e9
-    us_layer = ms_step * 1e3 / w.n_layers
-    achieved = kvb / (dec_ms * 1e-3) / 1e9
     rec = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "metric": METRIC, "value": round(m["step_gbs"], 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(m["ms_per_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "layers": w.n_layers, "batch": w.batch, "seq_len": w.seq_len,
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "split_keys": w.split_keys, "kv_bytes_per_layer": kvb},
-        "us_per_layer": round(us_layer, 3),
-        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "roofline": {"kernel": "kvq_decode_attn (4-bit split-K)", "bound": "hbm", "achieved": round(achieved, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "avg_launch_us": round(dec_ms * 1e3, 3), "traffic": None},
-        "wall_s": round(wall, 3),
+        "us_per_layer": round(m["us_per_layer"], 3),
+        "pct_hbm_peak": round(100 * m["step_gbs"] / HBM_PEAK_GBS, 2),
+        "roofline": {"kernel": "kvq_decode_attn (4-bit split-K)", "bound": "hbm",
+                     "achieved": round(m["decode_gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(m["decode_gbs"] / HBM_PEAK_GBS, 4), "avg_launch_us": round(m["decode_us"], 3),
+                     "traffic": None},
+        "wall_s": round(m["wall_s"], 3),
     }
     del b
     torch.cuda.empty_cache()
+    if not args.no_extras:
+        extras = {}
+        for name, cls in (("gqa_q4_32k", Q4Bench), ("mla_fp8_262k", MlaBench)):
+            wx = wl.WORKLOADS[name]
+            _log(f"bench: side measurement {name}")
+            bx = cls(wx)
+            steps = max(3, min(args.steps, 10)) if cls is MlaBench else args.steps
+            mx = measure(bx, steps, args.warmup)
+            e = {"layers": wx.n_layers, "seq_len": wx.seq_len, "split_keys": wx.split_keys, "steps": steps,
+                 "kv_bytes_per_layer": bx.kv_bytes_per_layer, "us_per_layer": round(mx["us_per_layer"], 3),
+                 "step_kv_gbs": round(mx["step_gbs"], 2), "decode_us": round(mx["decode_us"], 3),
+                 "decode_kv_gbs": round(mx["decode_gbs"], 2),
+                 "decode_frac_hbm": round(mx["decode_gbs"] / HBM_PEAK_GBS, 4)}
+            if "decode_tflops" in mx:
+                e["decode_tflops"] = round(mx["decode_tflops"], 2)
+            extras[name] = e
+            del bx
+            torch.cuda.empty_cache()
+        rec["extras"] = extras
     if not args.no_cpu_baseline:
         _log(f"bench: oracle CPU baseline on {args.cpu_sample_tokens} positions")
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)

@@ -19,8 +19,14 @@
 //
 // Per sub-tile:
 //  * DMA: the sub-tile's K and V rows (two 16-row page runs per pool) are
-//    copied global -> LDS with global_load_lds_dwordx4, double-buffered per
-//    wave, issued two sub-tiles ahead and waited for with s_waitcnt vmcnt.
+//    copied global -> LDS with global_load_lds_dwordx4 into per-wave K and V
+//    rings of two sub-tiles each.  The next-but-one K half is issued as soon
+//    as the scores have read the current one, the V half after the context
+//    step, so about one and a half sub-tiles are in flight at all times;
+//    completion is awaited with s_waitcnt vmcnt.  The byte offsets of the
+//    wave's page runs are resolved in the prologue into lane registers (lane
+//    r holds run r), in parallel with the sequence-length load, and read
+//    back with readlane when a copy is issued.
 //  * Scores: for each 16-key block and 32-channel group, A = the keys' codes
 //    (lane (key n, quarter q) holds code dword 4*group + q of key n), B = the
 //    pre-scaled query split into f16 hi + lo parts (two MFMAs).  Codes enter
@@ -64,9 +70,9 @@ struct Shape {
     static constexpr int RUN = 16 * RB;             // bytes of 16 rows (one run)
     static constexpr int RUN_INSTR = (RUN / 16 + 63) / 64;  // 16-byte DMA instructions per run
     static constexpr int TILE = kSub * RB;          // bytes of a sub-tile, one pool
-    static constexpr int STAGE = 2 * TILE;          // K then V
-    static constexpr int DMA_PER_SUB = 4 * RUN_INSTR;
-    static constexpr int LDS = kWaves * 2 * STAGE;
+    static constexpr int HALF = 2 * RUN_INSTR;      // DMA instructions of a sub-tile, one pool
+    static constexpr int WAVE_LDS = 4 * TILE;       // K ring (2 tiles) then V ring (2 tiles)
+    static constexpr int LDS = kWaves * WAVE_LDS;
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -143,37 +149,24 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
     using S = Shape<D>;
     constexpr int NG = S::NG, RB = S::RB, NB = S::NB;
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS];
-    __shared__ int64_t run_off[kWaves][kMaxRuns];
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches per wave
     const int n16 = lane & 15, q4 = lane >> 4;  // MFMA column / row-quarter of this lane
     const int G = a.n_q_heads / H;
     const int Sn = a.n_splits;
-    int T = a.seq_lens[b];
-    T = T < 0 ? 0 : (T > a.max_seq_len ? a.max_seq_len : T);
     const int j0 = s * a.split_keys;
-    const int j1 = min(j0 + a.split_keys, T);
     const int64_t hb = int64_t(b) * a.n_q_heads + int64_t(g) * G;
-
-    if (j0 >= j1) {  // split past the end: an empty partial
-        for (int i = tid; i < G * D; i += kWaves * 64) a.part_acc[((hb + i / D) * Sn + s) * D + i % D] = 0.0f;
-        if (tid < G) {
-            a.part_m[(hb + tid) * Sn + s] = -INFINITY;
-            a.part_z[(hb + tid) * Sn + s] = 0.0f;
-        }
-        return;
-    }
 
     // This wave's keys: a contiguous quarter of the split.
     const int kq = a.split_keys / kWaves;
     const int w0 = j0 + wave * kq;
-    const int w1 = min(w0 + kq, j1);
-    const int n_keys = w1 > w0 ? w1 - w0 : 0;
-    const int n_sub = (n_keys + kSub - 1) / kSub;
+    int T = a.seq_lens[b];  // first: its latency overlaps the loads below
 
-    // The query of head n16 (log2-scaled later), loaded first so its latency
-    // overlaps the page-table reads and the first copies.
+    // The query of head n16 (log2-scaled later), loaded first: the wait for the
+    // page-table reads below then covers it, and the copies issued after
+    // those reads are not waited for when the query is used.
     const bool live = n16 < G;
     const float* qh = a.q + (hb + (live ? n16 : 0)) * D;
     float4 qv[NG][2];
@@ -183,32 +176,66 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
         qv[gi][1] = *reinterpret_cast<const float4*>(qh + 32 * gi + 8 * q4 + 4);
     }
 
-    // Byte offset (within a pool) of every 16-row run of this wave; runs past
-    // the last key repeat the last valid run so every copy stays in bounds.
-    // Each wave reads back only entries its own lanes wrote.
+    // Byte offset (within a pool) of each 16-row run of this wave's quarter:
+    // lane l holds run l in the first register and run 64 + l in the second.
+    // Resolved before the sequence length is known: positions are clamped to
+    // the start of the 16-row run holding max_seq_len - 1 (a run never
+    // crosses a page, page_size being a multiple of 16) and pages to the
+    // pool, so every copy stays in bounds; rows past the sequence's end are
+    // masked in the scores.
     const int32_t* pt = a.page_table + int64_t(b) * a.max_pages;
-    const int last_run = n_keys > 0 ? (n_keys - 1) / 16 : 0;
-    for (int r = lane; r < 2 * n_sub; r += 64) {
-        const int pos = w0 + 16 * min(r, last_run);
+    const int n_runs = kq / 16;
+    const int last_pos = a.max_seq_len > 0 ? (a.max_seq_len - 1) & ~15 : 0;
+    int64_t roff[2] = {0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (h == 1 && n_runs <= 64) break;
+        const int r = min(lane + 64 * h, n_runs - 1);  // lanes past the last run repeat it
+        const int pos = min(w0 + 16 * r, last_pos);
         int page = pt[pos / page_size];
         page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
-        run_off[wave][r] = ((int64_t(page) * H + g) * page_size + pos % page_size) * RB;
+        roff[h] = ((int64_t(page) * H + g) * page_size + pos % page_size) * RB;
     }
 
-    uint8_t* stage0 = smem + wave * 2 * S::STAGE;
-    const uint32_t lds0 = lds_addr(stage0);
-    auto issue = [&](int t) {
-        const int st = t & 1;
-        const uint32_t dst = lds0 + uint32_t(st * S::STAGE);
-        const int64_t r0 = run_off[wave][2 * t], r1 = run_off[wave][2 * t + 1];
-        wait_lgkm0();
-        dma_run<D>(k_pool + r0, dst, lane);
-        dma_run<D>(k_pool + r1, dst + S::RUN, lane);
-        dma_run<D>(v_pool + r0, dst + S::TILE, lane);
-        dma_run<D>(v_pool + r1, dst + S::TILE + S::RUN, lane);
+    T = T < 0 ? 0 : (T > a.max_seq_len ? a.max_seq_len : T);
+    const int j1 = min(j0 + a.split_keys, T);
+    if (j0 >= j1) {  // split past the end: an empty partial
+        for (int i = tid; i < G * D; i += kWaves * 64) a.part_acc[((hb + i / D) * Sn + s) * D + i % D] = 0.0f;
+        if (tid < G) {
+            a.part_m[(hb + tid) * Sn + s] = -INFINITY;
+            a.part_z[(hb + tid) * Sn + s] = 0.0f;
+        }
+        return;
+    }
+    const int w1 = min(w0 + kq, j1);
+    const int n_keys = w1 > w0 ? w1 - w0 : 0;
+    const int n_sub = (n_keys + kSub - 1) / kSub;
+
+    uint8_t* ring = smem + wave * S::WAVE_LDS;  // K tiles 0, 1 then V tiles 0, 1
+    const uint32_t lds0 = lds_addr(ring);
+    auto run_at = [&](int r) -> int64_t {  // r is wave-uniform
+        const int64_t v = r < 64 ? roff[0] : roff[1];
+        const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(v), r & 63);
+        const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(uint64_t(v) >> 32), r & 63);
+        return int64_t((uint64_t(hi) << 32) | lo);
     };
-    if (n_sub > 0) issue(0);
-    if (n_sub > 1) issue(1);
+    // One pool's half of sub-tile t (two runs) into ring slot t & 1.
+    auto issue = [&](const uint8_t* pool, int t, uint32_t ring_base) {
+        const uint32_t dst = ring_base + uint32_t((t & 1) * S::TILE);
+        const int64_t r0 = run_at(2 * t), r1 = run_at(2 * t + 1);
+        wait_lgkm0();  // earlier LDS reads of this slot have completed
+        dma_run<D>(pool + r0, dst, lane);
+        dma_run<D>(pool + r1, dst + S::RUN, lane);
+    };
+    const uint32_t k_ring = lds0, v_ring = lds0 + uint32_t(2 * S::TILE);
+    if (n_sub > 0) {
+        issue(k_pool, 0, k_ring);
+        issue(v_pool, 0, v_ring);
+    }
+    if (n_sub > 1) {
+        issue(k_pool, 1, k_ring);
+        issue(v_pool, 1, v_ring);
+    }
 
     // B operands of the score MFMAs: pre-scaled query (log2 units) of head
     // n16 for the 8 channels that k-slots (q4, 0..7) of each group hold,
@@ -254,12 +281,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
     // K(q, e) = 4q + e (e < 4) or 16 + 4q + e - 4, at channel half n16 >> 3.
     const int e7 = n16 & 7;
     const int tr_key = e7 < 4 ? 4 * q4 + e7 : 16 + 4 * q4 + e7 - 4;
-    const int tr_off = S::TILE + tr_key * RB + 8 * (n16 >> 3);
+    const int tr_off = tr_key * RB + 8 * (n16 >> 3);
 
     for (int t = 0; t < n_sub; ++t) {
-        if (t + 1 < n_sub) wait_vmcnt<S::DMA_PER_SUB>();
-        else wait_vmcnt<0>();
-        const uint8_t* kt = stage0 + (t & 1) * S::STAGE;
+        // K of sub-tile t has landed once at most the halves issued after it
+        // are outstanding: V_t, K_t+1, V_t+1.
+        if (t + 1 < n_sub) wait_vmcnt<3 * S::HALF>();
+        else wait_vmcnt<S::HALF>();
+        const uint8_t* kt = ring + (t & 1) * S::TILE;
+        uint8_t* vt = ring + (2 + (t & 1)) * S::TILE;
         const int valid = min(kSub, n_keys - t * kSub);
 
         // ---- scores: two 16-key blocks; lane holds keys 16*kb + 4*q4 + i of head n16
@@ -328,12 +358,30 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
 #pragma unroll
         for (int r = 0; r < 4; ++r) pp[r] = half2_t{_Float16(p[0][r]), _Float16(p[1][r])};
 
+        // The K slot of sub-tile t is free: refill it with sub-tile t + 2.
+        if (t + 2 < n_sub) issue(k_pool, t + 2, k_ring);
+        // V of sub-tile t has landed once at most K_t+1, V_t+1, K_t+2 are outstanding.
+        if (t + 2 < n_sub) wait_vmcnt<3 * S::HALF>();
+        else if (t + 1 < n_sub) wait_vmcnt<2 * S::HALF>();
+        else wait_vmcnt<0>();
+
+        // In a partial tile (only a wave's last) the rows past the sequence's
+        // end may hold any bytes -- a NaN scale among them -- which must not
+        // meet p = 0 in the context products: zero their V scales in LDS.
+        if (valid < kSub) {
+            const int row = valid + lane;
+            if (row < kSub) {
+                uint8_t* srow = vt + row * RB + D / 2;
+#pragma unroll
+                for (int i = 0; i < D / 16; i += 4) *reinterpret_cast<uint32_t*>(srow + i) = 0u;
+            }
+        }
+
         // ---- context: per group, two 16-channel blocks
-        const uint8_t* vt = kt + S::TILE;
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
             const i32x2 cv = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
-                (__attribute__((address_space(3))) i32x2*)(kt + tr_off + 16 * gi));
+                (__attribute__((address_space(3))) i32x2*)(vt + tr_off + 16 * gi));
             // scale pair (key 4q+r, key 16+4q+r) of group gi, r = 0..3
             half8_t av;
 #pragma unroll
@@ -353,7 +401,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
             o[2 * gi + 1] = mfma(av, b1, o[2 * gi + 1]);
             o[2 * gi + 1] = mfma(av, bconst, o[2 * gi + 1]);
         }
-        if (t + 2 < n_sub) issue(t + 2);
+        if (t + 2 < n_sub) issue(v_pool, t + 2, v_ring);
     }
 
     // ---- per-wave results: m (log2), z per head; o rows = heads 4*q4 + i

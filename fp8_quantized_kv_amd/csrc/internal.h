@@ -37,6 +37,68 @@ __device__ __forceinline__ float load_elem<InType::F16>(const void* p, int64_t i
     return __half2float(__ushort_as_half(static_cast<const uint16_t*>(p)[i]));
 }
 
+// Four consecutive elements i .. i+3 (i a multiple of 4, the row 16-byte
+// aligned) widened to fp32.
+template <InType T>
+__device__ __forceinline__ void load4(const void* p, int64_t i, float (&x)[4]);
+
+template <>
+__device__ __forceinline__ void load4<InType::F32>(const void* p, int64_t i, float (&x)[4]) {
+    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    x[0] = v.x;
+    x[1] = v.y;
+    x[2] = v.z;
+    x[3] = v.w;
+}
+template <>
+__device__ __forceinline__ void load4<InType::BF16>(const void* p, int64_t i, float (&x)[4]) {
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    x[0] = __uint_as_float(w.x << 16);
+    x[1] = __uint_as_float(w.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(w.y << 16);
+    x[3] = __uint_as_float(w.y & 0xFFFF0000u);
+}
+template <>
+__device__ __forceinline__ void load4<InType::F16>(const void* p, int64_t i, float (&x)[4]) {
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    x[0] = __half2float(__ushort_as_half(uint16_t(w.x)));
+    x[1] = __half2float(__ushort_as_half(uint16_t(w.x >> 16)));
+    x[2] = __half2float(__ushort_as_half(uint16_t(w.y)));
+    x[3] = __half2float(__ushort_as_half(uint16_t(w.y >> 16)));
+}
+
+// Unnormalised Hadamard-32 butterfly of a group spread over 8 consecutive
+// lanes (8-aligned within the wave): lane j = lane & 7 holds elements
+// 4j .. 4j+3.  Stages 1 and 2 pair elements inside a lane, stages 4, 8 and
+// 16 pair lane j with lane j ^ 1, ^ 2, ^ 4.  Every pair (a, b), a the lower
+// element, becomes (a + b, a - b) exactly as in the one-lane butterfly.
+__device__ __forceinline__ void h32_butterfly_lanes8(float (&x)[4], int lane) {
+    float a = x[0], b = x[1];
+    x[0] = a + b;
+    x[1] = a - b;
+    a = x[2];
+    b = x[3];
+    x[2] = a + b;
+    x[3] = a - b;
+    a = x[0];
+    b = x[2];
+    x[0] = a + b;
+    x[2] = a - b;
+    a = x[1];
+    b = x[3];
+    x[1] = a + b;
+    x[3] = a - b;
+#pragma unroll
+    for (int m = 1; m <= 4; m <<= 1) {
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float o = __shfl_xor(x[i], m, 64);
+            x[i] = upper ? o - x[i] : x[i] + o;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ launchers
 // Each returns the hipError_t of its launch; shapes are validated by the caller.
 

@@ -11,6 +11,8 @@ using kvq::InType;
 
 constexpr uintptr_t kAlign = 16;
 
+constexpr int64_t kMaxLaunchThreads = 0xFFFFFF00LL;  // grid x block of a 1-D launch
+
 bool aligned(const void* p, uintptr_t a = kAlign) { return p && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 bool q4_dim_ok(int32_t D) { return D == 64 || D == 128 || D == 256 || D == 512; }
@@ -113,6 +115,9 @@ kvq_status kvq_store(const kvq_cache* cache, const void* k, const void* v, int32
     const InType dt = static_cast<InType>(dtype);
     if (cache->format == KVQ_FMT_Q4_H32) {
         if (!aligned(k) || !aligned(v)) return KVQ_ERR_INVALID_ARG;
+        // one lane per 4 values: the launch must stay under 2^32 threads
+        if (int64_t(n_tokens) * cache->num_kv_heads * 2 * (cache->head_dim / 4) > kMaxLaunchThreads)
+            return KVQ_ERR_UNSUPPORTED;
         return launched(kvq::launch_store_q4(q4_pool(cache), k, v, dt, slot_mapping, n_tokens, stream));
     }
     if (!aligned(k) || v) return KVQ_ERR_INVALID_ARG;
@@ -125,6 +130,7 @@ kvq_status kvq_rotate_q(const void* q, int32_t dtype, float* q_rot, int32_t n_ro
     if (n_rows == 0) return KVQ_OK;
     if (!aligned(q) || !aligned(q_rot)) return KVQ_ERR_INVALID_ARG;
     if (q == q_rot && dtype != KVQ_DT_F32) return KVQ_ERR_INVALID_ARG;
+    if (int64_t(n_rows) * (head_dim / 4) > kMaxLaunchThreads) return KVQ_ERR_UNSUPPORTED;
     return launched(kvq::launch_rotate_q(q, static_cast<InType>(dtype), q_rot, n_rows, head_dim, stream));
 }
 

@@ -10,39 +10,32 @@
 namespace kvq {
 namespace {
 
-// One thread per 32-group of the query: fp32 butterfly (stages 1..16), then
-// x fp32(1/sqrt(32)) -- the same transform the store applies to K and V.
+// One lane per 4 consecutive query values (a 32-group is 8 lanes, a row of
+// 256 values one wave): the fp32 butterfly (stages 1..16) with lane
+// exchanges for the upper stages, then x fp32(1/sqrt(32)) -- the same
+// transform, in the same order, that the store applies to K and V.  Each
+// value is read and written by the same lane, so q may alias q_rot.
 template <InType DT>
-__global__ __launch_bounds__(256) void rotate_q_kernel(const void* __restrict__ q, float* __restrict__ q_rot,
-                                                       int64_t n_groups) {
-    const int64_t gi = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (gi >= n_groups) return;
-    float x[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) x[i] = load_elem<DT>(q, gi * 32 + i);
-#pragma unroll
-    for (int hs = 1; hs < 32; hs <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            if (i & hs) continue;
-            const float a = x[i], b = x[i + hs];
-            x[i] = a + b;
-            x[i + hs] = a - b;
-        }
-    }
+__global__ __launch_bounds__(256) void rotate_q_kernel(const void* q, float* q_rot, int64_t n_quads) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= n_quads) return;
+    float x[4];
+    load4<DT>(q, 4 * i, x);
+    h32_butterfly_lanes8(x, threadIdx.x & 63);
     const float c = inv_sqrt32();
-    float4* o = reinterpret_cast<float4*>(q_rot + gi * 32);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = make_float4(x[4 * i] * c, x[4 * i + 1] * c, x[4 * i + 2] * c, x[4 * i + 3] * c);
+    *reinterpret_cast<float4*>(q_rot + 4 * i) = make_float4(x[0] * c, x[1] * c, x[2] * c, x[3] * c);
 }
 
 constexpr int kMergeWaves = 4;
-constexpr int kMergeCh = 64;   // output channels per workgroup (two Hadamard groups)
+constexpr int kMergeCh = 64;     // output channels per workgroup (two Hadamard groups)
+constexpr int kMergeBatch = 32;  // partial loads in flight per lane
 
 // Workgroup (sequence x query head, 64-channel block).  Weights w_s =
 // exp(m_s - M) are formed per used split; wave w sums acc_s[c] * w_s over a
 // contiguous quarter of the splits in ascending order, and the quarters are
 // added in order, so the result depends only on the sequence's own partials.
+// The first batch of each wave's partials is loaded before M is known, so
+// that load overlaps the max and weight passes.
 // For the 4-bit cache the normalized rotated-domain vector is rotated back
 // with H32 (its own inverse): out[c] = sum_j H[c%32][j] * O[32*(c/32) + j],
 // H[i][j] = (-1)^popcount(i&j) / sqrt(32).
@@ -74,6 +67,14 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __
     const float* pm = part_m + int64_t(bh) * S;
     const float* pz = part_z + int64_t(bh) * S;
 
+    // this wave's contiguous quarter of the splits, first batch in flight
+    const int per = (n + kMergeWaves - 1) / kMergeWaves;
+    const int s0 = wave * per, s1 = min(s0 + per, n);
+    const float* pa = part_acc + int64_t(bh) * S * dv + c0 + lane;
+    float v[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) v[k] = s0 + k < s1 ? pa[int64_t(s0 + k) * dv] : 0.0f;
+
     // M = max over the used splits (exact, so the reduction order is moot).
     float mx = -INFINITY;
     for (int s = tid; s < n; s += kMergeWaves * 64) mx = fmaxf(mx, pm[s]);
@@ -93,20 +94,17 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __
         for (int m = 1; m < 64; m <<= 1) z += __shfl_xor(z, m, 64);
         if (lane == 0) s_Z = z;
     }
-    // this wave's contiguous quarter of the splits
-    const int per = (n + kMergeWaves - 1) / kMergeWaves;
-    const int s0 = wave * per, s1 = min(s0 + per, n);
-    const float* pa = part_acc + int64_t(bh) * S * dv + c0 + lane;
     float acc = 0.0f;
-    int s = s0;
-    for (; s + 8 <= s1; s += 8) {  // eight loads in flight, then the sums in order
-        float v[8];
+    for (int s = s0; s < s1; s += kMergeBatch) {
+        if (s > s0) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = pa[int64_t(s + k) * dv];
+            for (int k = 0; k < kMergeBatch; ++k) v[k] = s + k < s1 ? pa[int64_t(s + k) * dv] : 0.0f;
+        }
+        const int cnt = min(kMergeBatch, s1 - s);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc += v[k] * w[s + k];
+        for (int k = 0; k < kMergeBatch; ++k)
+            if (k < cnt) acc += v[k] * w[s + k];
     }
-    for (; s < s1; ++s) acc += pa[int64_t(s) * dv] * w[s];
     part[wave][lane] = acc;
     __syncthreads();
     if (tid < kMergeCh)
@@ -130,13 +128,13 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __
 }  // namespace
 
 hipError_t launch_rotate_q(const void* q, InType dt, float* q_rot, int n_rows, int head_dim, hipStream_t s) {
-    const int64_t n_groups = int64_t(n_rows) * (head_dim / 32);
-    if (n_groups == 0) return hipSuccess;
-    const dim3 block(256), grid(unsigned((n_groups + 255) / 256));
+    const int64_t n_quads = int64_t(n_rows) * (head_dim / 4);
+    if (n_quads == 0) return hipSuccess;
+    const dim3 block(256), grid(unsigned((n_quads + 255) / 256));
     switch (dt) {
-        case InType::F32: rotate_q_kernel<InType::F32><<<grid, block, 0, s>>>(q, q_rot, n_groups); break;
-        case InType::BF16: rotate_q_kernel<InType::BF16><<<grid, block, 0, s>>>(q, q_rot, n_groups); break;
-        case InType::F16: rotate_q_kernel<InType::F16><<<grid, block, 0, s>>>(q, q_rot, n_groups); break;
+        case InType::F32: rotate_q_kernel<InType::F32><<<grid, block, 0, s>>>(q, q_rot, n_quads); break;
+        case InType::BF16: rotate_q_kernel<InType::BF16><<<grid, block, 0, s>>>(q, q_rot, n_quads); break;
+        case InType::F16: rotate_q_kernel<InType::F16><<<grid, block, 0, s>>>(q, q_rot, n_quads); break;
     }
     return hipGetLastError();
 }

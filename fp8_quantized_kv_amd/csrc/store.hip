@@ -20,79 +20,62 @@
 namespace kvq {
 namespace {
 
-// One thread quantizes one 32-value group of one row: the whole group lives
-// in registers, the butterfly needs no exchange, and the 16 code bytes leave
-// as one 16-byte store when the row allows it.  The store is off the decode
-// critical path (one token per layer per step), so simplicity wins here.
+// One lane per 4 consecutive values of a row, so a 32-group is 8 lanes and a
+// head_dim-256 row is one wave: loads and code stores are contiguous across
+// lanes.  Lanes of a group exchange values for the butterfly's upper stages
+// and the amax; each lane then packs its 4 codes into 2 bytes.  Rows are
+// ordered K rows first, then V rows, each (token, head) major.
 template <InType DT>
 __global__ __launch_bounds__(256) void store_q4_kernel(const void* __restrict__ k, const void* __restrict__ v,
                                                        const int64_t* __restrict__ slots, int n_tokens,
                                                        uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                        int H, int D, int page_size, int64_t n_slots) {
-    const int G = D / 32;
+    const int per_row = D / 4;
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t total = int64_t(n_tokens) * H * 2 * G;
-    if (idx >= total) return;
-    const int g = int(idx % G);
-    int64_t r = idx / G;
-    const int which = int(r & 1);
-    r >>= 1;
-    const int h = int(r % H);
+    const int64_t nth = int64_t(n_tokens) * H;
+    if (idx >= 2 * nth * per_row) return;
+    const int e = int(idx % per_row);  // lane-in-row: values 4e .. 4e+3
+    int64_t r = idx / per_row;
+    const int which = r >= nth ? 1 : 0;
+    r -= which * nth;                   // r = t * H + h
     const int64_t t = r / H;
+    const int h = int(r % H);
     const int64_t slot = slots[t];
-    if (slot < 0 || slot >= n_slots) return;
+    if (slot < 0 || slot >= n_slots) return;  // the whole row (all 8 lanes of each group) leaves
 
-    const void* src = which ? v : k;
-    const int64_t base = (t * H + h) * D + 32 * g;
-    float x[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) x[i] = load_elem<DT>(src, base + i);
-
-    // Hadamard butterfly, stages 1, 2, 4, 8, 16: (a, b) -> (a + b, a - b).
-#pragma unroll
-    for (int hs = 1; hs < 32; hs <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            if (i & hs) continue;
-            const float a = x[i], b = x[i + hs];
-            x[i] = a + b;
-            x[i + hs] = a - b;
-        }
-    }
+    float x[4];
+    load4<DT>(which ? v : k, r * D + 4 * e, x);
+    const int lane = threadIdx.x & 63;
+    h32_butterfly_lanes8(x, lane);
     const float c = inv_sqrt32();
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < 4; ++i) {
         x[i] = x[i] * c;
         amax = fmaxf(amax, fabsf(x[i]));
     }
+#pragma unroll
+    for (int m = 1; m <= 4; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
     // scale = fp16_rne(amax / 8); amax * 0.125 is the same exactly rounded value.
     const __half s16 = __float2half_rn(amax * 0.125f);
     const float s = __half2float(s16);
 
-    uint32_t words[4] = {0u, 0u, 0u, 0u};
+    // Values 4j .. 4j+3 of the group (j = e & 7) are code bytes 2j and 2j+1:
+    // value 2k in the low nibble of byte k, value 2k+1 in the high nibble.
+    uint32_t bits = 0u;
     if (s != 0.0f) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
+        for (int i = 0; i < 4; ++i) {
             float n = rintf(x[i] / s);  // correctly rounded divide, then half-to-even
             n = fminf(fmaxf(n, -8.0f), 7.0f);
-            const uint32_t nib = uint32_t(int(n)) & 0xFu;
-            words[i >> 3] |= nib << (4 * (i & 7));
+            bits |= (uint32_t(int(n)) & 0xFu) << (4 * i);
         }
     }
     const int rb = q4_row_bytes(D);
     const int64_t page = slot / page_size, off = slot % page_size;
     uint8_t* row = (which ? v_pool : k_pool) + ((page * H + h) * page_size + off) * rb;
-    uint32_t* cw = reinterpret_cast<uint32_t*>(row + 16 * g);
-    if ((reinterpret_cast<uintptr_t>(cw) & 15u) == 0) {
-        *reinterpret_cast<uint4*>(cw) = make_uint4(words[0], words[1], words[2], words[3]);
-    } else {
-        cw[0] = words[0];
-        cw[1] = words[1];
-        cw[2] = words[2];
-        cw[3] = words[3];
-    }
-    reinterpret_cast<uint16_t*>(row + D / 2)[g] = __half_as_ushort(s16);
+    reinterpret_cast<uint16_t*>(row)[e] = uint16_t(bits);
+    if ((e & 7) == 0) reinterpret_cast<uint16_t*>(row + D / 2)[e >> 3] = __half_as_ushort(s16);
 }
 
 // e4m3 ("fn": bias 7, max 448) code of v, round to nearest even, saturating
@@ -149,7 +132,7 @@ __global__ __launch_bounds__(64) void store_fp8_kernel(const void* __restrict__ 
 
 hipError_t launch_store_q4(const Q4Pool& pool, const void* k, const void* v, InType dt, const int64_t* slots,
                            int n_tokens, hipStream_t s) {
-    const int64_t total = int64_t(n_tokens) * pool.n_kv_heads * 2 * (pool.head_dim / 32);
+    const int64_t total = int64_t(n_tokens) * pool.n_kv_heads * 2 * (pool.head_dim / 4);
     if (total == 0) return hipSuccess;
     const dim3 block(256), grid(unsigned((total + 255) / 256));
     const int64_t n_slots = int64_t(pool.num_pages) * pool.page_size;

@@ -22,11 +22,14 @@ def rel_err(o_gpu, o_ref):
 class Q4Case:
     """A 4-bit workload instance: inputs, GPU cache, oracle pools."""
 
-    def __init__(self, w, lens, layer=0, device="cuda", store_chunk=None, build_oracle=True):
+    def __init__(self, w, lens, layer=0, device="cuda", store_chunk=None, build_oracle=True, fill=None):
         import fp8_quantized_kv_amd as kvq
         self.w, self.lens, self.layer = w, list(lens), layer
         self.lay = wl.page_layout(w, self.lens)
         self.cache = kvq.Q4Cache(self.lay.num_pages, w.n_kv_heads, w.head_dim, w.page_size, device)
+        if fill is not None:  # bytes the stores do not overwrite keep this value
+            self.cache.k_pool.fill_(fill)
+            self.cache.v_pool.fill_(fill)
         self.q = wl.q4_query(wl.shrink(w, batch=len(self.lens)), layer, device)
         self.page_table = self.lay.page_table.to(device)
         self.seq_lens = torch.tensor(self.lens, dtype=torch.int32, device=device)

@@ -193,6 +193,22 @@ def test_ragged_batch_paged(kvq):
     _check_q4(case, 2048)
 
 
+def test_rows_past_the_end_are_ignored(kvq):
+    """Pool bytes past a sequence's last position -- here 0xFF, whose fp16
+    scale is a NaN -- never reach the output, also inside a partial 16-row
+    run and a partial tile."""
+    w = wl.shrink(wl.RAGGED, prefill_chunk=0)
+    lens = [1000, 17, 2049, 530]
+    case = Q4Case(w, lens, fill=0xFF)
+    for split in (512, 2048):
+        o, lse = case.gpu_attention(split)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+        ro, rl = case.ref_attention()
+        err = rel_err(o, ro)
+        _say(f"  split={split} max_rel_err={err.max():.2e}")
+        assert err.max() < TOL
+
+
 def test_batch_invariance(kvq):
     """A sequence's output does not depend on the batch around it: solo and
     batched runs are bit-identical (TensorFold "What it is": concurrent

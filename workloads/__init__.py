@@ -88,7 +88,7 @@ TINY = Q4Workload("tiny_q4_d128_t1024", seed=1001, n_layers=1, batch=1, n_q_head
                   seq_len=1024, kv_dtype=torch.float32, q_std=128 ** -0.5, sm_scale=1.0, outlier_channels=4,
                   split_keys=512)
 GQA_32K = Q4Workload("gqa_q4_32k", seed=1002, n_layers=16, batch=1, n_q_heads=24, n_kv_heads=4, head_dim=256,
-                     seq_len=32768, sm_scale=1 / 16, heavy_channels=16, split_keys=1024)
+                     seq_len=32768, sm_scale=1 / 16, heavy_channels=16, split_keys=512)
 GQA_262K = Q4Workload("gqa_q4_262k", seed=1003, n_layers=16, batch=1, n_q_heads=24, n_kv_heads=4, head_dim=256,
                       seq_len=262144, sm_scale=1 / 16, heavy_channels=16, plant_at=131072, split_keys=2048)
 RAGGED = Q4Workload("ragged_q4_b16", seed=1004, n_layers=1, batch=16, n_q_heads=24, n_kv_heads=4, head_dim=256,
