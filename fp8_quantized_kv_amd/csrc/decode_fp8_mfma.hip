@@ -1,0 +1,372 @@
+// decode_fp8_mfma.hip -- split-T decode over the fp8 e4m3 MLA latent cache
+// with matrix cores (gfx950 v_mfma_f32_16x16x32_f16).
+//
+// Method: colibri pull request "KV cache quantization: fp8 (KV8) + 4-bit
+// TurboQuant", KV8 commit (latent rows of kv_lora + rope e4m3 codes with a
+// per-row f32 amax/448 scale each; absorbed attention, where the latent is
+// both key and value) and split-T commit (partials (cl[K], m, z) per (head,
+// split), merged by a log-sum-exp kernel); its correctness notes (e4m3 NaN
+// codes read as 0, where a GPU convert would read NaN).
+//
+// Per position j and head h:
+//   s_hj = sm_scale * (scL_j <qL_h, dec(Lc_j)> + scR_j <qR_h, dec(Rc_j)>),
+//   acc_h = sum_j exp(s_hj - m_h) scL_j dec(Lc_j),  z_h = sum_j exp(s_hj - m_h).
+// 128 heads x (576 + 512) multiply-adds per 584 cached bytes: the work is
+// bound by the matrix cores, not by HBM.
+//
+// Workgroup = 4 waves = 64 heads (16 per wave, the MFMA's 16-wide dimension)
+// x one split of the context; both head blocks of a split read the same
+// tiles (the second read is served by the caches).  Per 32-key tile:
+//  * Staging: the tile's rows (two 16-row page runs of 576 code bytes) and
+//    their scales go global -> registers -> LDS, one iteration ahead of use.
+//    On the way, codes 0x7F / 0xFF (NaN) are zeroed with byte-wise integer
+//    arithmetic, so every wave reads clean codes.  Rows are padded to 584
+//    bytes, which makes the column reads below free of bank conflicts.
+//  * Scores: A = 16 keys x 32 channels (8 code bytes per lane converted by
+//    v_cvt_scalef32_pk_f16_fp8, exact: every e4m3 value is an f16), B = the
+//    query pre-scaled by sm_scale*log2(e), split into f16 hi + lo parts; the
+//    latent and rope parts accumulate separately and meet their scales in
+//    fp32.  Output lane (head n, quarter q) holds keys 4q+i and 16+4q+i.
+//  * Softmax in log2 units with a lazily moving maximum (moves only when a
+//    tile exceeds it by more than 2^6).
+//  * Context: A = p * scL for the lane's 8 keys (exactly the score lane's
+//    own keys, so no exchange is needed) in f16, scaled by 2^-E with E a
+//    running exponent of the largest latent scale seen, which keeps A inside
+//    the f16 range whatever the rows' magnitude; B = 8 keys x 1 channel of
+//    latent codes gathered by ds_read_b64_tr_b8 (source lanes 2k and 2k+1
+//    address key k at channel offsets 0 and 8) and converted to f16.
+#include "internal.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kL = 512, kR = 64, kD = kL + kR;  // latent, rope, row
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kHeadsWG = 16 * kWaves;
+constexpr int kTile = 32;                            // keys per tile
+constexpr int kPitch = 584;                          // LDS bytes per row
+constexpr int kScaleOff = kTile * kPitch;            // scales after the rows
+constexpr int kStage = kScaleOff + kTile * 8;        // 18944 bytes
+constexpr int kChunks = kTile * kD / 16;             // 16-byte code chunks per tile (1152)
+constexpr int kChunkRow = kD / 16;                   // chunks per row (36)
+constexpr int kPerThread = (kChunks + kThreads - 1) / kThreads;  // 5 (the fifth of 128 threads)
+constexpr int kMaxRuns = 128;                        // 16-key runs per split (split_keys <= 2048)
+constexpr int kNG = kD / 32;                         // 18 channel groups of 32
+constexpr int kNGL = kL / 32;                        // 16 of them latent
+constexpr int kNB = kL / 16;                         // 32 output blocks of 16 channels
+constexpr float kRescale = 6.0f;
+
+__device__ __forceinline__ f32x4 mfma(half8_t a, half8_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 8 e4m3 codes (two dwords, byte order = k-slot order) as 8 f16 values.
+__device__ __forceinline__ half8_t cvt8(uint32_t w0, uint32_t w1) {
+    const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+    const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+    const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+    const half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+    return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Zero the bytes of w that are e4m3 NaN codes (low 7 bits all ones).
+__device__ __forceinline__ uint32_t clear_nan_codes(uint32_t w) {
+    const uint32_t t = ((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;  // bit 7 set where low 7 bits were 0x7F
+    return w & ~(t | (t - (t >> 7)));
+}
+
+__device__ __forceinline__ float quad_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 2^e for an integer e in [-126, 127], exactly.
+__device__ __forceinline__ float exp2i(int e) { return __uint_as_float(uint32_t(e + 127) << 23); }
+
+__global__ __launch_bounds__(kThreads, 1) void decode_fp8_mfma(const uint8_t* __restrict__ codes,
+                                                               const float* __restrict__ scales, int page_size,
+                                                               int num_pages, DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+
+    const int s = blockIdx.x, hblk = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n16 = lane & 15, q4 = lane >> 4;
+    const int H = a.n_q_heads, Sn = a.n_splits;
+    const int j0 = s * a.split_keys;
+    const int h_wave = hblk * kHeadsWG + wave * 16;  // first head of this wave
+    int T = a.seq_lens[b];
+
+    // Query of head h_wave + n16, channels 32g + 8q4 .. +7 of each group.
+    const int hq = h_wave + n16;
+    const bool live = hq < H;
+    const float* qh = a.q + (int64_t(b) * H + (live ? hq : 0)) * kD;
+    float4 qv[kNG][2];
+#pragma unroll
+    for (int g = 0; g < kNG; ++g) {
+        qv[g][0] = *reinterpret_cast<const float4*>(qh + 32 * g + 8 * q4);
+        qv[g][1] = *reinterpret_cast<const float4*>(qh + 32 * g + 8 * q4 + 4);
+    }
+
+    // Slot of the first row of each 16-row run of the split: lane l holds run
+    // l in the first register and run 64 + l in the second.  Positions are
+    // clamped to the start of the run holding max_seq_len - 1 and pages to
+    // the pool, so every read stays in bounds; rows past the end are masked.
+    const int32_t* pt = a.page_table + int64_t(b) * a.max_pages;
+    const int n_runs = a.split_keys / 16;
+    const int last_pos = a.max_seq_len > 0 ? (a.max_seq_len - 1) & ~15 : 0;
+    int64_t rslot[2] = {0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (h == 1 && n_runs <= 64) break;
+        const int r = min(lane + 64 * h, n_runs - 1);
+        const int pos = min(j0 + 16 * r, last_pos);
+        int page = pt[pos / page_size];
+        page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+        rslot[h] = int64_t(page) * page_size + pos % page_size;
+    }
+
+    T = T < 0 ? 0 : (T > a.max_seq_len ? a.max_seq_len : T);
+    const int j1 = min(j0 + a.split_keys, T);
+    if (j0 >= j1) {  // split past the end: empty partials for this workgroup's heads
+        const int nh = max(0, min(kHeadsWG, H - hblk * kHeadsWG));
+        const int64_t hb = int64_t(b) * H + hblk * kHeadsWG;
+        for (int i = tid; i < nh * kL; i += kThreads) a.part_acc[((hb + i / kL) * Sn + s) * kL + i % kL] = 0.0f;
+        if (tid < nh) {
+            a.part_m[(hb + tid) * Sn + s] = -INFINITY;
+            a.part_z[(hb + tid) * Sn + s] = 0.0f;
+        }
+        return;
+    }
+    const int n_keys = j1 - j0;
+    const int n_tiles = (n_keys + kTile - 1) / kTile;
+
+    auto run_slot = [&](int r) -> int64_t {  // r is wave-uniform
+        const int64_t v = r < 64 ? rslot[0] : rslot[1];
+        const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(v), r & 63);
+        const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(uint64_t(v) >> 32), r & 63);
+        return int64_t((uint64_t(hi) << 32) | lo);
+    };
+
+    // ---- staging: thread tid owns code chunks tid + 256 i (i < 5 while
+    // < 1152); threads 128..143 own the 16 scale chunks instead of a fifth.
+    u32x4 stg[kPerThread];
+    auto load_tile = [&](int t) {
+        const int64_t ra = run_slot(2 * t), rb = run_slot(2 * t + 1);
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const int c = tid + kThreads * i;
+            if (c < kChunks) {
+                const int kr = c / kChunkRow, col = c % kChunkRow;
+                const int64_t slot = (kr < 16 ? ra : rb) + (kr & 15);
+                stg[i] = *reinterpret_cast<const u32x4*>(codes + slot * kD + 16 * col);
+            } else if (tid >= 128 && tid < 144) {
+                const int sc = tid - 128;  // keys 2sc, 2sc+1
+                const int64_t slot = ((2 * sc) < 16 ? ra : rb) + ((2 * sc) & 15);
+                stg[i] = *reinterpret_cast<const u32x4*>(scales + slot * 2);
+            }
+        }
+    };
+    auto store_tile = [&](int t) {
+        uint8_t* st = smem + (t & 1) * kStage;
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const int c = tid + kThreads * i;
+            if (c < kChunks) {
+                const int kr = c / kChunkRow, col = c % kChunkRow;
+                u32x4 w = stg[i];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = clear_nan_codes(w[e]);
+                u32x2* d = reinterpret_cast<u32x2*>(st + kr * kPitch + 16 * col);
+                d[0] = u32x2{w[0], w[1]};
+                d[1] = u32x2{w[2], w[3]};
+            } else if (tid >= 128 && tid < 144) {
+                *reinterpret_cast<u32x4*>(st + kScaleOff + 16 * (tid - 128)) = stg[i];
+            }
+        }
+    };
+
+    load_tile(0);
+
+    // B operands of the score MFMAs: the pre-scaled query split into f16 hi + lo.
+    half8_t bq_hi[kNG], bq_lo[kNG];
+    {
+        const float qscale = a.sm_scale * kLog2e;
+#pragma unroll
+        for (int g = 0; g < kNG; ++g) {
+            const float c8[8] = {qv[g][0].x, qv[g][0].y, qv[g][0].z, qv[g][0].w,
+                                 qv[g][1].x, qv[g][1].y, qv[g][1].z, qv[g][1].w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float v = live ? c8[k] * qscale : 0.0f;
+                const _Float16 hi = _Float16(v);
+                bq_hi[g][k] = hi;
+                bq_lo[g][k] = _Float16(v - float(hi));
+            }
+        }
+    }
+
+    store_tile(0);
+    if (n_tiles > 1) load_tile(1);
+    __syncthreads();
+
+    f32x4 o[kNB];
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY;  // running max (log2 units) of head n16
+    float z_run = 0.0f;       // this lane's share of the running sum
+    int e_run = -1000;        // running exponent of the largest latent scale (unset)
+
+    // tr_b8 source row of this lane: key K(q4, k) with k = n16 >> 1, at
+    // channel offset 8 * (n16 & 1); K(q, k) = 4q + k (k < 4) or 16 + 4q + k - 4.
+    const int trk = n16 >> 1;
+    const int tr_key = trk < 4 ? 4 * q4 + trk : 16 + 4 * q4 + trk - 4;
+    const int tr_off = tr_key * kPitch + 8 * (n16 & 1);
+
+    for (int t = 0; t < n_tiles; ++t) {
+        const uint8_t* st = smem + (t & 1) * kStage;
+        const int valid = min(kTile, n_keys - t * kTile);
+
+        // ---- scores: two 16-key blocks; lane holds keys 16 kb + 4 q4 + i of head n16
+        float sc[2][4], scl[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const uint8_t* krow = st + (16 * kb + n16) * kPitch + 8 * q4;
+            f32x4 accL0 = {0.0f, 0.0f, 0.0f, 0.0f}, accL1 = accL0, accR = accL0;
+#pragma unroll
+            for (int g = 0; g < kNG; ++g) {
+                const u32x2 w = *reinterpret_cast<const u32x2*>(krow + 32 * g);
+                const half8_t av = cvt8(w[0], w[1]);
+                if (g >= kNGL) {
+                    accR = mfma(av, bq_hi[g], accR);
+                    accR = mfma(av, bq_lo[g], accR);
+                } else if (g & 1) {
+                    accL1 = mfma(av, bq_hi[g], accL1);
+                    accL1 = mfma(av, bq_lo[g], accL1);
+                } else {
+                    accL0 = mfma(av, bq_hi[g], accL0);
+                    accL0 = mfma(av, bq_lo[g], accL0);
+                }
+            }
+            const float4* sp = reinterpret_cast<const float4*>(st + kScaleOff + 8 * (16 * kb + 4 * q4));
+            const float4 s01 = sp[0], s23 = sp[1];
+            const float sl[4] = {s01.x, s01.z, s23.x, s23.z}, sr[4] = {s01.y, s01.w, s23.y, s23.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sc[kb][i] = sl[i] * (accL0[i] + accL1[i]) + sr[i] * accR[i];
+                scl[kb][i] = sl[i];
+            }
+        }
+        if (valid < kTile) {  // only the last tile can be partial
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * kb + 4 * q4 + i >= valid) {
+                        sc[kb][i] = -INFINITY;
+                        scl[kb][i] = 0.0f;  // rows past the end may hold any scale
+                    }
+        }
+
+        // ---- running maximum (per head) and running scale exponent (uniform)
+        float tmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                           fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        tmax = quad_max(tmax);
+        float smax = fmaxf(fmaxf(fmaxf(scl[0][0], scl[0][1]), fmaxf(scl[0][2], scl[0][3])),
+                           fmaxf(fmaxf(scl[1][0], scl[1][1]), fmaxf(scl[1][2], scl[1][3])));
+        smax = quad_max(smax);  // the same in every lane: scales belong to keys
+        const int e_tile = smax > 0.0f ? int((__float_as_uint(smax) >> 23) & 0xFF) - 127 : -1000;
+        const int e_new = __builtin_amdgcn_readfirstlane(
+            e_run == -1000 ? max(e_tile, -100) : (e_tile > e_run + 4 ? e_tile : e_run));
+        const bool move = tmax > m_run + kRescale || m_run == -INFINITY;
+        if (__builtin_amdgcn_ballot_w64(move) != 0ull || e_new != e_run) {
+            const float m_new = move ? fmaxf(m_run, tmax) : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+            z_run *= alpha;
+            m_run = m_new;
+            const float f = e_run == -1000 ? 1.0f : exp2i(max(e_run - e_new, -126));
+            e_run = e_new;
+            float al[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * q4 + i, 64) * f;  // rows 4 q4 + i are heads
+#pragma unroll
+            for (int blk = 0; blk < kNB; ++blk)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[blk][i] *= al[i];
+        }
+        const float sfac = exp2i(-e_run);
+
+        // ---- weights: p for z, p * scL * 2^-E (f16) for the context
+        half8_t av;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = __builtin_amdgcn_exp2f(sc[kb][i] - m_run);
+                z_run += p;
+                av[4 * kb + i] = _Float16(p * (scl[kb][i] * sfac));
+            }
+
+        // ---- context: 32 blocks of 16 latent channels
+#pragma unroll
+        for (int cb = 0; cb < kNB; ++cb) {
+            const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) i32x2*)(st + tr_off + 16 * cb));
+            o[cb] = mfma(av, cvt8(uint32_t(v[0]), uint32_t(v[1])), o[cb]);
+        }
+
+        // ---- next tile: registers -> LDS (the other stage), then the one after into registers
+        if (t + 1 < n_tiles) store_tile(t + 1);
+        if (t + 2 < n_tiles) load_tile(t + 2);
+        __syncthreads();
+    }
+
+    // ---- partials: o rows are heads 4 q4 + i, columns channels 16 cb + n16
+    z_run = quad_sum(z_run);
+    const float back = e_run == -1000 ? 0.0f : exp2i(e_run);
+    const int64_t hrow = int64_t(b) * H + h_wave;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = 4 * q4 + i;
+        if (h_wave + h < H) {
+            float* dst = a.part_acc + ((hrow + h) * Sn + s) * kL + n16;
+#pragma unroll
+            for (int cb = 0; cb < kNB; ++cb) dst[16 * cb] = o[cb][i] * back;
+        }
+    }
+    if (q4 == 0 && live) {
+        a.part_m[(hrow + n16) * Sn + s] = m_run * kLn2;
+        a.part_z[(hrow + n16) * Sn + s] = z_run;
+    }
+}
+
+}  // namespace
+
+bool decode_fp8_mfma_supported(const Fp8Pool& pool, const DecodeArgs& a) {
+    return pool.head_dim == kD && pool.rope_dim == kR && pool.page_size % 16 == 0 && a.split_keys % kTile == 0 &&
+           a.split_keys / 16 <= kMaxRuns;
+}
+
+hipError_t launch_decode_fp8_mfma(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s) {
+    const dim3 grid(unsigned(a.n_splits), unsigned((a.n_q_heads + kHeadsWG - 1) / kHeadsWG), unsigned(a.batch));
+    decode_fp8_mfma<<<grid, dim3(kThreads), 0, s>>>(pool.codes, pool.scales, pool.page_size, pool.num_pages, a);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -147,6 +147,11 @@ struct DecodeArgs {
 bool decode_q4_mfma_supported(const Q4Pool& pool, const DecodeArgs& a);
 hipError_t launch_decode_q4_mfma(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s);
 
+// Matrix-core kernel for the fp8 latent cache (512 + 64, pages of a
+// multiple of 16 tokens, split_keys <= 2048).
+bool decode_fp8_mfma_supported(const Fp8Pool& pool, const DecodeArgs& a);
+hipError_t launch_decode_fp8_mfma(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s);
+
 // Plain fp32 vector-math kernels (any supported head_dim).
 hipError_t launch_decode_q4_simple(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_fp8_simple(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s);

@@ -154,7 +154,9 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_h
         if (kvq::decode_q4_mfma_supported(pool, a)) return launched(kvq::launch_decode_q4_mfma(pool, a, stream));
         return launched(kvq::launch_decode_q4_simple(pool, a, stream));
     }
-    return launched(kvq::launch_decode_fp8_simple(fp8_pool(cache), a, stream));
+    const kvq::Fp8Pool pool = fp8_pool(cache);
+    if (kvq::decode_fp8_mfma_supported(pool, a)) return launched(kvq::launch_decode_fp8_mfma(pool, a, stream));
+    return launched(kvq::launch_decode_fp8_simple(pool, a, stream));
 }
 
 kvq_status kvq_merge(const kvq_cache* cache, const float* part_acc, const float* part_m, const float* part_z,

@@ -75,11 +75,14 @@ class Q4Case:
 class MlaCase:
     """An fp8 latent workload instance."""
 
-    def __init__(self, w, lens, layer=0, device="cuda", build_oracle=True):
+    def __init__(self, w, lens, layer=0, device="cuda", build_oracle=True, fill=None):
         import fp8_quantized_kv_amd as kvq
         self.w, self.lens = w, list(lens)
         self.lay = wl.page_layout(w, self.lens)
         self.cache = kvq.Fp8Cache(self.lay.num_pages, w.head_dim, w.rope_dim, w.page_size, device)
+        if fill is not None:  # bytes the stores do not overwrite keep this value
+            self.cache.codes.fill_(fill)
+            self.cache.scales.view(torch.uint8).fill_(fill)
         self.q = wl.mla_query(wl.shrink(w, batch=len(self.lens)), layer, device)
         self.page_table = self.lay.page_table.to(device)
         self.seq_lens = torch.tensor(self.lens, dtype=torch.int32, device=device)

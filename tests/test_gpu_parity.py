@@ -275,6 +275,41 @@ def test_mla_small(kvq):
         assert np.all(o[2] == 0)
 
 
+@pytest.mark.parametrize("n_heads", [16, 40, 128])
+def test_mla_heads_splits_and_tails(kvq, n_heads):
+    """Head counts that fill a 64-head workgroup partly or fully, splits of
+    512-4096 keys (the last on the plain kernel), lengths with partial 16-row
+    runs and tiles, and pool bytes past each sequence's end set to 0xFF (NaN
+    codes and NaN scales) that must never reach the output."""
+    w = wl.shrink(wl.MLA_262K, n_heads=n_heads, seq_len=0)
+    lens = [17, 2100, 33, 1000]
+    case = MlaCase(w, lens, fill=0xFF)
+    ro, rl = case.ref_attention()
+    for split in (512, 1024, 2048, 4096):
+        o, lse = case.gpu_attention(split)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+        err = rel_err(o, ro)
+        _say(f"  mla heads={n_heads} split={split} max_rel_err={err.max():.2e}")
+        assert err.max() < TOL
+        assert np.max(np.abs(lse - rl)) < 1e-3 * max(1.0, np.abs(rl).max())
+
+
+def test_mla_batch_invariance(kvq):
+    """An fp8-latent sequence's output is bit-identical alone and in a batch."""
+    w = wl.shrink(wl.MLA_262K, n_heads=64, seq_len=0)
+    lens = [1500, 300, 2500]
+    batch = MlaCase(w, lens, build_oracle=False)
+    ob, lb = batch.gpu_attention(1024)
+    import fp8_quantized_kv_amd as kvq_mod
+    for b, T in enumerate(lens):
+        pt = batch.page_table[b:b + 1].contiguous()
+        sl = batch.seq_lens[b:b + 1].contiguous()
+        q = batch.q[b:b + 1].contiguous()
+        pa, pm, pz = kvq_mod.kvq_decode_attn(batch.cache, q, pt, sl, max(lens), w.sm_scale, 1024)
+        o, l = kvq_mod.kvq_merge(batch.cache, pa, pm, pz, sl, max(lens), 1024)
+        assert np.array_equal(o.cpu().numpy()[0], ob[b]) and np.array_equal(l.cpu().numpy()[0], lb[b])
+
+
 def test_mla_nan_codes_read_zero(kvq):
     """Codes 0x7F/0xFF (e4m3 NaN) in a cache read as 0 (colibri correctness
     commit: the CPU table reads 0 for NaN codes)."""
