@@ -14,9 +14,13 @@
 // 128 heads x (576 + 512) multiply-adds per 584 cached bytes: the work is
 // bound by the matrix cores, not by HBM.
 //
-// Workgroup = 4 waves = 64 heads (16 per wave, the MFMA's 16-wide dimension)
+// Workgroup = 8 waves = 4 pairs x 16 heads (the MFMA's 16-wide dimension)
 // x one split of the context; both head blocks of a split read the same
-// tiles (the second read is served by the caches).  Per 32-key tile:
+// tiles (the second read is served by the caches).  The two waves of a pair
+// split the channels: each takes 9 of the 18 groups of 32 score channels
+// (the second the last 7 latent groups and the 2 rope groups) and 256 of the
+// 512 latent output channels, so a wave holds half the query and half the
+// accumulators and two waves fit on a SIMD.  Per 32-key tile:
 //  * Staging: the tile's rows (two 16-row page runs of 576 code bytes) and
 //    their scales go global -> registers -> LDS, one iteration ahead of use.
 //    On the way, codes 0x7F / 0xFF (NaN) are zeroed with byte-wise integer
@@ -25,8 +29,10 @@
 //  * Scores: A = 16 keys x 32 channels (8 code bytes per lane converted by
 //    v_cvt_scalef32_pk_f16_fp8, exact: every e4m3 value is an f16), B = the
 //    query pre-scaled by sm_scale*log2(e), split into f16 hi + lo parts; the
-//    latent and rope parts accumulate separately and meet their scales in
-//    fp32.  Output lane (head n, quarter q) holds keys 4q+i and 16+4q+i.
+//    latent and rope parts meet their scales in fp32.  The pair exchanges
+//    its two partial scores through LDS and both add them in the same order,
+//    so both hold bit-identical scores and softmax state.  Output lane
+//    (head n, quarter q) holds keys 4q+i and 16+4q+i.
 //  * Softmax in log2 units with a lazily moving maximum (moves only when a
 //    tile exceeds it by more than 2^6).
 //  * Context: A = p * scL for the lane's 8 keys (exactly the score lane's
@@ -48,20 +54,21 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kL = 512, kR = 64, kD = kL + kR;  // latent, rope, row
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                            // 4 pairs
 constexpr int kThreads = kWaves * 64;
-constexpr int kHeadsWG = 16 * kWaves;
+constexpr int kHeadsWG = 16 * (kWaves / 2);
 constexpr int kTile = 32;                            // keys per tile
 constexpr int kPitch = 584;                          // LDS bytes per row
 constexpr int kScaleOff = kTile * kPitch;            // scales after the rows
 constexpr int kStage = kScaleOff + kTile * 8;        // 18944 bytes
+constexpr int kXOff = 2 * kStage;                    // partial-score exchange: [wave][lane][8] f32
+constexpr int kLds = kXOff + kWaves * 64 * 8 * 4;
 constexpr int kChunks = kTile * kD / 16;             // 16-byte code chunks per tile (1152)
 constexpr int kChunkRow = kD / 16;                   // chunks per row (36)
-constexpr int kPerThread = (kChunks + kThreads - 1) / kThreads;  // 5 (the fifth of 128 threads)
+constexpr int kPerThread = (kChunks + kThreads - 1) / kThreads;  // 3 (the third of 128 threads)
 constexpr int kMaxRuns = 128;                        // 16-key runs per split (split_keys <= 2048)
-constexpr int kNG = kD / 32;                         // 18 channel groups of 32
-constexpr int kNGL = kL / 32;                        // 16 of them latent
-constexpr int kNB = kL / 16;                         // 32 output blocks of 16 channels
+constexpr int kQG = 9;                               // score channel groups (of 32) per wave
+constexpr int kNBW = kL / 16 / 2;                    // 16 output blocks of 16 channels per wave
 constexpr float kRescale = 6.0f;
 
 __device__ __forceinline__ f32x4 mfma(half8_t a, half8_t b, f32x4 c) {
@@ -99,29 +106,31 @@ __device__ __forceinline__ float quad_sum(float x) {
 // 2^e for an integer e in [-126, 127], exactly.
 __device__ __forceinline__ float exp2i(int e) { return __uint_as_float(uint32_t(e + 127) << 23); }
 
-__global__ __launch_bounds__(kThreads, 1) void decode_fp8_mfma(const uint8_t* __restrict__ codes,
-                                                               const float* __restrict__ scales, int page_size,
-                                                               int num_pages, DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+__global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __restrict__ codes,
+                                                            const float* __restrict__ scales, int page_size,
+                                                            int num_pages, DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
 
     const int s = blockIdx.x, hblk = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = wave & 1;                       // channel half of the pair
     const int n16 = lane & 15, q4 = lane >> 4;
     const int H = a.n_q_heads, Sn = a.n_splits;
     const int j0 = s * a.split_keys;
-    const int h_wave = hblk * kHeadsWG + wave * 16;  // first head of this wave
+    const int h_pair = hblk * kHeadsWG + (wave >> 1) * 16;  // first head of this pair
+    const int g0 = half * kQG;                       // first score group of this wave
     int T = a.seq_lens[b];
 
-    // Query of head h_wave + n16, channels 32g + 8q4 .. +7 of each group.
-    const int hq = h_wave + n16;
+    // Query of head h_pair + n16, channels 32 (g0 + gl) + 8 q4 .. +7.
+    const int hq = h_pair + n16;
     const bool live = hq < H;
-    const float* qh = a.q + (int64_t(b) * H + (live ? hq : 0)) * kD;
-    float4 qv[kNG][2];
+    const float* qh = a.q + (int64_t(b) * H + (live ? hq : 0)) * kD + 32 * g0 + 8 * q4;
+    float4 qv[kQG][2];
 #pragma unroll
-    for (int g = 0; g < kNG; ++g) {
-        qv[g][0] = *reinterpret_cast<const float4*>(qh + 32 * g + 8 * q4);
-        qv[g][1] = *reinterpret_cast<const float4*>(qh + 32 * g + 8 * q4 + 4);
+    for (int gl = 0; gl < kQG; ++gl) {
+        qv[gl][0] = *reinterpret_cast<const float4*>(qh + 32 * gl);
+        qv[gl][1] = *reinterpret_cast<const float4*>(qh + 32 * gl + 4);
     }
 
     // Slot of the first row of each 16-row run of the split: lane l holds run
@@ -164,22 +173,24 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_mfma(const uint8_t* __
         return int64_t((uint64_t(hi) << 32) | lo);
     };
 
-    // ---- staging: thread tid owns code chunks tid + 256 i (i < 5 while
-    // < 1152); threads 128..143 own the 16 scale chunks instead of a fifth.
+    // ---- staging: thread tid owns code chunks tid + 512 i (i < 3 while
+    // < 1152); threads 128..143 own the 16 scale chunks instead of a third.
     u32x4 stg[kPerThread];
+    const bool has_scale = tid >= 128 && tid < 144;
+    auto chunk_row = [&](int i) { return (tid + kThreads * i) / kChunkRow; };
+    auto chunk_col = [&](int i) { return (tid + kThreads * i) % kChunkRow; };
     auto load_tile = [&](int t) {
         const int64_t ra = run_slot(2 * t), rb = run_slot(2 * t + 1);
+        const uint8_t* ca = codes + ra * kD;
+        const uint8_t* cb = codes + rb * kD;
 #pragma unroll
         for (int i = 0; i < kPerThread; ++i) {
-            const int c = tid + kThreads * i;
-            if (c < kChunks) {
-                const int kr = c / kChunkRow, col = c % kChunkRow;
-                const int64_t slot = (kr < 16 ? ra : rb) + (kr & 15);
-                stg[i] = *reinterpret_cast<const u32x4*>(codes + slot * kD + 16 * col);
-            } else if (tid >= 128 && tid < 144) {
-                const int sc = tid - 128;  // keys 2sc, 2sc+1
-                const int64_t slot = ((2 * sc) < 16 ? ra : rb) + ((2 * sc) & 15);
-                stg[i] = *reinterpret_cast<const u32x4*>(scales + slot * 2);
+            if (tid + kThreads * i < kChunks) {
+                const int kr = chunk_row(i);
+                stg[i] = *reinterpret_cast<const u32x4*>((kr >= 16 ? cb : ca) + (kr & 15) * kD + 16 * chunk_col(i));
+            } else if (has_scale) {
+                const int key = 2 * (tid - 128);  // keys key, key + 1
+                stg[i] = *reinterpret_cast<const u32x4*>(scales + ((key >= 16 ? rb : ra) + (key & 15)) * 2);
             }
         }
     };
@@ -187,16 +198,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_mfma(const uint8_t* __
         uint8_t* st = smem + (t & 1) * kStage;
 #pragma unroll
         for (int i = 0; i < kPerThread; ++i) {
-            const int c = tid + kThreads * i;
-            if (c < kChunks) {
-                const int kr = c / kChunkRow, col = c % kChunkRow;
+            if (tid + kThreads * i < kChunks) {
                 u32x4 w = stg[i];
+                // NaN codes are rare: test the chunk, clear only if one is present.
+                uint32_t any = 0u;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = clear_nan_codes(w[e]);
-                u32x2* d = reinterpret_cast<u32x2*>(st + kr * kPitch + 16 * col);
+                for (int e = 0; e < 4; ++e) any |= (w[e] & 0x7F7F7F7Fu) + 0x01010101u;
+                if (any & 0x80808080u) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = clear_nan_codes(w[e]);
+                }
+                u32x2* d = reinterpret_cast<u32x2*>(st + chunk_row(i) * kPitch + 16 * chunk_col(i));
                 d[0] = u32x2{w[0], w[1]};
                 d[1] = u32x2{w[2], w[3]};
-            } else if (tid >= 128 && tid < 144) {
+            } else if (has_scale) {
                 *reinterpret_cast<u32x4*>(st + kScaleOff + 16 * (tid - 128)) = stg[i];
             }
         }
@@ -205,19 +220,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_mfma(const uint8_t* __
     load_tile(0);
 
     // B operands of the score MFMAs: the pre-scaled query split into f16 hi + lo.
-    half8_t bq_hi[kNG], bq_lo[kNG];
+    half8_t bq_hi[kQG], bq_lo[kQG];
     {
         const float qscale = a.sm_scale * kLog2e;
 #pragma unroll
-        for (int g = 0; g < kNG; ++g) {
-            const float c8[8] = {qv[g][0].x, qv[g][0].y, qv[g][0].z, qv[g][0].w,
-                                 qv[g][1].x, qv[g][1].y, qv[g][1].z, qv[g][1].w};
+        for (int gl = 0; gl < kQG; ++gl) {
+            const float c8[8] = {qv[gl][0].x, qv[gl][0].y, qv[gl][0].z, qv[gl][0].w,
+                                 qv[gl][1].x, qv[gl][1].y, qv[gl][1].z, qv[gl][1].w};
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const float v = live ? c8[k] * qscale : 0.0f;
                 const _Float16 hi = _Float16(v);
-                bq_hi[g][k] = hi;
-                bq_lo[g][k] = _Float16(v - float(hi));
+                bq_hi[gl][k] = hi;
+                bq_lo[gl][k] = _Float16(v - float(hi));
             }
         }
     }
@@ -226,9 +241,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_mfma(const uint8_t* __
     if (n_tiles > 1) load_tile(1);
     __syncthreads();
 
-    f32x4 o[kNB];
+    f32x4 o[kNBW];
 #pragma unroll
-    for (int i = 0; i < kNB; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < kNBW; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY;  // running max (log2 units) of head n16
     float z_run = 0.0f;       // this lane's share of the running sum
     int e_run = -1000;        // running exponent of the largest latent scale (unset)
@@ -237,31 +252,35 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_mfma(const uint8_t* __
     // channel offset 8 * (n16 & 1); K(q, k) = 4q + k (k < 4) or 16 + 4q + k - 4.
     const int trk = n16 >> 1;
     const int tr_key = trk < 4 ? 4 * q4 + trk : 16 + 4 * q4 + trk - 4;
-    const int tr_off = tr_key * kPitch + 8 * (n16 & 1);
+    const int tr_off = tr_key * kPitch + 8 * (n16 & 1) + half * (kL / 2);
+    float* xmine = reinterpret_cast<float*>(smem + kXOff) + (wave * 64 + lane) * 8;
+    const float* xpart = reinterpret_cast<const float*>(smem + kXOff) + ((wave ^ 1) * 64 + lane) * 8;
 
     for (int t = 0; t < n_tiles; ++t) {
         const uint8_t* st = smem + (t & 1) * kStage;
         const int valid = min(kTile, n_keys - t * kTile);
 
-        // ---- scores: two 16-key blocks; lane holds keys 16 kb + 4 q4 + i of head n16
-        float sc[2][4], scl[2][4];
+        // ---- partial scores over this wave's 9 groups: two 16-key blocks;
+        // lane holds keys 16 kb + 4 q4 + i of head n16.  Groups 0..6 are
+        // latent for both halves; 7 and 8 are latent (first half) or rope.
+        float part[2][4], scl[2][4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const uint8_t* krow = st + (16 * kb + n16) * kPitch + 8 * q4;
-            f32x4 accL0 = {0.0f, 0.0f, 0.0f, 0.0f}, accL1 = accL0, accR = accL0;
+            const uint8_t* krow = st + (16 * kb + n16) * kPitch + 32 * g0 + 8 * q4;
+            f32x4 accE = {0.0f, 0.0f, 0.0f, 0.0f}, accO = accE, acc78 = accE;
 #pragma unroll
-            for (int g = 0; g < kNG; ++g) {
-                const u32x2 w = *reinterpret_cast<const u32x2*>(krow + 32 * g);
+            for (int gl = 0; gl < kQG; ++gl) {
+                const u32x2 w = *reinterpret_cast<const u32x2*>(krow + 32 * gl);
                 const half8_t av = cvt8(w[0], w[1]);
-                if (g >= kNGL) {
-                    accR = mfma(av, bq_hi[g], accR);
-                    accR = mfma(av, bq_lo[g], accR);
-                } else if (g & 1) {
-                    accL1 = mfma(av, bq_hi[g], accL1);
-                    accL1 = mfma(av, bq_lo[g], accL1);
+                if (gl >= 7) {
+                    acc78 = mfma(av, bq_hi[gl], acc78);
+                    acc78 = mfma(av, bq_lo[gl], acc78);
+                } else if (gl & 1) {
+                    accO = mfma(av, bq_hi[gl], accO);
+                    accO = mfma(av, bq_lo[gl], accO);
                 } else {
-                    accL0 = mfma(av, bq_hi[g], accL0);
-                    accL0 = mfma(av, bq_lo[g], accL0);
+                    accE = mfma(av, bq_hi[gl], accE);
+                    accE = mfma(av, bq_lo[gl], accE);
                 }
             }
             const float4* sp = reinterpret_cast<const float4*>(st + kScaleOff + 8 * (16 * kb + 4 * q4));
@@ -269,9 +288,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_mfma(const uint8_t* __
             const float sl[4] = {s01.x, s01.z, s23.x, s23.z}, sr[4] = {s01.y, s01.w, s23.y, s23.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                sc[kb][i] = sl[i] * (accL0[i] + accL1[i]) + sr[i] * accR[i];
+                part[kb][i] = sl[i] * (accE[i] + accO[i]) + (half ? sr[i] : sl[i]) * acc78[i];
                 scl[kb][i] = sl[i];
             }
+        }
+        // ---- the pair's scores: first half's partial + second half's, in both waves
+        {
+            float4* xm = reinterpret_cast<float4*>(xmine);
+            xm[0] = make_float4(part[0][0], part[0][1], part[0][2], part[0][3]);
+            xm[1] = make_float4(part[1][0], part[1][1], part[1][2], part[1][3]);
+        }
+        __syncthreads();
+        float sc[2][4];
+        {
+            const float4* xp = reinterpret_cast<const float4*>(xpart);
+            const float4 o0 = xp[0], o1 = xp[1];
+            const float other[2][4] = {{o0.x, o0.y, o0.z, o0.w}, {o1.x, o1.y, o1.z, o1.w}};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sc[kb][i] = half ? other[kb][i] + part[kb][i] : part[kb][i] + other[kb][i];
         }
         if (valid < kTile) {  // only the last tile can be partial
 #pragma unroll
@@ -306,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_mfma(const uint8_t* __
 #pragma unroll
             for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * q4 + i, 64) * f;  // rows 4 q4 + i are heads
 #pragma unroll
-            for (int blk = 0; blk < kNB; ++blk)
+            for (int blk = 0; blk < kNBW; ++blk)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o[blk][i] *= al[i];
         }
@@ -323,9 +360,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_mfma(const uint8_t* __
                 av[4 * kb + i] = _Float16(p * (scl[kb][i] * sfac));
             }
 
-        // ---- context: 32 blocks of 16 latent channels
+        // ---- context: this wave's 16 blocks of 16 latent channels
 #pragma unroll
-        for (int cb = 0; cb < kNB; ++cb) {
+        for (int cb = 0; cb < kNBW; ++cb) {
             const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                 (__attribute__((address_space(3))) i32x2*)(st + tr_off + 16 * cb));
             o[cb] = mfma(av, cvt8(uint32_t(v[0]), uint32_t(v[1])), o[cb]);
@@ -337,20 +374,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_mfma(const uint8_t* __
         __syncthreads();
     }
 
-    // ---- partials: o rows are heads 4 q4 + i, columns channels 16 cb + n16
+    // ---- partials: o rows are heads 4 q4 + i, columns channels 256 half + 16 cb + n16
     z_run = quad_sum(z_run);
     const float back = e_run == -1000 ? 0.0f : exp2i(e_run);
-    const int64_t hrow = int64_t(b) * H + h_wave;
+    const int64_t hrow = int64_t(b) * H + h_pair;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int h = 4 * q4 + i;
-        if (h_wave + h < H) {
-            float* dst = a.part_acc + ((hrow + h) * Sn + s) * kL + n16;
+        if (h_pair + h < H) {
+            float* dst = a.part_acc + ((hrow + h) * Sn + s) * kL + half * (kL / 2) + n16;
 #pragma unroll
-            for (int cb = 0; cb < kNB; ++cb) dst[16 * cb] = o[cb][i] * back;
+            for (int cb = 0; cb < kNBW; ++cb) dst[16 * cb] = o[cb][i] * back;
         }
     }
-    if (q4 == 0 && live) {
+    if (half == 0 && q4 == 0 && live) {
         a.part_m[(hrow + n16) * Sn + s] = m_run * kLn2;
         a.part_z[(hrow + n16) * Sn + s] = z_run;
     }

@@ -95,7 +95,7 @@ RAGGED = Q4Workload("ragged_q4_b16", seed=1004, n_layers=1, batch=16, n_q_heads=
                     len_range=(4096, 65536), sm_scale=1 / 16, heavy_channels=16, shuffle_pages=True,
                     prefill_chunk=2048, split_keys=2048)
 MLA_262K = MlaWorkload("mla_fp8_262k", seed=1005, n_layers=4, batch=1, n_heads=128, kv_lora=512, rope_dim=64,
-                       seq_len=262144, sm_scale=576 ** -0.5, split_keys=1024)
+                       seq_len=262144, sm_scale=576 ** -0.5, split_keys=2048)
 
 WORKLOADS = {w.name: w for w in (TINY, GQA_32K, GQA_262K, RAGGED, MLA_262K)}
 
