@@ -29,6 +29,30 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+
+# HBM bytes per decode launch of the headline workload from rocprofv3 FETCH_SIZE and WRITE_SIZE
+# passes (KiB per dispatch), scaled by what the same counters read for a 256 MiB device copy
+# (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); valid only for the kernel source they were taken on.
+TRAFFIC = {
+    "3fd90bbd9a4b3ab6572161ec806edd1eb4a0aae04108d7aed69bd04ff2c41624": {
+        "fetch_kib": 147697.0, "write_kib": 3264.28, "fetch_scale": 2.0, "write_scale": 1.0,
+        "profile": "profiles/decode_q4_mfma_gqa_q4_262k.md"},
+}
+DECODE_SOURCE = os.path.join("fp8_quantized_kv_amd", "csrc", "decode_q4_mfma.hip")
+
+
+def decode_traffic():
+    """Calibrated HBM bytes per launch if the counters match the current kernel source, else None."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, DECODE_SOURCE), "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    t = TRAFFIC.get(digest)
+    if t is None:
+        return None
+    return int(round(t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"]))
 METRIC = "KV-read GB/s (% of HBM peak) and µs/layer, 4-bit split-K decode at 32K/262K"
 
 
@@ -327,7 +351,7 @@ def main():
         "roofline": {"kernel": "kvq_decode_attn (4-bit split-K)", "bound": "hbm",
                      "achieved": round(m["decode_gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(m["decode_gbs"] / HBM_PEAK_GBS, 4), "avg_launch_us": round(m["decode_us"], 3),
-                     "traffic": None},
+                     "traffic": decode_traffic()},
         "wall_s": round(m["wall_s"], 3),
     }
     del b
