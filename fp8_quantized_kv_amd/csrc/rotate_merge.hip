@@ -31,11 +31,12 @@ constexpr int kMergeCh = 64;     // output channels per workgroup (two Hadamard 
 constexpr int kMergeBatch = 32;  // partial loads in flight per lane
 
 // Workgroup (sequence x query head, 64-channel block).  Weights w_s =
-// exp(m_s - M) are formed per used split; wave w sums acc_s[c] * w_s over a
-// contiguous quarter of the splits in ascending order, and the quarters are
-// added in order, so the result depends only on the sequence's own partials.
-// The first batch of each wave's partials is loaded before M is known, so
-// that load overlaps the max and weight passes.
+// exp(m_s - M) are formed per used split s < n; wave w sums acc_s[c] * w_s
+// over the splits s = w, w + 4, w + 8, ... in ascending order, and the four
+// sums are added in wave order, so the result depends only on the sequence's
+// own partials.  Because that order does not depend on n, every load is
+// issued before the sequence length arrives (for all S allocated splits,
+// masked afterwards): one memory round trip instead of two.
 // For the 4-bit cache the normalized rotated-domain vector is rotated back
 // with H32 (its own inverse): out[c] = sum_j H[c%32][j] * O[32*(c/32) + j],
 // H[i][j] = (-1)^popcount(i&j) / sqrt(32).
@@ -54,8 +55,24 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __
 
     const int bh = blockIdx.x, c0 = blockIdx.y * kMergeCh;
     const int b = bh / n_q_heads;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const float* pm = part_m + int64_t(bh) * S;
+    const float* pz = part_z + int64_t(bh) * S;
+    const float* pa = part_acc + int64_t(bh) * S * dv + c0 + lane;
+
+    // Loads that do not need the sequence length: this wave's first batch of
+    // partials, and (m, z) of the splits this thread forms weights for.
     int T = seq_lens[b];
+    float v[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+        const int sk = wave + kMergeWaves * k;
+        v[k] = sk < S ? pa[int64_t(sk) * dv] : 0.0f;
+    }
+    const float my_m = tid < S ? pm[tid] : -INFINITY;
+    const float my_z = tid < S ? pz[tid] : 0.0f;
+
     T = T < 0 ? 0 : (T > max_seq_len ? max_seq_len : T);
     const int n = (T + split_keys - 1) / split_keys;
     float* o = out + int64_t(bh) * dv;
@@ -64,20 +81,10 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __
         if (lse && blockIdx.y == 0 && tid == 0) lse[bh] = -INFINITY;
         return;
     }
-    const float* pm = part_m + int64_t(bh) * S;
-    const float* pz = part_z + int64_t(bh) * S;
-
-    // this wave's contiguous quarter of the splits, first batch in flight
-    const int per = (n + kMergeWaves - 1) / kMergeWaves;
-    const int s0 = wave * per, s1 = min(s0 + per, n);
-    const float* pa = part_acc + int64_t(bh) * S * dv + c0 + lane;
-    float v[kMergeBatch];
-#pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) v[k] = s0 + k < s1 ? pa[int64_t(s0 + k) * dv] : 0.0f;
 
     // M = max over the used splits (exact, so the reduction order is moot).
-    float mx = -INFINITY;
-    for (int s = tid; s < n; s += kMergeWaves * 64) mx = fmaxf(mx, pm[s]);
+    float mx = tid < n ? my_m : -INFINITY;
+    for (int s = tid + kMergeWaves * 64; s < n; s += kMergeWaves * 64) mx = fmaxf(mx, pm[s]);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
     if (lane == 0) red[wave] = mx;
@@ -85,7 +92,8 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __
     if (tid == 0) s_M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();
     const float M = s_M;
-    for (int s = tid; s < n; s += kMergeWaves * 64) w[s] = pz[s] > 0.0f ? expf(pm[s] - M) : 0.0f;
+    if (tid < n) w[tid] = my_z > 0.0f ? expf(my_m - M) : 0.0f;
+    for (int s = tid + kMergeWaves * 64; s < n; s += kMergeWaves * 64) w[s] = pz[s] > 0.0f ? expf(pm[s] - M) : 0.0f;
     __syncthreads();
     if (wave == 0) {  // Z: lane-strided partial sums in ascending order, then a fixed butterfly
         float z = 0.0f;
@@ -94,16 +102,21 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __
         for (int m = 1; m < 64; m <<= 1) z += __shfl_xor(z, m, 64);
         if (lane == 0) s_Z = z;
     }
+    // this wave's splits wave + 4k < n, ascending
     float acc = 0.0f;
-    for (int s = s0; s < s1; s += kMergeBatch) {
-        if (s > s0) {
+    for (int k0 = 0; wave + kMergeWaves * k0 < n; k0 += kMergeBatch) {
+        if (k0 > 0) {
 #pragma unroll
-            for (int k = 0; k < kMergeBatch; ++k) v[k] = s + k < s1 ? pa[int64_t(s + k) * dv] : 0.0f;
+            for (int k = 0; k < kMergeBatch; ++k) {
+                const int sk = wave + kMergeWaves * (k0 + k);
+                v[k] = sk < n ? pa[int64_t(sk) * dv] : 0.0f;
+            }
         }
-        const int cnt = min(kMergeBatch, s1 - s);
 #pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k)
-            if (k < cnt) acc += v[k] * w[s + k];
+        for (int k = 0; k < kMergeBatch; ++k) {
+            const int sk = wave + kMergeWaves * (k0 + k);
+            if (sk < n) acc += v[k] * w[sk];
+        }
     }
     part[wave][lane] = acc;
     __syncthreads();

@@ -187,9 +187,10 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_h
 
 /* ---------------------------------------------------------------- merge */
 
-/* Log-sum-exp merge of the partials (colibri split-T commit), in split order
- * (TensorFold "What it is": an in-order merge: the splits are summed in
- * ascending order within four contiguous blocks, and the blocks in order),
+/* Log-sum-exp merge of the partials (colibri split-T commit), in a fixed
+ * order (TensorFold "What it is": an in-order merge): split s goes to partial
+ * sum s mod 4, each partial sum runs over its splits in ascending order, and
+ * the four are added in order 0, 1, 2, 3;
  * followed for Q4 by the single inverse rotation (H32 is its own inverse):
  *   M = max_s m_s, Z = sum_s z_s exp(m_s - M),
  *   out = R( sum_s acc_s exp(m_s - M) / Z ),  R = H32 (Q4) or identity (FP8),
