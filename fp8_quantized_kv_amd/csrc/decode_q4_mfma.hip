@@ -56,13 +56,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kEightWaveSplit = 1024;  // splits up to this many keys use 8-wave workgroups
 constexpr int kSub = 32;          // keys per sub-tile
 constexpr int kMaxRuns = 128;     // 16-key runs per wave (split_keys <= 8192)
 constexpr float kTwo24 = 16777216.0f;
 constexpr float kRescale = 6.0f;  // log2 headroom before the running max moves
 
-template <int D>
+template <int D, int W>
 struct Shape {
     static constexpr int NG = D / 32;               // 32-channel groups per row
     static constexpr int RB = D / 2 + D / 16;       // row bytes
@@ -72,7 +72,7 @@ struct Shape {
     static constexpr int TILE = kSub * RB;          // bytes of a sub-tile, one pool
     static constexpr int HALF = 2 * RUN_INSTR;      // DMA instructions of a sub-tile, one pool
     static constexpr int WAVE_LDS = 4 * TILE;       // K ring (2 tiles) then V ring (2 tiles)
-    static constexpr int LDS = kWaves * WAVE_LDS;
+    static constexpr int LDS = W * WAVE_LDS;
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -102,7 +102,7 @@ __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0
 // Copies one 16-row run (RUN bytes) from global to LDS.
 template <int D>
 __device__ __forceinline__ void dma_run(const uint8_t* src, uint32_t lds, int lane) {
-    using S = Shape<D>;
+    using S = Shape<D, 4>;  // the run geometry does not depend on the wave count
 #pragma unroll
     for (int i = 0; i < S::RUN_INSTR; ++i) {
         const int chunk = i * 64 + lane;
@@ -135,6 +135,11 @@ __device__ __forceinline__ float quad_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// x of lane l ^ 8 within each 16-lane row (DPP row_ror:8).
+__device__ __forceinline__ float row_xor8(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ f32x4 mfma(half8_t a, half8_t b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -142,11 +147,11 @@ __device__ __forceinline__ f32x4 mfma(half8_t a, half8_t b, f32x4 c) {
 __device__ __forceinline__ float lo_half(uint32_t w) { return float(__builtin_bit_cast(half2_t, w)[0]); }
 __device__ __forceinline__ float hi_half(uint32_t w) { return float(__builtin_bit_cast(half2_t, w)[1]); }
 
-template <int D>
-__global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* __restrict__ k_pool,
+template <int D, int W, bool PACK>
+__global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __restrict__ k_pool,
                                                                   const uint8_t* __restrict__ v_pool, int H,
                                                                   int page_size, int num_pages, DecodeArgs a) {
-    using S = Shape<D>;
+    using S = Shape<D, W>;
     constexpr int NG = S::NG, RB = S::RB, NB = S::NB;
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS];
 
@@ -160,15 +165,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
     const int64_t hb = int64_t(b) * a.n_q_heads + int64_t(g) * G;
 
     // This wave's keys: a contiguous quarter of the split.
-    const int kq = a.split_keys / kWaves;
+    const int kq = a.split_keys / W;
     const int w0 = j0 + wave * kq;
     int T = a.seq_lens[b];  // first: its latency overlaps the loads below
 
     // The query of head n16 (log2-scaled later), loaded first: the wait for the
     // page-table reads below then covers it, and the copies issued after
     // those reads are not waited for when the query is used.
-    const bool live = n16 < G;
-    const float* qh = a.q + (hb + (live ? n16 : 0)) * D;
+    // PACK (groups of at most 8 heads): B columns 0..7 carry the query's f16
+    // hi part and columns 8..15 its lo part, so one MFMA per group does both.
+    const int hcol = PACK ? (n16 & 7) : n16;  // the head this lane's B column holds
+    const bool live = hcol < G;
+    const float* qh = a.q + (hb + (live ? hcol : 0)) * D;
     float4 qv[NG][2];
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
@@ -200,7 +208,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
     T = T < 0 ? 0 : (T > a.max_seq_len ? a.max_seq_len : T);
     const int j1 = min(j0 + a.split_keys, T);
     if (j0 >= j1) {  // split past the end: an empty partial
-        for (int i = tid; i < G * D; i += kWaves * 64) a.part_acc[((hb + i / D) * Sn + s) * D + i % D] = 0.0f;
+        for (int i = tid; i < G * D; i += W * 64) a.part_acc[((hb + i / D) * Sn + s) * D + i % D] = 0.0f;
         if (tid < G) {
             a.part_m[(hb + tid) * Sn + s] = -INFINITY;
             a.part_z[(hb + tid) * Sn + s] = 0.0f;
@@ -241,7 +249,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
     // n16 for the 8 channels that k-slots (q4, 0..7) of each group hold,
     // split into f16 hi + lo.  Slot order (c0,c4,c1,c5,c2,c6,c3,c7) of the
     // dword 8*q4..8*q4+7 of the group; slots 2,3,6,7 carry x16 in A, so /16 here.
-    half8_t bq_hi[NG], bq_lo[NG];
+    half8_t bq_hi[NG], bq_lo[PACK ? 1 : NG];
     f32x4 cbias[NG];
     {
         const float qscale = a.sm_scale * kLog2e;
@@ -257,13 +265,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
                 const float v = live ? c8[order[k]] * qscale * f : 0.0f;
                 const _Float16 h = _Float16(v);
                 const _Float16 l = _Float16(v - float(h));
-                bq_hi[gi][k] = h;
-                bq_lo[gi][k] = l;
+                if (PACK) {
+                    bq_hi[gi][k] = (n16 & 8) ? l : h;
+                } else {
+                    bq_hi[gi][k] = h;
+                    bq_lo[gi][k] = l;
+                }
                 sum += (float(h) + float(l)) * ((k & 2) ? 16.0f : 1.0f);
             }
             sum = quad_sum(sum);
             const float bias = -8.0f * sum / kTwo24;
-            cbias[gi] = f32x4{bias, bias, bias, bias};
+            const float cb = (PACK && (n16 & 8)) ? 0.0f : bias;  // the offset once, in the hi column
+            cbias[gi] = f32x4{cb, cb, cb, cb};
         }
     }
     // Constant B of the context offset MFMA: -8 * 2^-24 (x16 on slots 2,3,6,7).
@@ -307,7 +320,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
                 const uint32_t w = *reinterpret_cast<const uint32_t*>(arow + 16 * gi + 4 * q4);
                 const half8_t av = unpack8(w);
                 f32x4 d = mfma(av, bq_hi[gi], cbias[gi]);
-                d = mfma(av, bq_lo[gi], d);
+                if (!PACK) d = mfma(av, bq_lo[PACK ? 0 : gi], d);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t sw = ks[i][gi >> 1];
@@ -315,7 +328,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[kb][i] = acc[i];  // log2 units / 2^24
+            for (int i = 0; i < 4; ++i) {
+                // PACK: column n16 ^ 8 holds the other part of the same head
+                // (DPP row rotate by 8); a + b = b + a, so both columns agree.
+                sc[kb][i] = PACK ? acc[i] + row_xor8(acc[i]) : acc[i];  // log2 units / 2^24
+            }
         }
         if (valid < kSub) {  // only the last tile of a wave can be partial
 #pragma unroll
@@ -404,40 +421,55 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
         if (t + 2 < n_sub) issue(v_pool, t + 2, v_ring);
     }
 
-    // ---- per-wave results: m (log2), z per head; o rows = heads 4*q4 + i
+    // ---- per-wave results: m (log2), z per head; o rows = heads 4*q4 + i.
+    // Only the G live rows go through LDS; each (wave, head) weight
+    // exp2(m_w - M) is formed once, then every output channel is a plain
+    // sum over the waves in wave order.
     z_run = quad_sum(z_run);
     __syncthreads();  // every wave is done with its tile buffers
-    float* wo = reinterpret_cast<float*>(smem);         // [kWaves][16][D]
-    float* wm = wo + kWaves * 16 * D;                     // [kWaves][16]
-    float* wz = wm + kWaves * 16;                         // [kWaves][16]
+    float* wo = reinterpret_cast<float*>(smem);  // [W][16][D]
+    float* wm = wo + W * 16 * D;                 // [W][16]
+    float* wz = wm + W * 16;                     // [W][16]
+    float* wf = wz + W * 16;                     // [W][16] weights exp2(m_w - M)
+    float* wM = wf + W * 16;                     // [16]
+    float* wZ = wM + 16;                         // [16]
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk)
+    for (int i = 0; i < 4; ++i) {
+        if (4 * q4 + i < G) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wo[(wave * 16 + 4 * q4 + i) * D + 16 * blk + n16] = o[blk][i] * kTwo24;
+            for (int blk = 0; blk < NB; ++blk) wo[(wave * 16 + 4 * q4 + i) * D + 16 * blk + n16] = o[blk][i] * kTwo24;
+        }
+    }
     if (lane < 16) {
         wm[wave * 16 + lane] = n_keys > 0 ? m_run : -INFINITY;
         wz[wave * 16 + lane] = n_keys > 0 ? z_run : 0.0f;
     }
     __syncthreads();
-    for (int i = tid; i < G * D; i += kWaves * 64) {
-        const int h = i / D, c = i % D;
+    if (tid < G) {
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w * 16 + h]);
-        float acc = 0.0f, Z = 0.0f;
+        for (int w = 0; w < W; ++w) M = fmaxf(M, wm[w * 16 + tid]);
+        float Z = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float zw = wz[w * 16 + h];
-            if (zw > 0.0f) {
-                const float f = __builtin_amdgcn_exp2f(wm[w * 16 + h] - M);
-                acc += wo[(w * 16 + h) * D + c] * f;
-                Z += zw * f;
-            }
+        for (int w = 0; w < W; ++w) {
+            const float zw = wz[w * 16 + tid];
+            const float f = zw > 0.0f ? __builtin_amdgcn_exp2f(wm[w * 16 + tid] - M) : 0.0f;
+            wf[w * 16 + tid] = f;
+            Z += zw * f;
         }
+        wM[tid] = M;
+        wZ[tid] = Z;
+    }
+    __syncthreads();
+    for (int i = tid; i < G * D; i += W * 64) {
+        const int h = i / D, c = i % D;
+        float acc = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) acc += wo[(w * 16 + h) * D + c] * wf[w * 16 + h];
         a.part_acc[((hb + h) * Sn + s) * D + c] = acc;
         if (c == 0) {
-            a.part_m[(hb + h) * Sn + s] = M * kLn2;
-            a.part_z[(hb + h) * Sn + s] = Z;
+            a.part_m[(hb + h) * Sn + s] = wM[h] * kLn2;
+            a.part_z[(hb + h) * Sn + s] = wZ[h];
         }
     }
 }
@@ -447,20 +479,38 @@ __global__ __launch_bounds__(kWaves * 64, 2) void decode_q4_mfma(const uint8_t* 
 bool decode_q4_mfma_supported(const Q4Pool& pool, const DecodeArgs& a) {
     const int G = a.n_q_heads / pool.n_kv_heads;
     return (pool.head_dim == 128 || pool.head_dim == 256) && G >= 1 && G <= 16 && pool.page_size % 16 == 0 &&
-           a.split_keys % 128 == 0 && a.split_keys / kWaves <= 16 * kMaxRuns;
+           a.split_keys % 128 == 0 && a.split_keys / 4 <= 16 * kMaxRuns;
 }
 
+// Workgroups of 4 waves, each streaming a quarter of a split of more than
+// 1024 keys; splits of 512 or 1024 keys (short contexts, where fewer and
+// larger splits would leave CUs idle) are shared by 8 waves, so each wave
+// has half as many tiles and a short context's copies are all in flight at
+// once.  The choice depends on split_keys alone, never on the batch, so a
+// sequence's partials do not depend on the sequences beside it.
 hipError_t launch_decode_q4_mfma(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s) {
-    const dim3 grid(unsigned(a.n_splits), unsigned(pool.n_kv_heads), unsigned(a.batch)), block(kWaves * 64);
+    const dim3 grid(unsigned(a.n_splits), unsigned(pool.n_kv_heads), unsigned(a.batch));
+    const bool eight = a.split_keys <= kEightWaveSplit;
+    const bool pack = a.n_q_heads / pool.n_kv_heads <= 8;
+#define KVQ_LAUNCH(D_, W_, P_)                                                                             \
+    decode_q4_mfma<D_, W_, P_><<<grid, dim3((W_) * 64), 0, s>>>(pool.k, pool.v, pool.n_kv_heads,          \
+                                                                 pool.page_size, pool.num_pages, a)
+#define KVQ_LAUNCH_W(D_, P_)          \
+    if (eight) KVQ_LAUNCH(D_, 8, P_); \
+    else KVQ_LAUNCH(D_, 4, P_)
     switch (pool.head_dim) {
         case 128:
-            decode_q4_mfma<128><<<grid, block, 0, s>>>(pool.k, pool.v, pool.n_kv_heads, pool.page_size, pool.num_pages, a);
+            if (pack) { KVQ_LAUNCH_W(128, true); }
+            else { KVQ_LAUNCH_W(128, false); }
             break;
         case 256:
-            decode_q4_mfma<256><<<grid, block, 0, s>>>(pool.k, pool.v, pool.n_kv_heads, pool.page_size, pool.num_pages, a);
+            if (pack) { KVQ_LAUNCH_W(256, true); }
+            else { KVQ_LAUNCH_W(256, false); }
             break;
         default: return hipErrorInvalidValue;
     }
+#undef KVQ_LAUNCH_W
+#undef KVQ_LAUNCH
     return hipGetLastError();
 }
 

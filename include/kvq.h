@@ -37,8 +37,9 @@
  *  - Validation: an invalid argument returns KVQ_ERR_INVALID_ARG (or
  *    KVQ_ERR_UNSUPPORTED for a valid but unimplemented shape) and launches
  *    nothing.  There is no fallback path.
- *  - Determinism: the split partition of a sequence depends only on its own
- *    length and split_keys, the merge adds the partials in a fixed order that
+ *  - Determinism: the split partition of a sequence, and the order in which
+ *    the kernels combine its keys, depend only on its own length, head_dim and
+ *    split_keys, the merge adds the partials in a fixed order that
  *    depends only on the number of splits, and no atomics are used, so outputs
  *    are bit-reproducible and independent of the other sequences in the
  *    batch.
