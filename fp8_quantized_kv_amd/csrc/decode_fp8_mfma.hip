@@ -311,6 +311,7 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
                     sc[kb][i] = half ? other[kb][i] + part[kb][i] : part[kb][i] + other[kb][i];
         }
         if (valid < kTile) {  // only the last tile can be partial
+            asm volatile("" ::: "memory");  // a real branch: keep the full tiles free of selects
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll

@@ -335,6 +335,7 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
             }
         }
         if (valid < kSub) {  // only the last tile of a wave can be partial
+            asm volatile("" ::: "memory");  // a real branch: keep the full tiles free of selects
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
