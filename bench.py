@@ -34,8 +34,8 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 # passes (KiB per dispatch), scaled by what the same counters read for a 256 MiB device copy
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); valid only for the kernel source they were taken on.
 TRAFFIC = {
-    "3fd90bbd9a4b3ab6572161ec806edd1eb4a0aae04108d7aed69bd04ff2c41624": {
-        "fetch_kib": 147697.0, "write_kib": 3264.28, "fetch_scale": 2.0, "write_scale": 1.0,
+    "6cfe797e1ddf200fa9f9193d3279117d0cf847abaad8938dcdab4e3983b43c72": {
+        "fetch_kib": 147699.375, "write_kib": 3264.3125, "fetch_scale": 2.0, "write_scale": 1.0,
         "profile": "profiles/decode_q4_mfma_gqa_q4_262k.md"},
 }
 DECODE_SOURCE = os.path.join("fp8_quantized_kv_amd", "csrc", "decode_q4_mfma.hip")
