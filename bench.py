@@ -62,21 +62,24 @@ def _log(*a):
 
 class _Bench:
     """Per-layer raw C-ABI calls of one step: a list of (entry point, args)
-    per layer, with the index of the decode call."""
+    per layer, with the index of the decode call (and of other calls to time)."""
 
     DECODE = None
+    EXTRA_TIMED = {}  # name -> call index, timed like the decode
 
-    def step(self, events=None):
+    def step(self, events=None, which=None):
         """Enqueue one step; if events is a list of (start, end) pairs, bracket
-        each decode launch with them (on the stream the kernels run on)."""
+        call `which` (default: the decode) of each layer with them, on the
+        stream the kernels run on."""
         L = self.kvq.lib
+        which = self.DECODE if which is None else which
         for layer, calls in enumerate(self.raw):
             rc = 0
             for i, (fn, args) in enumerate(calls):
-                if events is not None and i == self.DECODE:
+                if events is not None and i == which:
                     events[layer][0].record()
                 rc |= getattr(L, fn)(*args)
-                if events is not None and i == self.DECODE:
+                if events is not None and i == which:
                     events[layer][1].record()
             if rc:
                 raise RuntimeError(f"launch failed in layer {layer}")
@@ -237,6 +240,86 @@ class MlaBench(_Bench):
         return self.T * w.n_heads * 2 * (w.head_dim + w.kv_lora)
 
 
+class RaggedBench(_Bench):
+    """The ragged batch: 16 sequences of seeded lengths over a shuffled paged
+    pool (one layer).  Step: the 2048-token prefill chunk of a 17th sequence
+    packed into its reserved pages, each sequence's new token stored, the
+    queries rotated, decode over the batch, merge."""
+
+    DECODE = 3
+    EXTRA_TIMED = {"chunk_store": 0}
+
+    def __init__(self, w, device="cuda"):
+        import numpy as np
+        import torch
+
+        import fp8_quantized_kv_amd as kvq
+        import workloads as wl
+        self.w, self.kvq = w, kvq
+        lens = wl.seq_lens(w)
+        self.lens = lens
+        self.T = max(lens)
+        lay = wl.page_layout(w, lens)
+        self.page_table = lay.page_table.to(device)
+        self.seq_lens = torch.tensor(lens, dtype=torch.int32, device=device)
+        c = kvq.Q4Cache(lay.num_pages, w.n_kv_heads, w.head_dim, w.page_size, device)
+        self.cache = c
+        off, k_last, v_last, s_last = 0, [], [], []
+        for b, T in enumerate(lens):
+            k, v = wl.q4_kv_tokens(w, 0, off, T, device)
+            off += T
+            slots = wl.slots_for(lay.page_table[b], np.arange(T), w.page_size).to(device)
+            kvq.kvq_store(c, k, v, slots)
+            k_last.append(k[-1:])
+            v_last.append(v[-1:])
+            s_last.append(slots[-1:])
+        self.k_new, self.v_new, self.slot_new = torch.cat(k_last), torch.cat(v_last), torch.cat(s_last)
+        self.k_chunk, self.v_chunk = wl.q4_prefill_chunk(w, 0, device)
+        pages = lay.prefill_pages.to(torch.int64)
+        j = torch.arange(w.prefill_chunk, dtype=torch.int64)
+        self.slot_chunk = (pages[j // w.page_size] * w.page_size + j % w.page_size).to(device)
+        self.q = wl.q4_query(w, 0, device)
+        acc_shape, mz_shape = kvq.partial_shapes(c, w.batch, w.n_q_heads, self.T, w.split_keys)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.q_rot = torch.empty_like(self.q)
+        self.pa, self.pm, self.pz = torch.empty(acc_shape, **f32), torch.empty(mz_shape, **f32), torch.empty(mz_shape, **f32)
+        self.out = torch.empty((w.batch, w.n_q_heads, w.head_dim), **f32)
+        self.lse = torch.empty((w.batch, w.n_q_heads), **f32)
+        kvq.kvq_store(c, self.k_chunk, self.v_chunk, self.slot_chunk)
+        kvq.kvq_store(c, self.k_new, self.v_new, self.slot_new)
+        kvq.kvq_rotate_q(self.q, out=self.q_rot)
+        kvq.kvq_decode_attn(c, self.q_rot, self.page_table, self.seq_lens, self.T, w.sm_scale, w.split_keys,
+                            self.pa, self.pm, self.pz)
+        kvq.kvq_merge(c, self.pa, self.pm, self.pz, self.seq_lens, self.T, w.split_keys, out=self.out, lse=self.lse)
+        torch.cuda.synchronize()
+        P = ctypes.c_void_p
+        stream = P(torch.cuda.current_stream().cuda_stream)
+        d = ctypes.byref(c.desc)
+        dt = kvq._DTYPES[self.k_new.dtype]
+        B, Hq, D = w.batch, w.n_q_heads, w.head_dim
+        self.raw = [[
+            ("kvq_store", (d, P(self.k_chunk.data_ptr()), P(self.v_chunk.data_ptr()), dt, P(self.slot_chunk.data_ptr()),
+                           w.prefill_chunk, stream)),
+            ("kvq_store", (d, P(self.k_new.data_ptr()), P(self.v_new.data_ptr()), dt, P(self.slot_new.data_ptr()), B,
+                           stream)),
+            ("kvq_rotate_q", (P(self.q.data_ptr()), 0, P(self.q_rot.data_ptr()), B * Hq, D, stream)),
+            ("kvq_decode_attn", (d, P(self.q_rot.data_ptr()), Hq, P(self.page_table.data_ptr()),
+                                 self.page_table.shape[1], P(self.seq_lens.data_ptr()), B, self.T,
+                                 ctypes.c_float(w.sm_scale), w.split_keys, P(self.pa.data_ptr()),
+                                 P(self.pm.data_ptr()), P(self.pz.data_ptr()), stream)),
+            ("kvq_merge", (d, P(self.pa.data_ptr()), P(self.pm.data_ptr()), P(self.pz.data_ptr()),
+                           P(self.seq_lens.data_ptr()), B, Hq, self.T, w.split_keys, 1, P(self.out.data_ptr()),
+                           P(self.lse.data_ptr()), stream)),
+        ]]
+
+    @property
+    def kv_bytes_per_layer(self):
+        w = self.w
+        return sum(self.lens) * w.n_kv_heads * 2 * w.row_bytes
+
+    flops_per_layer = None
+
+
 def time_steps(b, steps, warmup):
     """ms per step of `steps` uninstrumented steps after `warmup` warm-up steps."""
     import torch
@@ -255,16 +338,17 @@ def time_steps(b, steps, warmup):
     return t_start.elapsed_time(t_end) / steps, wall
 
 
-def time_decode(b, steps):
-    """Average decode launch in ms: `steps` more steps with every decode
-    launch bracketed by HIP events.  (Event records stall the queue for a few
-    microseconds, so these steps are not the ones whose time is reported.)"""
+def time_decode(b, steps, which=None):
+    """Average launch of call `which` (default: the decode) in ms: `steps` more
+    steps with that launch bracketed by HIP events in every layer.  (Event
+    records stall the queue for a few microseconds, so these steps are not
+    the ones whose time is reported.)"""
     import torch
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(b.w.n_layers)] for _ in range(steps)]
     torch.cuda.synchronize()
     for s in range(steps):
-        b.step(ev[s])
+        b.step(ev[s], which)
     torch.cuda.synchronize()
     d = [e0.elapsed_time(e1) for row in ev for (e0, e1) in row]
     return sum(d) / len(d)
@@ -279,12 +363,15 @@ def measure(b, steps, warmup):
          "step_gbs": kvb * L / (ms_step * 1e-3) / 1e9, "decode_gbs": kvb / (dec_ms * 1e-3) / 1e9, "wall_s": wall}
     if b.flops_per_layer:
         r["decode_tflops"] = b.flops_per_layer / (dec_ms * 1e-3) / 1e12
+    for name, idx in b.EXTRA_TIMED.items():
+        r[name + "_us"] = time_decode(b, steps, idx) * 1e3
     return r
 
 
-def cpu_baseline(w, sample_tokens, repeats=3):
+def cpu_baseline(w, sample_tokens, min_seconds=10.0, max_repeats=60):
     """The oracle (fp64, OpenMP over heads) on one layer of the workload,
-    restricted to its first `sample_tokens` positions; median of `repeats`."""
+    restricted to its first `sample_tokens` positions; repeated until about
+    `min_seconds` of CPU work have run, median reported."""
     import numpy as np
 
     import oracle
@@ -300,16 +387,17 @@ def cpu_baseline(w, sample_tokens, repeats=3):
         wl.plant(w, k, q, t0)
         oracle.q4_store(kp, vp, k.float().numpy(), v.float().numpy(), np.arange(t0, t0 + n), w.page_size)
     times = []
-    for _ in range(repeats):
+    while len(times) < max_repeats and (len(times) < 3 or sum(times) < min_seconds):
         t0 = time.perf_counter()
         oracle.q4_attention(kp, vp, q.numpy(), lay.page_table.numpy(), np.array([T], np.int32), w.sm_scale)
         times.append(time.perf_counter() - t0)
+    repeats = len(times)
     dt = sorted(times)[len(times) // 2]
     kv_bytes = T * w.n_kv_heads * 2 * w.row_bytes
     threads = min(oracle.num_threads(), w.batch * w.n_q_heads)
     return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"layer 0 of {w.name}, first {T} positions, all {w.n_q_heads} query heads "
-                      f"(decode attention + merge in fp64; median {dt:.2f} s of {repeats})",
+                      f"(decode attention + merge in fp64; median {dt:.3f} s of {repeats} runs, {sum(times):.1f} s in all)",
             "seconds": round(dt, 3)}
 
 
@@ -358,19 +446,25 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extras:
         extras = {}
-        for name, cls in (("gqa_q4_32k", Q4Bench), ("mla_fp8_262k", MlaBench)):
+        for name, cls in (("gqa_q4_32k", Q4Bench), ("ragged_q4_b16", RaggedBench), ("mla_fp8_262k", MlaBench)):
             wx = wl.WORKLOADS[name]
             _log(f"bench: side measurement {name}")
             bx = cls(wx)
             steps = max(3, min(args.steps, 10)) if cls is MlaBench else args.steps
             mx = measure(bx, steps, args.warmup)
-            e = {"layers": wx.n_layers, "seq_len": wx.seq_len, "split_keys": wx.split_keys, "steps": steps,
+            e = {"layers": wx.n_layers, "seq_len": wx.seq_len or f"{min(bx.lens)}..{max(bx.lens)} x {len(bx.lens)}",
+                 "split_keys": wx.split_keys, "steps": steps,
                  "kv_bytes_per_layer": bx.kv_bytes_per_layer, "us_per_layer": round(mx["us_per_layer"], 3),
                  "step_kv_gbs": round(mx["step_gbs"], 2), "decode_us": round(mx["decode_us"], 3),
                  "decode_kv_gbs": round(mx["decode_gbs"], 2),
                  "decode_frac_hbm": round(mx["decode_gbs"] / HBM_PEAK_GBS, 4)}
             if "decode_tflops" in mx:
                 e["decode_tflops"] = round(mx["decode_tflops"], 2)
+            if "chunk_store_us" in mx:
+                e["chunk_store_us"] = round(mx["chunk_store_us"], 3)
+                # 2048 tokens x 4 KV heads x (K, V): bf16 rows in, 144-byte rows out
+                cb = wx.prefill_chunk * wx.n_kv_heads * 2 * (2 * wx.head_dim + wx.row_bytes)
+                e["chunk_store_gbs"] = round(cb / (mx["chunk_store_us"] * 1e-6) / 1e9, 2)
             extras[name] = e
             del bx
             torch.cuda.empty_cache()
