@@ -236,7 +236,8 @@ def test_mha_and_large_group(kvq):
         _check_q4(Q4Case(w, [1500]), 512)
 
 
-@pytest.mark.parametrize("D,page_size,hq,hkv", [(512, 16, 8, 2), (256, 8, 12, 2), (64, 16, 4, 4), (128, 32, 10, 1)])
+@pytest.mark.parametrize("D,page_size,hq,hkv", [(512, 16, 8, 2), (256, 8, 12, 2), (64, 16, 4, 4), (128, 32, 10, 1),
+                                                 (256, 64, 32, 4)])
 def test_other_shapes(kvq, D, page_size, hq, hkv):
     """Head sizes and page sizes on both kernel paths (the matrix-core kernel
     takes head_dim 128/256 with pages of a multiple of 16 tokens; the others
@@ -244,6 +245,45 @@ def test_other_shapes(kvq, D, page_size, hq, hkv):
     w = wl.shrink(wl.RAGGED, prefill_chunk=0, head_dim=D, page_size=page_size, n_q_heads=hq, n_kv_heads=hkv,
                   heavy_channels=D // 16)
     _check_q4(Q4Case(w, [1300, 2600, 40]), 1024)
+
+
+def test_pool_beyond_4gib(kvq):
+    """Byte offsets above 2^32: a sequence whose pages sit at the far end of
+    a pool of more than 4 GiB per K and V (the oracle sees the same rows in a
+    compact pool through its own page table)."""
+    w = wl.shrink(wl.GQA_32K, n_layers=1, seq_len=3000)
+    T, ps = w.seq_len, w.page_size
+    page_bytes = w.n_kv_heads * ps * w.row_bytes
+    n_far = (1 << 32) // page_bytes + 64            # pages past the 4 GiB mark
+    n_used = -(-T // ps)
+    num_pages = n_far + n_used
+    _say(f"pool of {num_pages} pages = {num_pages * page_bytes / 2**30:.2f} GiB per K and V")
+    cache = kvq.Q4Cache(num_pages, w.n_kv_heads, w.head_dim, ps, "cuda")
+    pt_far = torch.arange(n_far, n_far + n_used, dtype=torch.int32).flip(0).unsqueeze(0)  # reversed order
+    k, v = wl.q4_kv_tokens(w, 0, 0, T, "cuda")
+    q = wl.q4_query(w, 0, "cuda")
+    slots = wl.slots_for(pt_far[0], np.arange(T), ps)
+    kvq.kvq_store(cache, k, v, slots.cuda())
+    pt_d, sl = pt_far.cuda(), torch.tensor([T], dtype=torch.int32, device="cuda")
+    q_rot = kvq.kvq_rotate_q(q)
+    pa, pm, pz = kvq.kvq_decode_attn(cache, q_rot, pt_d, sl, T, w.sm_scale, 512)
+    o, _ = kvq.kvq_merge(cache, pa, pm, pz, sl, T, 512)
+    torch.cuda.synchronize()
+    # the same rows in a compact pool for the oracle
+    pt_c = torch.arange(n_used, dtype=torch.int32).unsqueeze(0)
+    shape = oracle.q4_pool_shape(n_used, w.n_kv_heads, ps, w.head_dim)
+    kref, vref = np.zeros(shape, np.uint8), np.zeros(shape, np.uint8)
+    oracle.q4_store(kref, vref, k.float().cpu().numpy(), v.float().cpu().numpy(),
+                    wl.slots_for(pt_c[0], np.arange(T), ps).numpy(), ps)
+    far = pt_far[0].to(torch.int64).cuda()
+    assert np.array_equal(cache.k_pool[far].cpu().numpy(), kref)
+    assert np.array_equal(cache.v_pool[far].cpu().numpy(), vref)
+    ro, _ = oracle.q4_attention(kref, vref, q.cpu().numpy(), pt_c.numpy(), np.array([T], np.int32), w.sm_scale)
+    err = rel_err(o.cpu().numpy(), ro)
+    _say(f"  max_rel_err={err.max():.2e}")
+    assert err.max() < TOL
+    del cache
+    torch.cuda.empty_cache()
 
 
 def test_empty_splits_are_written_empty(kvq):
