@@ -32,23 +32,28 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 
 # HBM bytes per decode launch of the headline workload from rocprofv3 FETCH_SIZE and WRITE_SIZE
 # passes (KiB per dispatch), scaled by what the same counters read for a 256 MiB device copy
-# (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); valid only for the kernel source they were taken on.
+# (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); valid only for the kernel sources they were taken on
+# (keyed by the sha256 of the kernel file followed by the device-helper header it includes).
 TRAFFIC = {
-    "6cfe797e1ddf200fa9f9193d3279117d0cf847abaad8938dcdab4e3983b43c72": {
-        "fetch_kib": 147699.375, "write_kib": 3264.3125, "fetch_scale": 2.0, "write_scale": 1.0,
+    "dd5c946ad5058592b67cad1db027e8dbd9ca196148aa2b412a283bee73c8f56a": {
+        "fetch_kib": 147699.4375, "write_kib": 3264.3125, "fetch_scale": 2.0, "write_scale": 1.0,
         "profile": "profiles/decode_q4_mfma_gqa_q4_262k.md"},
 }
-DECODE_SOURCE = os.path.join("fp8_quantized_kv_amd", "csrc", "decode_q4_mfma.hip")
+DECODE_SOURCES = (os.path.join("fp8_quantized_kv_amd", "csrc", "decode_q4_mfma.hip"),
+                  os.path.join("fp8_quantized_kv_amd", "csrc", "mfma_common.h"))
 
 
 def decode_traffic():
-    """Calibrated HBM bytes per launch if the counters match the current kernel source, else None."""
+    """Calibrated HBM bytes per launch if the counters match the current kernel sources, else None."""
     import hashlib
+    h = hashlib.sha256()
     try:
-        with open(os.path.join(ROOT, DECODE_SOURCE), "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
+        for src in DECODE_SOURCES:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
     except OSError:
         return None
+    digest = h.hexdigest()
     t = TRAFFIC.get(digest)
     if t is None:
         return None

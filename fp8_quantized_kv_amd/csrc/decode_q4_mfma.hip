@@ -43,23 +43,16 @@
 //    as MFMA k-slots; the same 6-op unpack makes the B operand.  A = P times
 //    the keys' V scale for the group (f16), and a second MFMA against a
 //    constant B removes the +8 offset.
-#include "internal.h"
-
-#pragma clang diagnostic ignored "-Winline-asm"
+#include "mfma_common.h"
 
 namespace kvq {
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+using namespace mx;
 
 constexpr int kEightWaveSplit = 1024;  // splits up to this many keys use 8-wave workgroups
 constexpr int kSub = 32;          // keys per sub-tile
 constexpr int kMaxRuns = 128;     // 16-key runs per wave (split_keys <= 8192)
-constexpr float kTwo24 = 16777216.0f;
 constexpr float kRescale = 6.0f;  // log2 headroom before the running max moves
 
 template <int D, int W>
@@ -75,30 +68,6 @@ struct Shape {
     static constexpr int LDS = W * WAVE_LDS;
 };
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return uint32_t(uintptr_t((__attribute__((address_space(3))) const void*)(p)));
-}
-
-// 16 bytes per lane from global (SGPR base + VGPR offset) to LDS at
-// m0 + 16 * lane.  Issued from asm so the compiler does not serialise it.
-// base and lds must be wave-uniform; they are moved to SGPRs here.
-__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
-    const uint64_t b = uint64_t(uintptr_t(base));
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(b));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(b >> 32));
-    const uint64_t sb = (uint64_t(hi) << 32) | lo;
-    const uint32_t sl = __builtin_amdgcn_readfirstlane(lds);
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(sl)
-                 : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
 // Copies one 16-row run (RUN bytes) from global to LDS.
 template <int D>
 __device__ __forceinline__ void dma_run(const uint8_t* src, uint32_t lds, int lane) {
@@ -110,42 +79,6 @@ __device__ __forceinline__ void dma_run(const uint8_t* src, uint32_t lds, int la
             dma16(src, uint32_t(chunk * 16), lds + uint32_t(i * 1024));
     }
 }
-
-// 8 codes of a dword as MFMA k-slots: (c0,c4) (c1,c5)x16 (c2,c6) (c3,c7)x16,
-// each the f16 subnormal (code + 8) * 2^-24 (x16 where marked).
-__device__ __forceinline__ half8_t unpack8(uint32_t w) {
-    constexpr uint32_t X = 0x88888888u;  // two's complement -> offset binary, per nibble
-    const uint32_t w2 = w >> 8;
-    const u32x4 r = {(w ^ X) & 0x000F000Fu, (w ^ X) & 0x00F000F0u, (w2 ^ X) & 0x000F000Fu, (w2 ^ X) & 0x00F000F0u};
-    return __builtin_bit_cast(half8_t, r);
-}
-
-// Max / sum of a value over the four lanes l, l^16, l^32, l^48 with
-// cross-lane moves on the vector ALU (no LDS round trip).
-__device__ __forceinline__ float quad_max(float x) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float quad_sum(float x) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// x of lane l ^ 8 within each 16-lane row (DPP row_ror:8).
-__device__ __forceinline__ float row_xor8(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ f32x4 mfma(half8_t a, half8_t b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float lo_half(uint32_t w) { return float(__builtin_bit_cast(half2_t, w)[0]); }
-__device__ __forceinline__ float hi_half(uint32_t w) { return float(__builtin_bit_cast(half2_t, w)[1]); }
 
 template <int D, int W, bool PACK>
 __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __restrict__ k_pool,

@@ -147,6 +147,12 @@ struct DecodeArgs {
 bool decode_q4_mfma_supported(const Q4Pool& pool, const DecodeArgs& a);
 hipError_t launch_decode_q4_mfma(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s);
 
+// Matrix-core kernel for head_dim 256 and groups of up to 8 query heads, a
+// pair of waves sharing each key tile by channel halves (split_keys a
+// multiple of 128, at most 1024).
+bool decode_q4_pair_supported(const Q4Pool& pool, const DecodeArgs& a);
+hipError_t launch_decode_q4_pair(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s);
+
 // Matrix-core kernel for the fp8 latent cache (512 + 64, pages of a
 // multiple of 16 tokens, split_keys <= 2048).
 bool decode_fp8_mfma_supported(const Fp8Pool& pool, const DecodeArgs& a);

@@ -160,8 +160,10 @@ def test_tiny_partials_match_oracle_chunks(kvq):
     assert rel_err(na, nr).max() < TOL
 
 
-@pytest.mark.parametrize("split_keys", [512, 1024, 2048])
+@pytest.mark.parametrize("split_keys", [512, 1024, 2048, 8192])
 def test_gqa_several_splits_and_tail(kvq, split_keys):
+    """Splits of 512 and 1024 keys run on the wave-pair kernel, 2048 and 8192
+    on the single-wave one (four waves of 512 and 2048 keys)."""
     w = wl.shrink(wl.GQA_32K, n_layers=1, seq_len=5000)
     case = Q4Case(w, [5000])
     assert np.array_equal(case.cache.k_pool.cpu().numpy(), case.k_ref)
