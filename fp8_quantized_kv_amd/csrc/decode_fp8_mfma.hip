@@ -24,10 +24,12 @@
 //  * Staging: the tile's rows (two 16-row page runs of 576 code bytes) and
 //    their scales go global -> registers -> LDS, one iteration ahead of use.
 //    On the way, codes 0x7F / 0xFF (NaN) are zeroed with byte-wise integer
-//    arithmetic, so every wave reads clean codes.  Rows are padded to 584
-//    bytes, which makes the column reads below free of bank conflicts.
-//  * Scores: A = 16 keys x 32 channels (8 code bytes per lane converted by
-//    v_cvt_scalef32_pk_f16_fp8, exact: every e4m3 value is an f16), B = the
+//    arithmetic and every code is converted to f16 by
+//    v_cvt_scalef32_pk_f16_fp8 (exact: every e4m3 value is an f16), once
+//    per workgroup: the four pairs that use a code read it converted.  Rows
+//    are 1168 bytes apart in LDS (576 f16 + 16), so the 16 rows an operand
+//    read touches at one column start in distinct banks.
+//  * Scores: A = 16 keys x 32 channels (16 bytes of f16 per lane), B = the
 //    query pre-scaled by sm_scale*log2(e), split into f16 hi + lo parts; the
 //    latent and rope parts meet their scales in fp32.  The pair exchanges
 //    its two partial scores through LDS and both add them in the same order,
@@ -39,8 +41,9 @@
 //    own keys, so no exchange is needed) in f16, scaled by 2^-E with E a
 //    running exponent of the largest latent scale seen, which keeps A inside
 //    the f16 range whatever the rows' magnitude; B = 8 keys x 1 channel of
-//    latent codes gathered by ds_read_b64_tr_b8 (source lanes 2k and 2k+1
-//    address key k at channel offsets 0 and 8) and converted to f16.
+//    the latent gathered by two ds_read_b64_tr_b16 (source lane 4e + m of a
+//    16-lane group addresses key slot e at channels 4m .. 4m + 3, so lane j
+//    receives channel j of keys e = 0..3; the second read takes slots 4..7).
 #include "internal.h"
 
 namespace kvq {
@@ -52,15 +55,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kL = 512, kR = 64, kD = kL + kR;  // latent, rope, row
 constexpr int kWaves = 8;                            // 4 pairs
 constexpr int kThreads = kWaves * 64;
 constexpr int kHeadsWG = 16 * (kWaves / 2);
 constexpr int kTile = 32;                            // keys per tile
-constexpr int kPitch = 584;                          // LDS bytes per row
+constexpr int kPitch = 1168;                         // LDS bytes per row: 576 f16 + 16
 constexpr int kScaleOff = kTile * kPitch;            // scales after the rows
-constexpr int kStage = kScaleOff + kTile * 8;        // 18944 bytes
+constexpr int kStage = kScaleOff + kTile * 8;        // 37632 bytes
 constexpr int kXOff = 2 * kStage;                    // partial-score exchange: [wave][lane][8] f32
 constexpr int kLds = kXOff + kWaves * 64 * 8 * 4;
 constexpr int kChunks = kTile * kD / 16;             // 16-byte code chunks per tile (1152)
@@ -208,9 +213,9 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
 #pragma unroll
                     for (int e = 0; e < 4; ++e) w[e] = clear_nan_codes(w[e]);
                 }
-                u32x2* d = reinterpret_cast<u32x2*>(st + chunk_row(i) * kPitch + 16 * chunk_col(i));
-                d[0] = u32x2{w[0], w[1]};
-                d[1] = u32x2{w[2], w[3]};
+                half8_t* d = reinterpret_cast<half8_t*>(st + chunk_row(i) * kPitch + 32 * chunk_col(i));
+                d[0] = cvt8(w[0], w[1]);
+                d[1] = cvt8(w[2], w[3]);
             } else if (has_scale) {
                 *reinterpret_cast<u32x4*>(st + kScaleOff + 16 * (tid - 128)) = stg[i];
             }
@@ -248,11 +253,10 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
     float z_run = 0.0f;       // this lane's share of the running sum
     int e_run = -1000;        // running exponent of the largest latent scale (unset)
 
-    // tr_b8 source row of this lane: key K(q4, k) with k = n16 >> 1, at
-    // channel offset 8 * (n16 & 1); K(q, k) = 4q + k (k < 4) or 16 + 4q + k - 4.
-    const int trk = n16 >> 1;
-    const int tr_key = trk < 4 ? 4 * q4 + trk : 16 + 4 * q4 + trk - 4;
-    const int tr_off = tr_key * kPitch + 8 * (n16 & 1) + half * (kL / 2);
+    // tr_b16 source of this lane: key slot n16 >> 2 of its quarter (key
+    // 4 q4 + (n16 >> 2), then 16 + the same for slots 4..7) at channels
+    // 4 (n16 & 3) .. +3 of the 16-channel block, this wave's latent half.
+    const int tr_off = (4 * q4 + (n16 >> 2)) * kPitch + 2 * (4 * (n16 & 3) + half * (kL / 2));
     float* xmine = reinterpret_cast<float*>(smem + kXOff) + (wave * 64 + lane) * 8;
     const float* xpart = reinterpret_cast<const float*>(smem + kXOff) + ((wave ^ 1) * 64 + lane) * 8;
 
@@ -266,12 +270,11 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
         float part[2][4], scl[2][4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const uint8_t* krow = st + (16 * kb + n16) * kPitch + 32 * g0 + 8 * q4;
+            const uint8_t* krow = st + (16 * kb + n16) * kPitch + 2 * (32 * g0 + 8 * q4);
             f32x4 accE = {0.0f, 0.0f, 0.0f, 0.0f}, accO = accE, acc78 = accE;
 #pragma unroll
             for (int gl = 0; gl < kQG; ++gl) {
-                const u32x2 w = *reinterpret_cast<const u32x2*>(krow + 32 * gl);
-                const half8_t av = cvt8(w[0], w[1]);
+                const half8_t av = *reinterpret_cast<const half8_t*>(krow + 64 * gl);
                 if (gl >= 7) {
                     acc78 = mfma(av, bq_hi[gl], acc78);
                     acc78 = mfma(av, bq_lo[gl], acc78);
@@ -364,9 +367,12 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
         // ---- context: this wave's 16 blocks of 16 latent channels
 #pragma unroll
         for (int cb = 0; cb < kNBW; ++cb) {
-            const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (__attribute__((address_space(3))) i32x2*)(st + tr_off + 16 * cb));
-            o[cb] = mfma(av, cvt8(uint32_t(v[0]), uint32_t(v[1])), o[cb]);
+            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(st + tr_off + 32 * cb));
+            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(st + tr_off + 16 * kPitch + 32 * cb));
+            const half8_t bv = __builtin_bit_cast(half8_t, i16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+            o[cb] = mfma(av, bv, o[cb]);
         }
 
         // ---- next tile: registers -> LDS (the other stage), then the one after into registers
