@@ -42,18 +42,38 @@ def test_inv_sqrt32_is_correctly_rounded():
     assert struct.unpack("<I", struct.pack("<f", float(c)))[0] == 0x3E3504F3
 
 
+# Rounding a float32 to a format that keeps its top k mantissa bits depends on
+# those bits, the next (round) bit and whether any bit below it is set.  For
+# binary16 (k <= 10) and e4m3 (k <= 3) the round bit is bit 12 or higher, so
+# bits 0..6 only ever act as sticky bits: the float32 patterns whose low 7
+# bits are 0, 1, 0x40 or 0x7F, with every higher bit pattern enumerated,
+# contain every rounding case of every float32 (64 times fewer values than
+# all of them).
+_LOW7 = np.array([0x00, 0x01, 0x40, 0x7F], np.uint32)
+
+
+def _rounding_classes(lo, hi, chunk=1 << 22):
+    """Chunks of float32 bit patterns in [lo, hi) with low 7 bits in _LOW7."""
+    for h0 in range(lo >> 7, (hi + 127) >> 7, chunk):
+        high = np.arange(h0, min(h0 + chunk, (hi + 127) >> 7), dtype=np.uint32)
+        bits = ((high[:, None] << np.uint32(7)) | _LOW7[None, :]).ravel()
+        yield bits[(bits >= lo) & (bits < hi)]
+
+
 def test_f16_exhaustive_against_library():
-    """binary16 RNE of every positive float32 in the binades where rounding is
-    not trivially 0 or infinity (2^-26 .. 2^16), against torch's cast."""
-    step = 1 << 25
+    """binary16 RNE of every rounding case of a positive float32 in the
+    binades where rounding is not trivially 0 or infinity (2^-26 .. 2^16),
+    against torch's cast."""
     lo, hi = 0x32800000, 0x47800000  # 2^-26 .. 2^16
-    for start in range(lo, hi, step):
-        bits = np.arange(start, min(start + step, hi), dtype=np.uint32)
+    n = 0
+    for bits in _rounding_classes(lo, hi):
         x = bits.view(np.float32)
         ours = oracle.f32_to_f16_bits(x)
         ref = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
         bad = np.nonzero(ours != ref)[0]
         assert bad.size == 0, f"f16 mismatch at {x[bad[:4]]}"
+        n += bits.size
+    assert n == (hi - lo) // 32
 
 
 def test_f16_sign_and_specials():
@@ -271,12 +291,11 @@ def test_e4m3_ties_and_saturation():
 
 
 def test_e4m3_exhaustive_against_library():
-    """Every float32 with |v| <= 448 against torch's RNE cast; every float32
-    in (448, 2^31) saturates.  Negative values by symmetry on the same bits."""
-    step = 1 << 26
+    """Every rounding case of a float32 with |v| <= 448 (see _rounding_classes)
+    against torch's RNE cast; float32 values in (448, 2^31) saturate.
+    Negative values on the same bits with the sign set."""
     top = 0x43E00000  # 448.0
-    for start in range(0, top + 1, step):
-        bits = np.arange(start, min(start + step, top + 1), dtype=np.uint32)
+    for bits in _rounding_classes(0, top + 1):
         for sign in (0, 0x80000000):
             x = (bits | np.uint32(sign)).view(np.float32)
             ours = oracle.e4m3_encode(x)
