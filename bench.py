@@ -10,12 +10,15 @@ working set (4.8 GB at 262K) is far above the 256 MB Infinity Cache.
 
 Prints one JSON line: whole-step KV-read throughput (algorithmic bytes:
 T x KV heads x (K, V) x 144 B per layer) and microseconds per layer, from
-uninstrumented steps; a roofline object for the decode kernel, from as many
-further steps whose decode launches are bracketed by HIP events on the
-stream they run on (event records stall the queue briefly, so those steps
-are kept out of the step time); side measurements of the 32K 4-bit and the
-262K fp8-latent workloads; and the CPU oracle timed on a bounded sample of
-the headline workload.
+uninstrumented steps; decode + merge alone per layer; the step replayed as
+one HIP graph per layer (each replay first checked against the eager step's
+outputs, bit for bit; not faster than the eager launches, which already
+keep the queue full); a roofline object for the
+decode kernel, from further eager steps whose decode launches are bracketed
+by HIP events on the stream they run on (event records stall the queue
+briefly, so those steps are kept out of the step time); side measurements
+of the 32K 4-bit, the ragged-batch and the 262K fp8-latent workloads; and
+the CPU oracle timed on a bounded sample of the headline workload.
 """
 import argparse
 import ctypes
@@ -70,17 +73,24 @@ class _Bench:
     per layer, with the index of the decode call (and of other calls to time)."""
 
     DECODE = None
+    DECODE_MERGE = ()  # indices of the decode and merge calls
     EXTRA_TIMED = {}  # name -> call index, timed like the decode
 
-    def step(self, events=None, which=None):
+    def step(self, events=None, which=None, stream=None, only=None):
         """Enqueue one step; if events is a list of (start, end) pairs, bracket
         call `which` (default: the decode) of each layer with them, on the
-        stream the kernels run on."""
+        stream the kernels run on.  `stream` (a raw handle) replaces the
+        stream the calls were built with; `only` restricts the step to the
+        calls with those indices."""
         L = self.kvq.lib
         which = self.DECODE if which is None else which
         for layer, calls in enumerate(self.raw):
             rc = 0
             for i, (fn, args) in enumerate(calls):
+                if only is not None and i not in only:
+                    continue
+                if stream is not None:
+                    args = args[:-1] + (stream,)
                 if events is not None and i == which:
                     events[layer][0].record()
                 rc |= getattr(L, fn)(*args)
@@ -89,6 +99,10 @@ class _Bench:
             if rc:
                 raise RuntimeError(f"launch failed in layer {layer}")
 
+    def outputs(self):
+        """Copies of the step's outputs (every layer's merged context and lse)."""
+        return self.out.clone(), self.lse.clone()
+
 
 class Q4Bench(_Bench):
     """Every layer's cache, query and buffers for one 4-bit workload, plus the
@@ -96,6 +110,7 @@ class Q4Bench(_Bench):
     through the binding's checks).  Step per layer: store, rotate, decode, merge."""
 
     DECODE = 2
+    DECODE_MERGE = (2, 3)
 
     def __init__(self, w, device="cuda"):
         import numpy as np
@@ -175,6 +190,7 @@ class MlaBench(_Bench):
     store the step's token, decode (absorbed attention, split-T), merge."""
 
     DECODE = 1
+    DECODE_MERGE = (1, 2)
 
     def __init__(self, w, device="cuda"):
         import numpy as np
@@ -252,6 +268,7 @@ class RaggedBench(_Bench):
     queries rotated, decode over the batch, merge."""
 
     DECODE = 3
+    DECODE_MERGE = (3, 4)
     EXTRA_TIMED = {"chunk_store": 0}
 
     def __init__(self, w, device="cuda"):
@@ -325,18 +342,73 @@ class RaggedBench(_Bench):
     flops_per_layer = None
 
 
-def time_steps(b, steps, warmup):
-    """ms per step of `steps` uninstrumented steps after `warmup` warm-up steps."""
+def capture(b, only=None):
+    """The step (or the calls `only`) captured as one HIP graph on a side
+    stream, after one eager run of it on that stream."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        b.step(stream=ctypes.c_void_p(side.cuda_stream), only=only)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        b.step(stream=ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), only=only)
+    torch.cuda.synchronize()
+    return g
+
+
+def check_graph(b, g, replays=3):
+    """Every replay of the step's graph, each after an eager step and a
+    synchronization, reproduces the eager step's outputs bit for bit."""
+    import torch
+    b.step()
+    torch.cuda.synchronize()
+    ref = b.outputs()
+    for _ in range(replays):
+        b.out.zero_()
+        b.lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = b.outputs()
+        if not (torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])):
+            raise RuntimeError("graph replay differs from the eager step")
+        b.step()
+        torch.cuda.synchronize()
+
+
+def time_graph(g, steps, warmup):
+    """ms per replay of `steps` back-to-back replays after `warmup` replays."""
     import torch
     for _ in range(warmup):
-        b.step()
+        g.replay()
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record()
     for _ in range(steps):
-        b.step()
+        g.replay()
+    t_end.record()
+    torch.cuda.synchronize()
+    return t_start.elapsed_time(t_end) / steps, time.perf_counter() - wall0
+
+
+def time_steps(b, steps, warmup, only=None):
+    """ms per step of `steps` uninstrumented steps (of the calls `only`, if
+    given) after `warmup` warm-up steps."""
+    import torch
+    for _ in range(warmup):
+        b.step(only=only)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for _ in range(steps):
+        b.step(only=only)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -360,11 +432,22 @@ def time_decode(b, steps, which=None):
 
 
 def measure(b, steps, warmup):
+    """The eager step; decode + merge alone; the step replayed as one HIP
+    graph (each replay first checked against the eager step's outputs); and
+    the decode launch (and other calls to time) by events."""
+    import torch
     ms_step, wall = time_steps(b, steps, warmup)
+    ms_dm, _ = time_steps(b, steps, warmup, only=b.DECODE_MERGE)
+    g = capture(b)
+    check_graph(b, g)
+    ms_graph, _ = time_graph(g, steps, warmup)
+    del g
+    torch.cuda.synchronize()
     dec_ms = time_decode(b, steps)
     kvb = b.kv_bytes_per_layer
     L = b.w.n_layers
     r = {"ms_per_step": ms_step, "us_per_layer": ms_step * 1e3 / L, "decode_us": dec_ms * 1e3,
+         "decode_merge_us_per_layer": ms_dm * 1e3 / L, "graph_us_per_layer": ms_graph * 1e3 / L,
          "step_gbs": kvb * L / (ms_step * 1e-3) / 1e9, "decode_gbs": kvb / (dec_ms * 1e-3) / 1e9, "wall_s": wall}
     if b.flops_per_layer:
         r["decode_tflops"] = b.flops_per_layer / (dec_ms * 1e-3) / 1e12
@@ -429,7 +512,8 @@ def main():
     torch.cuda.set_device(0)
     _log(f"bench: setting up {w.name} ({w.n_layers} layers, T={w.seq_len})")
     b = Q4Bench(w)
-    _log(f"bench: timing {args.steps} steps after {args.warmup} warm-up steps, then {args.steps} event-bracketed steps")
+    _log(f"bench: timing {args.steps} steps after {args.warmup} warm-up steps "
+         f"(then decode + merge alone, the step as a HIP graph, {args.steps} event-bracketed steps)")
     m = measure(b, args.steps, args.warmup)
     kvb = b.kv_bytes_per_layer
     rec = {
@@ -440,6 +524,8 @@ def main():
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "split_keys": w.split_keys, "kv_bytes_per_layer": kvb},
         "us_per_layer": round(m["us_per_layer"], 3),
+        "decode_merge_us_per_layer": round(m["decode_merge_us_per_layer"], 3),
+        "graph_us_per_layer": round(m["graph_us_per_layer"], 3),
         "pct_hbm_peak": round(100 * m["step_gbs"] / HBM_PEAK_GBS, 2),
         "roofline": {"kernel": "kvq_decode_attn (4-bit split-K)", "bound": "hbm",
                      "achieved": round(m["decode_gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -460,6 +546,8 @@ def main():
             e = {"layers": wx.n_layers, "seq_len": wx.seq_len or f"{min(bx.lens)}..{max(bx.lens)} x {len(bx.lens)}",
                  "split_keys": wx.split_keys, "steps": steps,
                  "kv_bytes_per_layer": bx.kv_bytes_per_layer, "us_per_layer": round(mx["us_per_layer"], 3),
+                 "decode_merge_us_per_layer": round(mx["decode_merge_us_per_layer"], 3),
+                 "graph_us_per_layer": round(mx["graph_us_per_layer"], 3),
                  "step_kv_gbs": round(mx["step_gbs"], 2), "decode_us": round(mx["decode_us"], 3),
                  "decode_kv_gbs": round(mx["decode_gbs"], 2),
                  "decode_frac_hbm": round(mx["decode_gbs"] / HBM_PEAK_GBS, 4)}
