@@ -249,6 +249,20 @@ def test_other_shapes(kvq, D, page_size, hq, hkv):
     _check_q4(Q4Case(w, [1300, 2600, 40]), 1024)
 
 
+@pytest.mark.parametrize("hq,hkv,page_size,split", [(4, 4, 16, 512), (8, 4, 32, 512), (16, 4, 64, 1024),
+                                                     (8, 1, 16, 1024)])
+def test_pair_kernel_edges(kvq, hq, hkv, page_size, split):
+    """The wave-pair kernel (head_dim 256, groups of up to 8 heads, splits of
+    up to 1024 keys): group sizes 1, 2, 4 and 8 and lengths around its tile
+    (32 keys) and pair-quarter (split / 4 keys) boundaries, where the pairs
+    of a workgroup run different numbers of tiles and idle pairs only join
+    the barriers."""
+    w = wl.shrink(wl.RAGGED, prefill_chunk=0, n_q_heads=hq, n_kv_heads=hkv, page_size=page_size)
+    q = split // 4
+    lens = [1, 31, 32, 33, q - 1, q, q + 1, 2 * q + 17, 3 * q + 31, split - 1, split, split + 1, 2 * split + q + 5]
+    _check_q4(Q4Case(w, lens), split)
+
+
 def test_pool_beyond_4gib(kvq):
     """Byte offsets above 2^32: a sequence whose pages sit at the far end of
     a pool of more than 4 GiB per K and V (the oracle sees the same rows in a
