@@ -231,6 +231,34 @@ def test_batch_invariance(kvq):
             assert np.array_equal(o.cpu().numpy()[0], ob[b]) and np.array_equal(l.cpu().numpy()[0], lb[b])
 
 
+@pytest.mark.parametrize("split_keys", [512, 2048])
+def test_drafted_rows_equal_serial(kvq, split_keys):
+    """Drafted output equals serial output (TensorFold issue "qwen27 CUDA: an
+    opt-in 4-bit attention cache", section "What it is", contracts).  Three
+    drafted tokens after a 2900-token prefix: the three rows decoded in one
+    call (one batch entry per row on the same page table, lengths L+1..L+3,
+    after storing the three tokens) equal, bit for bit, the rows decoded one
+    after another at those lengths.  512-key splits run the wave-pair kernel,
+    2048-key splits the single-wave one."""
+    import fp8_quantized_kv_amd as kvq_mod
+    w = wl.shrink(wl.RAGGED, prefill_chunk=0)
+    L, R = 2900, 3
+    case = Q4Case(w, [L + R], build_oracle=False)  # prefix and drafted tokens stored
+    gen = torch.Generator(device="cuda").manual_seed(21)
+    q = torch.randn((R, w.n_q_heads, w.head_dim), generator=gen, device="cuda")
+    q_rot = kvq_mod.kvq_rotate_q(q)
+    lens = torch.arange(L + 1, L + R + 1, dtype=torch.int32, device="cuda")
+    pt = case.page_table.expand(R, -1).contiguous()
+    pa, pm, pz = kvq_mod.kvq_decode_attn(case.cache, q_rot, pt, lens, L + R, w.sm_scale, split_keys)
+    o_draft, l_draft = kvq_mod.kvq_merge(case.cache, pa, pm, pz, lens, L + R, split_keys)
+    for r in range(R):
+        sl = lens[r:r + 1].contiguous()
+        pa, pm, pz = kvq_mod.kvq_decode_attn(case.cache, q_rot[r:r + 1].contiguous(), case.page_table, sl, L + r + 1,
+                                             w.sm_scale, split_keys)
+        o, lse = kvq_mod.kvq_merge(case.cache, pa, pm, pz, sl, L + r + 1, split_keys)
+        assert torch.equal(o[0], o_draft[r]) and torch.equal(lse[0], l_draft[r]), f"row {r}"
+
+
 def test_mha_and_large_group(kvq):
     """Group sizes 1 (plain multi-head) and 16 (the largest the kernels take)."""
     for hq, hkv in ((3, 3), (16, 1)):
