@@ -44,17 +44,13 @@
 //    the latent gathered by two ds_read_b64_tr_b16 (source lane 4e + m of a
 //    16-lane group addresses key slot e at channels 4m .. 4m + 3, so lane j
 //    receives channel j of keys e = 0..3; the second read takes slots 4..7).
-#include "internal.h"
+#include "mfma_common.h"
 
 namespace kvq {
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+using namespace mx;
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
@@ -76,10 +72,6 @@ constexpr int kQG = 9;                               // score channel groups (of
 constexpr int kNBW = kL / 16 / 2;                    // 16 output blocks of 16 channels per wave
 constexpr float kRescale = 6.0f;
 
-__device__ __forceinline__ f32x4 mfma(half8_t a, half8_t b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
 // 8 e4m3 codes (two dwords, byte order = k-slot order) as 8 f16 values.
 __device__ __forceinline__ half8_t cvt8(uint32_t w0, uint32_t w1) {
     const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
@@ -93,19 +85,6 @@ __device__ __forceinline__ half8_t cvt8(uint32_t w0, uint32_t w1) {
 __device__ __forceinline__ uint32_t clear_nan_codes(uint32_t w) {
     const uint32_t t = ((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;  // bit 7 set where low 7 bits were 0x7F
     return w & ~(t | (t - (t >> 7)));
-}
-
-__device__ __forceinline__ float quad_max(float x) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float quad_sum(float x) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // 2^e for an integer e in [-126, 127], exactly.
@@ -326,12 +305,9 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
         }
 
         // ---- running maximum (per head) and running scale exponent (uniform)
-        float tmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                           fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-        tmax = quad_max(tmax);
-        float smax = fmaxf(fmaxf(fmaxf(scl[0][0], scl[0][1]), fmaxf(scl[0][2], scl[0][3])),
-                           fmaxf(fmaxf(scl[1][0], scl[1][1]), fmaxf(scl[1][2], scl[1][3])));
-        smax = quad_max(smax);  // the same in every lane: scales belong to keys
+        // (scores are finite or -inf, scales finite or 0: no NaN reaches these maxima)
+        const float tmax = quad_max_nonan(max8f(sc));
+        const float smax = quad_max_nonan(max8f(scl));  // the same in every lane: scales belong to keys
         const int e_tile = smax > 0.0f ? int((__float_as_uint(smax) >> 23) & 0xFF) - 127 : -1000;
         const int e_new = __builtin_amdgcn_readfirstlane(
             e_run == -1000 ? max(e_tile, -100) : (e_tile > e_run + 4 ? e_tile : e_run));

@@ -61,6 +61,31 @@ __device__ __forceinline__ f32x4 mfma(half8_t a, half8_t b, f32x4 c) {
 __device__ __forceinline__ float lo_half(uint32_t w) { return float(__builtin_bit_cast(half2_t, w)[0]); }
 __device__ __forceinline__ float hi_half(uint32_t w) { return float(__builtin_bit_cast(half2_t, w)[1]); }
 
+// max(a, b, c) and max(a, b) as single instructions, for values that are
+// finite or -inf, never NaN (the compiler otherwise quiets each fmaxf
+// operand with a v_max of the operand with itself).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+// Max of the 8 values a lane holds for two 16-key blocks, then over the
+// lanes l, l^16, l^32, l^48.
+__device__ __forceinline__ float max8f(const float (&x)[2][4]) {
+    return max3f(max3f(x[0][0], x[0][1], x[0][2]), max3f(x[0][3], x[1][0], x[1][1]), max2f(x[1][2], x[1][3]));
+}
+__device__ __forceinline__ float quad_max_nonan(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = max2f(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return max2f(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Max / sum over the lanes l, l^16, l^32, l^48 (the four row-quarters of an
 // MFMA output column), with vector-ALU lane swaps rather than LDS.
 __device__ __forceinline__ float quad_max(float x) {
