@@ -76,7 +76,7 @@ __device__ __forceinline__ void dma_run(const uint8_t* src, uint32_t lds, int la
     for (int i = 0; i < S::RUN_INSTR; ++i) {
         const int chunk = i * 64 + lane;
         if (i + 1 < S::RUN_INSTR || chunk < S::RUN / 16)
-            dma16(src, uint32_t(chunk * 16), lds + uint32_t(i * 1024));
+            dma16<true>(src, uint32_t(chunk * 16), lds + uint32_t(i * 1024));  // each row is read once
     }
 }
 

@@ -160,10 +160,12 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
         const uint8_t* r0 = pool + run_at(2 * t);
         const uint8_t* r1 = pool + run_at(2 * t + 1);
         wait_lgkm0();  // earlier LDS reads of this slot have completed
-        dma16(r0, src_off[0], dst);
-        if (lane < 16) dma16(r0, src_off[1], dst + 1024u);
-        dma16(r1, src_off[0], dst + 1280u);
-        if (lane < 16) dma16(r1, src_off[1], dst + 2304u);
+        // Code bytes are read once (non-temporal); the scale chunk is read by
+        // both waves of the pair, the second time from the caches.
+        dma16<true>(r0, src_off[0], dst);
+        if (lane < 16) dma16<false>(r0, src_off[1], dst + 1024u);
+        dma16<true>(r1, src_off[0], dst + 1280u);
+        if (lane < 16) dma16<false>(r1, src_off[1], dst + 2304u);
     };
     if (n_sub > 0) {
         issue(k_pool, 0, k_ring);
