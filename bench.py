@@ -107,10 +107,11 @@ class _Bench:
 class Q4Bench(_Bench):
     """Every layer's cache, query and buffers for one 4-bit workload, plus the
     raw C-ABI argument tuples of one step (validated once by building them
-    through the binding's checks).  Step per layer: store, rotate, decode, merge."""
+    through the binding's checks).  Step per layer: store + rotate (one
+    launch, kvq_store_rotate_q), decode, merge."""
 
-    DECODE = 2
-    DECODE_MERGE = (2, 3)
+    DECODE = 1
+    DECODE_MERGE = (1, 2)
 
     def __init__(self, w, device="cuda"):
         import numpy as np
@@ -151,8 +152,8 @@ class Q4Bench(_Bench):
         # One checked pass through the binding validates every argument once.
         for layer in range(w.n_layers):
             c = self.caches[layer]
-            kvq.kvq_store(c, self.k_new[layer], self.v_new[layer], self.slot_new)
-            kvq.kvq_rotate_q(self.q[layer], out=self.q_rot)
+            kvq.kvq_store_rotate_q(c, self.k_new[layer], self.v_new[layer], self.slot_new, self.q[layer],
+                                   out=self.q_rot)
             kvq.kvq_decode_attn(c, self.q_rot, self.page_table, self.seq_lens, T, w.sm_scale, w.split_keys,
                                 self.pa, self.pm, self.pz)
             kvq.kvq_merge(c, self.pa, self.pm, self.pz, self.seq_lens, T, w.split_keys, out=self.out[layer],
@@ -164,10 +165,10 @@ class Q4Bench(_Bench):
         for layer, c in enumerate(self.caches):
             d = ctypes.byref(c.desc)
             self.raw.append([
-                ("kvq_store", (d, P(self.k_new[layer].data_ptr()), P(self.v_new[layer].data_ptr()),
-                               kvq._DTYPES[self.k_new[layer].dtype], P(self.slot_new.data_ptr()), 1, stream)),
-                ("kvq_rotate_q", (P(self.q[layer].data_ptr()), 0, P(self.q_rot.data_ptr()), w.n_q_heads, w.head_dim,
-                                  stream)),
+                ("kvq_store_rotate_q", (d, P(self.k_new[layer].data_ptr()), P(self.v_new[layer].data_ptr()),
+                                        kvq._DTYPES[self.k_new[layer].dtype], P(self.slot_new.data_ptr()), 1,
+                                        P(self.q[layer].data_ptr()), 0, P(self.q_rot.data_ptr()), w.n_q_heads,
+                                        stream)),
                 ("kvq_decode_attn", (d, P(self.q_rot.data_ptr()), w.n_q_heads, P(self.page_table.data_ptr()),
                                      self.page_table.shape[1], P(self.seq_lens.data_ptr()), 1, T,
                                      ctypes.c_float(w.sm_scale), w.split_keys, P(self.pa.data_ptr()),
@@ -264,11 +265,11 @@ class MlaBench(_Bench):
 class RaggedBench(_Bench):
     """The ragged batch: 16 sequences of seeded lengths over a shuffled paged
     pool (one layer).  Step: the 2048-token prefill chunk of a 17th sequence
-    packed into its reserved pages, each sequence's new token stored, the
-    queries rotated, decode over the batch, merge."""
+    packed into its reserved pages, each sequence's new token stored and the
+    queries rotated (one launch), decode over the batch, merge."""
 
-    DECODE = 3
-    DECODE_MERGE = (3, 4)
+    DECODE = 2
+    DECODE_MERGE = (2, 3)
     EXTRA_TIMED = {"chunk_store": 0}
 
     def __init__(self, w, device="cuda"):
@@ -308,8 +309,7 @@ class RaggedBench(_Bench):
         self.out = torch.empty((w.batch, w.n_q_heads, w.head_dim), **f32)
         self.lse = torch.empty((w.batch, w.n_q_heads), **f32)
         kvq.kvq_store(c, self.k_chunk, self.v_chunk, self.slot_chunk)
-        kvq.kvq_store(c, self.k_new, self.v_new, self.slot_new)
-        kvq.kvq_rotate_q(self.q, out=self.q_rot)
+        kvq.kvq_store_rotate_q(c, self.k_new, self.v_new, self.slot_new, self.q, out=self.q_rot)
         kvq.kvq_decode_attn(c, self.q_rot, self.page_table, self.seq_lens, self.T, w.sm_scale, w.split_keys,
                             self.pa, self.pm, self.pz)
         kvq.kvq_merge(c, self.pa, self.pm, self.pz, self.seq_lens, self.T, w.split_keys, out=self.out, lse=self.lse)
@@ -322,9 +322,9 @@ class RaggedBench(_Bench):
         self.raw = [[
             ("kvq_store", (d, P(self.k_chunk.data_ptr()), P(self.v_chunk.data_ptr()), dt, P(self.slot_chunk.data_ptr()),
                            w.prefill_chunk, stream)),
-            ("kvq_store", (d, P(self.k_new.data_ptr()), P(self.v_new.data_ptr()), dt, P(self.slot_new.data_ptr()), B,
-                           stream)),
-            ("kvq_rotate_q", (P(self.q.data_ptr()), 0, P(self.q_rot.data_ptr()), B * Hq, D, stream)),
+            ("kvq_store_rotate_q", (d, P(self.k_new.data_ptr()), P(self.v_new.data_ptr()), dt,
+                                    P(self.slot_new.data_ptr()), B, P(self.q.data_ptr()), 0, P(self.q_rot.data_ptr()),
+                                    B * Hq, stream)),
             ("kvq_decode_attn", (d, P(self.q_rot.data_ptr()), Hq, P(self.page_table.data_ptr()),
                                  self.page_table.shape[1], P(self.seq_lens.data_ptr()), B, self.T,
                                  ctypes.c_float(w.sm_scale), w.split_keys, P(self.pa.data_ptr()),

@@ -33,7 +33,7 @@ DT_F32, DT_BF16, DT_F16 = 0, 1, 2
 _DTYPES = {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float16: DT_F16}
 
 EXPORTED = ("kvq_status_string", "kvq_row_bytes", "kvq_pool_bytes", "kvq_num_splits", "kvq_store",
-            "kvq_rotate_q", "kvq_decode_attn", "kvq_merge")
+            "kvq_rotate_q", "kvq_store_rotate_q", "kvq_decode_attn", "kvq_merge")
 
 
 class KvqCacheDesc(ctypes.Structure):
@@ -57,6 +57,7 @@ def _load():
         "kvq_num_splits": ([I32, I32], I32),
         "kvq_store": ([C, P, P, I32, P, I32, P], I32),
         "kvq_rotate_q": ([P, I32, P, I32, I32, P], I32),
+        "kvq_store_rotate_q": ([C, P, P, I32, P, I32, P, I32, P, I32, P], I32),
         "kvq_decode_attn": ([C, P, I32, P, I32, P, I32, I32, F, I32, P, P, P, P], I32),
         "kvq_merge": ([C, P, P, P, P, I32, I32, I32, I32, I32, P, P, P], I32),
     }
@@ -191,6 +192,31 @@ def kvq_rotate_q(q, out=None):
     return out
 
 
+def kvq_store_rotate_q(cache, k, v, slot_mapping, q, out=None):
+    """kvq_store(cache, k, v, slot_mapping) and kvq_rotate_q(q) in one launch (4-bit cache only);
+    returns the rotated query (f32, q's shape)."""
+    if cache.fmt != FMT_Q4_H32:
+        raise ValueError("kvq_store_rotate_q takes a 4-bit cache")
+    n = int(slot_mapping.shape[0])
+    kdt, qdt = _DTYPES.get(k.dtype), _DTYPES.get(q.dtype)
+    if kdt is None or qdt is None:
+        raise ValueError(f"unsupported dtype {k.dtype if kdt is None else q.dtype}")
+    shape = (n, cache.num_kv_heads, cache.head_dim)
+    kp = _dev(k, "k", shape=shape)
+    vp = _dev(v, "v", dtype=k.dtype, shape=shape)
+    sp = _dev(slot_mapping, "slot_mapping", dtype=torch.int64)
+    if int(q.shape[-1]) != cache.head_dim:
+        raise ValueError(f"q rows must have the cache's head_dim {cache.head_dim}")
+    rows = q.numel() // cache.head_dim
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    qp = _dev(q, "q")
+    op = _dev(out, "out", dtype=torch.float32, shape=q.shape)
+    _check(lib.kvq_store_rotate_q(ctypes.byref(cache.desc), kp, vp, kdt, sp, n, qp, qdt, op, rows, _stream(q)),
+           "kvq_store_rotate_q")
+    return out
+
+
 def partial_shapes(cache, batch, n_q_heads, max_seq_len, split_keys):
     S = kvq_num_splits(max_seq_len, split_keys)
     return (batch, n_q_heads, S, cache.dv), (batch, n_q_heads, S)
@@ -242,10 +268,19 @@ def kvq_merge(cache, part_acc, part_m, part_z, seq_lens, max_seq_len, split_keys
     return out, lse
 
 
-def decode_step(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_keys, bufs=None):
-    """rotate (Q4) -> decode -> merge on preallocated buffers; returns (out, lse)."""
+def decode_step(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_keys, bufs=None, new_kv=None):
+    """[store the step's rows] -> rotate (Q4) -> decode -> merge on preallocated buffers; returns (out, lse).
+
+    new_kv = (k, v, slot_mapping) stores those rows first (for the 4-bit cache in the same launch as the
+    query rotation, kvq_store_rotate_q; v is None for the fp8 cache)."""
+    q_rot = None if bufs is None else bufs.get("q_rot")
     if cache.fmt == FMT_Q4_H32:
-        q = kvq_rotate_q(q, out=None if bufs is None else bufs.get("q_rot"))
+        if new_kv is not None:
+            q = kvq_store_rotate_q(cache, *new_kv, q, out=q_rot)
+        else:
+            q = kvq_rotate_q(q, out=q_rot)
+    elif new_kv is not None:
+        kvq_store(cache, *new_kv)
     pa, pm, pz = kvq_decode_attn(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_keys,
                                  *(() if bufs is None else (bufs["part_acc"], bufs["part_m"], bufs["part_z"])))
     return kvq_merge(cache, pa, pm, pz, seq_lens, max_seq_len, split_keys,

@@ -99,6 +99,20 @@ __device__ __forceinline__ void h32_butterfly_lanes8(float (&x)[4], int lane) {
     }
 }
 
+// Query rotation, one lane per 4 consecutive values i .. i+3 of q (i = 4 *
+// quad; a 32-group is 8 lanes, 8-aligned in the wave): the butterfly above,
+// then x fp32(1/sqrt(32)) -- the transform the store applies to K and V, in
+// the same order.  Each value is read and written by the same lane, so q may
+// alias q_rot.  Every lane of a group must call it (the lanes exchange values).
+template <InType DT>
+__device__ __forceinline__ void rotate_q_quad(const void* q, float* q_rot, int64_t quad, int lane) {
+    float x[4];
+    load4<DT>(q, 4 * quad, x);
+    h32_butterfly_lanes8(x, lane);
+    const float c = inv_sqrt32();
+    *reinterpret_cast<float4*>(q_rot + 4 * quad) = make_float4(x[0] * c, x[1] * c, x[2] * c, x[3] * c);
+}
+
 // ------------------------------------------------------------------ launchers
 // Each returns the hipError_t of its launch; shapes are validated by the caller.
 
@@ -125,6 +139,10 @@ hipError_t launch_store_q4(const Q4Pool& pool, const void* k, const void* v, InT
 hipError_t launch_store_fp8(const Fp8Pool& pool, const void* x, InType dt, const int64_t* slots, int n_tokens,
                             hipStream_t s);
 hipError_t launch_rotate_q(const void* q, InType dt, float* q_rot, int n_rows, int head_dim, hipStream_t s);
+// The 4-bit store and the query rotation (q rows of the pool's head_dim) as
+// one launch; the same results as the two launches above.
+hipError_t launch_store_rotate_q4(const Q4Pool& pool, const void* k, const void* v, InType dt, const int64_t* slots,
+                                  int n_tokens, const void* q, InType q_dt, float* q_rot, int n_rows, hipStream_t s);
 
 struct DecodeArgs {
     const float* q;

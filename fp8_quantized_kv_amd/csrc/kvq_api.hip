@@ -134,6 +134,28 @@ kvq_status kvq_rotate_q(const void* q, int32_t dtype, float* q_rot, int32_t n_ro
     return launched(kvq::launch_rotate_q(q, static_cast<InType>(dtype), q_rot, n_rows, head_dim, stream));
 }
 
+kvq_status kvq_store_rotate_q(const kvq_cache* cache, const void* k, const void* v, int32_t kv_dtype,
+                              const int64_t* slot_mapping, int32_t n_tokens, const void* q, int32_t q_dtype,
+                              float* q_rot, int32_t n_rows, hipStream_t stream) {
+    kvq_status st = check_cache(cache);
+    if (st != KVQ_OK) return st;
+    if (cache->format != KVQ_FMT_Q4_H32) return KVQ_ERR_INVALID_ARG;
+    if (!dtype_ok(kv_dtype) || !dtype_ok(q_dtype) || n_tokens < 0 || n_rows < 0) return KVQ_ERR_INVALID_ARG;
+    if (n_tokens > 0 && (!aligned(slot_mapping, 8) || !aligned(k) || !aligned(v))) return KVQ_ERR_INVALID_ARG;
+    if (n_rows > 0) {
+        if (!aligned(q) || !aligned(q_rot)) return KVQ_ERR_INVALID_ARG;
+        if (q == q_rot && q_dtype != KVQ_DT_F32) return KVQ_ERR_INVALID_ARG;
+    }
+    if (n_tokens == 0 && n_rows == 0) return KVQ_OK;
+    // one lane per 4 values in each role, each role rounded up to whole 256-lane workgroups
+    const int64_t quads = cache->head_dim / 4;
+    const int64_t store_lanes = (int64_t(n_tokens) * cache->num_kv_heads * 2 * quads + 255) / 256 * 256;
+    const int64_t rot_lanes = (int64_t(n_rows) * quads + 255) / 256 * 256;
+    if (store_lanes + rot_lanes > kMaxLaunchThreads) return KVQ_ERR_UNSUPPORTED;
+    return launched(kvq::launch_store_rotate_q4(q4_pool(cache), k, v, static_cast<InType>(kv_dtype), slot_mapping,
+                                                n_tokens, q, static_cast<InType>(q_dtype), q_rot, n_rows, stream));
+}
+
 kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
                            int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
                            float sm_scale, int32_t split_keys, float* part_acc, float* part_m, float* part_z,

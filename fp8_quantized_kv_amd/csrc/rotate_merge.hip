@@ -11,19 +11,12 @@ namespace kvq {
 namespace {
 
 // One lane per 4 consecutive query values (a 32-group is 8 lanes, a row of
-// 256 values one wave): the fp32 butterfly (stages 1..16) with lane
-// exchanges for the upper stages, then x fp32(1/sqrt(32)) -- the same
-// transform, in the same order, that the store applies to K and V.  Each
-// value is read and written by the same lane, so q may alias q_rot.
+// 256 values one wave); q may alias q_rot.
 template <InType DT>
 __global__ __launch_bounds__(256) void rotate_q_kernel(const void* q, float* q_rot, int64_t n_quads) {
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= n_quads) return;
-    float x[4];
-    load4<DT>(q, 4 * i, x);
-    h32_butterfly_lanes8(x, threadIdx.x & 63);
-    const float c = inv_sqrt32();
-    *reinterpret_cast<float4*>(q_rot + 4 * i) = make_float4(x[0] * c, x[1] * c, x[2] * c, x[3] * c);
+    if (i >= n_quads) return;  // n_quads is a multiple of 8: whole groups leave
+    rotate_q_quad<DT>(q, q_rot, i, threadIdx.x & 63);
 }
 
 constexpr int kMergeWaves = 4;

@@ -25,13 +25,13 @@ namespace {
 // lanes.  Lanes of a group exchange values for the butterfly's upper stages
 // and the amax; each lane then packs its 4 codes into 2 bytes.  Rows are
 // ordered K rows first, then V rows, each (token, head) major.
+// idx is the lane's global index; lane its index in the wave.
 template <InType DT>
-__global__ __launch_bounds__(256) void store_q4_kernel(const void* __restrict__ k, const void* __restrict__ v,
-                                                       const int64_t* __restrict__ slots, int n_tokens,
-                                                       uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
-                                                       int H, int D, int page_size, int64_t n_slots) {
+__device__ __forceinline__ void store_q4_quad(const void* __restrict__ k, const void* __restrict__ v,
+                                              const int64_t* __restrict__ slots, int n_tokens,
+                                              uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, int H,
+                                              int D, int page_size, int64_t n_slots, int64_t idx, int lane) {
     const int per_row = D / 4;
-    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t nth = int64_t(n_tokens) * H;
     if (idx >= 2 * nth * per_row) return;
     const int e = int(idx % per_row);  // lane-in-row: values 4e .. 4e+3
@@ -45,7 +45,6 @@ __global__ __launch_bounds__(256) void store_q4_kernel(const void* __restrict__ 
 
     float x[4];
     load4<DT>(which ? v : k, r * D + 4 * e, x);
-    const int lane = threadIdx.x & 63;
     h32_butterfly_lanes8(x, lane);
     const float c = inv_sqrt32();
     float amax = 0.0f;
@@ -76,6 +75,37 @@ __global__ __launch_bounds__(256) void store_q4_kernel(const void* __restrict__ 
     uint8_t* row = (which ? v_pool : k_pool) + ((page * H + h) * page_size + off) * rb;
     reinterpret_cast<uint16_t*>(row)[e] = uint16_t(bits);
     if ((e & 7) == 0) reinterpret_cast<uint16_t*>(row + D / 2)[e >> 3] = __half_as_ushort(s16);
+}
+
+template <InType DT>
+__global__ __launch_bounds__(256) void store_q4_kernel(const void* __restrict__ k, const void* __restrict__ v,
+                                                       const int64_t* __restrict__ slots, int n_tokens,
+                                                       uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                                                       int H, int D, int page_size, int64_t n_slots) {
+    store_q4_quad<DT>(k, v, slots, n_tokens, k_pool, v_pool, H, D, page_size, n_slots,
+                      int64_t(blockIdx.x) * blockDim.x + threadIdx.x, threadIdx.x & 63);
+}
+
+// The store's lanes in the first store_blocks workgroups, the query
+// rotation's in the rest: the two steps that precede the decode of a step
+// are independent, and one launch costs less than two.  A workgroup runs one
+// role only, and each role keeps its 8-lane groups whole.
+template <InType DK, InType DQ>
+__global__ __launch_bounds__(256) void store_rotate_q4_kernel(const void* __restrict__ k, const void* __restrict__ v,
+                                                              const int64_t* __restrict__ slots, int n_tokens,
+                                                              uint8_t* __restrict__ k_pool,
+                                                              uint8_t* __restrict__ v_pool, int H, int D,
+                                                              int page_size, int64_t n_slots, unsigned store_blocks,
+                                                              const void* q, float* q_rot, int64_t n_quads) {
+    const int lane = threadIdx.x & 63;
+    if (blockIdx.x < store_blocks) {
+        store_q4_quad<DK>(k, v, slots, n_tokens, k_pool, v_pool, H, D, page_size, n_slots,
+                          int64_t(blockIdx.x) * blockDim.x + threadIdx.x, lane);
+        return;
+    }
+    const int64_t i = int64_t(blockIdx.x - store_blocks) * blockDim.x + threadIdx.x;
+    if (i >= n_quads) return;  // n_quads is a multiple of 8: whole groups leave
+    rotate_q_quad<DQ>(q, q_rot, i, lane);
 }
 
 // e4m3 ("fn": bias 7, max 448) code of v, round to nearest even, saturating
@@ -148,6 +178,55 @@ hipError_t launch_store_q4(const Q4Pool& pool, const void* k, const void* v, InT
         case InType::F16:
             store_q4_kernel<InType::F16><<<grid, block, 0, s>>>(k, v, slots, n_tokens, pool.k, pool.v,
                                                                 pool.n_kv_heads, pool.head_dim, pool.page_size, n_slots);
+            break;
+    }
+    return hipGetLastError();
+}
+
+namespace {
+template <InType DK>
+void store_rotate_q4_dq(dim3 grid, hipStream_t s, const Q4Pool& pool, const void* k, const void* v,
+                        const int64_t* slots, int n_tokens, int64_t n_slots, unsigned store_blocks, const void* q,
+                        InType q_dt, float* q_rot, int64_t n_quads) {
+    const int H = pool.n_kv_heads, D = pool.head_dim, P = pool.page_size;
+    switch (q_dt) {
+        case InType::F32:
+            store_rotate_q4_kernel<DK, InType::F32><<<grid, 256, 0, s>>>(k, v, slots, n_tokens, pool.k, pool.v, H, D, P,
+                                                                         n_slots, store_blocks, q, q_rot, n_quads);
+            break;
+        case InType::BF16:
+            store_rotate_q4_kernel<DK, InType::BF16><<<grid, 256, 0, s>>>(k, v, slots, n_tokens, pool.k, pool.v, H, D,
+                                                                          P, n_slots, store_blocks, q, q_rot, n_quads);
+            break;
+        case InType::F16:
+            store_rotate_q4_kernel<DK, InType::F16><<<grid, 256, 0, s>>>(k, v, slots, n_tokens, pool.k, pool.v, H, D, P,
+                                                                         n_slots, store_blocks, q, q_rot, n_quads);
+            break;
+    }
+}
+}  // namespace
+
+hipError_t launch_store_rotate_q4(const Q4Pool& pool, const void* k, const void* v, InType dt, const int64_t* slots,
+                                  int n_tokens, const void* q, InType q_dt, float* q_rot, int n_rows, hipStream_t s) {
+    const int64_t store_lanes = int64_t(n_tokens) * pool.n_kv_heads * 2 * (pool.head_dim / 4);
+    const int64_t n_quads = int64_t(n_rows) * (pool.head_dim / 4);
+    const unsigned store_blocks = unsigned((store_lanes + 255) / 256);
+    const unsigned rot_blocks = unsigned((n_quads + 255) / 256);
+    if (store_blocks + rot_blocks == 0) return hipSuccess;
+    const dim3 grid(store_blocks + rot_blocks);
+    const int64_t n_slots = int64_t(pool.num_pages) * pool.page_size;
+    switch (dt) {
+        case InType::F32:
+            store_rotate_q4_dq<InType::F32>(grid, s, pool, k, v, slots, n_tokens, n_slots, store_blocks, q, q_dt, q_rot,
+                                            n_quads);
+            break;
+        case InType::BF16:
+            store_rotate_q4_dq<InType::BF16>(grid, s, pool, k, v, slots, n_tokens, n_slots, store_blocks, q, q_dt,
+                                             q_rot, n_quads);
+            break;
+        case InType::F16:
+            store_rotate_q4_dq<InType::F16>(grid, s, pool, k, v, slots, n_tokens, n_slots, store_blocks, q, q_dt, q_rot,
+                                            n_quads);
             break;
     }
     return hipGetLastError();

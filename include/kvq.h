@@ -153,6 +153,23 @@ kvq_status kvq_store(const kvq_cache* cache, const void* k, const void* v, int32
 kvq_status kvq_rotate_q(const void* q, int32_t dtype, float* q_rot, int32_t n_rows, int32_t head_dim,
                         hipStream_t stream);
 
+/* ---------------------------------------------------------------- store + rotate */
+
+/* kvq_store of n_tokens rows into a Q4 cache and kvq_rotate_q of n_rows query
+ * rows of the cache's head_dim, as one launch (TensorFold "What it is": the
+ * step packs the window's new keys and values and rotates the queries once
+ * before attending; the two are independent, so a decode step can issue them
+ * together and pay for one launch instead of two).
+ * Every argument means what it means for kvq_store (kv_dtype for `dtype`)
+ * and kvq_rotate_q (q_dtype for `dtype`, head_dim = cache->head_dim); the
+ * stored bytes and q_rot are bit-identical to those two calls.  Either count
+ * may be 0 (that part is skipped and its pointers are not read).  q_rot must
+ * not overlap k, v or the pools; q == q_rot is allowed for f32.
+ * Q4 only (KVQ_ERR_INVALID_ARG for an FP8 cache). */
+kvq_status kvq_store_rotate_q(const kvq_cache* cache, const void* k, const void* v, int32_t kv_dtype,
+                              const int64_t* slot_mapping, int32_t n_tokens, const void* q, int32_t q_dtype,
+                              float* q_rot, int32_t n_rows, hipStream_t stream);
+
 /* ---------------------------------------------------------------- decode */
 
 /* Split-K decode attention over the cache, writing one partial per

@@ -125,6 +125,26 @@ def test_rotate_argument_checks(kvq):
     assert r(P(A), 0, P(A), 0, 256, None) == 0
 
 
+def test_store_rotate_argument_checks(kvq):
+    P = ctypes.c_void_p
+    r = kvq.lib.kvq_store_rotate_q
+    d = _q4(kvq)
+    args = lambda **kw: [ctypes.byref(kw.get("d", d)), P(kw.get("k", A)), P(A), kw.get("kdt", 0), P(kw.get("sl", A)),
+                         kw.get("n", 4), P(kw.get("q", A)), kw.get("qdt", 0), P(kw.get("qr", A + 4096)),
+                         kw.get("rows", 24), None]
+    assert r(*args(d=_fp8(kvq))) == INVALID          # 4-bit cache only
+    assert r(*args(kdt=7)) == INVALID                 # kv dtype
+    assert r(*args(qdt=5)) == INVALID                 # q dtype
+    assert r(*args(n=-1)) == INVALID
+    assert r(*args(rows=-1)) == INVALID
+    assert r(*args(k=A + 2)) == INVALID               # misaligned k
+    assert r(*args(sl=A + 4)) == INVALID              # misaligned slots
+    assert r(*args(q=A + 8)) == INVALID               # misaligned q
+    assert r(*args(qr=A, qdt=1)) == INVALID           # in place needs f32
+    assert r(*args(d=_q4(kvq, head_dim=100))) == INVALID
+    assert r(*args(n=0, rows=0)) == 0                 # nothing to do: no launch
+
+
 def _decode(kvq, d, **kw):
     P = ctypes.c_void_p
     a = dict(q=P(A), n_q_heads=24, page_table=P(A), max_pages=64, seq_lens=P(A), batch=1, max_seq_len=1024,

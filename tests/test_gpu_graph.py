@@ -1,8 +1,8 @@
 """The decode step under HIP graph capture.
 
-The calls of one decode step -- store the step's token, rotate the queries
-(4-bit cache), decode, merge -- are captured in one graph on torch's capture
-stream and replayed.  Every replay, each after eager work and a
+The calls of one decode step -- store the step's token and rotate the
+queries (4-bit cache: one launch), decode, merge -- are captured in one
+graph on torch's capture stream and replayed.  Every replay, each after eager work and a
 synchronization, must reproduce the eager step's outputs bit for bit: the
 library's kernels write every output element themselves and record no
 memset, so a captured step is safe to replay.
@@ -76,10 +76,9 @@ def test_q4_step_replays_in_a_graph(kvq, split_keys):
             "part_m": torch.empty(mz_shape, **f32), "part_z": torch.empty(mz_shape, **f32),
             "out": torch.empty((B, Hq, D), **f32), "lse": torch.empty((B, Hq), **f32)}
 
-    def step():
-        kvq.kvq_store(case.cache, k_new, v_new, slots)
+    def step():  # the store and the rotation in one launch
         kvq.decode_step(case.cache, case.q, case.page_table, case.seq_lens, case.max_seq_len, w.sm_scale,
-                        split_keys, bufs)
+                        split_keys, bufs, new_kv=(k_new, v_new, slots))
 
     _replays_match(step, [bufs["out"], bufs["lse"]])
 
@@ -100,8 +99,7 @@ def test_fp8_step_replays_in_a_graph(kvq):
             "lse": torch.empty((B, H), **f32)}
 
     def step():
-        kvq.kvq_store(case.cache, x_new, None, slots)
         kvq.decode_step(case.cache, case.q, case.page_table, case.seq_lens, case.max_seq_len, w.sm_scale, 1024,
-                        bufs)
+                        bufs, new_kv=(x_new, None, slots))
 
     _replays_match(step, [bufs["out"], bufs["lse"]])

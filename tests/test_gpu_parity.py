@@ -121,6 +121,47 @@ def test_rotate_q_matches_oracle_butterfly(kvq):
     assert np.array_equal(qq.cpu().numpy(), got)
 
 
+@pytest.mark.parametrize("D,kdt,qdt", [(256, torch.float32, torch.float32), (256, torch.bfloat16, torch.float32),
+                                        (128, torch.float16, torch.bfloat16), (64, torch.bfloat16, torch.float16)])
+def test_store_rotate_q_one_launch(kvq, D, kdt, qdt):
+    """kvq_store_rotate_q stores the same bytes as the oracle's store and
+    rotates q bit-identically to the oracle's butterfly; either part may be
+    empty, and q may be rotated in place."""
+    _say(f"store_rotate D={D} kv={kdt} q={qdt}")
+    g = torch.Generator().manual_seed(D + 7)
+    n_tok, H, ps, pages = 300, 3, 16, 40
+    k = (torch.randn((n_tok, H, D), generator=g) * torch.exp(torch.randn((n_tok, H, 1), generator=g))).to(kdt)
+    v = torch.randn((n_tok, H, D), generator=g).to(kdt)
+    k[9] = 0.0
+    slots = torch.randperm(pages * ps, generator=g)[:n_tok].to(torch.int64)
+    slots[::13] = -1
+    q = torch.randn((5, 24 // 5 + 1, D), generator=g).to(qdt)   # 25 rows: the last workgroup is ragged
+    cache = kvq.Q4Cache(pages, H, D, ps)
+    q_rot = kvq.kvq_store_rotate_q(cache, k.cuda(), v.cuda(), slots.cuda(), q.cuda())
+    kref = np.zeros(cache.k_pool.shape, np.uint8)
+    vref = np.zeros_like(kref)
+    oracle.q4_store(kref, vref, k.float().numpy(), v.float().numpy(), slots.numpy(), ps)
+    qref = oracle.hadamard32_f32(q.float().numpy().reshape(-1, D)).reshape(q.shape)
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.k_pool.cpu().numpy(), kref)
+    assert np.array_equal(cache.v_pool.cpu().numpy(), vref)
+    assert np.array_equal(q_rot.cpu().numpy().view(np.uint32), qref.view(np.uint32))
+    # rotation only (no tokens), store only (no rows), and in place
+    cache2 = kvq.Q4Cache(pages, H, D, ps)
+    none = torch.empty((0,), dtype=torch.int64, device="cuda")
+    kv0 = torch.empty((0, H, D), dtype=kdt, device="cuda")
+    r2 = kvq.kvq_store_rotate_q(cache2, kv0, kv0, none, q.cuda())
+    kvq.kvq_store_rotate_q(cache2, k.cuda(), v.cuda(), slots.cuda(), torch.empty((0, D), dtype=qdt, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(r2, q_rot)
+    assert torch.equal(cache2.k_pool, cache.k_pool) and torch.equal(cache2.v_pool, cache.v_pool)
+    if qdt == torch.float32:
+        qq = q.cuda().clone()
+        kvq.kvq_store_rotate_q(cache2, k.cuda(), v.cuda(), slots.cuda(), qq, out=qq)
+        torch.cuda.synchronize()
+        assert torch.equal(qq, q_rot)
+
+
 # ----------------------------------------------------------------- 4-bit decode
 
 def _check_q4(case, split_keys, chunked_partials=False):
