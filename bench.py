@@ -456,6 +456,35 @@ def measure(b, steps, warmup):
     return r
 
 
+def read_ceiling(gib=2, batches=3, per_batch=5):
+    """HBM read rate of kvq_stream_read over a buffer well above the last-level
+    cache, with the non-temporal hint and with the default cache policy
+    (median over `batches` event-timed runs of `per_batch` back-to-back
+    launches, GB/s)."""
+    import torch
+
+    import fp8_quantized_kv_amd as kvq
+    buf = torch.ones((gib << 30,), dtype=torch.uint8, device="cuda")
+    res = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    out = {"kernel": "kvq_stream_read (LDS DMA, 16 KiB per workgroup step)", "bytes": buf.numel(), "unit": "GB/s"}
+    for name, nt in (("non_temporal", True), ("default_policy", False)):
+        kvq.kvq_stream_read(buf, nt, res)  # warm-up
+        times = []
+        for _ in range(batches):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(per_batch):
+                kvq.kvq_stream_read(buf, nt, res)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / per_batch)
+        ms = sorted(times)[len(times) // 2]
+        out[name] = round(buf.numel() / (ms * 1e-3) / 1e9, 1)
+    del buf
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, sample_tokens, min_seconds=10.0, max_repeats=60):
     """The oracle (fp64, OpenMP over heads) on one layer of the workload,
     restricted to its first `sample_tokens` positions; repeated until about
@@ -535,6 +564,10 @@ def main():
     }
     del b
     torch.cuda.empty_cache()
+    _log("bench: HBM read ceiling (kvq_stream_read over 2 GiB)")
+    ceil = read_ceiling()
+    rec["hbm_read_ceiling"] = ceil
+    rec["roofline"]["frac_of_read_ceiling"] = round(m["decode_gbs"] / ceil["non_temporal"], 4)
     if not args.no_extras:
         extras = {}
         for name, cls in (("gqa_q4_32k", Q4Bench), ("ragged_q4_b16", RaggedBench), ("mla_fp8_262k", MlaBench)):

@@ -33,7 +33,7 @@ DT_F32, DT_BF16, DT_F16 = 0, 1, 2
 _DTYPES = {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float16: DT_F16}
 
 EXPORTED = ("kvq_status_string", "kvq_row_bytes", "kvq_pool_bytes", "kvq_num_splits", "kvq_store",
-            "kvq_rotate_q", "kvq_store_rotate_q", "kvq_decode_attn", "kvq_merge")
+            "kvq_rotate_q", "kvq_store_rotate_q", "kvq_decode_attn", "kvq_merge", "kvq_stream_read")
 
 
 class KvqCacheDesc(ctypes.Structure):
@@ -60,6 +60,7 @@ def _load():
         "kvq_store_rotate_q": ([C, P, P, I32, P, I32, P, I32, P, I32, P], I32),
         "kvq_decode_attn": ([C, P, I32, P, I32, P, I32, I32, F, I32, P, P, P, P], I32),
         "kvq_merge": ([C, P, P, P, P, I32, I32, I32, I32, I32, P, P, P], I32),
+        "kvq_stream_read": ([P, ctypes.c_size_t, I32, P, P], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -266,6 +267,19 @@ def kvq_merge(cache, part_acc, part_m, part_z, seq_lens, max_seq_len, split_keys
     _check(lib.kvq_merge(ctypes.byref(cache.desc), pa, pm, pz, slp, B, Hq, int(max_seq_len), int(split_keys),
                          1 if cache.fmt == FMT_Q4_H32 else 0, op, lp, _stream(part_acc)), "kvq_merge")
     return out, lse
+
+
+def kvq_stream_read(src, non_temporal=True, xor_out=None):
+    """Reads the device buffer `src` (bytes a multiple of 16 KiB) once through LDS DMA -- the
+    read-bandwidth measurement.  Returns the int32 device tensor holding the XOR of the 32-bit words
+    of its final 16 KiB block."""
+    if xor_out is None:
+        xor_out = torch.zeros((1,), dtype=torch.int32, device=src.device)
+    sp = _dev(src, "src")
+    xp = _dev(xor_out, "xor_out", dtype=torch.int32, shape=(1,))
+    _check(lib.kvq_stream_read(sp, src.numel() * src.element_size(), 1 if non_temporal else 0, xp, _stream(src)),
+           "kvq_stream_read")
+    return xor_out
 
 
 def decode_step(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_keys, bufs=None, new_kv=None):

@@ -198,4 +198,8 @@ struct MergeArgs {
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 
+// Read-bandwidth measurement (bytes a multiple of 16 KiB): XOR of every
+// 32-bit word of src folded into *xor_out.
+hipError_t launch_stream_read(const void* src, size_t bytes, bool non_temporal, uint32_t* xor_out, hipStream_t s);
+
 }  // namespace kvq

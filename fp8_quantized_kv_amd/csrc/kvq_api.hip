@@ -202,4 +202,11 @@ kvq_status kvq_merge(const kvq_cache* cache, const float* part_acc, const float*
     return launched(kvq::launch_merge(a, stream));
 }
 
+kvq_status kvq_stream_read(const void* src, size_t bytes, int32_t non_temporal, uint32_t* xor_out,
+                           hipStream_t stream) {
+    if (!aligned(src) || !aligned(xor_out, 4) || bytes == 0 || bytes % 16384) return KVQ_ERR_INVALID_ARG;
+    if (non_temporal != 0 && non_temporal != 1) return KVQ_ERR_INVALID_ARG;
+    return launched(kvq::launch_stream_read(src, bytes, non_temporal == 1, xor_out, stream));
+}
+
 }  // extern "C"

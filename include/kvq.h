@@ -220,6 +220,21 @@ kvq_status kvq_merge(const kvq_cache* cache, const float* part_acc, const float*
                      const int32_t* seq_lens, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
                      int32_t split_keys, int32_t inverse_rotate, float* out, float* lse, hipStream_t stream);
 
+/* ---------------------------------------------------------------- measurement */
+
+/* The HBM read ceiling the decode kernels are judged against (not a step of
+ * the method): every 16-byte chunk of src is copied once into LDS with the
+ * LDS-DMA load the 4-bit decode kernels use for cache rows, with the
+ * non-temporal hint (non_temporal = 1) or the default cache policy (0).  As
+ * a checkable result, the XOR of the little-endian 32-bit words of the final
+ * 16 KiB block of src is XOR-ed into *xor_out; the caller sets it first,
+ * e.g. to 0.
+ * src: device, 16-byte aligned; bytes: a positive multiple of 16384;
+ * xor_out: device, 4-byte aligned.  Timing is the caller's (events around
+ * the call on `stream`). */
+kvq_status kvq_stream_read(const void* src, size_t bytes, int32_t non_temporal, uint32_t* xor_out,
+                           hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -145,6 +145,16 @@ def test_store_rotate_argument_checks(kvq):
     assert r(*args(n=0, rows=0)) == 0                 # nothing to do: no launch
 
 
+def test_stream_read_argument_checks(kvq):
+    P = ctypes.c_void_p
+    r = kvq.lib.kvq_stream_read
+    assert r(P(A + 4), 16384, 1, P(A), None) == INVALID     # misaligned source
+    assert r(P(A), 16384 + 16, 1, P(A), None) == INVALID    # not a multiple of 16 KiB
+    assert r(P(A), 0, 1, P(A), None) == INVALID
+    assert r(P(A), 16384, 2, P(A), None) == INVALID         # policy flag
+    assert r(P(A), 16384, 0, P(A + 2), None) == INVALID     # misaligned result
+
+
 def _decode(kvq, d, **kw):
     P = ctypes.c_void_p
     a = dict(q=P(A), n_q_heads=24, page_table=P(A), max_pages=64, seq_lens=P(A), batch=1, max_seq_len=1024,

@@ -162,6 +162,20 @@ def test_store_rotate_q_one_launch(kvq, D, kdt, qdt):
         assert torch.equal(qq, q_rot)
 
 
+@pytest.mark.parametrize("non_temporal", [True, False])
+def test_stream_read_reads_every_word(kvq, non_temporal):
+    """The read-ceiling measurement: its fold is the XOR of the final 16 KiB
+    block, for a buffer shorter and one longer than the grid."""
+    for blocks in (37, 2048 + 333):
+        _say(f"stream_read nt={non_temporal} blocks={blocks}")
+        x = torch.randint(0, 256, (blocks * 16384,), dtype=torch.uint8, generator=torch.Generator().manual_seed(5))
+        tail = x.numpy()[(blocks - 1) * 16384:]
+        want = np.bitwise_xor.reduce(tail.view(np.uint32))
+        got = kvq.kvq_stream_read(x.cuda(), non_temporal=non_temporal)
+        torch.cuda.synchronize()
+        assert int(got.cpu().numpy().view(np.uint32)[0]) == int(want)
+
+
 # ----------------------------------------------------------------- 4-bit decode
 
 def _check_q4(case, split_keys, chunked_partials=False):
