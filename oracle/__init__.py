@@ -59,6 +59,7 @@ def lib():
             "kvqo_mla_attention": ([_P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _D, _P, _P], _I),
             "kvqo_mla_attention_chunked": ([_P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _D, _I, _I,
                                             _P, _P, _P, _P, _P], _I),
+            "kvqo_mla_attention_sel": ([_P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _I, _D, _P, _P], _I),
             "kvqo_f32_to_f16_array": ([_P, _P, _I64], None),
             "kvqo_e4m3_encode_array": ([_P, _P, _I64], None),
         }
@@ -257,4 +258,26 @@ def mla_attention(codes_pool, scale_pool, q, page_table, seq_lens, sm_scale, rop
            "mla_attention_chunked")
     if return_partials:
         return out, lse, (pa, pm, pz)
+    return out, lse
+
+
+def mla_attention_sel(codes_pool, scale_pool, q, page_table, sel, n_sel, sm_scale, rope_dim, page_size):
+    """fp64 absorbed attention over the selected rows of the fp8 latent cache (DSA gather).
+    sel: int32 [B][max_sel] absolute positions (entries outside the page capacity, e.g. -1,
+    are absent); n_sel: int32 [B] entries used per sequence.  Returns (out [B][H][L], lse [B][H])."""
+    n_slots, D = codes_pool.shape
+    num_pages = n_slots // page_size
+    q = _c(q, np.float32)
+    B, H, Dq = q.shape
+    assert Dq == D
+    L = D - rope_dim
+    pt = _c(page_table, np.int32)
+    sl = _c(sel, np.int32)
+    ns = _c(n_sel, np.int32)
+    assert sl.ndim == 2 and sl.shape[0] == B and ns.shape == (B,)
+    out = np.empty((B, H, L), np.float64)
+    lse = np.empty((B, H), np.float64)
+    _check(lib().kvqo_mla_attention_sel(_ptr(codes_pool), _ptr(scale_pool), D, rope_dim, page_size, num_pages,
+                                        _ptr(q), H, _ptr(pt), pt.shape[1], _ptr(sl), sl.shape[1], _ptr(ns), B,
+                                        float(sm_scale), _ptr(out), _ptr(lse)), "mla_attention_sel")
     return out, lse

@@ -610,6 +610,67 @@ int kvqo_mla_attention_chunked(const uint8_t* codes_pool, const float* scale_poo
     return err;
 }
 
+/* Latent attention over a selection of cached rows ([CO] split-T commit,
+ * DSA gather: attend the selected rows, given as absolute positions).  For
+ * sequence b the keys are the positions sel[b * max_sel + k], k < n_sel[b],
+ * in list order; an entry outside [0, max_pages * page_size) -- e.g. the -1
+ * that pads a fixed-size list -- is absent, and a position listed twice is
+ * attended twice.  Per head, exactly the formula of kvqo_mla_attention over
+ * those keys; no key gives out = 0 and lse = -inf. */
+int kvqo_mla_attention_sel(const uint8_t* codes_pool, const float* scale_pool, int D, int rope_dim, int page_size,
+                           int num_pages, const float* q, int n_heads, const int32_t* page_table, int max_pages,
+                           const int32_t* sel, int max_sel, const int32_t* n_sel, int B, double sm_scale,
+                           double* out, double* lse) {
+    const int L = D - rope_dim;
+    const int64_t cap = (int64_t)max_pages * page_size;
+    for (int b = 0; b < B; ++b)
+        if (n_sel[b] < 0 || n_sel[b] > max_sel) return KVQO_ERANGE;
+    int err = KVQO_OK;
+#pragma omp parallel for schedule(dynamic, 1) reduction(min : err)
+    for (int bh = 0; bh < B * n_heads; ++bh) {
+        const int b = bh / n_heads;
+        const int n = n_sel[b];
+        const int32_t* list = sel + (size_t)b * max_sel;
+        const float* qh = q + (size_t)bh * D;
+        double* o = out + (size_t)bh * L;
+        double* s = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        int64_t* slots = malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
+        int st = KVQO_OK, kept = 0;
+        double m = -INFINITY;
+        for (int k = 0; k < n; ++k) {
+            slots[k] = -1;
+            if (list[k] < 0 || (int64_t)list[k] >= cap) continue;  /* absent entry */
+            int64_t slot = kvqo_slot(page_table, max_pages, b, list[k], page_size);
+            if (slot < 0 || slot >= (int64_t)num_pages * page_size) { st = KVQO_ERANGE; break; }
+            slots[k] = slot;
+            const uint8_t* c = codes_pool + (size_t)slot * D;
+            double dl = 0.0, dr = 0.0;
+            for (int i = 0; i < L; ++i) dl += (double)qh[i] * kvqo_e4m3_decode(c[i]);
+            for (int i = L; i < D; ++i) dr += (double)qh[i] * kvqo_e4m3_decode(c[i]);
+            s[k] = sm_scale * ((double)scale_pool[2 * slot] * dl + (double)scale_pool[2 * slot + 1] * dr);
+            if (s[k] > m) m = s[k];
+            ++kept;
+        }
+        for (int i = 0; i < L; ++i) o[i] = 0.0;
+        double z = 0.0;
+        if (st == KVQO_OK && kept > 0) {
+            for (int k = 0; k < n; ++k) {
+                if (slots[k] < 0) continue;
+                const uint8_t* c = codes_pool + (size_t)slots[k] * D;
+                double w = exp(s[k] - m);
+                z += w;
+                double ws = w * (double)scale_pool[2 * slots[k]];
+                for (int i = 0; i < L; ++i) o[i] += ws * kvqo_e4m3_decode(c[i]);
+            }
+            for (int i = 0; i < L; ++i) o[i] /= z;
+        }
+        if (lse) lse[bh] = kept > 0 ? m + log(z) : -INFINITY;
+        if (st < err) err = st;
+        free(s); free(slots);
+    }
+    return err;
+}
+
 /* Batch helpers for the tests: element-wise codecs over arrays. */
 void kvqo_f32_to_f16_array(const float* x, uint16_t* y, int64_t n) {
 #pragma omp parallel for schedule(static)

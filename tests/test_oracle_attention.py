@@ -255,3 +255,81 @@ def test_mla_row_bytes_match_the_page():
     w = wl.MLA_262K
     assert w.head_dim + 2 * 4 == 584
     assert w.seq_len * 584 == 153092096
+
+
+# ------------------------------------------------ fp8 latent, selected rows (DSA gather)
+
+def _brute_mla_sel(codes, scales, q, pt, sel, n_sel, w):
+    """numpy fp64 over an explicit key list: decoded rows gathered with torch's
+    e4m3 decoder, softmax by scipy, entries outside the page capacity skipped."""
+    deq = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    deq[np.isnan(deq)] = 0.0
+    L = w.kv_lora
+    cap = pt.shape[1] * w.page_size
+    B, H, _ = q.shape
+    o = np.zeros((B, H, L))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        pos = np.array([p for p in sel[b, :n_sel[b]] if 0 <= p < cap], np.int64)
+        if pos.size == 0:
+            continue
+        slots = pt[b, pos // w.page_size].astype(np.int64) * w.page_size + pos % w.page_size
+        lat = deq[slots, :L] * scales[slots, 0:1]
+        rope = deq[slots, L:] * scales[slots, 1:2]
+        for h in range(H):
+            s = w.sm_scale * (lat @ q[b, h, :L].astype(np.float64) + rope @ q[b, h, L:].astype(np.float64))
+            o[b, h] = scipy.special.softmax(s) @ lat
+            lse[b, h] = scipy.special.logsumexp(s)
+    return o, lse
+
+
+def test_mla_sel_all_positions_equals_dense():
+    """Selecting every position 0..T-1 in order is the dense attention, bit for bit."""
+    w = MLA_SMALL
+    lens = [700, 33]
+    codes, scales, q, pt, sl = _build_mla(w, lens)
+    o, lse = oracle.mla_attention(codes, scales, q, pt, sl, w.sm_scale, w.rope_dim, w.page_size)
+    sel = np.full((2, 800), -1, np.int32)
+    for b, T in enumerate(lens):
+        sel[b, :T] = np.arange(T)
+    os_, ls = oracle.mla_attention_sel(codes, scales, q, pt, sel, sl, w.sm_scale, w.rope_dim, w.page_size)
+    assert np.array_equal(o, os_) and np.array_equal(lse, ls)
+
+
+def test_mla_sel_matches_brute_force():
+    """A shuffled selection with repeats, padding (-1) and out-of-capacity
+    entries against the numpy brute force; an empty selection gives 0 / -inf."""
+    w = MLA_SMALL
+    lens = [900, 400, 50]
+    codes, scales, q, pt, sl = _build_mla(w, lens)
+    rng = np.random.default_rng(3)
+    cap = pt.shape[1] * w.page_size
+    sel = np.full((3, 300), -1, np.int32)
+    sel[0, :250] = rng.integers(0, 900, 250)                 # repeats likely
+    sel[0, 7], sel[0, 8] = cap, cap + 5                      # outside the capacity: absent
+    sel[1, :300] = rng.permutation(400)[:300]
+    n_sel = np.array([260, 300, 0], np.int32)                # entries 250..259 of row 0 are padding
+    o, lse = oracle.mla_attention_sel(codes, scales, q, pt, sel, n_sel, w.sm_scale, w.rope_dim, w.page_size)
+    ro, rl = _brute_mla_sel(codes, scales, q, pt, sel, n_sel, w)
+    for b in range(3):
+        for h in range(w.n_heads):
+            assert np.max(np.abs(o[b, h] - ro[b, h])) < 1e-12 * max(1.0, np.abs(ro[b, h]).max())
+    fin = np.isfinite(rl)
+    assert np.array_equal(fin, np.isfinite(lse)) and np.max(np.abs(lse[fin] - rl[fin])) < 1e-12
+    assert np.all(o[2] == 0) and np.all(np.isneginf(lse[2]))
+
+
+def test_mla_sel_order_and_duplicates():
+    """Softmax attention is a function of the key multiset: reversing the list
+    changes nothing beyond rounding, and listing every key twice changes
+    nothing (each weight doubles, so does the normalizer) except lse += ln 2."""
+    w = MLA_SMALL
+    codes, scales, q, pt, sl = _build_mla(w, [600])
+    sel = np.random.default_rng(4).permutation(600)[:400].astype(np.int32)[None, :]
+    n = np.array([400], np.int32)
+    a = oracle.mla_attention_sel(codes, scales, q, pt, sel, n, w.sm_scale, w.rope_dim, w.page_size)
+    r = oracle.mla_attention_sel(codes, scales, q, pt, sel[:, ::-1].copy(), n, w.sm_scale, w.rope_dim, w.page_size)
+    d = oracle.mla_attention_sel(codes, scales, q, pt, np.concatenate([sel, sel], 1), n * 2, w.sm_scale,
+                                 w.rope_dim, w.page_size)
+    assert np.max(np.abs(a[0] - r[0])) < 1e-12 and np.max(np.abs(a[1] - r[1])) < 1e-12
+    assert np.max(np.abs(a[0] - d[0])) < 1e-12 and np.max(np.abs(a[1] + np.log(2.0) - d[1])) < 1e-12
