@@ -262,6 +262,67 @@ class MlaBench(_Bench):
         return self.T * w.n_heads * 2 * (w.head_dim + w.kv_lora)
 
 
+class DsaBench(_Bench):
+    """Selected rows (DSA gather) over the fp8 latent workload's layer caches:
+    `batch` sequences share each layer's context (the same pages), each with
+    its own query and its own seeded selection of n_sel distinct positions;
+    step per layer: decode over the selection, merge."""
+
+    DECODE = 0
+    DECODE_MERGE = (0, 1)
+
+    def __init__(self, mla, n_sel, batch, split_keys=512, device="cuda"):
+        import torch
+
+        import workloads as wl
+        w, kvq = mla.w, mla.kvq
+        self.w, self.kvq, self.n_sel, self.batch = w, kvq, n_sel, batch
+        T = mla.T
+        H = w.n_heads
+        self.page_table = mla.page_table.expand(batch, -1).contiguous()
+        self.q, self.sel = [], []
+        for layer in range(w.n_layers):
+            self.q.append(wl.mla_query(wl.shrink(w, batch=batch), layer, device))
+            sel, ns = wl.dsa_selection(w, [T] * batch, [n_sel] * batch, n_sel, seed_key=layer)
+            self.sel.append(sel.to(device))
+        self.n_sel_t = ns.to(device)
+        acc_shape, mz_shape = kvq.partial_shapes(mla.caches[0], batch, H, n_sel, split_keys)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.pa, self.pm, self.pz = torch.empty(acc_shape, **f32), torch.empty(mz_shape, **f32), torch.empty(mz_shape, **f32)
+        self.out = torch.empty((w.n_layers, batch, H, w.kv_lora), **f32)
+        self.lse = torch.empty((w.n_layers, batch, H), **f32)
+        for layer, c in enumerate(mla.caches):  # one checked pass through the binding
+            kvq.kvq_decode_attn_sel(c, self.q[layer], self.page_table, self.sel[layer], self.n_sel_t, w.sm_scale,
+                                    split_keys, self.pa, self.pm, self.pz)
+            kvq.kvq_merge(c, self.pa, self.pm, self.pz, self.n_sel_t, n_sel, split_keys, out=self.out[layer],
+                          lse=self.lse[layer])
+        torch.cuda.synchronize()
+        P = ctypes.c_void_p
+        stream = P(torch.cuda.current_stream().cuda_stream)
+        self.raw = []
+        for layer, c in enumerate(mla.caches):
+            d = ctypes.byref(c.desc)
+            self.raw.append([
+                ("kvq_decode_attn_sel", (d, P(self.q[layer].data_ptr()), H, P(self.page_table.data_ptr()),
+                                         self.page_table.shape[1], P(self.sel[layer].data_ptr()),
+                                         P(self.n_sel_t.data_ptr()), batch, n_sel, ctypes.c_float(w.sm_scale),
+                                         split_keys, P(self.pa.data_ptr()), P(self.pm.data_ptr()),
+                                         P(self.pz.data_ptr()), stream)),
+                ("kvq_merge", (d, P(self.pa.data_ptr()), P(self.pm.data_ptr()), P(self.pz.data_ptr()),
+                               P(self.n_sel_t.data_ptr()), batch, H, n_sel, split_keys, 0,
+                               P(self.out[layer].data_ptr()), P(self.lse[layer].data_ptr()), stream)),
+            ])
+
+    @property
+    def kv_bytes_per_layer(self):
+        return self.batch * self.n_sel * (self.w.head_dim + 8)
+
+    @property
+    def flops_per_layer(self):
+        w = self.w
+        return self.batch * self.n_sel * w.n_heads * 2 * (w.head_dim + w.kv_lora)
+
+
 class RaggedBench(_Bench):
     """The ragged batch: 16 sequences of seeded lengths over a shuffled paged
     pool (one layer).  Step: the 2048-token prefill chunk of a 17th sequence
@@ -592,6 +653,26 @@ def main():
                 cb = wx.prefill_chunk * wx.n_kv_heads * 2 * (2 * wx.head_dim + wx.row_bytes)
                 e["chunk_store_gbs"] = round(cb / (mx["chunk_store_us"] * 1e-6) / 1e9, 2)
             extras[name] = e
+            if cls is MlaBench:
+                # selected rows (DSA gather) over the same layer caches
+                # splits as measured best: short lists need short splits to give the GPU workgroups
+                for n_sel, batch, split in ((2048, 1, 64), (4096, 1, 64), (2048, 16, 256)):
+                    dname = f"dsa_fp8_262k_sel{n_sel}_b{batch}"
+                    _log(f"bench: side measurement {dname}")
+                    bd = DsaBench(bx, n_sel, batch, split)
+                    md = measure(bd, args.steps, args.warmup)
+                    extras[dname] = {
+                        "layers": wx.n_layers, "context": wx.seq_len, "batch": batch, "n_sel": n_sel,
+                        "split_keys": split, "steps": args.steps,
+                        "gathered_bytes_per_layer": bd.kv_bytes_per_layer,
+                        "us_per_layer": round(md["us_per_layer"], 3),
+                        "graph_us_per_layer": round(md["graph_us_per_layer"], 3),
+                        "decode_us": round(md["decode_us"], 3),
+                        "decode_gathered_gbs": round(md["decode_gbs"], 2),
+                        "decode_tflops": round(md["decode_tflops"], 2),
+                        "note": "decode over the selection + merge per layer; the batch shares the layer's "
+                                "context; the gathered rows stay cache-resident across steps"}
+                    del bd
             del bx
             torch.cuda.empty_cache()
         rec["extras"] = extras

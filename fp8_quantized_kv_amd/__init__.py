@@ -33,7 +33,8 @@ DT_F32, DT_BF16, DT_F16 = 0, 1, 2
 _DTYPES = {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float16: DT_F16}
 
 EXPORTED = ("kvq_status_string", "kvq_row_bytes", "kvq_pool_bytes", "kvq_num_splits", "kvq_store",
-            "kvq_rotate_q", "kvq_store_rotate_q", "kvq_decode_attn", "kvq_merge", "kvq_stream_read")
+            "kvq_rotate_q", "kvq_store_rotate_q", "kvq_decode_attn", "kvq_decode_attn_sel", "kvq_merge",
+            "kvq_stream_read")
 
 
 class KvqCacheDesc(ctypes.Structure):
@@ -61,6 +62,7 @@ def _load():
         "kvq_decode_attn": ([C, P, I32, P, I32, P, I32, I32, F, I32, P, P, P, P], I32),
         "kvq_merge": ([C, P, P, P, P, I32, I32, I32, I32, I32, P, P, P], I32),
         "kvq_stream_read": ([P, ctypes.c_size_t, I32, P, P], I32),
+        "kvq_decode_attn_sel": ([C, P, I32, P, I32, P, P, I32, I32, F, I32, P, P, P, P], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -246,6 +248,34 @@ def kvq_decode_attn(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split
     _check(lib.kvq_decode_attn(ctypes.byref(cache.desc), qp, Hq, ptp, int(page_table.shape[1]), slp, B,
                                int(max_seq_len), float(sm_scale), int(split_keys), pa, pm, pz, _stream(q)),
            "kvq_decode_attn")
+    return part_acc, part_m, part_z
+
+
+def kvq_decode_attn_sel(cache, q, page_table, sel, n_sel, sm_scale, split_keys, part_acc=None, part_m=None,
+                        part_z=None):
+    """Decode attention over selected rows of the fp8 latent cache; returns the partials (acc, m, z).
+
+    sel: int32 [B][max_sel] absolute positions (entries outside the page capacity, e.g. -1, are
+    absent); n_sel: int32 [B] entries used.  Merge with kvq_merge(cache, ..., n_sel, max_sel, split_keys)."""
+    B, H, D = q.shape
+    max_sel = int(sel.shape[1])
+    acc_shape, mz_shape = partial_shapes(cache, B, H, max_sel, split_keys)
+    if part_acc is None:
+        part_acc = torch.empty(acc_shape, dtype=torch.float32, device=q.device)
+        part_m = torch.empty(mz_shape, dtype=torch.float32, device=q.device)
+        part_z = torch.empty(mz_shape, dtype=torch.float32, device=q.device)
+    qp = _dev(q, "q", dtype=torch.float32, shape=(B, H, cache.head_dim))
+    ptp = _dev(page_table, "page_table", dtype=torch.int32)
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [batch][max_pages]")
+    sp = _dev(sel, "sel", dtype=torch.int32, shape=(B, max_sel))
+    np_ = _dev(n_sel, "n_sel", dtype=torch.int32, shape=(B,))
+    pa = _dev(part_acc, "part_acc", dtype=torch.float32, shape=acc_shape)
+    pm = _dev(part_m, "part_m", dtype=torch.float32, shape=mz_shape)
+    pz = _dev(part_z, "part_z", dtype=torch.float32, shape=mz_shape)
+    _check(lib.kvq_decode_attn_sel(ctypes.byref(cache.desc), qp, H, ptp, int(page_table.shape[1]), sp, np_, B,
+                                   max_sel, float(sm_scale), int(split_keys), pa, pm, pz, _stream(q)),
+           "kvq_decode_attn_sel")
     return part_acc, part_m, part_z
 
 

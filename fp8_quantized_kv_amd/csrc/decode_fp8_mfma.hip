@@ -44,6 +44,15 @@
 //    the latent gathered by two ds_read_b64_tr_b16 (source lane 4e + m of a
 //    16-lane group addresses key slot e at channels 4m .. 4m + 3, so lane j
 //    receives channel j of keys e = 0..3; the second read takes slots 4..7).
+//
+// Selected rows (colibri split-T commit, DSA gather: attend the selected
+// rows, given as absolute positions): the keys of a split are entries
+// j0 .. j1-1 of the sequence's list instead of positions j0 .. j1-1.  The
+// workgroup first resolves every entry of its split to a cache slot (list,
+// then page table) into an LDS table; each staged row is then addressed on
+// its own, and entries outside the page capacity (the -1 of a padded list)
+// are masked like rows past the end.  Everything after the staging is the
+// same code.
 #include "mfma_common.h"
 
 namespace kvq {
@@ -64,6 +73,8 @@ constexpr int kScaleOff = kTile * kPitch;            // scales after the rows
 constexpr int kStage = kScaleOff + kTile * 8;        // 37632 bytes
 constexpr int kXOff = 2 * kStage;                    // partial-score exchange: [wave][lane][8] f32
 constexpr int kLds = kXOff + kWaves * 64 * 8 * 4;
+constexpr int kSelOff = kLds;                        // selected rows: the split's slot table
+constexpr int kLdsSel = kSelOff + 2048 * 4;          // int32 per entry, split_keys <= 2048
 constexpr int kChunks = kTile * kD / 16;             // 16-byte code chunks per tile (1152)
 constexpr int kChunkRow = kD / 16;                   // chunks per row (36)
 constexpr int kPerThread = (kChunks + kThreads - 1) / kThreads;  // 3 (the third of 128 threads)
@@ -90,10 +101,11 @@ __device__ __forceinline__ uint32_t clear_nan_codes(uint32_t w) {
 // 2^e for an integer e in [-126, 127], exactly.
 __device__ __forceinline__ float exp2i(int e) { return __uint_as_float(uint32_t(e + 127) << 23); }
 
+template <bool SEL>
 __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __restrict__ codes,
                                                             const float* __restrict__ scales, int page_size,
                                                             int num_pages, DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SEL ? kLdsSel : kLds];
 
     const int s = blockIdx.x, hblk = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -127,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
     int64_t rslot[2] = {0, 0};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        if (h == 1 && n_runs <= 64) break;
+        if (SEL || (h == 1 && n_runs <= 64)) break;
         const int r = min(lane + 64 * h, n_runs - 1);
         const int pos = min(j0 + 16 * r, last_pos);
         int page = pt[pos / page_size];
@@ -157,13 +169,54 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
         return int64_t((uint64_t(hi) << 32) | lo);
     };
 
+    // ---- selected rows: slot of every entry of the split (-1: absent entry;
+    // entries past the split's end point at slot 0 and are masked by `valid`).
+    int32_t* slot_tab = reinterpret_cast<int32_t*>(smem + kSelOff);
+    bool any_absent = false;
+    if constexpr (SEL) {
+        const int32_t* list = a.sel + int64_t(b) * a.sel_stride + j0;
+        const int64_t cap = int64_t(a.max_pages) * page_size;
+        for (int k = tid; k < n_tiles * kTile; k += kThreads) {
+            int32_t slot = 0;
+            if (k < n_keys) {
+                const int32_t pos = list[k];
+                if (pos >= 0 && pos < cap) {
+                    int page = pt[pos / page_size];
+                    page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+                    slot = page * page_size + pos % page_size;
+                } else {
+                    slot = -1;
+                    any_absent = true;
+                }
+            }
+            slot_tab[k] = slot;
+        }
+        any_absent = __syncthreads_or(any_absent);  // also publishes the table
+    }
+
     // ---- staging: thread tid owns code chunks tid + 512 i (i < 3 while
-    // < 1152); threads 128..143 own the 16 scale chunks instead of a third.
+    // < 1152); threads 128..143 own the 16 scale chunks instead of a third
+    // (selected rows: threads 128..159 the 32 rows' scale pairs).
     u32x4 stg[kPerThread];
-    const bool has_scale = tid >= 128 && tid < 144;
+    const bool has_scale = tid >= 128 && tid < (SEL ? 160 : 144);
     auto chunk_row = [&](int i) { return (tid + kThreads * i) / kChunkRow; };
     auto chunk_col = [&](int i) { return (tid + kThreads * i) % kChunkRow; };
     auto load_tile = [&](int t) {
+        if constexpr (SEL) {
+            const int32_t* tab = slot_tab + t * kTile;
+#pragma unroll
+            for (int i = 0; i < kPerThread; ++i) {
+                if (tid + kThreads * i < kChunks) {
+                    const int64_t sl = max(tab[chunk_row(i)], 0);
+                    stg[i] = *reinterpret_cast<const u32x4*>(codes + sl * kD + 16 * chunk_col(i));
+                } else if (has_scale) {
+                    const int64_t sl = max(tab[tid - 128], 0);
+                    const uint2 v = *reinterpret_cast<const uint2*>(scales + sl * 2);
+                    stg[i] = u32x4{v.x, v.y, 0u, 0u};
+                }
+            }
+            return;
+        }
         const int64_t ra = run_slot(2 * t), rb = run_slot(2 * t + 1);
         const uint8_t* ca = codes + ra * kD;
         const uint8_t* cb = codes + rb * kD;
@@ -196,7 +249,10 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
                 d[0] = cvt8(w[0], w[1]);
                 d[1] = cvt8(w[2], w[3]);
             } else if (has_scale) {
-                *reinterpret_cast<u32x4*>(st + kScaleOff + 16 * (tid - 128)) = stg[i];
+                if (SEL)
+                    *reinterpret_cast<uint2*>(st + kScaleOff + 8 * (tid - 128)) = make_uint2(stg[i][0], stg[i][1]);
+                else
+                    *reinterpret_cast<u32x4*>(st + kScaleOff + 16 * (tid - 128)) = stg[i];
             }
         }
     };
@@ -303,6 +359,17 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
                         scl[kb][i] = 0.0f;  // rows past the end may hold any scale
                     }
         }
+        if (SEL && any_absent) {  // absent entries of the list: slot 0 was staged in their place
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (slot_tab[t * kTile + 16 * kb + 4 * q4 + i] < 0) {
+                        sc[kb][i] = -INFINITY;
+                        scl[kb][i] = 0.0f;
+                    }
+        }
 
         // ---- running maximum (per head) and running scale exponent (uniform)
         // (scores are finite or -inf, scales finite or 0: no NaN reaches these maxima)
@@ -385,7 +452,12 @@ bool decode_fp8_mfma_supported(const Fp8Pool& pool, const DecodeArgs& a) {
 
 hipError_t launch_decode_fp8_mfma(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s) {
     const dim3 grid(unsigned(a.n_splits), unsigned((a.n_q_heads + kHeadsWG - 1) / kHeadsWG), unsigned(a.batch));
-    decode_fp8_mfma<<<grid, dim3(kThreads), 0, s>>>(pool.codes, pool.scales, pool.page_size, pool.num_pages, a);
+    if (a.sel)
+        decode_fp8_mfma<true><<<grid, dim3(kThreads), 0, s>>>(pool.codes, pool.scales, pool.page_size, pool.num_pages,
+                                                              a);
+    else
+        decode_fp8_mfma<false><<<grid, dim3(kThreads), 0, s>>>(pool.codes, pool.scales, pool.page_size,
+                                                               pool.num_pages, a);
     return hipGetLastError();
 }
 

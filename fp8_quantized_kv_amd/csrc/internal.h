@@ -158,6 +158,11 @@ struct DecodeArgs {
     float* part_acc;
     float* part_m;
     float* part_z;
+    // Selected rows (fp8 latent only): when set, the keys of sequence b are
+    // the positions sel[b * sel_stride + k], k < seq_lens[b] (max_seq_len is
+    // the list capacity); entries outside the page capacity are absent.
+    const int32_t* sel = nullptr;
+    int sel_stride = 0;
 };
 
 // Matrix-core kernel for the 4-bit cache (head_dim 128/256, pages of a
@@ -172,7 +177,8 @@ bool decode_q4_pair_supported(const Q4Pool& pool, const DecodeArgs& a);
 hipError_t launch_decode_q4_pair(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s);
 
 // Matrix-core kernel for the fp8 latent cache (512 + 64, pages of a
-// multiple of 16 tokens, split_keys <= 2048).
+// multiple of 16 tokens, split_keys <= 2048), over consecutive positions or
+// (a.sel set) over a list of selected positions.
 bool decode_fp8_mfma_supported(const Fp8Pool& pool, const DecodeArgs& a);
 hipError_t launch_decode_fp8_mfma(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s);
 

@@ -52,10 +52,12 @@ kvq::Fp8Pool fp8_pool(const kvq_cache* c) {
 
 kvq_status launched(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH; }
 
-// Shared checks of kvq_decode_attn / kvq_merge arguments.
+// Shared checks of kvq_decode_attn / kvq_decode_attn_sel / kvq_merge arguments; split_keys must be a
+// positive multiple of split_unit (512 for decode over positions, 32 for selections and the merge).
 kvq_status check_seq_args(const kvq_cache* c, int32_t n_q_heads, const int32_t* seq_lens, int32_t batch,
-                          int32_t max_seq_len, int32_t split_keys) {
-    if (n_q_heads < 1 || batch < 0 || max_seq_len < 0 || split_keys < 512 || split_keys % 512) return KVQ_ERR_INVALID_ARG;
+                          int32_t max_seq_len, int32_t split_keys, int32_t split_unit) {
+    if (n_q_heads < 1 || batch < 0 || max_seq_len < 0 || split_keys < split_unit || split_keys % split_unit)
+        return KVQ_ERR_INVALID_ARG;
     if (n_q_heads % c->num_kv_heads) return KVQ_ERR_INVALID_ARG;
     if (batch > 0 && !aligned(seq_lens, 4)) return KVQ_ERR_INVALID_ARG;
     if (batch > 65535) return KVQ_ERR_UNSUPPORTED;
@@ -162,7 +164,7 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_h
                            hipStream_t stream) {
     kvq_status st = check_cache(cache);
     if (st != KVQ_OK) return st;
-    st = check_seq_args(cache, n_q_heads, seq_lens, batch, max_seq_len, split_keys);
+    st = check_seq_args(cache, n_q_heads, seq_lens, batch, max_seq_len, split_keys, 512);
     if (st != KVQ_OK) return st;
     if (max_pages < 1 || int64_t(max_seq_len) > int64_t(max_pages) * cache->page_size) return KVQ_ERR_INVALID_ARG;
     if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return KVQ_ERR_INVALID_ARG;
@@ -182,12 +184,35 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_h
     return launched(kvq::launch_decode_fp8_simple(pool, a, stream));
 }
 
+kvq_status kvq_decode_attn_sel(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
+                               int32_t max_pages, const int32_t* sel, const int32_t* n_sel, int32_t batch,
+                               int32_t max_sel, float sm_scale, int32_t split_keys, float* part_acc, float* part_m,
+                               float* part_z, hipStream_t stream) {
+    kvq_status st = check_cache(cache);
+    if (st != KVQ_OK) return st;
+    if (cache->format != KVQ_FMT_FP8_E4M3_ROW) return KVQ_ERR_UNSUPPORTED;
+    st = check_seq_args(cache, n_q_heads, n_sel, batch, max_sel, split_keys, 32);
+    if (st != KVQ_OK) return st;
+    if (max_pages < 1) return KVQ_ERR_INVALID_ARG;
+    if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return KVQ_ERR_INVALID_ARG;
+    if (batch == 0) return KVQ_OK;
+    if (!aligned(q) || !aligned(page_table, 4) || !aligned(sel, 4) || !aligned(part_acc) || !aligned(part_m, 4) ||
+        !aligned(part_z, 4))
+        return KVQ_ERR_INVALID_ARG;
+    kvq::DecodeArgs a{q, n_q_heads, page_table, max_pages, n_sel, batch, max_sel,
+                      kvq_num_splits(max_sel, split_keys), sm_scale, split_keys, part_acc, part_m, part_z,
+                      sel, max_sel};
+    const kvq::Fp8Pool pool = fp8_pool(cache);
+    if (!kvq::decode_fp8_mfma_supported(pool, a)) return KVQ_ERR_UNSUPPORTED;
+    return launched(kvq::launch_decode_fp8_mfma(pool, a, stream));
+}
+
 kvq_status kvq_merge(const kvq_cache* cache, const float* part_acc, const float* part_m, const float* part_z,
                      const int32_t* seq_lens, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
                      int32_t split_keys, int32_t inverse_rotate, float* out, float* lse, hipStream_t stream) {
     kvq_status st = check_cache(cache);
     if (st != KVQ_OK) return st;
-    st = check_seq_args(cache, n_q_heads, seq_lens, batch, max_seq_len, split_keys);
+    st = check_seq_args(cache, n_q_heads, seq_lens, batch, max_seq_len, split_keys, 32);
     if (st != KVQ_OK) return st;
     const bool q4 = cache->format == KVQ_FMT_Q4_H32;
     if (inverse_rotate != (q4 ? 1 : 0)) return KVQ_ERR_INVALID_ARG;

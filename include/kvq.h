@@ -203,6 +203,27 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_h
                            float sm_scale, int32_t split_keys, float* part_acc, float* part_m, float* part_z,
                            hipStream_t stream);
 
+/* Split decode attention over SELECTED rows of an FP8 latent cache (colibri
+ * split-T commit, DSA gather: attend the selected rows, given as absolute
+ * positions; a list of 1024 or more entries is split into partials and
+ * merged).  Sequence b attends the positions sel[b*max_sel + k] for
+ * k < n_sel[b], in list order; an entry outside [0, max_pages*page_size)
+ * (e.g. -1 padding a fixed-size list) is absent, and a position listed
+ * twice is attended twice.  Split s covers list entries [s*split_keys,
+ * min((s+1)*split_keys, n_sel[b])); everything else -- q, the scores, the
+ * partials (S = kvq_num_splits(max_sel, split_keys)) -- is as for
+ * kvq_decode_attn on an FP8 cache, and kvq_merge(cache, ..., n_sel, batch,
+ * n_q_heads, max_sel, split_keys, 0, out, lse) completes the attention.
+ * sel: device int32 [batch][max_sel]; n_sel: device int32 [batch], each in
+ * [0, max_sel]; split_keys: a positive multiple of 32 (the key tile), at
+ * most 2048 -- short lists run faster with short splits, which give more
+ * workgroups; the cache's page_size a multiple of 16.  A Q4 cache gives
+ * KVQ_ERR_UNSUPPORTED. */
+kvq_status kvq_decode_attn_sel(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
+                               int32_t max_pages, const int32_t* sel, const int32_t* n_sel, int32_t batch,
+                               int32_t max_sel, float sm_scale, int32_t split_keys, float* part_acc, float* part_m,
+                               float* part_z, hipStream_t stream);
+
 /* ---------------------------------------------------------------- merge */
 
 /* Log-sum-exp merge of the partials (colibri split-T commit), in a fixed
@@ -215,6 +236,9 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_h
  *   lse = M + log Z.
  * A sequence with T = 0 gives out = 0 and lse = -inf.  Only the splits that
  * cover [0, T_b) are read.  inverse_rotate must be 1 for Q4 and 0 for FP8.
+ * seq_lens, max_seq_len and split_keys are those of the decode call that
+ * wrote the partials (for kvq_decode_attn_sel: n_sel and max_sel); split_keys
+ * is a positive multiple of 32.
  * out: [batch][n_q_heads][Dv] f32; lse: [batch][n_q_heads] f32 or NULL. */
 kvq_status kvq_merge(const kvq_cache* cache, const float* part_acc, const float* part_m, const float* part_z,
                      const int32_t* seq_lens, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,

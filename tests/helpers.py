@@ -109,6 +109,21 @@ class MlaCase:
         torch.cuda.synchronize()
         return out.cpu().numpy(), lse.cpu().numpy()
 
+    def gpu_attention_sel(self, sel, n_sel, split_keys):
+        """Decode over the selected rows, then the merge (sel, n_sel: CPU int32 tensors)."""
+        import fp8_quantized_kv_amd as kvq
+        sel_d, ns_d = sel.to("cuda"), n_sel.to("cuda")
+        pa, pm, pz = kvq.kvq_decode_attn_sel(self.cache, self.q, self.page_table, sel_d, ns_d, self.w.sm_scale,
+                                             split_keys)
+        out, lse = kvq.kvq_merge(self.cache, pa, pm, pz, ns_d, int(sel.shape[1]), split_keys)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), lse.cpu().numpy()
+
+    def ref_attention_sel(self, sel, n_sel):
+        return oracle.mla_attention_sel(self.codes_ref, self.scales_ref, self.q.cpu().numpy(),
+                                        self.lay.page_table.numpy(), sel.numpy(), n_sel.numpy(), self.w.sm_scale,
+                                        self.w.rope_dim, self.w.page_size)
+
     def ref_attention(self, heads=None):
         q = self.q.cpu().numpy()
         if heads is not None:

@@ -145,6 +145,23 @@ def test_store_rotate_argument_checks(kvq):
     assert r(*args(n=0, rows=0)) == 0                 # nothing to do: no launch
 
 
+def test_decode_sel_argument_checks(kvq):
+    P = ctypes.c_void_p
+    r = kvq.lib.kvq_decode_attn_sel
+    f = _fp8(kvq)
+    args = lambda **kw: [ctypes.byref(kw.get("d", f)), P(A), kw.get("h", 128), P(A), 64, P(kw.get("sel", A)), P(A),
+                         kw.get("b", 1), kw.get("ms", 4096), ctypes.c_float(kw.get("sm", 0.04)), kw.get("split", 1024),
+                         P(A), P(A), P(A), None]
+    assert r(*args(d=_q4(kvq))) == UNSUPPORTED           # fp8 latent only
+    assert r(*args(split=1000)) == INVALID                # split_keys % 32
+    assert r(*args(split=0)) == INVALID
+    assert r(*args(split=4096)) == UNSUPPORTED            # the matrix-core kernel takes <= 2048
+    assert r(*args(sel=A + 2)) == INVALID                 # misaligned list
+    assert r(*args(ms=-1)) == INVALID
+    assert r(*args(sm=float("nan"))) == INVALID
+    assert r(*args(b=0)) == 0                             # nothing to do: no launch
+
+
 def test_stream_read_argument_checks(kvq):
     P = ctypes.c_void_p
     r = kvq.lib.kvq_stream_read
@@ -187,6 +204,7 @@ def test_merge_argument_checks(kvq):
     assert m(ctypes.byref(d), P(A), P(A), P(A), P(A), 1, 24, 1024, 512, 0, P(A), None, None) == INVALID  # Q4 rotates
     assert m(ctypes.byref(f), P(A), P(A), P(A), P(A), 1, 16, 1024, 512, 1, P(A), None, None) == INVALID  # fp8 does not
     assert m(ctypes.byref(d), P(A), P(A), P(A), P(A), 1, 24, 1024, 1000, 1, P(A), None, None) == INVALID
+    assert m(ctypes.byref(d), P(A), P(A), P(A), P(A), 1, 24, 1024, 48, 1, P(A), None, None) == INVALID  # % 32
     assert m(ctypes.byref(d), P(A), P(A), P(A), P(A), 1, 24, 1024, 512, 1, P(A + 8), None, None) == INVALID
     assert m(ctypes.byref(d), P(A), P(A), P(A), P(A), 0, 24, 1024, 512, 1, P(A), None, None) == 0
 

@@ -449,6 +449,73 @@ def test_mla_batch_invariance(kvq):
         assert np.array_equal(o.cpu().numpy()[0], ob[b]) and np.array_equal(l.cpu().numpy()[0], lb[b])
 
 
+# ------------------------------------------------- fp8 latent, selected rows (DSA gather)
+
+@pytest.mark.parametrize("n_heads,n_sel,max_sel,split", [(128, [1000, 300, 0], 1024, 512), (40, [2049, 4096, 17], 4096, 2048),
+                                                         (16, [4096, 1536], 4096, 1024), (64, [100], 512, 512),
+                                                         (128, [2048, 33], 2048, 128), (24, [4096, 95], 4096, 32)])
+def test_mla_sel_matches_oracle(kvq, n_heads, n_sel, max_sel, split):
+    """Selected rows of a paged cache whose bytes past each sequence are 0xFF
+    (NaN codes and scales): seeded distinct positions in random order, padded
+    with -1, plus absent and repeated entries written into the lists."""
+    w = wl.shrink(wl.MLA_262K, n_heads=n_heads, seq_len=0)
+    lens = [6000, 4200, 5000][:len(n_sel)]
+    case = MlaCase(w, lens, fill=0xFF)
+    sel, ns = wl.dsa_selection(w, lens, n_sel, max_sel)
+    cap = case.page_table.shape[1] * w.page_size
+    if n_sel[0] > 40:
+        sel[0, 3], sel[0, 20] = -1, cap + 7     # absent entries inside the list
+        sel[0, 30] = sel[0, 31]                 # a repeat
+    _say(f"mla_sel heads={n_heads} n_sel={n_sel} max_sel={max_sel} split={split}")
+    o, lse = case.gpu_attention_sel(sel, ns, split)
+    ro, rl = case.ref_attention_sel(sel, ns)
+    assert np.all(np.isfinite(o))
+    err = rel_err(o, ro)
+    _say(f"  max_rel_err={err.max():.2e}")
+    assert err.max() < TOL
+    fin = np.isfinite(rl)
+    assert np.array_equal(fin, np.isfinite(lse)) and np.max(np.abs(lse[fin] - rl[fin])) < 1e-3 * max(1.0, np.abs(rl[fin]).max())
+    for b, n in enumerate(n_sel):
+        if n == 0:
+            assert np.all(o[b] == 0) and np.all(np.isneginf(lse[b]))
+
+
+def test_mla_sel_every_position_equals_dense(kvq):
+    """Selecting positions 0..T-1 in order reproduces the dense decode's
+    partials bit for bit: the staged tiles are the same bytes."""
+    import fp8_quantized_kv_amd as kvq_mod
+    w = wl.shrink(wl.MLA_262K, n_heads=128, seq_len=0)
+    lens = [3000, 1234]
+    case = MlaCase(w, lens, build_oracle=False)
+    T = max(lens)
+    sel = torch.full((2, T), -1, dtype=torch.int32)
+    for b, n in enumerate(lens):
+        sel[b, :n] = torch.arange(n, dtype=torch.int32)
+    ns = torch.tensor(lens, dtype=torch.int32)
+    for split in (512, 2048):
+        d = kvq_mod.kvq_decode_attn(case.cache, case.q, case.page_table, case.seq_lens, T, w.sm_scale, split)
+        s_ = kvq_mod.kvq_decode_attn_sel(case.cache, case.q, case.page_table, sel.cuda(), ns.cuda(), w.sm_scale, split)
+        torch.cuda.synchronize()
+        for x, y in zip(d, s_):
+            assert torch.equal(x, y)
+
+
+def test_mla_sel_batch_invariance(kvq):
+    """A sequence's selection gives bit-identical output alone and in a batch."""
+    import fp8_quantized_kv_amd as kvq_mod
+    w = wl.shrink(wl.MLA_262K, n_heads=64, seq_len=0)
+    lens = [5000, 3000, 4000]
+    case = MlaCase(w, lens, build_oracle=False)
+    sel, ns = wl.dsa_selection(w, lens, [2048, 700, 1500], 2048)
+    ob, lb = case.gpu_attention_sel(sel, ns, 1024)
+    for b in range(3):
+        pa, pm, pz = kvq_mod.kvq_decode_attn_sel(case.cache, case.q[b:b + 1].contiguous(),
+                                                 case.page_table[b:b + 1].contiguous(), sel[b:b + 1].cuda(),
+                                                 ns[b:b + 1].cuda(), w.sm_scale, 1024)
+        o, l = kvq_mod.kvq_merge(case.cache, pa, pm, pz, ns[b:b + 1].cuda(), 2048, 1024)
+        assert np.array_equal(o.cpu().numpy()[0], ob[b]) and np.array_equal(l.cpu().numpy()[0], lb[b])
+
+
 def test_mla_nan_codes_read_zero(kvq):
     """Codes 0x7F/0xFF (e4m3 NaN) in a cache read as 0 (colibri correctness
     commit: the CPU table reads 0 for NaN codes)."""

@@ -278,3 +278,17 @@ def mla_query(w, layer, device="cpu"):
     """Absorbed query [B][H][kv_lora + rope] float32 ~ N(0,1)."""
     g = _gen(device, w.seed, 202, layer)
     return torch.randn((w.batch, w.n_heads, w.head_dim), generator=g, device=device)
+
+
+def dsa_selection(w, lens, n_sel, max_sel=None, seed_key=0):
+    """A sparse-attention selection per sequence: n_sel[b] distinct positions
+    of [0, lens[b]) in a seeded random order (a top-k list has no order the
+    attention depends on), padded with -1 to max_sel entries.  Returns
+    (sel int32 [B][max_sel], n_sel int32 [B]) on the CPU."""
+    max_sel = max(n_sel) if max_sel is None else max_sel
+    sel = torch.full((len(lens), max_sel), -1, dtype=torch.int32)
+    for b, (T, n) in enumerate(zip(lens, n_sel)):
+        assert n <= T and n <= max_sel
+        g = _gen("cpu", w.seed, 404, seed_key, b)
+        sel[b, :n] = torch.randperm(T, generator=g)[:n].to(torch.int32)
+    return sel, torch.tensor(list(n_sel), dtype=torch.int32)
