@@ -131,6 +131,83 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __
     if (lse && blockIdx.y == 0 && tid == 0) lse[bh] = M + logf(s_Z);
 }
 
+// Partials with at most 64 splits (short contexts, short selections, many
+// rows): one wave per (sequence x query head, 64-channel block), four items
+// per workgroup, instead of four waves on one item.  Same arithmetic in the
+// same order as merge_kernel: lane s < n forms w_s = exp(m_s - M); Z is the
+// same lane-strided sum (one term per lane here) and butterfly; the context
+// keeps the four partial sums of the splits s = 0, 1, 2, 3 (mod 4), each in
+// ascending s, and adds them in that order -- so the bits equal merge_kernel's.
+constexpr int kSmallS = 64;
+
+__global__ __launch_bounds__(kMergeWaves * 64) void merge_small_kernel(const float* __restrict__ part_acc,
+                                                                       const float* __restrict__ part_m,
+                                                                       const float* __restrict__ part_z,
+                                                                       const int32_t* __restrict__ seq_lens,
+                                                                       int n_q_heads, int max_seq_len, int S,
+                                                                       int split_keys, int dv, int rotate,
+                                                                       int64_t n_items, float* __restrict__ out,
+                                                                       float* __restrict__ lse) {
+    __shared__ float o_rot[kMergeWaves][kMergeCh];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t item = int64_t(blockIdx.x) * kMergeWaves + wave;
+    if (item >= n_items) return;  // a whole wave; no workgroup barrier below
+    const int n_blk = dv / kMergeCh;
+    const int64_t bh = item / n_blk;
+    const int c0 = int(item % n_blk) * kMergeCh;
+    const int b = int(bh / n_q_heads);
+    const float* pa = part_acc + bh * S * dv + c0 + lane;
+
+    int T = seq_lens[b];
+    float v[kSmallS];
+#pragma unroll
+    for (int k = 0; k < kSmallS; ++k) v[k] = k < S ? pa[int64_t(k) * dv] : 0.0f;
+    const float my_m = lane < S ? part_m[bh * S + lane] : -INFINITY;
+    const float my_z = lane < S ? part_z[bh * S + lane] : 0.0f;
+
+    T = T < 0 ? 0 : (T > max_seq_len ? max_seq_len : T);
+    const int n = (T + split_keys - 1) / split_keys;
+    float* o = out + bh * dv;
+    if (n == 0) {
+        o[c0 + lane] = 0.0f;
+        if (lse && c0 == 0 && lane == 0) lse[bh] = -INFINITY;
+        return;
+    }
+    float M = lane < n ? my_m : -INFINITY;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+    const float w = lane < n ? (my_z > 0.0f ? expf(my_m - M) : 0.0f) : 0.0f;
+    float z = lane < n ? my_z * w : 0.0f;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) z += __shfl_xor(z, m, 64);
+
+    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < kSmallS; ++k) {
+        if (k < n) {
+            const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+            p[k & 3] += v[k] * wk;
+        }
+    }
+    const float orot = (((p[0] + p[1]) + p[2]) + p[3]) / z;
+    if (rotate) {
+        o_rot[wave][lane] = orot;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const float* blk = &o_rot[wave][lane & ~31];
+        const int i = lane & 31;
+        float r = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) r += (__popc(unsigned(i & j)) & 1) ? -blk[j] : blk[j];
+        o[c0 + lane] = r * inv_sqrt32();
+    } else {
+        o[c0 + lane] = orot;
+    }
+    if (lse && c0 == 0 && lane == 0) lse[bh] = M + logf(z);
+}
+
 }  // namespace
 
 hipError_t launch_rotate_q(const void* q, InType dt, float* q_rot, int n_rows, int head_dim, hipStream_t s) {
@@ -147,6 +224,17 @@ hipError_t launch_rotate_q(const void* q, InType dt, float* q_rot, int n_rows, i
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
     if (a.batch == 0) return hipSuccess;
+    // One wave per item pays off once there are enough items to fill the GPU
+    // (measured: 384 items 5.7 vs 6.0 us, 16384 items 13.7 vs 35 us; 96 items
+    // 5.9 vs 5.0 us).  Both kernels give the same bits, so the choice is free.
+    const int64_t n_items = int64_t(a.batch) * a.n_q_heads * (a.dv / kMergeCh);
+    if (a.n_splits <= kSmallS && n_items >= 256) {
+        const dim3 grid(unsigned((n_items + kMergeWaves - 1) / kMergeWaves));
+        merge_small_kernel<<<grid, dim3(kMergeWaves * 64), 0, s>>>(
+            a.part_acc, a.part_m, a.part_z, a.seq_lens, a.n_q_heads, a.max_seq_len, a.n_splits, a.split_keys, a.dv,
+            a.rotate ? 1 : 0, n_items, a.out, a.lse);
+        return hipGetLastError();
+    }
     const size_t shm = sizeof(float) * size_t(a.n_splits);
     const dim3 grid(unsigned(a.batch * a.n_q_heads), unsigned(a.dv / kMergeCh));
     merge_kernel<<<grid, dim3(kMergeWaves * 64), shm, s>>>(

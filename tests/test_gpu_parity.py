@@ -449,6 +449,37 @@ def test_mla_batch_invariance(kvq):
         assert np.array_equal(o.cpu().numpy()[0], ob[b]) and np.array_equal(l.cpu().numpy()[0], lb[b])
 
 
+@pytest.mark.parametrize("fmt", ["q4", "fp8"])
+def test_merge_few_splits_equals_merge_many(kvq, fmt):
+    """Partials of at most 64 splits over at least 256 (row, channel block)
+    items are merged one wave per item; the result is bit-identical to the
+    four-wave merge that larger split counts use.  The same partials are
+    merged once from a buffer of 100 splits per row (four-wave merge, only
+    the used splits are read) and once from a copy holding the first 64
+    (one-wave merge)."""
+    import fp8_quantized_kv_amd as kvq_mod
+    split = 512
+    if fmt == "q4":
+        w = wl.shrink(wl.RAGGED, prefill_chunk=0)
+        lens = [31000, 700, 32768, 1]  # 4 x 24 heads x 4 blocks = 384 items
+        case = Q4Case(w, lens, build_oracle=False)
+        q = kvq_mod.kvq_rotate_q(case.q)
+    else:
+        w = wl.shrink(wl.MLA_262K, n_heads=40, seq_len=0)
+        lens = [30000, 513, 0]  # 3 x 40 heads x 8 blocks = 960 items
+        case = MlaCase(w, lens, build_oracle=False)
+        q = case.q
+    big = 100 * split
+    pt = torch.zeros((len(lens), big // w.page_size), dtype=torch.int32, device="cuda")  # room for 100 splits
+    pt[:, :case.page_table.shape[1]] = case.page_table
+    pa, pm, pz = kvq_mod.kvq_decode_attn(case.cache, q, pt, case.seq_lens, big, w.sm_scale, split)
+    o1, l1 = kvq_mod.kvq_merge(case.cache, pa, pm, pz, case.seq_lens, big, split)
+    pa2, pm2, pz2 = (x[:, :, :64].contiguous() for x in (pa, pm, pz))
+    o2, l2 = kvq_mod.kvq_merge(case.cache, pa2, pm2, pz2, case.seq_lens, 64 * split, split)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 # ------------------------------------------------- fp8 latent, selected rows (DSA gather)
 
 @pytest.mark.parametrize("n_heads,n_sel,max_sel,split", [(128, [1000, 300, 0], 1024, 512), (40, [2049, 4096, 17], 4096, 2048),
