@@ -97,3 +97,30 @@ def test_mla_full_sampled_heads(kvq):
     _say(f"  max_rel_err={err.max():.2e}")
     assert err.max() < TOL
     assert np.max(np.abs(lse[:, heads] - rl)) < 1e-3 * max(1.0, np.abs(rl).max())
+
+    # Selected rows (DSA gather) of the same 262144-position cache, at the bench's
+    # splits: one sequence with 2048 and 4096 entries (split 64), and four
+    # sequences sharing the pages with their own queries and selections (split 256).
+    for n_sel, split in ((2048, 64), (4096, 64)):
+        sel, ns = wl.dsa_selection(w, [w.seq_len], [n_sel], n_sel, seed_key=9)
+        _say(f"full mla sel: n_sel={n_sel} split={split}")
+        o, lse = case.gpu_attention_sel(sel, ns, split)
+        ro, rl = case.ref_attention_sel(sel, ns)
+        err = rel_err(o, ro)
+        _say(f"  max_rel_err={err.max():.2e}")
+        assert err.max() < TOL
+        assert np.max(np.abs(lse - rl)) < 1e-3 * max(1.0, np.abs(rl).max())
+    B = 4
+    sel, ns = wl.dsa_selection(w, [w.seq_len] * B, [2048] * B, 2048, seed_key=10)
+    q = wl.mla_query(wl.shrink(w, batch=B), 1, "cuda")
+    pt = case.page_table.expand(B, -1).contiguous()
+    _say(f"full mla sel: batch {B} sharing the context, n_sel=2048 split=256")
+    pa, pm, pz = kvq.kvq_decode_attn_sel(case.cache, q, pt, sel.cuda(), ns.cuda(), w.sm_scale, 256)
+    o, lse = kvq.kvq_merge(case.cache, pa, pm, pz, ns.cuda(), 2048, 256)
+    torch.cuda.synchronize()
+    ro, rl = oracle.mla_attention_sel(case.codes_ref, case.scales_ref, q.cpu().numpy(), pt.cpu().numpy(),
+                                      sel.numpy(), ns.numpy(), w.sm_scale, w.rope_dim, w.page_size)
+    err = rel_err(o.cpu().numpy(), ro)
+    _say(f"  max_rel_err={err.max():.2e}")
+    assert err.max() < TOL
+    assert np.max(np.abs(lse.cpu().numpy() - rl)) < 1e-3 * max(1.0, np.abs(rl).max())
