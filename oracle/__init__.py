@@ -45,15 +45,16 @@ def lib():
             "kvqo_e4m3_encode": ([ctypes.c_float], ctypes.c_uint8),
             "kvqo_e4m3_decode": ([ctypes.c_uint8], _D),
             "kvqo_q4_row_bytes": ([_I], ctypes.c_size_t),
+            "kvqo_blk_row_bytes": ([_I, _I], ctypes.c_size_t),
             "kvqo_q4_encode_row": ([_P, _I, _P], _I),
-            "kvqo_q4_encode_rows": ([_P, _I64, _I, _P], _I),
-            "kvqo_q4_decode_rows": ([_P, _I64, _I, _P], None),
+            "kvqo_blk_encode_rows": ([_I, _P, _I64, _I, _P], _I),
+            "kvqo_blk_decode_rows": ([_I, _P, _I64, _I, _P], None),
             "kvqo_hadamard32_f32_rows": ([_P, _I64], None),
             "kvqo_rotate_f64": ([_P, _P, _I], None),
-            "kvqo_q4_store": ([_P, _P, _I, _I, _I, _I, _P, _P, _P, _I], _I),
-            "kvqo_q4_attention": ([_P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _D, _P, _P], _I),
-            "kvqo_q4_attention_chunked": ([_P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _D, _I, _I,
-                                           _P, _P, _P, _P, _P], _I),
+            "kvqo_blk_store": ([_I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I], _I),
+            "kvqo_blk_attention": ([_I, _P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _D, _P, _P], _I),
+            "kvqo_blk_attention_chunked": ([_I, _P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _D, _I, _I,
+                                            _P, _P, _P, _P, _P], _I),
             "kvqo_fp8_encode_part": ([_P, _I, _P, _P], None),
             "kvqo_fp8_store": ([_P, _P, _I, _I, _I64, _P, _P, _I], _I),
             "kvqo_mla_attention": ([_P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _D, _P, _P], _I),
@@ -114,10 +115,13 @@ def e4m3_decode(codes):
     return np.array([lib().kvqo_e4m3_decode(int(c)) for c in np.ravel(codes)], np.float64).reshape(np.shape(codes))
 
 
-# ---------------------------------------------------------------- 4-bit codec
+# ---------------------------------------------------------------- block codecs (4-, 6-, 8-bit)
+#
+# Every function below takes bits = 4 (the 144-byte-row format), 6 or 8: the
+# same rotated groups of 32 values and fp16 scale, with codes of that width.
 
-def q4_row_bytes(D):
-    return int(lib().kvqo_q4_row_bytes(D))
+def q4_row_bytes(D, bits=4):
+    return int(lib().kvqo_blk_row_bytes(bits, D))
 
 
 def hadamard32_f32(x):
@@ -139,27 +143,35 @@ def rotate_f64(x):
     return y.reshape(x.shape)
 
 
-def q4_encode_rows(x):
-    """x [..., D] float32 -> packed rows [..., D/2 + 2*D/32] uint8."""
+def q4_encode_rows(x, bits=4):
+    """x [..., D] float32 -> packed rows [..., row_bytes] uint8 (4 bits: D/2 + 2*D/32)."""
     x = _c(x, np.float32)
     D = x.shape[-1]
     n = x.size // D
-    out = np.empty(x.shape[:-1] + (q4_row_bytes(D),), np.uint8)
-    _check(lib().kvqo_q4_encode_rows(_ptr(x), n, D, _ptr(out)), "q4_encode_rows")
+    out = np.empty(x.shape[:-1] + (q4_row_bytes(D, bits),), np.uint8)
+    _check(lib().kvqo_blk_encode_rows(bits, _ptr(x), n, D, _ptr(out)), "blk_encode_rows")
     return out
 
 
-def q4_decode_rows(rows, D):
+def q4_decode_rows(rows, D, bits=4):
     """packed rows [..., row_bytes] -> dequantized rotated values [..., D] fp64."""
     rows = _c(rows, np.uint8)
-    n = rows.size // q4_row_bytes(D)
+    n = rows.size // q4_row_bytes(D, bits)
     out = np.empty(rows.shape[:-1] + (D,), np.float64)
-    lib().kvqo_q4_decode_rows(_ptr(rows), n, D, _ptr(out))
+    lib().kvqo_blk_decode_rows(bits, _ptr(rows), n, D, _ptr(out))
     return out
 
 
-def q4_pool_shape(num_pages, n_kv_heads, page_size, D):
-    return (num_pages, n_kv_heads, page_size, q4_row_bytes(D))
+def q4_pool_shape(num_pages, n_kv_heads, page_size, D, bits=4):
+    return (num_pages, n_kv_heads, page_size, q4_row_bytes(D, bits))
+
+
+def _bits_of_pool(pool, D):
+    rb = pool.shape[-1]
+    for bits in (4, 6, 8):
+        if q4_row_bytes(D, bits) == rb:
+            return bits
+    raise ValueError(f"row of {rb} bytes matches no block format at D={D}")
 
 
 def q4_store(k_pool, v_pool, k, v, slots, page_size):
@@ -171,13 +183,15 @@ def q4_store(k_pool, v_pool, k, v, slots, page_size):
     v = _c(v, np.float32)
     slots = _c(slots, np.int64)
     D = k.shape[-1]
-    _check(lib().kvqo_q4_store(_ptr(k_pool), _ptr(v_pool), H, D, page_size, num_pages, _ptr(k), _ptr(v),
-                               _ptr(slots), len(slots)), "q4_store")
+    bits = _bits_of_pool(k_pool, D)
+    _check(lib().kvqo_blk_store(bits, _ptr(k_pool), _ptr(v_pool), H, D, page_size, num_pages, _ptr(k), _ptr(v),
+                                _ptr(slots), len(slots)), "blk_store")
 
 
 def q4_attention(k_pool, v_pool, q, page_table, seq_lens, sm_scale, chunk=None, n_chunks=None,
                  return_partials=False):
-    """fp64 decode attention over the paged 4-bit cache.
+    """fp64 decode attention over a paged block-format cache (the format is
+    read off the pools' row size).
 
     q: [B][H_q][D] float32 (unrotated).  Returns (o [B][H_q][D], lse [B][H_q]),
     plus (acc, m, z) chunk partials when chunk is given and return_partials.
@@ -185,24 +199,25 @@ def q4_attention(k_pool, v_pool, q, page_table, seq_lens, sm_scale, chunk=None, 
     num_pages, H_kv, ps, rb = k_pool.shape
     q = _c(q, np.float32)
     B, H_q, D = q.shape
+    bits = _bits_of_pool(k_pool, D)
     pt = _c(page_table, np.int32)
     sl = _c(seq_lens, np.int32)
     out = np.empty((B, H_q, D), np.float64)
     lse = np.empty((B, H_q), np.float64)
     if chunk is None:
-        _check(lib().kvqo_q4_attention(_ptr(k_pool), _ptr(v_pool), H_kv, D, ps, num_pages, _ptr(q), H_q,
-                                       _ptr(pt), pt.shape[1], _ptr(sl), B, float(sm_scale), _ptr(out),
-                                       _ptr(lse)), "q4_attention")
+        _check(lib().kvqo_blk_attention(bits, _ptr(k_pool), _ptr(v_pool), H_kv, D, ps, num_pages, _ptr(q), H_q,
+                                        _ptr(pt), pt.shape[1], _ptr(sl), B, float(sm_scale), _ptr(out),
+                                        _ptr(lse)), "blk_attention")
         return out, lse
     if n_chunks is None:
         n_chunks = max(1, -(-int(sl.max()) // chunk)) if B else 1
     pa = np.empty((B, H_q, n_chunks, D), np.float64) if return_partials else None
     pm = np.empty((B, H_q, n_chunks), np.float64) if return_partials else None
     pz = np.empty((B, H_q, n_chunks), np.float64) if return_partials else None
-    _check(lib().kvqo_q4_attention_chunked(_ptr(k_pool), _ptr(v_pool), H_kv, D, ps, num_pages, _ptr(q), H_q,
-                                           _ptr(pt), pt.shape[1], _ptr(sl), B, float(sm_scale), chunk, n_chunks,
-                                           _ptr(pa), _ptr(pm), _ptr(pz), _ptr(out), _ptr(lse)),
-           "q4_attention_chunked")
+    _check(lib().kvqo_blk_attention_chunked(bits, _ptr(k_pool), _ptr(v_pool), H_kv, D, ps, num_pages, _ptr(q),
+                                            H_q, _ptr(pt), pt.shape[1], _ptr(sl), B, float(sm_scale), chunk,
+                                            n_chunks, _ptr(pa), _ptr(pm), _ptr(pz), _ptr(out), _ptr(lse)),
+           "blk_attention_chunked")
     if return_partials:
         return out, lse, (pa, pm, pz)
     return out, lse

@@ -158,18 +158,37 @@ void kvqo_rotate_f64(const double* x, double* y, int n) {
 /* 4-bit Hadamard-32 row codec                                         */
 /* ------------------------------------------------------------------ */
 
-size_t kvqo_q4_row_bytes(int D) { return (size_t)(D / 2 + 2 * (D / 32)); }
+/* Block formats of the same skeleton (rotated groups of 32 values, one fp16
+ * scale per group, codes of `bits` bits): 4 (the format above), 6 and 8.
+ * [FT] PR description: the q4_0 layout sits beside q8_0 (1.0625 bytes per
+ * element: 32 one-byte codes + one fp16 scale) in one spec, and a further
+ * scheme is a one-line change; test-fix commit: the exact-scale amax is 8.0
+ * for q4_0 and 31.0 for q6_0 (q6_0 divides by its largest magnitude 31).
+ * Readings (the pages give neither the q8 divisor nor any 6-bit layout):
+ *   divisor (largest magnitude): 8 (4-bit), 31 (6-bit), 127 (8-bit, as q8_0);
+ *   codes clamp to the signed range [-2^(bits-1), 2^(bits-1) - 1];
+ *   8-bit: code i is byte i of the group (two's complement);
+ *   6-bit: 16 bytes of low nibbles laid out as the 4-bit codes, then 8 bytes
+ *   of the high two bits, code 4j+i in bits 2i..2i+1 of byte j;
+ *   a row is the codes of all groups, then the fp16 scales. */
+static int kvqo_blk_group_bytes(int bits) { return bits == 4 ? 16 : (bits == 6 ? 24 : 32); }
+static float kvqo_blk_divisor(int bits) { return bits == 4 ? 8.0f : (bits == 6 ? 31.0f : 127.0f); }
 
-/* Encode one row of D values (D % 32 == 0) into D/2 + 2*D/32 bytes.
+size_t kvqo_blk_row_bytes(int bits, int D) { return (size_t)(kvqo_blk_group_bytes(bits) * (D / 32) + 2 * (D / 32)); }
+
+size_t kvqo_q4_row_bytes(int D) { return kvqo_blk_row_bytes(4, D); }
+
+/* Encode one row of D values (D % 32 == 0).
  * [TF] "What it is": rotated groups of 32, 4-bit codes plus an fp16 scale;
  * [FT] PR description: 32 values -> 16 bytes + one fp16 scale;
- * [FT] test-fix commit: scale = amax/8.
+ * [FT] test-fix commit: scale = amax/8 (4-bit), amax/31 (6-bit).
  * Returns KVQO_EDOMAIN for a non-finite value or a scale beyond fp16 range. */
-int kvqo_q4_encode_row(const float* x, int D, uint8_t* row) {
+int kvqo_blk_encode_row(int bits, const float* x, int D, uint8_t* row) {
     if (D <= 0 || D % 32) return KVQO_EARG;
-    const int G = D / 32;
-    uint8_t* codes = row;
-    uint8_t* scales = row + D / 2;
+    if (bits != 4 && bits != 6 && bits != 8) return KVQO_EARG;
+    const int G = D / 32, GB = kvqo_blk_group_bytes(bits);
+    const float qmax = (float)((1 << (bits - 1)) - 1), qmin = -(float)(1 << (bits - 1));
+    uint8_t* scales = row + GB * G;
     for (int g = 0; g < G; ++g) {
         float t[32];
         for (int i = 0; i < 32; ++i) {
@@ -182,7 +201,7 @@ int kvqo_q4_encode_row(const float* x, int D, uint8_t* row) {
             float a = fabsf(t[i]);
             if (a > amax) amax = a;
         }
-        uint16_t s16 = kvqo_f32_to_f16(amax / 8.0f);
+        uint16_t s16 = kvqo_f32_to_f16(amax / kvqo_blk_divisor(bits));
         if ((s16 & 0x7C00u) == 0x7C00u) return KVQO_EDOMAIN;
         float s = kvqo_f16_to_f32(s16);
         int q[32];
@@ -190,35 +209,54 @@ int kvqo_q4_encode_row(const float* x, int D, uint8_t* row) {
             if (s == 0.0f) { q[i] = 0; continue; }
             float r = t[i] / s;           /* one correctly rounded fp32 divide */
             float n = nearbyintf(r);      /* half to even */
-            if (n > 7.0f) n = 7.0f;
-            if (n < -8.0f) n = -8.0f;
+            if (n > qmax) n = qmax;
+            if (n < qmin) n = qmin;
             q[i] = (int)n;
         }
-        for (int k = 0; k < 16; ++k)
-            codes[16 * g + k] = (uint8_t)((q[2 * k] & 0xF) | ((q[2 * k + 1] & 0xF) << 4));
+        uint8_t* c = row + GB * g;
+        if (bits == 8) {
+            for (int i = 0; i < 32; ++i) c[i] = (uint8_t)(q[i] & 0xFF);
+        } else {
+            for (int k = 0; k < 16; ++k) c[k] = (uint8_t)((q[2 * k] & 0xF) | ((q[2 * k + 1] & 0xF) << 4));
+            if (bits == 6)
+                for (int j = 0; j < 8; ++j)
+                    c[16 + j] = (uint8_t)(((q[4 * j] >> 4) & 3) | (((q[4 * j + 1] >> 4) & 3) << 2) |
+                                          (((q[4 * j + 2] >> 4) & 3) << 4) | (((q[4 * j + 3] >> 4) & 3) << 6));
+        }
         scales[2 * g] = (uint8_t)(s16 & 0xFF);
         scales[2 * g + 1] = (uint8_t)(s16 >> 8);
     }
     return KVQO_OK;
 }
 
-/* Signed value of a two's-complement nibble. */
-static int kvqo_nibble(unsigned v) { return (v & 8u) ? (int)v - 16 : (int)v; }
+int kvqo_q4_encode_row(const float* x, int D, uint8_t* row) { return kvqo_blk_encode_row(4, x, D, row); }
+
+/* Signed value of an n-bit two's-complement field v (0 <= v < 2^n). */
+static int kvqo_signed(unsigned v, int n) { return (v & (1u << (n - 1))) ? (int)v - (1 << n) : (int)v; }
 
 /* Dequantized row in the rotated domain: v_i = scale_g * code_i, exact in fp64. */
-void kvqo_q4_decode_row(const uint8_t* row, int D, double* out) {
-    const uint8_t* codes = row;
-    const uint8_t* scales = row + D / 2;
-    for (int g = 0; g < D / 32; ++g) {
+void kvqo_blk_decode_row(int bits, const uint8_t* row, int D, double* out) {
+    const int G = D / 32, GB = kvqo_blk_group_bytes(bits);
+    const uint8_t* scales = row + GB * G;
+    for (int g = 0; g < G; ++g) {
         uint16_t s16 = (uint16_t)(scales[2 * g] | (scales[2 * g + 1] << 8));
         double s = (double)kvqo_f16_to_f32(s16);
-        for (int k = 0; k < 16; ++k) {
-            uint8_t b = codes[16 * g + k];
-            out[32 * g + 2 * k] = s * kvqo_nibble(b & 0xFu);
-            out[32 * g + 2 * k + 1] = s * kvqo_nibble(b >> 4);
+        const uint8_t* c = row + GB * g;
+        for (int i = 0; i < 32; ++i) {
+            int code;
+            if (bits == 8) {
+                code = kvqo_signed(c[i], 8);
+            } else {
+                unsigned lo = (c[i / 2] >> (4 * (i & 1))) & 0xFu;
+                if (bits == 4) code = kvqo_signed(lo, 4);
+                else code = kvqo_signed(lo | (((c[16 + i / 4] >> (2 * (i & 3))) & 3u) << 4), 6);
+            }
+            out[32 * g + i] = s * code;
         }
     }
 }
+
+void kvqo_q4_decode_row(const uint8_t* row, int D, double* out) { kvqo_blk_decode_row(4, row, D, out); }
 
 /* Byte offset of the row of (slot, kv head) in a pool laid out as
  * [num_pages][n_kv_heads][page_size][row_bytes]. */
@@ -227,11 +265,11 @@ static size_t kvqo_row_offset(int64_t slot, int head, int n_kv_heads, int page_s
     return (size_t)(((page * n_kv_heads + head) * page_size + off) * (int64_t)row_bytes);
 }
 
-/* Write K and V rows of n_tokens tokens into paged 4-bit pools.
+/* Write K and V rows of n_tokens tokens into paged pools of a block format.
  * k, v: [n_tokens][n_kv_heads][D] fp32.  slot < 0 skips the token. */
-int kvqo_q4_store(uint8_t* k_pool, uint8_t* v_pool, int n_kv_heads, int D, int page_size, int num_pages,
-                  const float* k, const float* v, const int64_t* slots, int n_tokens) {
-    const size_t rb = kvqo_q4_row_bytes(D);
+int kvqo_blk_store(int bits, uint8_t* k_pool, uint8_t* v_pool, int n_kv_heads, int D, int page_size,
+                   int num_pages, const float* k, const float* v, const int64_t* slots, int n_tokens) {
+    const size_t rb = kvqo_blk_row_bytes(bits, D);
     const int64_t n_slots = (int64_t)num_pages * page_size;
     int err = KVQO_OK;
     for (int t = 0; t < n_tokens; ++t)
@@ -242,8 +280,8 @@ int kvqo_q4_store(uint8_t* k_pool, uint8_t* v_pool, int n_kv_heads, int D, int p
         for (int h = 0; h < n_kv_heads; ++h) {
             size_t src = ((size_t)t * n_kv_heads + h) * D;
             size_t dst = kvqo_row_offset(slots[t], h, n_kv_heads, page_size, rb);
-            int e1 = kvqo_q4_encode_row(k + src, D, k_pool + dst);
-            int e2 = kvqo_q4_encode_row(v + src, D, v_pool + dst);
+            int e1 = kvqo_blk_encode_row(bits, k + src, D, k_pool + dst);
+            int e2 = kvqo_blk_encode_row(bits, v + src, D, v_pool + dst);
             if (e1 < err) err = e1;
             if (e2 < err) err = e2;
         }
@@ -251,8 +289,13 @@ int kvqo_q4_store(uint8_t* k_pool, uint8_t* v_pool, int n_kv_heads, int D, int p
     return err;
 }
 
+int kvqo_q4_store(uint8_t* k_pool, uint8_t* v_pool, int n_kv_heads, int D, int page_size, int num_pages,
+                  const float* k, const float* v, const int64_t* slots, int n_tokens) {
+    return kvqo_blk_store(4, k_pool, v_pool, n_kv_heads, D, page_size, num_pages, k, v, slots, n_tokens);
+}
+
 /* ------------------------------------------------------------------ */
-/* Q4 decode attention                                                 */
+/* Decode attention over a block-format cache                          */
 /* ------------------------------------------------------------------ */
 
 /* Slot of logical position j of sequence b (16-token or other pages). */
@@ -269,12 +312,12 @@ static int64_t kvqo_slot(const int32_t* page_table, int max_pages, int b, int64_
  *   lse = max_j s_j + log(sum_j exp(s_j - max))
  * T = 0 gives o = 0 and lse = -inf.  q: [B][n_q_heads][D] fp32, unrotated.
  * out: [B][n_q_heads][D], lse: [B][n_q_heads] (may be NULL). */
-int kvqo_q4_attention(const uint8_t* k_pool, const uint8_t* v_pool, int n_kv_heads, int D, int page_size,
-                      int num_pages, const float* q, int n_q_heads, const int32_t* page_table, int max_pages,
-                      const int32_t* seq_lens, int B, double sm_scale, double* out, double* lse) {
+int kvqo_blk_attention(int bits, const uint8_t* k_pool, const uint8_t* v_pool, int n_kv_heads, int D,
+                       int page_size, int num_pages, const float* q, int n_q_heads, const int32_t* page_table,
+                       int max_pages, const int32_t* seq_lens, int B, double sm_scale, double* out, double* lse) {
     if (n_q_heads % n_kv_heads) return KVQO_EARG;
     const int G = n_q_heads / n_kv_heads;
-    const size_t rb = kvqo_q4_row_bytes(D);
+    const size_t rb = kvqo_blk_row_bytes(bits, D);
     for (int b = 0; b < B; ++b)
         if (seq_lens[b] < 0 || (int64_t)seq_lens[b] > (int64_t)max_pages * page_size) return KVQO_ERANGE;
     int err = KVQO_OK;
@@ -295,7 +338,7 @@ int kvqo_q4_attention(const uint8_t* k_pool, const uint8_t* v_pool, int n_kv_hea
         for (int64_t j = 0; j < T; ++j) {
             int64_t slot = kvqo_slot(page_table, max_pages, b, j, page_size);
             if (slot < 0 || slot >= (int64_t)num_pages * page_size) { st = KVQO_ERANGE; break; }
-            kvqo_q4_decode_row(k_pool + kvqo_row_offset(slot, g, n_kv_heads, page_size, rb), D, row);
+            kvqo_blk_decode_row(bits, k_pool + kvqo_row_offset(slot, g, n_kv_heads, page_size, rb), D, row);
             double dot = 0.0;
             for (int i = 0; i < D; ++i) dot += qr[i] * row[i];
             s[j] = sm_scale * dot;
@@ -307,7 +350,7 @@ int kvqo_q4_attention(const uint8_t* k_pool, const uint8_t* v_pool, int n_kv_hea
                 int64_t slot = kvqo_slot(page_table, max_pages, b, j, page_size);
                 double w = exp(s[j] - m);
                 z += w;
-                kvqo_q4_decode_row(v_pool + kvqo_row_offset(slot, g, n_kv_heads, page_size, rb), D, row);
+                kvqo_blk_decode_row(bits, v_pool + kvqo_row_offset(slot, g, n_kv_heads, page_size, rb), D, row);
                 for (int i = 0; i < D; ++i) orot[i] += w * row[i];
             }
         }
@@ -324,6 +367,13 @@ int kvqo_q4_attention(const uint8_t* k_pool, const uint8_t* v_pool, int n_kv_hea
     return err;
 }
 
+int kvqo_q4_attention(const uint8_t* k_pool, const uint8_t* v_pool, int n_kv_heads, int D, int page_size,
+                      int num_pages, const float* q, int n_q_heads, const int32_t* page_table, int max_pages,
+                      const int32_t* seq_lens, int B, double sm_scale, double* out, double* lse) {
+    return kvqo_blk_attention(4, k_pool, v_pool, n_kv_heads, D, page_size, num_pages, q, n_q_heads, page_table,
+                              max_pages, seq_lens, B, sm_scale, out, lse);
+}
+
 /* The same attention in the method's own structure ([TF] "What it is":
  * chunks at absolute multiples of `chunk` keys, the last partial chunk being
  * the row's tail, merged in order; [CO] split-T commit: each chunk yields
@@ -334,14 +384,14 @@ int kvqo_q4_attention(const uint8_t* k_pool, const uint8_t* v_pool, int n_kv_hea
  *   M = max m_c, Z = sum z_c exp(m_c - M), o = H (sum acc_c exp(m_c - M)) / Z.
  * part_acc [B][n_q_heads][n_chunks][D], part_m/part_z [B][n_q_heads][n_chunks]
  * may be NULL; n_chunks = ceil(max(seq_lens) / chunk) when given. */
-int kvqo_q4_attention_chunked(const uint8_t* k_pool, const uint8_t* v_pool, int n_kv_heads, int D, int page_size,
-                              int num_pages, const float* q, int n_q_heads, const int32_t* page_table,
-                              int max_pages, const int32_t* seq_lens, int B, double sm_scale, int chunk,
-                              int n_chunks, double* part_acc, double* part_m, double* part_z, double* out,
-                              double* lse) {
+int kvqo_blk_attention_chunked(int bits, const uint8_t* k_pool, const uint8_t* v_pool, int n_kv_heads, int D,
+                               int page_size, int num_pages, const float* q, int n_q_heads,
+                               const int32_t* page_table, int max_pages, const int32_t* seq_lens, int B,
+                               double sm_scale, int chunk, int n_chunks, double* part_acc, double* part_m,
+                               double* part_z, double* out, double* lse) {
     if (n_q_heads % n_kv_heads || chunk <= 0) return KVQO_EARG;
     const int G = n_q_heads / n_kv_heads;
-    const size_t rb = kvqo_q4_row_bytes(D);
+    const size_t rb = kvqo_blk_row_bytes(bits, D);
     for (int b = 0; b < B; ++b) {
         if (seq_lens[b] < 0 || (int64_t)seq_lens[b] > (int64_t)max_pages * page_size) return KVQO_ERANGE;
         if (((int64_t)seq_lens[b] + chunk - 1) / chunk > n_chunks) return KVQO_EARG;
@@ -369,7 +419,7 @@ int kvqo_q4_attention_chunked(const uint8_t* k_pool, const uint8_t* v_pool, int 
             for (int64_t j = j0; j < j1; ++j) {
                 int64_t slot = kvqo_slot(page_table, max_pages, b, j, page_size);
                 if (slot < 0 || slot >= (int64_t)num_pages * page_size) { st = KVQO_ERANGE; j1 = j; break; }
-                kvqo_q4_decode_row(k_pool + kvqo_row_offset(slot, g, n_kv_heads, page_size, rb), D, row);
+                kvqo_blk_decode_row(bits, k_pool + kvqo_row_offset(slot, g, n_kv_heads, page_size, rb), D, row);
                 double dot = 0.0;
                 for (int i = 0; i < D; ++i) dot += qr[i] * row[i];
                 s[j - j0] = sm_scale * dot;
@@ -379,7 +429,7 @@ int kvqo_q4_attention_chunked(const uint8_t* k_pool, const uint8_t* v_pool, int 
                 int64_t slot = kvqo_slot(page_table, max_pages, b, j, page_size);
                 double w = exp(s[j - j0] - m);
                 z += w;
-                kvqo_q4_decode_row(v_pool + kvqo_row_offset(slot, g, n_kv_heads, page_size, rb), D, row);
+                kvqo_blk_decode_row(bits, v_pool + kvqo_row_offset(slot, g, n_kv_heads, page_size, rb), D, row);
                 for (int i = 0; i < D; ++i) a[i] += w * row[i];
             }
             cm[c] = m;
@@ -409,6 +459,16 @@ int kvqo_q4_attention_chunked(const uint8_t* k_pool, const uint8_t* v_pool, int 
         free(qd); free(qr); free(row); free(acc); free(cm); free(cz); free(s); free(orot);
     }
     return err;
+}
+
+int kvqo_q4_attention_chunked(const uint8_t* k_pool, const uint8_t* v_pool, int n_kv_heads, int D, int page_size,
+                              int num_pages, const float* q, int n_q_heads, const int32_t* page_table,
+                              int max_pages, const int32_t* seq_lens, int B, double sm_scale, int chunk,
+                              int n_chunks, double* part_acc, double* part_m, double* part_z, double* out,
+                              double* lse) {
+    return kvqo_blk_attention_chunked(4, k_pool, v_pool, n_kv_heads, D, page_size, num_pages, q, n_q_heads,
+                                      page_table, max_pages, seq_lens, B, sm_scale, chunk, n_chunks, part_acc,
+                                      part_m, part_z, out, lse);
 }
 
 /* ------------------------------------------------------------------ */
@@ -683,21 +743,21 @@ void kvqo_e4m3_encode_array(const float* x, uint8_t* y, int64_t n) {
 }
 
 /* Encode/decode many rows at once: x [n_rows][D] -> rows [n_rows][row_bytes]. */
-int kvqo_q4_encode_rows(const float* x, int64_t n_rows, int D, uint8_t* rows) {
-    const size_t rb = kvqo_q4_row_bytes(D);
+int kvqo_blk_encode_rows(int bits, const float* x, int64_t n_rows, int D, uint8_t* rows) {
+    const size_t rb = kvqo_blk_row_bytes(bits, D);
     int err = KVQO_OK;
 #pragma omp parallel for schedule(static) reduction(min : err)
     for (int64_t r = 0; r < n_rows; ++r) {
-        int e = kvqo_q4_encode_row(x + (size_t)r * D, D, rows + (size_t)r * rb);
+        int e = kvqo_blk_encode_row(bits, x + (size_t)r * D, D, rows + (size_t)r * rb);
         if (e < err) err = e;
     }
     return err;
 }
 
-void kvqo_q4_decode_rows(const uint8_t* rows, int64_t n_rows, int D, double* out) {
-    const size_t rb = kvqo_q4_row_bytes(D);
+void kvqo_blk_decode_rows(int bits, const uint8_t* rows, int64_t n_rows, int D, double* out) {
+    const size_t rb = kvqo_blk_row_bytes(bits, D);
 #pragma omp parallel for schedule(static)
-    for (int64_t r = 0; r < n_rows; ++r) kvqo_q4_decode_row(rows + (size_t)r * rb, D, out + (size_t)r * D);
+    for (int64_t r = 0; r < n_rows; ++r) kvqo_blk_decode_row(bits, rows + (size_t)r * rb, D, out + (size_t)r * D);
 }
 
 void kvqo_hadamard32_f32_rows(float* x, int64_t n_groups) {
