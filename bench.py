@@ -128,8 +128,9 @@ class Q4Bench(_Bench):
         self.caches, self.q, self.k_new, self.v_new = [], [], [], []
         chunk = 32768
         slots_all = wl.slots_for(lay.page_table[0], np.arange(T), w.page_size).to(device)
+        fmt = {4: kvq.FMT_Q4_H32, 6: kvq.FMT_Q6_H32, 8: kvq.FMT_Q8_H32}[w.bits]
         for layer in range(w.n_layers):
-            c = kvq.Q4Cache(lay.num_pages, w.n_kv_heads, w.head_dim, w.page_size, device)
+            c = kvq.Q4Cache(lay.num_pages, w.n_kv_heads, w.head_dim, w.page_size, device, fmt=fmt)
             q = wl.q4_query(w, layer, device)
             for t0 in range(0, T, chunk):
                 n = min(chunk, T - t0)
@@ -631,7 +632,8 @@ def main():
     rec["roofline"]["frac_of_read_ceiling"] = round(m["decode_gbs"] / ceil["non_temporal"], 4)
     if not args.no_extras:
         extras = {}
-        for name, cls in (("gqa_q4_32k", Q4Bench), ("ragged_q4_b16", RaggedBench), ("mla_fp8_262k", MlaBench)):
+        for name, cls in (("gqa_q4_32k", Q4Bench), ("gqa_q8_32k", Q4Bench), ("gqa_q6_32k", Q4Bench),
+                          ("ragged_q4_b16", RaggedBench), ("mla_fp8_262k", MlaBench)):
             wx = wl.WORKLOADS[name]
             _log(f"bench: side measurement {name}")
             bx = cls(wx)

@@ -27,6 +27,9 @@ KVQ_ERR_UNSUPPORTED = -2
 KVQ_ERR_LAUNCH = -3
 
 FMT_Q4_H32 = 1
+FMT_Q8_H32 = 3
+FMT_Q6_H32 = 4
+H32_FORMATS = (FMT_Q4_H32, FMT_Q8_H32, FMT_Q6_H32)
 FMT_FP8_E4M3_ROW = 2
 
 DT_F32, DT_BF16, DT_F16 = 0, 1, 2
@@ -110,12 +113,14 @@ def kvq_num_splits(max_seq_len, split_keys):
 
 
 class Q4Cache:
-    """Paged 4-bit Hadamard-32 K and V pools: [num_pages][H_kv][page_size][row_bytes] uint8."""
+    """Paged Hadamard-32 K and V pools: [num_pages][H_kv][page_size][row_bytes] uint8 -- the
+    4-bit format by default, or fmt=FMT_Q8_H32 / FMT_Q6_H32."""
 
-    fmt = FMT_Q4_H32
-
-    def __init__(self, num_pages, num_kv_heads, head_dim, page_size=16, device="cuda"):
-        rb = kvq_row_bytes(FMT_Q4_H32, head_dim)
+    def __init__(self, num_pages, num_kv_heads, head_dim, page_size=16, device="cuda", fmt=FMT_Q4_H32):
+        if fmt not in H32_FORMATS:
+            raise ValueError(f"not a Hadamard-32 format: {fmt}")
+        self.fmt = fmt
+        rb = kvq_row_bytes(fmt, head_dim)
         if rb == 0:
             raise ValueError(f"head_dim {head_dim} is not a multiple of 32")
         shape = (num_pages, num_kv_heads, page_size, rb)
@@ -124,7 +129,7 @@ class Q4Cache:
         self.num_kv_heads, self.head_dim, self.page_size, self.num_pages = num_kv_heads, head_dim, page_size, num_pages
         self.rope_dim = 0
         self.dv = head_dim
-        self.desc = KvqCacheDesc(FMT_Q4_H32, num_kv_heads, head_dim, 0, page_size, num_pages,
+        self.desc = KvqCacheDesc(fmt, num_kv_heads, head_dim, 0, page_size, num_pages,
                                  self.k_pool.data_ptr(), self.v_pool.data_ptr(), None)
 
     @property
@@ -167,7 +172,7 @@ def kvq_store(cache, k, v, slot_mapping):
     dt = _DTYPES.get(k.dtype)
     if dt is None:
         raise ValueError(f"unsupported dtype {k.dtype}")
-    if cache.fmt == FMT_Q4_H32:
+    if cache.fmt in H32_FORMATS:
         shape = (n, cache.num_kv_heads, cache.head_dim)
         kp = _dev(k, "k", shape=shape)
         vp = _dev(v, "v", dtype=k.dtype, shape=shape)
@@ -198,8 +203,8 @@ def kvq_rotate_q(q, out=None):
 def kvq_store_rotate_q(cache, k, v, slot_mapping, q, out=None):
     """kvq_store(cache, k, v, slot_mapping) and kvq_rotate_q(q) in one launch (4-bit cache only);
     returns the rotated query (f32, q's shape)."""
-    if cache.fmt != FMT_Q4_H32:
-        raise ValueError("kvq_store_rotate_q takes a 4-bit cache")
+    if cache.fmt not in H32_FORMATS:
+        raise ValueError("kvq_store_rotate_q takes a Hadamard-32 cache")
     n = int(slot_mapping.shape[0])
     kdt, qdt = _DTYPES.get(k.dtype), _DTYPES.get(q.dtype)
     if kdt is None or qdt is None:
@@ -295,7 +300,7 @@ def kvq_merge(cache, part_acc, part_m, part_z, seq_lens, max_seq_len, split_keys
     op = _dev(out, "out", dtype=torch.float32, shape=(B, Hq, Dv))
     lp = _dev(lse, "lse", dtype=torch.float32, shape=(B, Hq)) if lse is not None else None
     _check(lib.kvq_merge(ctypes.byref(cache.desc), pa, pm, pz, slp, B, Hq, int(max_seq_len), int(split_keys),
-                         1 if cache.fmt == FMT_Q4_H32 else 0, op, lp, _stream(part_acc)), "kvq_merge")
+                         1 if cache.fmt in H32_FORMATS else 0, op, lp, _stream(part_acc)), "kvq_merge")
     return out, lse
 
 
@@ -318,7 +323,7 @@ def decode_step(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_key
     new_kv = (k, v, slot_mapping) stores those rows first (for the 4-bit cache in the same launch as the
     query rotation, kvq_store_rotate_q; v is None for the fp8 cache)."""
     q_rot = None if bufs is None else bufs.get("q_rot")
-    if cache.fmt == FMT_Q4_H32:
+    if cache.fmt in H32_FORMATS:
         if new_kv is not None:
             q = kvq_store_rotate_q(cache, *new_kv, q, out=q_rot)
         else:

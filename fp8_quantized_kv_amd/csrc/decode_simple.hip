@@ -35,6 +35,17 @@ __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? l
 // Signed value of nibble `e` (0..7) of a code word.
 __device__ __forceinline__ float nibble(uint32_t w, int e) { return float(int32_t(w << (28 - 4 * e)) >> 28); }
 
+// Code c of a 6- or 8-bit row (the layouts of blk_group_bytes).
+template <int BITS>
+__device__ __forceinline__ float blk_code(const uint8_t* row, int c) {
+    const uint8_t* grp = row + (c >> 5) * blk_group_bytes(BITS);
+    const int i = c & 31;
+    if (BITS == 8) return float(int8_t(grp[i]));
+    const uint32_t lo = (uint32_t(grp[i >> 1]) >> (4 * (i & 1))) & 0xFu;
+    const uint32_t hi = (uint32_t(grp[16 + (i >> 2)]) >> (2 * (i & 3))) & 3u;
+    return float(int32_t((lo | (hi << 4)) << 26) >> 26);
+}
+
 // ---------------------------------------------------------------- 4-bit
 //
 // Workgroup (split s, KV head g, sequence b) serves the G query heads of g.
@@ -42,11 +53,13 @@ __device__ __forceinline__ float nibble(uint32_t w, int e) { return float(int32_
 // channels for all G heads; the four quarters are summed in LDS; one wave per
 // head runs the online softmax over the tile's 64 keys; then each thread
 // accumulates its channel(s) of p * v for all heads.
-template <int D>
+// (BITS = 6, 8: the same kernel over the 6- and 8-bit block formats.)
+template <int D, int BITS>
 __global__ __launch_bounds__(kThreads) void decode_q4_simple(const uint8_t* __restrict__ k_pool,
                                                              const uint8_t* __restrict__ v_pool, int H,
                                                              int page_size, int num_pages, DecodeArgs a) {
-    constexpr int RB = q4_row_bytes(D);
+    constexpr int RB = blk_row_bytes(BITS, D);
+    constexpr int SCALE_OFF = (D / 32) * blk_group_bytes(BITS);  // byte offset of the fp16 scales
     constexpr int RW = RB / 4;
     constexpr int CQ = D / 4;
     constexpr int CPT = (D + kThreads - 1) / kThreads;
@@ -108,13 +121,18 @@ __global__ __launch_bounds__(kThreads) void decode_q4_simple(const uint8_t* __re
             for (int h = 0; h < kMaxG; ++h) d[h] = 0.0f;
             if (kk < n) {
                 for (int c0 = qq * CQ; c0 < (qq + 1) * CQ; c0 += 8) {
-                    const uint32_t w = kt[kk * RW + c0 / 8];
+                    const uint8_t* krow = reinterpret_cast<const uint8_t*>(kt + kk * RW);
                     const int grp = c0 / 32;
-                    const uint32_t sw = kt[kk * RW + D / 8 + grp / 2];
-                    const float sc = __half2float(__ushort_as_half(uint16_t(sw >> (16 * (grp & 1)))));
+                    const float sc = __half2float(__ushort_as_half(reinterpret_cast<const uint16_t*>(krow + SCALE_OFF)[grp]));
                     float v8[8];
+                    if constexpr (BITS == 4) {
+                        const uint32_t w = kt[kk * RW + c0 / 8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v8[e] = nibble(w, e) * sc;
+                        for (int e = 0; e < 8; ++e) v8[e] = nibble(w, e) * sc;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v8[e] = blk_code<BITS>(krow, c0 + e) * sc;
+                    }
 #pragma unroll
                     for (int h = 0; h < kMaxG; ++h) {
                         if (h < G) {
@@ -157,10 +175,11 @@ __global__ __launch_bounds__(kThreads) void decode_q4_simple(const uint8_t* __re
                     if (h < G) acc[ci][h] *= alpha_s[h];
                 const int grp = c / 32;
                 for (int kk = 0; kk < n; ++kk) {
-                    const uint32_t w = vt[kk * RW + c / 8];
-                    const uint32_t sw = vt[kk * RW + D / 8 + grp / 2];
-                    const float sc = __half2float(__ushort_as_half(uint16_t(sw >> (16 * (grp & 1)))));
-                    const float vv = nibble(w, c & 7) * sc;
+                    const uint8_t* vrow = reinterpret_cast<const uint8_t*>(vt + kk * RW);
+                    const float sc = __half2float(__ushort_as_half(reinterpret_cast<const uint16_t*>(vrow + SCALE_OFF)[grp]));
+                    float vv;
+                    if constexpr (BITS == 4) vv = nibble(vt[kk * RW + c / 8], c & 7) * sc;
+                    else vv = blk_code<BITS>(vrow, c) * sc;
 #pragma unroll
                     for (int h = 0; h < kMaxG; ++h)
                         if (h < G) acc[ci][h] = fmaf(p[h][kk], vv, acc[ci][h]);
@@ -357,16 +376,24 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_simple(const uint8_t* __r
 
 }  // namespace
 
-hipError_t launch_decode_q4_simple(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s) {
+template <int BITS>
+hipError_t launch_blk_simple(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s) {
     const dim3 grid(unsigned(a.n_splits), unsigned(pool.n_kv_heads), unsigned(a.batch)), block(kThreads);
+    const int H = pool.n_kv_heads, P = pool.page_size, N = pool.num_pages;
     switch (pool.head_dim) {
-        case 64: decode_q4_simple<64><<<grid, block, 0, s>>>(pool.k, pool.v, pool.n_kv_heads, pool.page_size, pool.num_pages, a); break;
-        case 128: decode_q4_simple<128><<<grid, block, 0, s>>>(pool.k, pool.v, pool.n_kv_heads, pool.page_size, pool.num_pages, a); break;
-        case 256: decode_q4_simple<256><<<grid, block, 0, s>>>(pool.k, pool.v, pool.n_kv_heads, pool.page_size, pool.num_pages, a); break;
-        case 512: decode_q4_simple<512><<<grid, block, 0, s>>>(pool.k, pool.v, pool.n_kv_heads, pool.page_size, pool.num_pages, a); break;
+        case 64: decode_q4_simple<64, BITS><<<grid, block, 0, s>>>(pool.k, pool.v, H, P, N, a); break;
+        case 128: decode_q4_simple<128, BITS><<<grid, block, 0, s>>>(pool.k, pool.v, H, P, N, a); break;
+        case 256: decode_q4_simple<256, BITS><<<grid, block, 0, s>>>(pool.k, pool.v, H, P, N, a); break;
+        case 512: decode_q4_simple<512, BITS><<<grid, block, 0, s>>>(pool.k, pool.v, H, P, N, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_decode_q4_simple(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s) {
+    if (pool.bits == 8) return launch_blk_simple<8>(pool, a, s);
+    if (pool.bits == 6) return launch_blk_simple<6>(pool, a, s);
+    return launch_blk_simple<4>(pool, a, s);
 }
 
 hipError_t launch_decode_fp8_simple(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s) {

@@ -14,6 +14,14 @@ enum class InType : int { F32 = 0, BF16 = 1, F16 = 2 };
 // Rows of the 4-bit format: D/2 code bytes then D/32 fp16 scales.
 __host__ __device__ constexpr int q4_row_bytes(int D) { return D / 2 + 2 * (D / 32); }
 
+// Block formats of the same skeleton with codes of BITS = 4, 6 or 8 bits:
+// per 32-value group 16, 24 or 32 code bytes (6 bits: 16 bytes of low
+// nibbles laid out as the 4-bit codes, then 8 bytes holding the high two bits
+// of codes 4j..4j+3 in byte j); a row is all groups' codes, then the fp16
+// scales; scale = fp16(amax / divisor), codes clamped to the signed range.
+__host__ __device__ constexpr int blk_group_bytes(int bits) { return bits == 4 ? 16 : (bits == 6 ? 24 : 32); }
+__host__ __device__ constexpr int blk_row_bytes(int bits, int D) { return (blk_group_bytes(bits) + 2) * (D / 32); }
+
 // ln(2) and log2(e) in fp32.
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
@@ -123,6 +131,7 @@ struct Q4Pool {
     int head_dim;
     int page_size;
     int num_pages;
+    int bits = 4;  // code width of the block format (4, 6 or 8)
 };
 
 struct Fp8Pool {

@@ -17,12 +17,18 @@ bool aligned(const void* p, uintptr_t a = kAlign) { return p && (reinterpret_cas
 
 bool q4_dim_ok(int32_t D) { return D == 64 || D == 128 || D == 256 || D == 512; }
 
+// The Hadamard-32 block formats (K and V pools, rows of codes then fp16 scales).
+bool is_h32(int32_t format) {
+    return format == KVQ_FMT_Q4_H32 || format == KVQ_FMT_Q8_H32 || format == KVQ_FMT_Q6_H32;
+}
+int h32_bits(int32_t format) { return format == KVQ_FMT_Q8_H32 ? 8 : (format == KVQ_FMT_Q6_H32 ? 6 : 4); }
+
 // Validates a descriptor; returns KVQ_OK or the status to report.
 kvq_status check_cache(const kvq_cache* c) {
     if (!c) return KVQ_ERR_INVALID_ARG;
     if (c->page_size < 1 || c->num_pages < 1 || c->num_kv_heads < 1 || c->head_dim < 1) return KVQ_ERR_INVALID_ARG;
     if (int64_t(c->num_pages) * c->page_size > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
-    if (c->format == KVQ_FMT_Q4_H32) {
+    if (is_h32(c->format)) {
         if (c->head_dim % 32 || c->rope_dim != 0) return KVQ_ERR_INVALID_ARG;
         if (!q4_dim_ok(c->head_dim)) return KVQ_ERR_UNSUPPORTED;
         if (!aligned(c->k_pool) || !aligned(c->v_pool) || c->scale_pool) return KVQ_ERR_INVALID_ARG;
@@ -42,7 +48,7 @@ bool dtype_ok(int32_t dt) { return dt == KVQ_DT_F32 || dt == KVQ_DT_BF16 || dt =
 
 kvq::Q4Pool q4_pool(const kvq_cache* c) {
     return kvq::Q4Pool{static_cast<uint8_t*>(c->k_pool), static_cast<uint8_t*>(c->v_pool), c->num_kv_heads,
-                       c->head_dim, c->page_size, c->num_pages};
+                       c->head_dim, c->page_size, c->num_pages, h32_bits(c->format)};
 }
 
 kvq::Fp8Pool fp8_pool(const kvq_cache* c) {
@@ -61,7 +67,7 @@ kvq_status check_seq_args(const kvq_cache* c, int32_t n_q_heads, const int32_t* 
     if (n_q_heads % c->num_kv_heads) return KVQ_ERR_INVALID_ARG;
     if (batch > 0 && !aligned(seq_lens, 4)) return KVQ_ERR_INVALID_ARG;
     if (batch > 65535) return KVQ_ERR_UNSUPPORTED;
-    if (c->format == KVQ_FMT_Q4_H32 && n_q_heads / c->num_kv_heads > 16) return KVQ_ERR_UNSUPPORTED;
+    if (is_h32(c->format) && n_q_heads / c->num_kv_heads > 16) return KVQ_ERR_UNSUPPORTED;
     if (kvq_num_splits(max_seq_len, split_keys) > 16384) return KVQ_ERR_UNSUPPORTED;  // merge keeps one weight per split in LDS
     return KVQ_OK;
 }
@@ -81,9 +87,9 @@ const char* kvq_status_string(kvq_status s) {
 }
 
 size_t kvq_row_bytes(int32_t format, int32_t head_dim, int32_t rope_dim) {
-    if (format == KVQ_FMT_Q4_H32) {
+    if (is_h32(format)) {
         if (head_dim <= 0 || head_dim % 32 || rope_dim != 0) return 0;
-        return size_t(kvq::q4_row_bytes(head_dim));
+        return size_t(kvq::blk_row_bytes(h32_bits(format), head_dim));
     }
     if (format == KVQ_FMT_FP8_E4M3_ROW) {
         if (head_dim <= 0 || rope_dim <= 0 || rope_dim >= head_dim) return 0;
@@ -97,7 +103,7 @@ size_t kvq_pool_bytes(const kvq_cache* c) {
     const size_t rb = kvq_row_bytes(c->format, c->head_dim, c->rope_dim);
     if (!rb) return 0;
     const size_t slots = size_t(c->num_pages) * size_t(c->page_size);
-    if (c->format == KVQ_FMT_Q4_H32) return 2 * slots * size_t(c->num_kv_heads) * rb;
+    if (is_h32(c->format)) return 2 * slots * size_t(c->num_kv_heads) * rb;
     return slots * (rb + 2 * sizeof(float));
 }
 
@@ -115,7 +121,7 @@ kvq_status kvq_store(const kvq_cache* cache, const void* k, const void* v, int32
     if (n_tokens == 0) return KVQ_OK;
     if (!aligned(slot_mapping, 8)) return KVQ_ERR_INVALID_ARG;
     const InType dt = static_cast<InType>(dtype);
-    if (cache->format == KVQ_FMT_Q4_H32) {
+    if (is_h32(cache->format)) {
         if (!aligned(k) || !aligned(v)) return KVQ_ERR_INVALID_ARG;
         // one lane per 4 values: the launch must stay under 2^32 threads
         if (int64_t(n_tokens) * cache->num_kv_heads * 2 * (cache->head_dim / 4) > kMaxLaunchThreads)
@@ -141,7 +147,7 @@ kvq_status kvq_store_rotate_q(const kvq_cache* cache, const void* k, const void*
                               float* q_rot, int32_t n_rows, hipStream_t stream) {
     kvq_status st = check_cache(cache);
     if (st != KVQ_OK) return st;
-    if (cache->format != KVQ_FMT_Q4_H32) return KVQ_ERR_INVALID_ARG;
+    if (!is_h32(cache->format)) return KVQ_ERR_INVALID_ARG;
     if (!dtype_ok(kv_dtype) || !dtype_ok(q_dtype) || n_tokens < 0 || n_rows < 0) return KVQ_ERR_INVALID_ARG;
     if (n_tokens > 0 && (!aligned(slot_mapping, 8) || !aligned(k) || !aligned(v))) return KVQ_ERR_INVALID_ARG;
     if (n_rows > 0) {
@@ -173,8 +179,9 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_h
         return KVQ_ERR_INVALID_ARG;
     kvq::DecodeArgs a{q, n_q_heads, page_table, max_pages, seq_lens, batch, max_seq_len,
                       kvq_num_splits(max_seq_len, split_keys), sm_scale, split_keys, part_acc, part_m, part_z};
-    if (cache->format == KVQ_FMT_Q4_H32) {
+    if (is_h32(cache->format)) {
         const kvq::Q4Pool pool = q4_pool(cache);
+        if (pool.bits != 4) return launched(kvq::launch_decode_q4_simple(pool, a, stream));
         if (kvq::decode_q4_pair_supported(pool, a)) return launched(kvq::launch_decode_q4_pair(pool, a, stream));
         if (kvq::decode_q4_mfma_supported(pool, a)) return launched(kvq::launch_decode_q4_mfma(pool, a, stream));
         return launched(kvq::launch_decode_q4_simple(pool, a, stream));
@@ -214,7 +221,7 @@ kvq_status kvq_merge(const kvq_cache* cache, const float* part_acc, const float*
     if (st != KVQ_OK) return st;
     st = check_seq_args(cache, n_q_heads, seq_lens, batch, max_seq_len, split_keys, 32);
     if (st != KVQ_OK) return st;
-    const bool q4 = cache->format == KVQ_FMT_Q4_H32;
+    const bool q4 = is_h32(cache->format);  // rotated formats: inverse rotation, Dv = head_dim
     if (inverse_rotate != (q4 ? 1 : 0)) return KVQ_ERR_INVALID_ARG;
     if (batch == 0) return KVQ_OK;
     if (!aligned(part_acc) || !aligned(part_m, 4) || !aligned(part_z, 4) || !aligned(out) ||

@@ -25,8 +25,10 @@ namespace {
 // lanes.  Lanes of a group exchange values for the butterfly's upper stages
 // and the amax; each lane then packs its 4 codes into 2 bytes.  Rows are
 // ordered K rows first, then V rows, each (token, head) major.
-// idx is the lane's global index; lane its index in the wave.
-template <InType DT>
+// idx is the lane's global index; lane its index in the wave.  BITS: the
+// code width (4, 6, 8); the scale divides amax by 8, 31 or 127 and the codes
+// clamp to [-2^(BITS-1), 2^(BITS-1) - 1].
+template <InType DT, int BITS>
 __device__ __forceinline__ void store_q4_quad(const void* __restrict__ k, const void* __restrict__ v,
                                               const int64_t* __restrict__ slots, int n_tokens,
                                               uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, int H,
@@ -55,42 +57,61 @@ __device__ __forceinline__ void store_q4_quad(const void* __restrict__ k, const 
     }
 #pragma unroll
     for (int m = 1; m <= 4; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-    // scale = fp16_rne(amax / 8); amax * 0.125 is the same exactly rounded value.
-    const __half s16 = __float2half_rn(amax * 0.125f);
+    // scale = fp16_rne(amax / divisor); for 4 bits amax * 0.125 is the same
+    // exactly rounded value as amax / 8.
+    const __half s16 = __float2half_rn(BITS == 4 ? amax * 0.125f : amax / (BITS == 6 ? 31.0f : 127.0f));
     const float s = __half2float(s16);
-
-    // Values 4j .. 4j+3 of the group (j = e & 7) are code bytes 2j and 2j+1:
-    // value 2k in the low nibble of byte k, value 2k+1 in the high nibble.
-    uint32_t bits = 0u;
+    constexpr float kMax = float((1 << (BITS - 1)) - 1), kMin = -float(1 << (BITS - 1));
+    int q[4] = {0, 0, 0, 0};
     if (s != 0.0f) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float n = rintf(x[i] / s);  // correctly rounded divide, then half-to-even
-            n = fminf(fmaxf(n, -8.0f), 7.0f);
-            bits |= (uint32_t(int(n)) & 0xFu) << (4 * i);
+            n = fminf(fmaxf(n, kMin), kMax);
+            q[i] = int(n);
         }
     }
-    const int rb = q4_row_bytes(D);
+    const int rb = blk_row_bytes(BITS, D);
     const int64_t page = slot / page_size, off = slot % page_size;
     uint8_t* row = (which ? v_pool : k_pool) + ((page * H + h) * page_size + off) * rb;
-    reinterpret_cast<uint16_t*>(row)[e] = uint16_t(bits);
-    if ((e & 7) == 0) reinterpret_cast<uint16_t*>(row + D / 2)[e >> 3] = __half_as_ushort(s16);
+    // Values 4j .. 4j+3 of group g (j = e & 7, g = e >> 3).
+    const int g = e >> 3, j = e & 7;
+    uint8_t* grp = row + g * blk_group_bytes(BITS);
+    if (BITS == 8) {
+        uint32_t w = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w |= (uint32_t(q[i]) & 0xFFu) << (8 * i);
+        reinterpret_cast<uint32_t*>(grp)[j] = w;
+    } else {
+        // value 2k in the low nibble of byte k, value 2k+1 in the high nibble
+        uint32_t nib = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nib |= (uint32_t(q[i]) & 0xFu) << (4 * i);
+        reinterpret_cast<uint16_t*>(grp)[j] = uint16_t(nib);
+        if (BITS == 6) {
+            uint32_t top = 0u;  // high two bits of value 4j + i in bits 2i .. 2i+1 of byte j
+#pragma unroll
+            for (int i = 0; i < 4; ++i) top |= ((uint32_t(q[i]) >> 4) & 3u) << (2 * i);
+            grp[16 + j] = uint8_t(top);
+        }
+    }
+    if (j == 0) reinterpret_cast<uint16_t*>(row + (D / 32) * blk_group_bytes(BITS))[g] = __half_as_ushort(s16);
 }
 
-template <InType DT>
+template <InType DT, int BITS>
 __global__ __launch_bounds__(256) void store_q4_kernel(const void* __restrict__ k, const void* __restrict__ v,
                                                        const int64_t* __restrict__ slots, int n_tokens,
                                                        uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                        int H, int D, int page_size, int64_t n_slots) {
-    store_q4_quad<DT>(k, v, slots, n_tokens, k_pool, v_pool, H, D, page_size, n_slots,
-                      int64_t(blockIdx.x) * blockDim.x + threadIdx.x, threadIdx.x & 63);
+    store_q4_quad<DT, BITS>(k, v, slots, n_tokens, k_pool, v_pool, H, D, page_size, n_slots,
+                            int64_t(blockIdx.x) * blockDim.x + threadIdx.x, threadIdx.x & 63);
 }
 
 // The store's lanes in the first store_blocks workgroups, the query
 // rotation's in the rest: the two steps that precede the decode of a step
 // are independent, and one launch costs less than two.  A workgroup runs one
 // role only, and each role keeps its 8-lane groups whole.
-template <InType DK, InType DQ>
+template <InType DK, InType DQ, int BITS>
 __global__ __launch_bounds__(256) void store_rotate_q4_kernel(const void* __restrict__ k, const void* __restrict__ v,
                                                               const int64_t* __restrict__ slots, int n_tokens,
                                                               uint8_t* __restrict__ k_pool,
@@ -99,8 +120,8 @@ __global__ __launch_bounds__(256) void store_rotate_q4_kernel(const void* __rest
                                                               const void* q, float* q_rot, int64_t n_quads) {
     const int lane = threadIdx.x & 63;
     if (blockIdx.x < store_blocks) {
-        store_q4_quad<DK>(k, v, slots, n_tokens, k_pool, v_pool, H, D, page_size, n_slots,
-                          int64_t(blockIdx.x) * blockDim.x + threadIdx.x, lane);
+        store_q4_quad<DK, BITS>(k, v, slots, n_tokens, k_pool, v_pool, H, D, page_size, n_slots,
+                                int64_t(blockIdx.x) * blockDim.x + threadIdx.x, lane);
         return;
     }
     const int64_t i = int64_t(blockIdx.x - store_blocks) * blockDim.x + threadIdx.x;
@@ -160,51 +181,77 @@ __global__ __launch_bounds__(64) void store_fp8_kernel(const void* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_store_q4(const Q4Pool& pool, const void* k, const void* v, InType dt, const int64_t* slots,
-                           int n_tokens, hipStream_t s) {
-    const int64_t total = int64_t(n_tokens) * pool.n_kv_heads * 2 * (pool.head_dim / 4);
-    if (total == 0) return hipSuccess;
-    const dim3 block(256), grid(unsigned((total + 255) / 256));
-    const int64_t n_slots = int64_t(pool.num_pages) * pool.page_size;
+namespace {
+template <int BITS>
+void store_blk(dim3 grid, hipStream_t s, const Q4Pool& pool, const void* k, const void* v, InType dt,
+               const int64_t* slots, int n_tokens, int64_t n_slots) {
+    const int H = pool.n_kv_heads, D = pool.head_dim, P = pool.page_size;
     switch (dt) {
         case InType::F32:
-            store_q4_kernel<InType::F32><<<grid, block, 0, s>>>(k, v, slots, n_tokens, pool.k, pool.v,
-                                                                pool.n_kv_heads, pool.head_dim, pool.page_size, n_slots);
+            store_q4_kernel<InType::F32, BITS><<<grid, 256, 0, s>>>(k, v, slots, n_tokens, pool.k, pool.v, H, D, P, n_slots);
             break;
         case InType::BF16:
-            store_q4_kernel<InType::BF16><<<grid, block, 0, s>>>(k, v, slots, n_tokens, pool.k, pool.v,
-                                                                 pool.n_kv_heads, pool.head_dim, pool.page_size, n_slots);
+            store_q4_kernel<InType::BF16, BITS><<<grid, 256, 0, s>>>(k, v, slots, n_tokens, pool.k, pool.v, H, D, P, n_slots);
             break;
         case InType::F16:
-            store_q4_kernel<InType::F16><<<grid, block, 0, s>>>(k, v, slots, n_tokens, pool.k, pool.v,
-                                                                pool.n_kv_heads, pool.head_dim, pool.page_size, n_slots);
+            store_q4_kernel<InType::F16, BITS><<<grid, 256, 0, s>>>(k, v, slots, n_tokens, pool.k, pool.v, H, D, P, n_slots);
             break;
     }
-    return hipGetLastError();
 }
 
-namespace {
-template <InType DK>
-void store_rotate_q4_dq(dim3 grid, hipStream_t s, const Q4Pool& pool, const void* k, const void* v,
-                        const int64_t* slots, int n_tokens, int64_t n_slots, unsigned store_blocks, const void* q,
-                        InType q_dt, float* q_rot, int64_t n_quads) {
+template <InType DK, int BITS>
+void store_rotate_dq(dim3 grid, hipStream_t s, const Q4Pool& pool, const void* k, const void* v, const int64_t* slots,
+                     int n_tokens, int64_t n_slots, unsigned store_blocks, const void* q, InType q_dt, float* q_rot,
+                     int64_t n_quads) {
     const int H = pool.n_kv_heads, D = pool.head_dim, P = pool.page_size;
     switch (q_dt) {
         case InType::F32:
-            store_rotate_q4_kernel<DK, InType::F32><<<grid, 256, 0, s>>>(k, v, slots, n_tokens, pool.k, pool.v, H, D, P,
-                                                                         n_slots, store_blocks, q, q_rot, n_quads);
+            store_rotate_q4_kernel<DK, InType::F32, BITS><<<grid, 256, 0, s>>>(
+                k, v, slots, n_tokens, pool.k, pool.v, H, D, P, n_slots, store_blocks, q, q_rot, n_quads);
             break;
         case InType::BF16:
-            store_rotate_q4_kernel<DK, InType::BF16><<<grid, 256, 0, s>>>(k, v, slots, n_tokens, pool.k, pool.v, H, D,
-                                                                          P, n_slots, store_blocks, q, q_rot, n_quads);
+            store_rotate_q4_kernel<DK, InType::BF16, BITS><<<grid, 256, 0, s>>>(
+                k, v, slots, n_tokens, pool.k, pool.v, H, D, P, n_slots, store_blocks, q, q_rot, n_quads);
             break;
         case InType::F16:
-            store_rotate_q4_kernel<DK, InType::F16><<<grid, 256, 0, s>>>(k, v, slots, n_tokens, pool.k, pool.v, H, D, P,
-                                                                         n_slots, store_blocks, q, q_rot, n_quads);
+            store_rotate_q4_kernel<DK, InType::F16, BITS><<<grid, 256, 0, s>>>(
+                k, v, slots, n_tokens, pool.k, pool.v, H, D, P, n_slots, store_blocks, q, q_rot, n_quads);
+            break;
+    }
+}
+
+template <int BITS>
+void store_rotate_blk(dim3 grid, hipStream_t s, const Q4Pool& pool, const void* k, const void* v, InType dt,
+                      const int64_t* slots, int n_tokens, int64_t n_slots, unsigned store_blocks, const void* q,
+                      InType q_dt, float* q_rot, int64_t n_quads) {
+    switch (dt) {
+        case InType::F32:
+            store_rotate_dq<InType::F32, BITS>(grid, s, pool, k, v, slots, n_tokens, n_slots, store_blocks, q, q_dt,
+                                               q_rot, n_quads);
+            break;
+        case InType::BF16:
+            store_rotate_dq<InType::BF16, BITS>(grid, s, pool, k, v, slots, n_tokens, n_slots, store_blocks, q, q_dt,
+                                                q_rot, n_quads);
+            break;
+        case InType::F16:
+            store_rotate_dq<InType::F16, BITS>(grid, s, pool, k, v, slots, n_tokens, n_slots, store_blocks, q, q_dt,
+                                               q_rot, n_quads);
             break;
     }
 }
 }  // namespace
+
+hipError_t launch_store_q4(const Q4Pool& pool, const void* k, const void* v, InType dt, const int64_t* slots,
+                           int n_tokens, hipStream_t s) {
+    const int64_t total = int64_t(n_tokens) * pool.n_kv_heads * 2 * (pool.head_dim / 4);
+    if (total == 0) return hipSuccess;
+    const dim3 grid(unsigned((total + 255) / 256));
+    const int64_t n_slots = int64_t(pool.num_pages) * pool.page_size;
+    if (pool.bits == 8) store_blk<8>(grid, s, pool, k, v, dt, slots, n_tokens, n_slots);
+    else if (pool.bits == 6) store_blk<6>(grid, s, pool, k, v, dt, slots, n_tokens, n_slots);
+    else store_blk<4>(grid, s, pool, k, v, dt, slots, n_tokens, n_slots);
+    return hipGetLastError();
+}
 
 hipError_t launch_store_rotate_q4(const Q4Pool& pool, const void* k, const void* v, InType dt, const int64_t* slots,
                                   int n_tokens, const void* q, InType q_dt, float* q_rot, int n_rows, hipStream_t s) {
@@ -215,20 +262,12 @@ hipError_t launch_store_rotate_q4(const Q4Pool& pool, const void* k, const void*
     if (store_blocks + rot_blocks == 0) return hipSuccess;
     const dim3 grid(store_blocks + rot_blocks);
     const int64_t n_slots = int64_t(pool.num_pages) * pool.page_size;
-    switch (dt) {
-        case InType::F32:
-            store_rotate_q4_dq<InType::F32>(grid, s, pool, k, v, slots, n_tokens, n_slots, store_blocks, q, q_dt, q_rot,
-                                            n_quads);
-            break;
-        case InType::BF16:
-            store_rotate_q4_dq<InType::BF16>(grid, s, pool, k, v, slots, n_tokens, n_slots, store_blocks, q, q_dt,
-                                             q_rot, n_quads);
-            break;
-        case InType::F16:
-            store_rotate_q4_dq<InType::F16>(grid, s, pool, k, v, slots, n_tokens, n_slots, store_blocks, q, q_dt, q_rot,
-                                            n_quads);
-            break;
-    }
+    if (pool.bits == 8)
+        store_rotate_blk<8>(grid, s, pool, k, v, dt, slots, n_tokens, n_slots, store_blocks, q, q_dt, q_rot, n_quads);
+    else if (pool.bits == 6)
+        store_rotate_blk<6>(grid, s, pool, k, v, dt, slots, n_tokens, n_slots, store_blocks, q, q_dt, q_rot, n_quads);
+    else
+        store_rotate_blk<4>(grid, s, pool, k, v, dt, slots, n_tokens, n_slots, store_blocks, q, q_dt, q_rot, n_quads);
     return hipGetLastError();
 }
 

@@ -66,7 +66,9 @@ typedef enum {
 
 typedef enum {
     KVQ_FMT_Q4_H32 = 1,        /* 4-bit Hadamard-32 groups + fp16 scale, K and V pools */
-    KVQ_FMT_FP8_E4M3_ROW = 2   /* e4m3 latent rows + f32 scales (latent, rope) */
+    KVQ_FMT_FP8_E4M3_ROW = 2,  /* e4m3 latent rows + f32 scales (latent, rope) */
+    KVQ_FMT_Q8_H32 = 3,        /* the same skeleton with 8-bit codes */
+    KVQ_FMT_Q6_H32 = 4         /* the same skeleton with 6-bit codes */
 } kvq_format;
 
 typedef enum {
@@ -84,6 +86,16 @@ typedef enum {
  *   group (byte k of a group holds element 2k in its low nibble and element
  *   2k+1 in its high nibble, two's complement), then the D/32 fp16 scales,
  *   little-endian.  scale_pool = NULL.
+ * KVQ_FMT_Q8_H32, KVQ_FMT_Q6_H32 (FreeToken pull request "feat(kvcache):
+ *   add reliable quantized KV cache": the q4_0 layout sits beside q8_0, 1.0625
+ *   bytes per element, in one spec; q6_0 divides by 31): the same pools,
+ *   rotation and fp16 scale per group, with scale = fp16(amax/127) and codes
+ *   in [-128, 127] (8-bit) or fp16(amax/31) and [-32, 31] (6-bit).  A row is
+ *   the codes of every group, then the D/32 fp16 scales: 32 bytes per group
+ *   (code i in byte i) or 24 bytes per group (16 bytes of low nibbles laid
+ *   out as the 4-bit codes, then 8 bytes holding the high two bits of code
+ *   4j+i in bits 2i..2i+1 of byte j).  row_bytes = 34*(D/32) or 26*(D/32);
+ *   head_dim 64, 128, 256 or 512.  Decode runs the plain vector kernel.
  * KVQ_FMT_FP8_E4M3_ROW (the KV8 commit of the colibri pull request):
  *   num_kv_heads = 1 (one latent shared by all heads), head_dim = kv_lora +
  *   rope_dim (a multiple of 16; kv_lora a multiple of 64), rope_dim > 0.
@@ -165,7 +177,7 @@ kvq_status kvq_rotate_q(const void* q, int32_t dtype, float* q_rot, int32_t n_ro
  * stored bytes and q_rot are bit-identical to those two calls.  Either count
  * may be 0 (that part is skipped and its pointers are not read).  q_rot must
  * not overlap k, v or the pools; q == q_rot is allowed for f32.
- * Q4 only (KVQ_ERR_INVALID_ARG for an FP8 cache). */
+ * Hadamard-32 formats (Q4, Q8, Q6) only (KVQ_ERR_INVALID_ARG for an FP8 cache). */
 kvq_status kvq_store_rotate_q(const kvq_cache* cache, const void* k, const void* v, int32_t kv_dtype,
                               const int64_t* slot_mapping, int32_t n_tokens, const void* q, int32_t q_dtype,
                               float* q_rot, int32_t n_rows, hipStream_t stream);
@@ -197,7 +209,7 @@ kvq_status kvq_store_rotate_q(const kvq_cache* cache, const void* k, const void*
  * part_acc: [batch][n_q_heads][S][Dv] f32, part_m / part_z: [batch][n_q_heads][S]
  * f32 with S = kvq_num_splits(max_seq_len, split_keys).
  * Requires n_q_heads % num_kv_heads == 0 and a group of at most 16 query
- * heads per KV head (Q4). */
+ * heads per KV head (Hadamard-32 formats); Q8 and Q6 run the plain vector kernel. */
 kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
                            int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
                            float sm_scale, int32_t split_keys, float* part_acc, float* part_m, float* part_z,
@@ -232,10 +244,11 @@ kvq_status kvq_decode_attn_sel(const kvq_cache* cache, const float* q, int32_t n
  * the four are added in order 0, 1, 2, 3;
  * followed for Q4 by the single inverse rotation (H32 is its own inverse):
  *   M = max_s m_s, Z = sum_s z_s exp(m_s - M),
- *   out = R( sum_s acc_s exp(m_s - M) / Z ),  R = H32 (Q4) or identity (FP8),
+ *   out = R( sum_s acc_s exp(m_s - M) / Z ),  R = H32 (Q4/Q8/Q6) or identity (FP8),
  *   lse = M + log Z.
  * A sequence with T = 0 gives out = 0 and lse = -inf.  Only the splits that
- * cover [0, T_b) are read.  inverse_rotate must be 1 for Q4 and 0 for FP8.
+ * cover [0, T_b) are read.  inverse_rotate must be 1 for the Hadamard-32
+ * formats (Q4, Q8, Q6) and 0 for FP8.
  * seq_lens, max_seq_len and split_keys are those of the decode call that
  * wrote the partials (for kvq_decode_attn_sel: n_sel and max_sel); split_keys
  * is a positive multiple of 32.

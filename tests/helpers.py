@@ -26,7 +26,8 @@ class Q4Case:
         import fp8_quantized_kv_amd as kvq
         self.w, self.lens, self.layer = w, list(lens), layer
         self.lay = wl.page_layout(w, self.lens)
-        self.cache = kvq.Q4Cache(self.lay.num_pages, w.n_kv_heads, w.head_dim, w.page_size, device)
+        fmt = {4: kvq.FMT_Q4_H32, 6: kvq.FMT_Q6_H32, 8: kvq.FMT_Q8_H32}[w.bits]
+        self.cache = kvq.Q4Cache(self.lay.num_pages, w.n_kv_heads, w.head_dim, w.page_size, device, fmt=fmt)
         if fill is not None:  # bytes the stores do not overwrite keep this value
             self.cache.k_pool.fill_(fill)
             self.cache.v_pool.fill_(fill)
@@ -34,7 +35,7 @@ class Q4Case:
         self.page_table = self.lay.page_table.to(device)
         self.seq_lens = torch.tensor(self.lens, dtype=torch.int32, device=device)
         self.max_seq_len = max(self.lens) if self.lens else 0
-        shape = oracle.q4_pool_shape(self.lay.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+        shape = oracle.q4_pool_shape(self.lay.num_pages, w.n_kv_heads, w.page_size, w.head_dim, w.bits)
         self.k_ref = np.zeros(shape, np.uint8) if build_oracle else None
         self.v_ref = np.zeros(shape, np.uint8) if build_oracle else None
         off = 0

@@ -38,6 +38,11 @@ def test_size_helpers(kvq):
     assert L.kvq_row_bytes(kvq.FMT_Q4_H32, 256, 0) == 144
     assert L.kvq_row_bytes(kvq.FMT_Q4_H32, 128, 0) == 72
     assert L.kvq_row_bytes(kvq.FMT_Q4_H32, 100, 0) == 0
+    assert L.kvq_row_bytes(kvq.FMT_Q8_H32, 256, 0) == 272       # 1.0625 bytes per element
+    assert L.kvq_row_bytes(kvq.FMT_Q6_H32, 256, 0) == 208
+    assert L.kvq_row_bytes(kvq.FMT_Q6_H32, 64, 0) == 52
+    q8 = kvq.KvqCacheDesc(kvq.FMT_Q8_H32, 4, 256, 0, 16, 1024, 0x1000, 0x2000, None)
+    assert L.kvq_pool_bytes(ctypes.byref(q8)) == 2 * 1024 * 16 * 4 * 272
     assert L.kvq_row_bytes(kvq.FMT_FP8_E4M3_ROW, 576, 64) == 576
     assert L.kvq_row_bytes(7, 256, 0) == 0
     assert L.kvq_num_splits(262144, 2048) == 128

@@ -52,6 +52,75 @@ def test_store_q4_bit_exact(kvq, D, dtype):
     assert np.array_equal(cache.v_pool.cpu().numpy(), vref)
 
 
+@pytest.mark.parametrize("bits", [6, 8])
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_store_blk_bit_exact(kvq, bits, D, dtype):
+    """The 6- and 8-bit block formats: codes and scales bit-exact against the
+    oracle, with skipped slots, an all-zero row and a large value."""
+    _say(f"store bits={bits} D={D} dtype={dtype}")
+    g = torch.Generator().manual_seed(D + bits)
+    n_tok, H, ps, pages = 300, 3, 16, 40
+    k = (torch.randn((n_tok, H, D), generator=g) * torch.exp(torch.randn((n_tok, H, 1), generator=g))).to(dtype)
+    v = torch.randn((n_tok, H, D), generator=g).to(dtype)
+    k[5, 1, 3] = 40.0
+    k[7] = 0.0
+    slots = torch.randperm(pages * ps, generator=g)[:n_tok].to(torch.int64)
+    slots[::17] = -1
+    fmt = kvq.FMT_Q8_H32 if bits == 8 else kvq.FMT_Q6_H32
+    cache = kvq.Q4Cache(pages, H, D, ps, fmt=fmt)
+    kvq.kvq_store(cache, k.cuda(), v.cuda(), slots.cuda())
+    kref = np.zeros(cache.k_pool.shape, np.uint8)
+    vref = np.zeros_like(kref)
+    oracle.q4_store(kref, vref, k.float().numpy(), v.float().numpy(), slots.numpy(), ps)
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.k_pool.cpu().numpy(), kref)
+    assert np.array_equal(cache.v_pool.cpu().numpy(), vref)
+
+
+@pytest.mark.parametrize("bits", [6, 8])
+def test_blk_decode_matches_oracle(kvq, bits):
+    """Decode + merge over the 6- and 8-bit caches (the plain kernel): a ragged
+    batch with tails and an empty sequence, splits of 512 and 2048, the
+    one-launch store + rotation of a new token, and batch invariance."""
+    import fp8_quantized_kv_amd as kvq_mod
+    w = wl.shrink(wl.RAGGED, prefill_chunk=0, bits=bits)
+    lens = [3000, 17, 0, 1100]
+    case = Q4Case(w, lens)
+    assert np.array_equal(case.cache.k_pool.cpu().numpy(), case.k_ref)
+    ro, rl = case.ref_attention()
+    for split in (512, 2048):
+        o, lse = case.gpu_attention(split)
+        err = rel_err(o, ro)
+        _say(f"  bits={bits} split={split} max_rel_err={err.max():.2e}")
+        assert err.max() < TOL
+        fin = np.isfinite(rl)
+        assert np.array_equal(fin, np.isfinite(lse)) and np.max(np.abs(lse[fin] - rl[fin])) < 1e-3 * max(1.0, np.abs(rl[fin]).max())
+        assert np.all(o[2] == 0)
+    # alone == in the batch, bit for bit
+    o_b, l_b = case.gpu_attention(512)
+    q_rot = kvq_mod.kvq_rotate_q(case.q)
+    for b in (0, 3):
+        pa, pm, pz = kvq_mod.kvq_decode_attn(case.cache, q_rot[b:b + 1].contiguous(), case.page_table[b:b + 1].contiguous(),
+                                             case.seq_lens[b:b + 1].contiguous(), case.max_seq_len, w.sm_scale, 512)
+        o1, l1 = kvq_mod.kvq_merge(case.cache, pa, pm, pz, case.seq_lens[b:b + 1].contiguous(), case.max_seq_len, 512)
+        assert np.array_equal(o1.cpu().numpy()[0], o_b[b]) and np.array_equal(l1.cpu().numpy()[0], l_b[b])
+    # one-launch store + rotation on this format equals the two calls
+    gk = torch.Generator(device="cuda").manual_seed(5)
+    kn = torch.randn((1, w.n_kv_heads, w.head_dim), generator=gk, device="cuda").to(torch.bfloat16)
+    vn = torch.randn((1, w.n_kv_heads, w.head_dim), generator=gk, device="cuda").to(torch.bfloat16)
+    sl = torch.tensor([int(case.lay.page_table[0, 0]) * w.page_size + 2], dtype=torch.int64, device="cuda")
+    before_k, before_v = case.cache.k_pool.clone(), case.cache.v_pool.clone()
+    qr2 = kvq_mod.kvq_store_rotate_q(case.cache, kn, vn, sl, case.q)
+    fused_k, fused_v = case.cache.k_pool.clone(), case.cache.v_pool.clone()
+    case.cache.k_pool.copy_(before_k)
+    case.cache.v_pool.copy_(before_v)
+    kvq_mod.kvq_store(case.cache, kn, vn, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(qr2, q_rot)
+    assert torch.equal(case.cache.k_pool, fused_k) and torch.equal(case.cache.v_pool, fused_v)
+
+
 def test_store_q4_token_by_token_equals_bulk(kvq):
     """Storing a sequence one token per call gives the same bytes as one call."""
     w = wl.TINY

@@ -51,10 +51,11 @@ class Q4Workload:
     plant_at: Optional[int] = None   # position whose K equals the group's first query
     prefill_chunk: int = 0           # extra tokens stored per step (not attended)
     split_keys: int = 2048
+    bits: int = 4                    # code width of the block format (4, 6 or 8)
 
     @property
     def row_bytes(self):
-        return self.head_dim // 2 + 2 * (self.head_dim // 32)
+        return {4: 16, 6: 24, 8: 32}[self.bits] * (self.head_dim // 32) + 2 * (self.head_dim // 32)
 
     @property
     def group(self):
@@ -97,7 +98,11 @@ RAGGED = Q4Workload("ragged_q4_b16", seed=1004, n_layers=1, batch=16, n_q_heads=
 MLA_262K = MlaWorkload("mla_fp8_262k", seed=1005, n_layers=4, batch=1, n_heads=128, kv_lora=512, rope_dim=64,
                        seq_len=262144, sm_scale=576 ** -0.5, split_keys=2048)
 
-WORKLOADS = {w.name: w for w in (TINY, GQA_32K, GQA_262K, RAGGED, MLA_262K)}
+# The 8- and 6-bit block variants on the 32K shape (the same inputs; only the code width differs).
+GQA_32K_Q8 = replace(GQA_32K, name="gqa_q8_32k", bits=8)
+GQA_32K_Q6 = replace(GQA_32K, name="gqa_q6_32k", bits=6)
+
+WORKLOADS = {w.name: w for w in (TINY, GQA_32K, GQA_262K, RAGGED, MLA_262K, GQA_32K_Q8, GQA_32K_Q6)}
 
 
 def shrink(w, **kw):
