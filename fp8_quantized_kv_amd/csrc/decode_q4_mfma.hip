@@ -277,9 +277,8 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
         }
 
         // ---- online softmax over the tile (per head = per column n16)
-        float tmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                           fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-        tmax = quad_max(tmax) * kTwo24;
+        // scores are finite or -inf (valid rows have finite scales), never NaN
+        const float tmax = quad_max_nonan(max8f(sc)) * kTwo24;
         const bool move = tmax > m_run + kRescale || m_run == -INFINITY;
         if (__builtin_amdgcn_ballot_w64(move) != 0ull) {
             const float m_new = move ? fmaxf(m_run, tmax) : m_run;
@@ -328,22 +327,32 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
             }
         }
 
-        // ---- context: per group, two 16-channel blocks
+        // ---- context: per group, two 16-channel blocks.  A row n16 holds head
+        // n16 (or, PACK, head n16 & 7: rows 8..15 repeat heads 0..7).  PACK
+        // gives rows 0..7 the scales of the even group of a pair and rows
+        // 8..15 those of the odd group, so one A operand serves both groups:
+        // an even group's outputs are read from rows 0..7, an odd group's
+        // from rows 8..15, and the other rows are discarded.
+        const uint32_t psel_pair = (n16 & 8) ? 0x07060302u : 0x05040100u;
+        half8_t av;
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
             const i32x2 cv = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
                 (__attribute__((address_space(3))) i32x2*)(vt + tr_off + 16 * gi));
             // scale pair (key 4q+r, key 16+4q+r) of group gi, r = 0..3
-            half8_t av;
+            if (!PACK || (gi & 1) == 0) {
+                const uint32_t psel = PACK ? psel_pair : ((gi & 1) ? 0x07060302u : 0x05040100u);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint32_t sa = *reinterpret_cast<const uint32_t*>(vt + (4 * q4 + r) * RB + D / 2 + 4 * (gi >> 1));
-                const uint32_t sb = *reinterpret_cast<const uint32_t*>(vt + (16 + 4 * q4 + r) * RB + D / 2 + 4 * (gi >> 1));
-                const uint32_t pair = (gi & 1) ? __builtin_amdgcn_perm(sb, sa, 0x07060302u)
-                                               : __builtin_amdgcn_perm(sb, sa, 0x05040100u);
-                const half2_t w = pp[r] * __builtin_bit_cast(half2_t, pair);
-                av[2 * r] = w[0];
-                av[2 * r + 1] = w[1];
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t sa =
+                        *reinterpret_cast<const uint32_t*>(vt + (4 * q4 + r) * RB + D / 2 + 4 * (gi >> 1));
+                    const uint32_t sb =
+                        *reinterpret_cast<const uint32_t*>(vt + (16 + 4 * q4 + r) * RB + D / 2 + 4 * (gi >> 1));
+                    const uint32_t pair = __builtin_amdgcn_perm(sb, sa, psel);
+                    const half2_t w = pp[r] * __builtin_bit_cast(half2_t, pair);
+                    av[2 * r] = w[0];
+                    av[2 * r + 1] = w[1];
+                }
             }
             const half8_t b0 = unpack8(uint32_t(cv[0]));
             const half8_t b1 = unpack8(uint32_t(cv[1]));
@@ -369,9 +378,14 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
     float* wZ = wM + 16;                         // [16]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if (4 * q4 + i < G) {
+        const int row = 4 * q4 + i, h = PACK ? (row & 7) : row;
+        if (h < G) {
 #pragma unroll
-            for (int blk = 0; blk < NB; ++blk) wo[(wave * 16 + 4 * q4 + i) * D + 16 * blk + n16] = o[blk][i] * kTwo24;
+            for (int blk = 0; blk < NB; ++blk) {
+                // PACK: group blk / 2 is read from rows 0..7 if even, 8..15 if odd
+                if (!PACK || ((blk >> 1) & 1) == (row >> 3))
+                    wo[(wave * 16 + h) * D + 16 * blk + n16] = o[blk][i] * kTwo24;
+            }
         }
     }
     if (lane < 16) {
