@@ -238,34 +238,57 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
         uint8_t* vt = ring + (2 + (t & 1)) * S::TILE;
         const int valid = min(kSub, n_keys - t * kSub);
 
-        // ---- scores: two 16-key blocks; lane holds keys 16*kb + 4*q4 + i of head n16
+        // ---- scores: two 16-key blocks; lane holds keys 16*kb + 4*q4 + i of head n16.
+        // Both blocks' MFMAs of group gi are issued before the scale FMAs of
+        // group gi - 1 consume the previous results, so the matrix-core
+        // latency is covered by independent work; each acc still sums the
+        // groups in ascending order.
         float sc[2][4];
+        {
+            u32x4 ks[2][4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const uint8_t* arow = kt + (16 * kb + n16) * RB;
-            u32x4 ks[4];
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                ks[i] = *reinterpret_cast<const u32x4*>(kt + (16 * kb + 4 * q4 + i) * RB + D / 2);
-            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                for (int i = 0; i < 4; ++i)
+                    ks[kb][i] = *reinterpret_cast<const u32x4*>(kt + (16 * kb + 4 * q4 + i) * RB + D / 2);
+            float acc[2][4] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+            f32x4 dprev[2];
 #pragma unroll
-            for (int gi = 0; gi < NG; ++gi) {
-                const uint32_t w = *reinterpret_cast<const uint32_t*>(arow + 16 * gi + 4 * q4);
-                const half8_t av = unpack8(w);
-                f32x4 d = mfma(av, bq_hi[gi], cbias[gi]);
-                if (!PACK) d = mfma(av, bq_lo[PACK ? 0 : gi], d);
+            for (int gi = 0; gi <= NG; ++gi) {
+                f32x4 dcur[2];
+                if (gi < NG) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t sw = ks[i][gi >> 1];
-                    acc[i] = fmaf(d[i], (gi & 1) ? hi_half(sw) : lo_half(sw), acc[i]);
+                    for (int kb = 0; kb < 2; ++kb) {
+                        const uint32_t w =
+                            *reinterpret_cast<const uint32_t*>(kt + (16 * kb + n16) * RB + 16 * gi + 4 * q4);
+                        const half8_t av = unpack8(w);
+                        dcur[kb] = mfma(av, bq_hi[gi], cbias[gi]);
+                        if (!PACK) dcur[kb] = mfma(av, bq_lo[PACK ? 0 : gi], dcur[kb]);
+                    }
+                }
+                if (gi > 0) {
+                    const int gp = gi - 1;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t sw = ks[kb][i][gp >> 1];
+                            acc[kb][i] = fmaf(dprev[kb][i], (gp & 1) ? hi_half(sw) : lo_half(sw), acc[kb][i]);
+                        }
+                }
+                if (gi < NG) {
+                    dprev[0] = dcur[0];
+                    dprev[1] = dcur[1];
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                // PACK: column n16 ^ 8 holds the other part of the same head
-                // (DPP row rotate by 8); a + b = b + a, so both columns agree.
-                sc[kb][i] = PACK ? acc[i] + row_xor8(acc[i]) : acc[i];  // log2 units / 2^24
-            }
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    // PACK: column n16 ^ 8 holds the other part of the same head
+                    // (DPP row rotate by 8); a + b = b + a, so both columns agree.
+                    sc[kb][i] = PACK ? acc[kb][i] + row_xor8(acc[kb][i]) : acc[kb][i];  // log2 units / 2^24
+                }
         }
         if (valid < kSub) {  // only the last tile of a wave can be partial
             asm volatile("" ::: "memory");  // a real branch: keep the full tiles free of selects
