@@ -220,6 +220,12 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
     f32x4 o[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // PACK: the +8 offset of the V codes, summed apart from o per pair of
+    // groups (one MFMA per pair and sub-tile against the constant B; every
+    // column of it holds the same value) and added to o once at the end.
+    f32x4 ro[PACK ? NG / 2 : 1];
+#pragma unroll
+    for (int i = 0; i < (PACK ? NG / 2 : 1); ++i) ro[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY;  // running max (log2 units) of head n16
     float z_run = 0.0f;       // this lane's share of the running sum
 
@@ -315,6 +321,12 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
             for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o[blk][i] *= al[i];
+            if (PACK) {
+#pragma unroll
+                for (int gp = 0; gp < NG / 2; ++gp)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ro[gp][i] *= al[i];
+            }
         }
         // p for keys of slots 2,3,6,7 (i = 1, 3) is taken /16 to undo the x16
         // those V codes carry.
@@ -376,13 +388,14 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
                     av[2 * r] = w[0];
                     av[2 * r + 1] = w[1];
                 }
+                if (PACK) ro[gi >> 1] = mfma(av, bconst, ro[gi >> 1]);
             }
             const half8_t b0 = unpack8(uint32_t(cv[0]));
             const half8_t b1 = unpack8(uint32_t(cv[1]));
             o[2 * gi] = mfma(av, b0, o[2 * gi]);
-            o[2 * gi] = mfma(av, bconst, o[2 * gi]);
+            if (!PACK) o[2 * gi] = mfma(av, bconst, o[2 * gi]);
             o[2 * gi + 1] = mfma(av, b1, o[2 * gi + 1]);
-            o[2 * gi + 1] = mfma(av, bconst, o[2 * gi + 1]);
+            if (!PACK) o[2 * gi + 1] = mfma(av, bconst, o[2 * gi + 1]);
         }
         if (t + 2 < n_sub) issue(v_pool, t + 2, v_ring);
     }
@@ -407,7 +420,7 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
             for (int blk = 0; blk < NB; ++blk) {
                 // PACK: group blk / 2 is read from rows 0..7 if even, 8..15 if odd
                 if (!PACK || ((blk >> 1) & 1) == (row >> 3))
-                    wo[(wave * 16 + h) * D + 16 * blk + n16] = o[blk][i] * kTwo24;
+                    wo[(wave * 16 + h) * D + 16 * blk + n16] = (PACK ? o[blk][i] + ro[blk >> 2][i] : o[blk][i]) * kTwo24;
             }
         }
     }
