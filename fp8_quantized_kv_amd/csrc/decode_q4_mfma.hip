@@ -102,21 +102,6 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
     const int w0 = j0 + wave * kq;
     int T = a.seq_lens[b];  // first: its latency overlaps the loads below
 
-    // The query of head n16 (log2-scaled later), loaded first: the wait for the
-    // page-table reads below then covers it, and the copies issued after
-    // those reads are not waited for when the query is used.
-    // PACK (groups of at most 8 heads): B columns 0..7 carry the query's f16
-    // hi part and columns 8..15 its lo part, so one MFMA per group does both.
-    const int hcol = PACK ? (n16 & 7) : n16;  // the head this lane's B column holds
-    const bool live = hcol < G;
-    const float* qh = a.q + (hb + (live ? hcol : 0)) * D;
-    float4 qv[NG][2];
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-        qv[gi][0] = *reinterpret_cast<const float4*>(qh + 32 * gi + 8 * q4);
-        qv[gi][1] = *reinterpret_cast<const float4*>(qh + 32 * gi + 8 * q4 + 4);
-    }
-
     // Byte offset (within a pool) of each 16-row run of this wave's quarter:
     // lane l holds run l in the first register and run 64 + l in the second.
     // Resolved before the sequence length is known: positions are clamped to
@@ -176,6 +161,22 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
     if (n_sub > 1) {
         issue(k_pool, 1, k_ring);
         issue(v_pool, 1, v_ring);
+    }
+
+    // The query of head n16 (log2-scaled later), loaded after the first
+    // copies are issued: the copies then wait only for the page-table
+    // reads, not for the query's 16 KB per wave from L2 as well (when the
+    // query is used, the first copies are needed anyway).
+    // PACK (groups of at most 8 heads): B columns 0..7 carry the query's f16
+    // hi part and columns 8..15 its lo part, so one MFMA per group does both.
+    const int hcol = PACK ? (n16 & 7) : n16;  // the head this lane's B column holds
+    const bool live = hcol < G;
+    const float* qh = a.q + (hb + (live ? hcol : 0)) * D;
+    float4 qv[NG][2];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        qv[gi][0] = *reinterpret_cast<const float4*>(qh + 32 * gi + 8 * q4);
+        qv[gi][1] = *reinterpret_cast<const float4*>(qh + 32 * gi + 8 * q4 + 4);
     }
 
     // B operands of the score MFMAs: pre-scaled query (log2 units) of head
@@ -257,6 +258,16 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     ks[kb][i] = *reinterpret_cast<const u32x4*>(kt + (16 * kb + 4 * q4 + i) * RB + D / 2);
+            uint32_t kc[2][NG];
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    kc[kb][gi] = *reinterpret_cast<const uint32_t*>(kt + (16 * kb + n16) * RB + 16 * gi + 4 * q4);
+            // Everything the scores read from the K slot is now in registers
+            // (the copy's lgkmcnt wait sees to that): refill the slot with
+            // sub-tile t + 2 before the MFMAs rather than after them.
+            if (t + 2 < n_sub) issue(k_pool, t + 2, k_ring);
             float acc[2][4] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
             f32x4 dprev[2];
 #pragma unroll
@@ -265,9 +276,7 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
                 if (gi < NG) {
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb) {
-                        const uint32_t w =
-                            *reinterpret_cast<const uint32_t*>(kt + (16 * kb + n16) * RB + 16 * gi + 4 * q4);
-                        const half8_t av = unpack8(w);
+                        const half8_t av = unpack8(kc[kb][gi]);
                         dcur[kb] = mfma(av, bq_hi[gi], cbias[gi]);
                         if (!PACK) dcur[kb] = mfma(av, bq_lo[PACK ? 0 : gi], dcur[kb]);
                     }
@@ -304,6 +313,40 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
                 for (int i = 0; i < 4; ++i)
                     if (16 * kb + 4 * q4 + i >= valid) sc[kb][i] = -INFINITY;
         }
+
+        // V of sub-tile t has landed once at most K_t+1, V_t+1, K_t+2 are outstanding.
+        if (t + 2 < n_sub) wait_vmcnt<3 * S::HALF>();
+        else if (t + 1 < n_sub) wait_vmcnt<2 * S::HALF>();
+        else wait_vmcnt<0>();
+
+        // In a partial tile (only a wave's last) the rows past the sequence's
+        // end may hold any bytes -- a NaN scale among them -- which must not
+        // meet p = 0 in the context products: zero their V scales in LDS.
+        if (valid < kSub) {
+            const int row = valid + lane;
+            if (row < kSub) {
+                uint8_t* srow = vt + row * RB + D / 2;
+#pragma unroll
+                for (int i = 0; i < D / 16; i += 4) *reinterpret_cast<uint32_t*>(srow + i) = 0u;
+            }
+        }
+
+        // Everything the context reads from the V slot, into registers; the
+        // slot is then refilled with sub-tile t + 2 before the softmax and
+        // the context products run.
+        i32x2 cv[NG];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+            cv[gi] = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+                (__attribute__((address_space(3))) i32x2*)(vt + tr_off + 16 * gi));
+        // V scales of keys 4q+r and 16+4q+r, r = 0..3: all groups of each row
+        u32x4 vsa[4], vsb[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            vsa[r] = *reinterpret_cast<const u32x4*>(vt + (4 * q4 + r) * RB + D / 2);
+            vsb[r] = *reinterpret_cast<const u32x4*>(vt + (16 + 4 * q4 + r) * RB + D / 2);
+        }
+        if (t + 2 < n_sub) issue(v_pool, t + 2, v_ring);
 
         // ---- online softmax over the tile (per head = per column n16)
         // scores are finite or -inf (valid rows have finite scales), never NaN
@@ -343,25 +386,6 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
 #pragma unroll
         for (int r = 0; r < 4; ++r) pp[r] = half2_t{_Float16(p[0][r]), _Float16(p[1][r])};
 
-        // The K slot of sub-tile t is free: refill it with sub-tile t + 2.
-        if (t + 2 < n_sub) issue(k_pool, t + 2, k_ring);
-        // V of sub-tile t has landed once at most K_t+1, V_t+1, K_t+2 are outstanding.
-        if (t + 2 < n_sub) wait_vmcnt<3 * S::HALF>();
-        else if (t + 1 < n_sub) wait_vmcnt<2 * S::HALF>();
-        else wait_vmcnt<0>();
-
-        // In a partial tile (only a wave's last) the rows past the sequence's
-        // end may hold any bytes -- a NaN scale among them -- which must not
-        // meet p = 0 in the context products: zero their V scales in LDS.
-        if (valid < kSub) {
-            const int row = valid + lane;
-            if (row < kSub) {
-                uint8_t* srow = vt + row * RB + D / 2;
-#pragma unroll
-                for (int i = 0; i < D / 16; i += 4) *reinterpret_cast<uint32_t*>(srow + i) = 0u;
-            }
-        }
-
         // ---- context: per group, two 16-channel blocks.  A row n16 holds head
         // n16 (or, PACK, head n16 & 7: rows 8..15 repeat heads 0..7).  PACK
         // gives rows 0..7 the scales of the even group of a pair and rows
@@ -372,32 +396,25 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
         half8_t av;
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
-            const i32x2 cv = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
-                (__attribute__((address_space(3))) i32x2*)(vt + tr_off + 16 * gi));
             // scale pair (key 4q+r, key 16+4q+r) of group gi, r = 0..3
             if (!PACK || (gi & 1) == 0) {
                 const uint32_t psel = PACK ? psel_pair : ((gi & 1) ? 0x07060302u : 0x05040100u);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const uint32_t sa =
-                        *reinterpret_cast<const uint32_t*>(vt + (4 * q4 + r) * RB + D / 2 + 4 * (gi >> 1));
-                    const uint32_t sb =
-                        *reinterpret_cast<const uint32_t*>(vt + (16 + 4 * q4 + r) * RB + D / 2 + 4 * (gi >> 1));
-                    const uint32_t pair = __builtin_amdgcn_perm(sb, sa, psel);
+                    const uint32_t pair = __builtin_amdgcn_perm(vsb[r][gi >> 1], vsa[r][gi >> 1], psel);
                     const half2_t w = pp[r] * __builtin_bit_cast(half2_t, pair);
                     av[2 * r] = w[0];
                     av[2 * r + 1] = w[1];
                 }
                 if (PACK) ro[gi >> 1] = mfma(av, bconst, ro[gi >> 1]);
             }
-            const half8_t b0 = unpack8(uint32_t(cv[0]));
-            const half8_t b1 = unpack8(uint32_t(cv[1]));
+            const half8_t b0 = unpack8(uint32_t(cv[gi][0]));
+            const half8_t b1 = unpack8(uint32_t(cv[gi][1]));
             o[2 * gi] = mfma(av, b0, o[2 * gi]);
             if (!PACK) o[2 * gi] = mfma(av, bconst, o[2 * gi]);
             o[2 * gi + 1] = mfma(av, b1, o[2 * gi + 1]);
             if (!PACK) o[2 * gi + 1] = mfma(av, bconst, o[2 * gi + 1]);
         }
-        if (t + 2 < n_sub) issue(v_pool, t + 2, v_ring);
     }
 
     // ---- per-wave results: m (log2), z per head; o rows = heads 4*q4 + i.
