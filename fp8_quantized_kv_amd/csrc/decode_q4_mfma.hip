@@ -236,7 +236,13 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
     const int tr_key = e7 < 4 ? 4 * q4 + e7 : 16 + 4 * q4 + e7 - 4;
     const int tr_off = tr_key * RB + 8 * (n16 >> 3);
 
+    // Waves that are further along drop their issue priority, so the two
+    // workgroups on a CU stream their copies at the same pace to the end.
+    __builtin_amdgcn_s_setprio(3);
     for (int t = 0; t < n_sub; ++t) {
+        if (4 * t == n_sub) __builtin_amdgcn_s_setprio(2);
+        if (2 * t == n_sub) __builtin_amdgcn_s_setprio(1);
+        if (4 * t == 3 * n_sub) __builtin_amdgcn_s_setprio(0);
         // K of sub-tile t has landed once at most the halves issued after it
         // are outstanding: V_t, K_t+1, V_t+1.
         if (t + 1 < n_sub) wait_vmcnt<3 * S::HALF>();
