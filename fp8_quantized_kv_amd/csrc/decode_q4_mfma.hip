@@ -424,59 +424,53 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
     }
 
     // ---- per-wave results: m (log2), z per head; o rows = heads 4*q4 + i.
-    // Only the G live rows go through LDS; each (wave, head) weight
-    // exp2(m_w - M) is formed once, then every output channel is a plain
-    // sum over the waves in wave order.
+    // Each wave puts its G live head rows, m and z in its own ring (its
+    // copies have all landed and it has read them: no barrier needed before
+    // the writes); after one barrier every thread forms the weights
+    // exp2(m_w - M) of its head and sums each output channel over the waves
+    // in wave order.
+    static_assert(16 * D * 4 + 2 * 16 * 4 <= S::WAVE_LDS, "per-wave results fit the wave's ring");
     z_run = quad_sum(z_run);
-    __syncthreads();  // every wave is done with its tile buffers
-    float* wo = reinterpret_cast<float*>(smem);  // [W][16][D]
-    float* wm = wo + W * 16 * D;                 // [W][16]
-    float* wz = wm + W * 16;                     // [W][16]
-    float* wf = wz + W * 16;                     // [W][16] weights exp2(m_w - M)
-    float* wM = wf + W * 16;                     // [16]
-    float* wZ = wM + 16;                         // [16]
+    auto wo = [&](int w) { return reinterpret_cast<float*>(smem + w * S::WAVE_LDS); };  // [16][D]
+    auto wm = [&](int w) { return wo(w) + 16 * D; };                                     // [16]
+    auto wz = [&](int w) { return wo(w) + 16 * D + 16; };                                // [16]
+    {
+        float* mine = wo(wave);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 4 * q4 + i, h = PACK ? (row & 7) : row;
-        if (h < G) {
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * q4 + i, h = PACK ? (row & 7) : row;
+            if (h < G) {
 #pragma unroll
-            for (int blk = 0; blk < NB; ++blk) {
-                // PACK: group blk / 2 is read from rows 0..7 if even, 8..15 if odd
-                if (!PACK || ((blk >> 1) & 1) == (row >> 3))
-                    wo[(wave * 16 + h) * D + 16 * blk + n16] = (PACK ? o[blk][i] + ro[blk >> 2][i] : o[blk][i]) * kTwo24;
+                for (int blk = 0; blk < NB; ++blk) {
+                    // PACK: group blk / 2 is read from rows 0..7 if even, 8..15 if odd
+                    if (!PACK || ((blk >> 1) & 1) == (row >> 3))
+                        mine[h * D + 16 * blk + n16] = (PACK ? o[blk][i] + ro[blk >> 2][i] : o[blk][i]) * kTwo24;
+                }
             }
         }
-    }
-    if (lane < 16) {
-        wm[wave * 16 + lane] = n_keys > 0 ? m_run : -INFINITY;
-        wz[wave * 16 + lane] = n_keys > 0 ? z_run : 0.0f;
-    }
-    __syncthreads();
-    if (tid < G) {
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < W; ++w) M = fmaxf(M, wm[w * 16 + tid]);
-        float Z = 0.0f;
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-            const float zw = wz[w * 16 + tid];
-            const float f = zw > 0.0f ? __builtin_amdgcn_exp2f(wm[w * 16 + tid] - M) : 0.0f;
-            wf[w * 16 + tid] = f;
-            Z += zw * f;
+        if (lane < 16) {
+            wm(wave)[lane] = n_keys > 0 ? m_run : -INFINITY;
+            wz(wave)[lane] = n_keys > 0 ? z_run : 0.0f;
         }
-        wM[tid] = M;
-        wZ[tid] = Z;
     }
     __syncthreads();
     for (int i = tid; i < G * D; i += W * 64) {
         const int h = i / D, c = i % D;
-        float acc = 0.0f;
+        float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < W; ++w) acc += wo[(w * 16 + h) * D + c] * wf[w * 16 + h];
+        for (int w = 0; w < W; ++w) M = fmaxf(M, wm(w)[h]);
+        float acc = 0.0f, Z = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const float zw = wz(w)[h];
+            const float f = zw > 0.0f ? __builtin_amdgcn_exp2f(wm(w)[h] - M) : 0.0f;
+            acc += wo(w)[h * D + c] * f;
+            Z += zw * f;
+        }
         a.part_acc[((hb + h) * Sn + s) * D + c] = acc;
         if (c == 0) {
-            a.part_m[(hb + h) * Sn + s] = wM[h] * kLn2;
-            a.part_z[(hb + h) * Sn + s] = wZ[h];
+            a.part_m[(hb + h) * Sn + s] = M * kLn2;
+            a.part_z[(hb + h) * Sn + s] = Z;
         }
     }
 }
