@@ -38,8 +38,8 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); valid only for the kernel sources they were taken on
 # (keyed by the sha256 of the kernel file followed by the device-helper header it includes).
 TRAFFIC = {
-    "33961ccd9f338ee2a9d58359f07a3e8915de56588ecfb760782b2307bfadfb71": {
-        "fetch_kib": 147699.0, "write_kib": 3264.0, "fetch_scale": 2.0, "write_scale": 1.0,
+    "ebded891a27d633f3a65dd6c0463d39e247d261ab8e732823f001621c51a854a": {
+        "fetch_kib": 147702.5, "write_kib": 3264.0, "fetch_scale": 2.0, "write_scale": 1.0,
         "profile": "profiles/decode_q4_mfma_gqa_q4_262k.md"},
 }
 DECODE_SOURCES = (os.path.join("fp8_quantized_kv_amd", "csrc", "decode_q4_mfma.hip"),

@@ -13,36 +13,43 @@
 // 16-wide M dimension the score and context products become 16x16x32 MFMAs,
 // and the vector units are left with unpacking, scaling and the softmax.
 //
-// Workgroup = 4 waves = (split s, KV head g, sequence b); each wave streams
-// its own quarter of the split in 32-key sub-tiles and keeps its own online
-// softmax; the four are merged in LDS at the end into one partial.
+// Workgroup = 4 (or, for splits of at most 1024 keys, 8) waves = (split s,
+// KV head g, sequence b); each wave streams its own contiguous share of the
+// split in 32-key sub-tiles and keeps its own online softmax; the waves'
+// results are merged in LDS at the end into one partial.
 //
 // Per sub-tile:
 //  * DMA: the sub-tile's K and V rows (two 16-row page runs per pool) are
-//    copied global -> LDS with global_load_lds_dwordx4 into per-wave K and V
-//    rings of two sub-tiles each.  The next-but-one K half is issued as soon
-//    as the scores have read the current one, the V half after the context
-//    step, so about one and a half sub-tiles are in flight at all times;
-//    completion is awaited with s_waitcnt vmcnt.  The byte offsets of the
-//    wave's page runs are resolved in the prologue into lane registers (lane
-//    r holds run r), in parallel with the sequence-length load, and read
-//    back with readlane when a copy is issued.
+//    copied global -> LDS with global_load_lds_dwordx4 (non-temporal: each
+//    row is read once) into per-wave K and V rings of two sub-tiles each.
+//    A slot is refilled with sub-tile t + 2 as soon as everything the
+//    scores (K) or the context (V) read from it is in registers, so about
+//    two sub-tiles per pool are in flight; completion is awaited with
+//    s_waitcnt vmcnt.  The byte offsets of the wave's page runs are resolved
+//    in the prologue into lane registers (lane r holds run r) and read back
+//    with readlane when a copy is issued; the query is loaded after the
+//    first copies are issued, so they wait for the page table only.
 //  * Scores: for each 16-key block and 32-channel group, A = the keys' codes
 //    (lane (key n, quarter q) holds code dword 4*group + q of key n), B = the
-//    pre-scaled query split into f16 hi + lo parts (two MFMAs).  Codes enter
+//    pre-scaled query split into f16 hi + lo parts (for groups of at most 8
+//    heads, hi in B columns 0..7 and lo in 8..15: one MFMA).  Codes enter
 //    as f16 subnormals: (nibble ^ 8) masked into place is (code + 8) * 2^-24
 //    (or x16 for the high nibble of a byte, compensated in B), so unpacking a
-//    dword of 8 codes takes 6 integer ops.  The +8 offset is removed by the
+//    dword of 8 codes takes 5 integer ops.  The +8 offset is removed by the
 //    MFMA's C input (-8 * 2^-24 * sum of the group's query), and the group's
-//    fp16 scale is applied per key with one mixed-precision FMA.
+//    fp16 scale is applied per key with one mixed-precision FMA.  Both key
+//    blocks' MFMAs of a group are issued before the previous group's FMAs.
 //  * Softmax: lane (head h, quarter q) holds 8 scores of head h; the running
 //    maximum only moves when a tile exceeds it by more than 2^6, so the
 //    accumulators are rescaled a handful of times per split, not per tile.
 //  * Context: ds_read_b64_tr_b4 transposes a 16x16 tile of nibbles so that
 //    lane (channel n, quarter q) receives channel n of the 8 keys it needs
-//    as MFMA k-slots; the same 6-op unpack makes the B operand.  A = P times
-//    the keys' V scale for the group (f16), and a second MFMA against a
-//    constant B removes the +8 offset.
+//    as MFMA k-slots; the same unpack makes the B operand.  A = P times the
+//    keys' V scale (f16).  For groups of at most 8 heads A rows 8..15 repeat
+//    heads 0..7, so one A operand carries the scales of a pair of groups
+//    (rows 0..7 the even group, 8..15 the odd), and the +8 offset is summed
+//    in one accumulator per pair (an MFMA against a constant B) and added
+//    to the output once, at the end.
 #include "mfma_common.h"
 
 namespace kvq {
