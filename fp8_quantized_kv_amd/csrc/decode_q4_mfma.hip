@@ -62,10 +62,12 @@ constexpr int kSub = 32;          // keys per sub-tile
 constexpr int kMaxRuns = 128;     // 16-key runs per wave (split_keys <= 8192)
 constexpr float kRescale = 6.0f;  // log2 headroom before the running max moves
 
-template <int D, int W>
+template <int D, int W, int BITS = 4>
 struct Shape {
     static constexpr int NG = D / 32;               // 32-channel groups per row
-    static constexpr int RB = D / 2 + D / 16;       // row bytes
+    static constexpr int GB = 4 * BITS;             // code bytes of a group (4 or 8 bits per code)
+    static constexpr int SOFF = NG * GB;            // byte offset of the fp16 scales in a row
+    static constexpr int RB = SOFF + D / 16;        // row bytes
     static constexpr int NB = D / 16;               // 16-channel output blocks
     static constexpr int RUN = 16 * RB;             // bytes of 16 rows (one run)
     static constexpr int RUN_INSTR = (RUN / 16 + 63) / 64;  // 16-byte DMA instructions per run
@@ -76,9 +78,9 @@ struct Shape {
 };
 
 // Copies one 16-row run (RUN bytes) from global to LDS.
-template <int D>
+template <int D, int BITS>
 __device__ __forceinline__ void dma_run(const uint8_t* src, uint32_t lds, int lane) {
-    using S = Shape<D, 4>;  // the run geometry does not depend on the wave count
+    using S = Shape<D, 4, BITS>;  // the run geometry does not depend on the wave count
 #pragma unroll
     for (int i = 0; i < S::RUN_INSTR; ++i) {
         const int chunk = i * 64 + lane;
@@ -87,12 +89,27 @@ __device__ __forceinline__ void dma_run(const uint8_t* src, uint32_t lds, int la
     }
 }
 
-template <int D, int W, bool PACK>
-__global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __restrict__ k_pool,
+// 8 codes of an 8-bit row as MFMA k-slots (e0,e4) (e1,e5) (e2,e6) (e3,e7),
+// element e = byte e of the two dwords, each the f16 subnormal
+// (code + 128) * 2^-24: flipping bit 7 turns two's complement into offset
+// binary, and a byte permute puts each byte under a zero byte.
+__device__ __forceinline__ half8_t unpack8_b8(u32x2 w) {
+    const uint32_t x0 = w[0] ^ 0x80808080u, x1 = w[1] ^ 0x80808080u;
+    const u32x4 r = {__builtin_amdgcn_perm(x1, x0, 0x0C040C00u), __builtin_amdgcn_perm(x1, x0, 0x0C050C01u),
+                     __builtin_amdgcn_perm(x1, x0, 0x0C060C02u), __builtin_amdgcn_perm(x1, x0, 0x0C070C03u)};
+    return __builtin_bit_cast(half8_t, r);
+}
+
+// BITS = 4: the 4-bit format; BITS = 8: the 8-bit block format (byte codes,
+// same rows of codes then fp16 scales, same arithmetic with offset 128).
+template <int D, int W, bool PACK, int BITS>
+__global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(const uint8_t* __restrict__ k_pool,
                                                                   const uint8_t* __restrict__ v_pool, int H,
                                                                   int page_size, int num_pages, DecodeArgs a) {
-    using S = Shape<D, W>;
-    constexpr int NG = S::NG, RB = S::RB, NB = S::NB;
+    using S = Shape<D, W, BITS>;
+    constexpr int NG = S::NG, RB = S::RB, NB = S::NB, SOFF = S::SOFF, GB = S::GB;
+    static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
+    constexpr float kOff = BITS == 4 ? 8.0f : 128.0f;  // code offset of the f16 subnormals
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS];
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -157,8 +174,8 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
         const uint32_t dst = ring_base + uint32_t((t & 1) * S::TILE);
         const int64_t r0 = run_at(2 * t), r1 = run_at(2 * t + 1);
         wait_lgkm0();  // earlier LDS reads of this slot have completed
-        dma_run<D>(pool + r0, dst, lane);
-        dma_run<D>(pool + r1, dst + S::RUN, lane);
+        dma_run<D, BITS>(pool + r0, dst, lane);
+        dma_run<D, BITS>(pool + r1, dst + S::RUN, lane);
     };
     const uint32_t k_ring = lds0, v_ring = lds0 + uint32_t(2 * S::TILE);
     if (n_sub > 0) {
@@ -202,7 +219,7 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
             float sum = 0.0f;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const float f = (k & 2) ? 0.0625f : 1.0f;
+                const float f = (BITS == 4 && (k & 2)) ? 0.0625f : 1.0f;
                 const float v = live ? c8[order[k]] * qscale * f : 0.0f;
                 const _Float16 h = _Float16(v);
                 const _Float16 l = _Float16(v - float(h));
@@ -212,10 +229,10 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
                     bq_hi[gi][k] = h;
                     bq_lo[gi][k] = l;
                 }
-                sum += (float(h) + float(l)) * ((k & 2) ? 16.0f : 1.0f);
+                sum += (float(h) + float(l)) * ((BITS == 4 && (k & 2)) ? 16.0f : 1.0f);
             }
             sum = quad_sum(sum);
-            const float bias = -8.0f * sum / kTwo24;
+            const float bias = -kOff * sum / kTwo24;
             const float cb = (PACK && (n16 & 8)) ? 0.0f : bias;  // the offset once, in the hi column
             cbias[gi] = f32x4{cb, cb, cb, cb};
         }
@@ -223,7 +240,7 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
     // Constant B of the context offset MFMA: -8 * 2^-24 (x16 on slots 2,3,6,7).
     half8_t bconst;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) bconst[k] = _Float16((k & 2) ? -128.0f / kTwo24 : -8.0f / kTwo24);
+    for (int k = 0; k < 8; ++k) bconst[k] = _Float16((BITS == 4 && (k & 2)) ? -128.0f / kTwo24 : -kOff / kTwo24);
 
     f32x4 o[NB];
 #pragma unroll
@@ -239,9 +256,12 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
 
     // tr_b4 row address of this lane: key K(q4, e) for e = n16 & 7, where
     // K(q, e) = 4q + e (e < 4) or 16 + 4q + e - 4, at channel half n16 >> 3.
-    const int e7 = n16 & 7;
+    // (tr_b8: lane j of a 16-lane group receives byte j of the 8-byte reads of
+    // lanes 2e + (j >> 3), e = 0..7, as its element e; so lane n16 reads key
+    // K(q4, n16 >> 1) at channel offset 8 * (n16 & 1).)
+    const int e7 = BITS == 4 ? (n16 & 7) : (n16 >> 1);
     const int tr_key = e7 < 4 ? 4 * q4 + e7 : 16 + 4 * q4 + e7 - 4;
-    const int tr_off = tr_key * RB + 8 * (n16 >> 3);
+    const int tr_off = tr_key * RB + (BITS == 4 ? 8 * (n16 >> 3) : 8 * (n16 & 1));
 
     // Waves that are further along drop their issue priority, so the two
     // workgroups on a CU stream their copies at the same pace to the end.
@@ -270,13 +290,14 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    ks[kb][i] = *reinterpret_cast<const u32x4*>(kt + (16 * kb + 4 * q4 + i) * RB + D / 2);
-            uint32_t kc[2][NG];
+                    ks[kb][i] = *reinterpret_cast<const u32x4*>(kt + (16 * kb + 4 * q4 + i) * RB + SOFF);
+            using KW = std::conditional_t<BITS == 4, uint32_t, u32x2>;  // 8 codes
+            KW kc[2][NG];
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
-                    kc[kb][gi] = *reinterpret_cast<const uint32_t*>(kt + (16 * kb + n16) * RB + 16 * gi + 4 * q4);
+                    kc[kb][gi] = *reinterpret_cast<const KW*>(kt + (16 * kb + n16) * RB + GB * gi + (GB / 4) * q4);
             // Everything the scores read from the K slot is now in registers
             // (the copy's lgkmcnt wait sees to that): refill the slot with
             // sub-tile t + 2 before the MFMAs rather than after them.
@@ -289,7 +310,9 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
                 if (gi < NG) {
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb) {
-                        const half8_t av = unpack8(kc[kb][gi]);
+                        half8_t av;
+                        if constexpr (BITS == 4) av = unpack8(kc[kb][gi]);
+                        else av = unpack8_b8(kc[kb][gi]);
                         dcur[kb] = mfma(av, bq_hi[gi], cbias[gi]);
                         if (!PACK) dcur[kb] = mfma(av, bq_lo[PACK ? 0 : gi], dcur[kb]);
                     }
@@ -338,7 +361,7 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
         if (valid < kSub) {
             const int row = valid + lane;
             if (row < kSub) {
-                uint8_t* srow = vt + row * RB + D / 2;
+                uint8_t* srow = vt + row * RB + SOFF;
 #pragma unroll
                 for (int i = 0; i < D / 16; i += 4) *reinterpret_cast<uint32_t*>(srow + i) = 0u;
             }
@@ -347,17 +370,25 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
         // Everything the context reads from the V slot, into registers; the
         // slot is then refilled with sub-tile t + 2 before the softmax and
         // the context products run.
-        i32x2 cv[NG];
+        i32x2 cv[NG][BITS == 4 ? 1 : 2];
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi)
-            cv[gi] = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
-                (__attribute__((address_space(3))) i32x2*)(vt + tr_off + 16 * gi));
+        for (int gi = 0; gi < NG; ++gi) {
+            if constexpr (BITS == 4) {
+                cv[gi][0] = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+                    (__attribute__((address_space(3))) i32x2*)(vt + tr_off + 16 * gi));
+            } else {
+#pragma unroll
+                for (int hb2 = 0; hb2 < 2; ++hb2)
+                    cv[gi][hb2 % (BITS == 4 ? 1 : 2)] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) i32x2*)(vt + tr_off + 32 * gi + 16 * hb2));
+            }
+        }
         // V scales of keys 4q+r and 16+4q+r, r = 0..3: all groups of each row
         u32x4 vsa[4], vsb[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            vsa[r] = *reinterpret_cast<const u32x4*>(vt + (4 * q4 + r) * RB + D / 2);
-            vsb[r] = *reinterpret_cast<const u32x4*>(vt + (16 + 4 * q4 + r) * RB + D / 2);
+            vsa[r] = *reinterpret_cast<const u32x4*>(vt + (4 * q4 + r) * RB + SOFF);
+            vsb[r] = *reinterpret_cast<const u32x4*>(vt + (16 + 4 * q4 + r) * RB + SOFF);
         }
         if (t + 2 < n_sub) issue(v_pool, t + 2, v_ring);
 
@@ -392,8 +423,9 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[kb][i] = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], kTwo24, (i & 1) ? nm4 : nm0));
-                z_run = (i & 1) ? fmaf(16.0f, p[kb][i], z_run) : z_run + p[kb][i];
+                const bool x16 = BITS == 4 && (i & 1);  // 4-bit slots 2,3,6,7 carry x16 in B
+                p[kb][i] = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], kTwo24, x16 ? nm4 : nm0));
+                z_run = x16 ? fmaf(16.0f, p[kb][i], z_run) : z_run + p[kb][i];
             }
         half2_t pp[4];
 #pragma unroll
@@ -421,8 +453,14 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
                 }
                 if (PACK) ro[gi >> 1] = mfma(av, bconst, ro[gi >> 1]);
             }
-            const half8_t b0 = unpack8(uint32_t(cv[gi][0]));
-            const half8_t b1 = unpack8(uint32_t(cv[gi][1]));
+            half8_t b0, b1;
+            if constexpr (BITS == 4) {
+                b0 = unpack8(uint32_t(cv[gi][0][0]));
+                b1 = unpack8(uint32_t(cv[gi][0][1]));
+            } else {
+                b0 = unpack8_b8(__builtin_bit_cast(u32x2, cv[gi][0]));
+                b1 = unpack8_b8(__builtin_bit_cast(u32x2, cv[gi][BITS == 4 ? 0 : 1]));
+            }
             o[2 * gi] = mfma(av, b0, o[2 * gi]);
             if (!PACK) o[2 * gi] = mfma(av, bconst, o[2 * gi]);
             o[2 * gi + 1] = mfma(av, b1, o[2 * gi + 1]);
@@ -486,26 +524,36 @@ __global__ __launch_bounds__(W * 64, 2) void decode_q4_mfma(const uint8_t* __res
 
 bool decode_q4_mfma_supported(const Q4Pool& pool, const DecodeArgs& a) {
     const int G = a.n_q_heads / pool.n_kv_heads;
-    return (pool.head_dim == 128 || pool.head_dim == 256) && G >= 1 && G <= 16 && pool.page_size % 16 == 0 &&
-           a.split_keys % 128 == 0 && a.split_keys / 4 <= 16 * kMaxRuns;
+    // 8-bit rows are 272 bytes at head_dim 256 (16-byte aligned scale chunks)
+    const bool dims = pool.bits == 4 ? (pool.head_dim == 128 || pool.head_dim == 256)
+                                     : (pool.bits == 8 && pool.head_dim == 256);
+    return dims && G >= 1 && G <= 16 && pool.page_size % 16 == 0 && a.split_keys % 128 == 0 &&
+           a.split_keys / 4 <= 16 * kMaxRuns;
 }
 
 // Workgroups of 4 waves, each streaming a quarter of a split of more than
 // 1024 keys; splits of 512 or 1024 keys (short contexts, where fewer and
 // larger splits would leave CUs idle) are shared by 8 waves, so each wave
 // has half as many tiles and a short context's copies are all in flight at
-// once.  The choice depends on split_keys alone, never on the batch, so a
-// sequence's partials do not depend on the sequences beside it.
+// once.  The 8-bit format always uses 4 waves: its rings take 34 KB per
+// wave.  The choice depends on split_keys and the format alone, never on the
+// batch, so a sequence's partials do not depend on the sequences beside it.
 hipError_t launch_decode_q4_mfma(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s) {
     const dim3 grid(unsigned(a.n_splits), unsigned(pool.n_kv_heads), unsigned(a.batch));
     const bool eight = a.split_keys <= kEightWaveSplit;
     const bool pack = a.n_q_heads / pool.n_kv_heads <= 8;
-#define KVQ_LAUNCH(D_, W_, P_)                                                                             \
-    decode_q4_mfma<D_, W_, P_><<<grid, dim3((W_) * 64), 0, s>>>(pool.k, pool.v, pool.n_kv_heads,          \
-                                                                 pool.page_size, pool.num_pages, a)
-#define KVQ_LAUNCH_W(D_, P_)          \
-    if (eight) KVQ_LAUNCH(D_, 8, P_); \
-    else KVQ_LAUNCH(D_, 4, P_)
+#define KVQ_LAUNCH(D_, W_, P_, B_)                                                                             \
+    decode_q4_mfma<D_, W_, P_, B_><<<grid, dim3((W_) * 64), 0, s>>>(pool.k, pool.v, pool.n_kv_heads,          \
+                                                                     pool.page_size, pool.num_pages, a)
+#define KVQ_LAUNCH_W(D_, P_)             \
+    if (eight) KVQ_LAUNCH(D_, 8, P_, 4); \
+    else KVQ_LAUNCH(D_, 4, P_, 4)
+    if (pool.bits == 8) {
+        if (pool.head_dim != 256) return hipErrorInvalidValue;
+        if (pack) KVQ_LAUNCH(256, 4, true, 8);
+        else KVQ_LAUNCH(256, 4, false, 8);
+        return hipGetLastError();
+    }
     switch (pool.head_dim) {
         case 128:
             if (pack) { KVQ_LAUNCH_W(128, true); }

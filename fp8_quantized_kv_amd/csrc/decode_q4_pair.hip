@@ -413,7 +413,8 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
 bool decode_q4_pair_supported(const Q4Pool& pool, const DecodeArgs& a) {
     const int G = a.n_q_heads / pool.n_kv_heads;
     const int64_t rows = int64_t(pool.num_pages) * pool.n_kv_heads * pool.page_size;
-    return pool.head_dim == kD && G >= 1 && G <= 8 && pool.page_size % 16 == 0 && a.split_keys % (32 * kPairs) == 0 &&
+    return pool.bits == 4 && pool.head_dim == kD && G >= 1 && G <= 8 && pool.page_size % 16 == 0 &&
+           a.split_keys % (32 * kPairs) == 0 &&
            a.split_keys <= kMaxSplit && rows <= (int64_t(1) << 32);
 }
 

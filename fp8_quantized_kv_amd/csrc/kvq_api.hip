@@ -181,8 +181,8 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_h
                       kvq_num_splits(max_seq_len, split_keys), sm_scale, split_keys, part_acc, part_m, part_z};
     if (is_h32(cache->format)) {
         const kvq::Q4Pool pool = q4_pool(cache);
-        if (pool.bits != 4) return launched(kvq::launch_decode_q4_simple(pool, a, stream));
-        if (kvq::decode_q4_pair_supported(pool, a)) return launched(kvq::launch_decode_q4_pair(pool, a, stream));
+        if (pool.bits == 4 && kvq::decode_q4_pair_supported(pool, a))
+            return launched(kvq::launch_decode_q4_pair(pool, a, stream));
         if (kvq::decode_q4_mfma_supported(pool, a)) return launched(kvq::launch_decode_q4_mfma(pool, a, stream));
         return launched(kvq::launch_decode_q4_simple(pool, a, stream));
     }
