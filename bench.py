@@ -38,8 +38,8 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); valid only for the kernel sources they were taken on
 # (keyed by the sha256 of the kernel file followed by the device-helper header it includes).
 TRAFFIC = {
-    "ebded891a27d633f3a65dd6c0463d39e247d261ab8e732823f001621c51a854a": {
-        "fetch_kib": 147702.5, "write_kib": 3264.0, "fetch_scale": 2.0, "write_scale": 1.0,
+    "0af5eebda9609ba7a0c0c2a0b736a5ee3c911a851e01c7faa2389626c6463c6b": {
+        "fetch_kib": 147702.0, "write_kib": 3264.0, "fetch_scale": 2.0, "write_scale": 1.0,
         "profile": "profiles/decode_q4_mfma_gqa_q4_262k.md"},
 }
 DECODE_SOURCES = (os.path.join("fp8_quantized_kv_amd", "csrc", "decode_q4_mfma.hip"),
