@@ -14,9 +14,10 @@ uninstrumented steps; decode + merge alone per layer; the step replayed as
 one HIP graph per layer (each replay first checked against the eager step's
 outputs, bit for bit; not faster than the eager launches, which already
 keep the queue full); a roofline object for the
-decode kernel, from further eager steps whose decode launches are bracketed
-by HIP events on the stream they run on (event records stall the queue
-briefly, so those steps are kept out of the step time); side measurements
+decode kernel, whose average launch is timed by HIP events on the stream it
+runs on around steps of decode launches alone, back to back (region time /
+launches; the figure with an event pair around every launch, which adds the
+event records' own cost, is reported beside it); side measurements
 of the 32K 4-bit, the ragged-batch and the 262K fp8-latent workloads; and
 the CPU oracle timed on a bounded sample of the headline workload.
 """
@@ -505,10 +506,17 @@ def measure(b, steps, warmup):
     ms_graph, _ = time_graph(g, steps, warmup)
     del g
     torch.cuda.synchronize()
-    dec_ms = time_decode(b, steps)
-    kvb = b.kv_bytes_per_layer
     L = b.w.n_layers
+    # The decode's average launch: steps of decode launches alone, back to back
+    # between two events (region time / launches; inter-launch gaps included).
+    ms_dec, _ = time_steps(b, steps, warmup, only=(b.DECODE,))
+    dec_ms = ms_dec / L
+    # The same launches each bracketed by its own event pair (adds the event
+    # records' own cost, about 1.5 us per launch).
+    dec_ms_bracketed = time_decode(b, steps)
+    kvb = b.kv_bytes_per_layer
     r = {"ms_per_step": ms_step, "us_per_layer": ms_step * 1e3 / L, "decode_us": dec_ms * 1e3,
+         "decode_us_bracketed": dec_ms_bracketed * 1e3,
          "decode_merge_us_per_layer": ms_dm * 1e3 / L, "graph_us_per_layer": ms_graph * 1e3 / L,
          "step_gbs": kvb * L / (ms_step * 1e-3) / 1e9, "decode_gbs": kvb / (dec_ms * 1e-3) / 1e9, "wall_s": wall}
     if b.flops_per_layer:
@@ -621,6 +629,7 @@ def main():
         "roofline": {"kernel": "kvq_decode_attn (4-bit split-K)", "bound": "hbm",
                      "achieved": round(m["decode_gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(m["decode_gbs"] / HBM_PEAK_GBS, 4), "avg_launch_us": round(m["decode_us"], 3),
+                     "avg_launch_us_event_pair_each": round(m["decode_us_bracketed"], 3),
                      "traffic": decode_traffic()},
         "wall_s": round(m["wall_s"], 3),
     }
