@@ -337,8 +337,9 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     // PACK: column n16 ^ 8 holds the other part of the same head
-                    // (DPP row rotate by 8); a + b = b + a, so both columns agree.
-                    sc[kb][i] = PACK ? acc[kb][i] + row_xor8(acc[kb][i]) : acc[kb][i];  // log2 units / 2^24
+                    // (DPP row rotate by 8, folded into the add as its first
+                    // operand); a + b = b + a, so both columns agree.
+                    sc[kb][i] = PACK ? row_xor8(acc[kb][i]) + acc[kb][i] : acc[kb][i];  // log2 units / 2^24
                 }
         }
         if (valid < kSub) {  // only the last tile of a wave can be partial

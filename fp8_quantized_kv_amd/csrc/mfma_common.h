@@ -110,9 +110,11 @@ __device__ __forceinline__ float quad_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// x of lane l ^ 8 within each 16-lane row (DPP row_ror:8).
+// x of lane l ^ 8 within each 16-lane row (DPP row_ror:8; every lane is
+// written, so bound_ctrl has no effect -- it lets the move fold into the
+// instruction that uses it).
 __device__ __forceinline__ float row_xor8(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, true));
 }
 
 }  // namespace mx
