@@ -355,55 +355,48 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
         if (t + 2 < n_sub) issue(v_pool, t + 2, v_ring);
     }
 
-    // ---- combine the four pairs: live rows (heads) through LDS, weights
-    // exp2(m_p - M) formed once per (pair, head), sums in pair order.
+    // ---- combine the four pairs.  Each wave leaves its live head rows (its
+    // channel half) and, in half 0, m and z in its own V ring (read by no
+    // other wave); after one barrier every thread forms its head's weights
+    // exp2(m_p - M) and sums each channel over the pairs in pair order.
+    static_assert(kEpiRows * 128 * 4 + 2 * 16 * 4 <= 2 * kSlot, "per-wave results fit the wave's V ring");
     z_run = quad_sum(z_run);
-    __syncthreads();  // every wave is done with its rings
-    float* wo = reinterpret_cast<float*>(smem);  // [pairs][8][256]
-    float* wm = wo + kPairs * kEpiRows * kD;     // [pairs][16]
-    float* wz = wm + kPairs * 16;
-    float* wf = wz + kPairs * 16;
-    float* wM = wf + kPairs * 16;                // [16]
-    float* wZ = wM + 16;
+    auto wo = [&](int w) { return reinterpret_cast<float*>(smem + w * kWaveLds + 2 * kSlot); };  // [8][128]
+    auto wm = [&](int w) { return wo(w) + kEpiRows * 128; };                                       // [16]
+    auto wz = [&](int w) { return wo(w) + kEpiRows * 128 + 16; };                                  // [16]
+    {
+        float* mine = wo(wave);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 4 * q4 + i;
-        if (row < G) {
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * q4 + i;
+            if (row < G) {
 #pragma unroll
-            for (int blk = 0; blk < 8; ++blk)
-                wo[(pair * kEpiRows + row) * kD + 128 * h + 16 * blk + n16] = o[blk][i] * kTwo24;
+                for (int blk = 0; blk < 8; ++blk) mine[row * 128 + 16 * blk + n16] = o[blk][i] * kTwo24;
+            }
         }
-    }
-    if (h == 0 && lane < 16) {
-        wm[pair * 16 + lane] = n_keys > 0 ? m_run : -INFINITY;
-        wz[pair * 16 + lane] = n_keys > 0 ? z_run : 0.0f;
-    }
-    __syncthreads();
-    if (tid < G) {
-        float M = -INFINITY;
-#pragma unroll
-        for (int q = 0; q < kPairs; ++q) M = fmaxf(M, wm[q * 16 + tid]);
-        float Z = 0.0f;
-#pragma unroll
-        for (int q = 0; q < kPairs; ++q) {
-            const float zq = wz[q * 16 + tid];
-            const float f = zq > 0.0f ? __builtin_amdgcn_exp2f(wm[q * 16 + tid] - M) : 0.0f;
-            wf[q * 16 + tid] = f;
-            Z += zq * f;
+        if (h == 0 && lane < 16) {
+            wm(wave)[lane] = n_keys > 0 ? m_run : -INFINITY;
+            wz(wave)[lane] = n_keys > 0 ? z_run : 0.0f;
         }
-        wM[tid] = M;
-        wZ[tid] = Z;
     }
     __syncthreads();
     for (int i = tid; i < G * kD; i += kWaves * 64) {
-        const int hd = i / kD, c = i % kD;
-        float acc = 0.0f;
+        const int hd = i / kD, c = i % kD, half = c >> 7;
+        float M = -INFINITY;
 #pragma unroll
-        for (int q = 0; q < kPairs; ++q) acc += wo[(q * kEpiRows + hd) * kD + c] * wf[q * 16 + hd];
+        for (int q = 0; q < kPairs; ++q) M = fmaxf(M, wm(2 * q)[hd]);
+        float acc = 0.0f, Z = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kPairs; ++q) {
+            const float zq = wz(2 * q)[hd];
+            const float f = zq > 0.0f ? __builtin_amdgcn_exp2f(wm(2 * q)[hd] - M) : 0.0f;
+            acc += wo(2 * q + half)[hd * 128 + (c & 127)] * f;
+            Z += zq * f;
+        }
         a.part_acc[((hb + hd) * Sn + s) * kD + c] = acc;
         if (c == 0) {
-            a.part_m[(hb + hd) * Sn + s] = wM[hd] * kLn2;
-            a.part_z[(hb + hd) * Sn + s] = wZ[hd];
+            a.part_m[(hb + hd) * Sn + s] = M * kLn2;
+            a.part_z[(hb + hd) * Sn + s] = Z;
         }
     }
 }
