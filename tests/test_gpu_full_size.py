@@ -1,4 +1,5 @@
-"""GPU parity at the workloads' full sizes, in the launch configuration the
+"""GPU parity at the workloads' full sizes (4-bit at 32K and 262K, the 8- and
+6-bit formats at 32K), in the launch configuration the
 benchmark times (each workload's split_keys).  Codes are compared in full;
 attention is compared for every head (4-bit) or a sample of heads (fp8
 latent, whose fp64 oracle is slow at 262K positions)."""
@@ -24,7 +25,7 @@ def _say(*a):
     print(*a, flush=True)
 
 
-@pytest.mark.parametrize("name", ["gqa_q4_32k", "gqa_q4_262k"])
+@pytest.mark.parametrize("name", ["gqa_q4_32k", "gqa_q4_262k", "gqa_q8_32k", "gqa_q6_32k"])
 def test_dense_gqa_full(kvq, name):
     w = wl.WORKLOADS[name]
     _say(f"full {name}: T={w.seq_len} split={w.split_keys}")
