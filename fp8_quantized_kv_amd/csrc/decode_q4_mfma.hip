@@ -65,7 +65,7 @@ constexpr float kRescale = 6.0f;  // log2 headroom before the running max moves
 template <int D, int W, int BITS = 4>
 struct Shape {
     static constexpr int NG = D / 32;               // 32-channel groups per row
-    static constexpr int GB = 4 * BITS;             // code bytes of a group (4 or 8 bits per code)
+    static constexpr int GB = 4 * BITS;             // code bytes of a group (16, 24 or 32)
     static constexpr int SOFF = NG * GB;            // byte offset of the fp16 scales in a row
     static constexpr int RB = SOFF + D / 16;        // row bytes
     static constexpr int NB = D / 16;               // 16-channel output blocks
@@ -100,16 +100,46 @@ __device__ __forceinline__ half8_t unpack8_b8(u32x2 w) {
     return __builtin_bit_cast(half8_t, r);
 }
 
+// 8 codes of a 6-bit row as MFMA k-slots (c0,c4) (c1,c5)x16 (c2,c6) (c3,c7)x16
+// (the 4-bit order), each the f16 subnormal (code + 32) * 2^-24 (x16 where
+// marked): w holds the codes' low nibbles laid out as 4-bit codes (unsigned
+// here), hb their high two-bit fields (code i at bits 2i..2i+1; flipping
+// bit 1 of a field turns two's complement into offset binary), placed above
+// each nibble.
+__device__ __forceinline__ half8_t unpack8_b6(uint32_t w, uint32_t hb) {
+    const uint32_t w2 = w >> 8;
+    const uint32_t e = __builtin_amdgcn_perm(0u, hb ^ 0xAAAAu, 0x0C010C00u);  // fields of codes 0-3 | 4-7 << 16
+    const u32x4 r = {(w & 0x000F000Fu) | ((e << 4) & 0x00300030u), (w & 0x00F000F0u) | ((e << 6) & 0x03000300u),
+                     (w2 & 0x000F000Fu) | (e & 0x00300030u), (w2 & 0x00F000F0u) | ((e << 2) & 0x03000300u)};
+    return __builtin_bit_cast(half8_t, r);
+}
+
+// The same for the context operand: nib = 8 keys' low nibbles of one channel
+// (element e in nibble e, as ds_read_b64_tr_b4 delivers them), h0 / h1 = the
+// same keys' two-bit fields, offset binary, in bits 0..1 of byte e of h0
+// (e < 4) or of byte e - 4 of h1.
+__device__ __forceinline__ half8_t unpack8_b6_ctx(uint32_t nib, uint32_t h0, uint32_t h1) {
+    const uint32_t n2 = nib >> 8;
+    const u32x4 r = {(__builtin_amdgcn_perm(h1, h0, 0x0C040C00u) << 4) | (nib & 0x000F000Fu),
+                     (__builtin_amdgcn_perm(h1, h0, 0x0C050C01u) << 8) | (nib & 0x00F000F0u),
+                     (__builtin_amdgcn_perm(h1, h0, 0x0C060C02u) << 4) | (n2 & 0x000F000Fu),
+                     (__builtin_amdgcn_perm(h1, h0, 0x0C070C03u) << 8) | (n2 & 0x00F000F0u)};
+    return __builtin_bit_cast(half8_t, r);
+}
+
 // BITS = 4: the 4-bit format; BITS = 8: the 8-bit block format (byte codes,
-// same rows of codes then fp16 scales, same arithmetic with offset 128).
+// same rows of codes then fp16 scales, same arithmetic with offset 128);
+// BITS = 6: the 6-bit block format (per group 16 bytes of low nibbles laid
+// out as the 4-bit codes, then 8 bytes of high two-bit fields; offset 32).
 template <int D, int W, bool PACK, int BITS>
 __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(const uint8_t* __restrict__ k_pool,
                                                                   const uint8_t* __restrict__ v_pool, int H,
                                                                   int page_size, int num_pages, DecodeArgs a) {
     using S = Shape<D, W, BITS>;
     constexpr int NG = S::NG, RB = S::RB, NB = S::NB, SOFF = S::SOFF, GB = S::GB;
-    static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
-    constexpr float kOff = BITS == 4 ? 8.0f : 128.0f;  // code offset of the f16 subnormals
+    static_assert(BITS == 4 || BITS == 6 || BITS == 8, "4-, 6- or 8-bit codes");
+    constexpr float kOff = BITS == 4 ? 8.0f : (BITS == 6 ? 32.0f : 128.0f);  // code offset of the f16 subnormals
+    constexpr bool X16 = BITS != 8;  // 4 and 6 bits: k-slots 2,3,6,7 carry x16 (nibble in bits 4..7)
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS];
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -219,7 +249,7 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
             float sum = 0.0f;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const float f = (BITS == 4 && (k & 2)) ? 0.0625f : 1.0f;
+                const float f = (X16 && (k & 2)) ? 0.0625f : 1.0f;
                 const float v = live ? c8[order[k]] * qscale * f : 0.0f;
                 const _Float16 h = _Float16(v);
                 const _Float16 l = _Float16(v - float(h));
@@ -229,7 +259,7 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
                     bq_hi[gi][k] = h;
                     bq_lo[gi][k] = l;
                 }
-                sum += (float(h) + float(l)) * ((BITS == 4 && (k & 2)) ? 16.0f : 1.0f);
+                sum += (float(h) + float(l)) * ((X16 && (k & 2)) ? 16.0f : 1.0f);
             }
             sum = quad_sum(sum);
             const float bias = -kOff * sum / kTwo24;
@@ -240,7 +270,7 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
     // Constant B of the context offset MFMA: -8 * 2^-24 (x16 on slots 2,3,6,7).
     half8_t bconst;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) bconst[k] = _Float16((BITS == 4 && (k & 2)) ? -128.0f / kTwo24 : -kOff / kTwo24);
+    for (int k = 0; k < 8; ++k) bconst[k] = _Float16((X16 && (k & 2)) ? -16.0f * kOff / kTwo24 : -kOff / kTwo24);
 
     f32x4 o[NB];
 #pragma unroll
@@ -259,9 +289,18 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
     // (tr_b8: lane j of a 16-lane group receives byte j of the 8-byte reads of
     // lanes 2e + (j >> 3), e = 0..7, as its element e; so lane n16 reads key
     // K(q4, n16 >> 1) at channel offset 8 * (n16 & 1).)
-    const int e7 = BITS == 4 ? (n16 & 7) : (n16 >> 1);
+    const int e7 = BITS != 8 ? (n16 & 7) : (n16 >> 1);
     const int tr_key = e7 < 4 ? 4 * q4 + e7 : 16 + 4 * q4 + e7 - 4;
-    const int tr_off = tr_key * RB + (BITS == 4 ? 8 * (n16 >> 3) : 8 * (n16 & 1));
+    const int tr_off = tr_key * RB + (BITS != 8 ? 8 * (n16 >> 3) : 8 * (n16 & 1));
+    // 6 bits: a tr_b8 read of the high-field block (8 bytes per key) whose
+    // two source lanes 2e, 2e + 1 both read key K(q4, e) leaves byte n16 & 7
+    // of each key's block in lane n16; lane n16 of block b takes it from lane
+    // 4b + (n16 >> 2) of its 16 (byte 4b + (n16 >> 2) holds its channel's field,
+    // at bits 2 * (n16 & 3)).
+    const int e8 = n16 >> 1;
+    const int hi_off = (e8 < 4 ? 4 * q4 + e8 : 16 + 4 * q4 + e8 - 4) * RB + 16;
+    const int hi_src0 = 4 * ((lane & ~15) + (n16 >> 2));  // ds_bpermute byte address, block 0
+    const uint32_t hi_shift = 2u * uint32_t(n16 & 3);
 
     // Waves that are further along drop their issue priority, so the two
     // workgroups on a CU stream their copies at the same pace to the end.
@@ -291,13 +330,23 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     ks[kb][i] = *reinterpret_cast<const u32x4*>(kt + (16 * kb + 4 * q4 + i) * RB + SOFF);
-            using KW = std::conditional_t<BITS == 4, uint32_t, u32x2>;  // 8 codes
+            // 8 codes: 4 bits a dword of nibbles, 8 bits two dwords of bytes,
+            // 6 bits a dword of low nibbles and 16 bits of high fields
+            using KW = std::conditional_t<BITS == 8, u32x2, uint32_t>;
             KW kc[2][NG];
+            uint32_t kh[2][BITS == 6 ? NG : 1];
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-                    kc[kb][gi] = *reinterpret_cast<const KW*>(kt + (16 * kb + n16) * RB + GB * gi + (GB / 4) * q4);
+                for (int kb = 0; kb < 2; ++kb) {
+                    const uint8_t* rowp = kt + (16 * kb + n16) * RB + GB * gi;
+                    if constexpr (BITS == 6) {
+                        kc[kb][gi] = *reinterpret_cast<const uint32_t*>(rowp + 4 * q4);
+                        kh[kb][gi] = *reinterpret_cast<const uint16_t*>(rowp + 16 + 2 * q4);
+                    } else {
+                        kc[kb][gi] = *reinterpret_cast<const KW*>(rowp + (GB / 4) * q4);
+                    }
+                }
             // Everything the scores read from the K slot is now in registers
             // (the copy's lgkmcnt wait sees to that): refill the slot with
             // sub-tile t + 2 before the MFMAs rather than after them.
@@ -312,6 +361,7 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
                     for (int kb = 0; kb < 2; ++kb) {
                         half8_t av;
                         if constexpr (BITS == 4) av = unpack8(kc[kb][gi]);
+                        else if constexpr (BITS == 6) av = unpack8_b6(kc[kb][gi], kh[kb][BITS == 6 ? gi : 0]);
                         else av = unpack8_b8(kc[kb][gi]);
                         dcur[kb] = mfma(av, bq_hi[gi], cbias[gi]);
                         if (!PACK) dcur[kb] = mfma(av, bq_lo[PACK ? 0 : gi], dcur[kb]);
@@ -377,6 +427,11 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
             if constexpr (BITS == 4) {
                 cv[gi][0] = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
                     (__attribute__((address_space(3))) i32x2*)(vt + tr_off + 16 * gi));
+            } else if constexpr (BITS == 6) {
+                cv[gi][0] = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+                    (__attribute__((address_space(3))) i32x2*)(vt + tr_off + GB * gi));
+                cv[gi][1] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) i32x2*)(vt + hi_off + GB * gi));
             } else {
 #pragma unroll
                 for (int hb2 = 0; hb2 < 2; ++hb2)
@@ -424,7 +479,7 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool x16 = BITS == 4 && (i & 1);  // 4-bit slots 2,3,6,7 carry x16 in B
+                const bool x16 = X16 && (i & 1);  // 4- and 6-bit slots 2,3,6,7 carry x16 in B
                 p[kb][i] = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], kTwo24, x16 ? nm4 : nm0));
                 z_run = x16 ? fmaf(16.0f, p[kb][i], z_run) : z_run + p[kb][i];
             }
@@ -458,6 +513,20 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
             if constexpr (BITS == 4) {
                 b0 = unpack8(uint32_t(cv[gi][0][0]));
                 b1 = unpack8(uint32_t(cv[gi][0][1]));
+            } else if constexpr (BITS == 6) {
+                // high fields of block b from lane 4b + (n16 >> 2) of this 16,
+                // the field of channel n16 & 3 of its byte, offset binary
+                uint32_t hf[2][2];
+#pragma unroll
+                for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        const uint32_t v = uint32_t(
+                            __builtin_amdgcn_ds_bpermute(hi_src0 + 16 * b2, int(cv[gi][BITS == 6 ? 1 : 0][k])));
+                        hf[b2][k] = ((v >> hi_shift) & 0x03030303u) ^ 0x02020202u;
+                    }
+                b0 = unpack8_b6_ctx(uint32_t(cv[gi][0][0]), hf[0][0], hf[0][1]);
+                b1 = unpack8_b6_ctx(uint32_t(cv[gi][0][1]), hf[1][0], hf[1][1]);
             } else {
                 b0 = unpack8_b8(__builtin_bit_cast(u32x2, cv[gi][0]));
                 b1 = unpack8_b8(__builtin_bit_cast(u32x2, cv[gi][BITS == 4 ? 0 : 1]));
@@ -525,9 +594,9 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
 
 bool decode_q4_mfma_supported(const Q4Pool& pool, const DecodeArgs& a) {
     const int G = a.n_q_heads / pool.n_kv_heads;
-    // 8-bit rows are 272 bytes at head_dim 256 (16-byte aligned scale chunks)
+    // 8- and 6-bit rows are 272 and 208 bytes at head_dim 256 (16-byte aligned scale chunks)
     const bool dims = pool.bits == 4 ? (pool.head_dim == 128 || pool.head_dim == 256)
-                                     : (pool.bits == 8 && pool.head_dim == 256);
+                                     : ((pool.bits == 8 || pool.bits == 6) && pool.head_dim == 256);
     return dims && G >= 1 && G <= 16 && pool.page_size % 16 == 0 && a.split_keys % 128 == 0 &&
            a.split_keys / 4 <= 16 * kMaxRuns;
 }
@@ -536,8 +605,8 @@ bool decode_q4_mfma_supported(const Q4Pool& pool, const DecodeArgs& a) {
 // 1024 keys; splits of 512 or 1024 keys (short contexts, where fewer and
 // larger splits would leave CUs idle) are shared by 8 waves, so each wave
 // has half as many tiles and a short context's copies are all in flight at
-// once.  The 8-bit format always uses 4 waves: its rings take 34 KB per
-// wave.  The choice depends on split_keys and the format alone, never on the
+// once.  The 8- and 6-bit formats always use 4 waves: their rings take 34 and
+// 26 KB per wave.  The choice depends on split_keys and the format alone, never on the
 // batch, so a sequence's partials do not depend on the sequences beside it.
 hipError_t launch_decode_q4_mfma(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s) {
     const dim3 grid(unsigned(a.n_splits), unsigned(pool.n_kv_heads), unsigned(a.batch));
@@ -549,10 +618,15 @@ hipError_t launch_decode_q4_mfma(const Q4Pool& pool, const DecodeArgs& a, hipStr
 #define KVQ_LAUNCH_W(D_, P_)             \
     if (eight) KVQ_LAUNCH(D_, 8, P_, 4); \
     else KVQ_LAUNCH(D_, 4, P_, 4)
-    if (pool.bits == 8) {
+    if (pool.bits == 8 || pool.bits == 6) {
         if (pool.head_dim != 256) return hipErrorInvalidValue;
-        if (pack) KVQ_LAUNCH(256, 4, true, 8);
-        else KVQ_LAUNCH(256, 4, false, 8);
+        if (pool.bits == 8) {
+            if (pack) KVQ_LAUNCH(256, 4, true, 8);
+            else KVQ_LAUNCH(256, 4, false, 8);
+        } else {
+            if (pack) KVQ_LAUNCH(256, 4, true, 6);
+            else KVQ_LAUNCH(256, 4, false, 6);
+        }
         return hipGetLastError();
     }
     switch (pool.head_dim) {

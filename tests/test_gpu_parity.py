@@ -80,10 +80,10 @@ def test_store_blk_bit_exact(kvq, bits, D, dtype):
 
 @pytest.mark.parametrize("bits", [6, 8])
 def test_blk_decode_matches_oracle(kvq, bits):
-    """Decode + merge over the 6- and 8-bit caches (6 bits: the plain kernel;
-    8 bits at head_dim 256: the matrix-core kernel): a ragged batch with tails
-    and an empty sequence, splits of 512 and 2048, the one-launch store +
-    rotation of a new token, and batch invariance."""
+    """Decode + merge over the 6- and 8-bit caches (the matrix-core kernel at
+    head_dim 256): a ragged batch with tails and an empty sequence, splits of
+    512 and 2048, the one-launch store + rotation of a new token, and batch
+    invariance."""
     import fp8_quantized_kv_amd as kvq_mod
     w = wl.shrink(wl.RAGGED, prefill_chunk=0, bits=bits)
     lens = [3000, 17, 0, 1100]
@@ -122,19 +122,21 @@ def test_blk_decode_matches_oracle(kvq, bits):
     assert torch.equal(case.cache.k_pool, fused_k) and torch.equal(case.cache.v_pool, fused_v)
 
 
+@pytest.mark.parametrize("bits", [6, 8])
 @pytest.mark.parametrize("G", [1, 6, 8, 12])
-def test_blk8_mfma_edges(kvq, G):
-    """The 8-bit format on the matrix-core kernel: group sizes on both sides
-    of the packed hi/lo columns (G <= 8 packed, 12 not), lengths at sub-tile,
-    16-row run and wave-quarter boundaries, splits of 512, 1024 and 2048 keys."""
-    w = wl.shrink(wl.RAGGED, prefill_chunk=0, bits=8, n_q_heads=4 * G)
+def test_blk_mfma_edges(kvq, G, bits):
+    """The 8- and 6-bit formats on the matrix-core kernel: group sizes on both
+    sides of the packed hi/lo columns (G <= 8 packed, 12 not), lengths at
+    sub-tile, 16-row run and wave-quarter boundaries, splits of 512, 1024 and
+    2048 keys."""
+    w = wl.shrink(wl.RAGGED, prefill_chunk=0, bits=bits, n_q_heads=4 * G)
     lens = [1, 31, 32, 33, 129, 1024 + 16, 2048 + 5]
     case = Q4Case(w, lens)
     ro, rl = case.ref_attention()
     for split in (512, 1024, 2048):
         o, lse = case.gpu_attention(split)
         err = rel_err(o, ro)
-        _say(f"  G={G} split={split} max_rel_err={err.max():.2e}")
+        _say(f"  bits={bits} G={G} split={split} max_rel_err={err.max():.2e}")
         assert err.max() < TOL
         fin = np.isfinite(rl)
         assert np.array_equal(fin, np.isfinite(lse)) and np.max(np.abs(lse[fin] - rl[fin])) < 1e-3 * max(1.0, np.abs(rl[fin]).max())
