@@ -95,8 +95,8 @@ typedef enum {
  *   (code i in byte i) or 24 bytes per group (16 bytes of low nibbles laid
  *   out as the 4-bit codes, then 8 bytes holding the high two bits of code
  *   4j+i in bits 2i..2i+1 of byte j).  row_bytes = 34*(D/32) or 26*(D/32);
- *   head_dim 64, 128, 256 or 512.  The 8-bit decode at head_dim 256 runs on
- *   matrix cores; the other shapes and the 6-bit format on a plain vector kernel.
+ *   head_dim 64, 128, 256 or 512.  At head_dim 256 the decode runs on matrix
+ *   cores; other head sizes run a plain vector kernel.
  * KVQ_FMT_FP8_E4M3_ROW (the KV8 commit of the colibri pull request):
  *   num_kv_heads = 1 (one latent shared by all heads), head_dim = kv_lora +
  *   rope_dim (a multiple of 16; kv_lora a multiple of 64), rope_dim > 0.
@@ -210,8 +210,8 @@ kvq_status kvq_store_rotate_q(const kvq_cache* cache, const void* k, const void*
  * part_acc: [batch][n_q_heads][S][Dv] f32, part_m / part_z: [batch][n_q_heads][S]
  * f32 with S = kvq_num_splits(max_seq_len, split_keys).
  * Requires n_q_heads % num_kv_heads == 0 and a group of at most 16 query
- * heads per KV head (Hadamard-32 formats); Q8 at head_dim 256 runs on matrix
- * cores, Q6 and the other Q8 shapes on a plain vector kernel. */
+ * heads per KV head (Hadamard-32 formats); Q8 and Q6 run on matrix cores at
+ * head_dim 256 and on a plain vector kernel at other head sizes. */
 kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
                            int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
                            float sm_scale, int32_t split_keys, float* part_acc, float* part_m, float* part_z,
