@@ -1,8 +1,9 @@
 """CPU oracle for the sub-byte KV cache -- TEST INFRASTRUCTURE ONLY.
 
 A plain, slow, obviously correct implementation of what the GPU library
-computes: the 4-bit Hadamard-32 row codec, the fp8 e4m3 latent codec, and
-decode attention over both caches in fp64.  The arithmetic lives in
+computes: the 4-bit Hadamard-32 row codec (and its 6- and 8-bit variants),
+the fp8 e4m3 latent codec, the rotated-int4 + Lloyd-Max latent codec, and
+decode attention over these caches in fp64.  The arithmetic lives in
 kvq_oracle.c (see its header for the pages and readings it follows); this
 module only marshals numpy arrays through ctypes.
 
@@ -13,7 +14,9 @@ and the two share no code.
 Parity pins: every function here is pinned by tests/test_oracle_*.py to
 values fixed by the pages or by mathematics (exact-scale example, exhaustive
 e4m3 and binary16 checks, Hadamard orthogonality, brute-force fp64
-attention); none is "parity unpinned".
+attention, the Lloyd-Max optimality conditions by numerical integration, the
+page's 0.096 round-trip error, SplitMix64's published outputs); none is
+"parity unpinned".
 """
 import ctypes
 import os
@@ -62,6 +65,17 @@ def lib():
                                             _P, _P, _P, _P, _P], _I),
             "kvqo_mla_attention_sel": ([_P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _I, _P, _I, _D, _P, _P], _I),
             "kvqo_f32_to_f16_array": ([_P, _P, _I64], None),
+            "kvqo_splitmix64": ([ctypes.c_uint64, _I, _P], None),
+            "kvqo_tq_signs": ([_I, _I, _P], None),
+            "kvqo_lloyd_max_gauss": ([_I, _P], _I),
+            "kvqo_tq_tables": ([_P, _P], None),
+            "kvqo_tq_quantize": ([_P, _I, _P], None),
+            "kvqo_tq_rotate_f32": ([_P, _I, _I], None),
+            "kvqo_tq_unrotate_f64": ([_P, _I, _I], None),
+            "kvqo_tq_encode_part": ([_P, _I, _I, _P, _P], None),
+            "kvqo_tq_store": ([_P, _P, _I64, _P, _P, _I], _I),
+            "kvqo_tq_decode_rows": ([_P, _P, _I64, _P], None),
+            "kvqo_tq_attention": ([_P, _P, _I, _I, _P, _I, _P, _I, _P, _I, _D, _P, _P], _I),
             "kvqo_e4m3_encode_array": ([_P, _P, _I64], None),
         }
         for name, (args, res) in sig.items():
@@ -296,3 +310,107 @@ def mla_attention_sel(codes_pool, scale_pool, q, page_table, sel, n_sel, sm_scal
                                         _ptr(q), H, _ptr(pt), pt.shape[1], _ptr(sl), sl.shape[1], _ptr(ns), B,
                                         float(sm_scale), _ptr(out), _ptr(lse)), "mla_attention_sel")
     return out, lse
+
+
+# ---------------------------------------------------------------- rotated-int4 + Lloyd-Max latent codec
+#
+# colibri pull request "KV cache quantization: fp8 (KV8) + 4-bit TurboQuant
+# (KV_TQ)", Summary "Why rotated-int4 for the 4-bit tier": randomized
+# Hadamard rotation, 16-level Lloyd-Max codebook for N(0,1) scaled by
+# radius/sqrt(n), one radius per row part.  Readings: kvq_oracle.c.
+
+TQ_ROW_BYTES = 288      # 256 code bytes of the 512-wide latent part, 32 of the 64-wide rope part
+TQ_PARTS = ((0, 512), (1, 64))
+
+
+def splitmix64(seed, n):
+    out = np.empty(n, np.uint64)
+    lib().kvqo_splitmix64(int(seed), n, _ptr(out))
+    return out
+
+
+def tq_signs(part, n):
+    sig = np.empty(n, np.float32)
+    lib().kvqo_tq_signs(part, n, _ptr(sig))
+    return sig
+
+
+def lloyd_max_gauss(nlev=16):
+    """Levels (fp64, ascending) and the number of Lloyd iterations run."""
+    lev = np.empty(nlev, np.float64)
+    it = lib().kvqo_lloyd_max_gauss(nlev, _ptr(lev))
+    return lev, it
+
+
+def tq_tables():
+    """The codec's fp32 levels (16) and thresholds (15)."""
+    lev, thr = np.empty(16, np.float32), np.empty(15, np.float32)
+    lib().kvqo_tq_tables(_ptr(lev), _ptr(thr))
+    return lev, thr
+
+
+def tq_quantize(u):
+    u = _c(u, np.float32)
+    codes = np.empty(u.shape, np.uint8)
+    lib().kvqo_tq_quantize(_ptr(u), u.size, _ptr(codes))
+    return codes
+
+
+def tq_rotate_f32(x, part):
+    """The fp32 storage rotation of one part (returns a copy)."""
+    x = np.array(x, dtype=np.float32, order="C", copy=True)
+    lib().kvqo_tq_rotate_f32(_ptr(x), x.size, part)
+    return x
+
+
+def tq_unrotate_f64(y, part):
+    y = np.array(y, dtype=np.float64, order="C", copy=True)
+    lib().kvqo_tq_unrotate_f64(_ptr(y), y.size, part)
+    return y
+
+
+def tq_encode_part(x, part):
+    x = _c(x, np.float32)
+    out = np.empty(x.size // 2, np.uint8)
+    r = np.empty(1, np.float32)
+    lib().kvqo_tq_encode_part(_ptr(x), x.size, part, _ptr(out), _ptr(r))
+    return out, float(r[0])
+
+
+def tq_pool_shape(num_pages, page_size):
+    return (num_pages * page_size, TQ_ROW_BYTES), (num_pages * page_size, 2)
+
+
+def tq_store(codes_pool, radius_pool, x, slots):
+    """Store latent rows x [n][576] at slots (in place on the two pools)."""
+    assert codes_pool.flags.c_contiguous and radius_pool.flags.c_contiguous
+    x = _c(x, np.float32)
+    slots = _c(slots, np.int64)
+    _check(lib().kvqo_tq_store(_ptr(codes_pool), _ptr(radius_pool), codes_pool.shape[0], _ptr(x), _ptr(slots),
+                               len(slots)), "tq_store")
+
+
+def tq_decode_rows(codes, radii):
+    """Dequantized, rotated-back rows [n][576] (fp64)."""
+    codes = _c(codes, np.uint8).reshape(-1, TQ_ROW_BYTES)
+    radii = _c(radii, np.float32).reshape(-1, 2)
+    out = np.empty((codes.shape[0], 576), np.float64)
+    lib().kvqo_tq_decode_rows(_ptr(codes), _ptr(radii), codes.shape[0], _ptr(out))
+    return out
+
+
+def tq_attention(codes_pool, radius_pool, q, page_table, seq_lens, sm_scale, page_size):
+    """fp64 absorbed attention over the TQ4 cache: (out [B][H][512], lse [B][H])."""
+    q = _c(q, np.float32)
+    B, H, D = q.shape
+    assert D == 576
+    pt = _c(page_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    out = np.empty((B, H, 512), np.float64)
+    lse = np.empty((B, H), np.float64)
+    num_pages = codes_pool.shape[0] // page_size
+    _check(lib().kvqo_tq_attention(_ptr(_c(codes_pool, np.uint8)), _ptr(_c(radius_pool, np.float32)), page_size,
+                                   num_pages, _ptr(q), H, _ptr(pt), pt.shape[1], _ptr(sl), B, float(sm_scale),
+                                   _ptr(out), _ptr(lse)), "tq_attention")
+    return out, lse
+

@@ -28,7 +28,9 @@
  *         0, a guard for an amax so small that 448/amax overflows, absorbed
  *         attention where the latent is key and value), split-T commit
  *         (partials (cl[K], m, z) and a log-sum-exp merge), the
- *         correctness/performance commit (NaN codes read as 0).
+ *         correctness/performance commit (NaN codes read as 0), and the
+ *         Summary "Why rotated-int4 for the 4-bit tier" (the TQ4 codec at
+ *         the end of this file, with its own readings).
  *
  * Readings of points the pages leave open (each one is listed in the design
  * notes with its reason):
@@ -762,4 +764,279 @@ void kvqo_blk_decode_rows(int bits, const uint8_t* rows, int64_t n_rows, int D, 
 
 void kvqo_hadamard32_f32_rows(float* x, int64_t n_groups) {
     for (int64_t g = 0; g < n_groups; ++g) kvqo_hadamard32_f32(x + 32 * g);
+}
+
+/* ======================================================================
+ * Rotated-int4 + Lloyd-Max codec for the latent ([CO] PR description and
+ * Summary, "Why rotated-int4 for the 4-bit tier": a randomized-Hadamard
+ * rotation, then a fixed 16-level Lloyd-Max codebook, optimal for N(0,1),
+ * scaled by radius/sqrt(n); the rotation leaves the radius unchanged, so one
+ * scale per row survives; a radius-0 row decodes to the zero vector).
+ *
+ * Readings of points the page leaves open:
+ *   - each part of a latent row (the 512-wide latent, the 64-wide rope part)
+ *     is coded on its own, with its own radius, as the fp8 rows keep two
+ *     scales;
+ *   - rotation of a part of n values: v_i = s_i * x_i with signs s_i = +-1,
+ *     then the Sylvester butterfly in fp32 (stages h = 1, 2, ..., n/2), then
+ *     one multiply by fp32(1/sqrt(n)); orthonormal, and its inverse is the
+ *     butterfly, the multiply, then the signs;
+ *   - signs: s_i = -1 where bit 63 of the i-th output of SplitMix64 (Steele,
+ *     Lea and Flood, "Fast splittable pseudorandom number generators", 2014)
+ *     is set, from seed 0x4C41544E ("LATN") for the latent part and
+ *     0x524F5045 ("ROPE") for the rope part;
+ *   - radius r = fp32(sqrt(S)), S the fp64 sum of the squared inputs taken as
+ *     sums of 8 consecutive squares, those sums then added in order;
+ *   - u_i = y_i * fp32(fp32(sqrt(n)) / r); code = the number of the 15
+ *     fp32 thresholds (midpoints of neighbouring fp64 levels, rounded) that
+ *     u_i exceeds (0..15, ties to the lower code); levels = Lloyd's iteration
+ *     on N(0,1) run to convergence in fp64, made exactly symmetric (so the
+ *     middle threshold is exactly 0), kept as fp32;
+ *   - a row whose r is 0 or not finite, or whose sqrt(n)/r is not finite, is
+ *     inert: radius 0 and every code 0;
+ *   - codes are nibble-packed, element 2k low, 2k+1 high: a row is 256 code
+ *     bytes of the latent part, then 32 of the rope part (288 bytes), and
+ *     its two radii are kept as f32 [slot][2].
+ * ====================================================================== */
+
+#define KVQO_TQ_LEVELS 16
+
+static uint64_t kvqo_splitmix64_next(uint64_t* state) {
+    uint64_t z = (*state += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+/* First n outputs of SplitMix64 from `seed` (exposed for its known-answer test). */
+void kvqo_splitmix64(uint64_t seed, int n, uint64_t* out) {
+    uint64_t s = seed;
+    for (int i = 0; i < n; ++i) out[i] = kvqo_splitmix64_next(&s);
+}
+
+static uint64_t kvqo_tq_seed(int part) { return part == 0 ? 0x4C41544Eull : 0x524F5045ull; }
+
+/* Signs of a part: +1 or -1 as floats. */
+void kvqo_tq_signs(int part, int n, float* sig) {
+    uint64_t s = kvqo_tq_seed(part);
+    for (int i = 0; i < n; ++i) sig[i] = (kvqo_splitmix64_next(&s) >> 63) ? -1.0f : 1.0f;
+}
+
+static double kvqo_npdf(double x) { return exp(-0.5 * x * x) / sqrt(2.0 * 3.14159265358979323846); }
+static double kvqo_ncdf(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
+
+/* Lloyd-Max quantizer of N(0,1) with `nlev` levels: alternate the two
+ * optimality conditions (thresholds at midpoints of neighbouring levels;
+ * each level the mean of N(0,1) over its cell, (pdf(a) - pdf(b)) /
+ * (cdf(b) - cdf(a))) from evenly spaced levels until no level moves by more
+ * than 1e-15.  Returns the number of iterations; lev ascending. */
+int kvqo_lloyd_max_gauss(int nlev, double* lev) {
+    for (int k = 0; k < nlev; ++k) lev[k] = -3.0 + 6.0 * (k + 0.5) / nlev;
+    int it = 0;
+    for (; it < 100000; ++it) {
+        double move = 0.0;
+        double prev_t = -INFINITY;
+        double nl[64];
+        for (int k = 0; k < nlev; ++k) {
+            const double t = k + 1 < nlev ? 0.5 * (lev[k] + lev[k + 1]) : INFINITY;
+            const double pa = isinf(prev_t) ? 0.0 : kvqo_npdf(prev_t), pb = isinf(t) ? 0.0 : kvqo_npdf(t);
+            const double ca = isinf(prev_t) ? 0.0 : kvqo_ncdf(prev_t), cb = isinf(t) ? 1.0 : kvqo_ncdf(t);
+            nl[k] = (pa - pb) / (cb - ca);
+            prev_t = t;
+        }
+        for (int k = 0; k < nlev; ++k) {
+            const double d = fabs(nl[k] - lev[k]);
+            if (d > move) move = d;
+            lev[k] = nl[k];
+        }
+        if (move <= 1e-15) break;
+    }
+    /* N(0,1) is symmetric: make the levels exactly so (the middle threshold
+     * is then exactly 0), averaging the two magnitudes of each pair. */
+    for (int k = 0; k < nlev / 2; ++k) {
+        const double a = 0.5 * (lev[nlev - 1 - k] - lev[k]);
+        lev[k] = -a;
+        lev[nlev - 1 - k] = a;
+    }
+    return it;
+}
+
+/* The codec's tables: fp32 levels and the 15 fp32 thresholds (computed once). */
+void kvqo_tq_tables(float* lev32, float* thr32) {
+    static float s_lev[KVQO_TQ_LEVELS], s_thr[KVQO_TQ_LEVELS - 1];
+    static int s_done = 0;
+#pragma omp critical(kvqo_tq_tables)
+    {
+        if (!s_done) {
+            double lev[KVQO_TQ_LEVELS];
+            kvqo_lloyd_max_gauss(KVQO_TQ_LEVELS, lev);
+            for (int k = 0; k < KVQO_TQ_LEVELS; ++k) s_lev[k] = (float)lev[k];
+            for (int k = 0; k + 1 < KVQO_TQ_LEVELS; ++k) s_thr[k] = (float)(0.5 * (lev[k] + lev[k + 1]));
+            s_done = 1;
+        }
+    }
+    memcpy(lev32, s_lev, sizeof(s_lev));
+    memcpy(thr32, s_thr, sizeof(s_thr));
+}
+
+/* Code of one rotated, normalized value: how many thresholds it exceeds. */
+static int kvqo_tq_code(float u, const float* thr32) {
+    int q = 0;
+    for (int k = 0; k + 1 < KVQO_TQ_LEVELS; ++k) q += u > thr32[k];
+    return q;
+}
+
+void kvqo_tq_quantize(const float* u, int n, uint8_t* codes) {
+    float lev32[KVQO_TQ_LEVELS], thr32[KVQO_TQ_LEVELS - 1];
+    kvqo_tq_tables(lev32, thr32);
+    for (int i = 0; i < n; ++i) codes[i] = (uint8_t)kvqo_tq_code(u[i], thr32);
+}
+
+/* The forward rotation of a part (n a power of two), fp32, in place. */
+void kvqo_tq_rotate_f32(float* v, int n, int part) {
+    float sig[512];
+    kvqo_tq_signs(part, n, sig);
+    for (int i = 0; i < n; ++i) v[i] = v[i] * sig[i];
+    for (int h = 1; h < n; h <<= 1)
+        for (int i = 0; i < n; ++i)
+            if ((i & h) == 0) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+    const float c = (float)(1.0 / sqrt((double)n));
+    for (int i = 0; i < n; ++i) v[i] = v[i] * c;
+}
+
+/* Inverse rotation of a part in fp64 (the butterfly, 1/sqrt(n), the signs). */
+void kvqo_tq_unrotate_f64(double* v, int n, int part) {
+    float sig[512];
+    kvqo_tq_signs(part, n, sig);
+    for (int h = 1; h < n; h <<= 1)
+        for (int i = 0; i < n; ++i)
+            if ((i & h) == 0) {
+                const double a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+    const double c = 1.0 / sqrt((double)n);
+    for (int i = 0; i < n; ++i) v[i] = v[i] * c * (double)sig[i];
+}
+
+/* Encode one part of n values (n = 512 or 64) -> n/2 code bytes, radius. */
+void kvqo_tq_encode_part(const float* x, int n, int part, uint8_t* bytes, float* radius) {
+    double S = 0.0;
+    for (int b = 0; b < n; b += 8) {
+        double s8 = 0.0;
+        for (int i = b; i < b + 8; ++i) s8 += (double)x[i] * (double)x[i];
+        S += s8;
+    }
+    const float r = (float)sqrt(S);
+    const float kn = (float)sqrt((double)n);
+    const float inv = kn / r;
+    if (!(r > 0.0f) || !isfinite(r) || !isfinite(inv)) {
+        memset(bytes, 0, (size_t)n / 2);
+        *radius = 0.0f;
+        return;
+    }
+    float y[512];
+    memcpy(y, x, sizeof(float) * (size_t)n);
+    kvqo_tq_rotate_f32(y, n, part);
+    float lev32[KVQO_TQ_LEVELS], thr32[KVQO_TQ_LEVELS - 1];
+    kvqo_tq_tables(lev32, thr32);
+    for (int k = 0; k < n / 2; ++k) {
+        const int q0 = kvqo_tq_code(y[2 * k] * inv, thr32), q1 = kvqo_tq_code(y[2 * k + 1] * inv, thr32);
+        bytes[k] = (uint8_t)(q0 | (q1 << 4));
+    }
+    *radius = r;
+}
+
+/* Dequantize one part to the unrotated fp64 values. */
+void kvqo_tq_decode_part(const uint8_t* bytes, float radius, int n, int part, double* out) {
+    float lev32[KVQO_TQ_LEVELS], thr32[KVQO_TQ_LEVELS - 1];
+    kvqo_tq_tables(lev32, thr32);
+    const double sc = (double)radius / sqrt((double)n);
+    for (int i = 0; i < n; ++i) {
+        const int q = (bytes[i / 2] >> (4 * (i & 1))) & 15;
+        out[i] = (double)lev32[q] * sc;
+    }
+    kvqo_tq_unrotate_f64(out, n, part);
+}
+
+/* Store latent rows x [n_tokens][576] (512 latent + 64 rope) into
+ * codes_pool [slot][288] and radius_pool [slot][2]; slot < 0 skips. */
+int kvqo_tq_store(uint8_t* codes_pool, float* radius_pool, int64_t n_slots, const float* x,
+                  const int64_t* slots, int n_tokens) {
+    for (int t = 0; t < n_tokens; ++t)
+        if (slots[t] >= n_slots) return KVQO_ERANGE;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < n_tokens; ++t) {
+        if (slots[t] < 0) continue;
+        const float* r = x + (size_t)t * 576;
+        uint8_t* c = codes_pool + (size_t)slots[t] * 288;
+        float* rad = radius_pool + (size_t)slots[t] * 2;
+        kvqo_tq_encode_part(r, 512, 0, c, &rad[0]);
+        kvqo_tq_encode_part(r + 512, 64, 1, c + 256, &rad[1]);
+    }
+    return KVQO_OK;
+}
+
+/* Decode rows of the pool: out [n][576] fp64 (unrotated). */
+void kvqo_tq_decode_rows(const uint8_t* codes_pool, const float* radius_pool, int64_t n, double* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; ++j) {
+        kvqo_tq_decode_part(codes_pool + (size_t)j * 288, radius_pool[2 * j], 512, 0, out + (size_t)j * 576);
+        kvqo_tq_decode_part(codes_pool + (size_t)j * 288 + 256, radius_pool[2 * j + 1], 64, 1,
+                            out + (size_t)j * 576 + 512);
+    }
+}
+
+/* Absorbed latent attention over the TQ4 cache, by its definition: every
+ * position's latent row is dequantized and rotated back (fp64), then
+ *   s_j = sm_scale * <q_h, x_j> over all 576 values, p = softmax(s),
+ *   cl_h = sum_j p_j x_j[0:512];
+ * q: [B][n_heads][576] fp32; out: [B][n_heads][512]; lse: [B][n_heads]. */
+int kvqo_tq_attention(const uint8_t* codes_pool, const float* radius_pool, int page_size, int num_pages,
+                      const float* q, int n_heads, const int32_t* page_table, int max_pages,
+                      const int32_t* seq_lens, int B, double sm_scale, double* out, double* lse) {
+    for (int b = 0; b < B; ++b)
+        if (seq_lens[b] < 0 || (int64_t)seq_lens[b] > (int64_t)max_pages * page_size) return KVQO_ERANGE;
+    int err = KVQO_OK;
+    for (int b = 0; b < B; ++b) {
+        const int64_t T = seq_lens[b];
+        double* rows = malloc(sizeof(double) * 576 * (size_t)(T > 0 ? T : 1));
+        int st = KVQO_OK;
+        for (int64_t j = 0; j < T && st == KVQO_OK; ++j) {
+            const int64_t slot = kvqo_slot(page_table, max_pages, b, j, page_size);
+            if (slot < 0 || slot >= (int64_t)num_pages * page_size) { st = KVQO_ERANGE; break; }
+            kvqo_tq_decode_rows(codes_pool + (size_t)slot * 288, radius_pool + 2 * slot, 1, rows + (size_t)j * 576);
+        }
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int h = 0; h < n_heads; ++h) {
+            const float* qh = q + ((size_t)b * n_heads + h) * 576;
+            double* o = out + ((size_t)b * n_heads + h) * 512;
+            double* s = malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+            double m = -INFINITY;
+            for (int64_t j = 0; j < T && st == KVQO_OK; ++j) {
+                double d = 0.0;
+                for (int i = 0; i < 576; ++i) d += (double)qh[i] * rows[(size_t)j * 576 + i];
+                s[j] = sm_scale * d;
+                if (s[j] > m) m = s[j];
+            }
+            for (int i = 0; i < 512; ++i) o[i] = 0.0;
+            double z = 0.0;
+            if (st == KVQO_OK)
+                for (int64_t j = 0; j < T; ++j) {
+                    const double w = exp(s[j] - m);
+                    z += w;
+                    for (int i = 0; i < 512; ++i) o[i] += w * rows[(size_t)j * 576 + i];
+                }
+            if (T > 0) for (int i = 0; i < 512; ++i) o[i] /= z;
+            if (lse) lse[(size_t)b * n_heads + h] = T > 0 ? m + log(z) : -INFINITY;
+            free(s);
+        }
+        if (st < err) err = st;
+        free(rows);
+    }
+    return err;
 }
