@@ -31,6 +31,7 @@ FMT_Q8_H32 = 3
 FMT_Q6_H32 = 4
 H32_FORMATS = (FMT_Q4_H32, FMT_Q8_H32, FMT_Q6_H32)
 FMT_FP8_E4M3_ROW = 2
+FMT_TQ4_LATENT = 5
 
 DT_F32, DT_BF16, DT_F16 = 0, 1, 2
 _DTYPES = {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float16: DT_F16}
@@ -163,6 +164,31 @@ class Fp8Cache:
         return int(lib.kvq_pool_bytes(ctypes.byref(self.desc)))
 
 
+class TqCache:
+    """Paged rotated-int4 + Lloyd-Max latent rows: codes [num_pages*page_size][288] uint8 (nibbles of the
+    512 latent and 64 rope values), radii [..][2] f32.  Stores and decodes as Fp8Cache does: kvq_store
+    takes k [n_tokens][576] and v None; kvq_decode_attn takes the unrotated query."""
+
+    fmt = FMT_TQ4_LATENT
+
+    def __init__(self, num_pages, page_size=16, device="cuda"):
+        slots = num_pages * page_size
+        self.codes = torch.zeros((slots, 288), dtype=torch.uint8, device=device)
+        self.scales = torch.zeros((slots, 2), dtype=torch.float32, device=device)
+        self.num_kv_heads, self.head_dim, self.rope_dim = 1, 576, 64
+        self.page_size, self.num_pages = page_size, num_pages
+        self.dv = 512
+        self.desc = KvqCacheDesc(FMT_TQ4_LATENT, 1, 576, 64, page_size, num_pages, self.codes.data_ptr(), None,
+                                 self.scales.data_ptr())
+
+    @property
+    def device(self):
+        return self.codes.device
+
+    def pool_bytes(self):
+        return int(lib.kvq_pool_bytes(ctypes.byref(self.desc)))
+
+
 def kvq_store(cache, k, v, slot_mapping):
     """Quantize new rows into the cache.
 
@@ -178,7 +204,7 @@ def kvq_store(cache, k, v, slot_mapping):
         vp = _dev(v, "v", dtype=k.dtype, shape=shape)
     else:
         if v is not None:
-            raise ValueError("the fp8 latent cache takes no v")
+            raise ValueError("the latent caches take no v")
         kp = _dev(k, "k", shape=(n, cache.head_dim))
         vp = None
     sp = _dev(slot_mapping, "slot_mapping", dtype=torch.int64)

@@ -195,6 +195,19 @@ hipError_t launch_decode_fp8_mfma(const Fp8Pool& pool, const DecodeArgs& a, hipS
 hipError_t launch_decode_q4_simple(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_fp8_simple(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s);
 
+// Rotated-int4 + Lloyd-Max latent codec (tq4.hip): fp32 levels and the 15
+// thresholds between them, derived once per process on the host.  The pool
+// is an Fp8Pool whose codes are 288-byte nibble rows and whose scales are the
+// two radii.
+struct TqTables {
+    float lev[16];
+    float thr[15];
+};
+const TqTables& tq_tables();
+hipError_t launch_store_tq4(const Fp8Pool& pool, const void* x, InType dt, const int64_t* slots, int n_tokens,
+                            hipStream_t s);
+hipError_t launch_decode_tq4(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s);
+
 struct MergeArgs {
     const float* part_acc;
     const float* part_m;

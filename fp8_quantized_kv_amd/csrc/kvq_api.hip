@@ -34,6 +34,11 @@ kvq_status check_cache(const kvq_cache* c) {
         if (!aligned(c->k_pool) || !aligned(c->v_pool) || c->scale_pool) return KVQ_ERR_INVALID_ARG;
         return KVQ_OK;
     }
+    if (c->format == KVQ_FMT_TQ4_LATENT) {
+        if (c->num_kv_heads != 1 || c->head_dim != 576 || c->rope_dim != 64) return KVQ_ERR_INVALID_ARG;
+        if (!aligned(c->k_pool) || c->v_pool || !aligned(c->scale_pool)) return KVQ_ERR_INVALID_ARG;
+        return KVQ_OK;
+    }
     if (c->format == KVQ_FMT_FP8_E4M3_ROW) {
         if (c->num_kv_heads != 1 || c->rope_dim <= 0 || c->rope_dim >= c->head_dim) return KVQ_ERR_INVALID_ARG;
         if (c->head_dim % 16 || (c->head_dim - c->rope_dim) % 64) return KVQ_ERR_INVALID_ARG;
@@ -95,6 +100,7 @@ size_t kvq_row_bytes(int32_t format, int32_t head_dim, int32_t rope_dim) {
         if (head_dim <= 0 || rope_dim <= 0 || rope_dim >= head_dim) return 0;
         return size_t(head_dim);
     }
+    if (format == KVQ_FMT_TQ4_LATENT) return head_dim == 576 && rope_dim == 64 ? 288 : 0;
     return 0;
 }
 
@@ -129,6 +135,8 @@ kvq_status kvq_store(const kvq_cache* cache, const void* k, const void* v, int32
         return launched(kvq::launch_store_q4(q4_pool(cache), k, v, dt, slot_mapping, n_tokens, stream));
     }
     if (!aligned(k) || v) return KVQ_ERR_INVALID_ARG;
+    if (cache->format == KVQ_FMT_TQ4_LATENT)
+        return launched(kvq::launch_store_tq4(fp8_pool(cache), k, dt, slot_mapping, n_tokens, stream));
     return launched(kvq::launch_store_fp8(fp8_pool(cache), k, dt, slot_mapping, n_tokens, stream));
 }
 
@@ -187,6 +195,7 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_h
         return launched(kvq::launch_decode_q4_simple(pool, a, stream));
     }
     const kvq::Fp8Pool pool = fp8_pool(cache);
+    if (cache->format == KVQ_FMT_TQ4_LATENT) return launched(kvq::launch_decode_tq4(pool, a, stream));
     if (kvq::decode_fp8_mfma_supported(pool, a)) return launched(kvq::launch_decode_fp8_mfma(pool, a, stream));
     return launched(kvq::launch_decode_fp8_simple(pool, a, stream));
 }

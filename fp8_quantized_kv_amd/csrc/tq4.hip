@@ -1,0 +1,395 @@
+// tq4.hip -- the rotated-int4 + Lloyd-Max codec for the MLA latent (TQ4):
+// store (rotate, radius, quantize, pack) and a plain split-T decode.
+//
+// Method: colibri pull request "KV cache quantization: fp8 (KV8) + 4-bit
+// TurboQuant (KV_TQ)", Summary "Why rotated-int4 for the 4-bit tier": a
+// randomized Hadamard rotation, then a fixed 16-level Lloyd-Max codebook
+// optimal for N(0,1), scaled by radius/sqrt(n); the rotation keeps the
+// radius, so one scale per row part survives; a radius-0 row decodes to 0.
+// The latent is both key and value (absorbed attention, KV8 commit), and
+// the split-T partials (cl[K], m, z) are merged by the log-sum-exp kernel.
+//
+// Format (per position): the 512-wide latent part and the 64-wide rope part
+// are each rotated and coded apart: v = s (.) x with signs s_i = -1 where bit
+// 63 of the i-th SplitMix64 output (Steele, Lea and Flood 2014) from the
+// part's seed is set, the Sylvester butterfly in fp32 (stages h = 1 .. n/2),
+// times fp32(1/sqrt(n)).  Radius r = fp32(sqrt(S)), S the fp64 sum of the
+// squared inputs as sums of 8 consecutive squares added in order.  Code =
+// how many of the 15 fp32 thresholds y_i * fp32(fp32(sqrt(n)) / r) exceeds.
+// Nibbles packed element 2k low, 2k + 1 high: 256 + 32 bytes per position;
+// radii f32 [slot][2].  A zero, NaN or infinite row is stored inert (radius
+// 0, codes 0).
+//
+// Decode (plain fp32 vector kernel, the correctness path of this format):
+// the query is rotated with the same transform in the prologue; scores and
+// the context accumulate in rotated space against levels x radius/sqrt(n);
+// the split's context is rotated back before its partial is written, so the
+// partials and the merge are those of the fp8 latent cache.
+#include "internal.h"
+
+#include <cmath>
+
+namespace kvq {
+
+namespace {
+
+// ---- codebook: Lloyd's iteration on the positive half of N(0,1) ----------
+// Levels c_0 < .. < c_7 > 0 (the negative half mirrors them); cell k is
+// (t_k, t_k+1) with t_0 = 0, t_k = (c_k-1 + c_k) / 2, t_8 = inf; each level
+// moves to the mean of N(0,1) over its cell, (pdf(a) - pdf(b)) / (Q(a) -
+// Q(b)) with Q the upper tail, until no level moves by more than 1e-15.
+double npdf(double x) { return std::exp(-0.5 * x * x) * 0.39894228040143267794; }
+double upper_tail(double x) { return 0.5 * std::erfc(x * 0.70710678118654752440); }
+
+TqTables make_tables() {
+    double c[8];
+    for (int k = 0; k < 8; ++k) c[k] = 0.35 * (k + 0.5);
+    for (int it = 0; it < 100000; ++it) {
+        double t[9];
+        t[0] = 0.0;
+        for (int k = 1; k < 8; ++k) t[k] = 0.5 * (c[k - 1] + c[k]);
+        t[8] = INFINITY;
+        double move = 0.0;
+        for (int k = 0; k < 8; ++k) {
+            const double a = t[k], b = t[k + 1];
+            const double num = npdf(a) - (std::isinf(b) ? 0.0 : npdf(b));
+            const double den = upper_tail(a) - (std::isinf(b) ? 0.0 : upper_tail(b));
+            const double nc = num / den;
+            move = std::fmax(move, std::fabs(nc - c[k]));
+            c[k] = nc;
+        }
+        if (move <= 1e-15) break;
+    }
+    TqTables tb;
+    for (int k = 0; k < 8; ++k) {
+        tb.lev[8 + k] = float(c[k]);
+        tb.lev[7 - k] = -float(c[k]);
+    }
+    tb.thr[7] = 0.0f;
+    for (int k = 0; k < 7; ++k) {
+        tb.thr[8 + k] = float(0.5 * (c[k] + c[k + 1]));
+        tb.thr[6 - k] = -tb.thr[8 + k];
+    }
+    return tb;
+}
+
+constexpr uint64_t kSeedLatent = 0x4C41544Eull, kSeedRope = 0x524F5045ull;
+
+__device__ __forceinline__ int clamp_int(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Sign of element i of a part: bit 63 of SplitMix64 output i (counter-based:
+// output i mixes seed + (i + 1) * golden gamma).
+__device__ __forceinline__ float tq_sign(uint64_t seed, int i) {
+    uint64_t z = seed + uint64_t(i + 1) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return (z >> 63) ? -1.0f : 1.0f;
+}
+
+template <InType DT>
+__device__ __forceinline__ float load_x(const void* x, int64_t i) {
+    if constexpr (DT == InType::F32) return static_cast<const float*>(x)[i];
+    else if constexpr (DT == InType::BF16) return __uint_as_float(uint32_t(static_cast<const uint16_t*>(x)[i]) << 16);
+    else return __half2float(static_cast<const __half*>(x)[i]);
+}
+
+// ---- store: one wave per token; lane l holds elements 8l .. 8l + 7 -------
+// The butterfly stages below 8 run inside a lane, the others between lanes
+// (partner lane l ^ (h / 8)); each stage is (a + b, a - b) with a the element
+// whose index has bit h clear, in fp32, as the format states.
+template <int N>
+__device__ __forceinline__ void encode_part(float (&v)[8], int lane, uint64_t seed, const TqTables& tb,
+                                            double* red, uint8_t* out, float* radius) {
+    constexpr int LANES = N / 8;
+    const bool on = lane < LANES;
+    // radius: per-lane sums of 8 squares (fp64), then added in lane order
+    double s8 = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s8 += double(v[e]) * double(v[e]);
+    if (on) red[lane] = s8;
+    __syncthreads();
+    double S = 0.0;
+    for (int l = 0; l < LANES; ++l) S += red[l];
+    __syncthreads();
+    const float r = float(std::sqrt(S));
+    const float inv = float(std::sqrt(double(N))) / r;
+    const bool inert = !(r > 0.0f) || !isfinite(r) || !isfinite(inv);
+    // rotation
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * tq_sign(seed, 8 * lane + e);
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if ((e & h) == 0) {
+                const float a = v[e], b = v[e + h];
+                v[e] = a + b;
+                v[e + h] = a - b;
+            }
+#pragma unroll
+    for (int hl = 1; hl < LANES; hl <<= 1) {
+        const bool low = (lane & hl) == 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float o = __shfl_xor(v[e], hl, 64);
+            v[e] = low ? v[e] + o : o - v[e];
+        }
+    }
+    const float c = float(1.0 / std::sqrt(double(N)));
+    uint32_t word = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float u = (v[e] * c) * inv;
+        uint32_t q = 0u;
+#pragma unroll
+        for (int k = 0; k < 15; ++k) q += u > tb.thr[k] ? 1u : 0u;
+        word |= (inert ? 0u : q) << (4 * e);
+    }
+    if (on) reinterpret_cast<uint32_t*>(out)[lane] = word;
+    if (lane == 0) *radius = inert ? 0.0f : r;
+}
+
+template <InType DT>
+__global__ __launch_bounds__(64) void store_tq4_kernel(const void* __restrict__ x, const int64_t* __restrict__ slots,
+                                                       int n_tokens, uint8_t* __restrict__ codes,
+                                                       float* __restrict__ radii, int64_t n_slots, TqTables tb) {
+    __shared__ double red[64];
+    const int t = blockIdx.x, lane = threadIdx.x;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= n_slots) return;  // uniform over the workgroup
+    const int64_t base = int64_t(t) * 576;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = load_x<DT>(x, base + 8 * lane + e);
+    encode_part<512>(v, lane, kSeedLatent, tb, red, codes + slot * 288, radii + slot * 2);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = lane < 8 ? load_x<DT>(x, base + 512 + 8 * lane + e) : 0.0f;
+    encode_part<64>(v, lane, kSeedRope, tb, red, codes + slot * 288 + 256, radii + slot * 2 + 1);
+}
+
+// ---- decode: plain fp32, split-T --------------------------------------------
+constexpr int kTT = 256;     // threads
+constexpr int kTHB = 16;     // heads per workgroup
+constexpr int kTTile = 16;   // keys per tile
+constexpr int kTL = 512, kTR = 64, kTD = 576;
+
+// In-place rotation of rows of n values in LDS (n = 512 or 64) for `rows`
+// rows at `stride`, by all threads: signs (forward) or not, the butterfly,
+// times 1/sqrt(n), then signs (inverse).  fp32, stage order h = 1 .. n/2.
+template <int N>
+__device__ void lds_rotate(float* base, int stride, int rows, uint64_t seed, bool inverse, int tid) {
+    if (!inverse) {
+        for (int i = tid; i < rows * N; i += kTT) base[(i / N) * stride + i % N] *= tq_sign(seed, i % N);
+        __syncthreads();
+    }
+    for (int h = 1; h < N; h <<= 1) {
+        for (int i = tid; i < rows * (N / 2); i += kTT) {
+            const int row = i / (N / 2), p = i % (N / 2);
+            const int lo = (p / h) * 2 * h + p % h;  // index with bit h clear
+            float* r = base + row * stride;
+            const float a = r[lo], b = r[lo + h];
+            r[lo] = a + b;
+            r[lo + h] = a - b;
+        }
+        __syncthreads();
+    }
+    const float c = float(1.0 / std::sqrt(double(N)));
+    for (int i = tid; i < rows * N; i += kTT) {
+        float& e = base[(i / N) * stride + i % N];
+        e = inverse ? (e * c) * tq_sign(seed, i % N) : e * c;
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kTT) void decode_tq4_simple(const uint8_t* __restrict__ codes,
+                                                         const float* __restrict__ radii, int page_size,
+                                                         int num_pages, DecodeArgs a, TqTables tb) {
+    constexpr int DW = 288 / 4;  // code words per row
+    constexpr int CPT = kTL / kTT;
+    const int s = blockIdx.x, hblk = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int h0 = hblk * kTHB;
+    const int nh = min(kTHB, a.n_q_heads - h0);
+    const int T = clamp_int(a.seq_lens[b], 0, a.max_seq_len);
+    const int j0 = s * a.split_keys;
+    const int j1 = min(j0 + a.split_keys, T);
+    const int64_t hb = int64_t(b) * a.n_q_heads + h0;
+    const int S = a.n_splits;
+
+    if (j0 >= j1) {
+        for (int i = tid; i < nh * kTL; i += kTT) a.part_acc[((hb + i / kTL) * S + s) * kTL + i % kTL] = 0.0f;
+        if (tid < nh) {
+            a.part_m[(hb + tid) * S + s] = -INFINITY;
+            a.part_z[(hb + tid) * S + s] = 0.0f;
+        }
+        return;
+    }
+
+    __shared__ float qs[kTHB][kTD];
+    __shared__ uint32_t ct[kTTile * DW];
+    __shared__ float scl[kTTile], scr[kTTile];
+    __shared__ float part[16][kTHB][kTTile];
+    __shared__ float p[kTHB][kTTile];
+    __shared__ float m_s[kTHB], z_s[kTHB], alpha_s[kTHB];
+    __shared__ float lev[16];
+
+    if (tid < 16) lev[tid] = tb.lev[tid];
+    for (int i = tid; i < kTHB * kTD; i += kTT) {
+        const int h = i / kTD;
+        qs[h][i % kTD] = h < nh ? a.q[(hb + h) * kTD + i % kTD] : 0.0f;
+    }
+    if (tid < kTHB) {
+        m_s[tid] = -INFINITY;
+        z_s[tid] = 0.0f;
+    }
+    __syncthreads();
+    // the query in rotated space, pre-scaled by sm_scale * log2(e)
+    lds_rotate<kTL>(&qs[0][0], kTD, kTHB, kSeedLatent, false, tid);
+    lds_rotate<kTR>(&qs[0][kTL], kTD, kTHB, kSeedRope, false, tid);
+    const float qscale = a.sm_scale * kLog2e;
+    for (int i = tid; i < kTHB * kTD; i += kTT) qs[i / kTD][i % kTD] *= qscale;
+
+    float acc[CPT][kTHB];
+#pragma unroll
+    for (int ci = 0; ci < CPT; ++ci)
+#pragma unroll
+        for (int h = 0; h < kTHB; ++h) acc[ci][h] = 0.0f;
+    __syncthreads();
+
+    const float cL = float(1.0 / std::sqrt(512.0)), cR = 0.125f;
+    const int32_t* pt = a.page_table + int64_t(b) * a.max_pages;
+    auto code_at = [&](int kk, int c) -> float {  // level of element c (0..575) of tile row kk
+        const int byte = c < kTL ? c / 2 : 256 + (c - kTL) / 2;
+        const uint32_t w = ct[kk * DW + byte / 4];
+        return lev[(w >> (8 * (byte & 3) + 4 * (c & 1))) & 15u];
+    };
+    for (int t0 = j0; t0 < j1; t0 += kTTile) {
+        const int n = min(kTTile, j1 - t0);
+        for (int i = tid; i < n * DW; i += kTT) {
+            const int kk = i / DW, w = i % DW;
+            const int pos = t0 + kk;
+            const int page = clamp_int(pt[pos / page_size], 0, num_pages - 1);
+            const int64_t slot = int64_t(page) * page_size + pos % page_size;
+            ct[i] = reinterpret_cast<const uint32_t*>(codes + slot * 288)[w];
+        }
+        if (tid < n) {
+            const int pos = t0 + tid;
+            const int page = clamp_int(pt[pos / page_size], 0, num_pages - 1);
+            const int64_t slot = int64_t(page) * page_size + pos % page_size;
+            scl[tid] = radii[slot * 2] * cL;
+            scr[tid] = radii[slot * 2 + 1] * cR;
+        }
+        __syncthreads();
+        {
+            // thread (key kk, part_i): latent channels 32 part_i .. +31, rope 4 part_i .. +3
+            const int kk = tid & (kTTile - 1), part_i = tid / kTTile;
+            float dl[kTHB], dr[kTHB];
+#pragma unroll
+            for (int h = 0; h < kTHB; ++h) dl[h] = dr[h] = 0.0f;
+            if (kk < n) {
+                for (int c = 32 * part_i; c < 32 * part_i + 32; ++c) {
+                    const float v = code_at(kk, c);
+#pragma unroll
+                    for (int h = 0; h < kTHB; ++h) dl[h] = fmaf(qs[h][c], v, dl[h]);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = kTL + 4 * part_i + e;
+                    const float v = code_at(kk, c);
+#pragma unroll
+                    for (int h = 0; h < kTHB; ++h) dr[h] = fmaf(qs[h][c], v, dr[h]);
+                }
+            }
+            const float sl = kk < n ? scl[kk] : 0.0f, sr = kk < n ? scr[kk] : 0.0f;
+#pragma unroll
+            for (int h = 0; h < kTHB; ++h) part[part_i][h][kk] = fmaf(sl, dl[h], sr * dr[h]);
+        }
+        __syncthreads();
+        {
+            const int wave = tid >> 6, lane = tid & 63;
+            const int h = wave * 4 + (lane >> 4), kk = lane & 15;
+            float sc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc += part[i][h][kk];
+            sc = kk < n ? sc : -INFINITY;
+            float tmax = sc;
+#pragma unroll
+            for (int m = 8; m >= 1; m >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, m, 64));
+            const float m_old = m_s[h];
+            const float m_new = fmaxf(m_old, tmax);
+            const float e = kk < n ? exp2f(sc - m_new) : 0.0f;
+            float sum = e;
+#pragma unroll
+            for (int m = 8; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+            p[h][kk] = e * (kk < n ? scl[kk] : 0.0f);  // the value is level x radius / sqrt(512)
+            __syncthreads();  // every lane has read m_s[h] before lane 0 of the head writes it
+            if (kk == 0) {
+                const float al = exp2f(m_old - m_new);
+                alpha_s[h] = al;
+                z_s[h] = z_s[h] * al + sum;
+                m_s[h] = m_new;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ci = 0; ci < CPT; ++ci) {
+            const int c = tid + ci * kTT;
+#pragma unroll
+            for (int h = 0; h < kTHB; ++h) acc[ci][h] *= alpha_s[h];
+            for (int kk = 0; kk < n; ++kk) {
+                const float v = code_at(kk, c);
+#pragma unroll
+                for (int h = 0; h < kTHB; ++h) acc[ci][h] = fmaf(p[h][kk], v, acc[ci][h]);
+            }
+        }
+        __syncthreads();
+    }
+    // the split's context back from rotated space (the query rows are free now)
+#pragma unroll
+    for (int ci = 0; ci < CPT; ++ci)
+#pragma unroll
+        for (int h = 0; h < kTHB; ++h) qs[h][tid + ci * kTT] = acc[ci][h];
+    __syncthreads();
+    lds_rotate<kTL>(&qs[0][0], kTD, kTHB, kSeedLatent, true, tid);
+    for (int i = tid; i < nh * kTL; i += kTT) a.part_acc[((hb + i / kTL) * S + s) * kTL + i % kTL] = qs[i / kTL][i % kTL];
+    if (tid < nh) {
+        a.part_m[(hb + tid) * S + s] = m_s[tid] * kLn2;
+        a.part_z[(hb + tid) * S + s] = z_s[tid];
+    }
+}
+
+}  // namespace
+
+const TqTables& tq_tables() {
+    static const TqTables tb = make_tables();
+    return tb;
+}
+
+hipError_t launch_store_tq4(const Fp8Pool& pool, const void* x, InType dt, const int64_t* slots, int n_tokens,
+                            hipStream_t s) {
+    const int64_t n_slots = int64_t(pool.num_pages) * pool.page_size;
+    const dim3 grid(static_cast<unsigned>(n_tokens)), block(64);
+    const TqTables& tb = tq_tables();
+    switch (dt) {
+        case InType::F32:
+            store_tq4_kernel<InType::F32><<<grid, block, 0, s>>>(x, slots, n_tokens, pool.codes, pool.scales, n_slots, tb);
+            break;
+        case InType::BF16:
+            store_tq4_kernel<InType::BF16><<<grid, block, 0, s>>>(x, slots, n_tokens, pool.codes, pool.scales, n_slots, tb);
+            break;
+        case InType::F16:
+            store_tq4_kernel<InType::F16><<<grid, block, 0, s>>>(x, slots, n_tokens, pool.codes, pool.scales, n_slots, tb);
+            break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_tq4(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s) {
+    const int n_hblk = (a.n_q_heads + kTHB - 1) / kTHB;
+    const dim3 grid(unsigned(a.n_splits), unsigned(n_hblk), unsigned(a.batch)), block(kTT);
+    decode_tq4_simple<<<grid, block, 0, s>>>(pool.codes, pool.scales, pool.page_size, pool.num_pages, a, tq_tables());
+    return hipGetLastError();
+}
+
+}  // namespace kvq

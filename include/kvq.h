@@ -68,7 +68,8 @@ typedef enum {
     KVQ_FMT_Q4_H32 = 1,        /* 4-bit Hadamard-32 groups + fp16 scale, K and V pools */
     KVQ_FMT_FP8_E4M3_ROW = 2,  /* e4m3 latent rows + f32 scales (latent, rope) */
     KVQ_FMT_Q8_H32 = 3,        /* the same skeleton with 8-bit codes */
-    KVQ_FMT_Q6_H32 = 4         /* the same skeleton with 6-bit codes */
+    KVQ_FMT_Q6_H32 = 4,        /* the same skeleton with 6-bit codes */
+    KVQ_FMT_TQ4_LATENT = 5     /* rotated-int4 + Lloyd-Max latent rows + f32 radii (latent, rope) */
 } kvq_format;
 
 typedef enum {
@@ -102,6 +103,18 @@ typedef enum {
  *   rope_dim (a multiple of 16; kv_lora a multiple of 64), rope_dim > 0.
  *   k_pool: e4m3 codes [num_pages*page_size][head_dim]; v_pool = NULL;
  *   scale_pool: f32 [num_pages*page_size][2] = {latent scale, rope scale}.
+ * KVQ_FMT_TQ4_LATENT (the colibri pull request's Summary, "Why rotated-int4
+ *   for the 4-bit tier"): num_kv_heads = 1, head_dim = 576, rope_dim = 64.
+ *   Each part (512 latent, 64 rope values) is rotated by a randomized
+ *   Hadamard transform (signs from SplitMix64, seeds 0x4C41544E and
+ *   0x524F5045), normalized by its radius (Euclidean norm) times sqrt(n),
+ *   and coded as the index of the nearest of 16 Lloyd-Max levels of N(0,1).
+ *   k_pool: codes [num_pages*page_size][288] (256 latent + 32 rope bytes,
+ *   element 2k in the low nibble); v_pool = NULL; scale_pool: f32
+ *   [num_pages*page_size][2] = {latent radius, rope radius}; radius 0 marks an
+ *   inert (zero) row.  q for kvq_decode_attn is the unrotated [B][H][576]
+ *   query (the kernel rotates it); partials and kvq_merge are as for FP8.
+ *   Decode runs a plain vector kernel.
  */
 typedef struct kvq_cache {
     int32_t format;        /* kvq_format */

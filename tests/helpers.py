@@ -132,3 +132,45 @@ class MlaCase:
         return oracle.mla_attention(self.codes_ref, self.scales_ref, q, self.lay.page_table.numpy(),
                                     np.array(self.lens, np.int32), self.w.sm_scale, self.w.rope_dim,
                                     self.w.page_size)
+
+
+class TqCase:
+    """A rotated-int4 + Lloyd-Max latent workload instance (the fp8 workload's rows and queries)."""
+
+    def __init__(self, w, lens, layer=0, device="cuda", build_oracle=True, n_heads=None):
+        import fp8_quantized_kv_amd as kvq
+        self.w, self.lens = w, list(lens)
+        self.lay = wl.page_layout(w, self.lens)
+        self.cache = kvq.TqCache(self.lay.num_pages, w.page_size, device)
+        q = wl.mla_query(wl.shrink(w, batch=len(self.lens)), layer, device)
+        self.q = q[:, :n_heads].contiguous() if n_heads else q
+        self.page_table = self.lay.page_table.to(device)
+        self.seq_lens = torch.tensor(self.lens, dtype=torch.int32, device=device)
+        self.max_seq_len = max(self.lens) if self.lens else 0
+        n_slots = self.lay.num_pages * w.page_size
+        (cs, rs) = oracle.tq_pool_shape(self.lay.num_pages, w.page_size)
+        self.codes_ref = np.zeros(cs, np.uint8) if build_oracle else None
+        self.radii_ref = np.zeros(rs, np.float32) if build_oracle else None
+        off = 0
+        for b, T in enumerate(self.lens):
+            if T == 0:
+                continue
+            x = wl.mla_rows(w, layer, off, T, device)
+            off += T
+            slots = wl.slots_for(self.lay.page_table[b], np.arange(T), w.page_size)
+            kvq.kvq_store(self.cache, x, None, slots.to(device))
+            if build_oracle:
+                oracle.tq_store(self.codes_ref, self.radii_ref, x.float().cpu().numpy(), slots.numpy())
+
+    def gpu_attention(self, split_keys):
+        import fp8_quantized_kv_amd as kvq
+        pa, pm, pz = kvq.kvq_decode_attn(self.cache, self.q, self.page_table, self.seq_lens, self.max_seq_len,
+                                        self.w.sm_scale, split_keys)
+        out, lse = kvq.kvq_merge(self.cache, pa, pm, pz, self.seq_lens, self.max_seq_len, split_keys)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), lse.cpu().numpy()
+
+    def ref_attention(self):
+        return oracle.tq_attention(self.codes_ref, self.radii_ref, self.q.cpu().numpy(), self.lay.page_table.numpy(),
+                                   np.array(self.lens, np.int32), self.w.sm_scale, self.w.page_size)
+

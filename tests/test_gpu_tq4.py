@@ -1,0 +1,89 @@
+"""GPU parity of the rotated-int4 + Lloyd-Max latent codec (TQ4; colibri
+pull request "KV cache quantization: fp8 (KV8) + 4-bit TurboQuant (KV_TQ)",
+Summary "Why rotated-int4 for the 4-bit tier") against the oracle: stored
+codes and radii bit-exact, absorbed attention within 2e-3."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from helpers import TOL, TqCase, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    assert torch.cuda.is_available(), "no GPU"
+    import fp8_quantized_kv_amd as m
+    return m
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_tq4_store_bit_exact(kvq, dtype):
+    """Latent rows of the fp8 workload plus edge rows (zero, NaN, infinite,
+    huge, tiny, a single spike): codes and radii equal the oracle's."""
+    _say(f"tq4 store dtype={dtype}")
+    w = wl.MLA_262K
+    n = 300
+    x = wl.mla_rows(w, 0, 0, n, "cuda").to(dtype)
+    x[3] = 0
+    x[4, 7] = float("nan")
+    x[5, 600 % 576] = float("inf")
+    x[6] *= 1e30 if dtype == torch.float32 else 1e20
+    x[7] *= 1e-30 if dtype == torch.float32 else 1e-20
+    x[8] = 0
+    x[8, 511] = 3.0
+    x[9, 512:] = 0
+    cache = kvq.TqCache(n // 16 + 2, 16, "cuda")
+    slots = torch.randperm(cache.codes.shape[0], generator=torch.Generator().manual_seed(1))[:n].to(torch.int64)
+    slots[10] = -1  # skipped
+    kvq.kvq_store(cache, x, None, slots.cuda())
+    torch.cuda.synchronize()
+    codes = np.zeros(tuple(cache.codes.shape), np.uint8)
+    radii = np.zeros(tuple(cache.scales.shape), np.float32)
+    oracle.tq_store(codes, radii, x.float().cpu().numpy(), slots.numpy())
+    gc, gr = cache.codes.cpu().numpy(), cache.scales.cpu().numpy()
+    bad = np.nonzero(np.any(gc != codes, axis=1) | np.any(gr.view(np.uint32) != radii.view(np.uint32), axis=1))[0]
+    assert bad.size == 0, f"rows differ: {bad[:10]}"
+
+
+def test_tq4_decode_matches_oracle(kvq):
+    """Decode + merge over a ragged batch (one position, a tail, an empty
+    sequence, several splits), 16 heads, splits of 512 and 2048 keys; a
+    sequence alone equals the same sequence in the batch, bit for bit."""
+    w = wl.MLA_262K
+    lens = [1, 300, 0, 1100]
+    case = TqCase(w, lens, n_heads=16)
+    assert np.array_equal(case.cache.codes.cpu().numpy(), case.codes_ref)
+    ro, rl = case.ref_attention()
+    for split in (512, 2048):
+        o, lse = case.gpu_attention(split)
+        err = rel_err(o, ro)
+        _say(f"  split={split} max_rel_err={err.max():.2e}")
+        assert err.max() < TOL
+        fin = np.isfinite(rl)
+        assert np.array_equal(fin, np.isfinite(lse)) and np.max(np.abs(lse[fin] - rl[fin])) < 1e-3 * max(1.0, np.abs(rl[fin]).max())
+        assert np.all(o[2] == 0)
+    o_b, l_b = case.gpu_attention(512)
+    for b in (1, 3):
+        pa, pm, pz = kvq.kvq_decode_attn(case.cache, case.q[b:b + 1].contiguous(), case.page_table[b:b + 1].contiguous(),
+                                         case.seq_lens[b:b + 1].contiguous(), case.max_seq_len, w.sm_scale, 512)
+        o1, l1 = kvq.kvq_merge(case.cache, pa, pm, pz, case.seq_lens[b:b + 1].contiguous(), case.max_seq_len, 512)
+        assert np.array_equal(o1.cpu().numpy()[0], o_b[b]) and np.array_equal(l1.cpu().numpy()[0], l_b[b])
+
+
+def test_tq4_decode_all_heads(kvq):
+    """All 128 heads of the workload (eight head blocks) over one sequence."""
+    w = wl.MLA_262K
+    case = TqCase(w, [700])
+    ro, rl = case.ref_attention()
+    o, lse = case.gpu_attention(512)
+    err = rel_err(o, ro)
+    _say(f"  128 heads max_rel_err={err.max():.2e}")
+    assert err.max() < TOL
