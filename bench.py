@@ -211,7 +211,7 @@ class MlaBench(_Bench):
         self.caches, self.q, self.x_new = [], [], []
         chunk = 32768
         for layer in range(w.n_layers):
-            c = kvq.Fp8Cache(lay.num_pages, w.head_dim, w.rope_dim, w.page_size, device)
+            c = self._new_cache(kvq, lay, w, device)
             for t0 in range(0, T, chunk):
                 n = min(chunk, T - t0)
                 x = wl.mla_rows(w, layer, t0, n, device)
@@ -252,16 +252,32 @@ class MlaBench(_Bench):
                                P(self.out[layer].data_ptr()), P(self.lse[layer].data_ptr()), stream)),
             ])
 
+    ROW_BYTES = 576 + 8  # code bytes + two f32 scales per position
+
+    @staticmethod
+    def _new_cache(kvq, lay, w, device):
+        return kvq.Fp8Cache(lay.num_pages, w.head_dim, w.rope_dim, w.page_size, device)
+
     @property
     def kv_bytes_per_layer(self):
-        # 576 code bytes + two f32 scales per position
-        return self.T * (self.w.head_dim + 8)
+        return self.T * self.ROW_BYTES
 
     @property
     def flops_per_layer(self):
         # per position and head: <q, k> over 576 values and the 512-wide value accumulation, 2 flop per MAC
         w = self.w
         return self.T * w.n_heads * 2 * (w.head_dim + w.kv_lora)
+
+
+class TqBench(MlaBench):
+    """The same latent workload stored with the rotated-int4 + Lloyd-Max codec
+    (288 code bytes + two f32 radii per position), decoded by its plain kernel."""
+
+    ROW_BYTES = 288 + 8
+
+    @staticmethod
+    def _new_cache(kvq, lay, w, device):
+        return kvq.TqCache(lay.num_pages, w.page_size, device)
 
 
 class DsaBench(_Bench):
@@ -642,11 +658,11 @@ def main():
     if not args.no_extras:
         extras = {}
         for name, cls in (("gqa_q4_32k", Q4Bench), ("gqa_q8_32k", Q4Bench), ("gqa_q6_32k", Q4Bench),
-                          ("ragged_q4_b16", RaggedBench), ("mla_fp8_262k", MlaBench)):
+                          ("ragged_q4_b16", RaggedBench), ("mla_fp8_262k", MlaBench), ("mla_tq4_32k", TqBench)):
             wx = wl.WORKLOADS[name]
             _log(f"bench: side measurement {name}")
             bx = cls(wx)
-            steps = max(3, min(args.steps, 10)) if cls is MlaBench else args.steps
+            steps = max(3, min(args.steps, 10)) if issubclass(cls, MlaBench) else args.steps
             mx = measure(bx, steps, args.warmup)
             e = {"layers": wx.n_layers, "seq_len": wx.seq_len or f"{min(bx.lens)}..{max(bx.lens)} x {len(bx.lens)}",
                  "split_keys": wx.split_keys, "steps": steps,

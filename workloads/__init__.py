@@ -102,7 +102,10 @@ MLA_262K = MlaWorkload("mla_fp8_262k", seed=1005, n_layers=4, batch=1, n_heads=1
 GQA_32K_Q8 = replace(GQA_32K, name="gqa_q8_32k", bits=8)
 GQA_32K_Q6 = replace(GQA_32K, name="gqa_q6_32k", bits=6)
 
-WORKLOADS = {w.name: w for w in (TINY, GQA_32K, GQA_262K, RAGGED, MLA_262K, GQA_32K_Q8, GQA_32K_Q6)}
+# The latent workload's rows at 32K positions, stored with the rotated-int4 + Lloyd-Max codec.
+MLA_TQ4_32K = replace(MLA_262K, name="mla_tq4_32k", seq_len=32768, split_keys=512)
+
+WORKLOADS = {w.name: w for w in (TINY, GQA_32K, GQA_262K, RAGGED, MLA_262K, GQA_32K_Q8, GQA_32K_Q6, MLA_TQ4_32K)}
 
 
 def shrink(w, **kw):
