@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); valid only for the kernel sources they were taken on
 # (keyed by the sha256 of the kernel file followed by the device-helper header it includes).
 TRAFFIC = {
-    "2ea86718665d1596b83501858919c76de9103266c4af7754e9b83487a706da74": {
+    "8332fe27d603f766366ded67126bb2a66ca21da6a8306e9a3c3833a8b466d6d7": {
         "fetch_kib": 147702.0, "write_kib": 3264.0, "fetch_scale": 2.0, "write_scale": 1.0,
         "profile": "profiles/decode_q4_mfma_gqa_q4_262k.md"},
 }
