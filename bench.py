@@ -194,6 +194,7 @@ class MlaBench(_Bench):
 
     DECODE = 1
     DECODE_MERGE = (1, 2)
+    ROTATED = False  # the query is rotated before the decode, the context back in the merge
 
     def __init__(self, w, device="cuda"):
         import numpy as np
@@ -226,11 +227,13 @@ class MlaBench(_Bench):
         self.pa, self.pm, self.pz = torch.empty(acc_shape, **f32), torch.empty(mz_shape, **f32), torch.empty(mz_shape, **f32)
         self.out = torch.empty((w.n_layers, 1, w.n_heads, w.kv_lora), **f32)
         self.lse = torch.empty((w.n_layers, 1, w.n_heads), **f32)
+        self.q_rot = torch.empty((1, w.n_heads, w.head_dim), **f32)
         torch.cuda.synchronize()
         for layer in range(w.n_layers):
             c = self.caches[layer]
             kvq.kvq_store(c, self.x_new[layer], None, self.slot_new)
-            kvq.kvq_decode_attn(c, self.q[layer], self.page_table, self.seq_lens, T, w.sm_scale, w.split_keys,
+            qd = kvq.kvq_tq_rotate_q(self.q[layer], out=self.q_rot) if self.ROTATED else self.q[layer]
+            kvq.kvq_decode_attn(c, qd, self.page_table, self.seq_lens, T, w.sm_scale, w.split_keys,
                                 self.pa, self.pm, self.pz)
             kvq.kvq_merge(c, self.pa, self.pm, self.pz, self.seq_lens, T, w.split_keys, out=self.out[layer],
                           lse=self.lse[layer])
@@ -240,15 +243,18 @@ class MlaBench(_Bench):
         self.raw = []
         for layer, c in enumerate(self.caches):
             d = ctypes.byref(c.desc)
+            qd = self.q_rot if self.ROTATED else self.q[layer]
+            rot = [("kvq_tq_rotate_q", (P(self.q[layer].data_ptr()), P(self.q_rot.data_ptr()), w.n_heads, stream))]
             self.raw.append([
                 ("kvq_store", (d, P(self.x_new[layer].data_ptr()), None, kvq._DTYPES[self.x_new[layer].dtype],
                                P(self.slot_new.data_ptr()), 1, stream)),
-                ("kvq_decode_attn", (d, P(self.q[layer].data_ptr()), w.n_heads, P(self.page_table.data_ptr()),
+            ] + (rot if self.ROTATED else []) + [
+                ("kvq_decode_attn", (d, P(qd.data_ptr()), w.n_heads, P(self.page_table.data_ptr()),
                                      self.page_table.shape[1], P(self.seq_lens.data_ptr()), 1, T,
                                      ctypes.c_float(w.sm_scale), w.split_keys, P(self.pa.data_ptr()),
                                      P(self.pm.data_ptr()), P(self.pz.data_ptr()), stream)),
                 ("kvq_merge", (d, P(self.pa.data_ptr()), P(self.pm.data_ptr()), P(self.pz.data_ptr()),
-                               P(self.seq_lens.data_ptr()), 1, w.n_heads, T, w.split_keys, 0,
+                               P(self.seq_lens.data_ptr()), 1, w.n_heads, T, w.split_keys, 1 if self.ROTATED else 0,
                                P(self.out[layer].data_ptr()), P(self.lse[layer].data_ptr()), stream)),
             ])
 
@@ -271,9 +277,13 @@ class MlaBench(_Bench):
 
 class TqBench(MlaBench):
     """The same latent workload stored with the rotated-int4 + Lloyd-Max codec
-    (288 code bytes + two f32 radii per position), decoded by its plain kernel."""
+    (288 code bytes + two f32 radii per position); step per layer: store,
+    rotate the query, decode on matrix cores, merge + inverse rotation."""
 
     ROW_BYTES = 288 + 8
+    ROTATED = True
+    DECODE = 2
+    DECODE_MERGE = (2, 3)
 
     @staticmethod
     def _new_cache(kvq, lay, w, device):
@@ -658,7 +668,8 @@ def main():
     if not args.no_extras:
         extras = {}
         for name, cls in (("gqa_q4_32k", Q4Bench), ("gqa_q8_32k", Q4Bench), ("gqa_q6_32k", Q4Bench),
-                          ("ragged_q4_b16", RaggedBench), ("mla_fp8_262k", MlaBench), ("mla_tq4_32k", TqBench)):
+                          ("ragged_q4_b16", RaggedBench), ("mla_fp8_262k", MlaBench), ("mla_tq4_262k", TqBench),
+                          ("mla_tq4_32k", TqBench)):
             wx = wl.WORKLOADS[name]
             _log(f"bench: side measurement {name}")
             bx = cls(wx)

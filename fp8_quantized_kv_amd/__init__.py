@@ -32,13 +32,14 @@ FMT_Q6_H32 = 4
 H32_FORMATS = (FMT_Q4_H32, FMT_Q8_H32, FMT_Q6_H32)
 FMT_FP8_E4M3_ROW = 2
 FMT_TQ4_LATENT = 5
+ROTATED_FORMATS = H32_FORMATS + (FMT_TQ4_LATENT,)   # the merge rotates the context back
 
 DT_F32, DT_BF16, DT_F16 = 0, 1, 2
 _DTYPES = {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float16: DT_F16}
 
 EXPORTED = ("kvq_status_string", "kvq_row_bytes", "kvq_pool_bytes", "kvq_num_splits", "kvq_store",
             "kvq_rotate_q", "kvq_store_rotate_q", "kvq_decode_attn", "kvq_decode_attn_sel", "kvq_merge",
-            "kvq_stream_read")
+            "kvq_tq_rotate_q", "kvq_stream_read")
 
 
 class KvqCacheDesc(ctypes.Structure):
@@ -65,6 +66,7 @@ def _load():
         "kvq_store_rotate_q": ([C, P, P, I32, P, I32, P, I32, P, I32, P], I32),
         "kvq_decode_attn": ([C, P, I32, P, I32, P, I32, I32, F, I32, P, P, P, P], I32),
         "kvq_merge": ([C, P, P, P, P, I32, I32, I32, I32, I32, P, P, P], I32),
+        "kvq_tq_rotate_q": ([P, P, I32, P], I32),
         "kvq_stream_read": ([P, ctypes.c_size_t, I32, P, P], I32),
         "kvq_decode_attn_sel": ([C, P, I32, P, I32, P, P, I32, I32, F, I32, P, P, P, P], I32),
     }
@@ -226,6 +228,20 @@ def kvq_rotate_q(q, out=None):
     return out
 
 
+def kvq_tq_rotate_q(q, out=None):
+    """The TQ4 latent format's query rotation of f32 rows [..., 576]; returns an f32 tensor of q's shape
+    (out may be q itself)."""
+    if q.dtype != torch.float32 or int(q.shape[-1]) != 576:
+        raise ValueError("kvq_tq_rotate_q takes f32 rows of 576")
+    rows = q.numel() // 576
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    qp = _dev(q, "q")
+    op = _dev(out, "out", dtype=torch.float32, shape=q.shape)
+    _check(lib.kvq_tq_rotate_q(qp, op, rows, _stream(q)), "kvq_tq_rotate_q")
+    return out
+
+
 def kvq_store_rotate_q(cache, k, v, slot_mapping, q, out=None):
     """kvq_store(cache, k, v, slot_mapping) and kvq_rotate_q(q) in one launch (4-bit cache only);
     returns the rotated query (f32, q's shape)."""
@@ -326,7 +342,7 @@ def kvq_merge(cache, part_acc, part_m, part_z, seq_lens, max_seq_len, split_keys
     op = _dev(out, "out", dtype=torch.float32, shape=(B, Hq, Dv))
     lp = _dev(lse, "lse", dtype=torch.float32, shape=(B, Hq)) if lse is not None else None
     _check(lib.kvq_merge(ctypes.byref(cache.desc), pa, pm, pz, slp, B, Hq, int(max_seq_len), int(split_keys),
-                         1 if cache.fmt in H32_FORMATS else 0, op, lp, _stream(part_acc)), "kvq_merge")
+                         1 if cache.fmt in ROTATED_FORMATS else 0, op, lp, _stream(part_acc)), "kvq_merge")
     return out, lse
 
 
@@ -344,7 +360,7 @@ def kvq_stream_read(src, non_temporal=True, xor_out=None):
 
 
 def decode_step(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_keys, bufs=None, new_kv=None):
-    """[store the step's rows] -> rotate (Q4) -> decode -> merge on preallocated buffers; returns (out, lse).
+    """[store the step's rows] -> rotate (Q4, TQ4) -> decode -> merge on preallocated buffers; returns (out, lse).
 
     new_kv = (k, v, slot_mapping) stores those rows first (for the 4-bit cache in the same launch as the
     query rotation, kvq_store_rotate_q; v is None for the fp8 cache)."""
@@ -354,8 +370,11 @@ def decode_step(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_key
             q = kvq_store_rotate_q(cache, *new_kv, q, out=q_rot)
         else:
             q = kvq_rotate_q(q, out=q_rot)
-    elif new_kv is not None:
-        kvq_store(cache, *new_kv)
+    else:
+        if new_kv is not None:
+            kvq_store(cache, *new_kv)
+        if cache.fmt == FMT_TQ4_LATENT:
+            q = kvq_tq_rotate_q(q, out=q_rot)
     pa, pm, pz = kvq_decode_attn(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_keys,
                                  *(() if bufs is None else (bufs["part_acc"], bufs["part_m"], bufs["part_z"])))
     return kvq_merge(cache, pa, pm, pz, seq_lens, max_seq_len, split_keys,

@@ -45,6 +45,17 @@
 //    16-lane group addresses key slot e at channels 4m .. 4m + 3, so lane j
 //    receives channel j of keys e = 0..3; the second read takes slots 4..7).
 //
+// The rotated-int4 + Lloyd-Max latent cache (the same pull request, Summary
+// "Why rotated-int4 for the 4-bit tier": 288 nibble bytes and two radii per
+// row) runs through the same kernel in rotated space: the query arrives
+// rotated, the staging turns each nibble into the f16 value of c * lev[code]
+// (two byte tables looked up with v_perm_b32, the code's bit 3 choosing
+// between the halves of the table) and the row's scales become r_L / (c
+// sqrt(512)) and r_R / (c sqrt(64)), so everything after the staging is the
+// fp8 code.  c is the scale in [1, 2) that brings the 16 levels closest to
+// the f16 grid (largest relative deviation under 1e-4, against 3.2e-4 at
+// c = 1); the partials are the rotated context, rotated back after the merge.
+//
 // Selected rows (colibri split-T commit, DSA gather: attend the selected
 // rows, given as absolute positions): the keys of a split are entries
 // j0 .. j1-1 of the sequence's list instead of positions j0 .. j1-1.  The
@@ -75,9 +86,16 @@ constexpr int kXOff = 2 * kStage;                    // partial-score exchange: 
 constexpr int kLds = kXOff + kWaves * 64 * 8 * 4;
 constexpr int kSelOff = kLds;                        // selected rows: the split's slot table
 constexpr int kLdsSel = kSelOff + 2048 * 4;          // int32 per entry, split_keys <= 2048
-constexpr int kChunks = kTile * kD / 16;             // 16-byte code chunks per tile (1152)
-constexpr int kChunkRow = kD / 16;                   // chunks per row (36)
-constexpr int kPerThread = (kChunks + kThreads - 1) / kThreads;  // 3 (the third of 128 threads)
+// Code bytes per row, 16-byte chunks per row and per tile, chunks per thread:
+// fp8 576, 36, 1152, 3 (the third for 128 threads); TQ4 288, 18, 576, 2 (the
+// second for 64 threads).  Threads 128..143 own the scale chunks in their last
+// slot in both.
+template <bool TQ> struct Rows {
+    static constexpr int kBytes = TQ ? kD / 2 : kD;
+    static constexpr int kChunkRow = kBytes / 16;
+    static constexpr int kChunks = kTile * kChunkRow;
+    static constexpr int kPerThread = (kChunks + kThreads - 1) / kThreads;
+};
 constexpr int kMaxRuns = 128;                        // 16-key runs per split (split_keys <= 2048)
 constexpr int kQG = 9;                               // score channel groups (of 32) per wave
 constexpr int kNBW = kL / 16 / 2;                    // 16 output blocks of 16 channels per wave
@@ -98,13 +116,39 @@ __device__ __forceinline__ uint32_t clear_nan_codes(uint32_t w) {
     return w & ~(t | (t - (t >> 7)));
 }
 
+// 8 TQ4 codes (one dword: byte k holds code 2k in its low nibble, 2k+1 in its
+// high nibble) as the 8 f16 values c * lev[code], in element order.  lo / hi
+// hold the low / high bytes of the 16 f16 table entries (entry k is byte k of
+// the 16-byte table): v_perm_b32 looks up codes 0..7 in one 8-byte half and
+// 8..15 in the other, and the code's bit 3 picks the result byte-wise.
+__device__ __forceinline__ void tq_cvt8(uint32_t w, const uint32_t (&lo)[4], const uint32_t (&hi)[4], uint32_t* d) {
+    const uint32_t ce = w & 0x07070707u, co = (w >> 4) & 0x07070707u;          // codes & 7: even / odd elements
+    const uint32_t me = ((w >> 3) & 0x01010101u) * 0xFFu, mo = ((w >> 7) & 0x01010101u) * 0xFFu;  // bit 3
+    const uint32_t le = __builtin_amdgcn_perm(lo[1], lo[0], ce), le8 = __builtin_amdgcn_perm(lo[3], lo[2], ce);
+    const uint32_t he = __builtin_amdgcn_perm(hi[1], hi[0], ce), he8 = __builtin_amdgcn_perm(hi[3], hi[2], ce);
+    const uint32_t lO = __builtin_amdgcn_perm(lo[1], lo[0], co), lO8 = __builtin_amdgcn_perm(lo[3], lo[2], co);
+    const uint32_t hO = __builtin_amdgcn_perm(hi[1], hi[0], co), hO8 = __builtin_amdgcn_perm(hi[3], hi[2], co);
+    const uint32_t Le = (le & ~me) | (le8 & me), He = (he & ~me) | (he8 & me);  // bytes of elements 0, 2, 4, 6
+    const uint32_t Lo = (lO & ~mo) | (lO8 & mo), Ho = (hO & ~mo) | (hO8 & mo);  // bytes of elements 1, 3, 5, 7
+    const uint32_t e01 = __builtin_amdgcn_perm(He, Le, 0x05010400u);  // f16 of elements 0, 2
+    const uint32_t e23 = __builtin_amdgcn_perm(He, Le, 0x07030602u);  // elements 4, 6
+    const uint32_t o01 = __builtin_amdgcn_perm(Ho, Lo, 0x05010400u);  // elements 1, 3
+    const uint32_t o23 = __builtin_amdgcn_perm(Ho, Lo, 0x07030602u);  // elements 5, 7
+    d[0] = __builtin_amdgcn_perm(o01, e01, 0x05040100u);  // elements 0, 1
+    d[1] = __builtin_amdgcn_perm(o01, e01, 0x07060302u);  // 2, 3
+    d[2] = __builtin_amdgcn_perm(o23, e23, 0x05040100u);  // 4, 5
+    d[3] = __builtin_amdgcn_perm(o23, e23, 0x07060302u);  // 6, 7
+}
+
 // 2^e for an integer e in [-126, 127], exactly.
 __device__ __forceinline__ float exp2i(int e) { return __uint_as_float(uint32_t(e + 127) << 23); }
 
-template <bool SEL>
+template <bool SEL, bool TQ>
 __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __restrict__ codes,
                                                             const float* __restrict__ scales, int page_size,
-                                                            int num_pages, DecodeArgs a) {
+                                                            int num_pages, DecodeArgs a, TqMfmaTable tab) {
+    using R = Rows<TQ>;
+    constexpr int kRowB = R::kBytes, kChunkRow = R::kChunkRow, kChunks = R::kChunks, kPerThread = R::kPerThread;
     __shared__ __attribute__((aligned(16))) uint8_t smem[SEL ? kLdsSel : kLds];
 
     const int s = blockIdx.x, hblk = blockIdx.y, b = blockIdx.z;
@@ -208,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
             for (int i = 0; i < kPerThread; ++i) {
                 if (tid + kThreads * i < kChunks) {
                     const int64_t sl = max(tab[chunk_row(i)], 0);
-                    stg[i] = *reinterpret_cast<const u32x4*>(codes + sl * kD + 16 * chunk_col(i));
+                    stg[i] = *reinterpret_cast<const u32x4*>(codes + sl * kRowB + 16 * chunk_col(i));
                 } else if (has_scale) {
                     const int64_t sl = max(tab[tid - 128], 0);
                     const uint2 v = *reinterpret_cast<const uint2*>(scales + sl * 2);
@@ -218,13 +262,13 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
             return;
         }
         const int64_t ra = run_slot(2 * t), rb = run_slot(2 * t + 1);
-        const uint8_t* ca = codes + ra * kD;
-        const uint8_t* cb = codes + rb * kD;
+        const uint8_t* ca = codes + ra * kRowB;
+        const uint8_t* cb = codes + rb * kRowB;
 #pragma unroll
         for (int i = 0; i < kPerThread; ++i) {
             if (tid + kThreads * i < kChunks) {
                 const int kr = chunk_row(i);
-                stg[i] = *reinterpret_cast<const u32x4*>((kr >= 16 ? cb : ca) + (kr & 15) * kD + 16 * chunk_col(i));
+                stg[i] = *reinterpret_cast<const u32x4*>((kr >= 16 ? cb : ca) + (kr & 15) * kRowB + 16 * chunk_col(i));
             } else if (has_scale) {
                 const int key = 2 * (tid - 128);  // keys key, key + 1
                 stg[i] = *reinterpret_cast<const u32x4*>(scales + ((key >= 16 ? rb : ra) + (key & 15)) * 2);
@@ -235,7 +279,14 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
         uint8_t* st = smem + (t & 1) * kStage;
 #pragma unroll
         for (int i = 0; i < kPerThread; ++i) {
-            if (tid + kThreads * i < kChunks) {
+            if (TQ && tid + kThreads * i < kChunks) {
+                uint32_t d[16];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tq_cvt8(stg[i][e], tab.lo, tab.hi, d + 4 * e);
+                u32x4* dst = reinterpret_cast<u32x4*>(st + chunk_row(i) * kPitch + 64 * chunk_col(i));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[e] = u32x4{d[4 * e], d[4 * e + 1], d[4 * e + 2], d[4 * e + 3]};
+            } else if (tid + kThreads * i < kChunks) {
                 u32x4 w = stg[i];
                 // NaN codes are rare: test the chunk, clear only if one is present.
                 uint32_t any = 0u;
@@ -251,6 +302,10 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
             } else if (has_scale) {
                 if (SEL)
                     *reinterpret_cast<uint2*>(st + kScaleOff + 8 * (tid - 128)) = make_uint2(stg[i][0], stg[i][1]);
+                else if (TQ)  // radii (latent, rope) of two keys -> the table values' multipliers
+                    *reinterpret_cast<float4*>(st + kScaleOff + 16 * (tid - 128)) =
+                        make_float4(__uint_as_float(stg[i][0]) * tab.f_latent, __uint_as_float(stg[i][1]) * tab.f_rope,
+                                    __uint_as_float(stg[i][2]) * tab.f_latent, __uint_as_float(stg[i][3]) * tab.f_rope);
                 else
                     *reinterpret_cast<u32x4*>(st + kScaleOff + 16 * (tid - 128)) = stg[i];
             }
@@ -452,12 +507,21 @@ bool decode_fp8_mfma_supported(const Fp8Pool& pool, const DecodeArgs& a) {
 
 hipError_t launch_decode_fp8_mfma(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s) {
     const dim3 grid(unsigned(a.n_splits), unsigned((a.n_q_heads + kHeadsWG - 1) / kHeadsWG), unsigned(a.batch));
+    const TqMfmaTable none{};
     if (a.sel)
-        decode_fp8_mfma<true><<<grid, dim3(kThreads), 0, s>>>(pool.codes, pool.scales, pool.page_size, pool.num_pages,
-                                                              a);
+        decode_fp8_mfma<true, false><<<grid, dim3(kThreads), 0, s>>>(pool.codes, pool.scales, pool.page_size,
+                                                                     pool.num_pages, a, none);
     else
-        decode_fp8_mfma<false><<<grid, dim3(kThreads), 0, s>>>(pool.codes, pool.scales, pool.page_size,
-                                                               pool.num_pages, a);
+        decode_fp8_mfma<false, false><<<grid, dim3(kThreads), 0, s>>>(pool.codes, pool.scales, pool.page_size,
+                                                                      pool.num_pages, a, none);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_tq4_mfma(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s) {
+    if (a.sel) return hipErrorInvalidValue;
+    const dim3 grid(unsigned(a.n_splits), unsigned((a.n_q_heads + kHeadsWG - 1) / kHeadsWG), unsigned(a.batch));
+    decode_fp8_mfma<false, true><<<grid, dim3(kThreads), 0, s>>>(pool.codes, pool.scales, pool.page_size,
+                                                                 pool.num_pages, a, tq_mfma_table());
     return hipGetLastError();
 }
 

@@ -206,7 +206,21 @@ struct TqTables {
 const TqTables& tq_tables();
 hipError_t launch_store_tq4(const Fp8Pool& pool, const void* x, InType dt, const int64_t* slots, int n_tokens,
                             hipStream_t s);
-hipError_t launch_decode_tq4(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_tq4_simple(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s);
+// The levels as the matrix-core decode uses them: f16 of c * lev[k] split into
+// low / high bytes (entry k is byte k), and the radius multipliers
+// 1 / (c sqrt(512)), 1 / (c sqrt(64)).
+struct TqMfmaTable {
+    uint32_t lo[4];
+    uint32_t hi[4];
+    float f_latent;
+    float f_rope;
+    float c;          // the scale (host-side record)
+    float max_dev;    // max_k |f16(c lev[k]) - c lev[k]| / |c lev[k]|
+};
+const TqMfmaTable& tq_mfma_table();
+hipError_t launch_decode_tq4_mfma(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_tq_rotate(const float* x, float* y, int64_t n_rows, int row_len, bool inverse, hipStream_t s);
 
 struct MergeArgs {
     const float* part_acc;

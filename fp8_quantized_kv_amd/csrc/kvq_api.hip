@@ -178,7 +178,8 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_h
                            hipStream_t stream) {
     kvq_status st = check_cache(cache);
     if (st != KVQ_OK) return st;
-    st = check_seq_args(cache, n_q_heads, seq_lens, batch, max_seq_len, split_keys, 512);
+    // Hadamard-32 formats split at the 512-key chunk; the latent formats at any 32-key tile
+    st = check_seq_args(cache, n_q_heads, seq_lens, batch, max_seq_len, split_keys, is_h32(cache->format) ? 512 : 32);
     if (st != KVQ_OK) return st;
     if (max_pages < 1 || int64_t(max_seq_len) > int64_t(max_pages) * cache->page_size) return KVQ_ERR_INVALID_ARG;
     if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return KVQ_ERR_INVALID_ARG;
@@ -195,7 +196,10 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_h
         return launched(kvq::launch_decode_q4_simple(pool, a, stream));
     }
     const kvq::Fp8Pool pool = fp8_pool(cache);
-    if (cache->format == KVQ_FMT_TQ4_LATENT) return launched(kvq::launch_decode_tq4(pool, a, stream));
+    if (cache->format == KVQ_FMT_TQ4_LATENT) {
+        if (kvq::decode_fp8_mfma_supported(pool, a)) return launched(kvq::launch_decode_tq4_mfma(pool, a, stream));
+        return launched(kvq::launch_decode_tq4_simple(pool, a, stream));
+    }
     if (kvq::decode_fp8_mfma_supported(pool, a)) return launched(kvq::launch_decode_fp8_mfma(pool, a, stream));
     return launched(kvq::launch_decode_fp8_simple(pool, a, stream));
 }
@@ -230,8 +234,9 @@ kvq_status kvq_merge(const kvq_cache* cache, const float* part_acc, const float*
     if (st != KVQ_OK) return st;
     st = check_seq_args(cache, n_q_heads, seq_lens, batch, max_seq_len, split_keys, 32);
     if (st != KVQ_OK) return st;
-    const bool q4 = is_h32(cache->format);  // rotated formats: inverse rotation, Dv = head_dim
-    if (inverse_rotate != (q4 ? 1 : 0)) return KVQ_ERR_INVALID_ARG;
+    const bool q4 = is_h32(cache->format);  // Hadamard-32 formats: inverse rotation in the merge, Dv = head_dim
+    const bool tq = cache->format == KVQ_FMT_TQ4_LATENT;  // inverse rotation after the merge
+    if (inverse_rotate != (q4 || tq ? 1 : 0)) return KVQ_ERR_INVALID_ARG;
     if (batch == 0) return KVQ_OK;
     if (!aligned(part_acc) || !aligned(part_m, 4) || !aligned(part_z, 4) || !aligned(out) ||
         (lse && !aligned(lse, 4)))
@@ -240,7 +245,19 @@ kvq_status kvq_merge(const kvq_cache* cache, const float* part_acc, const float*
     kvq::MergeArgs a{part_acc, part_m, part_z, seq_lens, batch, n_q_heads, max_seq_len,
                      kvq_num_splits(max_seq_len, split_keys), split_keys,
                      q4 ? cache->head_dim : cache->head_dim - cache->rope_dim, q4, out, lse};
+    if (tq) {
+        st = launched(kvq::launch_merge(a, stream));
+        if (st != KVQ_OK) return st;
+        return launched(kvq::launch_tq_rotate(out, out, int64_t(batch) * n_q_heads, 512, true, stream));
+    }
     return launched(kvq::launch_merge(a, stream));
+}
+
+kvq_status kvq_tq_rotate_q(const float* q, float* q_rot, int32_t n_rows, hipStream_t stream) {
+    if (n_rows < 0) return KVQ_ERR_INVALID_ARG;
+    if (n_rows == 0) return KVQ_OK;
+    if (!aligned(q) || !aligned(q_rot)) return KVQ_ERR_INVALID_ARG;
+    return launched(kvq::launch_tq_rotate(q, q_rot, n_rows, 576, false, stream));
 }
 
 kvq_status kvq_stream_read(const void* src, size_t bytes, int32_t non_temporal, uint32_t* xor_out,

@@ -20,11 +20,13 @@
 // radii f32 [slot][2].  A zero, NaN or infinite row is stored inert (radius
 // 0, codes 0).
 //
-// Decode (plain fp32 vector kernel, the correctness path of this format):
-// the query is rotated with the same transform in the prologue; scores and
-// the context accumulate in rotated space against levels x radius/sqrt(n);
-// the split's context is rotated back before its partial is written, so the
-// partials and the merge are those of the fp8 latent cache.
+// Attention runs in rotated space, as for the 4-bit cache ("rotate the
+// queries once ... rotate the output back once"): the query rows are rotated
+// by tq_rotate_rows (kvq_tq_rotate), the decode scores and accumulates
+// against levels x radius/sqrt(n), the partials and their merge are those of
+// the fp8 latent cache, and the merged 512-wide context is rotated back by
+// tq_rotate_rows (inverse).  The decode here is the plain fp32 kernel, for
+// the shapes the matrix-core kernel (decode_fp8_mfma.hip) does not take.
 #include "internal.h"
 
 #include <cmath>
@@ -174,32 +176,63 @@ constexpr int kTHB = 16;     // heads per workgroup
 constexpr int kTTile = 16;   // keys per tile
 constexpr int kTL = 512, kTR = 64, kTD = 576;
 
-// In-place rotation of rows of n values in LDS (n = 512 or 64) for `rows`
-// rows at `stride`, by all threads: signs (forward) or not, the butterfly,
-// times 1/sqrt(n), then signs (inverse).  fp32, stage order h = 1 .. n/2.
+// Rotation of rows by one wave each (kvq_tq_rotate): row_len 576 (a query:
+// both parts) or 512 (a context: the latent part).  Forward: signs, the
+// butterfly, 1/sqrt(n); inverse: the butterfly, 1/sqrt(n), the signs.  Lane
+// l holds elements 8l .. 8l + 7 of the 512-wide part and lanes 0..7 those of
+// the 64-wide part, as in the store.
 template <int N>
-__device__ void lds_rotate(float* base, int stride, int rows, uint64_t seed, bool inverse, int tid) {
+__device__ __forceinline__ void rotate_part(float (&v)[8], int lane, uint64_t seed, bool inverse) {
+    constexpr int LANES = N / 8;
     if (!inverse) {
-        for (int i = tid; i < rows * N; i += kTT) base[(i / N) * stride + i % N] *= tq_sign(seed, i % N);
-        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = v[e] * tq_sign(seed, 8 * lane + e);
     }
-    for (int h = 1; h < N; h <<= 1) {
-        for (int i = tid; i < rows * (N / 2); i += kTT) {
-            const int row = i / (N / 2), p = i % (N / 2);
-            const int lo = (p / h) * 2 * h + p % h;  // index with bit h clear
-            float* r = base + row * stride;
-            const float a = r[lo], b = r[lo + h];
-            r[lo] = a + b;
-            r[lo + h] = a - b;
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if ((e & h) == 0) {
+                const float a = v[e], b = v[e + h];
+                v[e] = a + b;
+                v[e + h] = a - b;
+            }
+#pragma unroll
+    for (int hl = 1; hl < LANES; hl <<= 1) {
+        const bool low = (lane & hl) == 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float o = __shfl_xor(v[e], hl, 64);
+            v[e] = low ? v[e] + o : o - v[e];
         }
-        __syncthreads();
     }
     const float c = float(1.0 / std::sqrt(double(N)));
-    for (int i = tid; i < rows * N; i += kTT) {
-        float& e = base[(i / N) * stride + i % N];
-        e = inverse ? (e * c) * tq_sign(seed, i % N) : e * c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = inverse ? (v[e] * c) * tq_sign(seed, 8 * lane + e) : v[e] * c;
+}
+
+__global__ __launch_bounds__(64) void tq_rotate_rows(const float* __restrict__ x, float* __restrict__ y, int64_t n_rows,
+                                                     int row_len, int inverse) {
+    const int64_t r = blockIdx.x;
+    const int lane = threadIdx.x;
+    if (r >= n_rows) return;
+    const float* xr = x + r * row_len;
+    float* yr = y + r * row_len;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = xr[8 * lane + e];
+    rotate_part<kTL>(v, lane, kSeedLatent, inverse != 0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) yr[8 * lane + e] = v[e];
+    if (row_len == kTD) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = lane < 8 ? xr[kTL + 8 * lane + e] : 0.0f;
+        rotate_part<kTR>(v, lane, kSeedRope, inverse != 0);
+        if (lane < 8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) yr[kTL + 8 * lane + e] = v[e];
+        }
     }
-    __syncthreads();
 }
 
 __global__ __launch_bounds__(kTT) void decode_tq4_simple(const uint8_t* __restrict__ codes,
@@ -244,9 +277,7 @@ __global__ __launch_bounds__(kTT) void decode_tq4_simple(const uint8_t* __restri
         z_s[tid] = 0.0f;
     }
     __syncthreads();
-    // the query in rotated space, pre-scaled by sm_scale * log2(e)
-    lds_rotate<kTL>(&qs[0][0], kTD, kTHB, kSeedLatent, false, tid);
-    lds_rotate<kTR>(&qs[0][kTL], kTD, kTHB, kSeedRope, false, tid);
+    // the (rotated) query, pre-scaled by sm_scale * log2(e)
     const float qscale = a.sm_scale * kLog2e;
     for (int i = tid; i < kTHB * kTD; i += kTT) qs[i / kTD][i % kTD] *= qscale;
 
@@ -345,14 +376,12 @@ __global__ __launch_bounds__(kTT) void decode_tq4_simple(const uint8_t* __restri
         }
         __syncthreads();
     }
-    // the split's context back from rotated space (the query rows are free now)
+    // the split's context, in rotated space
 #pragma unroll
     for (int ci = 0; ci < CPT; ++ci)
 #pragma unroll
-        for (int h = 0; h < kTHB; ++h) qs[h][tid + ci * kTT] = acc[ci][h];
-    __syncthreads();
-    lds_rotate<kTL>(&qs[0][0], kTD, kTHB, kSeedLatent, true, tid);
-    for (int i = tid; i < nh * kTL; i += kTT) a.part_acc[((hb + i / kTL) * S + s) * kTL + i % kTL] = qs[i / kTL][i % kTL];
+        for (int h = 0; h < kTHB; ++h)
+            if (h < nh) a.part_acc[((hb + h) * S + s) * kTL + tid + ci * kTT] = acc[ci][h];
     if (tid < nh) {
         a.part_m[(hb + tid) * S + s] = m_s[tid] * kLn2;
         a.part_z[(hb + tid) * S + s] = z_s[tid];
@@ -360,6 +389,57 @@ __global__ __launch_bounds__(kTT) void decode_tq4_simple(const uint8_t* __restri
 }
 
 }  // namespace
+
+// The value of a double rounded to the nearest f16 (ties to even), for
+// positive values in the f16 normal range.
+static double round_f16(double v) {
+    int e;
+    std::frexp(v, &e);                            // v = m 2^e, m in [0.5, 1)
+    const double quantum = std::ldexp(1.0, e - 11);  // 10 fraction bits after the leading one
+    return std::nearbyint(v / quantum) * quantum;
+}
+
+// The matrix-core decode reads the levels as f16.  Scaling all of them by a
+// common c (undone in the radius multipliers) lets the 16 values sit closer
+// to the f16 grid: c is the multiple of 2^-16 in [1, 2) with the smallest
+// largest relative deviation (about 9.5e-5, against 3.2e-4 at c = 1).
+static TqMfmaTable make_mfma_table() {
+    const TqTables& tb = tq_tables();
+    double best_c = 1.0, best = 1.0;
+    for (int i = 0; i < 65536; ++i) {
+        const double c = 1.0 + i / 65536.0;
+        double dev = 0.0;
+        for (int k = 0; k < 16; ++k) {
+            const double v = c * std::fabs(double(tb.lev[k]));
+            dev = std::fmax(dev, std::fabs(round_f16(v) - v) / v);
+        }
+        if (dev < best) {
+            best = dev;
+            best_c = c;
+        }
+    }
+    TqMfmaTable t{};
+    for (int k = 0; k < 16; ++k) {
+        // f16 bits of the rounded value: sign, biased exponent, 10 fraction bits
+        const double v = round_f16(best_c * std::fabs(double(tb.lev[k])));
+        int e;
+        const double m = std::frexp(v, &e);  // v = m 2^e, m in [0.5, 1)
+        const uint32_t frac = uint32_t(std::ldexp(m, 11)) - 1024u;
+        const uint32_t bits = (tb.lev[k] < 0.0f ? 0x8000u : 0u) | (uint32_t(e - 1 + 15) << 10) | frac;
+        t.lo[k / 4] |= uint32_t(bits & 0xFF) << (8 * (k % 4));
+        t.hi[k / 4] |= uint32_t(bits >> 8) << (8 * (k % 4));
+    }
+    t.f_latent = float(1.0 / (best_c * std::sqrt(512.0)));
+    t.f_rope = float(1.0 / (best_c * 8.0));
+    t.c = float(best_c);
+    t.max_dev = float(best);
+    return t;
+}
+
+const TqMfmaTable& tq_mfma_table() {
+    static const TqMfmaTable t = make_mfma_table();
+    return t;
+}
 
 const TqTables& tq_tables() {
     static const TqTables tb = make_tables();
@@ -385,7 +465,13 @@ hipError_t launch_store_tq4(const Fp8Pool& pool, const void* x, InType dt, const
     return hipGetLastError();
 }
 
-hipError_t launch_decode_tq4(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_tq_rotate(const float* x, float* y, int64_t n_rows, int row_len, bool inverse, hipStream_t s) {
+    if (n_rows == 0) return hipSuccess;
+    tq_rotate_rows<<<dim3(unsigned(n_rows)), dim3(64), 0, s>>>(x, y, n_rows, row_len, inverse ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_tq4_simple(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s) {
     const int n_hblk = (a.n_q_heads + kTHB - 1) / kTHB;
     const dim3 grid(unsigned(a.n_splits), unsigned(n_hblk), unsigned(a.batch)), block(kTT);
     decode_tq4_simple<<<grid, block, 0, s>>>(pool.codes, pool.scales, pool.page_size, pool.num_pages, a, tq_tables());

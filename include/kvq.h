@@ -112,9 +112,12 @@ typedef enum {
  *   k_pool: codes [num_pages*page_size][288] (256 latent + 32 rope bytes,
  *   element 2k in the low nibble); v_pool = NULL; scale_pool: f32
  *   [num_pages*page_size][2] = {latent radius, rope radius}; radius 0 marks an
- *   inert (zero) row.  q for kvq_decode_attn is the unrotated [B][H][576]
- *   query (the kernel rotates it); partials and kvq_merge are as for FP8.
- *   Decode runs a plain vector kernel.
+ *   inert (zero) row.  Attention runs in rotated space (the same Summary:
+ *   rotate the queries once, the output back once): q for kvq_decode_attn
+ *   is the query rotated by kvq_tq_rotate_q, the partials hold the rotated
+ *   context, and kvq_merge rotates the merged context back (inverse_rotate
+ *   = 1).  The decode runs on matrix cores when the page size is a multiple
+ *   of 16 and split_keys at most 2048, else on a plain vector kernel.
  */
 typedef struct kvq_cache {
     int32_t format;        /* kvq_format */
@@ -212,14 +215,19 @@ kvq_status kvq_store_rotate_q(const kvq_cache* cache, const void* k, const void*
  *      head h reads KV head h / (n_q_heads / num_kv_heads); k_j, v_j are the
  *      dequantized rotated rows (scale * code), acc is in the rotated domain.
  *      Dv = head_dim.
+ * TQ4: q = the rotated query (kvq_tq_rotate_q) [batch][n_q_heads][576] f32;
+ *      k_j = lev[code] * radius / sqrt(n) per part, in rotated space; the
+ *      latent is the value, acc is in rotated space; Dv = 512.
  * FP8: q = [batch][n_q_heads][head_dim] f32 (latent part then rope part);
  *      s_j = sm_scale*(scL_j <qL, dec(Lc_j)> + scR_j <qR, dec(Rc_j)>),
  *      v_j = scL_j dec(Lc_j) (the latent is the value); Dv = head_dim -
  *      rope_dim.  NaN codes (0x7F, 0xFF) read as 0.
  * page_table: device int32 [batch][max_pages]; seq_lens: device int32
  * [batch], each in [0, max_seq_len]; max_seq_len <= max_pages*page_size.
- * split_keys: a positive multiple of 512 (the TensorFold chunk size); at most
- * 16384 splits per sequence.
+ * split_keys: a positive multiple of 512 (the TensorFold chunk size) for the
+ * Hadamard-32 formats, of 32 (the latent kernels' key tile) for FP8 and TQ4 --
+ * short splits give a short context more workgroups; at most 16384 splits per
+ * sequence.
  * part_acc: [batch][n_q_heads][S][Dv] f32, part_m / part_z: [batch][n_q_heads][S]
  * f32 with S = kvq_num_splits(max_seq_len, split_keys).
  * Requires n_q_heads % num_kv_heads == 0 and a group of at most 16 query
@@ -259,11 +267,13 @@ kvq_status kvq_decode_attn_sel(const kvq_cache* cache, const float* q, int32_t n
  * the four are added in order 0, 1, 2, 3;
  * followed for Q4 by the single inverse rotation (H32 is its own inverse):
  *   M = max_s m_s, Z = sum_s z_s exp(m_s - M),
- *   out = R( sum_s acc_s exp(m_s - M) / Z ),  R = H32 (Q4/Q8/Q6) or identity (FP8),
+ *   out = R( sum_s acc_s exp(m_s - M) / Z ),  R = H32 (Q4/Q8/Q6), the inverse
+ *   of the latent part's randomized Hadamard transform (TQ4, a second launch
+ *   on out) or identity (FP8),
  *   lse = M + log Z.
  * A sequence with T = 0 gives out = 0 and lse = -inf.  Only the splits that
- * cover [0, T_b) are read.  inverse_rotate must be 1 for the Hadamard-32
- * formats (Q4, Q8, Q6) and 0 for FP8.
+ * cover [0, T_b) are read.  inverse_rotate must be 1 for the rotated formats
+ * (Q4, Q8, Q6, TQ4) and 0 for FP8.
  * seq_lens, max_seq_len and split_keys are those of the decode call that
  * wrote the partials (for kvq_decode_attn_sel: n_sel and max_sel); split_keys
  * is a positive multiple of 32.
@@ -271,6 +281,17 @@ kvq_status kvq_decode_attn_sel(const kvq_cache* cache, const float* q, int32_t n
 kvq_status kvq_merge(const kvq_cache* cache, const float* part_acc, const float* part_m, const float* part_z,
                      const int32_t* seq_lens, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
                      int32_t split_keys, int32_t inverse_rotate, float* out, float* lse, hipStream_t stream);
+
+/* Query rotation of the TQ4 latent format (the colibri pull request's
+ * Summary, "Why rotated-int4 for the 4-bit tier": the query is rotated once,
+ * with the rotation the rows were stored with): each row's 512 latent values
+ * and 64 rope values are rotated by their parts' randomized Hadamard
+ * transforms, y = H (s * x) / sqrt(n) (signs s from SplitMix64 with the
+ * seeds above, H the Sylvester Hadamard matrix), in fp32 (the butterfly, then
+ * x fp32(1/sqrt(n))).
+ * q, q_rot: device f32 [n_rows][576], 16-byte aligned; q == q_rot is
+ * allowed (in place); other overlap is not. */
+kvq_status kvq_tq_rotate_q(const float* q, float* q_rot, int32_t n_rows, hipStream_t stream);
 
 /* ---------------------------------------------------------------- measurement */
 

@@ -163,14 +163,17 @@ class TqCase:
                 oracle.tq_store(self.codes_ref, self.radii_ref, x.float().cpu().numpy(), slots.numpy())
 
     def gpu_attention(self, split_keys):
+        """Rotate the query, decode, merge (+ inverse rotation)."""
         import fp8_quantized_kv_amd as kvq
-        pa, pm, pz = kvq.kvq_decode_attn(self.cache, self.q, self.page_table, self.seq_lens, self.max_seq_len,
+        q_rot = kvq.kvq_tq_rotate_q(self.q)
+        pa, pm, pz = kvq.kvq_decode_attn(self.cache, q_rot, self.page_table, self.seq_lens, self.max_seq_len,
                                         self.w.sm_scale, split_keys)
         out, lse = kvq.kvq_merge(self.cache, pa, pm, pz, self.seq_lens, self.max_seq_len, split_keys)
         torch.cuda.synchronize()
         return out.cpu().numpy(), lse.cpu().numpy()
 
-    def ref_attention(self):
-        return oracle.tq_attention(self.codes_ref, self.radii_ref, self.q.cpu().numpy(), self.lay.page_table.numpy(),
+    def ref_attention(self, heads=None):
+        q = self.q if heads is None else self.q[:, heads]
+        return oracle.tq_attention(self.codes_ref, self.radii_ref, q.cpu().numpy(), self.lay.page_table.numpy(),
                                    np.array(self.lens, np.int32), self.w.sm_scale, self.w.page_size)
 

@@ -218,3 +218,26 @@ def test_python_binding_checks_tensors(kvq):
     import torch
     with pytest.raises(ValueError):
         kvq.kvq_rotate_q(torch.zeros(4, 256))    # a CPU tensor is refused: no CPU path exists
+
+
+def test_latent_split_granularity_and_tq_rotation_checks(kvq):
+    """The latent formats split at any multiple of the 32-key tile, the
+    Hadamard-32 formats only at the 512-key chunk; the TQ4 merge rotates
+    back (inverse_rotate = 1); kvq_tq_rotate_q validates its arguments
+    (batch 0 / 0 rows return before any launch)."""
+    P = ctypes.c_void_p
+    q4, f8 = _q4(kvq), _fp8(kvq)
+    tq = _fp8(kvq, format=kvq.FMT_TQ4_LATENT)
+    assert _decode(kvq, q4, split_keys=256, batch=0) == INVALID
+    for d in (f8, tq):
+        assert _decode(kvq, d, n_q_heads=16, split_keys=256, batch=0) == 0
+        assert _decode(kvq, d, n_q_heads=16, split_keys=32, batch=0) == 0
+        assert _decode(kvq, d, n_q_heads=16, split_keys=48, batch=0) == INVALID
+    m = kvq.lib.kvq_merge
+    assert m(ctypes.byref(tq), P(A), P(A), P(A), P(A), 1, 16, 1024, 512, 0, P(A), None, None) == INVALID
+    assert m(ctypes.byref(tq), P(A), P(A), P(A), P(A), 0, 16, 1024, 512, 1, P(A), None, None) == 0
+    r = kvq.lib.kvq_tq_rotate_q
+    assert r(P(A), P(A), -1, None) == INVALID
+    assert r(P(A + 4), P(A), 1, None) == INVALID
+    assert r(P(A), P(A + 8), 1, None) == INVALID
+    assert r(P(A), P(A), 0, None) == 0

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads as wl
-from helpers import TOL, MlaCase, Q4Case, rel_err
+from helpers import TOL, MlaCase, Q4Case, TqCase, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -125,3 +125,23 @@ def test_mla_full_sampled_heads(kvq):
     _say(f"  max_rel_err={err.max():.2e}")
     assert err.max() < TOL
     assert np.max(np.abs(lse.cpu().numpy() - rl)) < 1e-3 * max(1.0, np.abs(rl).max())
+
+
+def test_tq4_full_sampled_heads(kvq):
+    """The latent workload at its full 262144 positions stored with the
+    rotated-int4 + Lloyd-Max codec: codes and radii bit-exact, and the
+    rotate + decode (matrix cores, split 2048) + merge path within tolerance
+    on sampled heads."""
+    w = wl.MLA_TQ4_262K
+    _say(f"full tq4: T={w.seq_len} split={w.split_keys}")
+    case = TqCase(w, [w.seq_len])
+    torch.cuda.synchronize()
+    assert np.array_equal(case.cache.codes.cpu().numpy(), case.codes_ref)
+    assert np.array_equal(case.cache.scales.cpu().numpy().view(np.uint32), case.radii_ref.view(np.uint32))
+    o, lse = case.gpu_attention(w.split_keys)
+    heads = [0, 17, 64, 127]
+    ro, rl = case.ref_attention(heads=heads)
+    err = rel_err(o[:, heads], ro)
+    _say(f"  max_rel_err={err.max():.2e}")
+    assert err.max() < TOL
+    assert np.max(np.abs(lse[:, heads] - rl)) < 1e-3 * max(1.0, np.abs(rl).max())

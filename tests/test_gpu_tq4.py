@@ -54,15 +54,17 @@ def test_tq4_store_bit_exact(kvq, dtype):
 
 
 def test_tq4_decode_matches_oracle(kvq):
-    """Decode + merge over a ragged batch (one position, a tail, an empty
-    sequence, several splits), 16 heads, splits of 512 and 2048 keys; a
-    sequence alone equals the same sequence in the batch, bit for bit."""
+    """Rotate + decode + merge over a ragged batch (one position, a tail, an
+    empty sequence, several splits), 16 heads, splits of 512 and 2048 keys
+    (matrix cores) and 4096 (beyond the matrix-core kernel's split limit: the
+    plain kernel); a sequence alone equals the same sequence in the batch,
+    bit for bit."""
     w = wl.MLA_262K
     lens = [1, 300, 0, 1100]
     case = TqCase(w, lens, n_heads=16)
     assert np.array_equal(case.cache.codes.cpu().numpy(), case.codes_ref)
     ro, rl = case.ref_attention()
-    for split in (512, 2048):
+    for split in (512, 2048, 4096):
         o, lse = case.gpu_attention(split)
         err = rel_err(o, ro)
         _say(f"  split={split} max_rel_err={err.max():.2e}")
@@ -72,7 +74,8 @@ def test_tq4_decode_matches_oracle(kvq):
         assert np.all(o[2] == 0)
     o_b, l_b = case.gpu_attention(512)
     for b in (1, 3):
-        pa, pm, pz = kvq.kvq_decode_attn(case.cache, case.q[b:b + 1].contiguous(), case.page_table[b:b + 1].contiguous(),
+        q1 = kvq.kvq_tq_rotate_q(case.q[b:b + 1].contiguous())
+        pa, pm, pz = kvq.kvq_decode_attn(case.cache, q1, case.page_table[b:b + 1].contiguous(),
                                          case.seq_lens[b:b + 1].contiguous(), case.max_seq_len, w.sm_scale, 512)
         o1, l1 = kvq.kvq_merge(case.cache, pa, pm, pz, case.seq_lens[b:b + 1].contiguous(), case.max_seq_len, 512)
         assert np.array_equal(o1.cpu().numpy()[0], o_b[b]) and np.array_equal(l1.cpu().numpy()[0], l_b[b])
@@ -87,3 +90,26 @@ def test_tq4_decode_all_heads(kvq):
     err = rel_err(o, ro)
     _say(f"  128 heads max_rel_err={err.max():.2e}")
     assert err.max() < TOL
+
+
+def test_tq_rotate_q_bit_exact(kvq):
+    """kvq_tq_rotate_q equals the oracle's fp32 rotation of each part, bit for
+    bit (same butterfly order, same final multiply), also in place."""
+    g = torch.Generator().manual_seed(21)
+    q = torch.randn((3, 5, 576), generator=g)
+    q[0, 0] = 0
+    q[1, 2, 100] = 1e30
+    q[2, 4, 513] = -7.5e-39
+    ref = np.empty((3, 5, 576), np.float32)
+    qn = q.numpy()
+    for b in range(3):
+        for h in range(5):
+            ref[b, h, :512] = oracle.tq_rotate_f32(qn[b, h, :512], 0)
+            ref[b, h, 512:] = oracle.tq_rotate_f32(qn[b, h, 512:], 1)
+    qd = q.cuda()
+    out = kvq.kvq_tq_rotate_q(qd)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    kvq.kvq_tq_rotate_q(qd, out=qd)
+    torch.cuda.synchronize()
+    assert np.array_equal(qd.cpu().numpy().view(np.uint32), ref.view(np.uint32))

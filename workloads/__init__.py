@@ -103,9 +103,11 @@ GQA_32K_Q8 = replace(GQA_32K, name="gqa_q8_32k", bits=8)
 GQA_32K_Q6 = replace(GQA_32K, name="gqa_q6_32k", bits=6)
 
 # The latent workload's rows at 32K positions, stored with the rotated-int4 + Lloyd-Max codec.
-MLA_TQ4_32K = replace(MLA_262K, name="mla_tq4_32k", seq_len=32768, split_keys=512)
+MLA_TQ4_32K = replace(MLA_262K, name="mla_tq4_32k", seq_len=32768, split_keys=256)
+MLA_TQ4_262K = replace(MLA_262K, name="mla_tq4_262k")
 
-WORKLOADS = {w.name: w for w in (TINY, GQA_32K, GQA_262K, RAGGED, MLA_262K, GQA_32K_Q8, GQA_32K_Q6, MLA_TQ4_32K)}
+WORKLOADS = {w.name: w for w in (TINY, GQA_32K, GQA_262K, RAGGED, MLA_262K, GQA_32K_Q8, GQA_32K_Q6, MLA_TQ4_32K,
+                                              MLA_TQ4_262K)}
 
 
 def shrink(w, **kw):
