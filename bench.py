@@ -39,8 +39,8 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); valid only for the kernel sources they were taken on
 # (keyed by the sha256 of the kernel file followed by the device-helper header it includes).
 TRAFFIC = {
-    "8332fe27d603f766366ded67126bb2a66ca21da6a8306e9a3c3833a8b466d6d7": {
-        "fetch_kib": 147702.0, "write_kib": 3264.0, "fetch_scale": 2.0, "write_scale": 1.0,
+    "85e9887c41ca8f886c7139d8a56226a21dca381fd4a7dd2ac924a11ed2c9fb1d": {
+        "fetch_kib": 147697.0, "write_kib": 3264.0, "fetch_scale": 2.0, "write_scale": 1.0,
         "profile": "profiles/decode_q4_mfma_gqa_q4_262k.md"},
 }
 DECODE_SOURCES = (os.path.join("fp8_quantized_kv_amd", "csrc", "decode_q4_mfma.hip"),
@@ -351,6 +351,70 @@ class DsaBench(_Bench):
         return self.batch * self.n_sel * w.n_heads * 2 * (w.head_dim + w.kv_lora)
 
 
+class RowsBench(_Bench):
+    """R drafted rows of the headline sequence over the 4-bit workload's layer
+    caches: row r attends the first T - R + 1 + r positions.  Step per layer:
+    rotate the R query rows, decode them, merge.  shared=True decodes them with
+    kvq_decode_attn_rows (one page-table row, the rows of a split dispatched
+    together on one XCD); shared=False with kvq_decode_attn over a batch of R
+    entries repeating that row (the rows' workgroups far apart in the grid).
+    Both give the same bits."""
+
+    DECODE = 1
+    DECODE_MERGE = (1, 2)
+
+    def __init__(self, q4, n_rows, shared, device="cuda"):
+        import torch
+
+        import workloads as wl
+        w, kvq = q4.w, q4.kvq
+        self.w, self.kvq, self.R, self.shared = w, kvq, n_rows, shared
+        T = q4.T
+        self.lens = [T - n_rows + 1 + r for r in range(n_rows)]
+        self.seq_lens = torch.tensor(self.lens, dtype=torch.int32, device=device)
+        pt_row = q4.page_table[0].contiguous()
+        self.page_table = pt_row if shared else pt_row.expand(n_rows, -1).contiguous()
+        self.q = [wl.q4_query(wl.shrink(w, batch=n_rows), layer, device) for layer in range(w.n_layers)]
+        acc_shape, mz_shape = kvq.partial_shapes(q4.caches[0], n_rows, w.n_q_heads, T, w.split_keys)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.q_rot = torch.empty((n_rows, w.n_q_heads, w.head_dim), **f32)
+        self.pa, self.pm, self.pz = torch.empty(acc_shape, **f32), torch.empty(mz_shape, **f32), torch.empty(mz_shape, **f32)
+        self.out = torch.empty((w.n_layers, n_rows, w.n_q_heads, w.head_dim), **f32)
+        self.lse = torch.empty((w.n_layers, n_rows, w.n_q_heads), **f32)
+        dec = kvq.kvq_decode_attn_rows if shared else kvq.kvq_decode_attn
+        for layer, c in enumerate(q4.caches):  # one checked pass through the binding
+            kvq.kvq_rotate_q(self.q[layer], out=self.q_rot)
+            dec(c, self.q_rot, self.page_table, self.seq_lens, T, w.sm_scale, w.split_keys, self.pa, self.pm, self.pz)
+            kvq.kvq_merge(c, self.pa, self.pm, self.pz, self.seq_lens, T, w.split_keys, out=self.out[layer],
+                          lse=self.lse[layer])
+        torch.cuda.synchronize()
+        P = ctypes.c_void_p
+        stream = P(torch.cuda.current_stream().cuda_stream)
+        n_pages = self.page_table.shape[-1]
+        self.raw = []
+        for layer, c in enumerate(q4.caches):
+            d = ctypes.byref(c.desc)
+            self.raw.append([
+                ("kvq_rotate_q", (P(self.q[layer].data_ptr()), 0, P(self.q_rot.data_ptr()), n_rows * w.n_q_heads,
+                                  w.head_dim, stream)),
+                ("kvq_decode_attn_rows" if shared else "kvq_decode_attn",
+                 (d, P(self.q_rot.data_ptr()), w.n_q_heads, P(self.page_table.data_ptr()), n_pages,
+                  P(self.seq_lens.data_ptr()), n_rows, T, ctypes.c_float(w.sm_scale), w.split_keys,
+                  P(self.pa.data_ptr()), P(self.pm.data_ptr()), P(self.pz.data_ptr()), stream)),
+                ("kvq_merge", (d, P(self.pa.data_ptr()), P(self.pm.data_ptr()), P(self.pz.data_ptr()),
+                               P(self.seq_lens.data_ptr()), n_rows, w.n_q_heads, T, w.split_keys, 1,
+                               P(self.out[layer].data_ptr()), P(self.lse[layer].data_ptr()), stream)),
+            ])
+
+    @property
+    def kv_bytes_per_layer(self):
+        """Cache bytes the rows attend, counted once (the bytes one row reads)."""
+        w = self.w
+        return max(self.lens) * w.n_kv_heads * 2 * w.row_bytes
+
+    flops_per_layer = None
+
+
 class RaggedBench(_Bench):
     """The ragged batch: 16 sequences of seeded lengths over a shuffled paged
     pool (one layer).  Step: the 2048-token prefill chunk of a 17th sequence
@@ -641,6 +705,22 @@ def main():
          f"(then decode + merge alone, the step as a HIP graph, {args.steps} event-bracketed steps)")
     m = measure(b, args.steps, args.warmup)
     kvb = b.kv_bytes_per_layer
+    rows = {}
+    if not args.no_extras:
+        # drafted rows of the same sequence over the same layer caches (shared vs separate reads)
+        for R in (4,):
+            for shared in (True, False):
+                name = f"rows{R}_q4_262k_{'shared' if shared else 'batch'}"
+                _log(f"bench: side measurement {name}")
+                br = RowsBench(b, R, shared)
+                mr = measure(br, args.steps, args.warmup)
+                rows[name] = {"rows": R, "lens": f"{min(br.lens)}..{max(br.lens)}", "split_keys": w.split_keys,
+                              "entry": "kvq_decode_attn_rows" if shared else "kvq_decode_attn (page-table row repeated)",
+                              "us_per_layer": round(mr["us_per_layer"], 3),
+                              "decode_us": round(mr["decode_us"], 3),
+                              "decode_us_per_row": round(mr["decode_us"] / R, 3),
+                              "decode_vs_one_row": round(mr["decode_us"] / m["decode_us"], 3)}
+                del br
     rec = {
         "metric": METRIC, "value": round(m["step_gbs"], 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(m["ms_per_step"], 4), "higher_is_better": True,
@@ -665,6 +745,8 @@ def main():
     ceil = read_ceiling()
     rec["hbm_read_ceiling"] = ceil
     rec["roofline"]["frac_of_read_ceiling"] = round(m["decode_gbs"] / ceil["non_temporal"], 4)
+    if rows:
+        rec["drafted_rows"] = rows
     if not args.no_extras:
         extras = {}
         for name, cls in (("gqa_q4_32k", Q4Bench), ("gqa_q8_32k", Q4Bench), ("gqa_q6_32k", Q4Bench),

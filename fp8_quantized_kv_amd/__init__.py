@@ -38,7 +38,7 @@ DT_F32, DT_BF16, DT_F16 = 0, 1, 2
 _DTYPES = {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float16: DT_F16}
 
 EXPORTED = ("kvq_status_string", "kvq_row_bytes", "kvq_pool_bytes", "kvq_num_splits", "kvq_store",
-            "kvq_rotate_q", "kvq_store_rotate_q", "kvq_decode_attn", "kvq_decode_attn_sel", "kvq_merge",
+            "kvq_rotate_q", "kvq_store_rotate_q", "kvq_decode_attn", "kvq_decode_attn_rows", "kvq_decode_attn_sel", "kvq_merge",
             "kvq_tq_rotate_q", "kvq_stream_read")
 
 
@@ -65,6 +65,7 @@ def _load():
         "kvq_rotate_q": ([P, I32, P, I32, I32, P], I32),
         "kvq_store_rotate_q": ([C, P, P, I32, P, I32, P, I32, P, I32, P], I32),
         "kvq_decode_attn": ([C, P, I32, P, I32, P, I32, I32, F, I32, P, P, P, P], I32),
+        "kvq_decode_attn_rows": ([C, P, I32, P, I32, P, I32, I32, F, I32, P, P, P, P], I32),
         "kvq_merge": ([C, P, P, P, P, I32, I32, I32, I32, I32, P, P, P], I32),
         "kvq_tq_rotate_q": ([P, P, I32, P], I32),
         "kvq_stream_read": ([P, ctypes.c_size_t, I32, P, P], I32),
@@ -295,6 +296,34 @@ def kvq_decode_attn(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split
     _check(lib.kvq_decode_attn(ctypes.byref(cache.desc), qp, Hq, ptp, int(page_table.shape[1]), slp, B,
                                int(max_seq_len), float(sm_scale), int(split_keys), pa, pm, pz, _stream(q)),
            "kvq_decode_attn")
+    return part_acc, part_m, part_z
+
+
+def kvq_decode_attn_rows(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_keys, part_acc=None,
+                         part_m=None, part_z=None):
+    """Split-K decode attention for R query rows of one sequence (drafted rows): row r attends
+    positions [0, seq_lens[r]) of the sequence with page-table row `page_table`; returns the partials
+    (acc, m, z), the same bits kvq_decode_attn gives with that row repeated R times.
+
+    q: f32 [R][H_q][head_dim] rotated with kvq_rotate_q; page_table: int32 [max_pages];
+    seq_lens: int32 [R].  Merge with kvq_merge(cache, ..., seq_lens, ...)."""
+    R, Hq, D = q.shape
+    acc_shape, mz_shape = partial_shapes(cache, R, Hq, max_seq_len, split_keys)
+    if part_acc is None:
+        part_acc = torch.empty(acc_shape, dtype=torch.float32, device=q.device)
+        part_m = torch.empty(mz_shape, dtype=torch.float32, device=q.device)
+        part_z = torch.empty(mz_shape, dtype=torch.float32, device=q.device)
+    qp = _dev(q, "q", dtype=torch.float32, shape=(R, Hq, cache.head_dim))
+    if page_table.dim() != 1:
+        raise ValueError("page_table must be one row [max_pages]")
+    ptp = _dev(page_table, "page_table", dtype=torch.int32)
+    slp = _dev(seq_lens, "seq_lens", dtype=torch.int32, shape=(R,))
+    pa = _dev(part_acc, "part_acc", dtype=torch.float32, shape=acc_shape)
+    pm = _dev(part_m, "part_m", dtype=torch.float32, shape=mz_shape)
+    pz = _dev(part_z, "part_z", dtype=torch.float32, shape=mz_shape)
+    _check(lib.kvq_decode_attn_rows(ctypes.byref(cache.desc), qp, Hq, ptp, int(page_table.shape[0]), slp, R,
+                                    int(max_seq_len), float(sm_scale), int(split_keys), pa, pm, pz, _stream(q)),
+           "kvq_decode_attn_rows")
     return part_acc, part_m, part_z
 
 

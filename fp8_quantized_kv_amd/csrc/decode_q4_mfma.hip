@@ -142,7 +142,8 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
     constexpr bool X16 = BITS != 8;  // 4 and 6 bits: k-slots 2,3,6,7 carry x16 (nibble in bits 4..7)
     __shared__ __attribute__((aligned(16))) uint8_t smem[S::LDS];
 
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    int s, g, b;
+    if (!decode_block(a, H, s, g, b)) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches per wave
     const int n16 = lane & 15, q4 = lane >> 4;  // MFMA column / row-quarter of this lane
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
     // crosses a page, page_size being a multiple of 16) and pages to the
     // pool, so every copy stays in bounds; rows past the sequence's end are
     // masked in the scores.
-    const int32_t* pt = a.page_table + int64_t(b) * a.max_pages;
+    const int32_t* pt = a.page_table + (a.rows ? 0 : int64_t(b) * a.max_pages);
     const int n_runs = kq / 16;
     const int last_pos = a.max_seq_len > 0 ? (a.max_seq_len - 1) & ~15 : 0;
     int64_t roff[2] = {0, 0};
@@ -609,7 +610,7 @@ bool decode_q4_mfma_supported(const Q4Pool& pool, const DecodeArgs& a) {
 // 26 KB per wave.  The choice depends on split_keys and the format alone, never on the
 // batch, so a sequence's partials do not depend on the sequences beside it.
 hipError_t launch_decode_q4_mfma(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s) {
-    const dim3 grid(unsigned(a.n_splits), unsigned(pool.n_kv_heads), unsigned(a.batch));
+    const dim3 grid = decode_grid(a, pool.n_kv_heads);
     const bool eight = a.split_keys <= kEightWaveSplit;
     const bool pack = a.n_q_heads / pool.n_kv_heads <= 8;
 #define KVQ_LAUNCH(D_, W_, P_, B_)                                                                             \

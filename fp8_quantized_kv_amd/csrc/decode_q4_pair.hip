@@ -76,7 +76,8 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
                     int page_size, int num_pages, DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
 
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    int s, g, b;
+    if (!decode_block(a, H, s, g, b)) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pair = wave >> 1, h = wave & 1;  // channel half of this wave
@@ -107,7 +108,7 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
     // single-wave kernel.  A row index fits 32 bits for pools up to 2^32 rows
     // (the launcher checks), so one register holds it; the byte offset is
     // formed in scalar registers when a copy is issued.
-    const int32_t* pt = a.page_table + int64_t(b) * a.max_pages;
+    const int32_t* pt = a.page_table + (a.rows ? 0 : int64_t(b) * a.max_pages);
     const int n_runs = kp / 16;
     const int last_pos = a.max_seq_len > 0 ? (a.max_seq_len - 1) & ~15 : 0;
     uint32_t rrow;
@@ -412,7 +413,7 @@ bool decode_q4_pair_supported(const Q4Pool& pool, const DecodeArgs& a) {
 }
 
 hipError_t launch_decode_q4_pair(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s) {
-    const dim3 grid(unsigned(a.n_splits), unsigned(pool.n_kv_heads), unsigned(a.batch));
+    const dim3 grid = decode_grid(a, pool.n_kv_heads);
     decode_q4_pair<<<grid, dim3(kWaves * 64), 0, s>>>(pool.k, pool.v, pool.n_kv_heads, pool.page_size, pool.num_pages,
                                                       a);
     return hipGetLastError();

@@ -172,7 +172,42 @@ struct DecodeArgs {
     // the list capacity); entries outside the page capacity are absent.
     const int32_t* sel = nullptr;
     int sel_stride = 0;
+    // Drafted rows (4-bit formats, kvq_decode_attn_rows): when rows > 0 the
+    // batch entries are `rows` query rows of one sequence, sharing one
+    // page-table row, and the grid is the row layout of decode_block.
+    int rows = 0;
 };
+
+// Block coordinates (split s, KV head g, batch entry b) of this workgroup.
+// Plain launches: the grid is (splits, KV heads, batch).  Row launches
+// (a.rows > 0): a 1-D grid whose workgroup L runs on XCD L % 8 (the
+// dispatcher's round robin) as that XCD's (L / 8)-th; each run of a.rows
+// consecutive workgroups on an XCD takes the rows of one (split, KV head), so
+// they are dispatched together and the rows after the first find the tiles
+// in that XCD's L2.  Returns false for the padding workgroups of the last
+// round (the whole workgroup then exits before any barrier).
+__device__ __forceinline__ bool decode_block(const DecodeArgs& a, int n_kv_heads, int& s, int& g, int& b) {
+    if (a.rows == 0) {
+        s = blockIdx.x;
+        g = blockIdx.y;
+        b = blockIdx.z;
+        return true;
+    }
+    const unsigned L = blockIdx.x, xcd = L % 8u, k = L / 8u;
+    const unsigned sg = (k / unsigned(a.rows)) * 8u + xcd;
+    b = int(k % unsigned(a.rows));
+    if (sg >= unsigned(a.n_splits) * unsigned(n_kv_heads)) return false;
+    s = int(sg % unsigned(a.n_splits));
+    g = int(sg / unsigned(a.n_splits));
+    return true;
+}
+
+// The launch grid matching decode_block.
+inline dim3 decode_grid(const DecodeArgs& a, int n_kv_heads) {
+    if (a.rows == 0) return dim3(unsigned(a.n_splits), unsigned(n_kv_heads), unsigned(a.batch));
+    const unsigned n_sg = unsigned(a.n_splits) * unsigned(n_kv_heads);
+    return dim3(8u * unsigned(a.rows) * ((n_sg + 7u) / 8u));
+}
 
 // Matrix-core kernel for the 4-bit cache (head_dim 128/256, pages of a
 // multiple of 16 tokens, groups of up to 16 query heads, split_keys <= 8192).

@@ -12,6 +12,7 @@ using kvq::InType;
 constexpr uintptr_t kAlign = 16;
 
 constexpr int64_t kMaxLaunchThreads = 0xFFFFFF00LL;  // grid x block of a 1-D launch
+constexpr int32_t kMaxDraftRows = 64;                 // rows per kvq_decode_attn_rows call
 
 bool aligned(const void* p, uintptr_t a = kAlign) { return p && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -202,6 +203,34 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_h
     }
     if (kvq::decode_fp8_mfma_supported(pool, a)) return launched(kvq::launch_decode_fp8_mfma(pool, a, stream));
     return launched(kvq::launch_decode_fp8_simple(pool, a, stream));
+}
+
+kvq_status kvq_decode_attn_rows(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
+                                int32_t max_pages, const int32_t* seq_lens, int32_t n_rows, int32_t max_seq_len,
+                                float sm_scale, int32_t split_keys, float* part_acc, float* part_m, float* part_z,
+                                hipStream_t stream) {
+    kvq_status st = check_cache(cache);
+    if (st != KVQ_OK) return st;
+    if (!is_h32(cache->format)) return KVQ_ERR_UNSUPPORTED;
+    st = check_seq_args(cache, n_q_heads, seq_lens, n_rows, max_seq_len, split_keys, 512);
+    if (st != KVQ_OK) return st;
+    if (max_pages < 1 || int64_t(max_seq_len) > int64_t(max_pages) * cache->page_size) return KVQ_ERR_INVALID_ARG;
+    if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return KVQ_ERR_INVALID_ARG;
+    if (n_rows > kMaxDraftRows) return KVQ_ERR_UNSUPPORTED;
+    if (n_rows == 0) return KVQ_OK;
+    if (!aligned(q) || !aligned(page_table, 4) || !aligned(part_acc) || !aligned(part_m, 4) || !aligned(part_z, 4))
+        return KVQ_ERR_INVALID_ARG;
+    kvq::DecodeArgs a{q, n_q_heads, page_table, max_pages, seq_lens, n_rows, max_seq_len,
+                      kvq_num_splits(max_seq_len, split_keys), sm_scale, split_keys, part_acc, part_m, part_z};
+    a.rows = n_rows;
+    // the row layout is one 1-D grid of workgroups of at most 512 threads
+    const int64_t n_sg = int64_t(a.n_splits) * cache->num_kv_heads;
+    if (8 * int64_t(n_rows) * ((n_sg + 7) / 8) * 512 > kMaxLaunchThreads) return KVQ_ERR_UNSUPPORTED;
+    // the kernel kvq_decode_attn would choose for the same rows, so the partials are the same bits
+    const kvq::Q4Pool pool = q4_pool(cache);
+    if (pool.bits == 4 && kvq::decode_q4_pair_supported(pool, a)) return launched(kvq::launch_decode_q4_pair(pool, a, stream));
+    if (kvq::decode_q4_mfma_supported(pool, a)) return launched(kvq::launch_decode_q4_mfma(pool, a, stream));
+    return KVQ_ERR_UNSUPPORTED;
 }
 
 kvq_status kvq_decode_attn_sel(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,

@@ -238,6 +238,28 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_h
                            float sm_scale, int32_t split_keys, float* part_acc, float* part_m, float* part_z,
                            hipStream_t stream);
 
+/* Split-K decode attention for several query rows of ONE sequence -- drafted
+ * rows, or a short prompt chunk, attending the cache they were just stored
+ * into (TensorFold "What it is": drafted rows reuse the cache's full chunks and
+ * stay bit-identical to decoding the rows one at a time).  Row r attends
+ * positions [0, seq_lens[r]) of the sequence whose page-table row is
+ * page_table[0 .. max_pages); every other argument, the partials' layout and
+ * the merge (kvq_merge with batch = n_rows and the same seq_lens) are those of
+ * kvq_decode_attn with batch = n_rows and that page-table row repeated, and
+ * the partials are the same bits (the same kernel, the same per-row work).
+ * The difference is the schedule: the workgroups of all rows of one split and
+ * KV head are dispatched together on one XCD, so the rows after the first
+ * read the split's tiles from that XCD's L2 instead of HBM.
+ * Hadamard-32 formats (Q4, Q8, Q6) on the matrix-core kernels: head_dim 256
+ * (Q4 also 128), page_size a multiple of 16, groups of at most 16 query
+ * heads; other shapes or formats give KVQ_ERR_UNSUPPORTED, as does n_rows >
+ * 64.  q: [n_rows][n_q_heads][head_dim] f32, rotated (kvq_rotate_q);
+ * seq_lens: device int32 [n_rows], each in [0, max_seq_len]. */
+kvq_status kvq_decode_attn_rows(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
+                                int32_t max_pages, const int32_t* seq_lens, int32_t n_rows, int32_t max_seq_len,
+                                float sm_scale, int32_t split_keys, float* part_acc, float* part_m, float* part_z,
+                                hipStream_t stream);
+
 /* Split decode attention over SELECTED rows of an FP8 latent cache (colibri
  * split-T commit, DSA gather: attend the selected rows, given as absolute
  * positions; a list of 1024 or more entries is split into partials and

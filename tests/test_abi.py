@@ -241,3 +241,20 @@ def test_latent_split_granularity_and_tq_rotation_checks(kvq):
     assert r(P(A + 4), P(A), 1, None) == INVALID
     assert r(P(A), P(A + 8), 1, None) == INVALID
     assert r(P(A), P(A), 0, None) == 0
+
+
+def test_rows_argument_checks(kvq):
+    """kvq_decode_attn_rows: the Hadamard-32 formats only, the 512-key chunk,
+    at most 64 rows; 0 rows return before any launch."""
+    P = ctypes.c_void_p
+    r = kvq.lib.kvq_decode_attn_rows
+
+    def call(d, n_rows=0, split=512, H=24):
+        return r(ctypes.byref(d), P(A), H, P(A), 64, P(A), n_rows, 1024, 0.0625, split, P(A), P(A), P(A), None)
+
+    assert call(_q4(kvq)) == 0
+    assert call(_q4(kvq), split=256) == INVALID
+    assert call(_q4(kvq), n_rows=65) == UNSUPPORTED
+    assert call(_q4(kvq), n_rows=-1) == INVALID
+    assert call(_fp8(kvq), H=16) == UNSUPPORTED
+    assert call(_fp8(kvq, format=kvq.FMT_TQ4_LATENT), H=16) == UNSUPPORTED
