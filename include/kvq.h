@@ -60,7 +60,7 @@ extern "C" {
 typedef enum {
     KVQ_OK = 0,
     KVQ_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size or pairing */
-    KVQ_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement */
+    KVQ_ERR_UNSUPPORTED = -2,  /* valid request the library does not implement */
     KVQ_ERR_LAUNCH = -3        /* the HIP runtime rejected a launch */
 } kvq_status;
 
@@ -317,7 +317,7 @@ kvq_status kvq_tq_rotate_q(const float* q, float* q_rot, int32_t n_rows, hipStre
 
 /* ---------------------------------------------------------------- measurement */
 
-/* The HBM read ceiling the decode kernels are judged against (not a step of
+/* The HBM read ceiling the decode kernels are measured against (not a step of
  * the method): every 16-byte chunk of src is copied once into LDS with the
  * LDS-DMA load the 4-bit decode kernels use for cache rows, with the
  * non-temporal hint (non_temporal = 1) or the default cache policy (0).  As

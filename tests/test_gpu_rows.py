@@ -51,12 +51,15 @@ def _rows_vs_batch_vs_serial(kvq, case, q, lens, split):
 
 
 @pytest.mark.parametrize("wname,split", [("gqa_q4_32k", 512), ("gqa_q4_32k", 2048), ("gqa_q8_32k", 512),
-                                         ("gqa_q6_32k", 1024)])
+                                         ("gqa_q6_32k", 1024), ("tiny_q4_d128_t1024", 512),
+                                         ("tiny_q4_d128_t1024", 2048)])
 def test_rows_match_oracle_batch_and_serial(kvq, wname, split):
     """Six consecutive drafted rows (lengths T0 .. T0 + 5 over one stored
     sequence), then ragged rows (0, 1, a chunk boundary, a tail): oracle
     parity within tolerance, partials equal to the repeated-row batch bit for
-    bit, merged rows equal to each row decoded alone."""
+    bit, merged rows equal to each row decoded alone.  head_dim 256 (wave-pair
+    kernel at 512-key 4-bit splits, single-wave kernel otherwise) and 128
+    (eight-wave workgroups at 512 keys, four at 2048)."""
     w = wl.WORKLOADS[wname]
     T_full = 3005
     case = Q4Case(w, [T_full])
