@@ -27,8 +27,9 @@
 //    arithmetic and every code is converted to f16 by
 //    v_cvt_scalef32_pk_f16_fp8 (exact: every e4m3 value is an f16), once
 //    per workgroup: the four pairs that use a code read it converted.  Rows
-//    are 1168 bytes apart in LDS (576 f16 + 16), so the 16 rows an operand
-//    read touches at one column start in distinct banks.
+//    are 1168 bytes apart in LDS (576 f16 + 16), with the keys permuted
+//    within each 16-row block (lds_row), so a score read and a context read
+//    each touch every bank once.
 //  * Scores: A = 16 keys x 32 channels (16 bytes of f16 per lane), B = the
 //    query pre-scaled by sm_scale*log2(e), split into f16 hi + lo parts; the
 //    latent and rope parts meet their scales in fp32.  The pair exchanges
@@ -139,6 +140,16 @@ __device__ __forceinline__ void tq_cvt8(uint32_t w, const uint32_t (&lo)[4], con
     d[2] = __builtin_amdgcn_perm(o23, e23, 0x05040100u);  // 4, 5
     d[3] = __builtin_amdgcn_perm(o23, e23, 0x07060302u);  // 6, 7
 }
+
+// LDS row of key k of a tile.  Rows are kPitch = 292 dwords apart, so row r
+// starts at bank 36 r mod 64: the even rows of a 16-row block start at banks
+// 0, 8, ..., 56 and the odd rows at 4, 12, ..., 60 (mod 64), each set tiling
+// the 64 banks with 8-dword spans.  A context read (ds_read_b64_tr_b16, 32
+// lanes per pass) takes 8 keys x 8 bytes; keys 0..7 of a 16-key block sit
+// on the even rows and keys 8..15 on the odd ones, so each pass touches one
+// set and no bank twice.  A score read (16 keys x 16 bytes) still touches
+// 16 distinct rows, all at distinct 4-dword spans.
+__device__ __forceinline__ int lds_row(int k) { return (k & 16) | ((k & 7) << 1) | ((k >> 3) & 1); }
 
 // 2^e for an integer e in [-126, 127], exactly.
 __device__ __forceinline__ float exp2i(int e) { return __uint_as_float(uint32_t(e + 127) << 23); }
@@ -283,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
                 uint32_t d[16];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) tq_cvt8(stg[i][e], tab.lo, tab.hi, d + 4 * e);
-                u32x4* dst = reinterpret_cast<u32x4*>(st + chunk_row(i) * kPitch + 64 * chunk_col(i));
+                u32x4* dst = reinterpret_cast<u32x4*>(st + lds_row(chunk_row(i)) * kPitch + 64 * chunk_col(i));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) dst[e] = u32x4{d[4 * e], d[4 * e + 1], d[4 * e + 2], d[4 * e + 3]};
             } else if (tid + kThreads * i < kChunks) {
@@ -296,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
 #pragma unroll
                     for (int e = 0; e < 4; ++e) w[e] = clear_nan_codes(w[e]);
                 }
-                half8_t* d = reinterpret_cast<half8_t*>(st + chunk_row(i) * kPitch + 32 * chunk_col(i));
+                half8_t* d = reinterpret_cast<half8_t*>(st + lds_row(chunk_row(i)) * kPitch + 32 * chunk_col(i));
                 d[0] = cvt8(w[0], w[1]);
                 d[1] = cvt8(w[2], w[3]);
             } else if (has_scale) {
@@ -346,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
     // tr_b16 source of this lane: key slot n16 >> 2 of its quarter (key
     // 4 q4 + (n16 >> 2), then 16 + the same for slots 4..7) at channels
     // 4 (n16 & 3) .. +3 of the 16-channel block, this wave's latent half.
-    const int tr_off = (4 * q4 + (n16 >> 2)) * kPitch + 2 * (4 * (n16 & 3) + half * (kL / 2));
+    const int tr_off = lds_row(4 * q4 + (n16 >> 2)) * kPitch + 2 * (4 * (n16 & 3) + half * (kL / 2));
     float* xmine = reinterpret_cast<float*>(smem + kXOff) + (wave * 64 + lane) * 8;
     const float* xpart = reinterpret_cast<const float*>(smem + kXOff) + ((wave ^ 1) * 64 + lane) * 8;
 
@@ -360,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
         float part[2][4], scl[2][4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const uint8_t* krow = st + (16 * kb + n16) * kPitch + 2 * (32 * g0 + 8 * q4);
+            const uint8_t* krow = st + lds_row(16 * kb + n16) * kPitch + 2 * (32 * g0 + 8 * q4);
             f32x4 accE = {0.0f, 0.0f, 0.0f, 0.0f}, accO = accE, acc78 = accE;
 #pragma unroll
             for (int gl = 0; gl < kQG; ++gl) {
