@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import workloads as wl
-from helpers import MlaCase, Q4Case
+from helpers import MlaCase, Q4Case, TqCase
 
 pytestmark = pytest.mark.gpu
 
@@ -103,3 +103,49 @@ def test_fp8_step_replays_in_a_graph(kvq):
                         bufs, new_kv=(x_new, None, slots))
 
     _replays_match(step, [bufs["out"], bufs["lse"]])
+
+
+def test_tq4_step_replays_in_a_graph(kvq):
+    """Store + query rotation + decode (matrix cores) + merge and inverse
+    rotation over the TQ4 latent cache, 40 heads, two sequences."""
+    w = wl.shrink(wl.MLA_TQ4_262K, n_layers=1, seq_len=0, n_heads=40)
+    lens = [2500, 900]
+    case = TqCase(w, lens, build_oracle=False)
+    B, H = len(lens), w.n_heads
+    gen = torch.Generator(device="cuda").manual_seed(13)
+    x_new = torch.randn((B, w.head_dim), generator=gen, device="cuda")
+    slots = _last_slots(case)
+    acc_shape, mz_shape = kvq.partial_shapes(case.cache, B, H, case.max_seq_len, 512)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    bufs = {"q_rot": torch.empty((B, H, w.head_dim), **f32), "part_acc": torch.empty(acc_shape, **f32),
+            "part_m": torch.empty(mz_shape, **f32), "part_z": torch.empty(mz_shape, **f32),
+            "out": torch.empty((B, H, w.kv_lora), **f32), "lse": torch.empty((B, H), **f32)}
+
+    def step():
+        kvq.decode_step(case.cache, case.q, case.page_table, case.seq_lens, case.max_seq_len, w.sm_scale, 512,
+                        bufs, new_kv=(x_new, None, slots))
+
+    _replays_match(step, [bufs["out"], bufs["lse"]])
+
+
+def test_drafted_rows_replay_in_a_graph(kvq):
+    """Rotate + kvq_decode_attn_rows + merge for four drafted rows of one
+    sequence (the row layout's 1-D grid) under capture."""
+    w = wl.GQA_32K
+    case = Q4Case(w, [3000], build_oracle=False)
+    R, Hq, D = 4, w.n_q_heads, w.head_dim
+    lens = torch.tensor([2997, 2998, 2999, 3000], dtype=torch.int32, device="cuda")
+    q = wl.q4_query(wl.shrink(w, batch=R), 1, "cuda")
+    row = case.page_table[0].contiguous()
+    acc_shape, mz_shape = kvq.partial_shapes(case.cache, R, Hq, 3000, 2048)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    q_rot = torch.empty((R, Hq, D), **f32)
+    pa, pm, pz = torch.empty(acc_shape, **f32), torch.empty(mz_shape, **f32), torch.empty(mz_shape, **f32)
+    out, lse = torch.empty((R, Hq, D), **f32), torch.empty((R, Hq), **f32)
+
+    def step():
+        kvq.kvq_rotate_q(q, out=q_rot)
+        kvq.kvq_decode_attn_rows(case.cache, q_rot, row, lens, 3000, w.sm_scale, 2048, pa, pm, pz)
+        kvq.kvq_merge(case.cache, pa, pm, pz, lens, 3000, 2048, out=out, lse=lse)
+
+    _replays_match(step, [out, lse])
