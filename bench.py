@@ -231,8 +231,11 @@ class MlaBench(_Bench):
         torch.cuda.synchronize()
         for layer in range(w.n_layers):
             c = self.caches[layer]
-            kvq.kvq_store(c, self.x_new[layer], None, self.slot_new)
-            qd = kvq.kvq_tq_rotate_q(self.q[layer], out=self.q_rot) if self.ROTATED else self.q[layer]
+            if self.ROTATED:
+                qd = kvq.kvq_store_rotate_q(c, self.x_new[layer], None, self.slot_new, self.q[layer], out=self.q_rot)
+            else:
+                kvq.kvq_store(c, self.x_new[layer], None, self.slot_new)
+                qd = self.q[layer]
             kvq.kvq_decode_attn(c, qd, self.page_table, self.seq_lens, T, w.sm_scale, w.split_keys,
                                 self.pa, self.pm, self.pz)
             kvq.kvq_merge(c, self.pa, self.pm, self.pz, self.seq_lens, T, w.split_keys, out=self.out[layer],
@@ -244,11 +247,14 @@ class MlaBench(_Bench):
         for layer, c in enumerate(self.caches):
             d = ctypes.byref(c.desc)
             qd = self.q_rot if self.ROTATED else self.q[layer]
-            rot = [("kvq_tq_rotate_q", (P(self.q[layer].data_ptr()), P(self.q_rot.data_ptr()), w.n_heads, stream))]
-            self.raw.append([
-                ("kvq_store", (d, P(self.x_new[layer].data_ptr()), None, kvq._DTYPES[self.x_new[layer].dtype],
-                               P(self.slot_new.data_ptr()), 1, stream)),
-            ] + (rot if self.ROTATED else []) + [
+            xdt = kvq._DTYPES[self.x_new[layer].dtype]
+            first = (("kvq_store_rotate_q", (d, P(self.x_new[layer].data_ptr()), None, xdt, P(self.slot_new.data_ptr()),
+                                             1, P(self.q[layer].data_ptr()), kvq.DT_F32, P(self.q_rot.data_ptr()),
+                                             w.n_heads, stream))
+                     if self.ROTATED else
+                     ("kvq_store", (d, P(self.x_new[layer].data_ptr()), None, xdt, P(self.slot_new.data_ptr()), 1,
+                                    stream)))
+            self.raw.append([first,
                 ("kvq_decode_attn", (d, P(qd.data_ptr()), w.n_heads, P(self.page_table.data_ptr()),
                                      self.page_table.shape[1], P(self.seq_lens.data_ptr()), 1, T,
                                      ctypes.c_float(w.sm_scale), w.split_keys, P(self.pa.data_ptr()),
@@ -277,13 +283,12 @@ class MlaBench(_Bench):
 
 class TqBench(MlaBench):
     """The same latent workload stored with the rotated-int4 + Lloyd-Max codec
-    (288 code bytes + two f32 radii per position); step per layer: store,
-    rotate the query, decode on matrix cores, merge + inverse rotation."""
+    (288 code bytes + two f32 radii per position); step per layer: store and
+    rotate the query (one launch), decode on matrix cores, merge + inverse
+    rotation."""
 
     ROW_BYTES = 288 + 8
     ROTATED = True
-    DECODE = 2
-    DECODE_MERGE = (2, 3)
 
     @staticmethod
     def _new_cache(kvq, lay, w, device):

@@ -244,10 +244,30 @@ def kvq_tq_rotate_q(q, out=None):
 
 
 def kvq_store_rotate_q(cache, k, v, slot_mapping, q, out=None):
-    """kvq_store(cache, k, v, slot_mapping) and kvq_rotate_q(q) in one launch (4-bit cache only);
-    returns the rotated query (f32, q's shape)."""
+    """kvq_store(cache, k, v, slot_mapping) and the query rotation in one launch; returns the rotated
+    query (f32, q's shape).  Hadamard-32 caches: kvq_rotate_q(q).  TQ4 cache: v is None, q is f32
+    [..., 576] and the rotation is kvq_tq_rotate_q(q)."""
+    if cache.fmt == FMT_TQ4_LATENT:
+        if v is not None:
+            raise ValueError("the latent caches take no v")
+        if q.dtype != torch.float32 or int(q.shape[-1]) != 576:
+            raise ValueError("the TQ4 query rotation takes f32 rows of 576")
+        n = int(slot_mapping.shape[0])
+        kdt = _DTYPES.get(k.dtype)
+        if kdt is None:
+            raise ValueError(f"unsupported dtype {k.dtype}")
+        kp = _dev(k, "k", shape=(n, cache.head_dim))
+        sp = _dev(slot_mapping, "slot_mapping", dtype=torch.int64)
+        rows = q.numel() // 576
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        qp = _dev(q, "q")
+        op = _dev(out, "out", dtype=torch.float32, shape=q.shape)
+        _check(lib.kvq_store_rotate_q(ctypes.byref(cache.desc), kp, None, kdt, sp, n, qp, DT_F32, op, rows,
+                                      _stream(q)), "kvq_store_rotate_q")
+        return out
     if cache.fmt not in H32_FORMATS:
-        raise ValueError("kvq_store_rotate_q takes a Hadamard-32 cache")
+        raise ValueError("kvq_store_rotate_q takes a Hadamard-32 or TQ4 cache")
     n = int(slot_mapping.shape[0])
     kdt, qdt = _DTYPES.get(k.dtype), _DTYPES.get(q.dtype)
     if kdt is None or qdt is None:
@@ -399,11 +419,13 @@ def decode_step(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_key
             q = kvq_store_rotate_q(cache, *new_kv, q, out=q_rot)
         else:
             q = kvq_rotate_q(q, out=q_rot)
-    else:
+    elif cache.fmt == FMT_TQ4_LATENT:
         if new_kv is not None:
-            kvq_store(cache, *new_kv)
-        if cache.fmt == FMT_TQ4_LATENT:
+            q = kvq_store_rotate_q(cache, *new_kv, q, out=q_rot)
+        else:
             q = kvq_tq_rotate_q(q, out=q_rot)
+    elif new_kv is not None:
+        kvq_store(cache, *new_kv)
     pa, pm, pz = kvq_decode_attn(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_keys,
                                  *(() if bufs is None else (bufs["part_acc"], bufs["part_m"], bufs["part_z"])))
     return kvq_merge(cache, pa, pm, pz, seq_lens, max_seq_len, split_keys,

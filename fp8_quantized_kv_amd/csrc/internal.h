@@ -256,6 +256,8 @@ struct TqMfmaTable {
 const TqMfmaTable& tq_mfma_table();
 hipError_t launch_decode_tq4_mfma(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_tq_rotate(const float* x, float* y, int64_t n_rows, int row_len, bool inverse, hipStream_t s);
+hipError_t launch_store_rotate_tq4(const Fp8Pool& pool, const void* x, InType dt, const int64_t* slots, int n_tokens,
+                                   const float* q, float* q_rot, int n_rows, hipStream_t s);
 
 struct MergeArgs {
     const float* part_acc;

@@ -156,6 +156,15 @@ kvq_status kvq_store_rotate_q(const kvq_cache* cache, const void* k, const void*
                               float* q_rot, int32_t n_rows, hipStream_t stream) {
     kvq_status st = check_cache(cache);
     if (st != KVQ_OK) return st;
+    if (cache->format == KVQ_FMT_TQ4_LATENT) {  // latent rows + f32 query rows of 576
+        if (!dtype_ok(kv_dtype) || q_dtype != KVQ_DT_F32 || n_tokens < 0 || n_rows < 0 || v) return KVQ_ERR_INVALID_ARG;
+        if (n_tokens > 0 && (!aligned(slot_mapping, 8) || !aligned(k))) return KVQ_ERR_INVALID_ARG;
+        if (n_rows > 0 && (!aligned(q) || !aligned(q_rot))) return KVQ_ERR_INVALID_ARG;
+        if (n_tokens == 0 && n_rows == 0) return KVQ_OK;
+        if (int64_t(n_tokens) + n_rows > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
+        return launched(kvq::launch_store_rotate_tq4(fp8_pool(cache), k, static_cast<InType>(kv_dtype), slot_mapping,
+                                                     n_tokens, static_cast<const float*>(q), q_rot, n_rows, stream));
+    }
     if (!is_h32(cache->format)) return KVQ_ERR_INVALID_ARG;
     if (!dtype_ok(kv_dtype) || !dtype_ok(q_dtype) || n_tokens < 0 || n_rows < 0) return KVQ_ERR_INVALID_ARG;
     if (n_tokens > 0 && (!aligned(slot_mapping, 8) || !aligned(k) || !aligned(v))) return KVQ_ERR_INVALID_ARG;

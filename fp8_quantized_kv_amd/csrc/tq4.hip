@@ -152,14 +152,13 @@ __device__ __forceinline__ void encode_part(float (&v)[8], int lane, uint64_t se
     if (lane == 0) *radius = inert ? 0.0f : r;
 }
 
+// Token t of x into its slot (one wave; a skipped slot is uniform over it).
 template <InType DT>
-__global__ __launch_bounds__(64) void store_tq4_kernel(const void* __restrict__ x, const int64_t* __restrict__ slots,
-                                                       int n_tokens, uint8_t* __restrict__ codes,
-                                                       float* __restrict__ radii, int64_t n_slots, TqTables tb) {
-    __shared__ double red[64];
-    const int t = blockIdx.x, lane = threadIdx.x;
+__device__ __forceinline__ void store_token(const void* __restrict__ x, const int64_t* __restrict__ slots, int t,
+                                            int lane, uint8_t* __restrict__ codes, float* __restrict__ radii,
+                                            int64_t n_slots, const TqTables& tb, double* red) {
     const int64_t slot = slots[t];
-    if (slot < 0 || slot >= n_slots) return;  // uniform over the workgroup
+    if (slot < 0 || slot >= n_slots) return;
     const int64_t base = int64_t(t) * 576;
     float v[8];
 #pragma unroll
@@ -168,6 +167,14 @@ __global__ __launch_bounds__(64) void store_tq4_kernel(const void* __restrict__ 
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = lane < 8 ? load_x<DT>(x, base + 512 + 8 * lane + e) : 0.0f;
     encode_part<64>(v, lane, kSeedRope, tb, red, codes + slot * 288 + 256, radii + slot * 2 + 1);
+}
+
+template <InType DT>
+__global__ __launch_bounds__(64) void store_tq4_kernel(const void* __restrict__ x, const int64_t* __restrict__ slots,
+                                                       int n_tokens, uint8_t* __restrict__ codes,
+                                                       float* __restrict__ radii, int64_t n_slots, TqTables tb) {
+    __shared__ double red[64];
+    store_token<DT>(x, slots, blockIdx.x, threadIdx.x, codes, radii, n_slots, tb, red);
 }
 
 // ---- decode: plain fp32, split-T --------------------------------------------
@@ -211,28 +218,49 @@ __device__ __forceinline__ void rotate_part(float (&v)[8], int lane, uint64_t se
     for (int e = 0; e < 8; ++e) v[e] = inverse ? (v[e] * c) * tq_sign(seed, 8 * lane + e) : v[e] * c;
 }
 
-__global__ __launch_bounds__(64) void tq_rotate_rows(const float* __restrict__ x, float* __restrict__ y, int64_t n_rows,
-                                                     int row_len, int inverse) {
-    const int64_t r = blockIdx.x;
-    const int lane = threadIdx.x;
-    if (r >= n_rows) return;
+// Row r of x (row_len 576: both parts; 512: the latent part) into y.
+__device__ __forceinline__ void rotate_row(const float* __restrict__ x, float* __restrict__ y, int64_t r, int row_len,
+                                           bool inverse, int lane) {
     const float* xr = x + r * row_len;
     float* yr = y + r * row_len;
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = xr[8 * lane + e];
-    rotate_part<kTL>(v, lane, kSeedLatent, inverse != 0);
+    rotate_part<kTL>(v, lane, kSeedLatent, inverse);
 #pragma unroll
     for (int e = 0; e < 8; ++e) yr[8 * lane + e] = v[e];
     if (row_len == kTD) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = lane < 8 ? xr[kTL + 8 * lane + e] : 0.0f;
-        rotate_part<kTR>(v, lane, kSeedRope, inverse != 0);
+        rotate_part<kTR>(v, lane, kSeedRope, inverse);
         if (lane < 8) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) yr[kTL + 8 * lane + e] = v[e];
         }
     }
+}
+
+__global__ __launch_bounds__(64) void tq_rotate_rows(const float* __restrict__ x, float* __restrict__ y, int64_t n_rows,
+                                                     int row_len, int inverse) {
+    if (int64_t(blockIdx.x) >= n_rows) return;
+    rotate_row(x, y, blockIdx.x, row_len, inverse != 0, threadIdx.x);
+}
+
+// The step's store and the query rotation in one launch (kvq_store_rotate_q
+// on a TQ4 cache): workgroups 0 .. n_tokens - 1 store a token each, the rest
+// rotate a query row each; the two sets touch disjoint memory.
+template <InType DT>
+__global__ __launch_bounds__(64) void store_rotate_tq4_kernel(const void* __restrict__ x,
+                                                              const int64_t* __restrict__ slots, int n_tokens,
+                                                              uint8_t* __restrict__ codes, float* __restrict__ radii,
+                                                              int64_t n_slots, TqTables tb, const float* __restrict__ q,
+                                                              float* __restrict__ q_rot, int n_rows) {
+    __shared__ double red[64];
+    const int b = blockIdx.x;
+    if (b < n_tokens)
+        store_token<DT>(x, slots, b, threadIdx.x, codes, radii, n_slots, tb, red);
+    else if (b - n_tokens < n_rows)
+        rotate_row(q, q_rot, b - n_tokens, kTD, false, threadIdx.x);
 }
 
 __global__ __launch_bounds__(kTT) void decode_tq4_simple(const uint8_t* __restrict__ codes,
@@ -460,6 +488,28 @@ hipError_t launch_store_tq4(const Fp8Pool& pool, const void* x, InType dt, const
             break;
         case InType::F16:
             store_tq4_kernel<InType::F16><<<grid, block, 0, s>>>(x, slots, n_tokens, pool.codes, pool.scales, n_slots, tb);
+            break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_store_rotate_tq4(const Fp8Pool& pool, const void* x, InType dt, const int64_t* slots, int n_tokens,
+                                   const float* q, float* q_rot, int n_rows, hipStream_t s) {
+    const int64_t n_slots = int64_t(pool.num_pages) * pool.page_size;
+    const dim3 grid(static_cast<unsigned>(n_tokens + n_rows)), block(64);
+    const TqTables& tb = tq_tables();
+    switch (dt) {
+        case InType::F32:
+            store_rotate_tq4_kernel<InType::F32><<<grid, block, 0, s>>>(x, slots, n_tokens, pool.codes, pool.scales,
+                                                                        n_slots, tb, q, q_rot, n_rows);
+            break;
+        case InType::BF16:
+            store_rotate_tq4_kernel<InType::BF16><<<grid, block, 0, s>>>(x, slots, n_tokens, pool.codes, pool.scales,
+                                                                         n_slots, tb, q, q_rot, n_rows);
+            break;
+        case InType::F16:
+            store_rotate_tq4_kernel<InType::F16><<<grid, block, 0, s>>>(x, slots, n_tokens, pool.codes, pool.scales,
+                                                                        n_slots, tb, q, q_rot, n_rows);
             break;
     }
     return hipGetLastError();

@@ -194,7 +194,10 @@ kvq_status kvq_rotate_q(const void* q, int32_t dtype, float* q_rot, int32_t n_ro
  * stored bytes and q_rot are bit-identical to those two calls.  Either count
  * may be 0 (that part is skipped and its pointers are not read).  q_rot must
  * not overlap k, v or the pools; q == q_rot is allowed for f32.
- * Hadamard-32 formats (Q4, Q8, Q6) only (KVQ_ERR_INVALID_ARG for an FP8 cache). */
+ * Hadamard-32 formats (Q4, Q8, Q6), and TQ4: there k is the latent rows
+ * [n_tokens][576] (v = NULL), q f32 [n_rows][576] (q_dtype KVQ_DT_F32) and
+ * q_rot kvq_tq_rotate_q's result, bit for bit.  KVQ_ERR_INVALID_ARG for an FP8
+ * cache. */
 kvq_status kvq_store_rotate_q(const kvq_cache* cache, const void* k, const void* v, int32_t kv_dtype,
                               const int64_t* slot_mapping, int32_t n_tokens, const void* q, int32_t q_dtype,
                               float* q_rot, int32_t n_rows, hipStream_t stream);

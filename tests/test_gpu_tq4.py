@@ -113,3 +113,28 @@ def test_tq_rotate_q_bit_exact(kvq):
     kvq.kvq_tq_rotate_q(qd, out=qd)
     torch.cuda.synchronize()
     assert np.array_equal(qd.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_tq4_store_rotate_one_launch(kvq):
+    """kvq_store_rotate_q on a TQ4 cache equals kvq_store + kvq_tq_rotate_q,
+    bit for bit (codes, radii, rotated query), with rows only, tokens only,
+    and both."""
+    w = wl.MLA_262K
+    n = 40
+    x = wl.mla_rows(w, 0, 0, n, "cuda").to(torch.bfloat16)
+    q = wl.mla_query(wl.shrink(w, batch=2), 0, "cuda")[:, :24].contiguous()
+    slots = torch.randperm(n * 2, generator=torch.Generator().manual_seed(3))[:n].to(torch.int64).cuda()
+    slots[5] = -1
+    a, b = kvq.TqCache(5, 16, "cuda"), kvq.TqCache(5, 16, "cuda")
+    kvq.kvq_store(a, x, None, slots)
+    qa = kvq.kvq_tq_rotate_q(q)
+    qb = kvq.kvq_store_rotate_q(b, x, None, slots, q)
+    torch.cuda.synchronize()
+    assert torch.equal(a.codes, b.codes) and torch.equal(a.scales.view(torch.int32), b.scales.view(torch.int32))
+    assert torch.equal(qa.view(torch.int32), qb.view(torch.int32))
+    c = kvq.TqCache(5, 16, "cuda")
+    qc = kvq.kvq_store_rotate_q(c, x[:0], None, slots[:0], q)      # rows only
+    kvq.kvq_store_rotate_q(c, x, None, slots, q[:0])               # tokens only
+    torch.cuda.synchronize()
+    assert torch.equal(qc.view(torch.int32), qa.view(torch.int32))
+    assert torch.equal(c.codes, a.codes) and torch.equal(c.scales.view(torch.int32), a.scales.view(torch.int32))
