@@ -24,7 +24,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# KVQ_ORACLE_LIB names another build of the same source (the sanitizer test
+# runs the pins against an -fsanitize=address,undefined build this way).
+_LIB_PATH = os.environ.get("KVQ_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _P = ctypes.c_void_p

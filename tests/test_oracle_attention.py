@@ -32,7 +32,20 @@ def _rot(x):
     return (x.reshape(-1, 32) @ H.T).reshape(s)
 
 
-def _build_q4(w, lens, seed=0):
+def _np_decode_q4(rows, D):
+    """Dequantized rotated values of 4-bit rows, decoded with numpy alone:
+    code bytes (element 2k low nibble, 2k+1 high, two's complement), then the
+    D/32 fp16 scales widened by numpy; value = code * scale of its group."""
+    rows = np.ascontiguousarray(rows, np.uint8)
+    c = rows[..., :D // 2].astype(np.int16)
+    codes = np.empty(rows.shape[:-1] + (D,), np.float64)
+    codes[..., 0::2] = ((c & 0xF) ^ 8) - 8
+    codes[..., 1::2] = ((c >> 4) ^ 8) - 8
+    scales = rows[..., D // 2:].copy().view(np.float16).astype(np.float64)
+    return codes * np.repeat(scales, 32, axis=-1)
+
+
+def _build_q4(w, lens, seed=0, scale=None):
     """Oracle-built paged caches for a small workload (inputs from workloads)."""
     lay = wl.page_layout(w, lens)
     num_pages = lay.num_pages
@@ -45,8 +58,11 @@ def _build_q4(w, lens, seed=0):
             continue
         k, v = wl.q4_kv_tokens(w, 0, off, T)
         off += T
+        k, v = k.float().numpy(), v.float().numpy()
+        if scale is not None:  # tiny rows: every group's scale a binary16 subnormal
+            k, v = k * np.float32(scale), v * np.float32(scale)
         slots = wl.slots_for(lay.page_table[b], np.arange(T), w.page_size).numpy()
-        oracle.q4_store(kp, vp, k.float().numpy(), v.float().numpy(), slots, w.page_size)
+        oracle.q4_store(kp, vp, k, v, slots, w.page_size)
     q = wl.q4_query(w, 0).numpy()
     return kp, vp, q, lay.page_table.numpy(), np.array(lens, np.int32)
 
@@ -66,8 +82,8 @@ def _brute_q4(kp, vp, q, pt, lens, w):
         pages, offs = slots // w.page_size, slots % w.page_size
         for h in range(Hq):
             g = h // G
-            K = oracle.q4_decode_rows(kp[pages, g, offs], D)
-            V = oracle.q4_decode_rows(vp[pages, g, offs], D)
+            K = _np_decode_q4(kp[pages, g, offs], D)
+            V = _np_decode_q4(vp[pages, g, offs], D)
             s = w.sm_scale * (K @ _rot(q[b, h].astype(np.float64)))
             p = scipy.special.softmax(s)
             o[b, h] = _rot(p @ V)
@@ -92,6 +108,25 @@ def test_q4_attention_matches_brute_force(lens):
     for b, T in enumerate(lens):
         if T == 0:
             assert np.all(o[b] == 0)
+
+
+def test_q4_attention_subnormal_scales_matches_brute_force():
+    """Rows scaled by 2^-17 put every group's fp16 scale among the binary16
+    subnormals (amax/8 < 2^-14); the oracle's attention over them equals the
+    numpy brute force (whose scales come from numpy's float16 widening).
+    The query is scaled up by 2^17 so the scores keep their spread."""
+    lens = [300, 77]
+    w = wl.shrink(SMALL, batch=len(lens))
+    kp, vp, q, pt, sl = _build_q4(w, lens, scale=2.0 ** -17)
+    scales = kp[..., w.head_dim // 2:].copy().view(np.float16)
+    used = scales[scales != 0]
+    assert used.size > 1000 and np.all(np.abs(used.astype(np.float32)) < 2.0 ** -14)
+    q = (q * np.float32(2.0 ** 17)).astype(np.float32)
+    o, lse = oracle.q4_attention(kp, vp, q, pt, sl, w.sm_scale)
+    ob, lb = _brute_q4(kp, vp, q, pt, sl, w)
+    den = np.abs(ob).max(axis=-1, keepdims=True)
+    assert np.max(np.abs(o - ob) / den) < 1e-12
+    assert np.max(np.abs(lse - lb)) < 1e-9
 
 
 def test_rotated_space_equals_original_space():
@@ -317,6 +352,26 @@ def test_mla_sel_matches_brute_force():
     fin = np.isfinite(rl)
     assert np.array_equal(fin, np.isfinite(lse)) and np.max(np.abs(lse[fin] - rl[fin])) < 1e-12
     assert np.all(o[2] == 0) and np.all(np.isneginf(lse[2]))
+
+
+def test_mla_sel_absent_throughout_is_empty():
+    """A fixed-size list counted in full (n_sel = max_sel) whose entries are
+    all absent attends no key: out = 0 and lse = -inf, as the brute force
+    (which drops absent entries) gives; a list whose leading 64 entries are
+    absent equals the list without them."""
+    w = MLA_SMALL
+    codes, scales, q, pt, sl = _build_mla(w, [500, 500])
+    sel = np.full((2, 256), -1, np.int32)
+    sel[1, 64:] = np.random.default_rng(9).permutation(500)[:192]
+    n_sel = np.array([256, 256], np.int32)
+    o, lse = oracle.mla_attention_sel(codes, scales, q, pt, sel, n_sel, w.sm_scale, w.rope_dim, w.page_size)
+    ro, rl = _brute_mla_sel(codes, scales, q, pt, sel, n_sel, w)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0])) and np.all(np.isneginf(rl[0]))
+    assert np.max(np.abs(o[1] - ro[1])) < 1e-12 * max(1.0, np.abs(ro[1]).max())
+    tail = np.ascontiguousarray(sel[1:, 64:])
+    o2, l2 = oracle.mla_attention_sel(codes, scales, q[1:].copy(), pt[1:].copy(), tail, np.array([192], np.int32),
+                                      w.sm_scale, w.rope_dim, w.page_size)
+    assert np.array_equal(o2[0], o[1]) and np.array_equal(l2[0], lse[1])
 
 
 def test_mla_sel_order_and_duplicates():

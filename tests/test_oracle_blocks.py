@@ -138,7 +138,7 @@ def test_codes_are_nearest_in_range(bits):
     x[1::11, 5] *= 40
     rows = oracle.q4_encode_rows(x, bits)
     y = oracle.hadamard32_f32(x).reshape(-1, 2, 32)
-    s = oracle.f16_bits_to_f32(_scales(rows, 64, bits))
+    s = _scales(rows, 64, bits).view(np.float16).astype(np.float32)
     codes = _unpack(rows, 64, bits).reshape(-1, 2, 32).astype(np.float64)
     r = (y / s[..., None].astype(np.float32)).astype(np.float64)        # the fp32 quotient
     cand = np.arange(-(1 << (bits - 1)), 1 << (bits - 1), dtype=np.float64)
@@ -195,7 +195,7 @@ def test_attention_matches_brute_force(bits):
             g = h // G
             def deq(pool):
                 rows = pool[pg, g, off]
-                s = oracle.f16_bits_to_f32(_scales(rows, D, bits)).astype(np.float64)
+                s = _scales(rows, D, bits).view(np.float16).astype(np.float64)
                 return _unpack(rows, D, bits) * np.repeat(s, 32, axis=-1)
             K, V = deq(kp), deq(vp)
             sc = 0.125 * (K @ rot(q[b, h].astype(np.float64)))

@@ -76,6 +76,24 @@ def test_f16_exhaustive_against_library():
     assert n == (hi - lo) // 32
 
 
+def test_f16_decode_every_pattern_against_library():
+    """binary16 -> float32 widening of all 65536 bit patterns (zeros, the
+    1023 subnormals per sign, normals, infinities, NaNs) against numpy's
+    float16 -> float32 conversion: identical bits, NaN for NaN."""
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.f16_bits_to_f32(h)
+    ref = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert nan.sum() == 2 * 1023
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    # subnormals are m * 2^-24 exactly, by a closed form too
+    m = np.arange(1, 1024)
+    assert np.array_equal(oracle.f16_bits_to_f32(m.astype(np.uint16)).astype(np.float64), np.ldexp(m, -24))
+    assert np.array_equal(oracle.f16_bits_to_f32((m | 0x8000).astype(np.uint16)).astype(np.float64),
+                          -np.ldexp(m, -24))
+
+
 def test_f16_sign_and_specials():
     rng = np.random.default_rng(5)
     bits = rng.integers(0, 2 ** 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
@@ -128,11 +146,19 @@ def _scales(rows, D):
 
 
 def _codes(rows, D):
-    """Signed codes from the oracle's decoder at scale 1 (tests only)."""
-    r = rows.copy()
-    s = r[..., D // 2:].view(np.uint16)
-    s[...] = 0x3C00
-    return oracle.q4_decode_rows(r, D)
+    """Signed codes unpacked with numpy, independently of the oracle: byte k of
+    the code bytes holds element 2k in its low nibble and 2k+1 in its high
+    nibble, two's complement (FreeToken test-fix commit: int32 sign extension)."""
+    c = rows[..., :D // 2].astype(np.int16)
+    out = np.empty(rows.shape[:-1] + (D,), np.float64)
+    out[..., 0::2] = ((c & 0xF) ^ 8) - 8
+    out[..., 1::2] = ((c >> 4) ^ 8) - 8
+    return out
+
+
+def _np_scales(rows, D):
+    """The fp16 scales widened by numpy (the library's binary16 decoding)."""
+    return _scales(rows, D).view(np.float16).astype(np.float64)
 
 
 def test_row_sizes():
@@ -173,6 +199,57 @@ def test_exact_scale_example(trial_seed):
     assert np.array_equal(_codes(rows, 32), c.astype(np.float64))
 
 
+@pytest.mark.parametrize("trial_seed", range(3))
+def test_exact_scale_example_subnormal_scales(trial_seed):
+    """The exact-scale example at binary16 subnormal scales: rotated-domain
+    rows y = c * s with c in [-8, 7]^32 (-8 present) and s = m * 2^-24 a
+    subnormal (m < 1024), so amax/8 = s exactly; the stored scale must be the
+    subnormal bit pattern m, the codes c, and the dequantized values c * s
+    (numpy's float16 widening of the stored bits)."""
+    rng = np.random.default_rng(300 + trial_seed)
+    H = _h32()
+    n = 600
+    m = rng.integers(1, 1024, size=n)
+    m[:4] = [1, 2, 1023, 512]
+    c = rng.integers(-8, 8, size=(n, 32))
+    c[np.arange(n), rng.integers(0, 32, n)] = -8
+    y = c.astype(np.float64) * np.ldexp(m, -24)[:, None]
+    x = (y @ H.T).astype(np.float32)
+    rows = oracle.q4_encode_rows(x)
+    assert np.array_equal(_scales(rows, 32)[:, 0], m.astype(np.uint16))
+    assert np.array_equal(_codes(rows, 32), c.astype(np.float64))
+    deq = oracle.q4_decode_rows(rows, 32)
+    assert np.array_equal(deq, c * _np_scales(rows, 32))
+    assert np.array_equal(deq, y)
+
+
+def test_tiny_groups_round_to_subnormal_or_zero_scale():
+    """Groups whose amax/8 falls below 2^-14 get the nearest subnormal scale
+    (numpy's binary16 rounding of amax/8), codes nearest in [-8, 7]; below
+    2^-25 the scale rounds to 0 and the group is inert."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((800, 64)).astype(np.float32)
+    mag = np.ldexp(1.0, -rng.integers(12, 30, size=(800, 1))).astype(np.float32)
+    x = x * mag
+    rows = oracle.q4_encode_rows(x)
+    y = oracle.hadamard32_f32(x).reshape(800, 2, 32)
+    amax = np.abs(y).max(axis=2).astype(np.float32)
+    ref = (amax / np.float32(8)).astype(np.float16)
+    assert np.array_equal(_scales(rows, 64), ref.view(np.uint16))
+    sub = (ref > 0) & (ref < np.float16(2.0 ** -14))
+    assert sub.sum() > 200 and (ref == 0).sum() > 50  # both regimes are exercised
+    s = _np_scales(rows, 64)
+    codes = _codes(rows, 64).reshape(800, 2, 32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = (y / s[..., None].astype(np.float32)).astype(np.float64)
+    expect = np.clip(np.round(r), -8, 7)  # numpy rounds half to even
+    live = s > 0
+    assert np.array_equal(codes[live], expect[live])
+    assert np.all(codes[~live] == 0)
+    deq = oracle.q4_decode_rows(rows, 64).reshape(800, 2, 32)
+    assert np.array_equal(deq, codes * s[..., None])
+
+
 def test_plus_eight_clamps_to_seven():
     """+amax maps to +8, which the [-8, 7] code range clamps to 7."""
     H = _h32()
@@ -206,7 +283,7 @@ def test_codes_are_nearest_in_range():
     x[1::11, 5] *= 40
     rows = oracle.q4_encode_rows(x)
     y = oracle.hadamard32_f32(x).reshape(-1, 2, 32).astype(np.float64)
-    s = oracle.f16_bits_to_f32(_scales(rows, 64)).astype(np.float64)
+    s = _np_scales(rows, 64)
     codes = _codes(rows, 64).reshape(-1, 2, 32)
     r = (y.astype(np.float32) / s[..., None].astype(np.float32)).astype(np.float64)  # fp32 quotient
     cand = np.arange(-8, 8, dtype=np.float64)
