@@ -444,10 +444,14 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
         const int e_tile = smax > 0.0f ? int((__float_as_uint(smax) >> 23) & 0xFF) - 127 : -1000;
         const int e_new = __builtin_amdgcn_readfirstlane(
             e_run == -1000 ? max(e_tile, -100) : (e_tile > e_run + 4 ? e_tile : e_run));
-        const bool move = tmax > m_run + kRescale || m_run == -INFINITY;
+        // The maximum moves to the first finite tile maximum (-inf + 6 = -inf), then
+        // by more than 2^6.  A tile whose keys are all masked (absent entries of a
+        // selection) while the maximum is still -inf does not move it, and its p
+        // are 0 below, so no -inf - -inf = NaN reaches z or the accumulators.
+        const bool move = tmax > m_run + kRescale;
         if (__builtin_amdgcn_ballot_w64(move) != 0ull || e_new != e_run) {
             const float m_new = move ? fmaxf(m_run, tmax) : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+            const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // 0 when m_run = -inf
             z_run *= alpha;
             m_run = m_new;
             const float f = e_run == -1000 ? 1.0f : exp2i(max(e_run - e_new, -126));
@@ -461,6 +465,8 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
                 for (int i = 0; i < 4; ++i) o[blk][i] *= al[i];
         }
         const float sfac = exp2i(-e_run);
+        // while the maximum is -inf every score of the tile is -inf: p = 2^-inf = 0
+        const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
 
         // ---- weights: p for z, p * scL * 2^-E (f16) for the context
         half8_t av;
@@ -468,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = __builtin_amdgcn_exp2f(sc[kb][i] - m_run);
+                const float p = __builtin_amdgcn_exp2f(sc[kb][i] - m_ref);
                 z_run += p;
                 av[4 * kb + i] = _Float16(p * (scl[kb][i] * sfac));
             }

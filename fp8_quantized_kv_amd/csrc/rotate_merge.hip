@@ -113,8 +113,10 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __
     }
     part[wave][lane] = acc;
     __syncthreads();
+    // Z = 0: no split holds a key (every entry of a selection absent): out = 0, lse = -inf
+    const float Zs = s_Z;
     if (tid < kMergeCh)
-        o_rot[tid] = (((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid]) / s_Z;
+        o_rot[tid] = Zs > 0.0f ? (((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid]) / Zs : 0.0f;
     __syncthreads();
     if (tid < kMergeCh) {
         if (rotate) {
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __
             o[c0 + tid] = o_rot[tid];
         }
     }
-    if (lse && blockIdx.y == 0 && tid == 0) lse[bh] = M + logf(s_Z);
+    if (lse && blockIdx.y == 0 && tid == 0) lse[bh] = Zs > 0.0f ? M + logf(Zs) : -INFINITY;
 }
 
 // Partials with at most 64 splits (short contexts, short selections, many
@@ -190,7 +192,8 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_small_kernel(const flo
             p[k & 3] += v[k] * wk;
         }
     }
-    const float orot = (((p[0] + p[1]) + p[2]) + p[3]) / z;
+    // z = 0: no split holds a key (every entry of a selection absent): out = 0, lse = -inf
+    const float orot = z > 0.0f ? (((p[0] + p[1]) + p[2]) + p[3]) / z : 0.0f;
     if (rotate) {
         o_rot[wave][lane] = orot;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_small_kernel(const flo
     } else {
         o[c0 + lane] = orot;
     }
-    if (lse && c0 == 0 && lane == 0) lse[bh] = M + logf(z);
+    if (lse && c0 == 0 && lane == 0) lse[bh] = z > 0.0f ? M + logf(z) : -INFINITY;
 }
 
 }  // namespace

@@ -22,7 +22,8 @@ def rel_err(o_gpu, o_ref):
 class Q4Case:
     """A 4-bit workload instance: inputs, GPU cache, oracle pools."""
 
-    def __init__(self, w, lens, layer=0, device="cuda", store_chunk=None, build_oracle=True, fill=None):
+    def __init__(self, w, lens, layer=0, device="cuda", store_chunk=None, build_oracle=True, fill=None,
+                 kv_scale=None):
         import fp8_quantized_kv_amd as kvq
         self.w, self.lens, self.layer = w, list(lens), layer
         self.lay = wl.page_layout(w, self.lens)
@@ -35,6 +36,9 @@ class Q4Case:
         self.page_table = self.lay.page_table.to(device)
         self.seq_lens = torch.tensor(self.lens, dtype=torch.int32, device=device)
         self.max_seq_len = max(self.lens) if self.lens else 0
+        q_planted = self.q.clone()
+        if kv_scale is not None:  # the query grows by the inverse, so the scores keep their spread
+            self.q = (self.q / kv_scale).contiguous()
         shape = oracle.q4_pool_shape(self.lay.num_pages, w.n_kv_heads, w.page_size, w.head_dim, w.bits)
         self.k_ref = np.zeros(shape, np.uint8) if build_oracle else None
         self.v_ref = np.zeros(shape, np.uint8) if build_oracle else None
@@ -44,7 +48,9 @@ class Q4Case:
                 continue
             k, v = wl.q4_kv_tokens(w, layer, off, T, device)
             if b == 0:
-                wl.plant(w, k, self.q, 0, b=0)
+                wl.plant(w, k, q_planted, 0, b=0)
+            if kv_scale is not None:  # a power of two: exact in f32/bf16, scales become binary16 subnormals
+                k, v = k * kv_scale, v * kv_scale
             off += T
             slots = wl.slots_for(self.lay.page_table[b], np.arange(T), w.page_size)
             step = store_chunk or T

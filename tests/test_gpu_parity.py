@@ -52,6 +52,50 @@ def test_store_q4_bit_exact(kvq, D, dtype):
     assert np.array_equal(cache.v_pool.cpu().numpy(), vref)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_store_q4_subnormal_scales_bit_exact(kvq, dtype):
+    """Rows of magnitude 2^-12 .. 2^-30: group scales amax/8 fall among the
+    binary16 subnormals (m * 2^-24) or round to 0 (inert groups); codes and
+    scales bit-exact against the oracle."""
+    _say(f"store_q4 subnormal scales dtype={dtype}")
+    g = torch.Generator().manual_seed(77)
+    n_tok, H, D, ps, pages = 400, 2, 256, 16, 30
+    mag = torch.pow(2.0, -torch.randint(12, 31, (n_tok, H, 1), generator=g).float())
+    k = (torch.randn((n_tok, H, D), generator=g) * mag).to(dtype)
+    v = (torch.randn((n_tok, H, D), generator=g) * mag.flip(0)).to(dtype)
+    slots = torch.randperm(pages * ps, generator=g)[:n_tok].to(torch.int64)
+    cache = kvq.Q4Cache(pages, H, D, ps)
+    kvq.kvq_store(cache, k.cuda(), v.cuda(), slots.cuda())
+    kref = np.zeros(cache.k_pool.shape, np.uint8)
+    vref = np.zeros_like(kref)
+    oracle.q4_store(kref, vref, k.float().numpy(), v.float().numpy(), slots.numpy(), ps)
+    torch.cuda.synchronize()
+    sc = kref[..., D // 2:].copy().view(np.float16).astype(np.float32)
+    assert np.count_nonzero((sc > 0) & (sc < 2.0 ** -14)) > 1000 and np.count_nonzero(sc == 0) > 1000
+    assert np.array_equal(cache.k_pool.cpu().numpy(), kref)
+    assert np.array_equal(cache.v_pool.cpu().numpy(), vref)
+
+
+@pytest.mark.parametrize("split", [512, 2048])
+def test_decode_q4_subnormal_scales(kvq, split):
+    """Attention over a cache whose every group scale is a binary16 subnormal
+    (K and V scaled by 2^-17, the query by 2^17): within the tolerance of the
+    oracle's fp64 attention, on both matrix-core kernels (split 512: the
+    wave-pair kernel; 2048: the four-wave kernel)."""
+    w = wl.shrink(wl.GQA_32K, n_layers=1, batch=2, seq_len=0)
+    case = Q4Case(w, [3000, 1500], kv_scale=2.0 ** -17)
+    sc = case.k_ref[..., w.head_dim // 2:].copy().view(np.float16).astype(np.float32)
+    used = sc[sc != 0]
+    assert used.size > 10000 and np.all(used < 2.0 ** -14)
+    _say(f"decode_q4 subnormal scales split={split}")
+    o, lse = case.gpu_attention(split)
+    ro, rl = case.ref_attention()
+    err = rel_err(o, ro)
+    _say(f"  max_rel_err={err.max():.2e}")
+    assert np.all(np.isfinite(o)) and err.max() < TOL
+    assert np.max(np.abs(lse - rl)) < 1e-3 * max(1.0, np.abs(rl).max())
+
+
 @pytest.mark.parametrize("bits", [6, 8])
 @pytest.mark.parametrize("D", [64, 128, 256, 512])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -623,6 +667,49 @@ def test_mla_sel_matches_oracle(kvq, n_heads, n_sel, max_sel, split):
     for b, n in enumerate(n_sel):
         if n == 0:
             assert np.all(o[b] == 0) and np.all(np.isneginf(lse[b]))
+
+
+@pytest.mark.parametrize("split", [64, 512, 1024])
+def test_mla_sel_absent_tiles_splits_and_rows(kvq, split):
+    """Fixed-size lists (n_sel = max_sel) whose -1 padding covers whole key
+    tiles and whole splits, including the first tile of a split, and one
+    sequence whose list is absent throughout: outputs match the oracle, stay
+    finite, an all-absent row gives out = 0 and lse = -inf, and every split
+    without a present entry is an empty partial (m = -inf, z = 0, acc = 0)."""
+    import fp8_quantized_kv_amd as kvq_mod
+    w = wl.shrink(wl.MLA_262K, n_heads=32, seq_len=0)
+    lens = [5000, 3000, 4000]
+    case = MlaCase(w, lens, fill=0xFF)
+    max_sel = 2048
+    sel, ns = wl.dsa_selection(w, lens, [max_sel, max_sel, 100], max_sel)
+    sel[0, 0:32] = -1            # the first tile of split 0
+    sel[0, 512:1024] = -1        # whole splits at 64 and 512, half of one at 1024
+    sel[0, 1056:1100] = -1       # a tile and a half inside a split
+    sel[1, :] = -1               # every entry absent
+    sel[2, 100:] = -1            # the list's -1 padding, counted in n_sel
+    ns[:] = max_sel
+    _say(f"mla_sel_absent split={split}")
+    pa, pm, pz = kvq_mod.kvq_decode_attn_sel(case.cache, case.q, case.page_table, sel.cuda(), ns.cuda(),
+                                             w.sm_scale, split)
+    o, lse = kvq_mod.kvq_merge(case.cache, pa, pm, pz, ns.cuda(), max_sel, split)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    pa, pm, pz = pa.cpu().numpy(), pm.cpu().numpy(), pz.cpu().numpy()
+    assert np.all(np.isfinite(pa)) and np.all(np.isfinite(pz)) and not np.any(np.isnan(pm))
+    present = (sel.numpy() >= 0).reshape(3, -1, split).any(axis=2)  # [B][S]
+    for b in range(3):
+        for s_ in range(present.shape[1]):
+            if not present[b, s_]:
+                assert np.all(pz[b, :, s_] == 0) and np.all(np.isneginf(pm[b, :, s_])) and np.all(pa[b, :, s_] == 0)
+    assert np.all(np.isfinite(o))
+    assert np.all(o[1] == 0) and np.all(np.isneginf(lse[1]))
+    ro, rl = case.ref_attention_sel(sel, ns)
+    err = rel_err(o, ro)
+    _say(f"  max_rel_err={err.max():.2e}")
+    assert err.max() < TOL
+    fin = np.isfinite(rl)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.max(np.abs(lse[fin] - rl[fin])) < 1e-3 * max(1.0, np.abs(rl[fin]).max())
 
 
 def test_mla_sel_every_position_equals_dense(kvq):
