@@ -283,7 +283,11 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
 #pragma unroll
     for (int i = 0; i < (PACK ? NG / 2 : 1); ++i) ro[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY;  // running max (log2 units) of head n16
-    float z_run = 0.0f;       // this lane's share of the running sum
+    float z_run = 0.0f;       // this lane's share of the running sum (of p * 2^a_exp)
+    // The f16 context operand's exponent (mfma_common.h): p enters as p * 2^a_exp,
+    // so the partial's maximum is m_run - a_exp.  Wave-uniform.
+    int a_exp = 0;
+    uint32_t win_lo = f16_bits_pow2(-8), win_hi = f16_bits_pow2(9);
 
     // tr_b4 row address of this lane: key K(q4, e) for e = n16 & 7, where
     // K(q, e) = 4q + e (e < 4) or 16 + 4q + e - 4, at channel half n16 >> 3.
@@ -447,15 +451,29 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
             vsa[r] = *reinterpret_cast<const u32x4*>(vt + (4 * q4 + r) * RB + SOFF);
             vsb[r] = *reinterpret_cast<const u32x4*>(vt + (16 + 4 * q4 + r) * RB + SOFF);
         }
+        // The tile's largest V scale (lane: 4 scales of row lane / 2), for the
+        // context operand's exponent window.
+        const uint32_t vmax = [&] {
+            const u32x2 w = *reinterpret_cast<const u32x2*>(vt + (lane >> 1) * RB + SOFF + (NG >= 8 ? 8 * (lane & 1) : 0));
+            return max4_u16(w[0], w[1]);
+        }();
         if (t + 2 < n_sub) issue(v_pool, t + 2, v_ring);
 
         // ---- online softmax over the tile (per head = per column n16)
         // scores are finite or -inf (valid rows have finite scales), never NaN
         const float tmax = quad_max_nonan(max8f(sc)) * kTwo24;
         const bool move = tmax > m_run + kRescale || m_run == -INFINITY;
-        if (__builtin_amdgcn_ballot_w64(move) != 0ull) {
+        const bool rebase = outside_window(vmax, win_lo, win_hi);  // rare: scales far from 1
+        if (__builtin_amdgcn_ballot_w64(move) != 0ull || rebase) {
+            const int a_new = rebase ? v_exponent_for(vmax, a_exp) : a_exp;
             const float m_new = move ? fmaxf(m_run, tmax) : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+            // 0 when m_run = -inf; x 2^(a_new - a_exp) (x 1 when the exponent stays)
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new) * pow2i(a_new - a_exp);
+            if (rebase) {  // wave-uniform values: kept in scalar registers
+                a_exp = __builtin_amdgcn_readfirstlane(a_new);
+                win_lo = __builtin_amdgcn_readfirstlane(f16_bits_pow2(-8 - a_exp));
+                win_hi = __builtin_amdgcn_readfirstlane(f16_bits_pow2(9 - a_exp));
+            }
             z_run *= alpha;
             m_run = m_new;
             float al[4];
@@ -475,7 +493,7 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
         // p for keys of slots 2,3,6,7 (i = 1, 3) is taken /16 to undo the x16
         // those V codes carry.
         float p[2][4];
-        const float nm0 = -m_run, nm4 = -m_run - 4.0f;
+        const float nm0 = float(a_exp) - m_run, nm4 = nm0 - 4.0f;  // p * 2^a_exp
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -565,7 +583,7 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
             }
         }
         if (lane < 16) {
-            wm(wave)[lane] = n_keys > 0 ? m_run : -INFINITY;
+            wm(wave)[lane] = n_keys > 0 ? m_run - float(a_exp) : -INFINITY;
             wz(wave)[lane] = n_keys > 0 ? z_run : 0.0f;
         }
     }

@@ -142,13 +142,11 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
     // the code bytes 64h + 16 part, part 4 the scale chunk (bytes 128..143).
     // Lanes 0..63 copy chunks 0..63, lanes 0..15 chunks 64..79; the LDS
     // destination of chunk c is 16c, so rows land at a pitch of 80 bytes.
-    uint32_t src_off[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int c = 64 * i + (i == 0 ? lane : (lane & 15));
+    auto chunk_src = [&](int c) {
         const int row = c / 5, part = c % 5;
-        src_off[i] = uint32_t(row * kRB + (part < 4 ? 64 * h + 16 * part : 128));
-    }
+        return uint32_t(row * kRB + (part < 4 ? 64 * h + 16 * part : 128));
+    };
+    const uint32_t src_off0 = chunk_src(lane);
     uint8_t* ring = smem + wave * kWaveLds;
     uint8_t* pring = smem + (wave ^ 1) * kWaveLds;  // the other half's ring
     const uint32_t lds0 = lds_addr(ring);
@@ -160,13 +158,19 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
         const uint32_t dst = ring_base + uint32_t((t & 1) * kSlot);
         const uint8_t* r0 = pool + run_at(2 * t);
         const uint8_t* r1 = pool + run_at(2 * t + 1);
+        // The offset of chunks 64..79 is recomputed at each copy from a lane id
+        // the compiler cannot hoist: kept across the loop it would be one
+        // register too many and spill (a reload waits for every copy in flight).
+        int l16 = lane & 15;
+        asm volatile("" : "+v"(l16));
+        const uint32_t src_off1 = chunk_src(64 + l16);
         wait_lgkm0();  // earlier LDS reads of this slot have completed
         // Code bytes are read once (non-temporal); the scale chunk is read by
         // both waves of the pair, the second time from the caches.
-        dma16<true>(r0, src_off[0], dst);
-        if (lane < 16) dma16<false>(r0, src_off[1], dst + 1024u);
-        dma16<true>(r1, src_off[0], dst + 1280u);
-        if (lane < 16) dma16<false>(r1, src_off[1], dst + 2304u);
+        dma16<true>(r0, src_off0, dst);
+        if (lane < 16) dma16<false>(r0, src_off1, dst + 1024u);
+        dma16<true>(r1, src_off0, dst + 1280u);
+        if (lane < 16) dma16<false>(r1, src_off1, dst + 2304u);
     };
     if (n_sub > 0) {
         issue(k_pool, 0, k_ring);
@@ -211,7 +215,12 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY;
-    float z_run = 0.0f;
+    float z_run = 0.0f;  // of p * 2^a_exp
+    // The f16 context operand's exponent (mfma_common.h): p enters as p * 2^a_exp
+    // and the partial's maximum is m_run - a_exp.  Both halves of a pair copy the
+    // row's whole scale chunk, so they take the same a_exp.
+    int a_exp = 0;
+    uint32_t win_lo = f16_bits_pow2(-8), win_hi = f16_bits_pow2(9);
 
     const int e7 = n16 & 7;
     const int tr_key = e7 < 4 ? 4 * q4 + e7 : 16 + 4 * q4 + e7 - 4;
@@ -256,7 +265,11 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
         }
         // ---- exchange through the consumed K slot; both halves add half 0's first
         float* mine = reinterpret_cast<float*>(kt);
-        const float* other = reinterpret_cast<const float*>(pring + (t & 1) * kSlot);
+        // The partner's slot, addressed from a lane id the compiler cannot hoist
+        // (a hoisted address is one register too many across the loop).
+        int lx = lane;
+        asm volatile("" : "+v"(lx));
+        const float* other = reinterpret_cast<const float*>(pring + (t & 1) * kSlot) + lx;
         if (act) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -269,7 +282,7 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float x = other[(4 * kb + i) * 64 + lane];
+                    const float x = other[(4 * kb + i) * 64];
                     sc[kb][i] = h == 0 ? sc[kb][i] + x : x + sc[kb][i];
                 }
         }
@@ -286,37 +299,7 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
                     if (16 * kb + 4 * q4 + i >= valid) sc[kb][i] = -INFINITY;
         }
 
-        // ---- online softmax (identical in both halves)
-        float tmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                           fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-        tmax = quad_max(tmax) * kTwo24;
-        const bool move = tmax > m_run + kRescale || m_run == -INFINITY;
-        if (__builtin_amdgcn_ballot_w64(move) != 0ull) {
-            const float m_new = move ? fmaxf(m_run, tmax) : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            z_run *= alpha;
-            m_run = m_new;
-            float al[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * q4 + i, 64);
-#pragma unroll
-            for (int blk = 0; blk < 8; ++blk)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) o[blk][i] *= al[i];
-        }
-        float p[2][4];
-        const float nm0 = -m_run, nm4 = -m_run - 4.0f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[kb][i] = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], kTwo24, (i & 1) ? nm4 : nm0));
-                z_run = (i & 1) ? fmaf(16.0f, p[kb][i], z_run) : z_run + p[kb][i];
-            }
-        half2_t pp[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pp[r] = half2_t{_Float16(p[0][r]), _Float16(p[1][r])};
-
+        // V of sub-tile t has landed once at most K_t+1, V_t+1, K_t+2 are outstanding.
         if (t + 2 < n_sub) wait_vmcnt<3 * kHalfInstr>();
         else if (t + 1 < n_sub) wait_vmcnt<2 * kHalfInstr>();
         else wait_vmcnt<0>();
@@ -329,6 +312,53 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
                 for (int i = 0; i < 4; ++i) srow[i] = 0u;
             }
         }
+        // The tile's largest V scale, for the context operand's exponent window:
+        // lane reads the scales of groups 4 (n16 >> 3) .. +3 of the key its
+        // transposed code reads address (tr_off covers every key and half once;
+        // reusing its address register costs no register across the loop).
+        const uint32_t vmax = [&] {
+            const u32x2 w = *reinterpret_cast<const u32x2*>(vt + tr_off + 64);
+            return max4_u16(w[0], w[1]);
+        }();
+
+        // ---- online softmax (identical in both halves)
+        float tmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                           fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        tmax = quad_max(tmax) * kTwo24;
+        const bool move = tmax > m_run + kRescale || m_run == -INFINITY;
+        const bool rebase = outside_window(vmax, win_lo, win_hi);  // rare: scales far from 1
+        if (__builtin_amdgcn_ballot_w64(move) != 0ull || rebase) {
+            const int a_new = rebase ? v_exponent_for(vmax, a_exp) : a_exp;
+            const float m_new = move ? fmaxf(m_run, tmax) : m_run;
+            // x 2^(a_new - a_exp): x 1 when the exponent stays
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new) * pow2i(a_new - a_exp);
+            if (rebase) {  // wave-uniform values: kept in scalar registers
+                a_exp = __builtin_amdgcn_readfirstlane(a_new);
+                win_lo = __builtin_amdgcn_readfirstlane(f16_bits_pow2(-8 - a_exp));
+                win_hi = __builtin_amdgcn_readfirstlane(f16_bits_pow2(9 - a_exp));
+            }
+            z_run *= alpha;
+            m_run = m_new;
+            float al[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * q4 + i, 64);
+#pragma unroll
+            for (int blk = 0; blk < 8; ++blk)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[blk][i] *= al[i];
+        }
+        float p[2][4];
+        const float nm0 = float(a_exp) - m_run, nm4 = nm0 - 4.0f;  // p * 2^a_exp
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[kb][i] = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], kTwo24, (i & 1) ? nm4 : nm0));
+                z_run = (i & 1) ? fmaf(16.0f, p[kb][i], z_run) : z_run + p[kb][i];
+            }
+        half2_t pp[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pp[r] = half2_t{_Float16(p[0][r]), _Float16(p[1][r])};
 
         // ---- context over this half's four groups
 #pragma unroll
@@ -376,7 +406,7 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
             }
         }
         if (h == 0 && lane < 16) {
-            wm(wave)[lane] = n_keys > 0 ? m_run : -INFINITY;
+            wm(wave)[lane] = n_keys > 0 ? m_run - float(a_exp) : -INFINITY;
             wz(wave)[lane] = n_keys > 0 ? z_run : 0.0f;
         }
     }

@@ -63,6 +63,52 @@ __device__ __forceinline__ half8_t unpack8(uint32_t w) {
     return __builtin_bit_cast(half8_t, r);
 }
 
+// The f16 context operand p * 2^a * (V scale): p = 2^(score - m) <= 2^6 (the
+// lazily moving maximum), so with the tile's largest V scale s in
+// [2^(-8-a), 2^(9-a)) every product stays below 2^15 and the dominant ones
+// above 2^-8 (full f16 precision).  a is a per-wave power-of-two exponent in
+// [-7, 9] (p * 2^a <= 2^15); it starts at 0 and moves when a tile's largest
+// V scale leaves the window, e.g. for binary16-subnormal scales.  Scales are
+// non-negative f16, so their bit patterns order as the values do.
+constexpr int kVExpMin = -7, kVExpMax = 9;
+
+// binary16 bits of 2^e (0x10000, above every f16, for e >= 16; 0 below 2^-24).
+__device__ __forceinline__ uint32_t f16_bits_pow2(int e) {
+    return e >= 16 ? 0x10000u : (e >= -14 ? uint32_t(e + 15) << 10 : (e >= -24 ? 1u << (e + 24) : 0u));
+}
+
+// Largest of the four f16 bit patterns held in two dwords.
+__device__ __forceinline__ uint32_t max4_u16(uint32_t w0, uint32_t w1) {
+    typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+    const u16x2 m = __builtin_elementwise_max(__builtin_bit_cast(u16x2, w0), __builtin_bit_cast(u16x2, w1));
+    return max(uint32_t(m[0]), uint32_t(m[1]));
+}
+
+// Wave-uniform: does the wave's largest value of x (one f16 bit pattern per
+// lane) lie outside [lo, hi)?
+__device__ __forceinline__ bool outside_window(uint32_t x, uint32_t lo, uint32_t hi) {
+    return __builtin_amdgcn_ballot_w64(x >= lo) == 0ull || __builtin_amdgcn_ballot_w64(x >= hi) != 0ull;
+}
+
+// The exponent a for the wave's largest V scale (x: one f16 bit pattern per
+// lane), clamped to [kVExpMin, kVExpMax]; a_old if every scale is 0.  The
+// scale's exponent e = floor(log2 max) in [-24, 15] is found by a binary
+// search on wave ballots (compares against scalars only: no vector registers
+// beyond x in this rarely taken path).
+__device__ __forceinline__ int v_exponent_for(uint32_t x, int a_old) {
+    if (__builtin_amdgcn_ballot_w64(x != 0u) == 0ull) return a_old;
+    int lo = -24, hi = 15;  // some lane holds at least 2^lo; none holds 2^(hi + 1)
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (__builtin_amdgcn_ballot_w64(x >= f16_bits_pow2(mid)) != 0ull) lo = mid;
+        else hi = mid - 1;
+    }
+    return min(max(-lo, kVExpMin), kVExpMax);
+}
+
+// 2^e for an integer e in [-126, 127], exactly.
+__device__ __forceinline__ float pow2i(int e) { return __uint_as_float(uint32_t(e + 127) << 23); }
+
 __device__ __forceinline__ f32x4 mfma(half8_t a, half8_t b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
