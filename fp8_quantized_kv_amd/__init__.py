@@ -39,7 +39,7 @@ _DTYPES = {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float16: DT_F16
 
 EXPORTED = ("kvq_status_string", "kvq_row_bytes", "kvq_pool_bytes", "kvq_num_splits", "kvq_store",
             "kvq_rotate_q", "kvq_store_rotate_q", "kvq_decode_attn", "kvq_decode_attn_rows", "kvq_decode_attn_sel", "kvq_merge",
-            "kvq_tq_rotate_q", "kvq_stream_read")
+            "kvq_tq_rotate_q", "kvq_stream_read", "kvq_attend_workspace_bytes", "kvq_attend")
 
 
 class KvqCacheDesc(ctypes.Structure):
@@ -70,6 +70,8 @@ def _load():
         "kvq_tq_rotate_q": ([P, P, I32, P], I32),
         "kvq_stream_read": ([P, ctypes.c_size_t, I32, P, P], I32),
         "kvq_decode_attn_sel": ([C, P, I32, P, I32, P, P, I32, I32, F, I32, P, P, P, P], I32),
+        "kvq_attend_workspace_bytes": ([C, I32, I32, I32, I32], ctypes.c_size_t),
+        "kvq_attend": ([C, P, I32, P, I32, P, I32, I32, F, I32, P, ctypes.c_size_t, P, P, P], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -392,6 +394,36 @@ def kvq_merge(cache, part_acc, part_m, part_z, seq_lens, max_seq_len, split_keys
     lp = _dev(lse, "lse", dtype=torch.float32, shape=(B, Hq)) if lse is not None else None
     _check(lib.kvq_merge(ctypes.byref(cache.desc), pa, pm, pz, slp, B, Hq, int(max_seq_len), int(split_keys),
                          1 if cache.fmt in ROTATED_FORMATS else 0, op, lp, _stream(part_acc)), "kvq_merge")
+    return out, lse
+
+
+def kvq_attend_workspace_bytes(cache, batch, n_q_heads, max_seq_len, split_keys):
+    return int(lib.kvq_attend_workspace_bytes(ctypes.byref(cache.desc), batch, n_q_heads, int(max_seq_len),
+                                              int(split_keys)))
+
+
+def kvq_attend(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_keys, workspace=None, out=None, lse=None,
+               want_lse=True):
+    """Decode attention and merge in one call (kvq_decode_attn + kvq_merge, the partials in `workspace`,
+    a uint8 device tensor of at least kvq_attend_workspace_bytes bytes).  Returns (out, lse)."""
+    B, Hq, D = q.shape
+    need = kvq_attend_workspace_bytes(cache, B, Hq, max_seq_len, split_keys)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, cache.dv), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    qp = _dev(q, "q", dtype=torch.float32, shape=(B, Hq, cache.head_dim))
+    ptp = _dev(page_table, "page_table", dtype=torch.int32)
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [batch][max_pages]")
+    slp = _dev(seq_lens, "seq_lens", dtype=torch.int32, shape=(B,))
+    wp = _dev(workspace, "workspace", dtype=torch.uint8)
+    op = _dev(out, "out", dtype=torch.float32, shape=(B, Hq, cache.dv))
+    lp = _dev(lse, "lse", dtype=torch.float32, shape=(B, Hq)) if lse is not None else None
+    _check(lib.kvq_attend(ctypes.byref(cache.desc), qp, Hq, ptp, int(page_table.shape[1]), slp, B, int(max_seq_len),
+                          float(sm_scale), int(split_keys), wp, workspace.numel(), op, lp, _stream(q)), "kvq_attend")
     return out, lse
 
 

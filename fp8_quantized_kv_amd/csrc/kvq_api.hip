@@ -78,6 +78,95 @@ kvq_status check_seq_args(const kvq_cache* c, int32_t n_q_heads, const int32_t* 
     return KVQ_OK;
 }
 
+// The decode kernel kvq_decode_attn runs for these (validated) arguments.
+kvq_status launch_decode_for(const kvq_cache* cache, const kvq::DecodeArgs& a, hipStream_t stream) {
+    if (is_h32(cache->format)) {
+        const kvq::Q4Pool pool = q4_pool(cache);
+        if (pool.bits == 4 && kvq::decode_q4_pair_supported(pool, a))
+            return launched(kvq::launch_decode_q4_pair(pool, a, stream));
+        if (kvq::decode_q4_mfma_supported(pool, a)) return launched(kvq::launch_decode_q4_mfma(pool, a, stream));
+        return launched(kvq::launch_decode_q4_simple(pool, a, stream));
+    }
+    const kvq::Fp8Pool pool = fp8_pool(cache);
+    if (cache->format == KVQ_FMT_TQ4_LATENT) {
+        if (kvq::decode_fp8_mfma_supported(pool, a)) return launched(kvq::launch_decode_tq4_mfma(pool, a, stream));
+        return launched(kvq::launch_decode_tq4_simple(pool, a, stream));
+    }
+    if (kvq::decode_fp8_mfma_supported(pool, a)) return launched(kvq::launch_decode_fp8_mfma(pool, a, stream));
+    return launched(kvq::launch_decode_fp8_simple(pool, a, stream));
+}
+
+// Checks shared by kvq_decode_attn and kvq_attend, after check_cache.
+kvq_status check_decode_args(const kvq_cache* cache, int32_t n_q_heads, int32_t max_pages, const int32_t* seq_lens,
+                             int32_t batch, int32_t max_seq_len, float sm_scale, int32_t split_keys) {
+    // Hadamard-32 formats split at the 512-key chunk; the latent formats at any 32-key tile
+    kvq_status st = check_seq_args(cache, n_q_heads, seq_lens, batch, max_seq_len, split_keys,
+                                   is_h32(cache->format) ? 512 : 32);
+    if (st != KVQ_OK) return st;
+    if (max_pages < 1 || int64_t(max_seq_len) > int64_t(max_pages) * cache->page_size) return KVQ_ERR_INVALID_ARG;
+    if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return KVQ_ERR_INVALID_ARG;
+    return KVQ_OK;
+}
+
+// Output channels of a cache's attention (the merge's Dv).
+int32_t value_dim(const kvq_cache* c) { return is_h32(c->format) ? c->head_dim : c->head_dim - c->rope_dim; }
+
+// The merge (and, for TQ4, the inverse rotation after it) of validated arguments.
+kvq_status launch_merge_for(const kvq_cache* cache, const kvq::MergeArgs& a, hipStream_t stream) {
+    kvq_status st = launched(kvq::launch_merge(a, stream));
+    if (st != KVQ_OK || cache->format != KVQ_FMT_TQ4_LATENT) return st;
+    return launched(kvq::launch_tq_rotate(a.out, a.out, int64_t(a.batch) * a.n_q_heads, 512, true, stream));
+}
+
+// Partials of kvq_attend inside its workspace: part_acc [B][H_q][S][Dv], then
+// part_m and part_z [B][H_q][S], all f32, each starting on a 256-byte boundary.
+struct AttendLayout {
+    size_t acc, m, z, total;
+};
+AttendLayout attend_layout(int64_t batch, int64_t n_q_heads, int64_t S, int64_t dv) {
+    auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+    AttendLayout l{};
+    const size_t n_mz = size_t(batch) * size_t(n_q_heads) * size_t(S);
+    l.acc = 0;
+    l.m = up(n_mz * size_t(dv) * sizeof(float));
+    l.z = l.m + up(n_mz * sizeof(float));
+    l.total = l.z + up(n_mz * sizeof(float));
+    return l;
+}
+
+// kvq_attend's work on a validated workspace of at least attend_layout().total bytes.
+kvq_status attend_on(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
+                     int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
+                     int32_t split_keys, uint8_t* ws, float* out, float* lse, hipStream_t stream) {
+    const int32_t S = kvq_num_splits(max_seq_len, split_keys);
+    const AttendLayout l = attend_layout(batch, n_q_heads, S, value_dim(cache));
+    float* pa = reinterpret_cast<float*>(ws + l.acc);
+    float* pm = reinterpret_cast<float*>(ws + l.m);
+    float* pz = reinterpret_cast<float*>(ws + l.z);
+    const kvq::DecodeArgs d{q, n_q_heads, page_table, max_pages, seq_lens, batch, max_seq_len, S, sm_scale,
+                            split_keys, pa, pm, pz};
+    kvq_status st = launch_decode_for(cache, d, stream);
+    if (st != KVQ_OK) return st;
+    const kvq::MergeArgs m{pa, pm, pz, seq_lens, batch, n_q_heads, max_seq_len, S, split_keys, value_dim(cache),
+                           is_h32(cache->format), out, lse};
+    return launch_merge_for(cache, m, stream);
+}
+
+// Argument checks of kvq_attend (and its variants) before the workspace.
+kvq_status check_attend_args(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
+                             int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                             float sm_scale, int32_t split_keys, const float* out, const float* lse) {
+    kvq_status st = check_cache(cache);
+    if (st != KVQ_OK) return st;
+    st = check_decode_args(cache, n_q_heads, max_pages, seq_lens, batch, max_seq_len, sm_scale, split_keys);
+    if (st != KVQ_OK) return st;
+    if (batch == 0) return KVQ_OK;
+    if (!aligned(q) || !aligned(page_table, 4) || !aligned(out) || (lse && !aligned(lse, 4)))
+        return KVQ_ERR_INVALID_ARG;
+    if (int64_t(batch) * n_q_heads > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
+    return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -188,30 +277,14 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const float* q, int32_t n_q_h
                            hipStream_t stream) {
     kvq_status st = check_cache(cache);
     if (st != KVQ_OK) return st;
-    // Hadamard-32 formats split at the 512-key chunk; the latent formats at any 32-key tile
-    st = check_seq_args(cache, n_q_heads, seq_lens, batch, max_seq_len, split_keys, is_h32(cache->format) ? 512 : 32);
+    st = check_decode_args(cache, n_q_heads, max_pages, seq_lens, batch, max_seq_len, sm_scale, split_keys);
     if (st != KVQ_OK) return st;
-    if (max_pages < 1 || int64_t(max_seq_len) > int64_t(max_pages) * cache->page_size) return KVQ_ERR_INVALID_ARG;
-    if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return KVQ_ERR_INVALID_ARG;
     if (batch == 0) return KVQ_OK;
     if (!aligned(q) || !aligned(page_table, 4) || !aligned(part_acc) || !aligned(part_m, 4) || !aligned(part_z, 4))
         return KVQ_ERR_INVALID_ARG;
-    kvq::DecodeArgs a{q, n_q_heads, page_table, max_pages, seq_lens, batch, max_seq_len,
-                      kvq_num_splits(max_seq_len, split_keys), sm_scale, split_keys, part_acc, part_m, part_z};
-    if (is_h32(cache->format)) {
-        const kvq::Q4Pool pool = q4_pool(cache);
-        if (pool.bits == 4 && kvq::decode_q4_pair_supported(pool, a))
-            return launched(kvq::launch_decode_q4_pair(pool, a, stream));
-        if (kvq::decode_q4_mfma_supported(pool, a)) return launched(kvq::launch_decode_q4_mfma(pool, a, stream));
-        return launched(kvq::launch_decode_q4_simple(pool, a, stream));
-    }
-    const kvq::Fp8Pool pool = fp8_pool(cache);
-    if (cache->format == KVQ_FMT_TQ4_LATENT) {
-        if (kvq::decode_fp8_mfma_supported(pool, a)) return launched(kvq::launch_decode_tq4_mfma(pool, a, stream));
-        return launched(kvq::launch_decode_tq4_simple(pool, a, stream));
-    }
-    if (kvq::decode_fp8_mfma_supported(pool, a)) return launched(kvq::launch_decode_fp8_mfma(pool, a, stream));
-    return launched(kvq::launch_decode_fp8_simple(pool, a, stream));
+    const kvq::DecodeArgs a{q, n_q_heads, page_table, max_pages, seq_lens, batch, max_seq_len,
+                            kvq_num_splits(max_seq_len, split_keys), sm_scale, split_keys, part_acc, part_m, part_z};
+    return launch_decode_for(cache, a, stream);
 }
 
 kvq_status kvq_decode_attn_rows(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
@@ -280,15 +353,29 @@ kvq_status kvq_merge(const kvq_cache* cache, const float* part_acc, const float*
         (lse && !aligned(lse, 4)))
         return KVQ_ERR_INVALID_ARG;
     if (int64_t(batch) * n_q_heads > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
-    kvq::MergeArgs a{part_acc, part_m, part_z, seq_lens, batch, n_q_heads, max_seq_len,
-                     kvq_num_splits(max_seq_len, split_keys), split_keys,
-                     q4 ? cache->head_dim : cache->head_dim - cache->rope_dim, q4, out, lse};
-    if (tq) {
-        st = launched(kvq::launch_merge(a, stream));
-        if (st != KVQ_OK) return st;
-        return launched(kvq::launch_tq_rotate(out, out, int64_t(batch) * n_q_heads, 512, true, stream));
-    }
-    return launched(kvq::launch_merge(a, stream));
+    const kvq::MergeArgs a{part_acc, part_m, part_z, seq_lens, batch, n_q_heads, max_seq_len,
+                           kvq_num_splits(max_seq_len, split_keys), split_keys, value_dim(cache), q4, out, lse};
+    return launch_merge_for(cache, a, stream);
+}
+
+size_t kvq_attend_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
+                                  int32_t split_keys) {
+    if (check_cache(cache) != KVQ_OK || batch < 0 || n_q_heads < 1 || max_seq_len < 0 || split_keys < 1) return 0;
+    return attend_layout(batch, n_q_heads, kvq_num_splits(max_seq_len, split_keys), value_dim(cache)).total;
+}
+
+kvq_status kvq_attend(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
+                      int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
+                      int32_t split_keys, void* workspace, size_t workspace_bytes, float* out, float* lse,
+                      hipStream_t stream) {
+    kvq_status st = check_attend_args(cache, q, n_q_heads, page_table, max_pages, seq_lens, batch, max_seq_len,
+                                      sm_scale, split_keys, out, lse);
+    if (st != KVQ_OK || batch == 0) return st;
+    const size_t need =
+        attend_layout(batch, n_q_heads, kvq_num_splits(max_seq_len, split_keys), value_dim(cache)).total;
+    if (!aligned(workspace, 256) || workspace_bytes < need) return KVQ_ERR_INVALID_ARG;
+    return attend_on(cache, q, n_q_heads, page_table, max_pages, seq_lens, batch, max_seq_len, sm_scale, split_keys,
+                     static_cast<uint8_t*>(workspace), out, lse, stream);
 }
 
 kvq_status kvq_tq_rotate_q(const float* q, float* q_rot, int32_t n_rows, hipStream_t stream) {

@@ -307,6 +307,33 @@ kvq_status kvq_merge(const kvq_cache* cache, const float* part_acc, const float*
                      const int32_t* seq_lens, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
                      int32_t split_keys, int32_t inverse_rotate, float* out, float* lse, hipStream_t stream);
 
+/* ---------------------------------------------------------------- decode + merge */
+
+/* Bytes of the workspace kvq_attend needs for these sizes: the partials
+ * [batch][n_q_heads][S][Dv] f32 and two [batch][n_q_heads][S] f32 arrays,
+ * each rounded up to 256 bytes (S = kvq_num_splits(max_seq_len, split_keys),
+ * Dv as for kvq_decode_attn).  0 on invalid input.  Host only. */
+size_t kvq_attend_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
+                                  int32_t split_keys);
+
+/* The attention of a decode step in one call (TensorFold "What it is": attend
+ * over the 4-bit cache in chunks, merge in order, rotate the output back once;
+ * colibri split-T commit: partials (cl[K], m, z), then the log-sum-exp merge):
+ * kvq_decode_attn with its partials in `workspace`, then kvq_merge of them into
+ * out / lse (with the inverse rotation of the rotated formats).  Every argument
+ * means what it means for those two calls; out and lse are the same bits as
+ * the two calls give.  q is the rotated query for the rotated formats.
+ * workspace: device, 256-byte aligned, at least kvq_attend_workspace_bytes()
+ * bytes, owned by the caller; its contents on entry do not matter and on
+ * return are the partials (layout: part_acc, then part_m, then part_z, each
+ * at a 256-byte boundary).  out: [batch][n_q_heads][Dv] f32; lse:
+ * [batch][n_q_heads] f32 or NULL.  KVQ_ERR_INVALID_ARG for a workspace that
+ * is too small or misaligned. */
+kvq_status kvq_attend(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
+                      int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
+                      int32_t split_keys, void* workspace, size_t workspace_bytes, float* out, float* lse,
+                      hipStream_t stream);
+
 /* Query rotation of the TQ4 latent format (the colibri pull request's
  * Summary, "Why rotated-int4 for the 4-bit tier": the query is rotated once,
  * with the rotation the rows were stored with): each row's 512 latent values

@@ -258,3 +258,33 @@ def test_rows_argument_checks(kvq):
     assert call(_q4(kvq), n_rows=-1) == INVALID
     assert call(_fp8(kvq), H=16) == UNSUPPORTED
     assert call(_fp8(kvq, format=kvq.FMT_TQ4_LATENT), H=16) == UNSUPPORTED
+
+
+def test_attend_workspace_and_argument_checks(kvq):
+    """kvq_attend: the workspace size helper's layout (partials, then m, then z,
+    each rounded up to 256 bytes) and the host checks of the call itself."""
+    L = kvq.lib
+    P = ctypes.c_void_p
+    d = _q4(kvq)
+    # 262144 positions, split 2048: S = 128; 24 heads x 128 x 256 f32, then 2 x 24 x 128 f32
+    acc = 24 * 128 * 256 * 4
+    mz = ((24 * 128 * 4 + 255) // 256) * 256
+    big = _q4(kvq, num_pages=16384)
+    assert L.kvq_attend_workspace_bytes(ctypes.byref(big), 1, 24, 262144, 2048) == acc + 2 * mz
+    e = _fp8(kvq, num_pages=16384)
+    assert L.kvq_attend_workspace_bytes(ctypes.byref(e), 1, 128, 262144, 2048) == (128 * 128 * 512 * 4 +
+                                                                                    2 * 128 * 128 * 4)
+    assert L.kvq_attend_workspace_bytes(None, 1, 24, 1024, 512) == 0
+    assert L.kvq_attend_workspace_bytes(ctypes.byref(d), 1, 0, 1024, 512) == 0
+    need = L.kvq_attend_workspace_bytes(ctypes.byref(d), 2, 24, 1024, 512)
+    assert need > 0
+    f = ctypes.c_float(0.0625)
+
+    def call(ws=A + 0x200000, nbytes=need, out=A + 0x300000, lse=A + 0x400000, split=512, batch=2, desc=d):
+        return L.kvq_attend(ctypes.byref(desc), P(A), 24, P(A), 64, P(A), batch, 1024, f, split, P(ws), nbytes,
+                            P(out), P(lse), None)
+    assert call(nbytes=need - 1) == INVALID          # workspace too small
+    assert call(ws=A + 0x200010) == INVALID          # workspace not 256-byte aligned
+    assert call(out=A + 8) == INVALID                # misaligned out
+    assert call(split=500) == INVALID                # split_keys % 512
+    assert call(batch=0) == 0                        # nothing to do
