@@ -39,7 +39,8 @@ _DTYPES = {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float16: DT_F16
 
 EXPORTED = ("kvq_status_string", "kvq_row_bytes", "kvq_pool_bytes", "kvq_num_splits", "kvq_store",
             "kvq_rotate_q", "kvq_store_rotate_q", "kvq_decode_attn", "kvq_decode_attn_rows", "kvq_decode_attn_sel", "kvq_merge",
-            "kvq_tq_rotate_q", "kvq_stream_read", "kvq_attend_workspace_bytes", "kvq_attend")
+            "kvq_tq_rotate_q", "kvq_stream_read", "kvq_attend_workspace_bytes", "kvq_attend",
+            "kvq_attend_noalloc")
 
 
 class KvqCacheDesc(ctypes.Structure):
@@ -72,6 +73,7 @@ def _load():
         "kvq_decode_attn_sel": ([C, P, I32, P, I32, P, P, I32, I32, F, I32, P, P, P, P], I32),
         "kvq_attend_workspace_bytes": ([C, I32, I32, I32, I32], ctypes.c_size_t),
         "kvq_attend": ([C, P, I32, P, I32, P, I32, I32, F, I32, P, ctypes.c_size_t, P, P, P], I32),
+        "kvq_attend_noalloc": ([C, P, I32, P, I32, P, I32, I32, F, I32, P, P, P], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -424,6 +426,26 @@ def kvq_attend(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_keys
     lp = _dev(lse, "lse", dtype=torch.float32, shape=(B, Hq)) if lse is not None else None
     _check(lib.kvq_attend(ctypes.byref(cache.desc), qp, Hq, ptp, int(page_table.shape[1]), slp, B, int(max_seq_len),
                           float(sm_scale), int(split_keys), wp, workspace.numel(), op, lp, _stream(q)), "kvq_attend")
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # KVQ_NOALLOC_SCRATCH_BYTES
+
+
+def kvq_attend_noalloc(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_keys, out, lse=None):
+    """kvq_attend with the partials in the library's static per-GPU scratch (no workspace argument,
+    nothing allocated; out and lse must be given).  Calls that overlap on one GPU race on the scratch."""
+    B, Hq, D = q.shape
+    qp = _dev(q, "q", dtype=torch.float32, shape=(B, Hq, cache.head_dim))
+    ptp = _dev(page_table, "page_table", dtype=torch.int32)
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [batch][max_pages]")
+    slp = _dev(seq_lens, "seq_lens", dtype=torch.int32, shape=(B,))
+    op = _dev(out, "out", dtype=torch.float32, shape=(B, Hq, cache.dv))
+    lp = _dev(lse, "lse", dtype=torch.float32, shape=(B, Hq)) if lse is not None else None
+    _check(lib.kvq_attend_noalloc(ctypes.byref(cache.desc), qp, Hq, ptp, int(page_table.shape[1]), slp, B,
+                                  int(max_seq_len), float(sm_scale), int(split_keys), op, lp, _stream(q)),
+           "kvq_attend_noalloc")
     return out, lse
 
 

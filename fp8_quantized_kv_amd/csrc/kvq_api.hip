@@ -3,7 +3,13 @@
 // frees or synchronizes.
 #include "kvq.h"
 
+#include <mutex>
+
 #include "internal.h"
+
+// kvq_attend_noalloc's workspace (see device_scratch below).
+static_assert(KVQ_NOALLOC_SCRATCH_BYTES % 256 == 0, "whole 256-byte blocks");
+static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -167,6 +173,30 @@ kvq_status check_attend_args(const kvq_cache* cache, const float* q, int32_t n_q
     return KVQ_OK;
 }
 
+// ------------------------------------------------------------ static scratch
+// kvq_attend_noalloc's workspace: a file-scope device array, one copy per GPU
+// the library runs on, held until the process ends.  In host code `scratch`
+// is only a host-side stand-in for the symbol; the device address of each
+// GPU's copy comes from hipGetSymbolAddress, taken once per device (with that
+// device current) on the entry point's first call there, and only that
+// address is ever passed to a kernel.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+uint8_t* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The current device's copy of the scratch array (nullptr if the runtime cannot give it).
+uint8_t* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? static_cast<uint8_t*>(p) : nullptr;
+    });
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -177,6 +207,7 @@ const char* kvq_status_string(kvq_status s) {
         case KVQ_ERR_INVALID_ARG: return "invalid argument";
         case KVQ_ERR_UNSUPPORTED: return "unsupported shape or format";
         case KVQ_ERR_LAUNCH: return "kernel launch failed";
+        case KVQ_ERR_TOO_LARGE: return "request exceeds the static scratch of kvq_attend_noalloc";
     }
     return "unknown status";
 }
@@ -376,6 +407,23 @@ kvq_status kvq_attend(const kvq_cache* cache, const float* q, int32_t n_q_heads,
     if (!aligned(workspace, 256) || workspace_bytes < need) return KVQ_ERR_INVALID_ARG;
     return attend_on(cache, q, n_q_heads, page_table, max_pages, seq_lens, batch, max_seq_len, sm_scale, split_keys,
                      static_cast<uint8_t*>(workspace), out, lse, stream);
+}
+
+kvq_status kvq_attend_noalloc(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
+                              int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                              float sm_scale, int32_t split_keys, float* out, float* lse, hipStream_t stream) {
+    kvq_status st = check_attend_args(cache, q, n_q_heads, page_table, max_pages, seq_lens, batch, max_seq_len,
+                                      sm_scale, split_keys, out, lse);
+    if (st != KVQ_OK || batch == 0) return st;
+    const size_t need =
+        attend_layout(batch, n_q_heads, kvq_num_splits(max_seq_len, split_keys), value_dim(cache)).total;
+    if (need > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_TOO_LARGE;
+    uint8_t* ws = device_scratch();
+    if (!ws) return KVQ_ERR_LAUNCH;
+    // The partials are written in full by the decode before the merge reads
+    // them, so what an earlier call left in the array needs no clearing.
+    return attend_on(cache, q, n_q_heads, page_table, max_pages, seq_lens, batch, max_seq_len, sm_scale, split_keys,
+                     ws, out, lse, stream);
 }
 
 kvq_status kvq_tq_rotate_q(const float* q, float* q_rot, int32_t n_rows, hipStream_t stream) {

@@ -29,7 +29,8 @@
  * Conventions for every entry point:
  *  - Ownership: the caller allocates and owns every buffer (device memory
  *    unless stated).  The library never allocates, frees or synchronizes,
- *    and keeps no mutable global state, so calls are thread-safe.
+ *    and keeps no mutable global state, so calls are thread-safe -- except
+ *    kvq_attend_noalloc, whose partials live in a static per-GPU array.
  *  - Asynchrony: work is enqueued on `stream` (0 = the null stream).  The
  *    returned status covers argument validation, done on the host before any
  *    launch, and the launch itself; a device fault surfaces at the caller's
@@ -61,7 +62,8 @@ typedef enum {
     KVQ_OK = 0,
     KVQ_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size or pairing */
     KVQ_ERR_UNSUPPORTED = -2,  /* valid request the library does not implement */
-    KVQ_ERR_LAUNCH = -3        /* the HIP runtime rejected a launch */
+    KVQ_ERR_LAUNCH = -3,       /* the HIP runtime rejected a launch */
+    KVQ_ERR_TOO_LARGE = -4     /* kvq_attend_noalloc: partials beyond its static scratch */
 } kvq_status;
 
 typedef enum {
@@ -333,6 +335,25 @@ kvq_status kvq_attend(const kvq_cache* cache, const float* q, int32_t n_q_heads,
                       int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
                       int32_t split_keys, void* workspace, size_t workspace_bytes, float* out, float* lse,
                       hipStream_t stream);
+
+/* kvq_attend for callers that cannot allocate device memory -- code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc:
+ * the same work with the partials in a static device array of
+ * KVQ_NOALLOC_SCRATCH_BYTES (64 MiB) held on each GPU the library runs on
+ * until the process ends, instead of a workspace argument.  The entry point
+ * calls no allocating routine; the first call on a device looks the array's
+ * address up once (hipGetSymbolAddress).  Every argument, the outputs and
+ * their bits are those of kvq_attend.  A request whose partials
+ * (kvq_attend_workspace_bytes) exceed the array returns KVQ_ERR_TOO_LARGE
+ * before any launch.  All calls on one GPU share its array: calls that
+ * overlap in time on one GPU (different streams, or threads) race on it and
+ * must be serialized by the caller; calls on one stream are ordered.  The
+ * array keeps the last call's partials; nothing in it needs clearing, since
+ * every call writes the partials it reads. */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kvq_status kvq_attend_noalloc(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
+                              int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                              float sm_scale, int32_t split_keys, float* out, float* lse, hipStream_t stream);
 
 /* Query rotation of the TQ4 latent format (the colibri pull request's
  * Summary, "Why rotated-int4 for the 4-bit tier": the query is rotated once,
