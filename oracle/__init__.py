@@ -178,6 +178,21 @@ def q4_decode_rows(rows, D, bits=4):
     return out
 
 
+def q4_chunk_attention(k_pool, v_pool, q, page_row, row_lens, sm_scale):
+    """Attention of several query rows of ONE sequence over its paged cache
+    (a prompt chunk: TensorFold issue "qwen27 CUDA: an opt-in 4-bit attention
+    cache", "What it is" -- prompt chunks are packed, then attended over the
+    decoded slots): row i attends positions [0, row_lens[i]) of the sequence
+    whose page-table row is page_row; for a chunk starting at position P,
+    row_lens[i] = P + i + 1 (causal within the chunk).  This is
+    q4_attention with the page-table row repeated for every row.
+    q: [C][H_q][D] float32 (unrotated).  Returns (o [C][H_q][D], lse [C][H_q])."""
+    q = _c(q, np.float32)
+    page_row = _c(page_row, np.int32).reshape(-1)
+    pt = np.ascontiguousarray(np.broadcast_to(page_row, (q.shape[0], page_row.size)))
+    return q4_attention(k_pool, v_pool, q, pt, _c(row_lens, np.int32), sm_scale)
+
+
 def q4_pool_shape(num_pages, n_kv_heads, page_size, D, bits=4):
     return (num_pages, n_kv_heads, page_size, q4_row_bytes(D, bits))
 

@@ -129,6 +129,37 @@ def test_q4_attention_subnormal_scales_matches_brute_force():
     assert np.max(np.abs(lse - lb)) < 1e-9
 
 
+@pytest.mark.parametrize("P,C", [(300, 40), (0, 33), (1000, 1)])
+def test_chunk_attention_matches_causal_brute_force(P, C):
+    """A prompt chunk of C rows at positions P .. P + C - 1 (TensorFold "What
+    it is": prompt chunks are packed, then attended over the decoded slots):
+    numpy in matrix form -- all scores at once, the causal mask j > P + i set
+    to -inf, a row softmax, the weighted sum, the inverse rotation -- against
+    the oracle's chunk attention."""
+    T = P + C
+    w = wl.shrink(SMALL, batch=1)
+    kp, vp, _, pt, _ = _build_q4(w, [T])
+    g = np.random.default_rng(P + C)
+    q = g.standard_normal((C, w.n_q_heads, w.head_dim)).astype(np.float32)
+    lens = P + 1 + np.arange(C, dtype=np.int32)
+    o, lse = oracle.q4_chunk_attention(kp, vp, q, pt[0], lens, w.sm_scale)
+    j = np.arange(T)
+    slots = pt[0, j // w.page_size].astype(np.int64) * w.page_size + j % w.page_size
+    pages, offs = slots // w.page_size, slots % w.page_size
+    mask = j[None, :] > (P + np.arange(C))[:, None]              # [C][T]
+    for h in range(w.n_q_heads):
+        g_kv = h // w.group
+        K = _np_decode_q4(kp[pages, g_kv, offs], w.head_dim)     # [T][D], rotated space
+        V = _np_decode_q4(vp[pages, g_kv, offs], w.head_dim)
+        S = w.sm_scale * (_rot(q[:, h].astype(np.float64)) @ K.T)  # [C][T]
+        S[mask] = -np.inf
+        Pm = scipy.special.softmax(S, axis=1)
+        ob = _rot(Pm @ V)
+        lb = scipy.special.logsumexp(S, axis=1)
+        assert np.max(np.abs(o[:, h] - ob)) < 1e-12 * max(1.0, np.abs(ob).max())
+        assert np.max(np.abs(lse[:, h] - lb)) < 1e-12 * max(1.0, np.abs(lb).max())
+
+
 def test_rotated_space_equals_original_space():
     """Attending with H q over rotated rows, then rotating back, equals plain
     attention of q over the reconstructed rows x = H y."""
