@@ -500,6 +500,82 @@ class RaggedBench(_Bench):
     flops_per_layer = None
 
 
+class ChunkBench(_Bench):
+    """A prompt chunk (TensorFold "What it is": prompt chunks are packed, then
+    attended over the decoded slots): one layer's 32K-position 4-bit cache and
+    a chunk of chunk_rows rows after it.  Step: the chunk's K/V stored
+    (kvq_store), its queries rotated (kvq_rotate_q), the chunk's attention as
+    split partials (kvq_prefill_attn; row r attends [0, P + r]), the merge."""
+
+    DECODE = 2
+    DECODE_MERGE = (2, 3)
+
+    def __init__(self, w, device="cuda"):
+        import numpy as np
+        import torch
+
+        import fp8_quantized_kv_amd as kvq
+        import workloads as wl
+        self.w, self.kvq = w, kvq
+        T, C = w.seq_len, w.chunk_rows
+        P = T - C
+        self.T, self.P, self.C = T, P, C
+        lay = wl.page_layout(w, [T])
+        c = kvq.Q4Cache(lay.num_pages, w.n_kv_heads, w.head_dim, w.page_size, device)
+        self.cache = c
+        slots = wl.slots_for(lay.page_table[0], np.arange(T), w.page_size).to(device)
+        for t0 in range(0, T, 32768):
+            k, v = wl.q4_kv_tokens(w, 0, t0, min(32768, T - t0), device)
+            kvq.kvq_store(c, k, v, slots[t0:t0 + k.shape[0]])
+            if t0 + k.shape[0] == T:
+                self.k_chunk, self.v_chunk = k[-C:].contiguous(), v[-C:].contiguous()
+        self.slot_chunk = slots[P:].contiguous()
+        self.q = wl.q4_chunk_queries(w, 0, C, device)
+        self.page_row = lay.page_table[0].to(device).contiguous()
+        self.row_lens = torch.arange(P + 1, T + 1, dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        acc_shape, mz_shape = kvq.partial_shapes(c, C, w.n_q_heads, T, w.split_keys)
+        self.q_rot = torch.empty_like(self.q)
+        self.pa, self.pm, self.pz = torch.empty(acc_shape, **f32), torch.empty(mz_shape, **f32), torch.empty(mz_shape, **f32)
+        self.out = torch.empty((C, w.n_q_heads, w.head_dim), **f32)
+        self.lse = torch.empty((C, w.n_q_heads), **f32)
+        # one checked pass through the binding
+        kvq.kvq_store(c, self.k_chunk, self.v_chunk, self.slot_chunk)
+        kvq.kvq_rotate_q(self.q, out=self.q_rot)
+        kvq.kvq_prefill_attn(c, self.q_rot, self.page_row, self.row_lens, T, w.sm_scale, w.split_keys,
+                             self.pa, self.pm, self.pz)
+        kvq.kvq_merge(c, self.pa, self.pm, self.pz, self.row_lens, T, w.split_keys, out=self.out, lse=self.lse)
+        torch.cuda.synchronize()
+        P_ = ctypes.c_void_p
+        stream = P_(torch.cuda.current_stream().cuda_stream)
+        d = ctypes.byref(c.desc)
+        Hq, D = w.n_q_heads, w.head_dim
+        self.raw = [[
+            ("kvq_store", (d, P_(self.k_chunk.data_ptr()), P_(self.v_chunk.data_ptr()), kvq._DTYPES[self.k_chunk.dtype],
+                           P_(self.slot_chunk.data_ptr()), C, stream)),
+            ("kvq_rotate_q", (P_(self.q.data_ptr()), 0, P_(self.q_rot.data_ptr()), C * Hq, D, stream)),
+            ("kvq_prefill_attn", (d, P_(self.q_rot.data_ptr()), Hq, P_(self.page_row.data_ptr()),
+                                  self.page_row.shape[0], P_(self.row_lens.data_ptr()), C, T,
+                                  ctypes.c_float(w.sm_scale), w.split_keys, P_(self.pa.data_ptr()),
+                                  P_(self.pm.data_ptr()), P_(self.pz.data_ptr()), stream)),
+            ("kvq_merge", (d, P_(self.pa.data_ptr()), P_(self.pm.data_ptr()), P_(self.pz.data_ptr()),
+                           P_(self.row_lens.data_ptr()), C, Hq, T, w.split_keys, 1, P_(self.out.data_ptr()),
+                           P_(self.lse.data_ptr()), stream)),
+        ]]
+
+    @property
+    def kv_bytes_per_layer(self):
+        w = self.w
+        return self.T * w.n_kv_heads * 2 * w.row_bytes
+
+    @property
+    def flops_per_layer(self):
+        """Scores and context of every (row, head, attended key): 2 x 2 x D flop each."""
+        w = self.w
+        keys = self.C * self.P + self.C * (self.C + 1) // 2
+        return 4 * w.n_q_heads * w.head_dim * keys
+
+
 def capture(b, only=None):
     """The step (or the calls `only`) captured as one HIP graph on a side
     stream, after one eager run of it on that stream."""
@@ -755,8 +831,8 @@ def main():
     if not args.no_extras:
         extras = {}
         for name, cls in (("gqa_q4_32k", Q4Bench), ("gqa_q8_32k", Q4Bench), ("gqa_q6_32k", Q4Bench),
-                          ("ragged_q4_b16", RaggedBench), ("mla_fp8_262k", MlaBench), ("mla_tq4_262k", TqBench),
-                          ("mla_tq4_32k", TqBench)):
+                          ("ragged_q4_b16", RaggedBench), ("chunk_q4_32k", ChunkBench), ("mla_fp8_262k", MlaBench),
+                          ("mla_tq4_262k", TqBench), ("mla_tq4_32k", TqBench)):
             wx = wl.WORKLOADS[name]
             _log(f"bench: side measurement {name}")
             bx = cls(wx)
@@ -772,6 +848,13 @@ def main():
                  "decode_frac_hbm": round(mx["decode_gbs"] / HBM_PEAK_GBS, 4)}
             if "decode_tflops" in mx:
                 e["decode_tflops"] = round(mx["decode_tflops"], 2)
+            if cls is ChunkBench:
+                # the chunk's attention is a dense contraction: its roofline is the f16 matrix-core peak
+                e["chunk_rows"] = wx.chunk_rows
+                e["attended_keys"] = int(bx.flops_per_layer // (4 * wx.n_q_heads * wx.head_dim))
+                e["roofline"] = {"kernel": "kvq_prefill_attn", "bound": "mfma", "achieved": round(mx["decode_tflops"], 2),
+                                 "peak": 2500.0, "unit": "TFLOP/s",
+                                 "frac": round(mx["decode_tflops"] / 2500.0, 4)}
             if "chunk_store_us" in mx:
                 e["chunk_store_us"] = round(mx["chunk_store_us"], 3)
                 # 2048 tokens x 4 KV heads x (K, V): bf16 rows in, 144-byte rows out

@@ -40,7 +40,7 @@ _DTYPES = {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float16: DT_F16
 EXPORTED = ("kvq_status_string", "kvq_row_bytes", "kvq_pool_bytes", "kvq_num_splits", "kvq_store",
             "kvq_rotate_q", "kvq_store_rotate_q", "kvq_decode_attn", "kvq_decode_attn_rows", "kvq_decode_attn_sel", "kvq_merge",
             "kvq_tq_rotate_q", "kvq_stream_read", "kvq_attend_workspace_bytes", "kvq_attend",
-            "kvq_attend_noalloc")
+            "kvq_attend_noalloc", "kvq_prefill_attn")
 
 
 class KvqCacheDesc(ctypes.Structure):
@@ -74,6 +74,7 @@ def _load():
         "kvq_attend_workspace_bytes": ([C, I32, I32, I32, I32], ctypes.c_size_t),
         "kvq_attend": ([C, P, I32, P, I32, P, I32, I32, F, I32, P, ctypes.c_size_t, P, P, P], I32),
         "kvq_attend_noalloc": ([C, P, I32, P, I32, P, I32, I32, F, I32, P, P, P], I32),
+        "kvq_prefill_attn": ([C, P, I32, P, I32, P, I32, I32, F, I32, P, P, P, P], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -348,6 +349,33 @@ def kvq_decode_attn_rows(cache, q, page_table, seq_lens, max_seq_len, sm_scale, 
     _check(lib.kvq_decode_attn_rows(ctypes.byref(cache.desc), qp, Hq, ptp, int(page_table.shape[0]), slp, R,
                                     int(max_seq_len), float(sm_scale), int(split_keys), pa, pm, pz, _stream(q)),
            "kvq_decode_attn_rows")
+    return part_acc, part_m, part_z
+
+
+def kvq_prefill_attn(cache, q, page_table, row_lens, max_seq_len, sm_scale, split_keys, part_acc=None, part_m=None,
+                     part_z=None):
+    """Attention of a prompt chunk's rows over their sequence's 4-bit cache, as partials: row r
+    attends positions [0, row_lens[r]) of the sequence with page-table row `page_table`.
+
+    q: f32 [R][H_q][head_dim] rotated with kvq_rotate_q; page_table: int32 [max_pages];
+    row_lens: int32 [R].  Merge with kvq_merge(cache, ..., row_lens, max_seq_len, split_keys)."""
+    R, Hq, D = q.shape
+    acc_shape, mz_shape = partial_shapes(cache, R, Hq, max_seq_len, split_keys)
+    if part_acc is None:
+        part_acc = torch.empty(acc_shape, dtype=torch.float32, device=q.device)
+        part_m = torch.empty(mz_shape, dtype=torch.float32, device=q.device)
+        part_z = torch.empty(mz_shape, dtype=torch.float32, device=q.device)
+    qp = _dev(q, "q", dtype=torch.float32, shape=(R, Hq, cache.head_dim))
+    if page_table.dim() != 1:
+        raise ValueError("page_table must be one row [max_pages]")
+    ptp = _dev(page_table, "page_table", dtype=torch.int32)
+    rlp = _dev(row_lens, "row_lens", dtype=torch.int32, shape=(R,))
+    pa = _dev(part_acc, "part_acc", dtype=torch.float32, shape=acc_shape)
+    pm = _dev(part_m, "part_m", dtype=torch.float32, shape=mz_shape)
+    pz = _dev(part_z, "part_z", dtype=torch.float32, shape=mz_shape)
+    _check(lib.kvq_prefill_attn(ctypes.byref(cache.desc), qp, Hq, ptp, int(page_table.shape[0]), rlp, R,
+                                int(max_seq_len), float(sm_scale), int(split_keys), pa, pm, pz, _stream(q)),
+           "kvq_prefill_attn")
     return part_acc, part_m, part_z
 
 

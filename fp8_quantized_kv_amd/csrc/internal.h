@@ -226,6 +226,13 @@ hipError_t launch_decode_q4_pair(const Q4Pool& pool, const DecodeArgs& a, hipStr
 bool decode_fp8_mfma_supported(const Fp8Pool& pool, const DecodeArgs& a);
 hipError_t launch_decode_fp8_mfma(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s);
 
+// Matrix-core kernel for several query rows of one sequence (a prompt chunk):
+// a.batch rows with lengths a.seq_lens over the one page-table row
+// a.page_table; head_dim 128/256, groups of up to 8 query heads, pages of a
+// multiple of 16 tokens, split_keys a multiple of 32.
+bool decode_q4_chunk_supported(const Q4Pool& pool, const DecodeArgs& a);
+hipError_t launch_decode_q4_chunk(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s);
+
 // Plain fp32 vector-math kernels (any supported head_dim).
 hipError_t launch_decode_q4_simple(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_fp8_simple(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s);

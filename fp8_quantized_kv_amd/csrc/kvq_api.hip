@@ -346,6 +346,27 @@ kvq_status kvq_decode_attn_rows(const kvq_cache* cache, const float* q, int32_t 
     return KVQ_ERR_UNSUPPORTED;
 }
 
+kvq_status kvq_prefill_attn(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
+                            int32_t max_pages, const int32_t* row_lens, int32_t n_rows, int32_t max_seq_len,
+                            float sm_scale, int32_t split_keys, float* part_acc, float* part_m, float* part_z,
+                            hipStream_t stream) {
+    kvq_status st = check_cache(cache);
+    if (st != KVQ_OK) return st;
+    if (cache->format != KVQ_FMT_Q4_H32) return KVQ_ERR_UNSUPPORTED;
+    st = check_seq_args(cache, n_q_heads, row_lens, n_rows, max_seq_len, split_keys, 32);
+    if (st != KVQ_OK) return st;
+    if (max_pages < 1 || int64_t(max_seq_len) > int64_t(max_pages) * cache->page_size) return KVQ_ERR_INVALID_ARG;
+    if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return KVQ_ERR_INVALID_ARG;
+    if (n_rows == 0) return KVQ_OK;
+    if (!aligned(q) || !aligned(page_table, 4) || !aligned(part_acc) || !aligned(part_m, 4) || !aligned(part_z, 4))
+        return KVQ_ERR_INVALID_ARG;
+    const kvq::DecodeArgs a{q, n_q_heads, page_table, max_pages, row_lens, n_rows, max_seq_len,
+                            kvq_num_splits(max_seq_len, split_keys), sm_scale, split_keys, part_acc, part_m, part_z};
+    const kvq::Q4Pool pool = q4_pool(cache);
+    if (!kvq::decode_q4_chunk_supported(pool, a)) return KVQ_ERR_UNSUPPORTED;
+    return launched(kvq::launch_decode_q4_chunk(pool, a, stream));
+}
+
 kvq_status kvq_decode_attn_sel(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
                                int32_t max_pages, const int32_t* sel, const int32_t* n_sel, int32_t batch,
                                int32_t max_sel, float sm_scale, int32_t split_keys, float* part_acc, float* part_m,

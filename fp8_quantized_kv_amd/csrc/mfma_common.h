@@ -109,6 +109,18 @@ __device__ __forceinline__ int v_exponent_for(uint32_t x, int a_old) {
 // 2^e for an integer e in [-126, 127], exactly.
 __device__ __forceinline__ float pow2i(int e) { return __uint_as_float(uint32_t(e + 127) << 23); }
 
+// The context weights of two keys, each p times its key's f16 V scale, as
+// one f16 pair: p0 * lo(s2), p1 * hi(s2), each formed in fp32 from the fp32 p
+// (exact but for the fp32 rounding, 2^-24) and rounded to f16 once, rather
+// than rounding p to f16 first and the f16 product again (the decode kernels'
+// cheaper form, whose error averages out over a decode's many keys but not
+// over the few keys of a prompt chunk's first rows).  Plain code, so the
+// compiler sees every operand (it picks the instructions and their waits).
+__device__ __forceinline__ half2_t ctx_weights(float p0, float p1, uint32_t s2) {
+    const half2_t s = __builtin_bit_cast(half2_t, s2);
+    return half2_t{_Float16(p0 * float(s[0])), _Float16(p1 * float(s[1]))};
+}
+
 __device__ __forceinline__ f32x4 mfma(half8_t a, half8_t b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

@@ -265,6 +265,30 @@ kvq_status kvq_decode_attn_rows(const kvq_cache* cache, const float* q, int32_t 
                                 float sm_scale, int32_t split_keys, float* part_acc, float* part_m, float* part_z,
                                 hipStream_t stream);
 
+/* Attention of a prompt chunk's query rows over their sequence's 4-bit cache
+ * (TensorFold "What it is": prompt chunks are packed into the 4-bit cache --
+ * kvq_store -- and then attended over the decoded slots, in rotated space),
+ * split into the decode's partials: row r attends positions [0, row_lens[r])
+ * of the sequence whose page-table row is page_table[0 .. max_pages); for a
+ * chunk of n_rows rows starting at position P (stored before the call),
+ * row_lens[r] = P + r + 1 (causal within the chunk).  q: [n_rows][n_q_heads]
+ * [head_dim] f32, rotated (kvq_rotate_q); row_lens: device int32 [n_rows],
+ * each in [0, max_seq_len]; split_keys: a positive multiple of 32 (long
+ * splits write fewer partials; short ones give a short context more
+ * workgroups); the partials [n_rows][n_q_heads][S][head_dim] and
+ * [n_rows][n_q_heads][S] (S = kvq_num_splits(max_seq_len, split_keys)) are
+ * those of kvq_decode_attn with batch = n_rows, and kvq_merge(cache, ...,
+ * row_lens, n_rows, n_q_heads, max_seq_len, split_keys, 1, out, lse)
+ * completes the attention.  Eight rows share every staged key tile, so the
+ * work is bound by the matrix cores, not by HBM (kvq_decode_attn_rows serves
+ * a few drafted rows with the decode kernels' arithmetic instead).
+ * KVQ_FMT_Q4_H32 caches, head_dim 128 or 256, groups of up to 8 query heads,
+ * page_size a multiple of 16, n_rows <= 65535; KVQ_ERR_UNSUPPORTED otherwise. */
+kvq_status kvq_prefill_attn(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
+                            int32_t max_pages, const int32_t* row_lens, int32_t n_rows, int32_t max_seq_len,
+                            float sm_scale, int32_t split_keys, float* part_acc, float* part_m, float* part_z,
+                            hipStream_t stream);
+
 /* Split decode attention over SELECTED rows of an FP8 latent cache (colibri
  * split-T commit, DSA gather: attend the selected rows, given as absolute
  * positions; a list of 1024 or more entries is split into partials and

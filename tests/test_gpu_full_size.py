@@ -145,3 +145,33 @@ def test_tq4_full_sampled_heads(kvq):
     _say(f"  max_rel_err={err.max():.2e}")
     assert err.max() < TOL
     assert np.max(np.abs(lse[:, heads] - rl)) < 1e-3 * max(1.0, np.abs(rl).max())
+
+
+def test_prefill_chunk_full(kvq):
+    """A 2048-row prompt chunk after the 32K context, in the benchmark's launch
+    (one split over the 34816 positions): codes in full, attention of 24
+    sampled rows (the first and last of row groups, the chunk's ends) on all
+    24 heads against the oracle."""
+    w = wl.WORKLOADS["chunk_q4_32k"]
+    T, C = w.seq_len, w.chunk_rows
+    P = T - C
+    _say(f"full chunk: P={P} C={C} split={w.split_keys}")
+    case = Q4Case(w, [T])
+    torch.cuda.synchronize()
+    assert np.array_equal(case.cache.k_pool.cpu().numpy(), case.k_ref)
+    assert np.array_equal(case.cache.v_pool.cpu().numpy(), case.v_ref)
+    q = wl.q4_chunk_queries(w, 0, C, "cuda")
+    lens = torch.arange(P + 1, T + 1, dtype=torch.int32, device="cuda")
+    q_rot = kvq.kvq_rotate_q(q)
+    pa, pm, pz = kvq.kvq_prefill_attn(case.cache, q_rot, case.page_table[0].contiguous(), lens, T, w.sm_scale,
+                                      w.split_keys)
+    o, lse = kvq.kvq_merge(case.cache, pa, pm, pz, lens, T, w.split_keys)
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set([0, 1, 7, 8, 9, 255, 256, 1023, 1024, 1535, 2040, 2046, 2047] +
+                               list(np.random.default_rng(17).integers(0, C, 11)))))
+    ro, rl = oracle.q4_chunk_attention(case.k_ref, case.v_ref, q.cpu().numpy()[rows],
+                                       case.lay.page_table[0].numpy(), lens.cpu().numpy()[rows], w.sm_scale)
+    err = rel_err(o.cpu().numpy()[rows], ro)
+    _say(f"  rows={len(rows)} max_rel_err={err.max():.2e}")
+    assert err.max() < TOL
+    assert np.max(np.abs(lse.cpu().numpy()[rows] - rl)) < 1e-3 * max(1.0, np.abs(rl).max())

@@ -52,6 +52,7 @@ class Q4Workload:
     prefill_chunk: int = 0           # extra tokens stored per step (not attended)
     split_keys: int = 2048
     bits: int = 4                    # code width of the block format (4, 6 or 8)
+    chunk_rows: int = 0              # a prompt chunk: the last chunk_rows positions, each a query row
 
     @property
     def row_bytes(self):
@@ -106,8 +107,14 @@ GQA_32K_Q6 = replace(GQA_32K, name="gqa_q6_32k", bits=6)
 MLA_TQ4_32K = replace(MLA_262K, name="mla_tq4_32k", seq_len=32768, split_keys=256)
 MLA_TQ4_262K = replace(MLA_262K, name="mla_tq4_262k")
 
+# A 2048-row prompt chunk after the 32K context (one layer): the chunk's rows are
+# positions 32768 .. 34815, stored first, and row r attends [0, 32768 + r];
+# one split covers the whole context (34816 = 1088 tiles of 32 keys).
+CHUNK_32K = replace(GQA_32K, name="chunk_q4_32k", n_layers=1, seq_len=32768 + 2048, chunk_rows=2048,
+                    split_keys=32768 + 2048)
+
 WORKLOADS = {w.name: w for w in (TINY, GQA_32K, GQA_262K, RAGGED, MLA_262K, GQA_32K_Q8, GQA_32K_Q6, MLA_TQ4_32K,
-                                              MLA_TQ4_262K)}
+                                              MLA_TQ4_262K, CHUNK_32K)}
 
 
 def shrink(w, **kw):
@@ -234,6 +241,13 @@ def plant(w, k_tokens, q, token_offset, b=0):
     for gkv in range(w.n_kv_heads):
         k_tokens[j, gkv] = q[b, gkv * w.group].to(k_tokens.dtype)
     return True
+
+
+def q4_chunk_queries(w, layer, n_rows, device="cpu", seed_key=0):
+    """Queries of a prompt chunk's rows: [n_rows][H_q][D] f32 ~ N(0,1), as the
+    decode query (the chunk's rows are ordinary positions of the sequence)."""
+    g = _gen(device, w.seed, 505, layer, seed_key)
+    return torch.randn((n_rows, w.n_q_heads, w.head_dim), generator=g, device=device, dtype=torch.float32)
 
 
 def q4_prefill_chunk(w, layer, device="cpu"):
