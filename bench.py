@@ -759,6 +759,153 @@ def cpu_baseline(w, sample_tokens, min_seconds=10.0, max_repeats=60):
             "seconds": round(dt, 3)}
 
 
+def _median_timing(fn, min_seconds, max_repeats=50):
+    """Median wall time (s) of fn() repeated until about min_seconds have run."""
+    times = []
+    while len(times) < max_repeats and (len(times) < 3 or sum(times) < min_seconds):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return sorted(times)[len(times) // 2], len(times)
+
+
+def cpu_per_config(min_seconds=1.0):
+    """The oracle timed on a bounded sample of each workload configuration
+    (decode attention + merge in fp64, KV bytes read per second), and its
+    store (rotate + quantise + pack in fp32) in cache rows per second, a row
+    being one (token, KV head) K or V vector."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+    out = {}
+
+    def q4_pools(w, lens):
+        lay = wl.page_layout(w, lens)
+        shape = oracle.q4_pool_shape(lay.num_pages, w.n_kv_heads, w.page_size, w.head_dim, w.bits)
+        kp, vp = np.zeros(shape, np.uint8), np.zeros(shape, np.uint8)
+        off = 0
+        for b, T in enumerate(lens):
+            for t0 in range(0, T, 32768):
+                n = min(32768, T - t0)
+                k, v = wl.q4_kv_tokens(w, 0, off + t0, n)
+                slots = wl.slots_for(lay.page_table[b], np.arange(t0, t0 + n), w.page_size).numpy()
+                oracle.q4_store(kp, vp, k.float().numpy(), v.float().numpy(), slots, w.page_size)
+            off += T
+        return lay, kp, vp
+
+    # 4-bit dense configurations: tiny (whole), 32K (whole), ragged (first two sequences)
+    for name, lens in (("tiny_q4_d128_t1024", None), ("gqa_q4_32k", None), ("gqa_q8_32k", None), ("gqa_q6_32k", None),
+                       ("ragged_q4_b16", "first2")):
+        w = wl.WORKLOADS[name]
+        if lens is None:
+            lens = [w.seq_len] * w.batch
+            sample = f"all {sum(lens)} positions"
+        else:
+            lens = [int(x) for x in wl.seq_lens(w)[:2]]
+            sample = f"sequences 0-1 of the batch ({lens[0]} and {lens[1]} positions)"
+        lay, kp, vp = q4_pools(w, lens)
+        q = wl.q4_query(wl.shrink(w, batch=len(lens)), 0).numpy()
+        sl = np.array(lens, np.int32)
+        dt, n = _median_timing(lambda: oracle.q4_attention(kp, vp, q, lay.page_table.numpy(), sl, w.sm_scale),
+                               min_seconds)
+        kvb = sum(lens) * w.n_kv_heads * 2 * w.row_bytes
+        out[name] = {"value": round(kvb / dt / 1e9, 4), "unit": "GB/s", "seconds": round(dt, 4), "runs": n,
+                     "sample": sample + f", all {w.n_q_heads} query heads"}
+    # fp8 latent: the first 4096 positions of the 262K context, all 128 heads
+    w = wl.MLA_262K
+    T = 4096
+    lay = wl.page_layout(wl.shrink(w, seq_len=T), [T])
+    n_slots = lay.num_pages * w.page_size
+    codes, scales = np.zeros((n_slots, w.head_dim), np.uint8), np.zeros((n_slots, 2), np.float32)
+    x = wl.mla_rows(w, 0, 0, T).numpy()
+    slots = wl.slots_for(lay.page_table[0], np.arange(T), w.page_size).numpy()
+    oracle.fp8_store(codes, scales, x, slots, w.rope_dim)
+    q = wl.mla_query(w, 0).numpy()
+    dt, n = _median_timing(lambda: oracle.mla_attention(codes, scales, q, lay.page_table.numpy(),
+                                                         np.array([T], np.int32), w.sm_scale, w.rope_dim,
+                                                         w.page_size), min_seconds)
+    out["mla_fp8_262k"] = {"value": round(T * MlaBench.ROW_BYTES / dt / 1e9, 4), "unit": "GB/s", "seconds": round(dt, 4),
+                           "runs": n, "sample": f"first {T} of {w.seq_len} positions, all {w.n_heads} heads"}
+    # stores, rows per second: 4096 tokens of the 4-bit shape (4 KV heads, K and V) and of the latent
+    w = wl.GQA_262K
+    n_tok = 4096
+    lay = wl.page_layout(wl.shrink(w, seq_len=n_tok), [n_tok])
+    shape = oracle.q4_pool_shape(lay.num_pages, w.n_kv_heads, w.page_size, w.head_dim)
+    kp, vp = np.zeros(shape, np.uint8), np.zeros(shape, np.uint8)
+    k, v = wl.q4_kv_tokens(w, 0, 0, n_tok)
+    k, v = k.float().numpy(), v.float().numpy()
+    sl = np.arange(n_tok)
+    dt, n = _median_timing(lambda: oracle.q4_store(kp, vp, k, v, sl, w.page_size), min_seconds)
+    rows = n_tok * w.n_kv_heads * 2
+    out["store_q4"] = {"value": round(rows / dt, 1), "unit": "rows/s", "seconds": round(dt, 4), "runs": n,
+                       "sample": f"{n_tok} tokens x {w.n_kv_heads} KV heads x (K, V), head_dim {w.head_dim}"}
+    w = wl.MLA_262K
+    x = wl.mla_rows(w, 0, 0, n_tok).numpy()
+    codes, scales = np.zeros((n_tok, w.head_dim), np.uint8), np.zeros((n_tok, 2), np.float32)
+    dt, n = _median_timing(lambda: oracle.fp8_store(codes, scales, x, sl, w.rope_dim), min_seconds)
+    out["store_fp8"] = {"value": round(n_tok / dt, 1), "unit": "rows/s", "seconds": round(dt, 4), "runs": n,
+                        "sample": f"{n_tok} latent rows of {w.kv_lora} + {w.rope_dim}"}
+    return out
+
+
+def gpu_store_rates(steps=20):
+    """kvq_store throughput on the GPU in cache rows per second (a row = one
+    (token, KV head) K or V vector, or one latent row), for a 32768-token
+    chunk of the 4-bit shape and of the fp8 latent, event-timed over `steps`
+    back-to-back calls."""
+    import numpy as np
+    import torch
+
+    import fp8_quantized_kv_amd as kvq
+    import workloads as wl
+    out = {}
+    n_tok = 32768
+    w = wl.GQA_262K
+    lay = wl.page_layout(wl.shrink(w, seq_len=n_tok), [n_tok])
+    c = kvq.Q4Cache(lay.num_pages, w.n_kv_heads, w.head_dim, w.page_size, "cuda")
+    k, v = wl.q4_kv_tokens(w, 0, 0, n_tok, "cuda")
+    slots = wl.slots_for(lay.page_table[0], np.arange(n_tok), w.page_size).cuda()
+    wm = wl.MLA_262K
+    cl = kvq.Fp8Cache(lay.num_pages, wm.head_dim, wm.rope_dim, wm.page_size, "cuda")
+    x = wl.mla_rows(wm, 0, 0, n_tok, "cuda")
+    for name, fn, rows, what in (
+            ("store_q4", lambda: kvq.kvq_store(c, k, v, slots), n_tok * w.n_kv_heads * 2,
+             f"{n_tok} tokens x {w.n_kv_heads} KV heads x (K, V), {str(k.dtype).split('.')[-1]} rows of {w.head_dim}"),
+            ("store_fp8", lambda: kvq.kvq_store(cl, x, None, slots), n_tok,
+             f"{n_tok} latent rows of {wm.kv_lora} + {wm.rope_dim}, {str(x.dtype).split('.')[-1]}")):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        out[name] = {"value": round(rows / (us * 1e-6), 1), "unit": "rows/s", "us_per_call": round(us, 3),
+                     "sample": what}
+    del c, cl
+    torch.cuda.empty_cache()
+    return out
+
+
+def profile_run(name, steps, warmup):
+    """One workload's step, `warmup` + `steps` times with nothing else in the
+    process: the command the rocprofv3 summaries under profiles/ run."""
+    import torch
+
+    import workloads as wl
+    w = wl.WORKLOADS[name]
+    cls = {"ragged_q4_b16": RaggedBench, "chunk_q4_32k": ChunkBench, "mla_fp8_262k": MlaBench,
+           "mla_tq4_262k": TqBench, "mla_tq4_32k": TqBench}.get(name, Q4Bench)
+    torch.cuda.set_device(0)
+    b = cls(w)
+    ms, _ = time_steps(b, steps, warmup)
+    print(json.dumps({"profile": name, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+                      "us_per_layer": round(ms * 1e3 / w.n_layers, 3)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -768,11 +915,16 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=262144)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the 32K and fp8-latent side measurements")
+    ap.add_argument("--profile-workload", metavar="NAME",
+                    help="only run NAME's step (--warmup + --steps times) and print its time: for profilers")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the decode path is "
               "built and measured for a single GPU's share of the work", file=sys.stderr)
         sys.exit(2)
+    if args.profile_workload:
+        profile_run(args.profile_workload, args.steps, args.warmup)
+        return
 
     import torch
 
@@ -805,7 +957,7 @@ def main():
     rec = {
         "metric": METRIC, "value": round(m["step_gbs"], 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(m["ms_per_step"], 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16 MFMA operands, f32 accumulate", "data": "synthetic",
         "config": {"workload": w.name, "layers": w.n_layers, "batch": w.batch, "seq_len": w.seq_len,
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "split_keys": w.split_keys, "kv_bytes_per_layer": kvb},
@@ -884,9 +1036,13 @@ def main():
             del bx
             torch.cuda.empty_cache()
         rec["extras"] = extras
+    if not args.no_extras:
+        _log("bench: kvq_store throughput (rows/s)")
+        rec["store"] = gpu_store_rates()
     if not args.no_cpu_baseline:
-        _log(f"bench: oracle CPU baseline on {args.cpu_sample_tokens} positions")
+        _log(f"bench: oracle CPU baseline on {args.cpu_sample_tokens} positions, then per configuration")
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+        rec["cpu_baseline"]["per_config"] = cpu_per_config()
     print(json.dumps(rec), flush=True)
 
 

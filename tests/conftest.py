@@ -18,3 +18,18 @@ def oracle_lib():
     import oracle
     oracle.lib()
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter):
+    """The largest attention error (relative to the reference's largest
+    value) of each test that compared attention outputs, worst first."""
+    helpers = sys.modules.get("helpers")
+    margins = getattr(helpers, "MARGINS", None)
+    if not margins:
+        return
+    worst = {}
+    for test, e in margins:
+        worst[test] = max(worst.get(test, 0.0), e)
+    terminalreporter.write_sep("-", f"attention parity: largest relative error per test (bar {helpers.TOL:.0e})")
+    for test, e in sorted(worst.items(), key=lambda kv: -kv[1]):
+        terminalreporter.write_line(f"{e:.2e}  {e / helpers.TOL:5.1%} of the bar  {test}")

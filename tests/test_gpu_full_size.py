@@ -1,8 +1,9 @@
 """GPU parity at the workloads' full sizes (4-bit at 32K and 262K, the 8- and
 6-bit formats at 32K), in the launch configuration the
 benchmark times (each workload's split_keys).  Codes are compared in full;
-attention is compared for every head (4-bit) or a sample of heads (fp8
-latent, whose fp64 oracle is slow at 262K positions)."""
+attention is compared for every head (4-bit) or for one head of each 16-head
+slot of the latent kernels (fp8 and rotated-int4 latents, whose fp64 oracle
+is slow at 262K positions)."""
 import numpy as np
 import pytest
 import torch
@@ -23,6 +24,13 @@ def kvq():
 
 def _say(*a):
     print(*a, flush=True)
+
+
+# One head from each of the latent decode's eight 16-head slots (a workgroup
+# takes 64 heads, each of its four wave pairs 16), each at a different
+# position within its slot, so every (head block, wave pair) combination of
+# the full-size launch is compared; the fp64 oracle costs ~a second a head.
+SLOT_HEADS = [0, 17, 34, 51, 68, 85, 102, 127]
 
 
 @pytest.mark.parametrize("name", ["gqa_q4_32k", "gqa_q4_262k", "gqa_q8_32k", "gqa_q6_32k"])
@@ -92,7 +100,7 @@ def test_mla_full_sampled_heads(kvq):
     assert np.array_equal(case.cache.codes.cpu().numpy(), case.codes_ref)
     assert np.array_equal(case.cache.scales.cpu().numpy().view(np.uint32), case.scales_ref.view(np.uint32))
     o, lse = case.gpu_attention(w.split_keys)
-    heads = [0, 17, 64, 127]
+    heads = SLOT_HEADS
     ro, rl = case.ref_attention(heads=heads)
     err = rel_err(o[:, heads], ro)
     _say(f"  max_rel_err={err.max():.2e}")
@@ -139,7 +147,7 @@ def test_tq4_full_sampled_heads(kvq):
     assert np.array_equal(case.cache.codes.cpu().numpy(), case.codes_ref)
     assert np.array_equal(case.cache.scales.cpu().numpy().view(np.uint32), case.radii_ref.view(np.uint32))
     o, lse = case.gpu_attention(w.split_keys)
-    heads = [0, 17, 64, 127]
+    heads = SLOT_HEADS
     ro, rl = case.ref_attention(heads=heads)
     err = rel_err(o[:, heads], ro)
     _say(f"  max_rel_err={err.max():.2e}")
