@@ -39,8 +39,8 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); valid only for the kernel sources they were taken on
 # (keyed by the sha256 of the kernel file followed by the device-helper header it includes).
 TRAFFIC = {
-    "85e9887c41ca8f886c7139d8a56226a21dca381fd4a7dd2ac924a11ed2c9fb1d": {
-        "fetch_kib": 147697.0, "write_kib": 3264.0, "fetch_scale": 2.0, "write_scale": 1.0,
+    "f5b4c6569f1923aaeea09b8cd85809d7b3cb0fa58f0cc69adc215a292f4db9c5": {
+        "fetch_kib": 147708.0, "write_kib": 3264.0, "fetch_scale": 2.0, "write_scale": 1.0,
         "profile": "profiles/decode_q4_mfma_gqa_q4_262k.md"},
 }
 DECODE_SOURCES = (os.path.join("fp8_quantized_kv_amd", "csrc", "decode_q4_mfma.hip"),
@@ -969,7 +969,10 @@ def main():
                      "achieved": round(m["decode_gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(m["decode_gbs"] / HBM_PEAK_GBS, 4), "avg_launch_us": round(m["decode_us"], 3),
                      "avg_launch_us_event_pair_each": round(m["decode_us_bracketed"], 3),
-                     "traffic": decode_traffic()},
+                     "traffic": decode_traffic(),
+                     "traffic_source": "rocprofv3 FETCH_SIZE and WRITE_SIZE of this kernel build, calibrated by a "
+                                       "256 MiB copy (profiles/decode_q4_mfma_gqa_q4_262k.md); null when the kernel "
+                                       "sources differ from the build the counters were taken on"},
         "wall_s": round(m["wall_s"], 3),
     }
     del b

@@ -29,10 +29,15 @@ constexpr int kMergeBatch = 32;  // partial loads in flight per lane
 // sums are added in wave order, so the result depends only on the sequence's
 // own partials.  Because that order does not depend on n, every load is
 // issued before the sequence length arrives (for all S allocated splits,
-// masked afterwards): one memory round trip instead of two.
+// masked afterwards): one memory round trip instead of two.  Z = sum_s z_s
+// w_s runs over s = lane, lane + 64, ... ascending, then a butterfly; every
+// wave forms it from the z_s it loaded up front (splits past 256 are read in
+// the loop), so no barrier hands it over.
 // For the 4-bit cache the normalized rotated-domain vector is rotated back
 // with H32 (its own inverse): out[c] = sum_j H[c%32][j] * O[32*(c/32) + j],
 // H[i][j] = (-1)^popcount(i&j) / sqrt(32).
+constexpr int kMergeZPre = 4;  // z_s preloaded per lane: s = lane + 64 k, k < 4 (s < 256)
+
 __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __restrict__ part_acc,
                                                                  const float* __restrict__ part_m,
                                                                  const float* __restrict__ part_z,
@@ -42,9 +47,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __
                                                                  float* __restrict__ out, float* __restrict__ lse) {
     extern __shared__ float w[];  // [S] split weights
     __shared__ float part[kMergeWaves][kMergeCh];
-    __shared__ float o_rot[kMergeCh];
     __shared__ float red[kMergeWaves];
-    __shared__ float s_M, s_Z;
 
     const int bh = blockIdx.x, c0 = blockIdx.y * kMergeCh;
     const int b = bh / n_q_heads;
@@ -55,7 +58,8 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __
     const float* pa = part_acc + int64_t(bh) * S * dv + c0 + lane;
 
     // Loads that do not need the sequence length: this wave's first batch of
-    // partials, and (m, z) of the splits this thread forms weights for.
+    // partials, (m, z) of the split this thread forms the weight of, and the
+    // z_s of this lane's first Z terms.
     int T = seq_lens[b];
     float v[kMergeBatch];
 #pragma unroll
@@ -65,6 +69,9 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __
     }
     const float my_m = tid < S ? pm[tid] : -INFINITY;
     const float my_z = tid < S ? pz[tid] : 0.0f;
+    float zl[kMergeZPre];
+#pragma unroll
+    for (int k = 0; k < kMergeZPre; ++k) zl[k] = lane + 64 * k < S ? pz[lane + 64 * k] : 0.0f;
 
     T = T < 0 ? 0 : (T > max_seq_len ? max_seq_len : T);
     const int n = (T + split_keys - 1) / split_keys;
@@ -82,19 +89,18 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __
     for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
     if (lane == 0) red[wave] = mx;
     __syncthreads();
-    if (tid == 0) s_M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
-    const float M = s_M;
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     if (tid < n) w[tid] = my_z > 0.0f ? expf(my_m - M) : 0.0f;
     for (int s = tid + kMergeWaves * 64; s < n; s += kMergeWaves * 64) w[s] = pz[s] > 0.0f ? expf(pm[s] - M) : 0.0f;
     __syncthreads();
-    if (wave == 0) {  // Z: lane-strided partial sums in ascending order, then a fixed butterfly
-        float z = 0.0f;
-        for (int s = lane; s < n; s += 64) z += pz[s] * w[s];
+    // Z: lane-strided partial sums in ascending order, then a fixed butterfly (every wave alike)
+    float z = 0.0f;
 #pragma unroll
-        for (int m = 1; m < 64; m <<= 1) z += __shfl_xor(z, m, 64);
-        if (lane == 0) s_Z = z;
-    }
+    for (int k = 0; k < kMergeZPre; ++k)
+        if (lane + 64 * k < n) z += zl[k] * w[lane + 64 * k];
+    for (int s = lane + 64 * kMergeZPre; s < n; s += 64) z += pz[s] * w[s];
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) z += __shfl_xor(z, m, 64);
     // this wave's splits wave + 4k < n, ascending
     float acc = 0.0f;
     for (int k0 = 0; wave + kMergeWaves * k0 < n; k0 += kMergeBatch) {
@@ -113,24 +119,26 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const float* __
     }
     part[wave][lane] = acc;
     __syncthreads();
+    if (wave != 0) return;
     // Z = 0: no split holds a key (every entry of a selection absent): out = 0, lse = -inf
-    const float Zs = s_Z;
-    if (tid < kMergeCh)
-        o_rot[tid] = Zs > 0.0f ? (((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid]) / Zs : 0.0f;
-    __syncthreads();
-    if (tid < kMergeCh) {
-        if (rotate) {
-            const float* blk = o_rot + (tid & ~31);
-            const int i = tid & 31;
-            float r = 0.0f;
+    const float orot = z > 0.0f ? (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]) / z : 0.0f;
+    if (rotate) {  // within wave 0: its own LDS row, a wave barrier
+        float* o_rot = part[0];
+        __builtin_amdgcn_wave_barrier();
+        o_rot[lane] = orot;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const float* blk = o_rot + (lane & ~31);
+        const int i = lane & 31;
+        float r = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 32; ++j) r += (__popc(unsigned(i & j)) & 1) ? -blk[j] : blk[j];
-            o[c0 + tid] = r * inv_sqrt32();
-        } else {
-            o[c0 + tid] = o_rot[tid];
-        }
+        for (int j = 0; j < 32; ++j) r += (__popc(unsigned(i & j)) & 1) ? -blk[j] : blk[j];
+        o[c0 + lane] = r * inv_sqrt32();
+    } else {
+        o[c0 + lane] = orot;
     }
-    if (lse && blockIdx.y == 0 && tid == 0) lse[bh] = Zs > 0.0f ? M + logf(Zs) : -INFINITY;
+    if (lse && blockIdx.y == 0 && lane == 0) lse[bh] = z > 0.0f ? M + logf(z) : -INFINITY;
 }
 
 // Partials with at most 64 splits (short contexts, short selections, many
