@@ -22,11 +22,14 @@
 // 512 latent output channels, so a wave holds half the query and half the
 // accumulators and two waves fit on a SIMD.  Per 32-key tile:
 //  * Staging: the tile's rows (two 16-row page runs of 576 code bytes) and
-//    their scales go global -> registers -> LDS, one iteration ahead of use.
-//    On the way, codes 0x7F / 0xFF (NaN) are zeroed with byte-wise integer
+//    their scales are copied raw by LDS DMA three tiles ahead of use, into a
+//    ring of three raw stages; one iteration ahead of use every thread
+//    converts its chunks of the raw tile into one of two f16 stages.  On the
+//    way, codes 0x7F / 0xFF (NaN) are zeroed with byte-wise integer
 //    arithmetic and every code is converted to f16 by
 //    v_cvt_scalef32_pk_f16_fp8 (exact: every e4m3 value is an f16), once
-//    per workgroup: the four pairs that use a code read it converted.  Rows
+//    per workgroup: the four pairs that use a code read it converted.
+//    (Selected rows go global -> registers -> LDS, one row at a time.)  Rows
 //    are 1168 bytes apart in LDS (576 f16 + 16), with the keys permuted
 //    within each 16-row block (lds_row), so a score read and a context read
 //    each touch every bank once.
@@ -97,6 +100,27 @@ template <bool TQ> struct Rows {
     static constexpr int kChunks = kTile * kChunkRow;
     static constexpr int kPerThread = (kChunks + kThreads - 1) / kThreads;
 };
+// Rows staged by LDS DMA (dense rows): a tile's two 16-row page runs are two
+// contiguous blocks of 16 rows in the pool, copied raw into one of three raw
+// stages (run a, run b, then both runs' scale pairs) two tiles ahead of the
+// conversion.  DMA instruction j of a tile (64 lanes x 16 bytes) is issued by
+// wave j mod 8; the scale pairs of run a / b by waves 2 / 3.
+template <bool TQ> struct Raw {
+    static constexpr int kRunBytes = 16 * Rows<TQ>::kBytes;       // fp8 9216, TQ4 4608
+    static constexpr int kRunInstr = (kRunBytes / 16 + 63) / 64;   // 9, 5 (the fifth: 32 lanes)
+    static constexpr int kInstr = 2 * kRunInstr;
+    static constexpr int kScaleOff = 2 * kRunBytes;
+    static constexpr int kStage = kScaleOff + kTile * 8;
+    // DMA instructions a wave issues per tile
+    static constexpr int count(int w) { return (kInstr - w + 7) / 8 + (w == 2 || w == 3 ? 1 : 0); }
+    static constexpr int kFirst = count(0);  // waves 0..3
+    static constexpr int kLast = count(4);   // waves 4..7
+    static_assert(count(1) == kFirst && count(2) == kFirst && count(3) == kFirst && count(5) == kLast &&
+                  count(7) == kLast && kInstr <= 24, "per-wave DMA counts");
+};
+constexpr int kRawStages = 3;
+constexpr int kRawOff = kLds;
+template <bool TQ> constexpr int kLdsDense = kRawOff + kRawStages * Raw<TQ>::kStage;
 constexpr int kMaxRuns = 128;                        // 16-key runs per split (split_keys <= 2048)
 constexpr int kQG = 9;                               // score channel groups (of 32) per wave
 constexpr int kNBW = kL / 16 / 2;                    // 16 output blocks of 16 channels per wave
@@ -160,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
                                                             int num_pages, DecodeArgs a, TqMfmaTable tab) {
     using R = Rows<TQ>;
     constexpr int kRowB = R::kBytes, kChunkRow = R::kChunkRow, kChunks = R::kChunks, kPerThread = R::kPerThread;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[SEL ? kLdsSel : kLds];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SEL ? kLdsSel : kLdsDense<TQ>];
 
     const int s = blockIdx.x, hblk = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -323,7 +347,54 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
         }
     };
 
-    load_tile(0);
+    // Dense rows: DMA of tile t's raw rows into raw stage t % 3 (no registers).
+    auto issue_tile = [&](int t) {
+        using RW = Raw<TQ>;
+        const int64_t ra = run_slot(2 * t), rb = run_slot(2 * t + 1);
+        const uint32_t raw = lds_addr(smem + kRawOff + (t % kRawStages) * RW::kStage);
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            const int j = wave + 8 * m;
+            if (j < RW::kInstr) {
+                const int run = j >= RW::kRunInstr ? 1 : 0;
+                const int k = j - run * RW::kRunInstr;
+                const int chunk = 64 * k + lane;
+                if (chunk < RW::kRunBytes / 16)
+                    dma16<false>(codes + (run ? rb : ra) * kRowB, uint32_t(16 * chunk),
+                                 raw + uint32_t(run * RW::kRunBytes + 1024 * k));
+            }
+        }
+        if (wave == 2 || wave == 3) {
+            const int run = wave - 2;
+            if (lane < 8)
+                dma16<false>(reinterpret_cast<const uint8_t*>(scales + (run ? rb : ra) * 2), uint32_t(16 * lane),
+                             raw + uint32_t(RW::kScaleOff + 128 * run));
+        }
+    };
+    // Dense rows: this thread's chunks of tile t, raw stage -> registers, for store_tile.
+    auto raw_to_stg = [&](int t) {
+        using RW = Raw<TQ>;
+        const uint8_t* rw = smem + kRawOff + (t % kRawStages) * RW::kStage;
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            if (tid + kThreads * i < kChunks)
+                stg[i] = *reinterpret_cast<const u32x4*>(rw + 16 * (tid + kThreads * i));
+            else if (has_scale)
+                stg[i] = *reinterpret_cast<const u32x4*>(rw + RW::kScaleOff + 16 * (tid - 128));
+        }
+    };
+    // Own DMAs of the tile before the newest landed (the newest may be in flight).
+    auto wait_own = [&](bool newest_in_flight) {
+        if (!newest_in_flight) wait_vmcnt<0>();
+        else if (wave < 4) wait_vmcnt<Raw<TQ>::kFirst>();
+        else wait_vmcnt<Raw<TQ>::kLast>();
+    };
+
+    if constexpr (SEL) {
+        load_tile(0);
+    } else {
+        issue_tile(0);  // tiles 1 and 2 after the query is in registers (its wait covers tile 0 only)
+    }
 
     // B operands of the score MFMAs: the pre-scaled query split into f16 hi + lo.
     half8_t bq_hi[kQG], bq_lo[kQG];
@@ -343,8 +414,17 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
         }
     }
 
-    store_tile(0);
-    if (n_tiles > 1) load_tile(1);
+    if constexpr (SEL) {
+        store_tile(0);
+        if (n_tiles > 1) load_tile(1);
+    } else {
+        wait_vmcnt<0>();
+        if (n_tiles > 1) issue_tile(1);
+        if (n_tiles > 2) issue_tile(2);
+        __syncthreads();  // tile 0 staged raw
+        raw_to_stg(0);
+        store_tile(0);
+    }
     __syncthreads();
 
     f32x4 o[kNBW];
@@ -402,7 +482,8 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
             xm[0] = make_float4(part[0][0], part[0][1], part[0][2], part[0][3]);
             xm[1] = make_float4(part[1][0], part[1][1], part[1][2], part[1][3]);
         }
-        __syncthreads();
+        if (!SEL && t + 1 < n_tiles) wait_own(t + 2 < n_tiles);  // tile t + 1 raw, own part
+        __syncthreads();  // partial scores exchanged (dense rows: tile t + 1 staged raw)
         float sc[2][4];
         {
             const float4* xp = reinterpret_cast<const float4*>(xpart);
@@ -491,8 +572,16 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
         }
 
         // ---- next tile: registers -> LDS (the other stage), then the one after into registers
-        if (t + 1 < n_tiles) store_tile(t + 1);
-        if (t + 2 < n_tiles) load_tile(t + 2);
+        if constexpr (SEL) {
+            if (t + 1 < n_tiles) store_tile(t + 1);
+            if (t + 2 < n_tiles) load_tile(t + 2);
+        } else {
+            if (t + 1 < n_tiles) {
+                raw_to_stg(t + 1);
+                store_tile(t + 1);
+            }
+            if (t + 3 < n_tiles) issue_tile(t + 3);  // into the raw stage of tile t, converted before
+        }
         __syncthreads();
     }
 
