@@ -36,7 +36,9 @@
 // streams the p-th quarter of the split, and the four pairs' results are
 // combined in LDS at the end into one partial.  Per sub-tile and wave the
 // steps are those of the single-wave kernel restricted to the wave's four
-// groups: LDS DMA of the half-rows into K and V rings of two sub-tiles,
+// groups: LDS DMA of the half-rows into K and V rings of two sub-tiles
+// (the next sub-tile's K copied after the exchange, its V after the
+// context: one sub-tile ahead, see the copy schedule below),
 // score MFMAs with the codes as f16 subnormals and the +8 offset removed in
 // the accumulator input, a lazily moving running maximum, and context MFMAs
 // on ds_read_b64_tr_b4-transposed V codes.
@@ -172,13 +174,18 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
         dma16<true>(r1, src_off0, dst + 1280u);
         if (lane < 16) dma16<false>(r1, src_off1, dst + 2304u);
     };
+    // Copy schedule: one sub-tile ahead.  Sub-tile 0 is copied here; sub-tile
+    // t + 1's K after sub-tile t's exchange and its V after sub-tile t's
+    // context.  A copy instruction stalls its wave until the memory system
+    // accepts it, and at a launch's start every wave queues its copies at
+    // once: with two sub-tiles ahead each wave waited ~4 us behind its 20 KB
+    // before its first scores, though its first K had landed ~0.5 us after
+    // issue.  With one ahead the first scores start once sub-tile 0 is
+    // accepted (32768 keys at split 512: 14.1 vs 15.0 us per layer; 131072
+    // keys at split 1024: 39.0 vs 40.5 us; the same bits).
     if (n_sub > 0) {
         issue(k_pool, 0, k_ring);
         issue(v_pool, 0, v_ring);
-    }
-    if (n_sub > 1) {
-        issue(k_pool, 1, k_ring);
-        issue(v_pool, 1, v_ring);
     }
 
     // Score B operands (pre-scaled query in log2 units, hi/lo by column) and
@@ -233,11 +240,10 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
         const int valid = min(kSub, n_keys - t * kSub);
 
         // ---- partial scores over this half's four groups (K of sub-tile t has
-        // landed once at most V_t, K_t+1, V_t+1 are outstanding)
+        // landed once at most V_t is outstanding)
         float sc[2][4];
         if (act) {
-            if (t + 1 < n_sub) wait_vmcnt<3 * kHalfInstr>();
-            else wait_vmcnt<kHalfInstr>();
+            wait_vmcnt<kHalfInstr>();
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 const uint8_t* arow = kt + (16 * kb + n16) * kPitch;
@@ -288,7 +294,7 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
         }
         barrier_lds();  // the other half has read this slot: it may be refilled
         if (!act) continue;
-        if (t + 2 < n_sub) issue(k_pool, t + 2, k_ring);
+        if (t + 1 < n_sub) issue(k_pool, t + 1, k_ring);  // into the slot of sub-tile t - 1
 
         if (valid < kSub) {
             asm volatile("" ::: "memory");
@@ -299,9 +305,8 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
                     if (16 * kb + 4 * q4 + i >= valid) sc[kb][i] = -INFINITY;
         }
 
-        // V of sub-tile t has landed once at most K_t+1, V_t+1, K_t+2 are outstanding.
-        if (t + 2 < n_sub) wait_vmcnt<3 * kHalfInstr>();
-        else if (t + 1 < n_sub) wait_vmcnt<2 * kHalfInstr>();
+        // V of sub-tile t has landed once at most K_t+1 is outstanding.
+        if (t + 1 < n_sub) wait_vmcnt<kHalfInstr>();
         else wait_vmcnt<0>();
 
         if (valid < kSub) {  // rows past the end: zero their V scales
@@ -383,7 +388,7 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
             o[2 * j + 1] = mfma(av, unpack8(uint32_t(cv[1])), o[2 * j + 1]);
             o[2 * j + 1] = mfma(av, bconst, o[2 * j + 1]);
         }
-        if (t + 2 < n_sub) issue(v_pool, t + 2, v_ring);
+        if (t + 1 < n_sub) issue(v_pool, t + 1, v_ring);  // into the slot of sub-tile t - 1
     }
 
     // ---- combine the four pairs.  Each wave leaves its live head rows (its
