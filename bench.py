@@ -39,8 +39,8 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); valid only for the kernel sources they were taken on
 # (keyed by the sha256 of the kernel file followed by the device-helper header it includes).
 TRAFFIC = {
-    "f5b4c6569f1923aaeea09b8cd85809d7b3cb0fa58f0cc69adc215a292f4db9c5": {
-        "fetch_kib": 147708.0, "write_kib": 3264.0, "fetch_scale": 2.0, "write_scale": 1.0,
+    "d41e067b2914e9684b37aec3a4fbc18fbf5e6c00ed15f8691659ab5044dc297a": {
+        "fetch_kib": 147708.5, "write_kib": 3264.0, "fetch_scale": 2.0, "write_scale": 1.0,
         "profile": "profiles/decode_q4_mfma_gqa_q4_262k.md"},
 }
 DECODE_SOURCES = (os.path.join("fp8_quantized_kv_amd", "csrc", "decode_q4_mfma.hip"),

@@ -601,10 +601,10 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
             acc += wo(w)[h * D + c] * f;
             Z += zw * f;
         }
-        a.part_acc[((hb + h) * Sn + s) * D + c] = acc;
+        store_wt(&a.part_acc[((hb + h) * Sn + s) * D + c], acc);
         if (c == 0) {
-            a.part_m[(hb + h) * Sn + s] = M * kLn2;
-            a.part_z[(hb + h) * Sn + s] = Z;
+            store_wt(&a.part_m[(hb + h) * Sn + s], M * kLn2);
+            store_wt(&a.part_z[(hb + h) * Sn + s], Z);
         }
     }
 }

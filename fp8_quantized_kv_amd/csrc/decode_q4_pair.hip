@@ -429,10 +429,10 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
             acc += wo(2 * q + half)[hd * 128 + (c & 127)] * f;
             Z += zq * f;
         }
-        a.part_acc[((hb + hd) * Sn + s) * kD + c] = acc;
+        store_wt(&a.part_acc[((hb + hd) * Sn + s) * kD + c], acc);
         if (c == 0) {
-            a.part_m[(hb + hd) * Sn + s] = M * kLn2;
-            a.part_z[(hb + hd) * Sn + s] = Z;
+            store_wt(&a.part_m[(hb + hd) * Sn + s], M * kLn2);
+            store_wt(&a.part_z[(hb + hd) * Sn + s], Z);
         }
     }
 }
