@@ -40,7 +40,7 @@ _DTYPES = {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float16: DT_F16
 EXPORTED = ("kvq_status_string", "kvq_row_bytes", "kvq_pool_bytes", "kvq_num_splits", "kvq_store",
             "kvq_rotate_q", "kvq_store_rotate_q", "kvq_decode_attn", "kvq_decode_attn_rows", "kvq_decode_attn_sel", "kvq_merge",
             "kvq_tq_rotate_q", "kvq_stream_read", "kvq_attend_workspace_bytes", "kvq_attend",
-            "kvq_attend_noalloc", "kvq_prefill_attn")
+            "kvq_attend_noalloc", "kvq_prefill_attn", "kvq_decode_step")
 
 
 class KvqCacheDesc(ctypes.Structure):
@@ -75,6 +75,8 @@ def _load():
         "kvq_attend": ([C, P, I32, P, I32, P, I32, I32, F, I32, P, ctypes.c_size_t, P, P, P], I32),
         "kvq_attend_noalloc": ([C, P, I32, P, I32, P, I32, I32, F, I32, P, P, P], I32),
         "kvq_prefill_attn": ([C, P, I32, P, I32, P, I32, I32, F, I32, P, P, P, P], I32),
+        "kvq_decode_step": ([C, P, P, I32, P, I32, I32, P, I32, P, I32, I32, F, I32, P, ctypes.c_size_t, P, P, P],
+                            I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -454,6 +456,40 @@ def kvq_attend(cache, q, page_table, seq_lens, max_seq_len, sm_scale, split_keys
     lp = _dev(lse, "lse", dtype=torch.float32, shape=(B, Hq)) if lse is not None else None
     _check(lib.kvq_attend(ctypes.byref(cache.desc), qp, Hq, ptp, int(page_table.shape[1]), slp, B, int(max_seq_len),
                           float(sm_scale), int(split_keys), wp, workspace.numel(), op, lp, _stream(q)), "kvq_attend")
+    return out, lse
+
+
+def kvq_decode_step(cache, k, v, q, page_table, seq_lens, max_seq_len, sm_scale, split_keys, workspace=None,
+                    out=None, lse=None, want_lse=True):
+    """A decode step in two launches: token b's K and V rows (k, v: [batch][num_kv_heads][head_dim]) stored
+    at position seq_lens[b] - 1 of sequence b through the page table, the query q ([batch][n_q_heads]
+    [head_dim], before rotation) rotated, attention and merge.  Returns (out, lse), the same bits as
+    kvq_store_rotate_q + kvq_attend."""
+    B, Hq, D = q.shape
+    need = kvq_attend_workspace_bytes(cache, B, Hq, max_seq_len, split_keys)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, cache.dv), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    kdt, qdt = _DTYPES.get(k.dtype), _DTYPES.get(q.dtype)
+    if kdt is None or qdt is None:
+        raise ValueError(f"unsupported dtype {k.dtype if kdt is None else q.dtype}")
+    shape = (B, cache.num_kv_heads, cache.head_dim)
+    kp = _dev(k, "k", shape=shape)
+    vp = _dev(v, "v", dtype=k.dtype, shape=shape)
+    qp = _dev(q, "q", shape=(B, Hq, cache.head_dim))
+    ptp = _dev(page_table, "page_table", dtype=torch.int32)
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [batch][max_pages]")
+    slp = _dev(seq_lens, "seq_lens", dtype=torch.int32, shape=(B,))
+    wp = _dev(workspace, "workspace", dtype=torch.uint8)
+    op = _dev(out, "out", dtype=torch.float32, shape=(B, Hq, cache.dv))
+    lp = _dev(lse, "lse", dtype=torch.float32, shape=(B, Hq)) if lse is not None else None
+    _check(lib.kvq_decode_step(ctypes.byref(cache.desc), kp, vp, kdt, qp, qdt, Hq, ptp, int(page_table.shape[1]),
+                               slp, B, int(max_seq_len), float(sm_scale), int(split_keys), wp, workspace.numel(),
+                               op, lp, _stream(q)), "kvq_decode_step")
     return out, lse
 
 

@@ -131,7 +131,12 @@ __device__ __forceinline__ half8_t unpack8_b6_ctx(uint32_t nib, uint32_t h0, uin
 // same rows of codes then fp16 scales, same arithmetic with offset 128);
 // BITS = 6: the 6-bit block format (per group 16 bytes of low nibbles laid
 // out as the 4-bit codes, then 8 bytes of high two-bit fields; offset 32).
-template <int D, int W, bool PACK, int BITS>
+// STEP (kvq_decode_step): the query arrives unrotated and is rotated here,
+// and the wave whose key range holds position seq_lens[b] - 1 first stores
+// token b's K and V rows there (the store kernel's encoder, so the bytes are
+// the same), before its own copy of that row: each wave copies only its own
+// rows, so no other wave of the launch reads them.
+template <int D, int W, bool PACK, int BITS, bool STEP = false>
 __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(const uint8_t* __restrict__ k_pool,
                                                                   const uint8_t* __restrict__ v_pool, int H,
                                                                   int page_size, int num_pages, DecodeArgs a) {
@@ -192,6 +197,29 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
     const int n_keys = w1 > w0 ? w1 - w0 : 0;
     const int n_sub = (n_keys + kSub - 1) / kSub;
 
+    // STEP: store token b's K and V rows at position T - 1 if this wave's
+    // keys hold it.  Stores then a full wait, so no store is outstanding when
+    // the copies' waits count (vmcnt counts both), and the row is in the L2
+    // before this wave copies it.  A position whose page is outside the pool
+    // is not stored (kvq_store skips such a slot too).
+    const int pos_new = T - 1;
+    const bool storer = STEP && T > 0 && pos_new >= w0 && pos_new < w1;  // wave-uniform
+    auto store_token = [&]() {
+        const int page = pt[pos_new / page_size];
+        if (page >= 0 && page < num_pages) {
+            const int64_t row = (int64_t(page) * H + g) * page_size + pos_new % page_size;
+            const int64_t src = (int64_t(b) * H + g) * D + 4 * lane;
+            float x[4];
+            load4_dyn(a.step_kv_dt, a.step_k, src, x);
+            encode_blk_quad<BITS>(x, const_cast<uint8_t*>(k_pool) + row * RB, D, lane, lane);
+            load4_dyn(a.step_kv_dt, a.step_v, src, x);
+            encode_blk_quad<BITS>(x, const_cast<uint8_t*>(v_pool) + row * RB, D, lane, lane);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    // Rows of sub-tiles 0 and 1 are copied just below: store first.
+    if (storer && (pos_new - w0) / kSub <= 1) store_token();
+
     uint8_t* ring = smem + wave * S::WAVE_LDS;  // K tiles 0, 1 then V tiles 0, 1
     const uint32_t lds0 = lds_addr(ring);
     auto run_at = [&](int r) -> int64_t {  // r is wave-uniform
@@ -226,13 +254,34 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
     // hi part and columns 8..15 its lo part, so one MFMA per group does both.
     const int hcol = PACK ? (n16 & 7) : n16;  // the head this lane's B column holds
     const bool live = hcol < G;
-    const float* qh = a.q + (hb + (live ? hcol : 0)) * D;
     float4 qv[NG][2];
+    if constexpr (STEP) {  // rotated here, bit for bit as kvq_rotate_q rotates it
+        const int64_t qrow = (hb + (live ? hcol : 0)) * D;
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-        qv[gi][0] = *reinterpret_cast<const float4*>(qh + 32 * gi + 8 * q4);
-        qv[gi][1] = *reinterpret_cast<const float4*>(qh + 32 * gi + 8 * q4 + 4);
+        for (int gi = 0; gi < NG; ++gi) {
+            float y[8], x0[4], x1[4];
+            load4_dyn(a.step_q_dt, a.step_q, qrow + 32 * gi + 8 * q4, x0);
+            load4_dyn(a.step_q_dt, a.step_q, qrow + 32 * gi + 8 * q4 + 4, x1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                y[i] = x0[i];
+                y[4 + i] = x1[i];
+            }
+            rotate_q_lanes4(y, lane);
+            qv[gi][0] = make_float4(y[0], y[1], y[2], y[3]);
+            qv[gi][1] = make_float4(y[4], y[5], y[6], y[7]);
+        }
+    } else {
+        const float* qh = a.q + (hb + (live ? hcol : 0)) * D;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            qv[gi][0] = *reinterpret_cast<const float4*>(qh + 32 * gi + 8 * q4);
+            qv[gi][1] = *reinterpret_cast<const float4*>(qh + 32 * gi + 8 * q4 + 4);
+        }
     }
+    // STEP, a later sub-tile holds the new row: store it now, while the first
+    // copies land (its copy is issued two sub-tiles ahead, after this).
+    if (storer && (pos_new - w0) / kSub > 1) store_token();
 
     // B operands of the score MFMAs: pre-scaled query (log2 units) of head
     // n16 for the 8 channels that k-slots (q4, 0..7) of each group hold,
@@ -627,10 +676,21 @@ bool decode_q4_mfma_supported(const Q4Pool& pool, const DecodeArgs& a) {
 // once.  The 8- and 6-bit formats always use 4 waves: their rings take 34 and
 // 26 KB per wave.  The choice depends on split_keys and the format alone, never on the
 // batch, so a sequence's partials do not depend on the sequences beside it.
+bool decode_q4_mfma_step_supported(const Q4Pool& pool, const DecodeArgs& a) {
+    return decode_q4_mfma_supported(pool, a) && pool.bits == 4 && pool.head_dim == 256 &&
+           a.n_q_heads / pool.n_kv_heads <= 8 && a.split_keys > kEightWaveSplit && a.rows == 0;
+}
+
 hipError_t launch_decode_q4_mfma(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s) {
     const dim3 grid = decode_grid(a, pool.n_kv_heads);
     const bool eight = a.split_keys <= kEightWaveSplit;
     const bool pack = a.n_q_heads / pool.n_kv_heads <= 8;
+    if (a.step_k) {  // kvq_decode_step: one configuration (the launcher's caller checks it)
+        if (!decode_q4_mfma_step_supported(pool, a)) return hipErrorInvalidValue;
+        decode_q4_mfma<256, 4, true, 4, true><<<grid, dim3(4 * 64), 0, s>>>(pool.k, pool.v, pool.n_kv_heads,
+                                                                            pool.page_size, pool.num_pages, a);
+        return hipGetLastError();
+    }
 #define KVQ_LAUNCH(D_, W_, P_, B_)                                                                             \
     decode_q4_mfma<D_, W_, P_, B_><<<grid, dim3((W_) * 64), 0, s>>>(pool.k, pool.v, pool.n_kv_heads,          \
                                                                      pool.page_size, pool.num_pages, a)

@@ -73,6 +73,14 @@ __device__ __forceinline__ void barrier_lds() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// STEP (kvq_decode_step): the query arrives unrotated and is rotated here,
+// and wave 0 of the pair whose key range holds position seq_lens[b] - 1
+// first stores token b's K and V rows there (the store kernel's encoder, so
+// the bytes are the same).  Both waves of that pair copy the row, so the
+// store completes before either copy: before the workgroup's first barrier
+// if the row's sub-tile is copied in the prologue, else before the storing
+// wave's first exchange barrier, which precedes every later copy.
+template <bool STEP>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWaves * 64, kWaves * 64), amdgpu_waves_per_eu(4, 4)))
 void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool, int H,
                     int page_size, int num_pages, DecodeArgs a) {
@@ -97,12 +105,30 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
     // f16 hi part and 8..15 the lo part.
     const int hcol = n16 & 7;
     const bool live = hcol < G;
-    const float* qh = a.q + (hb + (live ? hcol : 0)) * kD + 128 * h;
     float4 qv[4][2];
+    if constexpr (STEP) {  // rotated here, bit for bit as kvq_rotate_q rotates it
+        const int64_t qrow = (hb + (live ? hcol : 0)) * kD + 128 * h;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        qv[j][0] = *reinterpret_cast<const float4*>(qh + 32 * j + 8 * q4);
-        qv[j][1] = *reinterpret_cast<const float4*>(qh + 32 * j + 8 * q4 + 4);
+        for (int j = 0; j < 4; ++j) {
+            float y[8], x0[4], x1[4];
+            load4_dyn(a.step_q_dt, a.step_q, qrow + 32 * j + 8 * q4, x0);
+            load4_dyn(a.step_q_dt, a.step_q, qrow + 32 * j + 8 * q4 + 4, x1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                y[i] = x0[i];
+                y[4 + i] = x1[i];
+            }
+            rotate_q_lanes4(y, lane);
+            qv[j][0] = make_float4(y[0], y[1], y[2], y[3]);
+            qv[j][1] = make_float4(y[4], y[5], y[6], y[7]);
+        }
+    } else {
+        const float* qh = a.q + (hb + (live ? hcol : 0)) * kD + 128 * h;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            qv[j][0] = *reinterpret_cast<const float4*>(qh + 32 * j + 8 * q4);
+            qv[j][1] = *reinterpret_cast<const float4*>(qh + 32 * j + 8 * q4 + 4);
+        }
     }
 
     // Pool row index of the first row of each 16-row run of the pair's
@@ -174,6 +200,32 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
         dma16<true>(r1, src_off0, dst + 1280u);
         if (lane < 16) dma16<false>(r1, src_off1, dst + 2304u);
     };
+    // STEP: the new row (position T - 1) and the wave that stores it.  The
+    // store ends with a full wait, so no store is outstanding when the
+    // copies' waits count (vmcnt counts both).  A position whose page is
+    // outside the pool is not stored (kvq_store skips such a slot too).
+    const int pos_new = T - 1;
+    const bool holds = STEP && T > 0 && pos_new >= j0 && pos_new < j1;  // workgroup-uniform
+    const bool early = holds && ((pos_new - j0) % kp) / kSub == 0;     // copied in the prologue
+    const bool storer = holds && pair == (pos_new - j0) / kp && h == 0;
+    auto store_token = [&]() {
+        const int page = pt[pos_new / page_size];
+        if (page >= 0 && page < num_pages) {
+            const int64_t row = (int64_t(page) * H + g) * page_size + pos_new % page_size;
+            const int64_t src = (int64_t(b) * H + g) * kD + 4 * lane;
+            float x[4];
+            load4_dyn(a.step_kv_dt, a.step_k, src, x);
+            encode_blk_quad<4>(x, const_cast<uint8_t*>(k_pool) + row * kRB, kD, lane, lane);
+            load4_dyn(a.step_kv_dt, a.step_v, src, x);
+            encode_blk_quad<4>(x, const_cast<uint8_t*>(v_pool) + row * kRB, kD, lane, lane);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    if (early) {  // both waves of the pair copy the row below: store, then a workgroup barrier
+        if (storer) store_token();
+        __syncthreads();
+    }
+
     // Copy schedule: one sub-tile ahead.  Sub-tile 0 is copied here; sub-tile
     // t + 1's K after sub-tile t's exchange and its V after sub-tile t's
     // context.  A copy instruction stalls its wave until the memory system
@@ -217,6 +269,9 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
     half8_t bconst;
 #pragma unroll
     for (int k = 0; k < 8; ++k) bconst[k] = _Float16((k & 2) ? -128.0f / kTwo24 : -8.0f / kTwo24);
+    // STEP, a later sub-tile holds the new row: store it now (its copies come
+    // after this wave's first exchange barrier).
+    if (storer && !early) store_token();
 
     f32x4 o[8];
 #pragma unroll
@@ -449,8 +504,12 @@ bool decode_q4_pair_supported(const Q4Pool& pool, const DecodeArgs& a) {
 
 hipError_t launch_decode_q4_pair(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s) {
     const dim3 grid = decode_grid(a, pool.n_kv_heads);
-    decode_q4_pair<<<grid, dim3(kWaves * 64), 0, s>>>(pool.k, pool.v, pool.n_kv_heads, pool.page_size, pool.num_pages,
-                                                      a);
+    if (a.step_k)
+        decode_q4_pair<true><<<grid, dim3(kWaves * 64), 0, s>>>(pool.k, pool.v, pool.n_kv_heads, pool.page_size,
+                                                                pool.num_pages, a);
+    else
+        decode_q4_pair<false><<<grid, dim3(kWaves * 64), 0, s>>>(pool.k, pool.v, pool.n_kv_heads, pool.page_size,
+                                                                 pool.num_pages, a);
     return hipGetLastError();
 }
 

@@ -121,6 +121,118 @@ __device__ __forceinline__ void rotate_q_quad(const void* q, float* q_rot, int64
     *reinterpret_cast<float4*>(q_rot + 4 * quad) = make_float4(x[0] * c, x[1] * c, x[2] * c, x[3] * c);
 }
 
+// load4 with the element type chosen at run time (uniform across the wave).
+__device__ __forceinline__ void load4_dyn(InType dt, const void* p, int64_t i, float (&x)[4]) {
+    if (dt == InType::F32) load4<InType::F32>(p, i, x);
+    else if (dt == InType::BF16) load4<InType::BF16>(p, i, x);
+    else load4<InType::F16>(p, i, x);
+}
+
+// The query rotation above for the decode kernels' lane layout: lane (n, q)
+// = n + 16 q holds elements 8q .. 8q + 7 of a 32-group (q = 0..3), i.e. the
+// quads 2q and 2q + 1 of rotate_q_quad.  The same stages in the same order
+// on the same operands: stages 1 and 2 inside each quad, stage 4 between the
+// lane's two quads, stages 8 and 16 with lane ^ 16 and lane ^ 32; every pair
+// (a, b), a the lower element, becomes (a + b, a - b); then x
+// fp32(1/sqrt(32)).  So y equals kvq_rotate_q's output bit for bit.  Every
+// lane of the four q-lanes of a group must call it.
+__device__ __forceinline__ void rotate_q_lanes4(float (&y)[8], int lane) {
+#pragma unroll
+    for (int h = 0; h < 8; h += 4) {
+        float a = y[h], b = y[h + 1];
+        y[h] = a + b;
+        y[h + 1] = a - b;
+        a = y[h + 2];
+        b = y[h + 3];
+        y[h + 2] = a + b;
+        y[h + 3] = a - b;
+        a = y[h];
+        b = y[h + 2];
+        y[h] = a + b;
+        y[h + 2] = a - b;
+        a = y[h + 1];
+        b = y[h + 3];
+        y[h + 1] = a + b;
+        y[h + 3] = a - b;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = y[i], b = y[i + 4];
+        y[i] = a + b;
+        y[i + 4] = a - b;
+    }
+#pragma unroll
+    for (int m = 16; m <= 32; m <<= 1) {
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float o = __shfl_xor(y[i], m, 64);
+            y[i] = upper ? o - y[i] : y[i] + o;
+        }
+    }
+    const float c = inv_sqrt32();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = y[i] * c;
+}
+
+// The block-format encoder of one lane's 4 consecutive values x of a row
+// (lane-in-row e: values 4e .. 4e + 3; a 32-group is 8 lanes, 8-aligned in
+// the wave): the Hadamard-32 butterfly, x fp32(1/sqrt(32)), the group's amax,
+// scale = fp16_rne(amax / divisor) and codes round-half-even(x / scale)
+// clamped to the signed BITS-bit range, written into `row` (a row of
+// blk_row_bytes(BITS, D) bytes).  Every step is one IEEE fp32 operation in a
+// fixed order (compiled without contraction, with the correctly rounded
+// divide), so the stored bytes do not depend on which kernel calls it.
+template <int BITS>
+__device__ __forceinline__ void encode_blk_quad(float (&x)[4], uint8_t* __restrict__ row, int D, int e, int lane) {
+    h32_butterfly_lanes8(x, lane);
+    const float c = inv_sqrt32();
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = x[i] * c;
+        amax = fmaxf(amax, fabsf(x[i]));
+    }
+#pragma unroll
+    for (int m = 1; m <= 4; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    // scale = fp16_rne(amax / divisor); for 4 bits amax * 0.125 is the same
+    // exactly rounded value as amax / 8.
+    const __half s16 = __float2half_rn(BITS == 4 ? amax * 0.125f : amax / (BITS == 6 ? 31.0f : 127.0f));
+    const float s = __half2float(s16);
+    constexpr float kMax = float((1 << (BITS - 1)) - 1), kMin = -float(1 << (BITS - 1));
+    int q[4] = {0, 0, 0, 0};
+    if (s != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float n = rintf(x[i] / s);  // correctly rounded divide, then half-to-even
+            n = fminf(fmaxf(n, kMin), kMax);
+            q[i] = int(n);
+        }
+    }
+    // Values 4j .. 4j+3 of group g (j = e & 7, g = e >> 3).
+    const int g = e >> 3, j = e & 7;
+    uint8_t* grp = row + g * blk_group_bytes(BITS);
+    if (BITS == 8) {
+        uint32_t w = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w |= (uint32_t(q[i]) & 0xFFu) << (8 * i);
+        reinterpret_cast<uint32_t*>(grp)[j] = w;
+    } else {
+        // value 2k in the low nibble of byte k, value 2k+1 in the high nibble
+        uint32_t nib = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nib |= (uint32_t(q[i]) & 0xFu) << (4 * i);
+        reinterpret_cast<uint16_t*>(grp)[j] = uint16_t(nib);
+        if (BITS == 6) {
+            uint32_t top = 0u;  // high two bits of value 4j + i in bits 2i .. 2i+1 of byte j
+#pragma unroll
+            for (int i = 0; i < 4; ++i) top |= ((uint32_t(q[i]) >> 4) & 3u) << (2 * i);
+            grp[16 + j] = uint8_t(top);
+        }
+    }
+    if (j == 0) reinterpret_cast<uint16_t*>(row + (D / 32) * blk_group_bytes(BITS))[g] = __half_as_ushort(s16);
+}
+
 // ------------------------------------------------------------------ launchers
 // Each returns the hipError_t of its launch; shapes are validated by the caller.
 
@@ -176,6 +288,17 @@ struct DecodeArgs {
     // batch entries are `rows` query rows of one sequence, sharing one
     // page-table row, and the grid is the row layout of decode_block.
     int rows = 0;
+    // Decode step (kvq_decode_step, 4-bit format): when step_k is set, q is
+    // unused and step_q holds the query before rotation ([batch][n_q_heads]
+    // [D], type step_q_dt), which each workgroup rotates for the heads it
+    // reads; and token b's K and V rows (step_k, step_v: [batch][H][D], type
+    // step_kv_dt) are stored at position seq_lens[b] - 1 of sequence b by the
+    // one wave whose key range holds that position, before any copy of it.
+    const void* step_k = nullptr;
+    const void* step_v = nullptr;
+    const void* step_q = nullptr;
+    InType step_kv_dt = InType::F32;
+    InType step_q_dt = InType::F32;
 };
 
 // Block coordinates (split s, KV head g, batch entry b) of this workgroup.
@@ -213,12 +336,16 @@ inline dim3 decode_grid(const DecodeArgs& a, int n_kv_heads) {
 // multiple of 16 tokens, groups of up to 16 query heads, split_keys <= 8192).
 bool decode_q4_mfma_supported(const Q4Pool& pool, const DecodeArgs& a);
 hipError_t launch_decode_q4_mfma(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s);
+// The STEP form of it (a.step_k set): head_dim 256, 4 bits, groups of up to
+// 8 query heads, splits of more than 1024 keys, no drafted rows.
+bool decode_q4_mfma_step_supported(const Q4Pool& pool, const DecodeArgs& a);
 
 // Matrix-core kernel for head_dim 256 and groups of up to 8 query heads, a
 // pair of waves sharing each key tile by channel halves (split_keys a
 // multiple of 128, at most 1024).
 bool decode_q4_pair_supported(const Q4Pool& pool, const DecodeArgs& a);
 hipError_t launch_decode_q4_pair(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s);
+// Both forms (plain and STEP) run wherever decode_q4_pair_supported holds.
 
 // Matrix-core kernel for the fp8 latent cache (512 + 64, pages of a
 // multiple of 16 tokens, split_keys <= 2048), over consecutive positions or

@@ -430,6 +430,47 @@ kvq_status kvq_attend(const kvq_cache* cache, const float* q, int32_t n_q_heads,
                      static_cast<uint8_t*>(workspace), out, lse, stream);
 }
 
+kvq_status kvq_decode_step(const kvq_cache* cache, const void* k, const void* v, int32_t kv_dtype, const void* q,
+                           int32_t q_dtype, int32_t n_q_heads, const int32_t* page_table, int32_t max_pages,
+                           const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
+                           int32_t split_keys, void* workspace, size_t workspace_bytes, float* out, float* lse,
+                           hipStream_t stream) {
+    kvq_status st = check_cache(cache);
+    if (st != KVQ_OK) return st;
+    st = check_decode_args(cache, n_q_heads, max_pages, seq_lens, batch, max_seq_len, sm_scale, split_keys);
+    if (st != KVQ_OK) return st;
+    if (!dtype_ok(kv_dtype) || !dtype_ok(q_dtype)) return KVQ_ERR_INVALID_ARG;
+    if (batch == 0) return KVQ_OK;
+    if (!aligned(k) || !aligned(v) || !aligned(q) || !aligned(page_table, 4) || !aligned(out) ||
+        (lse && !aligned(lse, 4)))
+        return KVQ_ERR_INVALID_ARG;
+    if (int64_t(batch) * n_q_heads > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
+    const int32_t S = kvq_num_splits(max_seq_len, split_keys);
+    const AttendLayout l = attend_layout(batch, n_q_heads, S, value_dim(cache));
+    if (!aligned(workspace, 256) || workspace_bytes < l.total) return KVQ_ERR_INVALID_ARG;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    float* pa = reinterpret_cast<float*>(ws + l.acc);
+    float* pm = reinterpret_cast<float*>(ws + l.m);
+    float* pz = reinterpret_cast<float*>(ws + l.z);
+    kvq::DecodeArgs d{nullptr, n_q_heads, page_table, max_pages, seq_lens, batch, max_seq_len, S, sm_scale,
+                      split_keys, pa, pm, pz};
+    d.step_k = k;
+    d.step_v = v;
+    d.step_q = q;
+    d.step_kv_dt = static_cast<InType>(kv_dtype);
+    d.step_q_dt = static_cast<InType>(q_dtype);
+    // The kernel kvq_decode_attn would run (launch_decode_for), in its STEP form.
+    if (cache->format != KVQ_FMT_Q4_H32) return KVQ_ERR_UNSUPPORTED;
+    const kvq::Q4Pool pool = q4_pool(cache);
+    if (kvq::decode_q4_pair_supported(pool, d)) st = launched(kvq::launch_decode_q4_pair(pool, d, stream));
+    else if (kvq::decode_q4_mfma_step_supported(pool, d)) st = launched(kvq::launch_decode_q4_mfma(pool, d, stream));
+    else return KVQ_ERR_UNSUPPORTED;
+    if (st != KVQ_OK) return st;
+    const kvq::MergeArgs m{pa, pm, pz, seq_lens, batch, n_q_heads, max_seq_len, S, split_keys, value_dim(cache),
+                           true, out, lse};
+    return launch_merge_for(cache, m, stream);
+}
+
 kvq_status kvq_attend_noalloc(const kvq_cache* cache, const float* q, int32_t n_q_heads, const int32_t* page_table,
                               int32_t max_pages, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
                               float sm_scale, int32_t split_keys, float* out, float* lse, hipStream_t stream) {

@@ -47,55 +47,9 @@ __device__ __forceinline__ void store_q4_quad(const void* __restrict__ k, const 
 
     float x[4];
     load4<DT>(which ? v : k, r * D + 4 * e, x);
-    h32_butterfly_lanes8(x, lane);
-    const float c = inv_sqrt32();
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x[i] = x[i] * c;
-        amax = fmaxf(amax, fabsf(x[i]));
-    }
-#pragma unroll
-    for (int m = 1; m <= 4; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-    // scale = fp16_rne(amax / divisor); for 4 bits amax * 0.125 is the same
-    // exactly rounded value as amax / 8.
-    const __half s16 = __float2half_rn(BITS == 4 ? amax * 0.125f : amax / (BITS == 6 ? 31.0f : 127.0f));
-    const float s = __half2float(s16);
-    constexpr float kMax = float((1 << (BITS - 1)) - 1), kMin = -float(1 << (BITS - 1));
-    int q[4] = {0, 0, 0, 0};
-    if (s != 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float n = rintf(x[i] / s);  // correctly rounded divide, then half-to-even
-            n = fminf(fmaxf(n, kMin), kMax);
-            q[i] = int(n);
-        }
-    }
-    const int rb = blk_row_bytes(BITS, D);
     const int64_t page = slot / page_size, off = slot % page_size;
-    uint8_t* row = (which ? v_pool : k_pool) + ((page * H + h) * page_size + off) * rb;
-    // Values 4j .. 4j+3 of group g (j = e & 7, g = e >> 3).
-    const int g = e >> 3, j = e & 7;
-    uint8_t* grp = row + g * blk_group_bytes(BITS);
-    if (BITS == 8) {
-        uint32_t w = 0u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w |= (uint32_t(q[i]) & 0xFFu) << (8 * i);
-        reinterpret_cast<uint32_t*>(grp)[j] = w;
-    } else {
-        // value 2k in the low nibble of byte k, value 2k+1 in the high nibble
-        uint32_t nib = 0u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) nib |= (uint32_t(q[i]) & 0xFu) << (4 * i);
-        reinterpret_cast<uint16_t*>(grp)[j] = uint16_t(nib);
-        if (BITS == 6) {
-            uint32_t top = 0u;  // high two bits of value 4j + i in bits 2i .. 2i+1 of byte j
-#pragma unroll
-            for (int i = 0; i < 4; ++i) top |= ((uint32_t(q[i]) >> 4) & 3u) << (2 * i);
-            grp[16 + j] = uint8_t(top);
-        }
-    }
-    if (j == 0) reinterpret_cast<uint16_t*>(row + (D / 32) * blk_group_bytes(BITS))[g] = __half_as_ushort(s16);
+    uint8_t* row = (which ? v_pool : k_pool) + ((page * H + h) * page_size + off) * blk_row_bytes(BITS, D);
+    encode_blk_quad<BITS>(x, row, D, e, lane);
 }
 
 template <InType DT, int BITS>

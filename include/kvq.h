@@ -360,6 +360,32 @@ kvq_status kvq_attend(const kvq_cache* cache, const float* q, int32_t n_q_heads,
                       int32_t split_keys, void* workspace, size_t workspace_bytes, float* out, float* lse,
                       hipStream_t stream);
 
+/* A whole decode step of the 4-bit cache in two launches (TensorFold "What
+ * it is": the step packs the new key and value, rotates the query once,
+ * attends over the cache in chunks, merges them in order and rotates the
+ * output back once): the store and the query rotation run inside the decode
+ * launch, then the merge.  Token b's K and V rows (k, v: device
+ * [batch][num_kv_heads][head_dim] of kv_dtype) are stored at position
+ * T_b - 1 of sequence b, T_b = seq_lens[b], i.e. at slot
+ * page_table[b*max_pages + (T_b-1)/page_size]*page_size + (T_b-1)%page_size
+ * (a page outside the pool is not stored, as kvq_store skips such a slot;
+ * a sequence with T_b = 0 stores nothing); q ([batch][n_q_heads][head_dim]
+ * of q_dtype) is the query BEFORE rotation; every other argument means what
+ * it means for kvq_attend.  The stored bytes and out / lse are bit-identical
+ * to kvq_store_rotate_q (that slot mapping, n_tokens = batch, n_rows =
+ * batch * n_q_heads) followed by kvq_attend on the rotated query, and the
+ * workspace holds the same partials.  The positions T_b - 1 of different
+ * sequences must map to different slots.  k, v, q, out: 16-byte aligned.
+ * KVQ_ERR_UNSUPPORTED outside the kernels that carry the step (format Q4,
+ * head_dim 256, groups of at most 8 query heads, pages of a multiple of 16
+ * tokens, split_keys up to 1024 or above 1024 and at most 8192): call
+ * kvq_store_rotate_q and kvq_attend instead. */
+kvq_status kvq_decode_step(const kvq_cache* cache, const void* k, const void* v, int32_t kv_dtype, const void* q,
+                           int32_t q_dtype, int32_t n_q_heads, const int32_t* page_table, int32_t max_pages,
+                           const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
+                           int32_t split_keys, void* workspace, size_t workspace_bytes, float* out, float* lse,
+                           hipStream_t stream);
+
 /* kvq_attend for callers that cannot allocate device memory -- code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc:
  * the same work with the partials in a static device array of
