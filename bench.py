@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); valid only for the kernel sources they were taken on
 # (keyed by the sha256 of the kernel file followed by the device-helper header it includes).
 TRAFFIC = {
-    "d41e067b2914e9684b37aec3a4fbc18fbf5e6c00ed15f8691659ab5044dc297a": {
+    "cb49a6e0450434563dceb0d3d89e053cb4eb6254b14d2ed8c71e106d5196a936": {
         "fetch_kib": 147708.5, "write_kib": 3264.0, "fetch_scale": 2.0, "write_scale": 1.0,
         "profile": "profiles/decode_q4_mfma_gqa_q4_262k.md"},
 }
@@ -76,6 +76,8 @@ class _Bench:
     DECODE = None
     DECODE_MERGE = ()  # indices of the decode and merge calls
     EXTRA_TIMED = {}  # name -> call index, timed like the decode
+    STEP = None  # indices of the calls one step runs (None: every call)
+    EVENT_CALLS = None  # the calls run while one of them is timed by events (None: the step's)
 
     def step(self, events=None, which=None, stream=None, only=None):
         """Enqueue one step; if events is a list of (start, end) pairs, bracket
@@ -85,6 +87,8 @@ class _Bench:
         calls with those indices."""
         L = self.kvq.lib
         which = self.DECODE if which is None else which
+        if only is None:
+            only = self.STEP
         for layer, calls in enumerate(self.raw):
             rc = 0
             for i, (fn, args) in enumerate(calls):
@@ -108,8 +112,12 @@ class _Bench:
 class Q4Bench(_Bench):
     """Every layer's cache, query and buffers for one 4-bit workload, plus the
     raw C-ABI argument tuples of one step (validated once by building them
-    through the binding's checks).  Step per layer: store + rotate (one
-    launch, kvq_store_rotate_q), decode, merge."""
+    through the binding's checks).  Calls per layer: store + rotate (one
+    launch, kvq_store_rotate_q), decode, merge; and, where the library has
+    it (the 4-bit format at head_dim 256), kvq_decode_step, the same work in
+    two launches with the same bits.  A step runs kvq_decode_step where it
+    exists (the three calls are timed too, as us_per_layer_three_launches),
+    else the three calls."""
 
     DECODE = 1
     DECODE_MERGE = (1, 2)
@@ -150,8 +158,12 @@ class Q4Bench(_Bench):
         self.pa, self.pm, self.pz = torch.empty(acc_shape, **f32), torch.empty(mz_shape, **f32), torch.empty(mz_shape, **f32)
         self.out = torch.empty((w.n_layers, 1, w.n_q_heads, w.head_dim), **f32)
         self.lse = torch.empty((w.n_layers, 1, w.n_q_heads), **f32)
+        ws_bytes = kvq.kvq_attend_workspace_bytes(self.caches[0], 1, w.n_q_heads, T, w.split_keys)
+        self.ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=device)
         torch.cuda.synchronize()
-        # One checked pass through the binding validates every argument once.
+        # One checked pass through the binding validates every argument once;
+        # the step's outputs are then those of kvq_decode_step where it runs.
+        self.fused = True
         for layer in range(w.n_layers):
             c = self.caches[layer]
             kvq.kvq_store_rotate_q(c, self.k_new[layer], self.v_new[layer], self.slot_new, self.q[layer],
@@ -160,6 +172,15 @@ class Q4Bench(_Bench):
                                 self.pa, self.pm, self.pz)
             kvq.kvq_merge(c, self.pa, self.pm, self.pz, self.seq_lens, T, w.split_keys, out=self.out[layer],
                           lse=self.lse[layer])
+            if self.fused:
+                try:
+                    kvq.kvq_decode_step(c, self.k_new[layer], self.v_new[layer], self.q[layer], self.page_table,
+                                        self.seq_lens, T, w.sm_scale, w.split_keys, workspace=self.ws,
+                                        out=self.out[layer], lse=self.lse[layer])
+                except kvq.KvqError as e:
+                    if e.status != kvq.KVQ_ERR_UNSUPPORTED:
+                        raise
+                    self.fused = False
         torch.cuda.synchronize()
         P = ctypes.c_void_p
         stream = P(torch.cuda.current_stream().cuda_stream)
@@ -179,6 +200,17 @@ class Q4Bench(_Bench):
                                P(self.seq_lens.data_ptr()), 1, w.n_q_heads, T, w.split_keys, 1,
                                P(self.out[layer].data_ptr()), P(self.lse[layer].data_ptr()), stream)),
             ])
+            if self.fused:
+                self.raw[-1].append(
+                    ("kvq_decode_step", (d, P(self.k_new[layer].data_ptr()), P(self.v_new[layer].data_ptr()),
+                                         kvq._DTYPES[self.k_new[layer].dtype], P(self.q[layer].data_ptr()), 0,
+                                         w.n_q_heads, P(self.page_table.data_ptr()), self.page_table.shape[1],
+                                         P(self.seq_lens.data_ptr()), 1, T, ctypes.c_float(w.sm_scale),
+                                         w.split_keys, P(self.ws.data_ptr()), ctypes.c_size_t(self.ws.numel()),
+                                         P(self.out[layer].data_ptr()), P(self.lse[layer].data_ptr()), stream)))
+        if self.fused:
+            self.STEP = (3,)
+            self.THREE_CALLS = self.EVENT_CALLS = (0, 1, 2)
 
     @property
     def kv_bytes_per_layer(self):
@@ -659,7 +691,7 @@ def time_decode(b, steps, which=None):
            for _ in range(b.w.n_layers)] for _ in range(steps)]
     torch.cuda.synchronize()
     for s in range(steps):
-        b.step(ev[s], which)
+        b.step(ev[s], which, only=b.EVENT_CALLS)
     torch.cuda.synchronize()
     d = [e0.elapsed_time(e1) for row in ev for (e0, e1) in row]
     return sum(d) / len(d)
@@ -671,6 +703,7 @@ def measure(b, steps, warmup):
     the decode launch (and other calls to time) by events."""
     import torch
     ms_step, wall = time_steps(b, steps, warmup)
+    ms_three = time_steps(b, steps, warmup, only=b.THREE_CALLS)[0] if getattr(b, "THREE_CALLS", None) else None
     ms_dm, _ = time_steps(b, steps, warmup, only=b.DECODE_MERGE)
     g = capture(b)
     check_graph(b, g)
@@ -690,6 +723,8 @@ def measure(b, steps, warmup):
          "decode_us_bracketed": dec_ms_bracketed * 1e3,
          "decode_merge_us_per_layer": ms_dm * 1e3 / L, "graph_us_per_layer": ms_graph * 1e3 / L,
          "step_gbs": kvb * L / (ms_step * 1e-3) / 1e9, "decode_gbs": kvb / (dec_ms * 1e-3) / 1e9, "wall_s": wall}
+    if ms_three is not None:
+        r["us_per_layer_three_launches"] = ms_three * 1e3 / L
     if b.flops_per_layer:
         r["decode_tflops"] = b.flops_per_layer / (dec_ms * 1e-3) / 1e12
     for name, idx in b.EXTRA_TIMED.items():
@@ -962,6 +997,8 @@ def main():
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "split_keys": w.split_keys, "kv_bytes_per_layer": kvb},
         "us_per_layer": round(m["us_per_layer"], 3),
+        "step_entry": ("kvq_decode_step (store and query rotation inside the decode launch, then the merge)"
+                       if b.fused else "kvq_store_rotate_q, kvq_decode_attn, kvq_merge"),
         "decode_merge_us_per_layer": round(m["decode_merge_us_per_layer"], 3),
         "graph_us_per_layer": round(m["graph_us_per_layer"], 3),
         "pct_hbm_peak": round(100 * m["step_gbs"] / HBM_PEAK_GBS, 2),
@@ -975,6 +1012,8 @@ def main():
                                        "sources differ from the build the counters were taken on"},
         "wall_s": round(m["wall_s"], 3),
     }
+    if "us_per_layer_three_launches" in m:
+        rec["us_per_layer_three_launches"] = round(m["us_per_layer_three_launches"], 3)
     del b
     torch.cuda.empty_cache()
     _log("bench: HBM read ceiling (kvq_stream_read over 2 GiB)")
@@ -1003,6 +1042,8 @@ def main():
                  "decode_frac_hbm": round(mx["decode_gbs"] / HBM_PEAK_GBS, 4)}
             if "decode_tflops" in mx:
                 e["decode_tflops"] = round(mx["decode_tflops"], 2)
+            if "us_per_layer_three_launches" in mx:
+                e["us_per_layer_three_launches"] = round(mx["us_per_layer_three_launches"], 3)
             if cls is ChunkBench:
                 # the chunk's attention is a dense contraction: its roofline is the f16 matrix-core peak
                 e["chunk_rows"] = wx.chunk_rows

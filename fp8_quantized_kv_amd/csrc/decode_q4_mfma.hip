@@ -198,27 +198,32 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
     const int n_sub = (n_keys + kSub - 1) / kSub;
 
     // STEP: store token b's K and V rows at position T - 1 if this wave's
-    // keys hold it.  Stores then a full wait, so no store is outstanding when
-    // the copies' waits count (vmcnt counts both), and the row is in the L2
-    // before this wave copies it.  A position whose page is outside the pool
-    // is not stored (kvq_store skips such a slot too).
+    // keys hold it; the row must be in the L2 (the stores acknowledged:
+    // vmcnt(0)) before this wave copies it.  vmcnt counts stores too, but an
+    // older store still outstanding can only make the copies' count-based
+    // waits wait longer, never let one pass early: a load completes before
+    // every later load, so while it is outstanding all later loads are too.
+    // A position whose page is outside the pool is not stored (kvq_store
+    // skips such a slot too).
     const int pos_new = T - 1;
     const bool storer = STEP && T > 0 && pos_new >= w0 && pos_new < w1;  // wave-uniform
-    auto store_token = [&]() {
+    const int t_new = storer ? (pos_new - w0) / kSub : -1;              // the row's sub-tile
+    auto store_token = [&](bool wait) {
         const int page = pt[pos_new / page_size];
         if (page >= 0 && page < num_pages) {
             const int64_t row = (int64_t(page) * H + g) * page_size + pos_new % page_size;
             const int64_t src = (int64_t(b) * H + g) * D + 4 * lane;
-            float x[4];
-            load4_dyn(a.step_kv_dt, a.step_k, src, x);
-            encode_blk_quad<BITS>(x, const_cast<uint8_t*>(k_pool) + row * RB, D, lane, lane);
-            load4_dyn(a.step_kv_dt, a.step_v, src, x);
-            encode_blk_quad<BITS>(x, const_cast<uint8_t*>(v_pool) + row * RB, D, lane, lane);
+            const void* const ptr[2] = {a.step_k, a.step_v};
+            const int64_t idx[2] = {src, src};
+            float x[2][4];
+            load4n_dyn<2>(a.step_kv_dt, ptr, idx, x);
+            encode_blk_quad<BITS>(x[0], const_cast<uint8_t*>(k_pool) + row * RB, D, lane, lane);
+            encode_blk_quad<BITS>(x[1], const_cast<uint8_t*>(v_pool) + row * RB, D, lane, lane);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (wait) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
-    // Rows of sub-tiles 0 and 1 are copied just below: store first.
-    if (storer && (pos_new - w0) / kSub <= 1) store_token();
+    // Rows of sub-tiles 0 and 1 are copied just below: store and wait first.
+    if (storer && t_new <= 1) store_token(true);
 
     uint8_t* ring = smem + wave * S::WAVE_LDS;  // K tiles 0, 1 then V tiles 0, 1
     const uint32_t lds0 = lds_addr(ring);
@@ -255,21 +260,33 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
     const int hcol = PACK ? (n16 & 7) : n16;  // the head this lane's B column holds
     const bool live = hcol < G;
     float4 qv[NG][2];
-    if constexpr (STEP) {  // rotated here, bit for bit as kvq_rotate_q rotates it
-        const int64_t qrow = (hb + (live ? hcol : 0)) * D;
+    if constexpr (STEP) {  // rotated here, bit for bit as kvq_rotate_q rotates it (PACK only)
+        static_assert(!STEP || PACK, "the step's rotation uses the packed columns");
+        // lane column n16 loads groups 2k + (n16 >> 3): the two column halves
+        // hold the same head (PACK), so each rotates half the groups
+        const int64_t qrow = (hb + (live ? hcol : 0)) * D + 32 * (n16 >> 3);
+        const void* ptr[NG];
+        int64_t idx[NG];
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-            float y[8], x0[4], x1[4];
-            load4_dyn(a.step_q_dt, a.step_q, qrow + 32 * gi + 8 * q4, x0);
-            load4_dyn(a.step_q_dt, a.step_q, qrow + 32 * gi + 8 * q4 + 4, x1);
+        for (int n = 0; n < NG; ++n) {
+            ptr[n] = a.step_q;
+            idx[n] = qrow + 64 * (n >> 1) + 8 * q4 + 4 * (n & 1);
+        }
+        float xl[NG][4];
+        load4n_dyn<NG>(a.step_q_dt, ptr, idx, xl);
+        float x[NG / 2][8], y[NG][8];
+#pragma unroll
+        for (int k = 0; k < NG / 2; ++k)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                y[i] = x0[i];
-                y[4 + i] = x1[i];
+                x[k][i] = xl[2 * k][i];
+                x[k][4 + i] = xl[2 * k + 1][i];
             }
-            rotate_q_lanes4(y, lane);
-            qv[gi][0] = make_float4(y[0], y[1], y[2], y[3]);
-            qv[gi][1] = make_float4(y[4], y[5], y[6], y[7]);
+        rotate_q_packed<NG>(x, y, lane);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            qv[gi][0] = make_float4(y[gi][0], y[gi][1], y[gi][2], y[gi][3]);
+            qv[gi][1] = make_float4(y[gi][4], y[gi][5], y[gi][6], y[gi][7]);
         }
     } else {
         const float* qh = a.q + (hb + (live ? hcol : 0)) * D;
@@ -280,8 +297,9 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
         }
     }
     // STEP, a later sub-tile holds the new row: store it now, while the first
-    // copies land (its copy is issued two sub-tiles ahead, after this).
-    if (storer && (pos_new - w0) / kSub > 1) store_token();
+    // copies land; the acknowledgement is awaited just before that sub-tile's
+    // copy is issued (two sub-tiles ahead, in the loop).
+    if (storer && t_new > 1) store_token(false);
 
     // B operands of the score MFMAs: pre-scaled query (log2 units) of head
     // n16 for the 8 channels that k-slots (q4, 0..7) of each group hold,
@@ -404,6 +422,7 @@ __global__ __launch_bounds__(W * 64, BITS == 4 ? 2 : 1) void decode_q4_mfma(cons
             // Everything the scores read from the K slot is now in registers
             // (the copy's lgkmcnt wait sees to that): refill the slot with
             // sub-tile t + 2 before the MFMAs rather than after them.
+            if (STEP && t + 2 == t_new) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the new row stored
             if (t + 2 < n_sub) issue(k_pool, t + 2, k_ring);
             float acc[2][4] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
             f32x4 dprev[2];

@@ -74,12 +74,13 @@ __device__ __forceinline__ void barrier_lds() {
 }
 
 // STEP (kvq_decode_step): the query arrives unrotated and is rotated here,
-// and wave 0 of the pair whose key range holds position seq_lens[b] - 1
-// first stores token b's K and V rows there (the store kernel's encoder, so
-// the bytes are the same).  Both waves of that pair copy the row, so the
-// store completes before either copy: before the workgroup's first barrier
-// if the row's sub-tile is copied in the prologue, else before the storing
-// wave's first exchange barrier, which precedes every later copy.
+// and the pair whose key range holds position seq_lens[b] - 1 first stores
+// token b's K row (wave 0 of the pair) and V row (wave 1) there (the store
+// kernel's encoder, so the bytes are the same).  Both waves of that pair
+// copy both rows, so both stores complete before either copy: before the
+// workgroup's first barrier if the row's sub-tile is copied in the
+// prologue, else before the exchange barrier after which that sub-tile is
+// copied.
 template <bool STEP>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWaves * 64, kWaves * 64), amdgpu_waves_per_eu(4, 4)))
 void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool, int H,
@@ -106,22 +107,20 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
     const int hcol = n16 & 7;
     const bool live = hcol < G;
     float4 qv[4][2];
-    if constexpr (STEP) {  // rotated here, bit for bit as kvq_rotate_q rotates it
-        const int64_t qrow = (hb + (live ? hcol : 0)) * kD + 128 * h;
+    // STEP: the unrotated query, rotated after the first copies are issued;
+    // column n16 loads groups 2k + (n16 >> 3) of this half (columns n16 and
+    // n16 ^ 8 hold the same head, so each rotates half the groups)
+    float qraw[4][4];
+    if constexpr (STEP) {
+        const int64_t qrow = (hb + (live ? hcol : 0)) * kD + 128 * h + 32 * (n16 >> 3);
+        const void* ptr[4];
+        int64_t idx[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float y[8], x0[4], x1[4];
-            load4_dyn(a.step_q_dt, a.step_q, qrow + 32 * j + 8 * q4, x0);
-            load4_dyn(a.step_q_dt, a.step_q, qrow + 32 * j + 8 * q4 + 4, x1);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                y[i] = x0[i];
-                y[4 + i] = x1[i];
-            }
-            rotate_q_lanes4(y, lane);
-            qv[j][0] = make_float4(y[0], y[1], y[2], y[3]);
-            qv[j][1] = make_float4(y[4], y[5], y[6], y[7]);
+        for (int n = 0; n < 4; ++n) {
+            ptr[n] = a.step_q;
+            idx[n] = qrow + 64 * (n >> 1) + 8 * q4 + 4 * (n & 1);
         }
+        load4n_dyn<4>(a.step_q_dt, ptr, idx, qraw);
     } else {
         const float* qh = a.q + (hb + (live ? hcol : 0)) * kD + 128 * h;
 #pragma unroll
@@ -200,29 +199,33 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
         dma16<true>(r1, src_off0, dst + 1280u);
         if (lane < 16) dma16<false>(r1, src_off1, dst + 2304u);
     };
-    // STEP: the new row (position T - 1) and the wave that stores it.  The
-    // store ends with a full wait, so no store is outstanding when the
-    // copies' waits count (vmcnt counts both).  A position whose page is
-    // outside the pool is not stored (kvq_store skips such a slot too).
+    // STEP: the new row (position T - 1) and the pair that stores it (wave h
+    // of the pair: the K row if h = 0, the V row if h = 1); the stores must be
+    // acknowledged (vmcnt(0)) before either wave of the pair copies the row.  vmcnt counts stores too, but an older store still
+    // outstanding can only make the copies' count-based waits wait longer,
+    // never let one pass early (a load completes before every later load).
+    // A position whose page is outside the pool is not stored (kvq_store
+    // skips such a slot too).
     const int pos_new = T - 1;
     const bool holds = STEP && T > 0 && pos_new >= j0 && pos_new < j1;  // workgroup-uniform
-    const bool early = holds && ((pos_new - j0) % kp) / kSub == 0;     // copied in the prologue
-    const bool storer = holds && pair == (pos_new - j0) / kp && h == 0;
-    auto store_token = [&]() {
+    const int t_new = holds ? ((pos_new - j0) % kp) / kSub : -1;       // the row's sub-tile
+    const bool early = holds && t_new == 0;                            // copied in the prologue
+    const bool storer = holds && pair == (pos_new - j0) / kp;  // both waves of the pair
+    auto store_token = [&](bool wait) {
         const int page = pt[pos_new / page_size];
         if (page >= 0 && page < num_pages) {
             const int64_t row = (int64_t(page) * H + g) * page_size + pos_new % page_size;
             const int64_t src = (int64_t(b) * H + g) * kD + 4 * lane;
-            float x[4];
-            load4_dyn(a.step_kv_dt, a.step_k, src, x);
-            encode_blk_quad<4>(x, const_cast<uint8_t*>(k_pool) + row * kRB, kD, lane, lane);
-            load4_dyn(a.step_kv_dt, a.step_v, src, x);
-            encode_blk_quad<4>(x, const_cast<uint8_t*>(v_pool) + row * kRB, kD, lane, lane);
+            const void* const ptr[1] = {h ? a.step_v : a.step_k};
+            const int64_t idx[1] = {src};
+            float x[1][4];
+            load4n_dyn<1>(a.step_kv_dt, ptr, idx, x);
+            encode_blk_quad<4>(x[0], const_cast<uint8_t*>(h ? v_pool : k_pool) + row * kRB, kD, lane, lane);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (wait) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
     if (early) {  // both waves of the pair copy the row below: store, then a workgroup barrier
-        if (storer) store_token();
+        if (storer) store_token(true);
         __syncthreads();
     }
 
@@ -238,6 +241,23 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
     if (n_sub > 0) {
         issue(k_pool, 0, k_ring);
         issue(v_pool, 0, v_ring);
+    }
+
+    if constexpr (STEP) {  // rotated here, bit for bit as kvq_rotate_q rotates it
+        float x[2][8], y[4][8];
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[k][i] = qraw[2 * k][i];
+                x[k][4 + i] = qraw[2 * k + 1][i];
+            }
+        rotate_q_packed<4>(x, y, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            qv[j][0] = make_float4(y[j][0], y[j][1], y[j][2], y[j][3]);
+            qv[j][1] = make_float4(y[j][4], y[j][5], y[j][6], y[j][7]);
+        }
     }
 
     // Score B operands (pre-scaled query in log2 units, hi/lo by column) and
@@ -269,9 +289,10 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
     half8_t bconst;
 #pragma unroll
     for (int k = 0; k < 8; ++k) bconst[k] = _Float16((k & 2) ? -128.0f / kTwo24 : -8.0f / kTwo24);
-    // STEP, a later sub-tile holds the new row: store it now (its copies come
-    // after this wave's first exchange barrier).
-    if (storer && !early) store_token();
+    // STEP, a later sub-tile holds the new row: store it now; the
+    // acknowledgement is awaited before the exchange barrier after which both
+    // waves of the pair copy that sub-tile.
+    if (storer && !early) store_token(false);
 
     f32x4 o[8];
 #pragma unroll
@@ -347,6 +368,7 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
                     sc[kb][i] = h == 0 ? sc[kb][i] + x : x + sc[kb][i];
                 }
         }
+        if (STEP && storer && t + 1 == t_new) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // new row stored
         barrier_lds();  // the other half has read this slot: it may be refilled
         if (!act) continue;
         if (t + 1 < n_sub) issue(k_pool, t + 1, k_ring);  // into the slot of sub-tile t - 1

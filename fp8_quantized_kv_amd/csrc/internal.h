@@ -121,11 +121,22 @@ __device__ __forceinline__ void rotate_q_quad(const void* q, float* q_rot, int64
     *reinterpret_cast<float4*>(q_rot + 4 * quad) = make_float4(x[0] * c, x[1] * c, x[2] * c, x[3] * c);
 }
 
-// load4 with the element type chosen at run time (uniform across the wave).
-__device__ __forceinline__ void load4_dyn(InType dt, const void* p, int64_t i, float (&x)[4]) {
-    if (dt == InType::F32) load4<InType::F32>(p, i, x);
-    else if (dt == InType::BF16) load4<InType::BF16>(p, i, x);
-    else load4<InType::F16>(p, i, x);
+// N load4s (elements i[n] .. i[n] + 3 of p[n]) with the element type chosen
+// at run time (uniform across the wave): one branch around all N, so the
+// loads are issued together and waited for once.
+template <int N>
+__device__ __forceinline__ void load4n_dyn(InType dt, const void* const (&p)[N], const int64_t (&i)[N],
+                                           float (&x)[N][4]) {
+    if (dt == InType::F32) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) load4<InType::F32>(p[n], i[n], x[n]);
+    } else if (dt == InType::BF16) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) load4<InType::BF16>(p[n], i[n], x[n]);
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) load4<InType::F16>(p[n], i[n], x[n]);
+    }
 }
 
 // The query rotation above for the decode kernels' lane layout: lane (n, q)
@@ -134,8 +145,12 @@ __device__ __forceinline__ void load4_dyn(InType dt, const void* p, int64_t i, f
 // on the same operands: stages 1 and 2 inside each quad, stage 4 between the
 // lane's two quads, stages 8 and 16 with lane ^ 16 and lane ^ 32; every pair
 // (a, b), a the lower element, becomes (a + b, a - b); then x
-// fp32(1/sqrt(32)).  So y equals kvq_rotate_q's output bit for bit.  Every
-// lane of the four q-lanes of a group must call it.
+// fp32(1/sqrt(32)).  So y equals kvq_rotate_q's output bit for bit.  The
+// cross-lane stages take the partner's value with the permlane swaps (of the
+// pair they return, element 0 is the lower lane's value, element 1 the upper
+// lane's) and form lo + s * hi with s = +1 (lower lane) or -1 (upper lane) in
+// one fma: s * hi is exact, so the single rounding gives lo + hi or lo - hi
+// exactly.  Every lane of the four q-lanes of a group must call it.
 __device__ __forceinline__ void rotate_q_lanes4(float (&y)[8], int lane) {
 #pragma unroll
     for (int h = 0; h < 8; h += 4) {
@@ -161,18 +176,41 @@ __device__ __forceinline__ void rotate_q_lanes4(float (&y)[8], int lane) {
         y[i] = a + b;
         y[i + 4] = a - b;
     }
+    const float s16 = (lane & 16) ? -1.0f : 1.0f, s32 = (lane & 32) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int m = 16; m <= 32; m <<= 1) {
-        const bool upper = (lane & m) != 0;
+    for (int i = 0; i < 8; ++i) {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(y[i]), __float_as_uint(y[i]), false, false);
+        y[i] = fmaf(s16, __uint_as_float(p[1]), __uint_as_float(p[0]));
+    }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float o = __shfl_xor(y[i], m, 64);
-            y[i] = upper ? o - y[i] : y[i] + o;
-        }
+    for (int i = 0; i < 8; ++i) {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(y[i]), __float_as_uint(y[i]), false, false);
+        y[i] = fmaf(s32, __uint_as_float(p[1]), __uint_as_float(p[0]));
     }
     const float c = inv_sqrt32();
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = y[i] * c;
+}
+
+// The rotated query for the packed B layout (columns n and n ^ 8 of a
+// 16-lane row hold the same head): lane n of a row rotates the groups of
+// parity n >> 3 of each pair (2k, 2k + 1) -- x[k] holds its 8 raw values of
+// group 2k + (n >> 3) -- and the two halves swap the results (row_ror:8), so
+// every lane ends with all NG groups of its head, NG / 2 rotations each.
+template <int NG>
+__device__ __forceinline__ void rotate_q_packed(float (&x)[NG / 2][8], float (&q)[NG][8], int lane) {
+    const bool odd = (lane & 8) != 0;
+#pragma unroll
+    for (int k = 0; k < NG / 2; ++k) {
+        rotate_q_lanes4(x[k], lane);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float other =
+                __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[k][i]), 0x128, 0xF, 0xF, true));
+            q[2 * k][i] = odd ? other : x[k][i];
+            q[2 * k + 1][i] = odd ? x[k][i] : other;
+        }
+    }
 }
 
 // The block-format encoder of one lane's 4 consecutive values x of a row
