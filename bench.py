@@ -114,8 +114,8 @@ class Q4Bench(_Bench):
     raw C-ABI argument tuples of one step (validated once by building them
     through the binding's checks).  Calls per layer: store + rotate (one
     launch, kvq_store_rotate_q), decode, merge; and, where the library has
-    it (the 4-bit format at head_dim 256), kvq_decode_step, the same work in
-    two launches with the same bits.  A step runs kvq_decode_step where it
+    it (the Hadamard-32 formats at head_dim 256), kvq_decode_step, the same
+    work in two launches with the same bits.  A step runs kvq_decode_step where it
     exists (the three calls are timed too, as us_per_layer_three_launches),
     else the three calls."""
 

@@ -696,18 +696,26 @@ bool decode_q4_mfma_supported(const Q4Pool& pool, const DecodeArgs& a) {
 // 26 KB per wave.  The choice depends on split_keys and the format alone, never on the
 // batch, so a sequence's partials do not depend on the sequences beside it.
 bool decode_q4_mfma_step_supported(const Q4Pool& pool, const DecodeArgs& a) {
-    return decode_q4_mfma_supported(pool, a) && pool.bits == 4 && pool.head_dim == 256 &&
-           a.n_q_heads / pool.n_kv_heads <= 8 && a.split_keys > kEightWaveSplit && a.rows == 0;
+    // 4 bits: the 4-wave kernel (splits over 1024 keys); 8 and 6 bits always run on 4 waves
+    return decode_q4_mfma_supported(pool, a) && pool.head_dim == 256 && a.n_q_heads / pool.n_kv_heads <= 8 &&
+           (pool.bits != 4 || a.split_keys > kEightWaveSplit) && a.rows == 0;
 }
 
 hipError_t launch_decode_q4_mfma(const Q4Pool& pool, const DecodeArgs& a, hipStream_t s) {
     const dim3 grid = decode_grid(a, pool.n_kv_heads);
     const bool eight = a.split_keys <= kEightWaveSplit;
     const bool pack = a.n_q_heads / pool.n_kv_heads <= 8;
-    if (a.step_k) {  // kvq_decode_step: one configuration (the launcher's caller checks it)
+    if (a.step_k) {  // kvq_decode_step: head_dim 256, packed columns, 4 waves (the caller checks it)
         if (!decode_q4_mfma_step_supported(pool, a)) return hipErrorInvalidValue;
-        decode_q4_mfma<256, 4, true, 4, true><<<grid, dim3(4 * 64), 0, s>>>(pool.k, pool.v, pool.n_kv_heads,
-                                                                            pool.page_size, pool.num_pages, a);
+        if (pool.bits == 8)
+            decode_q4_mfma<256, 4, true, 8, true><<<grid, dim3(4 * 64), 0, s>>>(pool.k, pool.v, pool.n_kv_heads,
+                                                                                pool.page_size, pool.num_pages, a);
+        else if (pool.bits == 6)
+            decode_q4_mfma<256, 4, true, 6, true><<<grid, dim3(4 * 64), 0, s>>>(pool.k, pool.v, pool.n_kv_heads,
+                                                                                pool.page_size, pool.num_pages, a);
+        else
+            decode_q4_mfma<256, 4, true, 4, true><<<grid, dim3(4 * 64), 0, s>>>(pool.k, pool.v, pool.n_kv_heads,
+                                                                                pool.page_size, pool.num_pages, a);
         return hipGetLastError();
     }
 #define KVQ_LAUNCH(D_, W_, P_, B_)                                                                             \

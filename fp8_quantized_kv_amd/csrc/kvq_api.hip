@@ -460,9 +460,10 @@ kvq_status kvq_decode_step(const kvq_cache* cache, const void* k, const void* v,
     d.step_kv_dt = static_cast<InType>(kv_dtype);
     d.step_q_dt = static_cast<InType>(q_dtype);
     // The kernel kvq_decode_attn would run (launch_decode_for), in its STEP form.
-    if (cache->format != KVQ_FMT_Q4_H32) return KVQ_ERR_UNSUPPORTED;
+    if (!is_h32(cache->format)) return KVQ_ERR_UNSUPPORTED;
     const kvq::Q4Pool pool = q4_pool(cache);
-    if (kvq::decode_q4_pair_supported(pool, d)) st = launched(kvq::launch_decode_q4_pair(pool, d, stream));
+    if (pool.bits == 4 && kvq::decode_q4_pair_supported(pool, d))
+        st = launched(kvq::launch_decode_q4_pair(pool, d, stream));
     else if (kvq::decode_q4_mfma_step_supported(pool, d)) st = launched(kvq::launch_decode_q4_mfma(pool, d, stream));
     else return KVQ_ERR_UNSUPPORTED;
     if (st != KVQ_OK) return st;

@@ -376,10 +376,10 @@ kvq_status kvq_attend(const kvq_cache* cache, const float* q, int32_t n_q_heads,
  * batch * n_q_heads) followed by kvq_attend on the rotated query, and the
  * workspace holds the same partials.  The positions T_b - 1 of different
  * sequences must map to different slots.  k, v, q, out: 16-byte aligned.
- * KVQ_ERR_UNSUPPORTED outside the kernels that carry the step (format Q4,
- * head_dim 256, groups of at most 8 query heads, pages of a multiple of 16
- * tokens, split_keys up to 1024 or above 1024 and at most 8192): call
- * kvq_store_rotate_q and kvq_attend instead. */
+ * KVQ_ERR_UNSUPPORTED outside the kernels that carry the step (formats Q4,
+ * Q8 and Q6 at head_dim 256, groups of at most 8 query heads, pages of a
+ * multiple of 16 tokens, split_keys at most 8192): call kvq_store_rotate_q
+ * and kvq_attend instead. */
 kvq_status kvq_decode_step(const kvq_cache* cache, const void* k, const void* v, int32_t kv_dtype, const void* q,
                            int32_t q_dtype, int32_t n_q_heads, const int32_t* page_table, int32_t max_pages,
                            const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,

@@ -2,10 +2,10 @@
 decode launch, then the merge) against kvq_store_rotate_q + kvq_attend, bit
 for bit: the pools, the partials, out and lse; and the step's output against
 the oracle after the oracle stores the same token.  Both 4-bit matrix-core
-kernels, both places the store can take (before the first copies when the
-new row's sub-tile is copied at once, later otherwise), every input dtype,
-an empty sequence, a page outside the pool, and the configurations the step
-does not carry."""
+kernels and the 8- and 6-bit block formats, both places the store can take
+(before the first copies when the new row's sub-tile is copied at once,
+later otherwise), every input dtype, an empty sequence, a page outside the
+pool, and the configurations the step does not carry."""
 import numpy as np
 import pytest
 import torch
@@ -54,7 +54,8 @@ def _step_slots(case):
 
 def _clone_cache(kvq, case):
     w = case.w
-    c = kvq.Q4Cache(case.lay.num_pages, w.n_kv_heads, w.head_dim, w.page_size, "cuda")
+    fmt = {4: kvq.FMT_Q4_H32, 6: kvq.FMT_Q6_H32, 8: kvq.FMT_Q8_H32}[w.bits]
+    c = kvq.Q4Cache(case.lay.num_pages, w.n_kv_heads, w.head_dim, w.page_size, "cuda", fmt=fmt)
     c.k_pool.copy_(case.cache.k_pool)
     c.v_pool.copy_(case.cache.v_pool)
     return c
@@ -114,6 +115,16 @@ def test_step_equals_store_rotate_then_attend(kvq, split, lens):
     _both_paths(kvq, case, split)
 
 
+@pytest.mark.parametrize("bits", [8, 6])
+@pytest.mark.parametrize("split,lens", [(512, [3000, 0, 5000]), (2048, [33000, 1, 4097, 2048])])
+def test_step_block_formats(kvq, bits, split, lens):
+    """The 8- and 6-bit block formats (the single-wave kernel, 4 waves at every split)."""
+    w = wl.shrink(wl.GQA_32K, n_layers=1, batch=len(lens), seq_len=0, bits=bits)
+    case = Q4Case(w, lens, build_oracle=False)
+    _say(f"step bits={bits} split={split} lens={lens}")
+    _both_paths(kvq, case, split, seed=19)
+
+
 @pytest.mark.parametrize("kv_dtype,q_dtype", [(torch.float32, torch.float32), (torch.float16, torch.bfloat16),
                                               (torch.bfloat16, torch.float16)])
 def test_step_dtypes(kvq, kv_dtype, q_dtype):
@@ -158,8 +169,8 @@ def test_step_matches_oracle(kvq, split):
 
 def test_step_unsupported_configurations(kvq):
     """Configurations without a step kernel are refused before any launch."""
-    for w, lens in ((wl.shrink(wl.TINY, batch=1, seq_len=0), [1000]),                     # head_dim 128
-                    (wl.shrink(wl.GQA_32K_Q8, n_layers=1, batch=1, seq_len=0), [1000])):  # 8-bit codes
+    for w, lens in ((wl.shrink(wl.TINY, batch=1, seq_len=0), [1000]),  # head_dim 128
+                    (wl.shrink(wl.GQA_32K, n_layers=1, batch=1, seq_len=0, n_q_heads=48), [1000])):  # 12 heads a group
         case = Q4Case(w, lens, build_oracle=False)
         k, v = _new_token(case, torch.bfloat16, 3)
         with pytest.raises(kvq.KvqError) as e:
