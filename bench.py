@@ -455,8 +455,10 @@ class RowsBench(_Bench):
 class RaggedBench(_Bench):
     """The ragged batch: 16 sequences of seeded lengths over a shuffled paged
     pool (one layer).  Step: the 2048-token prefill chunk of a 17th sequence
-    packed into its reserved pages, each sequence's new token stored and the
-    queries rotated (one launch), decode over the batch, merge."""
+    packed into its reserved pages, then kvq_decode_step (each sequence's new
+    token stored and the queries rotated inside the decode launch, merge);
+    the same with the store and rotation as one launch of their own
+    (kvq_store_rotate_q, decode, merge) is timed too."""
 
     DECODE = 2
     DECODE_MERGE = (2, 3)
@@ -503,6 +505,10 @@ class RaggedBench(_Bench):
         kvq.kvq_decode_attn(c, self.q_rot, self.page_table, self.seq_lens, self.T, w.sm_scale, w.split_keys,
                             self.pa, self.pm, self.pz)
         kvq.kvq_merge(c, self.pa, self.pm, self.pz, self.seq_lens, self.T, w.split_keys, out=self.out, lse=self.lse)
+        ws_bytes = kvq.kvq_attend_workspace_bytes(c, w.batch, w.n_q_heads, self.T, w.split_keys)
+        self.ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=device)
+        kvq.kvq_decode_step(c, self.k_new, self.v_new, self.q, self.page_table, self.seq_lens, self.T, w.sm_scale,
+                            w.split_keys, workspace=self.ws, out=self.out, lse=self.lse)
         torch.cuda.synchronize()
         P = ctypes.c_void_p
         stream = P(torch.cuda.current_stream().cuda_stream)
@@ -522,7 +528,14 @@ class RaggedBench(_Bench):
             ("kvq_merge", (d, P(self.pa.data_ptr()), P(self.pm.data_ptr()), P(self.pz.data_ptr()),
                            P(self.seq_lens.data_ptr()), B, Hq, self.T, w.split_keys, 1, P(self.out.data_ptr()),
                            P(self.lse.data_ptr()), stream)),
+            ("kvq_decode_step", (d, P(self.k_new.data_ptr()), P(self.v_new.data_ptr()), dt, P(self.q.data_ptr()), 0,
+                                 Hq, P(self.page_table.data_ptr()), self.page_table.shape[1],
+                                 P(self.seq_lens.data_ptr()), B, self.T, ctypes.c_float(w.sm_scale), w.split_keys,
+                                 P(self.ws.data_ptr()), ctypes.c_size_t(self.ws.numel()), P(self.out.data_ptr()),
+                                 P(self.lse.data_ptr()), stream)),
         ]]
+        self.STEP = (0, 4)
+        self.THREE_CALLS = self.EVENT_CALLS = (0, 1, 2, 3)
 
     @property
     def kv_bytes_per_layer(self):
@@ -697,11 +710,30 @@ def time_decode(b, steps, which=None):
     return sum(d) / len(d)
 
 
-def measure(b, steps, warmup):
+def settle(b, min_ms=50.0):
+    """Untimed steps for at least min_ms of GPU time: a side workload's first
+    timing right after its setup ran several percent slow when its warm-up
+    was only a few short steps."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    done = 0.0
+    while done < min_ms:
+        e0.record()
+        for _ in range(10):
+            b.step()
+        e1.record()
+        torch.cuda.synchronize()
+        done += e0.elapsed_time(e1)
+
+
+def measure(b, steps, warmup, side=False):
     """The eager step; decode + merge alone; the step replayed as one HIP
     graph (each replay first checked against the eager step's outputs); and
-    the decode launch (and other calls to time) by events."""
+    the decode launch (and other calls to time) by events.  Side workloads
+    (side=True) first run settle()."""
     import torch
+    if side:
+        settle(b)
     ms_step, wall = time_steps(b, steps, warmup)
     ms_three = time_steps(b, steps, warmup, only=b.THREE_CALLS)[0] if getattr(b, "THREE_CALLS", None) else None
     ms_dm, _ = time_steps(b, steps, warmup, only=b.DECODE_MERGE)
@@ -984,7 +1016,7 @@ def main():
                 name = f"rows{R}_q4_262k_{'shared' if shared else 'batch'}"
                 _log(f"bench: side measurement {name}")
                 br = RowsBench(b, R, shared)
-                mr = measure(br, args.steps, args.warmup)
+                mr = measure(br, args.steps, args.warmup, side=True)
                 rows[name] = {"rows": R, "lens": f"{min(br.lens)}..{max(br.lens)}", "split_keys": w.split_keys,
                               "entry": "kvq_decode_attn_rows" if shared else "kvq_decode_attn (page-table row repeated)",
                               "us_per_layer": round(mr["us_per_layer"], 3),
@@ -1034,7 +1066,7 @@ def main():
             _log(f"bench: side measurement {name}")
             bx = cls(wx)
             steps = max(3, min(args.steps, 10)) if issubclass(cls, MlaBench) else args.steps
-            mx = measure(bx, steps, args.warmup)
+            mx = measure(bx, steps, args.warmup, side=True)
             e = {"layers": wx.n_layers, "seq_len": wx.seq_len or f"{min(bx.lens)}..{max(bx.lens)} x {len(bx.lens)}",
                  "split_keys": wx.split_keys, "steps": steps,
                  "kv_bytes_per_layer": bx.kv_bytes_per_layer, "us_per_layer": round(mx["us_per_layer"], 3),
@@ -1067,7 +1099,7 @@ def main():
                     dname = f"dsa_fp8_262k_sel{n_sel}_b{batch}"
                     _log(f"bench: side measurement {dname}")
                     bd = DsaBench(bx, n_sel, batch, split)
-                    md = measure(bd, args.steps, args.warmup)
+                    md = measure(bd, args.steps, args.warmup, side=True)
                     extras[dname] = {
                         "layers": wx.n_layers, "context": wx.seq_len, "batch": batch, "n_sel": n_sel,
                         "split_keys": split, "steps": args.steps,
