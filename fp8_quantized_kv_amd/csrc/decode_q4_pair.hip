@@ -23,8 +23,8 @@
 // four waves per SIMD fit.
 //
 // Where it pays: a pair spends more instructions per key than a single wave
-// (both halves run the softmax, and the exchange adds LDS traffic and two
-// barriers per tile), so once every CU is full of work the single-wave
+// (both halves run the softmax, and the exchange adds LDS traffic and a
+// barrier per tile), so once every CU is full of work the single-wave
 // kernel, with fewer instructions per key, is as fast or faster (measured:
 // 65 vs 61 us for a 262144-token, 2048-key-split layer).  For short splits
 // (up to 1024 keys, e.g. 32K contexts) the doubled occupancy wins (16.2 vs
@@ -358,6 +358,12 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mine[(4 * kb + i) * 64 + lane] = sc[kb][i];
         }
+        if (STEP && storer && t + 1 == t_new) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // new row stored
+        // One barrier per sub-tile: both halves' scores are in LDS, and each
+        // half has finished reading the other's sub-tile t - 1 exchange (its
+        // reads completed before it reached this barrier), so the slot of
+        // sub-tile t - 1 may take sub-tile t + 1's K below.  Sub-tile t's
+        // exchange (slot t & 1) is refilled only after the next barrier.
         barrier_lds();
         if (act) {
 #pragma unroll
@@ -368,8 +374,6 @@ void decode_q4_pair(const uint8_t* __restrict__ k_pool, const uint8_t* __restric
                     sc[kb][i] = h == 0 ? sc[kb][i] + x : x + sc[kb][i];
                 }
         }
-        if (STEP && storer && t + 1 == t_new) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // new row stored
-        barrier_lds();  // the other half has read this slot: it may be refilled
         if (!act) continue;
         if (t + 1 < n_sub) issue(k_pool, t + 1, k_ring);  // into the slot of sub-tile t - 1
 
