@@ -222,7 +222,9 @@ class Q4Bench(_Bench):
 
 class MlaBench(_Bench):
     """The fp8 latent workload: every layer's cache and query; step per layer:
-    store the step's token, decode (absorbed attention, split-T), merge."""
+    store the step's token, decode (absorbed attention, split-T), merge -- as
+    kvq_decode_step (the store inside the decode launch, then the merge), with
+    the three calls timed too (us_per_layer_three_launches)."""
 
     DECODE = 1
     DECODE_MERGE = (1, 2)
@@ -260,6 +262,10 @@ class MlaBench(_Bench):
         self.out = torch.empty((w.n_layers, 1, w.n_heads, w.kv_lora), **f32)
         self.lse = torch.empty((w.n_layers, 1, w.n_heads), **f32)
         self.q_rot = torch.empty((1, w.n_heads, w.head_dim), **f32)
+        self.fused = not self.ROTATED  # the fp8 rows' step form; the rotated rows have none
+        if self.fused:
+            ws_bytes = kvq.kvq_attend_workspace_bytes(self.caches[0], 1, w.n_heads, T, w.split_keys)
+            self.ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=device)
         torch.cuda.synchronize()
         for layer in range(w.n_layers):
             c = self.caches[layer]
@@ -272,6 +278,10 @@ class MlaBench(_Bench):
                                 self.pa, self.pm, self.pz)
             kvq.kvq_merge(c, self.pa, self.pm, self.pz, self.seq_lens, T, w.split_keys, out=self.out[layer],
                           lse=self.lse[layer])
+            if self.fused:
+                kvq.kvq_decode_step(c, self.x_new[layer], None, self.q[layer], self.page_table, self.seq_lens, T,
+                                    w.sm_scale, w.split_keys, workspace=self.ws, out=self.out[layer],
+                                    lse=self.lse[layer])
         torch.cuda.synchronize()
         P = ctypes.c_void_p
         stream = P(torch.cuda.current_stream().cuda_stream)
@@ -295,6 +305,17 @@ class MlaBench(_Bench):
                                P(self.seq_lens.data_ptr()), 1, w.n_heads, T, w.split_keys, 1 if self.ROTATED else 0,
                                P(self.out[layer].data_ptr()), P(self.lse[layer].data_ptr()), stream)),
             ])
+            if self.fused:
+                self.raw[-1].append(
+                    ("kvq_decode_step", (d, P(self.x_new[layer].data_ptr()), None, xdt, P(self.q[layer].data_ptr()),
+                                         kvq.DT_F32, w.n_heads, P(self.page_table.data_ptr()),
+                                         self.page_table.shape[1], P(self.seq_lens.data_ptr()), 1, T,
+                                         ctypes.c_float(w.sm_scale), w.split_keys, P(self.ws.data_ptr()),
+                                         ctypes.c_size_t(self.ws.numel()), P(self.out[layer].data_ptr()),
+                                         P(self.lse[layer].data_ptr()), stream)))
+        if self.fused:
+            self.STEP = (3,)
+            self.THREE_CALLS = self.EVENT_CALLS = (0, 1, 2)
 
     ROW_BYTES = 576 + 8  # code bytes + two f32 scales per position
 
@@ -1079,6 +1100,8 @@ def main():
                 e["decode_tflops"] = round(mx["decode_tflops"], 2)
             if "us_per_layer_three_launches" in mx:
                 e["us_per_layer_three_launches"] = round(mx["us_per_layer_three_launches"], 3)
+            if getattr(bx, "STEP", None) and "kvq_decode_step" in [bx.raw[0][i][0] for i in bx.STEP]:
+                e["step_entry"] = "kvq_decode_step"
             if cls is ChunkBench:
                 # the chunk's attention is a dense contraction: its roofline is the f16 matrix-core peak
                 e["chunk_rows"] = wx.chunk_rows

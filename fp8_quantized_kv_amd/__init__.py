@@ -464,7 +464,8 @@ def kvq_decode_step(cache, k, v, q, page_table, seq_lens, max_seq_len, sm_scale,
     """A decode step in two launches: token b's K and V rows (k, v: [batch][num_kv_heads][head_dim]) stored
     at position seq_lens[b] - 1 of sequence b through the page table, the query q ([batch][n_q_heads]
     [head_dim], before rotation) rotated, attention and merge.  Returns (out, lse), the same bits as
-    kvq_store_rotate_q + kvq_attend."""
+    kvq_store_rotate_q + kvq_attend.  Fp8Cache: k is the latent rows [batch][head_dim], v None, q f32
+    (the same bits as kvq_store + kvq_attend)."""
     B, Hq, D = q.shape
     need = kvq_attend_workspace_bytes(cache, B, Hq, max_seq_len, split_keys)
     if workspace is None:
@@ -476,9 +477,15 @@ def kvq_decode_step(cache, k, v, q, page_table, seq_lens, max_seq_len, sm_scale,
     kdt, qdt = _DTYPES.get(k.dtype), _DTYPES.get(q.dtype)
     if kdt is None or qdt is None:
         raise ValueError(f"unsupported dtype {k.dtype if kdt is None else q.dtype}")
-    shape = (B, cache.num_kv_heads, cache.head_dim)
-    kp = _dev(k, "k", shape=shape)
-    vp = _dev(v, "v", dtype=k.dtype, shape=shape)
+    if cache.fmt in H32_FORMATS:
+        shape = (B, cache.num_kv_heads, cache.head_dim)
+        kp = _dev(k, "k", shape=shape)
+        vp = _dev(v, "v", dtype=k.dtype, shape=shape)
+    else:
+        if v is not None:
+            raise ValueError("the latent caches take no v")
+        kp = _dev(k, "k", shape=(B, cache.head_dim))
+        vp = None
     qp = _dev(q, "q", shape=(B, Hq, cache.head_dim))
     ptp = _dev(page_table, "page_table", dtype=torch.int32)
     if page_table.dim() != 2 or page_table.shape[0] != B:

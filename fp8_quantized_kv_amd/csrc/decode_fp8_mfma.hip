@@ -178,7 +178,16 @@ __device__ __forceinline__ int lds_row(int k) { return (k & 16) | ((k & 7) << 1)
 // 2^e for an integer e in [-126, 127], exactly.
 __device__ __forceinline__ float exp2i(int e) { return __uint_as_float(uint32_t(e + 127) << 23); }
 
-template <bool SEL, bool TQ>
+// STEP (kvq_decode_step, fp8 rows over consecutive positions): wave 0 of
+// each workgroup whose split holds position seq_lens[b] - 1 first stores
+// token b's latent row there, with the store kernel's arithmetic per element
+// (amax per part over fabsf, 448 / amax, e4m3_encode), so the bytes are the
+// same.  Both head-block workgroups of that split store the row, writing the
+// same bytes; each copies the row only after its own store is acknowledged:
+// at once when the row's tile is copied first (then a workgroup barrier), by
+// the prologue's full wait before tiles 1 and 2 are copied (then a barrier if
+// the row is in one of them), else long before (the barriers that follow).
+template <bool SEL, bool TQ, bool STEP = false>
 __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __restrict__ codes,
                                                             const float* __restrict__ scales, int page_size,
                                                             int num_pages, DecodeArgs a, TqMfmaTable tab) {
@@ -240,6 +249,47 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
     }
     const int n_keys = j1 - j0;
     const int n_tiles = (n_keys + kTile - 1) / kTile;
+
+    const int pos_new = T - 1;
+    const bool holds = STEP && T > 0 && pos_new >= j0 && pos_new < j1;  // workgroup-uniform
+    const int t_new = holds ? (pos_new - j0) / kTile : -1;               // the row's tile
+    // Wave 0: the token's row (lane: latent elements lane + 64 k, k < 8, and
+    // rope element lane) into its slot; a page outside the pool is not
+    // stored (kvq_store skips such a slot too).
+    auto store_token = [&](bool wait) {
+        float xv[9];
+        const int64_t base = int64_t(b) * kD + lane;
+        const void* x = a.step_k;
+        if (a.step_kv_dt == InType::F32) {
+#pragma unroll
+            for (int k = 0; k < 9; ++k) xv[k] = load_elem<InType::F32>(x, base + 64 * k);
+        } else if (a.step_kv_dt == InType::BF16) {
+#pragma unroll
+            for (int k = 0; k < 9; ++k) xv[k] = load_elem<InType::BF16>(x, base + 64 * k);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 9; ++k) xv[k] = load_elem<InType::F16>(x, base + 64 * k);
+        }
+        const int page = pt[pos_new / page_size];
+        if (page >= 0 && page < num_pages) {
+            const int64_t slot = int64_t(page) * page_size + pos_new % page_size;
+            uint8_t* out = const_cast<uint8_t*>(codes) + slot * kD;
+#pragma unroll
+            for (int part = 0; part < 2; ++part) {
+                const int k0 = part ? 8 : 0, nk = part ? 1 : 8;
+                float amax = 0.0f;
+                for (int k = k0; k < k0 + nk; ++k) amax = fmaxf(amax, fabsf(xv[k]));  // NaN ignored
+#pragma unroll
+                for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+                const float inv = 448.0f / amax;
+                const bool inert = !(amax > 0.0f) || !isfinite(amax) || !isfinite(inv);
+                for (int k = k0; k < k0 + nk; ++k)
+                    out[lane + 64 * k] = inert ? uint8_t(0) : uint8_t(e4m3_encode(xv[k] * inv));
+                if (lane == 0) const_cast<float*>(scales)[slot * 2 + part] = inert ? 0.0f : amax / 448.0f;
+            }
+        }
+        if (wait) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
 
     auto run_slot = [&](int r) -> int64_t {  // r is wave-uniform
         const int64_t v = r < 64 ? rslot[0] : rslot[1];
@@ -393,6 +443,8 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
     if constexpr (SEL) {
         load_tile(0);
     } else {
+        if (STEP && holds && wave == 0) store_token(t_new == 0);
+        if (STEP && holds && t_new == 0) __syncthreads();  // the row's tile is copied next
         issue_tile(0);  // tiles 1 and 2 after the query is in registers (its wait covers tile 0 only)
     }
 
@@ -418,7 +470,8 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
         store_tile(0);
         if (n_tiles > 1) load_tile(1);
     } else {
-        wait_vmcnt<0>();
+        wait_vmcnt<0>();  // (wave 0 of a STEP workgroup: also its stores of the new row)
+        if (STEP && holds && (t_new == 1 || t_new == 2)) __syncthreads();
         if (n_tiles > 1) issue_tile(1);
         if (n_tiles > 2) issue_tile(2);
         __syncthreads();  // tile 0 staged raw
@@ -614,6 +667,12 @@ bool decode_fp8_mfma_supported(const Fp8Pool& pool, const DecodeArgs& a) {
 hipError_t launch_decode_fp8_mfma(const Fp8Pool& pool, const DecodeArgs& a, hipStream_t s) {
     const dim3 grid(unsigned(a.n_splits), unsigned((a.n_q_heads + kHeadsWG - 1) / kHeadsWG), unsigned(a.batch));
     const TqMfmaTable none{};
+    if (a.step_k) {  // kvq_decode_step: dense rows only
+        if (a.sel) return hipErrorInvalidValue;
+        decode_fp8_mfma<false, false, true><<<grid, dim3(kThreads), 0, s>>>(pool.codes, pool.scales, pool.page_size,
+                                                                            pool.num_pages, a, none);
+        return hipGetLastError();
+    }
     if (a.sel)
         decode_fp8_mfma<true, false><<<grid, dim3(kThreads), 0, s>>>(pool.codes, pool.scales, pool.page_size,
                                                                      pool.num_pages, a, none);

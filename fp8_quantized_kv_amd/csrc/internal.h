@@ -271,6 +271,25 @@ __device__ __forceinline__ void encode_blk_quad(float (&x)[4], uint8_t* __restri
     if (j == 0) reinterpret_cast<uint16_t*>(row + (D / 32) * blk_group_bytes(BITS))[g] = __half_as_ushort(s16);
 }
 
+// e4m3 ("fn": bias 7, max 448) code of v, round to nearest even, saturating
+// to +-448, NaN -> 0x00, signed zero kept.  Bit manipulation on the fp32
+// encoding: the top 3 mantissa bits survive and the 20 below decide rounding.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return 0u;                 // NaN
+    if (a >= 0x43E00000u) return sign | 0x7Eu;      // |v| >= 448, incl. infinity
+    if (a < 0x3C800000u) {                          // |v| < 2^-6: spacing 2^-9
+        const float n = rintf(__uint_as_float(a) * 512.0f);  // exact scaling, then RNE
+        return sign | uint32_t(n);                  // n == 8 is the smallest normal
+    }
+    uint32_t code = ((((a >> 23) - 127u + 7u)) << 3) | ((a >> 20) & 7u);
+    const uint32_t rem = a & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) code += 1u;  // carry may bump the exponent
+    return sign | code;
+}
+
 // ------------------------------------------------------------------ launchers
 // Each returns the hipError_t of its launch; shapes are validated by the caller.
 

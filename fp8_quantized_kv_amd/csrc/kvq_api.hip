@@ -440,8 +440,11 @@ kvq_status kvq_decode_step(const kvq_cache* cache, const void* k, const void* v,
     st = check_decode_args(cache, n_q_heads, max_pages, seq_lens, batch, max_seq_len, sm_scale, split_keys);
     if (st != KVQ_OK) return st;
     if (!dtype_ok(kv_dtype) || !dtype_ok(q_dtype)) return KVQ_ERR_INVALID_ARG;
+    const bool latent = cache->format == KVQ_FMT_FP8_E4M3_ROW;  // one latent row a token, the f32 query as is
+    if (!latent && !is_h32(cache->format)) return KVQ_ERR_UNSUPPORTED;  // TQ4: no step form
+    if (latent && (v || q_dtype != KVQ_DT_F32)) return KVQ_ERR_INVALID_ARG;
     if (batch == 0) return KVQ_OK;
-    if (!aligned(k) || !aligned(v) || !aligned(q) || !aligned(page_table, 4) || !aligned(out) ||
+    if (!aligned(k) || (!latent && !aligned(v)) || !aligned(q) || !aligned(page_table, 4) || !aligned(out) ||
         (lse && !aligned(lse, 4)))
         return KVQ_ERR_INVALID_ARG;
     if (int64_t(batch) * n_q_heads > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
@@ -460,15 +463,22 @@ kvq_status kvq_decode_step(const kvq_cache* cache, const void* k, const void* v,
     d.step_kv_dt = static_cast<InType>(kv_dtype);
     d.step_q_dt = static_cast<InType>(q_dtype);
     // The kernel kvq_decode_attn would run (launch_decode_for), in its STEP form.
-    if (!is_h32(cache->format)) return KVQ_ERR_UNSUPPORTED;
-    const kvq::Q4Pool pool = q4_pool(cache);
-    if (pool.bits == 4 && kvq::decode_q4_pair_supported(pool, d))
-        st = launched(kvq::launch_decode_q4_pair(pool, d, stream));
-    else if (kvq::decode_q4_mfma_step_supported(pool, d)) st = launched(kvq::launch_decode_q4_mfma(pool, d, stream));
-    else return KVQ_ERR_UNSUPPORTED;
+    if (latent) {
+        d.q = static_cast<const float*>(q);
+        const kvq::Fp8Pool pool = fp8_pool(cache);
+        if (!kvq::decode_fp8_mfma_supported(pool, d)) return KVQ_ERR_UNSUPPORTED;
+        st = launched(kvq::launch_decode_fp8_mfma(pool, d, stream));
+    } else {
+        const kvq::Q4Pool pool = q4_pool(cache);
+        if (pool.bits == 4 && kvq::decode_q4_pair_supported(pool, d))
+            st = launched(kvq::launch_decode_q4_pair(pool, d, stream));
+        else if (kvq::decode_q4_mfma_step_supported(pool, d))
+            st = launched(kvq::launch_decode_q4_mfma(pool, d, stream));
+        else return KVQ_ERR_UNSUPPORTED;
+    }
     if (st != KVQ_OK) return st;
     const kvq::MergeArgs m{pa, pm, pz, seq_lens, batch, n_q_heads, max_seq_len, S, split_keys, value_dim(cache),
-                           true, out, lse};
+                           is_h32(cache->format), out, lse};
     return launch_merge_for(cache, m, stream);
 }
 

@@ -375,11 +375,20 @@ kvq_status kvq_attend(const kvq_cache* cache, const float* q, int32_t n_q_heads,
  * to kvq_store_rotate_q (that slot mapping, n_tokens = batch, n_rows =
  * batch * n_q_heads) followed by kvq_attend on the rotated query, and the
  * workspace holds the same partials.  The positions T_b - 1 of different
- * sequences must map to different slots.  k, v, q, out: 16-byte aligned.
+ * sequences must map to different slots, and none of those slots may be one
+ * that another sequence of the batch reads (a page shared below its length).
+ * k, v, q, out: 16-byte aligned.
+ * FP8 (the KV8 commit of the colibri pull request: one e4m3 latent row per
+ * token, no rotation): k is the latent rows [batch][head_dim] of kv_dtype,
+ * v is NULL, q is [batch][n_q_heads][head_dim] f32 (q_dtype KVQ_DT_F32) as
+ * kvq_attend takes it; the stored bytes and scales and out / lse are
+ * bit-identical to kvq_store (that slot mapping) followed by kvq_attend.
+ * KVQ_ERR_INVALID_ARG for a non-NULL v or another q_dtype with FP8.
  * KVQ_ERR_UNSUPPORTED outside the kernels that carry the step (formats Q4,
  * Q8 and Q6 at head_dim 256, groups of at most 8 query heads, pages of a
- * multiple of 16 tokens, split_keys at most 8192): call kvq_store_rotate_q
- * and kvq_attend instead. */
+ * multiple of 16 tokens, split_keys at most 8192; FP8 at head_dim 576 with
+ * rope_dim 64, pages of a multiple of 16 tokens, split_keys at most 2048;
+ * not TQ4): call kvq_store_rotate_q (kvq_store) and kvq_attend instead. */
 kvq_status kvq_decode_step(const kvq_cache* cache, const void* k, const void* v, int32_t kv_dtype, const void* q,
                            int32_t q_dtype, int32_t n_q_heads, const int32_t* page_table, int32_t max_pages,
                            const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
