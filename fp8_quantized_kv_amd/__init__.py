@@ -411,7 +411,7 @@ def kvq_decode_attn_sel(cache, q, page_table, sel, n_sel, sm_scale, split_keys, 
 
 def kvq_merge(cache, part_acc, part_m, part_z, seq_lens, max_seq_len, split_keys, out=None, lse=None,
               want_lse=True):
-    """Log-sum-exp merge of the partials, then (Q4) the inverse rotation.  Returns (out, lse)."""
+    """Log-sum-exp merge of the partials, then (Q4, Q8, Q6, TQ4) the inverse rotation.  Returns (out, lse)."""
     B, Hq, S, Dv = part_acc.shape
     if out is None:
         out = torch.empty((B, Hq, Dv), dtype=torch.float32, device=part_acc.device)

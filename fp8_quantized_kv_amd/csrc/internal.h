@@ -467,6 +467,10 @@ struct MergeArgs {
 };
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+// TQ4 latent rows (dv 512, a.rotate false): the merge and the inverse rotation
+// of the merged context in one launch, the bits of launch_merge followed by
+// launch_tq_rotate(out, out, rows, 512, inverse).
+hipError_t launch_merge_tq(const MergeArgs& a, hipStream_t s);
 
 // Read-bandwidth measurement (bytes a multiple of 16 KiB): XOR of every
 // 32-bit word of src folded into *xor_out.

@@ -117,11 +117,10 @@ kvq_status check_decode_args(const kvq_cache* cache, int32_t n_q_heads, int32_t 
 // Output channels of a cache's attention (the merge's Dv).
 int32_t value_dim(const kvq_cache* c) { return is_h32(c->format) ? c->head_dim : c->head_dim - c->rope_dim; }
 
-// The merge (and, for TQ4, the inverse rotation after it) of validated arguments.
+// The merge (and, for TQ4, the inverse rotation in the same launch) of validated arguments.
 kvq_status launch_merge_for(const kvq_cache* cache, const kvq::MergeArgs& a, hipStream_t stream) {
-    kvq_status st = launched(kvq::launch_merge(a, stream));
-    if (st != KVQ_OK || cache->format != KVQ_FMT_TQ4_LATENT) return st;
-    return launched(kvq::launch_tq_rotate(a.out, a.out, int64_t(a.batch) * a.n_q_heads, 512, true, stream));
+    if (cache->format == KVQ_FMT_TQ4_LATENT) return launched(kvq::launch_merge_tq(a, stream));
+    return launched(kvq::launch_merge(a, stream));
 }
 
 // Partials of kvq_attend inside its workspace: part_acc [B][H_q][S][Dv], then

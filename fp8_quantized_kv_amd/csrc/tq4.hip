@@ -416,6 +416,119 @@ __global__ __launch_bounds__(kTT) void decode_tq4_simple(const uint8_t* __restri
     }
 }
 
+// ---- merge + inverse rotation in one launch ------------------------------
+// The log-sum-exp merge of the split-T partials (colibri pull request,
+// split-T commit) followed by rotating the merged latent context back
+// ("rotate the output back once"), for one (sequence x query head) row per
+// workgroup of 16 waves.  The merge's arithmetic is merge_kernel's, term
+// for term: M is the exact maximum of the used splits' m; w_s = exp(m_s - M)
+// for z_s > 0, else 0; Z sums z_s w_s over s = lane, lane + 64, ... in
+// ascending order per lane, then a lane-xor butterfly (every wave alike);
+// wave w sums acc_s[c] w_s over s = (w & 3) + 4k ascending, for channels
+// 128 (w >> 2) + lane and 128 (w >> 2) + 64 + lane, as merge_kernel's wave
+// w & 3 does for the 64-channel block holding c; the four sums are added in
+// order and divided by Z.  (One 8-byte load per lane and split for two
+// adjacent channels instead ran slower: 9.7 against 8.4 us per launch.)  Wave 0 then rotates the row back with
+// rotate_part (lane l: elements 8l .. 8l + 7), as tq_rotate_rows does on
+// merge_kernel's output, so out and lse have the bits of the two launches.
+constexpr int kMtWaves = 16;
+constexpr int kMtBatch = 32;  // partial loads in flight per lane and channel
+constexpr int kMtZPre = 4;    // z_s preloaded per lane (s < 256)
+
+__global__ __launch_bounds__(kMtWaves * 64) void merge_tq_kernel(const float* __restrict__ part_acc,
+                                                                 const float* __restrict__ part_m,
+                                                                 const float* __restrict__ part_z,
+                                                                 const int32_t* __restrict__ seq_lens, int n_q_heads,
+                                                                 int max_seq_len, int S, int split_keys,
+                                                                 float* __restrict__ out, float* __restrict__ lse) {
+    extern __shared__ float w[];  // [S] split weights
+    __shared__ float part[4][kTL];
+    __shared__ float red[kMtWaves];
+
+    const int bh = blockIdx.x;
+    const int b = bh / n_q_heads;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int sw = wave & 3, cb = wave >> 2;
+    const float* pm = part_m + int64_t(bh) * S;
+    const float* pz = part_z + int64_t(bh) * S;
+    const float* pa = part_acc + int64_t(bh) * S * kTL + 128 * cb + lane;
+
+    // loads that do not need the sequence length (one memory round trip)
+    int T = seq_lens[b];
+    float v0[kMtBatch], v1[kMtBatch];
+#pragma unroll
+    for (int k = 0; k < kMtBatch; ++k) {
+        const int sk = sw + 4 * k;
+        v0[k] = sk < S ? pa[int64_t(sk) * kTL] : 0.0f;
+        v1[k] = sk < S ? pa[int64_t(sk) * kTL + 64] : 0.0f;
+    }
+    const float my_m = tid < S ? pm[tid] : -INFINITY;
+    const float my_z = tid < S ? pz[tid] : 0.0f;
+    float zl[kMtZPre];
+#pragma unroll
+    for (int k = 0; k < kMtZPre; ++k) zl[k] = lane + 64 * k < S ? pz[lane + 64 * k] : 0.0f;
+
+    T = T < 0 ? 0 : (T > max_seq_len ? max_seq_len : T);
+    const int n = (T + split_keys - 1) / split_keys;  // workgroup-uniform
+    float M = -INFINITY, z = 0.0f;
+    if (n > 0) {
+        float mx = tid < n ? my_m : -INFINITY;
+        for (int s = tid + kMtWaves * 64; s < n; s += kMtWaves * 64) mx = fmaxf(mx, pm[s]);
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+        if (lane == 0) red[wave] = mx;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kMtWaves; ++i) M = fmaxf(M, red[i]);  // exact: any order
+        if (tid < n) w[tid] = my_z > 0.0f ? expf(my_m - M) : 0.0f;
+        for (int s = tid + kMtWaves * 64; s < n; s += kMtWaves * 64) w[s] = pz[s] > 0.0f ? expf(pm[s] - M) : 0.0f;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kMtZPre; ++k)
+            if (lane + 64 * k < n) z += zl[k] * w[lane + 64 * k];
+        for (int s = lane + 64 * kMtZPre; s < n; s += 64) z += pz[s] * w[s];
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) z += __shfl_xor(z, m, 64);
+        float acc0 = 0.0f, acc1 = 0.0f;
+        for (int k0 = 0; sw + 4 * k0 < n; k0 += kMtBatch) {
+            if (k0 > 0) {
+#pragma unroll
+                for (int k = 0; k < kMtBatch; ++k) {
+                    const int sk = sw + 4 * (k0 + k);
+                    v0[k] = sk < n ? pa[int64_t(sk) * kTL] : 0.0f;
+                    v1[k] = sk < n ? pa[int64_t(sk) * kTL + 64] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kMtBatch; ++k) {
+                const int sk = sw + 4 * (k0 + k);
+                if (sk < n) {
+                    acc0 += v0[k] * w[sk];
+                    acc1 += v1[k] * w[sk];
+                }
+            }
+        }
+        part[sw][128 * cb + lane] = acc0;
+        part[sw][128 * cb + 64 + lane] = acc1;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    // Z = 0 (no split holds a key) and T = 0 give a zero context, rotated like any other
+    const bool any = n > 0 && z > 0.0f;
+    float r[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int j = 8 * lane + e;
+        r[e] = any ? (((part[0][j] + part[1][j]) + part[2][j]) + part[3][j]) / z : 0.0f;
+    }
+    rotate_part<kTL>(r, lane, kSeedLatent, true);
+    float* o = out + int64_t(bh) * kTL + 8 * lane;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = r[e];
+    if (lse && lane == 0) lse[bh] = any ? M + logf(z) : -INFINITY;
+}
+
 }  // namespace
 
 // The value of a double rounded to the nearest f16 (ties to even), for
@@ -518,6 +631,15 @@ hipError_t launch_store_rotate_tq4(const Fp8Pool& pool, const void* x, InType dt
 hipError_t launch_tq_rotate(const float* x, float* y, int64_t n_rows, int row_len, bool inverse, hipStream_t s) {
     if (n_rows == 0) return hipSuccess;
     tq_rotate_rows<<<dim3(unsigned(n_rows)), dim3(64), 0, s>>>(x, y, n_rows, row_len, inverse ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge_tq(const MergeArgs& a, hipStream_t s) {
+    if (a.batch == 0) return hipSuccess;
+    if (a.dv != kTL || a.rotate) return hipErrorInvalidValue;
+    merge_tq_kernel<<<dim3(unsigned(a.batch * a.n_q_heads)), dim3(kMtWaves * 64), sizeof(float) * size_t(a.n_splits),
+                      s>>>(a.part_acc, a.part_m, a.part_z, a.seq_lens, a.n_q_heads, a.max_seq_len, a.n_splits,
+                           a.split_keys, a.out, a.lse);
     return hipGetLastError();
 }
 

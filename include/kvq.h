@@ -319,8 +319,8 @@ kvq_status kvq_decode_attn_sel(const kvq_cache* cache, const float* q, int32_t n
  * followed for Q4 by the single inverse rotation (H32 is its own inverse):
  *   M = max_s m_s, Z = sum_s z_s exp(m_s - M),
  *   out = R( sum_s acc_s exp(m_s - M) / Z ),  R = H32 (Q4/Q8/Q6), the inverse
- *   of the latent part's randomized Hadamard transform (TQ4, a second launch
- *   on out) or identity (FP8),
+ *   of the latent part's randomized Hadamard transform (TQ4, in the same
+ *   launch: one workgroup per row) or identity (FP8),
  *   lse = M + log Z.
  * A sequence with T = 0 gives out = 0 and lse = -inf.  Only the splits that
  * cover [0, T_b) are read.  inverse_rotate must be 1 for the rotated formats

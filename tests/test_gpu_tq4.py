@@ -138,3 +138,45 @@ def test_tq4_store_rotate_one_launch(kvq):
     torch.cuda.synchronize()
     assert torch.equal(qc.view(torch.int32), qa.view(torch.int32))
     assert torch.equal(c.codes, a.codes) and torch.equal(c.scales.view(torch.int32), a.scales.view(torch.int32))
+
+
+def _unrotate_f32(y):
+    """The codec's inverse rotation of 512-wide rows in fp32, stage by stage
+    (colibri pull request, Summary "Why rotated-int4 for the 4-bit tier"):
+    the Sylvester butterfly (a + b, a - b) for h = 1 .. 256, times
+    fp32(1/sqrt(512)), times the part's signs.  numpy float32 rounds each
+    step as the kernel does."""
+    v = np.array(y, dtype=np.float32).reshape(-1, 512).copy()
+    h = 1
+    while h < 512:
+        x = v.reshape(-1, 512 // (2 * h), 2, h)
+        a, b = x[:, :, 0, :].copy(), x[:, :, 1, :].copy()
+        x[:, :, 0, :] = a + b
+        x[:, :, 1, :] = a - b
+        v = x.reshape(-1, 512)
+        h *= 2
+    c = np.float32(1.0 / np.sqrt(512.0))
+    return ((v * c) * oracle.tq_signs(0, 512)).astype(np.float32)
+
+
+# (split, lens): 33000 positions at split 32 give 1032 splits (the merge's
+# maximum past 1024, Z terms past 256, partial batches past 128 splits a
+# lane); an empty sequence gives a zero context, rotated like any other.
+@pytest.mark.parametrize("split,lens", [(2048, [3000, 0, 700, 33]), (32, [33000, 9000, 1])])
+def test_tq4_merge_rotates_back_in_one_launch(kvq, split, lens):
+    """kvq_merge on a TQ4 cache (merge and inverse rotation in one launch)
+    against the plain merge of the same partials (an FP8 cache descriptor,
+    no rotation) followed by the inverse rotation in numpy fp32: out and lse
+    bit for bit."""
+    w = wl.shrink(wl.MLA_262K, n_heads=20, seq_len=0)
+    t = TqCase(w, lens, build_oracle=False, n_heads=20)
+    _say(f"tq4 merge split={split} lens={lens}")
+    q_rot = kvq.kvq_tq_rotate_q(t.q)
+    pa, pm, pz = kvq.kvq_decode_attn(t.cache, q_rot, t.page_table, t.seq_lens, t.max_seq_len, w.sm_scale, split)
+    out, lse = kvq.kvq_merge(t.cache, pa, pm, pz, t.seq_lens, t.max_seq_len, split)
+    plain = kvq.Fp8Cache(1, 576, 64, w.page_size, "cuda")  # the same merge without a rotation
+    o_plain, l_plain = kvq.kvq_merge(plain, pa, pm, pz, t.seq_lens, t.max_seq_len, split)
+    torch.cuda.synchronize()
+    ref = _unrotate_f32(o_plain.cpu().numpy()).reshape(tuple(out.shape))
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    assert torch.equal(lse.view(torch.int32), l_plain.view(torch.int32))
