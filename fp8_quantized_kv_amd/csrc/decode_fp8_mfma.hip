@@ -501,32 +501,46 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
         // ---- partial scores over this wave's 9 groups: two 16-key blocks;
         // lane holds keys 16 kb + 4 q4 + i of head n16.  Groups 0..6 are
         // latent for both halves; 7 and 8 are latent (first half) or rope.
+        // The 18 A operands are read from LDS kAhead steps ahead of their
+        // MFMAs (the order is pinned by scheduling barriers: left to itself
+        // the compiler read two and waited for them before each pair of
+        // groups), and both blocks' scale factors are applied after all 36
+        // MFMAs are issued, so that work overlaps the last ones.
         float part[2][4], scl[2][4];
+        {
+            constexpr int kSteps = 2 * kQG, kAhead = 3;
+            const float4* sp = reinterpret_cast<const float4*>(st + kScaleOff + 8 * (4 * q4));
+            const float4 s01[2] = {sp[0], sp[8]}, s23[2] = {sp[1], sp[9]};  // keys 16 kb + 4 q4 + 0..3 (8 bytes a key)
+            const uint8_t* krow[2] = {st + lds_row(n16) * kPitch + 2 * (32 * g0 + 8 * q4),
+                                      st + lds_row(16 + n16) * kPitch + 2 * (32 * g0 + 8 * q4)};
+            half8_t av[kSteps];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const uint8_t* krow = st + lds_row(16 * kb + n16) * kPitch + 2 * (32 * g0 + 8 * q4);
-            f32x4 accE = {0.0f, 0.0f, 0.0f, 0.0f}, accO = accE, acc78 = accE;
+            for (int j = 0; j < kAhead; ++j) av[j] = *reinterpret_cast<const half8_t*>(krow[j / kQG] + 64 * (j % kQG));
+            f32x4 acc[2][3];
 #pragma unroll
-            for (int gl = 0; gl < kQG; ++gl) {
-                const half8_t av = *reinterpret_cast<const half8_t*>(krow + 64 * gl);
-                if (gl >= 7) {
-                    acc78 = mfma(av, bq_hi[gl], acc78);
-                    acc78 = mfma(av, bq_lo[gl], acc78);
-                } else if (gl & 1) {
-                    accO = mfma(av, bq_hi[gl], accO);
-                    accO = mfma(av, bq_lo[gl], accO);
-                } else {
-                    accE = mfma(av, bq_hi[gl], accE);
-                    accE = mfma(av, bq_lo[gl], accE);
-                }
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int c = 0; c < 3; ++c) acc[kb][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int j = 0; j < kSteps; ++j) {
+                if (j + kAhead < kSteps)
+                    av[j + kAhead] = *reinterpret_cast<const half8_t*>(krow[(j + kAhead) / kQG] +
+                                                                       64 * ((j + kAhead) % kQG));
+                const int kb = j / kQG, gl = j % kQG;
+                const int c = gl >= 7 ? 2 : (gl & 1);  // chains: even groups, odd groups, groups 7 and 8
+                acc[kb][c] = mfma(av[j], bq_hi[gl], acc[kb][c]);
+                acc[kb][c] = mfma(av[j], bq_lo[gl], acc[kb][c]);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            const float4* sp = reinterpret_cast<const float4*>(st + kScaleOff + 8 * (16 * kb + 4 * q4));
-            const float4 s01 = sp[0], s23 = sp[1];
-            const float sl[4] = {s01.x, s01.z, s23.x, s23.z}, sr[4] = {s01.y, s01.w, s23.y, s23.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                part[kb][i] = sl[i] * (accE[i] + accO[i]) + (half ? sr[i] : sl[i]) * acc78[i];
-                scl[kb][i] = sl[i];
+            for (int kb = 0; kb < 2; ++kb) {
+                const float sl[4] = {s01[kb].x, s01[kb].z, s23[kb].x, s23[kb].z};
+                const float sr[4] = {s01[kb].y, s01[kb].w, s23[kb].y, s23[kb].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    part[kb][i] = sl[i] * (acc[kb][0][i] + acc[kb][1][i]) + (half ? sr[i] : sl[i]) * acc[kb][2][i];
+                    scl[kb][i] = sl[i];
+                }
             }
         }
         // ---- the pair's scores: first half's partial + second half's, in both waves
@@ -613,15 +627,27 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
                 av[4 * kb + i] = _Float16(p * (scl[kb][i] * sfac));
             }
 
-        // ---- context: this wave's 16 blocks of 16 latent channels
+        // ---- context: this wave's 16 blocks of 16 latent channels (each
+        // block's two transposed reads issued kAhead blocks before its MFMA)
+        {
+            constexpr int kAhead = 4;
+            i16x4 v0[kNBW], v1[kNBW];
+            auto read_blk = [&](int cb) {
+                v0[cb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4*)(st + tr_off + 32 * cb));
+                v1[cb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4*)(st + tr_off + 16 * kPitch + 32 * cb));
+            };
 #pragma unroll
-        for (int cb = 0; cb < kNBW; ++cb) {
-            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(st + tr_off + 32 * cb));
-            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(st + tr_off + 16 * kPitch + 32 * cb));
-            const half8_t bv = __builtin_bit_cast(half8_t, i16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-            o[cb] = mfma(av, bv, o[cb]);
+            for (int cb = 0; cb < kAhead; ++cb) read_blk(cb);
+#pragma unroll
+            for (int cb = 0; cb < kNBW; ++cb) {
+                if (cb + kAhead < kNBW) read_blk(cb + kAhead);
+                const half8_t bv = __builtin_bit_cast(
+                    half8_t, i16x8{v0[cb][0], v0[cb][1], v0[cb][2], v0[cb][3], v1[cb][0], v1[cb][1], v1[cb][2], v1[cb][3]});
+                o[cb] = mfma(av, bv, o[cb]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
 
         // ---- next tile: registers -> LDS (the other stage), then the one after into registers
