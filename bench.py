@@ -42,6 +42,11 @@ TRAFFIC = {
     "cb49a6e0450434563dceb0d3d89e053cb4eb6254b14d2ed8c71e106d5196a936": {
         "fetch_kib": 147708.5, "write_kib": 3264.0, "fetch_scale": 2.0, "write_scale": 1.0,
         "profile": "profiles/decode_q4_mfma_gqa_q4_262k.md"},
+    # the same counters: these sources add the 8- and 6-bit step forms, and the 4-bit
+    # instantiations compile to the same instructions as those of the key above
+    "ac089d7e295e717113db3d57be593225a95ce96e804d6331cb38e6dce4e76b79": {
+        "fetch_kib": 147708.5, "write_kib": 3264.0, "fetch_scale": 2.0, "write_scale": 1.0,
+        "profile": "profiles/decode_q4_mfma_gqa_q4_262k.md"},
 }
 DECODE_SOURCES = (os.path.join("fp8_quantized_kv_amd", "csrc", "decode_q4_mfma.hip"),
                   os.path.join("fp8_quantized_kv_amd", "csrc", "mfma_common.h"))
