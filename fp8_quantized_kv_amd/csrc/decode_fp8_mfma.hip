@@ -514,6 +514,10 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
             const uint8_t* krow[2] = {st + lds_row(n16) * kPitch + 2 * (32 * g0 + 8 * q4),
                                       st + lds_row(16 + n16) * kPitch + 2 * (32 * g0 + 8 * q4)};
             half8_t av[kSteps];
+            // Raised issue priority while this wave feeds its score MFMAs (the other wave
+            // of the SIMD is then mostly in its vector work): 151 vs 152.6 us at 262K;
+            // raising it for the context MFMAs as well was slower (155 us).
+            __builtin_amdgcn_s_setprio(2);
 #pragma unroll
             for (int j = 0; j < kAhead; ++j) av[j] = *reinterpret_cast<const half8_t*>(krow[j / kQG] + 64 * (j % kQG));
             f32x4 acc[2][3];
@@ -532,6 +536,7 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
                 acc[kb][c] = mfma(av[j], bq_lo[gl], acc[kb][c]);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_s_setprio(0);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 const float sl[4] = {s01[kb].x, s01[kb].z, s23[kb].x, s23[kb].z};
