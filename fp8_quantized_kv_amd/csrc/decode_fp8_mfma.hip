@@ -543,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
                 const float sr[4] = {s01[kb].y, s01[kb].w, s23[kb].y, s23[kb].w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    part[kb][i] = sl[i] * (acc[kb][0][i] + acc[kb][1][i]) + (half ? sr[i] : sl[i]) * acc[kb][2][i];
+                    part[kb][i] = fmaf(half ? sr[i] : sl[i], acc[kb][2][i], sl[i] * (acc[kb][0][i] + acc[kb][1][i]));
                     scl[kb][i] = sl[i];
                 }
             }
