@@ -288,3 +288,37 @@ def test_attend_workspace_and_argument_checks(kvq):
     assert call(out=A + 8) == INVALID                # misaligned out
     assert call(split=500) == INVALID                # split_keys % 512
     assert call(batch=0) == 0                        # nothing to do
+
+
+def test_decode_step_argument_checks(kvq):
+    """kvq_decode_step: the host checks and the configurations without a step
+    kernel, all refused before any launch (Q4 at head_dim 128, groups of 12
+    heads, the fp8 latent rows with a V pointer, a non-f32 query or splits past
+    the matrix-core kernel's 2048 keys, the TQ4 latent format)."""
+    L = kvq.lib
+    P = ctypes.c_void_p
+    f = ctypes.c_float(0.0625)
+
+    def call(desc, v=A + 0x10000, qdt=0, heads=24, split=512, ws=A + 0x200000, nbytes=None, batch=2, out=A + 0x300000):
+        if nbytes is None:
+            nbytes = L.kvq_attend_workspace_bytes(ctypes.byref(desc), batch, heads, 1024, split)
+        return L.kvq_decode_step(ctypes.byref(desc), P(A), None if v is None else P(v), 1, P(A + 0x20000), qdt,
+                                 heads, P(A + 0x30000), 64, P(A + 0x40000), batch, 1024, f, split, P(ws), nbytes,
+                                 P(out), P(A + 0x400000), None)
+    d = _q4(kvq)
+    assert call(d, nbytes=L.kvq_attend_workspace_bytes(ctypes.byref(d), 2, 24, 1024, 512) - 1) == INVALID
+    assert call(d, ws=A + 0x200010) == INVALID           # workspace not 256-byte aligned
+    assert call(d, out=A + 8) == INVALID                 # misaligned out
+    assert call(d, v=A + 4) == INVALID                   # misaligned v
+    assert call(d, qdt=7) == INVALID                     # unknown query dtype
+    assert call(d, batch=0) == 0                         # nothing to do
+    assert call(_q4(kvq, head_dim=128)) == UNSUPPORTED   # the step forms are built for head_dim 256
+    assert call(d, heads=48) == UNSUPPORTED              # groups of 12 query heads
+    e = _fp8(kvq)
+    assert call(e, heads=128) == INVALID                 # latent rows take no V
+    assert call(e, v=None, heads=128, qdt=1) == INVALID  # the latent query is f32
+    assert call(e, v=None, heads=128, split=4096) == UNSUPPORTED
+    assert call(e, v=None, heads=128, batch=0) == 0
+    t = kvq.KvqCacheDesc(format=kvq.FMT_TQ4_LATENT, num_kv_heads=1, head_dim=576, rope_dim=64, page_size=16,
+                         num_pages=64, k_pool=A, v_pool=None, scale_pool=A + 0x100000)
+    assert call(t, v=None, heads=128) == UNSUPPORTED
