@@ -421,18 +421,69 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
                              raw + uint32_t(RW::kScaleOff + 128 * run));
         }
     };
-    // Dense rows: this thread's chunks of tile t, raw stage -> registers, for store_tile.
-    auto raw_to_stg = [&](int t) {
+    // Dense rows, the conversion split so that it can sit between the context
+    // MFMAs: every thread reads its kFull chunks (tid + 512 i, always in the
+    // tile), the first kRemWaves waves one more code chunk, threads 128..143 a
+    // scale chunk (wave-uniform conditions but for that one), all before any
+    // is used; NaN codes are cleared in one test over all of a thread's chunks
+    // (clear_nan_codes leaves chunks without one as they are, so the bytes are
+    // those of the per-chunk test); then each chunk is converted on its own.
+    constexpr int kFull = R::kChunks / kThreads, kRemWaves = (R::kChunks % kThreads) / 64;
+    static_assert(R::kChunks % 64 == 0 && kRemWaves <= 2 && kFull + 1 == kPerThread, "dense chunk mapping");
+    auto dense_read = [&](int t) {
         using RW = Raw<TQ>;
         const uint8_t* rw = smem + kRawOff + (t % kRawStages) * RW::kStage;
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            if (tid + kThreads * i < kChunks)
-                stg[i] = *reinterpret_cast<const u32x4*>(rw + 16 * (tid + kThreads * i));
-            else if (has_scale)
-                stg[i] = *reinterpret_cast<const u32x4*>(rw + RW::kScaleOff + 16 * (tid - 128));
+        for (int i = 0; i < kFull; ++i) stg[i] = *reinterpret_cast<const u32x4*>(rw + 16 * (tid + kThreads * i));
+        if (wave < kRemWaves)
+            stg[kFull] = *reinterpret_cast<const u32x4*>(rw + 16 * (tid + kThreads * kFull));
+        else if (has_scale)
+            stg[kFull] = *reinterpret_cast<const u32x4*>(rw + RW::kScaleOff + 16 * (tid - 128));
+    };
+    auto dense_clear_nan = [&]() {
+        if constexpr (!TQ) {
+            uint32_t any = 0u;
+#pragma unroll
+            for (int i = 0; i < kPerThread; ++i)
+                if (i < kFull || wave < kRemWaves) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) any |= (stg[i][e] & 0x7F7F7F7Fu) + 0x01010101u;
+                }
+            if (any & 0x80808080u) {  // rare
+#pragma unroll
+                for (int i = 0; i < kPerThread; ++i)
+                    if (i < kFull || wave < kRemWaves) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) stg[i][e] = clear_nan_codes(stg[i][e]);
+                    }
+            }
         }
     };
+    // slot i of this thread into f16 stage t & 1 (slot kFull: the remainder code chunk or the scales)
+    auto dense_convert = [&](int t, int i) {
+        uint8_t* st = smem + (t & 1) * kStage;
+        const bool code = i < kFull || wave < kRemWaves;
+        if (code && TQ) {
+            uint32_t d[16];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tq_cvt8(stg[i][e], tab.lo, tab.hi, d + 4 * e);
+            u32x4* dst = reinterpret_cast<u32x4*>(st + lds_row(chunk_row(i)) * kPitch + 64 * chunk_col(i));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[e] = u32x4{d[4 * e], d[4 * e + 1], d[4 * e + 2], d[4 * e + 3]};
+        } else if (code) {
+            half8_t* d = reinterpret_cast<half8_t*>(st + lds_row(chunk_row(i)) * kPitch + 32 * chunk_col(i));
+            d[0] = cvt8(stg[i][0], stg[i][1]);
+            d[1] = cvt8(stg[i][2], stg[i][3]);
+        } else if (has_scale) {
+            if (TQ)
+                *reinterpret_cast<float4*>(st + kScaleOff + 16 * (tid - 128)) =
+                    make_float4(__uint_as_float(stg[i][0]) * tab.f_latent, __uint_as_float(stg[i][1]) * tab.f_rope,
+                                __uint_as_float(stg[i][2]) * tab.f_latent, __uint_as_float(stg[i][3]) * tab.f_rope);
+            else
+                *reinterpret_cast<u32x4*>(st + kScaleOff + 16 * (tid - 128)) = stg[i];
+        }
+    };
+
     // Own DMAs of the tile before the newest landed (the newest may be in flight).
     auto wait_own = [&](bool newest_in_flight) {
         if (!newest_in_flight) wait_vmcnt<0>();
@@ -475,8 +526,10 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
         if (n_tiles > 1) issue_tile(1);
         if (n_tiles > 2) issue_tile(2);
         __syncthreads();  // tile 0 staged raw
-        raw_to_stg(0);
-        store_tile(0);
+        dense_read(0);
+        dense_clear_nan();
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) dense_convert(0, i);
     }
     __syncthreads();
 
@@ -556,6 +609,7 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
         }
         if (!SEL && t + 1 < n_tiles) wait_own(t + 2 < n_tiles);  // tile t + 1 raw, own part
         __syncthreads();  // partial scores exchanged (dense rows: tile t + 1 staged raw)
+        if (!SEL && !TQ && t + 1 < n_tiles) dense_read(t + 1);  // converted between the context MFMAs
         float sc[2][4];
         {
             const float4* xp = reinterpret_cast<const float4*>(xpart);
@@ -643,11 +697,16 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
                 v1[cb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) i16x4*)(st + tr_off + 16 * kPitch + 32 * cb));
             };
+            // fp8 dense rows: tile t + 1 is converted here (the TQ4 levels' heavier conversion
+            // measured slower between the MFMAs, 173.7 vs 159.8 us, and runs after them)
+            const bool next = !SEL && !TQ && t + 1 < n_tiles;
+            if (next) dense_clear_nan();
 #pragma unroll
             for (int cb = 0; cb < kAhead; ++cb) read_blk(cb);
 #pragma unroll
             for (int cb = 0; cb < kNBW; ++cb) {
                 if (cb + kAhead < kNBW) read_blk(cb + kAhead);
+                if (next && cb % 5 == 2 && cb / 5 < kPerThread) dense_convert(t + 1, cb / 5);
                 const half8_t bv = __builtin_bit_cast(
                     half8_t, i16x8{v0[cb][0], v0[cb][1], v0[cb][2], v0[cb][3], v1[cb][0], v1[cb][1], v1[cb][2], v1[cb][3]});
                 o[cb] = mfma(av, bv, o[cb]);
@@ -660,11 +719,12 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
             if (t + 1 < n_tiles) store_tile(t + 1);
             if (t + 2 < n_tiles) load_tile(t + 2);
         } else {
-            if (t + 1 < n_tiles) {
-                raw_to_stg(t + 1);
-                store_tile(t + 1);
+            if (TQ && t + 1 < n_tiles) {
+                dense_read(t + 1);
+#pragma unroll
+                for (int i = 0; i < kPerThread; ++i) dense_convert(t + 1, i);
             }
-            if (t + 3 < n_tiles) issue_tile(t + 3);  // into the raw stage of tile t, converted before
+            if (t + 3 < n_tiles) issue_tile(t + 3);  // into the raw stage of tile t, converted before  // into the raw stage of tile t, converted before
         }
         __syncthreads();
     }
