@@ -475,7 +475,9 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
             d[0] = cvt8(stg[i][0], stg[i][1]);
             d[1] = cvt8(stg[i][2], stg[i][3]);
         } else if (has_scale) {
-            if (TQ)
+            if (SEL)  // selected rows: one row's scale pair a thread
+                *reinterpret_cast<uint2*>(st + kScaleOff + 8 * (tid - 128)) = make_uint2(stg[i][0], stg[i][1]);
+            else if (TQ)
                 *reinterpret_cast<float4*>(st + kScaleOff + 16 * (tid - 128)) =
                     make_float4(__uint_as_float(stg[i][0]) * tab.f_latent, __uint_as_float(stg[i][1]) * tab.f_rope,
                                 __uint_as_float(stg[i][2]) * tab.f_latent, __uint_as_float(stg[i][3]) * tab.f_rope);
@@ -697,9 +699,10 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
                 v1[cb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) i16x4*)(st + tr_off + 16 * kPitch + 32 * cb));
             };
-            // fp8 dense rows: tile t + 1 is converted here (the TQ4 levels' heavier conversion
-            // measured slower between the MFMAs, 173.7 vs 159.8 us, and runs after them)
-            const bool next = !SEL && !TQ && t + 1 < n_tiles;
+            // fp8 rows (dense, or selected: loaded into registers an iteration ahead): tile
+            // t + 1 is converted here (the TQ4 levels' heavier conversion measured slower
+            // between the MFMAs, 173.7 vs 159.8 us, and runs after them)
+            const bool next = !TQ && t + 1 < n_tiles;
             if (next) dense_clear_nan();
 #pragma unroll
             for (int cb = 0; cb < kAhead; ++cb) read_blk(cb);
@@ -716,8 +719,7 @@ __global__ __launch_bounds__(kThreads) void decode_fp8_mfma(const uint8_t* __res
 
         // ---- next tile: registers -> LDS (the other stage), then the one after into registers
         if constexpr (SEL) {
-            if (t + 1 < n_tiles) store_tile(t + 1);
-            if (t + 2 < n_tiles) load_tile(t + 2);
+            if (t + 2 < n_tiles) load_tile(t + 2);  // (tile t + 1 was converted between the context MFMAs)
         } else {
             if (TQ && t + 1 < n_tiles) {
                 dense_read(t + 1);
